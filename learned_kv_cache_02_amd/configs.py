@@ -1,0 +1,108 @@
+"""The five synthetic workloads the Nectar hot path is measured and checked on.
+
+Shapes follow Qwen3-4B, Qwen2.5-7B-1M and Llama-3.1-8B attention layers
+(KV heads, query heads, head dim); the document lengths stand in for the
+documents of Table 1 of the Nectar reading notes (section 3.1), which are not
+available here.  Every tensor is drawn from a seeded N(0, 1) (modules:
+N(0, 1/fan_in)); see ``synth.py`` for the recipe.
+
+Local part (section 2.2 of the notes): a question's own tokens after the
+document.  ``prompt`` tokens are already in the local cache; decode step ``s``
+adds token ``prompt + s`` and its query sees local keys ``0 .. prompt + s``.
+Prefill workloads (``decode_steps == 0``) run ``Tq == prompt`` causal query
+tokens at once.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Tuple
+
+
+@dataclass(frozen=True)
+class MLPShape:
+    Ht: int          # target hidden width (d -> Ht -> d)
+    Hs: int          # score hidden width  (d -> Hs -> 1)
+
+    def params(self, d: int) -> int:
+        """Parameters per KV head including all biases."""
+        return (d * self.Ht + self.Ht + self.Ht * d + d) + (d * self.Hs + self.Hs + self.Hs + 1)
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    seed: int
+    dtype: str               # "f32" or "bf16": storage type of q, caches and weights
+    layers: int
+    Hkv: int
+    Hq: int
+    d: int
+    n: int                   # document tokens
+    rope_base: float
+    B: int                   # concurrent questions
+    prompt: int              # local tokens per question before the first decode step
+    decode_steps: int        # 0: one causal prefill chunk of `prompt` tokens per question
+    mlps: Tuple[MLPShape, ...] = field(default_factory=tuple)
+    kv_pairs: int = 0        # Quadrature pairs p (0: form not used)
+    description: str = ""
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def prefill(self) -> bool:
+        return self.decode_steps == 0
+
+    @property
+    def Tq(self) -> int:
+        """Query tokens per question in one step."""
+        return self.prompt if self.prefill else 1
+
+    @property
+    def R(self) -> int:
+        """Query tokens per step."""
+        return self.B * self.Tq
+
+    @property
+    def T_cap(self) -> int:
+        """Local cache capacity per (question, KV head)."""
+        return self.prompt if self.prefill else self.prompt + self.decode_steps
+
+    def local_len(self, step: int = 0) -> int:
+        """Valid local keys at a step."""
+        return self.prompt if self.prefill else self.prompt + step + 1
+
+    def q_offset(self, step: int = 0) -> int:
+        """Local index seen by query token 0 of a step (it sees 0..q_offset+t)."""
+        return 0 if self.prefill else self.prompt + step
+
+    def query_pos(self, step: int = 0):
+        """Absolute RoPE positions of the Tq query tokens of a step."""
+        if self.prefill:
+            return [self.n + t for t in range(self.prompt)]
+        return [self.n + self.prompt + step]
+
+    def rho(self, params_per_head: int) -> float:
+        """Capacity ratio |theta| / (2 n d) per (layer, KV head)."""
+        return params_per_head / (2.0 * self.n * self.d)
+
+
+C1 = Config("c1_tiny_f32", 0, "f32", 1, 1, 2, 64, 512, 1e4, 1, 16, 0,
+            (MLPShape(256, 256),), 0,
+            "tiny single head, fp32: n=512, 16 local causal tokens")
+C2 = Config("c2_qwen3_4b_decode", 1, "bf16", 1, 8, 32, 128, 61440, 1e6, 1, 512, 1,
+            (MLPShape(4608, 2944),), 0,
+            "Qwen3-4B-shaped layer, decode batch 1, n=61,440, 512 prompt + 1 decode token")
+C3 = Config("c3_qwen25_7b_prefill", 2, "bf16", 28, 4, 28, 128, 131072, 1e7, 16, 1024, 0,
+            (MLPShape(768, 512), MLPShape(7680, 5120)), 0,
+            "Qwen2.5-7B-1M-shaped 28-layer stack, prefill 16 x 1,024 tokens, n=131,072")
+C4 = Config("c4_llama31_8b_decode", 3, "bf16", 32, 8, 32, 128, 262144, 5e5, 64, 256, 128,
+            (MLPShape(9984, 6144),), 0,
+            "Llama-3.1-8B-shaped 32-layer stack, decode batch 64, n=262,144")
+C5 = Config("c5_qwen25_7b_1m_decode", 4, "bf16", 28, 4, 28, 128, 1048576, 1e7, 8, 256, 128,
+            (MLPShape(5120, 3072),), 10486,
+            "Qwen2.5-7B-1M-shaped 28-layer stack, 1M-token document, decode batch 8")
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5)}
+BY_INDEX = [C1, C2, C3, C4, C5]

@@ -1,0 +1,190 @@
+"""Nectar CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Plain fp64 reference of the Nectar attention hot path (see ``nectar_oracle.c``
+for the definitions and the passages of the Nectar reading notes they follow).
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
+may import this package.  It shares no code with the HIP library.
+
+Arrays are numpy: bf16 tensors are passed as their raw ``uint16`` bit patterns,
+fp32 as ``float32``, fp64 as ``float64``; biases and merge inputs are
+``float64`` (fp32 values widen exactly).  Results are ``float64``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nectar_oracle.c")
+_LIB = os.path.join(_HERE, "libnectar_oracle.so")
+
+DT = {"f32": 0, "bf16": 1, "f64": 2}
+ACT = {"gelu": 0, "silu": 1}
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, OpenMP over rows)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-fno-fast-math", "-fopenmp", "-fPIC",
+                               "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P, I, L, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_double
+        lib.oracle_doc_attn.argtypes = [I, I, I, I, I, L, D, P, P, P, P, I, P, P, I]
+        lib.oracle_kvpair.argtypes = [I, I, I, I, I, L, D, P, P, P, P, I, P, P, I]
+        lib.oracle_local_attn.argtypes = [I, I, I, I, I, I, I, I, D, P, P, P, P, I, P, P, I]
+        lib.oracle_full_attn.argtypes = [I, I, I, I, I, I, L, I, I, D, P, P, P, P, P, P, I, P, P, I]
+        lib.oracle_mlp.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
+        lib.oracle_merge.argtypes = [L, I, P, P, P, P, P, P]
+        lib.oracle_merge.restype = None
+        lib.oracle_gelu.argtypes = [D]
+        lib.oracle_gelu.restype = D
+        lib.oracle_silu.argtypes = [D]
+        lib.oracle_silu.restype = D
+        _lib = lib
+    return _lib
+
+
+_NP = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}
+
+
+def _arr(x, dt):
+    a = np.ascontiguousarray(x)
+    if a.dtype != _NP[dt]:
+        raise TypeError("expected %s array for dtype %s, got %s" % (_NP[dt], dt, a.dtype))
+    return a
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _toks(toks, R):
+    if toks is None:
+        return None, R
+    t = np.ascontiguousarray(toks, dtype=np.int32)
+    if t.size and (t.min() < 0 or t.max() >= R):
+        raise IndexError("token index out of range")
+    return t, int(t.size)
+
+
+def _scale(scale, d):
+    return float(scale) if scale else 1.0 / np.sqrt(d)
+
+
+def doc_attn(q, K, V, *, dt, Hq, Hkv, scale=0.0, toks=None, threads=0):
+    """Eq. (3.1) per token/query head.  q [R][Hq][d], K/V [Hkv][n][d].
+    Returns (alpha [ntok][Hq], A [ntok][Hq][d]) in float64."""
+    q, K, V = _arr(q, dt), _arr(K, dt), _arr(V, dt)
+    d = q.shape[-1]
+    R = q.size // (Hq * d)
+    n = K.size // (Hkv * d)
+    t, nt = _toks(toks, R)
+    alpha = np.empty((nt, Hq)); A = np.empty((nt, Hq, d))
+    rc = _L().oracle_doc_attn(DT[dt], R, Hq, Hkv, d, n, _scale(scale, d), _p(q), _p(K), _p(V),
+                              _p(t), nt, _p(alpha), _p(A), threads)
+    if rc:
+        raise ValueError("oracle_doc_attn failed (%d)" % rc)
+    return alpha, A
+
+
+def kvpair(q, W, Z, *, dt, Hq, Hkv, scale=0.0, toks=None, threads=0):
+    """Quadrature module: exact attention over the p pairs (W, Z)."""
+    q, W, Z = _arr(q, dt), _arr(W, dt), _arr(Z, dt)
+    d = q.shape[-1]
+    R = q.size // (Hq * d)
+    p = W.size // (Hkv * d)
+    t, nt = _toks(toks, R)
+    a = np.empty((nt, Hq)); A = np.empty((nt, Hq, d))
+    rc = _L().oracle_kvpair(DT[dt], R, Hq, Hkv, d, p, _scale(scale, d), _p(q), _p(W), _p(Z),
+                            _p(t), nt, _p(a), _p(A), threads)
+    if rc:
+        raise ValueError("oracle_kvpair failed (%d)" % rc)
+    return a, A
+
+
+def local_attn(q, Kl, Vl, *, dt, B, Tq, Hq, Hkv, Tloc, q_offset, scale=0.0, toks=None, threads=0):
+    """Causal local attention.  q [B*Tq][Hq][d], Kl/Vl [B][Hkv][Tloc][d]."""
+    q, Kl, Vl = _arr(q, dt), _arr(Kl, dt), _arr(Vl, dt)
+    d = q.shape[-1]
+    t, nt = _toks(toks, B * Tq)
+    lse = np.empty((nt, Hq)); A = np.empty((nt, Hq, d))
+    rc = _L().oracle_local_attn(DT[dt], B, Tq, Hq, Hkv, d, Tloc, q_offset, _scale(scale, d),
+                                _p(q), _p(Kl), _p(Vl), _p(t), nt, _p(lse), _p(A), threads)
+    if rc:
+        raise ValueError("oracle_local_attn failed (%d)" % rc)
+    return lse, A
+
+
+def full_attn(q, K, V, Kl, Vl, *, dt, B, Tq, Hq, Hkv, Tloc, q_offset, scale=0.0, toks=None,
+              threads=0):
+    """Attention over [document; local] with the causal mask on the local part."""
+    q, K, V, Kl, Vl = (_arr(x, dt) for x in (q, K, V, Kl, Vl))
+    d = q.shape[-1]
+    n = K.size // (Hkv * d)
+    t, nt = _toks(toks, B * Tq)
+    lse = np.empty((nt, Hq)); out = np.empty((nt, Hq, d))
+    rc = _L().oracle_full_attn(DT[dt], B, Tq, Hq, Hkv, d, n, Tloc, q_offset, _scale(scale, d),
+                               _p(q), _p(K), _p(V), _p(Kl), _p(Vl), _p(t), nt, _p(lse), _p(out),
+                               threads)
+    if rc:
+        raise ValueError("oracle_full_attn failed (%d)" % rc)
+    return lse, out
+
+
+def mlp(q, W1, b1, W2t, b2, Ws, bs, ws2, bs2, *, dt, Hq, Hkv, act="gelu", toks=None, threads=0):
+    """One-hidden-layer score/target MLP module.  Returns (a [ntok][Hq], A [ntok][Hq][d])."""
+    q, W1, W2t, Ws, ws2 = (_arr(x, dt) for x in (q, W1, W2t, Ws, ws2))
+    b1, b2, bs, bs2 = (_f64(x) for x in (b1, b2, bs, bs2))
+    d = q.shape[-1]
+    R = q.size // (Hq * d)
+    Ht = W1.size // (Hkv * d)
+    Hs = Ws.size // (Hkv * d)
+    if W2t.size != W1.size or b1.size != Hkv * Ht or b2.size != Hkv * d or bs.size != Hkv * Hs \
+            or ws2.size != Hkv * Hs or bs2.size != Hkv:
+        raise ValueError("inconsistent MLP parameter shapes")
+    t, nt = _toks(toks, R)
+    a = np.empty((nt, Hq)); A = np.empty((nt, Hq, d))
+    rc = _L().oracle_mlp(DT[dt], R, Hq, Hkv, d, Ht, Hs, ACT[act], _p(W1), _p(b1), _p(W2t), _p(b2),
+                         _p(Ws), _p(bs), _p(ws2), _p(bs2), _p(q), _p(t), nt, _p(a), _p(A), threads)
+    if rc:
+        raise ValueError("oracle_mlp failed (%d)" % rc)
+    return a, A
+
+
+def merge(a, A, lam, Aloc):
+    """Log-sum-exp merge of (a, A) with (lam, A_loc).  Returns (out, lse) in float64."""
+    a, A, lam, Aloc = _f64(a), _f64(A), _f64(lam), _f64(Aloc)
+    d = A.shape[-1]
+    rows = a.size
+    if A.size != rows * d or lam.size != rows or Aloc.size != rows * d:
+        raise ValueError("inconsistent merge shapes")
+    out = np.empty(A.shape); lse = np.empty(a.shape)
+    _L().oracle_merge(rows, d, _p(a), _p(A), _p(lam), _p(Aloc), _p(out), _p(lse))
+    return out, lse
+
+
+def gelu(x: float) -> float:
+    return _L().oracle_gelu(float(x))
+
+
+def silu(x: float) -> float:
+    return _L().oracle_silu(float(x))

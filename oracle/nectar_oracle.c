@@ -1,0 +1,318 @@
+/*
+ * Nectar CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct fp64 implementation of what the Nectar
+ * attention hot path computes.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the product path never
+ * does.  It shares no code, header, table or helper with the HIP library.
+ *
+ * Source of every definition: the reading notes "Nectar: Neural Estimation of
+ * Cached-Token Attention via Regression" (cc.laoqi.cc/papers/2605.09778/v2/r1),
+ * section 2 ("method"):
+ *   - section 2.1, Eq. (3.1): s_j = q.k_j / sqrt(d),
+ *       alpha(q) = log sum_j exp(s_j),
+ *       A(q)     = sum_j exp(s_j) v_j / sum_j exp(s_j);
+ *     GQA: the query heads of one KV group share K, V and the module pair.
+ *   - section 2.2, Eqs. (3.4)-(3.5): Z_local, N_local over the causally visible
+ *     local tokens (index i <= t), and the log-sum-exp merge of the document
+ *     pair with the local part (the "virtual logit").
+ *   - section 2.4, Quadrature form: a = log sum_j exp((W q)_j / sqrt(d)),
+ *     A = softmax(W q / sqrt(d))^T Z  -- exact attention over (W, Z, p).
+ *   - section 2.4, Eq. (3.6): MLP form.  The workloads fix one hidden layer
+ *     with GELU: A = W2 GELU(W1 q + b1) + b2, a = w2 . GELU(Ws q + bs) + bs2.
+ *     SiLU is provided as the activation Eq. (3.6) itself names.
+ *
+ * Precision: every input element is widened exactly to double (bf16 bits are
+ * shifted into an fp32 pattern; fp32 widens exactly); every sum is a plain
+ * sequential double sum in index order.  The log-sum-exp is evaluated as
+ * m + log(sum_j exp(s_j - m)) with m = max_j s_j, which is the same number as
+ * log(sum_j exp(s_j)) in exact arithmetic and does not overflow.
+ *
+ * Parallelism: independent (token, query head) rows are spread over OpenMP
+ * threads; each row is computed exactly as written, so the result does not
+ * depend on the thread count.
+ *
+ * Layouts (row-major, innermost last):
+ *   q      [R][Hq][d]             R = query tokens
+ *   K, V   [Hkv][n][d]            document cache (keys already RoPE'd)
+ *   Kl, Vl [B][Hkv][Tloc][d]      local cache per question
+ *   W1, W2t[Hkv][Ht][d]           W2t[h][j][c] = weight from hidden j to output c
+ *   Ws     [Hkv][Hs][d], ws2 [Hkv][Hs]
+ *   b1 [Hkv][Ht], b2 [Hkv][d], bs [Hkv][Hs], bs2 [Hkv]  (double)
+ *   query head hq reads KV head hq / (Hq / Hkv).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
+enum { OR_GELU = 0, OR_SILU = 1 };
+
+/* Read element i of an array of the given element type, widened to double. */
+static double ld(const void *p, int dt, size_t i)
+{
+    if (dt == OR_F64) return ((const double *)p)[i];
+    if (dt == OR_F32) return (double)((const float *)p)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static int valid_dt(int dt) { return dt == OR_F32 || dt == OR_BF16 || dt == OR_F64; }
+
+static void set_threads(int nthreads)
+{
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+}
+
+double oracle_gelu(double x) { return x * 0.5 * (1.0 + erf(x / sqrt(2.0))); }
+double oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+
+static double act_fn(int act, double x) { return act == OR_SILU ? oracle_silu(x) : oracle_gelu(x); }
+
+/*
+ * Attention of one query vector over a set of key/value rows, returning the
+ * log of the sum of exponentiated scores and the normalized read-out.
+ * keys: row j at K + (koff + j * d) elements, j = 0..nk-1.
+ * An empty set gives lse = -inf and a zero read-out.
+ */
+static void attend(int dt, int d, long nk, double scale,
+                   const void *q, size_t qoff,
+                   const void *K, const void *V, size_t koff,
+                   double *s /* scratch, nk */, double *lse, double *out)
+{
+    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    if (nk <= 0) { *lse = -INFINITY; return; }
+    double m = -INFINITY;
+    for (long j = 0; j < nk; ++j) {
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c)
+            dot += ld(q, dt, qoff + c) * ld(K, dt, koff + (size_t)j * d + c);
+        s[j] = dot * scale;
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (long j = 0; j < nk; ++j) {
+        double w = exp(s[j] - m);
+        l += w;
+        for (int c = 0; c < d; ++c) out[c] += w * ld(V, dt, koff + (size_t)j * d + c);
+    }
+    for (int c = 0; c < d; ++c) out[c] /= l;
+    *lse = m + log(l);
+}
+
+static int shape_ok(int R, int Hq, int Hkv, int d)
+{
+    return R >= 0 && Hq > 0 && Hkv > 0 && d > 0 && Hq % Hkv == 0;
+}
+
+/*
+ * Exact document attention, Eq. (3.1), for the listed tokens (toks == NULL:
+ * all R tokens).  alpha_out[i][hq], A_out[i][hq][c] for i = 0..ntok-1.
+ */
+int oracle_doc_attn(int dt, int R, int Hq, int Hkv, int d, long n, double scale,
+                    const void *q, const void *K, const void *V,
+                    const int32_t *toks, int ntok,
+                    double *alpha_out, double *A_out, int nthreads)
+{
+    if (!valid_dt(dt) || !shape_ok(R, Hq, Hkv, d) || n < 0) return 1;
+    if (!toks) ntok = R;
+    const int G = Hq / Hkv;
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        if (!s) {
+#pragma omp atomic write
+            err = 2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long row = 0; row < (long)ntok * Hq; ++row) {
+            if (!s) continue;
+            int i = (int)(row / Hq), hq = (int)(row % Hq);
+            int r = toks ? toks[i] : i;
+            int h = hq / G;
+            attend(dt, d, n, scale, q, ((size_t)r * Hq + hq) * d,
+                   K, V, (size_t)h * n * d, s,
+                   &alpha_out[(size_t)i * Hq + hq], &A_out[((size_t)i * Hq + hq) * d]);
+        }
+        free(s);
+    }
+    return err;
+}
+
+/*
+ * Quadrature (learnable KV pair) module, section 2.4: exact attention over the
+ * p parameter pairs (W, Z) with the same 1/sqrt(d) scaling.
+ */
+int oracle_kvpair(int dt, int R, int Hq, int Hkv, int d, long p, double scale,
+                  const void *q, const void *W, const void *Z,
+                  const int32_t *toks, int ntok,
+                  double *a_out, double *A_out, int nthreads)
+{
+    return oracle_doc_attn(dt, R, Hq, Hkv, d, p, scale, q, W, Z, toks, ntok, a_out, A_out, nthreads);
+}
+
+/*
+ * Local causal attention, section 2.2: token t of question b (query row
+ * r = b*Tq + t) sees local keys i = 0 .. min(q_offset + t, Tloc - 1) of its
+ * own question's cache.  Returns lse = log Z_local and A_local = N_local / Z_local;
+ * an empty visible set gives lse = -inf and A_local = 0.
+ */
+int oracle_local_attn(int dt, int B, int Tq, int Hq, int Hkv, int d, int Tloc, int q_offset,
+                      double scale, const void *q, const void *Kl, const void *Vl,
+                      const int32_t *toks, int ntok, double *lse_out, double *A_out, int nthreads)
+{
+    if (!valid_dt(dt) || B < 0 || Tq < 0 || !shape_ok(B * Tq, Hq, Hkv, d) || Tloc < 0) return 1;
+    const int R = B * Tq;
+    if (!toks) ntok = R;
+    const int G = Hq / Hkv;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Tloc > 0 ? Tloc : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (long row = 0; row < (long)ntok * Hq; ++row) {
+            int i = (int)(row / Hq), hq = (int)(row % Hq);
+            int r = toks ? toks[i] : i;
+            int b = r / Tq, t = r % Tq, h = hq / G;
+            long vis = (long)q_offset + t + 1;
+            if (vis > Tloc) vis = Tloc;
+            if (vis < 0) vis = 0;
+            attend(dt, d, vis, scale, q, ((size_t)r * Hq + hq) * d,
+                   Kl, Vl, ((size_t)b * Hkv + h) * (size_t)Tloc * d, s,
+                   &lse_out[(size_t)i * Hq + hq], &A_out[((size_t)i * Hq + hq) * d]);
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/*
+ * Full attention over the concatenated [document; local] cache with the causal
+ * mask on the local part only (the left-hand side of Eq. (3.4)).
+ */
+int oracle_full_attn(int dt, int B, int Tq, int Hq, int Hkv, int d, long n, int Tloc, int q_offset,
+                     double scale, const void *q, const void *K, const void *V,
+                     const void *Kl, const void *Vl,
+                     const int32_t *toks, int ntok, double *lse_out, double *out, int nthreads)
+{
+    if (!valid_dt(dt) || B < 0 || Tq < 0 || !shape_ok(B * Tq, Hq, Hkv, d) || n < 0 || Tloc < 0) return 1;
+    const int R = B * Tq;
+    if (!toks) ntok = R;
+    const int G = Hq / Hkv;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(n + Tloc + 1));
+#pragma omp for schedule(dynamic, 1)
+        for (long row = 0; row < (long)ntok * Hq; ++row) {
+            int i = (int)(row / Hq), hq = (int)(row % Hq);
+            int r = toks ? toks[i] : i;
+            int b = r / Tq, t = r % Tq, h = hq / G;
+            long vis = (long)q_offset + t + 1;
+            if (vis > Tloc) vis = Tloc;
+            if (vis < 0) vis = 0;
+            size_t qo = ((size_t)r * Hq + hq) * d;
+            size_t dko = (size_t)h * n * d;
+            size_t lko = ((size_t)b * Hkv + h) * (size_t)Tloc * d;
+            long nk = n + vis;
+            double *o = &out[((size_t)i * Hq + hq) * d];
+            for (int c = 0; c < d; ++c) o[c] = 0.0;
+            if (nk == 0) { lse_out[(size_t)i * Hq + hq] = -INFINITY; continue; }
+            double m = -INFINITY;
+            for (long j = 0; j < nk; ++j) {
+                const void *Kp = j < n ? K : Kl;
+                size_t ko = j < n ? dko + (size_t)j * d : lko + (size_t)(j - n) * d;
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c) dot += ld(q, dt, qo + c) * ld(Kp, dt, ko + c);
+                s[j] = dot * scale;
+                if (s[j] > m) m = s[j];
+            }
+            double l = 0.0;
+            for (long j = 0; j < nk; ++j) {
+                const void *Vp = j < n ? V : Vl;
+                size_t vo = j < n ? dko + (size_t)j * d : lko + (size_t)(j - n) * d;
+                double w = exp(s[j] - m);
+                l += w;
+                for (int c = 0; c < d; ++c) o[c] += w * ld(Vp, dt, vo + c);
+            }
+            for (int c = 0; c < d; ++c) o[c] /= l;
+            lse_out[(size_t)i * Hq + hq] = m + log(l);
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/*
+ * One-hidden-layer MLP module (Eq. (3.6) with only h_0), for the listed tokens:
+ *   z_j   = sum_c W1[h][j][c] q_c + b1[h][j],     A_c = sum_j W2t[h][j][c] act(z_j) + b2[h][c]
+ *   zs_j  = sum_c Ws[h][j][c] q_c + bs[h][j],     a   = sum_j ws2[h][j] act(zs_j) + bs2[h]
+ */
+int oracle_mlp(int dt, int R, int Hq, int Hkv, int d, int Ht, int Hs, int act,
+               const void *W1, const double *b1, const void *W2t, const double *b2,
+               const void *Ws, const double *bs, const void *ws2, const double *bs2,
+               const void *q, const int32_t *toks, int ntok,
+               double *a_out, double *A_out, int nthreads)
+{
+    if (!valid_dt(dt) || !shape_ok(R, Hq, Hkv, d) || Ht < 0 || Hs < 0) return 1;
+    if (act != OR_GELU && act != OR_SILU) return 1;
+    if (!toks) ntok = R;
+    const int G = Hq / Hkv;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long row = 0; row < (long)ntok * Hq; ++row) {
+        int i = (int)(row / Hq), hq = (int)(row % Hq);
+        int r = toks ? toks[i] : i;
+        int h = hq / G;
+        size_t qo = ((size_t)r * Hq + hq) * d;
+        double *A = &A_out[((size_t)i * Hq + hq) * d];
+        for (int c = 0; c < d; ++c) A[c] = b2[(size_t)h * d + c];
+        for (int j = 0; j < Ht; ++j) {
+            size_t wo = ((size_t)h * Ht + j) * d;
+            double z = 0.0;
+            for (int c = 0; c < d; ++c) z += ld(W1, dt, wo + c) * ld(q, dt, qo + c);
+            double y = act_fn(act, z + b1[(size_t)h * Ht + j]);
+            for (int c = 0; c < d; ++c) A[c] += ld(W2t, dt, wo + c) * y;
+        }
+        double a = bs2[h];
+        for (int j = 0; j < Hs; ++j) {
+            size_t wo = ((size_t)h * Hs + j) * d;
+            double z = 0.0;
+            for (int c = 0; c < d; ++c) z += ld(Ws, dt, wo + c) * ld(q, dt, qo + c);
+            a += ld(ws2, dt, (size_t)h * Hs + j) * act_fn(act, z + bs[(size_t)h * Hs + j]);
+        }
+        a_out[(size_t)i * Hq + hq] = a;
+    }
+    return 0;
+}
+
+/*
+ * Log-sum-exp merge of two (lse, read-out) pairs, Eqs. (3.4)-(3.5): the first
+ * pair is the document part (exact alpha, A or the module's a, A), used as one
+ * extra "virtual logit" with value A beside the local part (lse_loc, A_loc):
+ *   out = (e^a A + e^lam A_loc) / (e^a + e^lam),   lse = log(e^a + e^lam),
+ * evaluated with M = max(a, lam).  Both sides -inf gives out = 0, lse = -inf.
+ */
+void oracle_merge(long rows, int d, const double *a, const double *A,
+                  const double *lam, const double *Aloc, double *out, double *lse)
+{
+    for (long r = 0; r < rows; ++r) {
+        double M = a[r] > lam[r] ? a[r] : lam[r];
+        double *o = &out[(size_t)r * d];
+        if (M == -INFINITY) {
+            for (int c = 0; c < d; ++c) o[c] = 0.0;
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double wa = exp(a[r] - M), wl = exp(lam[r] - M);
+        for (int c = 0; c < d; ++c)
+            o[c] = (wa * A[(size_t)r * d + c] + wl * Aloc[(size_t)r * d + c]) / (wa + wl);
+        lse[r] = M + log(wa + wl);
+    }
+}

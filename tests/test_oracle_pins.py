@@ -1,0 +1,376 @@
+"""Pins of the fp64 CPU oracle to facts fixed outside the oracle itself.
+
+Each test names the passage of the Nectar reading notes
+(cc.laoqi.cc/papers/2605.09778/v2/r1) or the mathematical fact it checks.
+They are chosen so that a plausible slip in the oracle -- a dropped 1/sqrt(d),
+a wrong GQA head map, an off-by-one causal mask, a transposed weight, a
+dropped bias, the wrong activation -- fails at least one of them.
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+def _rand(*shape, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+# --- P1: Eq. (3.1) against an independent 50-digit decimal evaluation ---------
+
+def _decimal_attn(q, K, V, scale):
+    """alpha and A of Eq. (3.1) in 50-digit decimal arithmetic, no max shift."""
+    getcontext().prec = 50
+    n, d = K.shape
+    sc = Decimal(scale)
+    w = []
+    for j in range(n):
+        s = sum(Decimal(float(q[c])) * Decimal(float(K[j, c])) for c in range(d)) * sc
+        w.append(s.exp())
+    Z = sum(w)
+    alpha = float(Z.ln())
+    A = [float(sum(w[j] * Decimal(float(V[j, c])) for j in range(n)) / Z) for c in range(d)]
+    return alpha, np.array(A)
+
+
+@pytest.mark.parametrize("n,d", [(1, 1), (3, 2), (5, 4), (8, 4)])
+def test_p1_eq31_decimal_bruteforce(n, d):
+    q = _rand(1, 1, d)
+    K = _rand(1, n, d)
+    V = _rand(1, n, d)
+    a, A = oracle.doc_attn(q, K, V, dt="f64", Hq=1, Hkv=1)
+    ea, eA = _decimal_attn(q[0, 0], K[0], V[0], 1.0 / math.sqrt(d))
+    assert abs(a[0, 0] - ea) <= 1e-13 * max(1.0, abs(ea))
+    np.testing.assert_allclose(A[0, 0], eA, rtol=0, atol=1e-13)
+
+
+def test_p1_scale_and_explicit_scale():
+    # n = 1: alpha = q.k / sqrt(d) exactly; d = 4 -> 1/2.
+    q = np.array([[[2.0, 0.0, 0.0, 0.0]]])
+    K = np.array([[[1.0, 5.0, 0.0, 0.0]]])
+    V = np.array([[[7.0, -1.0, 0.5, 3.0]]])
+    a, A = oracle.doc_attn(q, K, V, dt="f64", Hq=1, Hkv=1)
+    assert a[0, 0] == 1.0
+    np.testing.assert_array_equal(A[0, 0], V[0, 0])
+    a2, _ = oracle.doc_attn(q, K, V, dt="f64", Hq=1, Hkv=1, scale=0.25)
+    assert a2[0, 0] == 0.5
+
+
+# --- P4: closed forms derived from Eq. (3.1) ----------------------------------
+
+def test_p4_zero_query():
+    n, d = 7, 4
+    K, V = _rand(1, n, d), _rand(1, n, d)
+    a, A = oracle.doc_attn(np.zeros((1, 1, d)), K, V, dt="f64", Hq=1, Hkv=1)
+    assert abs(a[0, 0] - math.log(n)) < 1e-15
+    np.testing.assert_allclose(A[0, 0], V[0].mean(axis=0), atol=1e-15)
+
+
+def test_p4_equal_keys_and_duplication():
+    n, d = 6, 4
+    q = _rand(1, 1, d)
+    k = _rand(d)
+    K = np.tile(k, (1, n, 1))
+    V = _rand(1, n, d)
+    a, A = oracle.doc_attn(q, K, V, dt="f64", Hq=1, Hkv=1)
+    assert abs(a[0, 0] - (math.log(n) + float(q[0, 0] @ k) / 2.0)) < 1e-14
+    np.testing.assert_allclose(A[0, 0], V[0].mean(axis=0), atol=1e-14)
+    K2, V2 = _rand(1, 5, d), _rand(1, 5, d)
+    a1, A1 = oracle.doc_attn(q, K2, V2, dt="f64", Hq=1, Hkv=1)
+    ad, Ad = oracle.doc_attn(q, np.concatenate([K2, K2], 1), np.concatenate([V2, V2], 1),
+                             dt="f64", Hq=1, Hkv=1)
+    assert abs(ad[0, 0] - (a1[0, 0] + math.log(2.0))) < 1e-14
+    np.testing.assert_allclose(Ad, A1, atol=1e-14)
+
+
+def test_gqa_head_map_contiguous_groups():
+    # section 2.1: the query heads of one KV group share K and V; groups are contiguous.
+    R, Hq, Hkv, n, d = 2, 6, 3, 4, 4
+    q = _rand(R, Hq, d)
+    K = _rand(Hkv, n, d)
+    V = np.stack([np.full((n, d), float(h)) for h in range(Hkv)])
+    _, A = oracle.doc_attn(q, K, V, dt="f64", Hq=Hq, Hkv=Hkv)
+    for hq in range(Hq):
+        np.testing.assert_allclose(A[:, hq], hq // 2, atol=1e-14)
+
+
+def test_token_subset_matches_full():
+    R, Hq, Hkv, n, d = 5, 4, 2, 9, 8
+    q, K, V = _rand(R, Hq, d), _rand(Hkv, n, d), _rand(Hkv, n, d)
+    a, A = oracle.doc_attn(q, K, V, dt="f64", Hq=Hq, Hkv=Hkv)
+    a2, A2 = oracle.doc_attn(q, K, V, dt="f64", Hq=Hq, Hkv=Hkv, toks=[4, 1])
+    np.testing.assert_array_equal(a2, a[[4, 1]])
+    np.testing.assert_array_equal(A2, A[[4, 1]])
+
+
+# --- P3: the worked example printed with the gate form (section 2.2) ----------
+
+def test_p3_printed_worked_example():
+    g = json.load(open(os.path.join(GOLD, "worked_example_merge.json")))
+    a = np.array([math.log(g["doc_weight_sum"])])
+    lam = np.array([math.log(g["local_weight_sum"])])
+    out, lse = oracle.merge(a, np.array([[g["doc_readout"]]]), lam, np.array([[g["local_readout"]]]))
+    assert abs(out[0, 0] - g["expected_output"]) < 1e-14
+    assert abs(lse[0] - math.log(g["doc_weight_sum"] + g["local_weight_sum"])) < 1e-14
+    # gate form: g = sigmoid(a - log Z_local) = 0.75 gives the same output
+    gate = 1.0 / (1.0 + math.exp(-(a[0] - lam[0])))
+    assert abs(gate - 0.75) < 1e-15
+    assert abs(gate * g["doc_readout"] + (1 - gate) * g["local_readout"] - out[0, 0]) < 1e-14
+
+
+def test_merge_infinities():
+    d = 3
+    A = _rand(2, d)
+    Al = _rand(2, d)
+    out, lse = oracle.merge(np.array([0.3, -np.inf]), A, np.array([-np.inf, -np.inf]), Al)
+    np.testing.assert_allclose(out[0], A[0], atol=0)
+    assert lse[0] == 0.3
+    assert np.all(out[1] == 0.0) and lse[1] == -np.inf
+
+
+# --- P2: Appendix B identity, Eq. (3.4) -----------------------------------------
+
+@pytest.mark.parametrize("q_offset,Tq,Tloc", [(0, 5, 5), (3, 2, 5), (0, 3, 7)])
+def test_p2_split_identity_equals_full_attention(q_offset, Tq, Tloc):
+    B, Hq, Hkv, n, d = 2, 4, 2, 11, 8
+    R = B * Tq
+    q = _rand(R, Hq, d)
+    K, V = _rand(Hkv, n, d), _rand(Hkv, n, d)
+    Kl, Vl = _rand(B, Hkv, Tloc, d), _rand(B, Hkv, Tloc, d)
+    kw = dict(dt="f64", B=B, Tq=Tq, Hq=Hq, Hkv=Hkv, Tloc=Tloc, q_offset=q_offset)
+    alpha, Ad = oracle.doc_attn(q, K, V, dt="f64", Hq=Hq, Hkv=Hkv)
+    lam, Al = oracle.local_attn(q, Kl, Vl, **kw)
+    out, lse = oracle.merge(alpha, Ad, lam, Al)
+    flse, fout = oracle.full_attn(q, K, V, Kl, Vl, **kw)
+    assert np.max(np.abs(out - fout)) < 1e-12
+    assert np.max(np.abs(lse - flse)) < 1e-12
+
+
+# --- local attention: the causal visible set i <= q_offset + t (section 2.2) ----
+
+def test_local_first_token_sees_only_key0():
+    Hq = Hkv = 1
+    d, Tloc = 4, 3
+    q = _rand(Tloc, Hq, d)
+    Kl, Vl = _rand(1, Hkv, Tloc, d), _rand(1, Hkv, Tloc, d)
+    lam, A = oracle.local_attn(q, Kl, Vl, dt="f64", B=1, Tq=Tloc, Hq=1, Hkv=1, Tloc=Tloc, q_offset=0)
+    assert abs(lam[0, 0] - float(q[0, 0] @ Kl[0, 0, 0]) / 2.0) < 1e-15
+    np.testing.assert_allclose(A[0, 0], Vl[0, 0, 0], atol=1e-15)
+    # token 1 sees keys 0 and 1: compare with document attention over those two keys
+    a2, A2 = oracle.doc_attn(q[1:2], Kl[0, :, :2], Vl[0, :, :2], dt="f64", Hq=1, Hkv=1)
+    assert abs(lam[1, 0] - a2[0, 0]) < 1e-15
+    np.testing.assert_allclose(A[1, 0], A2[0, 0], atol=1e-15)
+
+
+def test_local_offset_beyond_cache_and_empty():
+    B, Hq, Hkv, d, Tloc = 2, 2, 1, 4, 6
+    q = _rand(B, Hq, d)
+    Kl, Vl = _rand(B, Hkv, Tloc, d), _rand(B, Hkv, Tloc, d)
+    lam, A = oracle.local_attn(q, Kl, Vl, dt="f64", B=B, Tq=1, Hq=Hq, Hkv=Hkv, Tloc=Tloc, q_offset=100)
+    for b in range(B):
+        a2, A2 = oracle.doc_attn(q[b:b + 1], Kl[b], Vl[b], dt="f64", Hq=Hq, Hkv=Hkv)
+        np.testing.assert_allclose(lam[b], a2[0], atol=1e-15)
+        np.testing.assert_allclose(A[b], A2[0], atol=1e-15)
+    lam0, A0 = oracle.local_attn(q, Kl[:, :, :0], Vl[:, :, :0], dt="f64", B=B, Tq=1, Hq=Hq,
+                                 Hkv=Hkv, Tloc=0, q_offset=0)
+    assert np.all(lam0 == -np.inf) and np.all(A0 == 0.0)
+
+
+# --- P5: split invariance (the regrouping of Eq. (3.4) applied to document keys)
+
+def test_p5_split_invariance():
+    Hq, Hkv, n, d = 2, 1, 13, 8
+    q = _rand(3, Hq, d)
+    K, V = _rand(Hkv, n, d), _rand(Hkv, n, d)
+    a, A = oracle.doc_attn(q, K, V, dt="f64", Hq=Hq, Hkv=Hkv)
+    for m in (1, 6, 12):
+        a1, A1 = oracle.doc_attn(q, K[:, :m], V[:, :m], dt="f64", Hq=Hq, Hkv=Hkv)
+        a2, A2 = oracle.doc_attn(q, K[:, m:], V[:, m:], dt="f64", Hq=Hq, Hkv=Hkv)
+        o, l = oracle.merge(a1, A1, a2, A2)
+        assert np.max(np.abs(o - A)) < 1e-14 and np.max(np.abs(l - a)) < 1e-14
+
+
+# --- P6: gradient identity of the log-normalizer (Appendix B) ------------------
+
+def test_p6_gradient_is_key_weighted_average():
+    n, d = 9, 4
+    q = _rand(1, 1, d)
+    K, V = _rand(1, n, d), _rand(1, n, d)
+    # d alpha / dq = sum_j softmax_j k_j / sqrt(d): the read-out with V := K, scaled.
+    _, AK = oracle.doc_attn(q, K, K, dt="f64", Hq=1, Hkv=1)
+    grad = AK[0, 0] / math.sqrt(d)
+    h = 1e-5
+    for c in range(d):
+        e = np.zeros_like(q); e[0, 0, c] = h
+        ap, _ = oracle.doc_attn(q + e, K, V, dt="f64", Hq=1, Hkv=1)
+        am, _ = oracle.doc_attn(q - e, K, V, dt="f64", Hq=1, Hkv=1)
+        assert abs((ap[0, 0] - am[0, 0]) / (2 * h) - grad[c]) < 1e-8
+    # and the read-out uses the values, not the keys (the two differ in general)
+    _, AV = oracle.doc_attn(q, K, V, dt="f64", Hq=1, Hkv=1)
+    assert np.max(np.abs(AV - AK)) > 1e-3
+
+
+# --- P7: low-temperature limit (Appendix B) ------------------------------------
+
+def test_p7_low_temperature_limit_no_overflow():
+    n, d = 50, 16
+    q = _rand(1, 1, d)
+    K, V = _rand(1, n, d), _rand(1, n, d)
+    mx = float(np.max(K[0] @ q[0, 0]))
+    for beta in (10.0, 100.0, 1000.0):
+        a, A = oracle.doc_attn(q * beta, K, V, dt="f64", Hq=1, Hkv=1)
+        approx = a[0, 0] * math.sqrt(d) / beta
+        assert np.isfinite(a[0, 0]) and np.all(np.isfinite(A))
+        assert mx - 1e-12 <= approx <= mx + math.sqrt(d) * math.log(n) / beta + 1e-12
+    jmax = int(np.argmax(K[0] @ q[0, 0]))
+    np.testing.assert_allclose(A[0, 0], V[0, jmax], atol=1e-9)
+
+
+# --- P8: Quadrature initialised with the first p cache rows (section 2.4) -------
+
+def test_p8_kvpair_with_cache_init_equals_exact_prefix():
+    Hq, Hkv, n, d, p = 4, 2, 20, 8, 7
+    q = _rand(3, Hq, d)
+    K, V = _rand(Hkv, n, d), _rand(Hkv, n, d)
+    a, A = oracle.kvpair(q, K[:, :p].copy(), V[:, :p].copy(), dt="f64", Hq=Hq, Hkv=Hkv)
+    e, E = oracle.doc_attn(q, K[:, :p].copy(), V[:, :p].copy(), dt="f64", Hq=Hq, Hkv=Hkv)
+    np.testing.assert_array_equal(a, e)
+    np.testing.assert_array_equal(A, E)
+
+
+# --- P9: activations against textbook values -----------------------------------
+
+def test_p9_gelu_textbook_values():
+    # GELU(x) = x * Phi(x); Phi from standard normal tables.
+    phi = {1.0: 0.8413447460685429, -1.0: 0.15865525393145707, 2.0: 0.9772498680518208,
+           0.5: 0.6914624612740131, -3.0: 0.0013498980316300946}
+    for x, p in phi.items():
+        assert abs(oracle.gelu(x) - x * p) < 1e-15
+    assert oracle.gelu(0.0) == 0.0
+    assert abs(oracle.gelu(12.0) - 12.0) < 1e-15
+    assert abs(oracle.gelu(-12.0)) < 1e-15
+
+
+def test_p9_silu_textbook_values():
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(1.0) - 0.7310585786300049) < 1e-15      # 1 / (1 + e^-1)
+    assert abs(oracle.silu(-2.0) - (-2.0 * 0.11920292202211755)) < 1e-15
+
+
+# --- P10: MLP module special cases and a hand-worked example --------------------
+
+def _mlp_zero(Hkv, d, Ht, Hs):
+    return dict(W1=np.zeros((Hkv, Ht, d)), b1=np.zeros((Hkv, Ht)), W2t=np.zeros((Hkv, Ht, d)),
+                b2=np.zeros((Hkv, d)), Ws=np.zeros((Hkv, Hs, d)), bs=np.zeros((Hkv, Hs)),
+                ws2=np.zeros((Hkv, Hs)), bs2=np.zeros(Hkv))
+
+
+def _run_mlp(q, P, Hq, Hkv, act="gelu"):
+    return oracle.mlp(q, P["W1"], P["b1"], P["W2t"], P["b2"], P["Ws"], P["bs"], P["ws2"], P["bs2"],
+                      dt="f64", Hq=Hq, Hkv=Hkv, act=act)
+
+
+def test_p10_mlp_hand_worked_example():
+    # d = 2, Ht = 2, Hs = 2, one head.  z = W1 q + b1 = (1, -2); A_c = sum_j W2t[j][c] GELU(z_j) + b2_c.
+    Phi1, Phi2 = 0.8413447460685429, 0.9772498680518208
+    g1, gm2 = 1.0 * Phi1, -2.0 * (1.0 - Phi2)            # GELU(1), GELU(-2)
+    P = _mlp_zero(1, 2, 2, 2)
+    P["W1"][0] = [[1.0, 0.0], [0.0, 2.0]]
+    q = np.array([[[1.0, -1.0]]])
+    P["W2t"][0] = [[0.0, 1.0], [3.0, 0.0]]               # hidden 0 -> output 1, hidden 1 -> output 0
+    P["b2"][0] = [0.5, -0.25]
+    P["Ws"][0] = [[0.0, 1.0], [1.0, 1.0]]                # zs = (-1, 0) + bs
+    P["bs"][0] = [0.0, 1.0]                              # zs = (-1, 1)
+    P["ws2"][0] = [2.0, -1.0]
+    P["bs2"][0] = 0.125
+    a, A = _run_mlp(q, P, 1, 1)
+    np.testing.assert_allclose(A[0, 0], [3.0 * gm2 + 0.5, g1 - 0.25], atol=1e-15)
+    expect_a = 2.0 * (-1.0 * (1 - Phi1)) - 1.0 * (1.0 * Phi1) + 0.125
+    assert abs(a[0, 0] - expect_a) < 1e-15
+    # SiLU variant of the same network
+    a_s, A_s = _run_mlp(q, P, 1, 1, act="silu")
+    sg = lambda x: x / (1 + math.exp(-x))
+    np.testing.assert_allclose(A_s[0, 0], [3.0 * sg(-2.0) + 0.5, sg(1.0) - 0.25], atol=1e-15)
+    assert abs(a_s[0, 0] - (2.0 * sg(-1.0) - sg(1.0) + 0.125)) < 1e-15
+
+
+def test_p10_mlp_special_cases():
+    Hq, Hkv, d, Ht, Hs = 4, 2, 8, 16, 8
+    q = _rand(3, Hq, d)
+    P = {k: _rand(*v.shape) if v.ndim else v for k, v in _mlp_zero(Hkv, d, Ht, Hs).items()}
+    P["bs2"] = _rand(Hkv)
+    # W2 = 0 -> target = b2; ws2 = 0 -> score = bs2   (per KV head of each query head)
+    Z = dict(P); Z["W2t"] = np.zeros_like(P["W2t"]); Z["ws2"] = np.zeros_like(P["ws2"])
+    a, A = _run_mlp(q, Z, Hq, Hkv)
+    for hq in range(Hq):
+        np.testing.assert_allclose(A[:, hq], np.broadcast_to(P["b2"][hq // 2], (3, d)), atol=1e-15)
+        np.testing.assert_allclose(a[:, hq], P["bs2"][hq // 2], atol=1e-15)
+    # q = 0 and b1 = bs = 0 -> hidden GELU(0) = 0 -> outputs are the output biases
+    Y = dict(P); Y["b1"] = np.zeros_like(P["b1"]); Y["bs"] = np.zeros_like(P["bs"])
+    a, A = _run_mlp(np.zeros_like(q), Y, Hq, Hkv)
+    for hq in range(Hq):
+        np.testing.assert_allclose(A[:, hq], np.broadcast_to(P["b2"][hq // 2], (3, d)), atol=1e-15)
+        np.testing.assert_allclose(a[:, hq], P["bs2"][hq // 2], atol=1e-15)
+    # W1 = 0 -> hidden is GELU(b1) for every query: the target is constant over tokens
+    X = dict(P); X["W1"] = np.zeros_like(P["W1"]); X["Ws"] = np.zeros_like(P["Ws"])
+    a, A = _run_mlp(q, X, Hq, Hkv)
+    assert np.max(np.abs(A - A[:1])) < 1e-14 and np.max(np.abs(a - a[:1])) < 1e-14
+
+
+def test_p10_mlp_linear_in_output_layer():
+    # The read-out is linear in (W2, b2): doubling both doubles the target.
+    Hq, Hkv, d, Ht, Hs = 2, 1, 4, 6, 5
+    q = _rand(2, Hq, d)
+    P = {k: _rand(*v.shape) for k, v in _mlp_zero(Hkv, d, Ht, Hs).items()}
+    a, A = _run_mlp(q, P, Hq, Hkv)
+    P2 = dict(P); P2["W2t"] = 2 * P["W2t"]; P2["b2"] = 2 * P["b2"]
+    P2["ws2"] = 2 * P["ws2"]; P2["bs2"] = 2 * P["bs2"]
+    a2, A2 = _run_mlp(q, P2, Hq, Hkv)
+    np.testing.assert_allclose(A2, 2 * A, atol=1e-13)
+    np.testing.assert_allclose(a2, 2 * a, atol=1e-13)
+
+
+# --- storage types: bf16 / fp32 inputs widen exactly --------------------------
+
+def test_bf16_and_f32_inputs_widen_exactly():
+    from learned_kv_cache_02_amd import synth
+    R, Hq, Hkv, n, d = 2, 2, 1, 5, 8
+    x = [_rand(R, Hq, d), _rand(Hkv, n, d), _rand(Hkv, n, d)]
+    bits = [synth.to_bf16_bits(t) for t in x]
+    wide = [synth.bf16_bits_to_f32(b).astype(np.float64).reshape(t.shape) for b, t in zip(bits, x)]
+    a, A = oracle.doc_attn(*bits, dt="bf16", Hq=Hq, Hkv=Hkv)
+    a64, A64 = oracle.doc_attn(*wide, dt="f64", Hq=Hq, Hkv=Hkv)
+    np.testing.assert_array_equal(a, a64)
+    np.testing.assert_array_equal(A, A64)
+    f32 = [t.astype(np.float32) for t in x]
+    a, A = oracle.doc_attn(*f32, dt="f32", Hq=Hq, Hkv=Hkv)
+    a64, A64 = oracle.doc_attn(*[t.astype(np.float64) for t in f32], dt="f64", Hq=Hq, Hkv=Hkv)
+    np.testing.assert_array_equal(a, a64)
+
+
+def test_thread_count_does_not_change_results():
+    R, Hq, Hkv, n, d = 4, 4, 2, 33, 16
+    q, K, V = _rand(R, Hq, d), _rand(Hkv, n, d), _rand(Hkv, n, d)
+    a1, A1 = oracle.doc_attn(q, K, V, dt="f64", Hq=Hq, Hkv=Hkv, threads=1)
+    a4, A4 = oracle.doc_attn(q, K, V, dt="f64", Hq=Hq, Hkv=Hkv, threads=4)
+    np.testing.assert_array_equal(a1, a4)
+    np.testing.assert_array_equal(A1, A4)
+
+
+# --- capacity ratio against Table 9 (section 4.8) and section 2.5 ---------------
+
+def test_capacity_ratio_matches_table9():
+    g = json.load(open(os.path.join(GOLD, "table9_storage.json")))
+    for row in g["rows"]:
+        for rho, mb in row["module_mb"].items():
+            # module bytes = rho * doc KV bytes; the KV column is printed to 10 MB
+            # (half-unit 5 MB) and the module column to 1 MB (half-unit 0.5 MB).
+            assert abs(float(rho) * row["doc_kv_gb"] * 1000.0 - mb) <= float(rho) * 5.0 + 0.5 + 1e-9

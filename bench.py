@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the Nectar attention hot path on one MI355X.
+
+Workload: the Qwen3-4B-shaped decode layer (8 KV heads, 32 query heads, d=128,
+bf16; document n = 61,440 keys; local cache 512 prompt tokens + the decode
+token; Nectar MLP 128->4608->128 target and 128->2944->1 score per KV head,
+GELU).  A step is one decode step of one layer through the whole hot path:
+
+  exact document attention (alpha, A) over the 61,440-key cache,
+  the MLP module forward (a, A_theta),
+  causal local attention over the 513 local keys, merged with the module pair
+  (the Nectar output), and the merge of the exact pair with the local pair
+  (the exact output).
+
+Every step reads a distinct layer replica (its own document cache, module and
+local cache), so consecutive steps never hit a cache the previous step
+warmed; the replicas together exceed the 256 MB Infinity Cache many times.
+Inputs are resident in HBM before timing.  The launches of one pass over all
+replicas (one step per replica, like a decode step through a stack of that
+many layers) are captured once in a HIP graph and replayed; timing uses HIP
+events on the replay stream around K steps (K rounded up to whole passes),
+bracketed by synchronizations.
+
+Prints one JSON line.  `value` is query-tokens/s/layer of the whole step;
+`paths` gives the Nectar and exact paths timed alone; `roofline` covers the
+dominant kernel (exact document attention, HBM-bound); `cpu_baseline` times the
+fp64 CPU oracle on a bounded sample of the same step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+SOURCES_FOR_TRAFFIC = ["learned_kv_cache_02_amd/csrc/attn.hip", "learned_kv_cache_02_amd/csrc/device_common.hpp"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--replicas", type=int, default=24)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0: skip)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--only", choices=["step", "exact", "nectar", "doc"], default=None,
+                    help="time only one graph (for profiling runs)")
+    return ap.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in SOURCES_FOR_TRAFFIC:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from learned_kv_cache_02_amd import configs, nectar, synth
+
+    cfg = configs.C2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    NREP = args.replicas
+
+    def up(x):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
+
+    t0 = time.time()
+    q_h = synth.queries(cfg)
+    K_h, V_h = synth.doc_kv(cfg)
+    Kl_h, Vl_h = synth.local_kv(cfg)
+    P_h = synth.mlp_params(cfg)
+    gen_s = time.time() - t0
+    print("generated inputs in %.1fs" % gen_s, file=sys.stderr, flush=True)
+
+    q0, K0, V0, Kl0, Vl0 = up(q_h), up(K_h), up(V_h), up(Kl_h), up(Vl_h)
+    mod0 = [up(P_h[k]) for k in ("W1", "b1", "W2t", "b2", "Ws", "bs", "ws2", "bs2")]
+    reps = []
+    for r in range(NREP):
+        reps.append(dict(q=q0.clone(), K=K0.clone(), V=V0.clone(), Kl=Kl0.clone(), Vl=Vl0.clone(),
+                         mod=nectar.MLPModule(*(t.clone() for t in mod0))))
+    del K0, V0
+    torch.cuda.synchronize()
+
+    Hkv, Hq, d, R = cfg.Hkv, cfg.Hq, cfg.d, cfg.R
+    T, qoff = cfg.local_len(0), cfg.q_offset(0)
+    f32 = dict(dtype=torch.float32, device=dev)
+    o = dict(alpha=torch.empty((R, Hq), **f32), Ax=torch.empty((R, Hq, d), **f32),
+             a=torch.empty((R, Hq), **f32), Am=torch.empty((R, Hq, d), **f32),
+             lam=torch.empty((R, Hq), **f32), Al=torch.empty((R, Hq, d), **f32),
+             out_n=torch.empty((R, Hq, d), dtype=torch.bfloat16, device=dev), lse_n=torch.empty((R, Hq), **f32),
+             out_x=torch.empty((R, Hq, d), dtype=torch.bfloat16, device=dev), lse_x=torch.empty((R, Hq), **f32))
+
+    def doc(r):
+        x = reps[r]
+        nectar.doc_attn_exact(x["q"], x["K"], x["V"], Hkv, alpha_out=o["alpha"], A_out=o["Ax"])
+
+    def module(r):
+        x = reps[r]
+        nectar.module_forward(x["q"], x["mod"], Hkv, a_out=o["a"], A_out=o["Am"])
+
+    def local_nectar(r):
+        x = reps[r]
+        nectar.local_attn_lse(x["q"], x["Kl"], x["Vl"], Hkv, B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff,
+                              lse_out=o["lam"], A_out=o["Al"], doc_lse=o["a"], doc_A=o["Am"],
+                              out=o["out_n"], out_lse=o["lse_n"])
+
+    def local_pair(r):
+        x = reps[r]
+        nectar.local_attn_lse(x["q"], x["Kl"], x["Vl"], Hkv, B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff,
+                              lse_out=o["lam"], A_out=o["Al"])
+
+    def merge_exact(r):
+        nectar.merge(o["alpha"], o["Ax"], o["lam"], o["Al"], Hkv=Hkv, out_dtype=torch.bfloat16,
+                     out=o["out_x"], lse_out=o["lse_x"])
+
+    steps = {
+        "step": lambda r: (doc(r), module(r), local_nectar(r), merge_exact(r)),
+        "nectar": lambda r: (module(r), local_nectar(r)),
+        "exact": lambda r: (doc(r), local_pair(r), merge_exact(r)),
+        "doc": lambda r: doc(r),
+    }
+    names = [args.only] if args.only else ["step", "nectar", "exact", "doc"]
+
+    # warm every call once (allocates the binding's cached workspace outside capture)
+    for fn in steps.values():
+        fn(0)
+    torch.cuda.synchronize()
+
+    graphs = {}
+    if not args.no_graph:
+        for nm in names:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(NREP):
+                    steps[nm](r)
+            graphs[nm] = g
+        torch.cuda.synchronize()
+
+    passes = max(1, -(-args.steps // NREP))
+    wpasses = max(1, -(-args.warmup // NREP))
+    n_steps, n_warm = passes * NREP, wpasses * NREP
+
+    def one_pass(nm):
+        if args.no_graph:
+            for r in range(NREP):
+                steps[nm](r)
+        else:
+            graphs[nm].replay()
+
+    def timed(nm):
+        for _ in range(wpasses):
+            one_pass(nm)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(passes):
+            one_pass(nm)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_steps   # ms per step
+
+    ms = {nm: timed(nm) for nm in names}
+
+    # Correctness spot check of the timed outputs against the oracle is the job of
+    # the test suite; here only finite outputs are asserted.
+    for k in ("out_n", "out_x"):
+        if not torch.isfinite(o[k].float()).all():
+            raise RuntimeError("non-finite output in %s" % k)
+
+    layer_tokens = R * 1   # one layer per step
+    doc_bytes = Hkv * cfg.n * 2 * d * 2
+    mlp_bytes = Hkv * cfg.mlps[0].params(d) * 2
+    res = {
+        "metric": "query-tokens/s/layer, Nectar vs exact cache attn; % of HBM / MFMA roofline",
+        "unit": "query-tokens/s/layer",
+        "higher_is_better": True,
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": n_warm,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    if "step" in ms:
+        res["value"] = layer_tokens / (ms["step"] / 1e3)
+        res["ms_per_step"] = ms["step"]
+    res["config"] = {"workload": "%s: Hkv=8 Hq=32 d=128 bf16, n=61440 document keys, 513 local keys, "
+                                 "decode batch 1, MLP 4608/2944 GELU; one layer replica per step, %d replicas"
+                                 % (cfg.name, NREP),
+                     "global_batch": cfg.B, "seq_len": cfg.n + T, "parallelism": "single-gpu",
+                     "graph": not args.no_graph}
+    paths = {}
+    for nm in ("nectar", "exact"):
+        if nm in ms:
+            paths[nm] = {"qtok_s_layer": layer_tokens / (ms[nm] / 1e3), "us_per_layer": ms[nm] * 1e3}
+    if "nectar" in ms and "exact" in ms:
+        paths["nectar_speedup_vs_exact"] = ms["exact"] / ms["nectar"]
+        paths["module_rho"] = cfg.rho(cfg.mlps[0].params(d))
+    res["paths"] = paths
+    if "doc" in ms:
+        us = ms["doc"] * 1e3
+        ach = doc_bytes / (us * 1e-6) / 1e9
+        traffic = None
+        tf = os.path.join(ROOT, "profiles", "traffic_doc_attn_c2.json")
+        if os.path.exists(tf):
+            with open(tf) as fh:
+                tj = json.load(fh)
+            if tj.get("source_hash") == source_hash():
+                traffic = tj.get("hbm_bytes_per_launch")
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+                           "kernel": "nectar_doc_attn_exact (split-K partial + combine), %.1f us per launch, "
+                                     "%d algorithmic bytes per launch" % (us, doc_bytes)}
+        res["module_roofline_hint"] = {"bytes_per_launch": mlp_bytes}
+
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(cfg, q_h, K_h, V_h, Kl_h, Vl_h, P_h, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, q, K, V, Kl, Vl, P, budget_s):
+    """The fp64 oracle on the same step (both paths, one token), repeated until
+    the time budget is used; tokens per second per layer."""
+    import numpy as np
+
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    T = cfg.local_len(0)
+    Klv, Vlv = (np.ascontiguousarray(x[:, :, :T]) for x in (Kl, Vl))
+    kw = dict(dt="bf16", Hq=cfg.Hq, Hkv=cfg.Hkv, threads=threads)
+    n_tok = 0
+    t0 = time.time()
+    while True:
+        alpha, A = oracle.doc_attn(q, K, V, **kw)
+        a, Am = oracle.mlp(q, P["W1"], P["b1"], P["W2t"], P["b2"], P["Ws"], P["bs"], P["ws2"], P["bs2"], **kw)
+        lam, Al = oracle.local_attn(q, Klv, Vlv, B=cfg.B, Tq=cfg.Tq, Tloc=T, q_offset=cfg.q_offset(0), **kw)
+        oracle.merge(a, Am, lam, Al)
+        oracle.merge(alpha, A, lam, Al)
+        n_tok += cfg.R
+        el = time.time() - t0
+        if el >= budget_s:
+            break
+    return {"value": n_tok / el, "unit": "query-tokens/s/layer", "cores": threads, "kind": "oracle",
+            "sample": "%d decode steps of the same layer (exact + Nectar paths, 1 query token x 32 heads "
+                      "each) in %.1f s" % (n_tok, el)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * nectar.h -- C ABI of the MI355X (gfx950) Nectar attention hot path.
+ *
+ * Nectar ("Nectar: Neural Estimation of Cached-Token Attention via
+ * Regression"; reading notes at cc.laoqi.cc/papers/2605.09778/v2/r1) replaces,
+ * per layer and KV head, softmax attention over a fixed document's cached keys
+ * and values by two small networks of the RoPE'd query: a score net a(q) for
+ * the document log-normalizer and a target net A(q) for the document-normalized
+ * read-out.  Their pair is merged by log-sum-exp with exact causal attention
+ * over the question's own tokens.  This library computes, on one GPU:
+ *
+ *   nectar_doc_attn_exact   exact (alpha, A) over the document cache, Eq. (3.1)
+ *   nectar_module_forward   (a, A) from the MLP form (Eq. (3.6), one hidden
+ *                           layer) or the Quadrature KV-pair form (section 2.4)
+ *   nectar_local_attn_lse   causal local attention (log Z_local, A_local),
+ *                           section 2.2, optionally merged with a document pair
+ *   nectar_merge            the log-sum-exp merge of Eqs. (3.4)-(3.5)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are caller-owned DEVICE memory, contiguous, row-major
+ *   (innermost index last), 16-byte aligned.  The library never allocates,
+ *   frees or synchronizes; every call is asynchronous on `stream` (a
+ *   hipStream_t; NULL = the null stream).  Outputs are complete when later work
+ *   on that stream runs.  No global mutable state: calls are thread-safe;
+ *   concurrent calls must use distinct workspaces.
+ * - Query layout q[R][Hq][d] (token-major).  Query head h' reads KV head
+ *   h = h' / (Hq / Hkv) (contiguous GQA groups; the group's query heads share
+ *   K, V and the module, section 2.1).  Per-query outputs are [R][Hq] (scalars)
+ *   and [R][Hq][d] (vectors).
+ * - Element type of q, caches and module weights is desc->dtype (fp32 or bf16);
+ *   biases are fp32; log-normalizers and read-outs are returned in fp32
+ *   (section 3.2 of the notes caches its regression targets in fp32).
+ *   Log-normalizers use the natural logarithm.
+ * - Scores are s_j = scale * q.k_j with scale = desc->scale, or 1/sqrt(d) when
+ *   desc->scale == 0 (Eq. (3.1)).
+ * - Errors: every argument is checked on the host before any HIP call; a non-OK
+ *   status is returned synchronously and nothing is launched.  NECTAR_EHIP
+ *   reports a launch failure (hipGetLastError); faults inside kernels surface at
+ *   the caller's next synchronization.  With NECTAR_SYNC_CHECK=1 in the
+ *   environment each call synchronizes its stream and reports such faults as
+ *   NECTAR_EHIP.  Outputs are undefined after a non-OK return.  NaN/Inf inputs
+ *   are propagated, not checked.
+ * - Workspaces: the *_workspace_size functions return the exact number of
+ *   bytes (0 allowed) the matching call needs for the same arguments; they
+ *   need no GPU.  The workspace is scratch owned by the caller; its contents
+ *   need no initialisation and are undefined afterwards.
+ */
+#ifndef NECTAR_H
+#define NECTAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NECTAR_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define NECTAR_API __attribute__((visibility("default")))
+#else
+#define NECTAR_API
+#endif
+
+typedef enum {
+    NECTAR_OK = 0,
+    NECTAR_EINVAL = 1,        /* null pointer, bad shape, misalignment, bad enum */
+    NECTAR_EUNSUPPORTED = 2,  /* well-formed but not implemented (d not 64/128, ...) */
+    NECTAR_EWORKSPACE = 3,    /* ws_bytes smaller than the size query returns */
+    NECTAR_EHIP = 4           /* HIP launch (or, with NECTAR_SYNC_CHECK, execution) error */
+} nectar_status;
+
+typedef enum { NECTAR_F32 = 0, NECTAR_BF16 = 1 } nectar_dtype;
+
+/* Shape of the query side of one call. */
+typedef struct {
+    int32_t R;       /* query tokens (rows of q); R == 0 is a valid no-op */
+    int32_t Hq;      /* query heads, > 0 */
+    int32_t Hkv;     /* KV heads, > 0, Hq % Hkv == 0 */
+    int32_t d;       /* head dimension: 64 or 128 */
+    int32_t dtype;   /* nectar_dtype of q, caches and module weights */
+    float scale;     /* score scale; 0 selects 1/sqrt(d) */
+    int32_t splits;  /* 0: automatic; > 0: requested number of key (or hidden)
+                        splits per head, clamped to [1, #32-wide tiles].  Results
+                        agree across split counts up to fp32 rounding. */
+} nectar_attn_desc;
+
+/* The local (question + generated tokens) cache of nectar_local_attn_lse. */
+typedef struct {
+    int32_t B;         /* questions; R == B * Tq */
+    int32_t Tq;        /* query tokens per question in this call */
+    int32_t T_loc;     /* valid local keys per (question, KV head), >= 0 */
+    int32_t T_cap;     /* allocated rows per (question, KV head), >= T_loc */
+    int32_t q_offset;  /* query token t of a question sees local keys
+                          0 .. min(q_offset + t, T_loc - 1) (section 2.2: the
+                          same causal set i <= t as full attention, including
+                          the token itself).  Decode: Tq = 1, q_offset = T_loc - 1.
+                          Prefill of the whole local chunk: Tq = T_loc, 0. */
+} nectar_local_desc;
+
+typedef enum { NECTAR_MODULE_MLP = 0, NECTAR_MODULE_KVPAIR = 1 } nectar_module_kind;
+typedef enum { NECTAR_ACT_GELU = 0, NECTAR_ACT_SILU = 1 } nectar_act;
+
+/*
+ * A Nectar module for one layer: per KV head h (section 2.4 of the notes).
+ *
+ * MLP (Eq. (3.6) with one hidden layer, the workloads' depth):
+ *   target  A(q) = sum_j W2t[h][j][:] * act(W1[h][j] . q + b1[h][j]) + b2[h]
+ *   score   a(q) = sum_j ws2[h][j]   * act(Ws[h][j] . q + bs[h][j]) + bs2[h]
+ *   W1, W2t [Hkv][Ht][d] (W2t[h][j] holds hidden unit j's outgoing weights),
+ *   Ws [Hkv][Hs][d], ws2 [Hkv][Hs] (dtype); b1 [Hkv][Ht], b2 [Hkv][d],
+ *   bs [Hkv][Hs], bs2 [Hkv] (fp32).  act: GELU(x) = x * Phi(x) (erf form) or
+ *   SiLU(x) = x * sigmoid(x).  Ht, Hs >= 0 (any value; 0 leaves the bias).
+ * KVPAIR (Quadrature): exact attention over p learnable pairs,
+ *   a(q) = log sum_j exp(scale * W[h][j] . q),  A(q) = softmax(scale * W q)^T Z,
+ *   W, Z [Hkv][p][d] (dtype), p >= 0 (p == 0 gives a = -inf, A = 0).
+ */
+typedef struct {
+    int32_t kind;      /* nectar_module_kind */
+    int32_t act;       /* nectar_act (MLP only) */
+    int32_t Ht, Hs;    /* MLP hidden widths */
+    const void *W1;  const float *b1;
+    const void *W2t; const float *b2;
+    const void *Ws;  const float *bs;
+    const void *ws2; const float *bs2;
+    int64_t p;         /* KVPAIR pair count */
+    const void *W;   const void *Z;
+} nectar_module;
+
+/*
+ * Exact document attention, Eq. (3.1) with GQA sharing (section 2.1):
+ *   alpha_out[r][h'] = log sum_{j<n} exp(s_j),  A_out[r][h'][:] = sum_j e^{s_j} v_j / sum_j e^{s_j}
+ * over the document cache k, v [Hkv][n][d] (keys already RoPE'd).  Split-K over
+ * the keys with a log-sum-exp combine (the regrouping of Eq. (3.4)); n == 0
+ * gives alpha = -inf and A = 0.  The same call produces the fp32 regression
+ * targets of section 2.3.
+ */
+NECTAR_API size_t nectar_doc_attn_workspace_size(const nectar_attn_desc *desc, int64_t n);
+NECTAR_API nectar_status nectar_doc_attn_exact(const nectar_attn_desc *desc, int64_t n,
+                                    const void *q, const void *k, const void *v,
+                                    float *alpha_out, float *A_out,
+                                    void *ws, size_t ws_bytes, void *stream);
+
+/* Module forward: (a_out [R][Hq], A_out [R][Hq][d]) for every query row. */
+NECTAR_API size_t nectar_module_workspace_size(const nectar_attn_desc *desc, const nectar_module *m);
+NECTAR_API nectar_status nectar_module_forward(const nectar_attn_desc *desc, const nectar_module *m,
+                                    const void *q, float *a_out, float *A_out,
+                                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Causal local attention (section 2.2): for query row r = b * Tq + t and query
+ * head h', lse = log Z_local and A_local = N_local / Z_local over the visible
+ * keys of k_loc, v_loc [B][Hkv][T_cap][d]; no visible key gives lse = -inf and
+ * A_local = 0.
+ * Outputs (each group optional, at least one requested):
+ *   lse_out [R][Hq], A_out [R][Hq][d] (fp32): the local pair;
+ *   out [R][Hq][d] (dtype) and out_lse [R][Hq] (fp32, may be NULL when out is
+ *   given): the merge (Eqs. (3.4)-(3.5)) of the local part with the document
+ *   pair doc_lse [R][Hq], doc_A [R][Hq][d] (fp32) -- exact (alpha, A) or a
+ *   module's (a, A), the "virtual logit".  doc_lse/doc_A are required iff out
+ *   or out_lse is given.
+ */
+NECTAR_API size_t nectar_local_workspace_size(const nectar_attn_desc *desc, const nectar_local_desc *loc);
+NECTAR_API nectar_status nectar_local_attn_lse(const nectar_attn_desc *desc, const nectar_local_desc *loc,
+                                    const void *q, const void *k_loc, const void *v_loc,
+                                    float *lse_out, float *A_out,
+                                    const float *doc_lse, const float *doc_A,
+                                    void *out, float *out_lse,
+                                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Log-sum-exp merge, Eqs. (3.4)-(3.5): per row (R * Hq rows),
+ *   M = max(a, lam);  out = (e^{a-M} A + e^{lam-M} A_loc) / (e^{a-M} + e^{lam-M});
+ *   lse_out = M + log(e^{a-M} + e^{lam-M});   a = lam = -inf gives out = 0, lse = -inf.
+ * a, lam: [R][Hq] fp32; A, A_loc: [R][Hq][d] fp32; out [R][Hq][d] in desc->dtype;
+ * lse_out nullable.
+ */
+NECTAR_API nectar_status nectar_merge(const nectar_attn_desc *desc, const float *a, const float *A,
+                           const float *lam, const float *A_loc, void *out, float *lse_out,
+                           void *stream);
+
+NECTAR_API const char *nectar_status_string(nectar_status s);
+NECTAR_API int nectar_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NECTAR_H */

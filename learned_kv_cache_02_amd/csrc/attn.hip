@@ -1,0 +1,518 @@
+// Split-K softmax attention with log-sum-exp partials, its combine, and the
+// log-sum-exp merge: the exact document path (Eq. (3.1) of the Nectar notes),
+// the Quadrature module (exact attention over p pairs) and the causal local
+// part (section 2.2), all as one kernel family.
+//
+// bf16 path (attn_partial_mfma): every wave owns RT tiles of 16 query rows and
+// one contiguous key range, and streams 32-key tiles of K and V straight from
+// HBM into registers (no LDS):
+//   S^T (32 keys x 16 rows) = K_tile . Q^T   -- K rows are MFMA A operands as
+//       loaded: lane (g, c) holds 16 bytes of key c, so four consecutive lanes'
+//       loads cover 64 contiguous bytes of one key row;
+//   online max/sum per row in fp32, P = exp2(S * scale * log2e - m) -> bf16;
+//   O^T (d x 16 rows) += V_tile^T . P^T -- lane (g, c) loads dims 8c..8c+7 of
+//       the eight keys its P slots hold (one 256-byte key row per 16 lanes) and
+//       transposes the 8x8 bf16 block inside its own registers, so each wave
+//       load instruction reads four whole key rows.
+// The S^T layout puts one query row per lane column, so every row statistic
+// (max, sum, rescale) stays in the lane; only the tile max crosses the four
+// 16-lane groups.  Tiles are double-buffered in registers so the next tile's
+// 16 KB is in flight while the current one is computed.
+//
+// A block's four waves cover WR row groups x WS key splits; the WS splits of a
+// row group are folded in LDS (log-sum-exp rescale, then a sum), so each block
+// leaves one partial per row.  When one block spans the whole key range the
+// block finishes the rows itself (lse, read-out, optional merge); otherwise
+// attn_combine folds the per-block partials.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace nectar {
+
+template <int D> struct VRow;
+template <> struct VRow<128> { typedef u32x4 T; };   // 8 bf16 per lane per key
+template <> struct VRow<64> { typedef u32x2 T; };    // 4 bf16 per lane per key
+
+template <int D> struct KVTile {
+    static constexpr int KS = D / 32;
+    u32x4 k[2][KS];
+    typename VRow<D>::T v[8];
+};
+
+// Key held by P slot j of lane group g within a 32-key tile.
+__device__ __forceinline__ int slot_key(int g, int j) { return 16 * (j >> 2) + 4 * g + (j & 3); }
+
+template <int D>
+__device__ __forceinline__ void load_kv_tile(KVTile<D> &T, const uint16_t *kb, const uint16_t *vb,
+                                             int k0, int kmax, int g, int c) {
+    constexpr int KS = D / 32, DV = D / 16;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int key = min(k0 + 16 * hh + c, kmax);
+        const uint16_t *kp = kb + (size_t)key * D;
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) T.k[hh][kt] = *(const u32x4 *)(kp + (4 * kt + g) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int key = min(k0 + slot_key(g, j), kmax);
+        T.v[j] = *(const typename VRow<D>::T *)(vb + (size_t)key * D + c * DV);
+    }
+}
+
+// vt[mm] slot j = V[key(g, j)][c * DV + mm]: in-lane 8 x DV transpose of bf16.
+template <int D>
+__device__ __forceinline__ void transpose_v(const KVTile<D> &T, u32x4 (&vt)[D / 16]) {
+    constexpr int DV = D / 16;
+#pragma unroll
+    for (int mm = 0; mm < DV; ++mm) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t a0 = T.v[2 * w][mm >> 1], a1 = T.v[2 * w + 1][mm >> 1];
+            vt[mm][w] = (mm & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+        }
+    }
+}
+
+template <int D, int RT>
+__device__ __forceinline__ void attend_tile(const KVTile<D> &T, int k0, const u32x4 (&qv)[RT][D / 32],
+                                            const int (&lim)[RT], float sl2, int g,
+                                            f32x4 (&O)[RT][D / 16], float (&m)[RT], float (&l)[RT]) {
+    constexpr int KS = D / 32, DV = D / 16;
+    u32x4 vt[DV];
+    transpose_v<D>(T, vt);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) {
+            s0 = mfma16(T.k[0][kt], qv[rt][kt], s0);
+            s1 = mfma16(T.k[1][kt], qv[rt][kt], s1);
+        }
+        float sv[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { sv[r] = s0[r] * sl2; sv[4 + r] = s1[r] * sl2; }
+        if (k0 + 32 > lim[rt]) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (k0 + slot_key(g, j) >= lim[rt]) sv[j] = -INFINITY;
+        }
+        float mt = sv[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
+        mt = group4_max(mt);
+        const float mnew = fmaxf(m[rt], mt);
+        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = fast_exp2(m[rt] - muse);
+        float pv[8], ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { pv[j] = fast_exp2(sv[j] - muse); ps += pv[j]; }
+        l[rt] = l[rt] * alpha + ps;
+        m[rt] = mnew;
+        const u32x4 P = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                         pack_bf16(pv[6], pv[7])};
+#pragma unroll
+        for (int mm = 0; mm < DV; ++mm) {
+            O[rt][mm] *= alpha;
+            O[rt][mm] = mfma16(vt[mm], P, O[rt][mm]);
+        }
+    }
+}
+
+// Output row index of row rho of problem p.
+__device__ __forceinline__ size_t out_row(int p, int rho, int Hkv, int G, int Tq, int Hq) {
+    const int b = p / Hkv, h = p - b * Hkv;
+    const int t = rho / G, gg = rho - t * G;
+    return (size_t)(b * Tq + t) * Hq + h * G + gg;
+}
+
+// Finish one row held in lane layout: lane (g, c) owns dims DV*(4g+r)+mm of the
+// row; m (log2 units) and l are the row's folded statistics.
+template <int D, typename OutT>
+__device__ __forceinline__ void finish_row_lanes(const AttnParams &a, size_t o, int g, float m, float l,
+                                                 const f32x4 (&O)[D / 16]) {
+    constexpr int DV = D / 16;
+    const bool empty = (m == -INFINITY);
+    const float inv = empty ? 0.f : 1.0f / l;
+    if (a.lse_out && g == 0) a.lse_out[o] = empty ? -INFINITY : (m + log2f(l)) * kLn2;
+    if (a.A_out) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int m4 = 0; m4 < DV; m4 += 4) {
+                f32x4 v = {O[m4][r] * inv, O[m4 + 1][r] * inv, O[m4 + 2][r] * inv, O[m4 + 3][r] * inv};
+                *(f32x4 *)(a.A_out + o * D + DV * (4 * g + r) + m4) = v;
+            }
+    }
+    if (a.x_lse) {
+        const float mx = a.x_lse[o] * kLog2e;
+        const float Mt = fmaxf(m, mx);
+        const bool none = (Mt == -INFINITY);
+        const float wl = (none || empty) ? 0.f : exp2f(m - Mt);
+        const float wx = none ? 0.f : exp2f(mx - Mt);
+        const float Lt = wl * l + wx;
+        const float it = none ? 0.f : 1.0f / Lt;
+        if (a.out_lse && g == 0) a.out_lse[o] = none ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
+        if (a.out) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float ov[DV];
+                const float *xa = a.x_A + o * D + DV * (4 * g + r);
+#pragma unroll
+                for (int mm = 0; mm < DV; ++mm) ov[mm] = none ? 0.f : (wl * O[mm][r] + wx * xa[mm]) * it;
+#pragma unroll
+                for (int mm = 0; mm < DV; ++mm) st_out<OutT>((OutT *)a.out, o * D + DV * (4 * g + r) + mm, ov[mm]);
+            }
+        }
+    }
+}
+
+template <int D, int RT, typename OutT>
+__global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams a) {
+    constexpr int KS = D / 32, DV = D / 16;
+    // Fold buffers (used when WS > 1, hence WR <= 2): per row group one f32x4
+    // per (register, lane), lane-major so each wave access is conflict-free.
+    __shared__ f32x4 fold_O[2][RT * DV][64];
+    __shared__ float fold_l[2][RT][64];
+    __shared__ float fold_m[4][RT][16];
+
+    const int w = threadIdx.x >> 6;
+    const int wr = w % a.WR, ws = w / a.WR;
+    int blk = blockIdx.x;
+    const int sb = blk % a.SB;
+    blk /= a.SB;
+    const int rb = blk % a.RB;
+    const int p = blk / a.RB;
+    const int rg = rb * a.WR + wr;
+    const int s = sb * a.WS + ws;
+    const int b = p / a.Hkv, h = p - b * a.Hkv;
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    const uint16_t *kb = (const uint16_t *)a.k + b * a.kv_bstride + h * a.kv_hstride;
+    const uint16_t *vb = (const uint16_t *)a.v + b * a.kv_bstride + h * a.kv_hstride;
+
+    u32x4 qv[RT][KS];
+    int lim[RT];
+    int wlim = 0;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int rho = (rg * RT + rt) * 16 + c;
+        if (rg < a.RG && rho < a.Rp) {
+            const int t = rho / a.G, gg = rho - t * a.G;
+            const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(b * a.Tq + t) * a.Hq + h * a.G + gg) * D;
+#pragma unroll
+            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
+            int L = a.T_kv;
+            if (a.causal) L = min(L, a.q_offset + t + 1);
+            lim[rt] = max(L, 0);
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
+            lim[rt] = 0;
+        }
+        wlim = max(wlim, lim[rt]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) wlim = max(wlim, __shfl_xor(wlim, o, 64));
+
+    f32x4 O[RT][DV];
+    float m[RT], l[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        m[rt] = -INFINITY;
+        l[rt] = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < DV; ++mm) O[rt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int k_lo = s * a.chunk;
+    const int k_hi = min(k_lo + a.chunk, wlim);
+    if (k_lo < k_hi) {
+        const int kmax = a.T_kv - 1;
+        KVTile<D> t0, t1;
+        load_kv_tile<D>(t0, kb, vb, k_lo, kmax, g, c);
+        for (int k0 = k_lo; k0 < k_hi; k0 += 64) {
+            const bool has1 = k0 + 32 < k_hi;
+            if (has1) load_kv_tile<D>(t1, kb, vb, k0 + 32, kmax, g, c);
+            attend_tile<D, RT>(t0, k0, qv, lim, a.sl2, g, O, m, l);
+            if (!has1) break;
+            if (k0 + 64 < k_hi) load_kv_tile<D>(t0, kb, vb, k0 + 64, kmax, g, c);
+            attend_tile<D, RT>(t1, k0 + 32, qv, lim, a.sl2, g, O, m, l);
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) l[rt] = group4_sum(l[rt]);
+
+    if (a.WS > 1) {
+        // Fold the WS splits of this row group: common max, rescale, sum.
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            if (g == 0) fold_m[w][rt][c] = m[rt];
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float M = -INFINITY;
+            for (int k = 0; k < a.WS; ++k) M = fmaxf(M, fold_m[k * a.WR + wr][rt][c]);
+            const float sc = (m[rt] == -INFINITY) ? 0.f : exp2f(m[rt] - M);
+            l[rt] *= sc;
+#pragma unroll
+            for (int mm = 0; mm < DV; ++mm) O[rt][mm] *= sc;
+            m[rt] = M;
+        }
+        for (int k = a.WS - 1; k >= 1; --k) {
+            if (ws == k) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    fold_l[wr][rt][lane] = (k == a.WS - 1) ? l[rt] : fold_l[wr][rt][lane] + l[rt];
+#pragma unroll
+                    for (int mm = 0; mm < DV; ++mm)
+                        fold_O[wr][rt * DV + mm][lane] =
+                            (k == a.WS - 1) ? O[rt][mm] : fold_O[wr][rt * DV + mm][lane] + O[rt][mm];
+                }
+            }
+            __syncthreads();
+        }
+        if (ws != 0) return;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            l[rt] += fold_l[wr][rt][lane];
+#pragma unroll
+            for (int mm = 0; mm < DV; ++mm) O[rt][mm] += fold_O[wr][rt * DV + mm][lane];
+        }
+    }
+    if (rg >= a.RG) return;
+
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int rho = (rg * RT + rt) * 16 + c;
+        if (rho >= a.Rp) continue;
+        if (a.SB == 1) {
+            finish_row_lanes<D, OutT>(a, out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq), g, m[rt], l[rt], O[rt]);
+        } else {
+            const size_t row = (size_t)(p * a.SB + sb) * a.Rp + rho;
+            if (g == 0) a.part_ml[row] = make_float2(m[rt], l[rt]);
+            float *op = a.part_O + row * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int m4 = 0; m4 < DV; m4 += 4) {
+                    f32x4 v = {O[rt][m4][r], O[rt][m4 + 1][r], O[rt][m4 + 2][r], O[rt][m4 + 3][r]};
+                    *(f32x4 *)(op + DV * (4 * g + r) + m4) = v;
+                }
+        }
+    }
+}
+
+// fp32 path: one wave per (problem, row, split); lanes own head dimensions,
+// keys are visited in order with a wave-wide dot product.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void attn_partial_valu(AttnParams a) {
+    constexpr int NPL = D / 64;
+    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wave >= a.P * a.S * a.Rp) return;
+    const int s = wave % a.S;
+    const int rho = (wave / a.S) % a.Rp;
+    const int p = wave / (a.S * a.Rp);
+    const int b = p / a.Hkv, h = p - b * a.Hkv;
+    const int lane = threadIdx.x & 63;
+    const int t = rho / a.G, gg = rho - t * a.G;
+    const T *qp = (const T *)a.q + ((size_t)(b * a.Tq + t) * a.Hq + h * a.G + gg) * D;
+    const T *kb = (const T *)a.k + b * a.kv_bstride + h * a.kv_hstride;
+    const T *vb = (const T *)a.v + b * a.kv_bstride + h * a.kv_hstride;
+    float qf[NPL], acc[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) { qf[i] = Elem<T>::ld(qp, lane + 64 * i); acc[i] = 0.f; }
+    int L = a.T_kv;
+    if (a.causal) L = min(L, a.q_offset + t + 1);
+    const int k_lo = s * a.chunk, k_hi = min(k_lo + a.chunk, L);
+    float m = -INFINITY, l = 0.f;
+    for (int j = k_lo; j < k_hi; ++j) {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) part += qf[i] * Elem<T>::ld(kb, (size_t)j * D + lane + 64 * i);
+        const float s2 = wave_sum(part) * a.sl2;
+        const float mnew = fmaxf(m, s2);
+        const float alpha = exp2f(m - mnew);
+        const float pj = exp2f(s2 - mnew);
+        l = l * alpha + pj;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) acc[i] = acc[i] * alpha + pj * Elem<T>::ld(vb, (size_t)j * D + lane + 64 * i);
+        m = mnew;
+    }
+    const size_t row = (size_t)(p * a.S + s) * a.Rp + rho;
+    if (lane == 0) a.part_ml[row] = make_float2(m, l);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) a.part_O[row * D + lane + 64 * i] = acc[i];
+}
+
+// One block per (problem, row): log-sum-exp fold of the S partials, fixed
+// order, then the optional merge with an extra (lse, A) pair (Eq. (3.5)).
+// Thread (sg, dq) owns 4 dims of the splits sg, sg + NSG, ...; it issues every
+// load it needs (statistics, read-outs, the extra pair) before the first
+// reduction, so the block pays one memory round trip.
+template <int D, typename OutT, int MAXI>
+__global__ __launch_bounds__(256) void attn_combine(CombineParams a) {
+    constexpr int DQ = D / 4;            // float4 columns
+    constexpr int NSG = 256 / DQ;        // split groups
+    __shared__ float red[256];
+    __shared__ f32x4 accs[NSG][DQ];
+    const int idx = blockIdx.x;
+    const int p = idx / a.Rp, rho = idx - p * a.Rp;
+    const int tid = threadIdx.x;
+    const size_t o = out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq);
+    const float2 *ml = a.part_ml + (size_t)p * a.S * a.Rp + rho;   // stride Rp over splits
+    const float *po = a.part_O + ((size_t)p * a.S * a.Rp + rho) * D;
+    const int sg = tid / DQ, dq = tid - sg * DQ;
+
+    float2 st[MAXI];
+    f32x4 ov[MAXI];
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        const int s = sg + i * NSG;
+        if (s < a.S) {
+            st[i] = ml[(size_t)s * a.Rp];
+            ov[i] = *(const f32x4 *)(po + (size_t)s * a.Rp * D + 4 * dq);
+        } else {
+            st[i] = make_float2(-INFINITY, 0.f);
+            ov[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    float mx = -INFINITY;
+    f32x4 xa = {0.f, 0.f, 0.f, 0.f};
+    if (a.x_lse) {
+        mx = a.x_lse[o] * kLog2e;
+        if (a.out && tid < DQ) xa = *(const f32x4 *)(a.x_A + o * D + 4 * tid);
+    }
+    // splits beyond MAXI * NSG (very long split lists) are folded serially
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) mloc = fmaxf(mloc, st[i].x);
+    for (int s = sg + MAXI * NSG; s < a.S; s += NSG) mloc = fmaxf(mloc, ml[(size_t)s * a.Rp].x);
+    red[tid] = mloc;
+    __syncthreads();
+    for (int k = 128; k > 0; k >>= 1) {
+        if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
+        __syncthreads();
+    }
+    const float M = red[0];
+    __syncthreads();
+    const bool empty = (M == -INFINITY);
+    float lloc = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (!empty) {
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            const float w = exp2f(st[i].x - M);
+            lloc += w * st[i].y;
+            acc += w * ov[i];
+        }
+        for (int s = sg + MAXI * NSG; s < a.S; s += NSG) {
+            const float2 v = ml[(size_t)s * a.Rp];
+            const float w = exp2f(v.x - M);
+            lloc += w * v.y;
+            acc += w * *(const f32x4 *)(po + (size_t)s * a.Rp * D + 4 * dq);
+        }
+    }
+    // every split's l is counted once: only the dq == 0 thread of a group adds it
+    red[tid] = (dq == 0) ? lloc : 0.f;
+    accs[sg][dq] = acc;
+    __syncthreads();
+    for (int k = 128; k > 0; k >>= 1) {
+        if (tid < k) red[tid] += red[tid + k];
+        __syncthreads();
+    }
+    if (tid >= DQ) return;
+    const float L = red[0];
+    f32x4 O = accs[0][tid];
+    for (int k = 1; k < NSG; ++k) O += accs[k][tid];
+
+    const float inv = empty ? 0.f : 1.0f / L;
+    if (a.lse_out && tid == 0) a.lse_out[o] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+    if (a.A_out) *(f32x4 *)(a.A_out + o * D + 4 * tid) = O * inv;
+    if (a.x_lse) {
+        const float Mt = fmaxf(M, mx);
+        const bool none = (Mt == -INFINITY);
+        const float wl = (none || empty) ? 0.f : exp2f(M - Mt);
+        const float wx = none ? 0.f : exp2f(mx - Mt);
+        const float Lt = wl * L + wx;
+        const float it = none ? 0.f : 1.0f / Lt;
+        if (a.out_lse && tid == 0) a.out_lse[o] = none ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
+        if (a.out) {
+            const f32x4 r = (wl * O + wx * xa) * it;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st_out<OutT>((OutT *)a.out, o * D + 4 * tid + i, none ? 0.f : r[i]);
+        }
+    }
+}
+
+// Standalone merge of two (lse, A) pairs, one wave per row.
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void merge_pairs(MergeParams a) {
+    constexpr int NPL = D / 64;
+    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= a.rows) return;
+    const int lane = threadIdx.x & 63;
+    const float x = a.a[r], y = a.lam[r];
+    float va[NPL], vl[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const size_t e = (size_t)r * D + lane + 64 * i;
+        va[i] = a.A[e];
+        vl[i] = a.A_loc[e];
+    }
+    const float M = fmaxf(x, y);
+    if (M == -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) st_out<OutT>((OutT *)a.out, r * D + lane + 64 * i, 0.f);
+        if (a.lse_out && lane == 0) a.lse_out[r] = -INFINITY;
+        return;
+    }
+    const float wa = expf(x - M), wl = expf(y - M), den = wa + wl;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+        st_out<OutT>((OutT *)a.out, (size_t)r * D + lane + 64 * i, (wa * va[i] + wl * vl[i]) / den);
+    if (a.lse_out && lane == 0) a.lse_out[r] = M + logf(den);
+}
+
+int row_tiles_for(int Rp) { return Rp <= 16 ? 1 : 2; }
+
+static inline unsigned blocks_for_waves(long waves) { return (unsigned)((waves + 3) / 4); }
+
+hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hipStream_t st) {
+    if (dtype == 1) {
+        dim3 grid((unsigned)((long)p.P * p.RB * p.SB)), block(256);
+#define NECTAR_ATTN_CASE(DD, RR) \
+        if (d == DD && rt == RR) { hipLaunchKernelGGL((attn_partial_mfma<DD, RR, uint16_t>), grid, block, 0, st, p); return hipGetLastError(); }
+        NECTAR_ATTN_CASE(128, 1) NECTAR_ATTN_CASE(128, 2)
+        NECTAR_ATTN_CASE(64, 1) NECTAR_ATTN_CASE(64, 2)
+#undef NECTAR_ATTN_CASE
+        return hipErrorInvalidValue;
+    }
+    const long waves = (long)p.P * p.S * p.Rp;
+    dim3 grid(blocks_for_waves(waves)), block(256);
+    if (d == 128) hipLaunchKernelGGL((attn_partial_valu<128, float>), grid, block, 0, st, p);
+    else if (d == 64) hipLaunchKernelGGL((attn_partial_valu<64, float>), grid, block, 0, st, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st) {
+    dim3 grid((unsigned)((long)p.P * p.Rp)), block(256);
+    if (d == 128 && dtype == 1) hipLaunchKernelGGL((attn_combine<128, uint16_t, 8>), grid, block, 0, st, p);
+    else if (d == 128) hipLaunchKernelGGL((attn_combine<128, float, 8>), grid, block, 0, st, p);
+    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((attn_combine<64, uint16_t, 4>), grid, block, 0, st, p);
+    else if (d == 64) hipLaunchKernelGGL((attn_combine<64, float, 4>), grid, block, 0, st, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st) {
+    dim3 grid(blocks_for_waves(p.rows)), block(256);
+    if (d == 128 && dtype == 1) hipLaunchKernelGGL((merge_pairs<128, uint16_t>), grid, block, 0, st, p);
+    else if (d == 128) hipLaunchKernelGGL((merge_pairs<128, float>), grid, block, 0, st, p);
+    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((merge_pairs<64, uint16_t>), grid, block, 0, st, p);
+    else if (d == 64) hipLaunchKernelGGL((merge_pairs<64, float>), grid, block, 0, st, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace nectar

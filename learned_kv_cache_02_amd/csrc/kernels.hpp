@@ -1,0 +1,78 @@
+// Internal launch interface between the C ABI (nectar_abi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nectar {
+
+// One batched attention problem set: problem p = b * Hkv + h attends query rows
+// rho = t * G + g (query token b * Tq + t, query head h * G + g) over the keys
+// 0 .. T_kv - 1 of the cache at k/v + b * kv_bstride + h * kv_hstride (elements,
+// rows of d).  With causal != 0 row t only sees keys < q_offset + t + 1.
+struct AttnParams {
+    const void *q, *k, *v;
+    int64_t kv_bstride, kv_hstride;
+    int Hq, G, Hkv, Tq, B, Rp, T_kv, causal, q_offset;
+    float sl2;           // score scale * log2(e)
+    // split plan: S key splits of `chunk` keys; RG row groups of 16*RT rows.
+    // MFMA path: a block of 4 waves covers WR row groups x WS splits and folds
+    // its WS splits together, leaving SB = ceil(S / WS) partials per row;
+    // RB = ceil(RG / WR).  fp32 path: one wave per (row, split), SB = S.
+    int P, S, chunk, RG, WR, WS, RB, SB;
+    float *part_O;       // [P][SB][Rp][d]    unnormalised read-out
+    float2 *part_ml;     // [P][SB][Rp]       (running max in log2 units, sum)
+    // Finishing in place when SB == 1 (same meaning as in CombineParams).
+    float *lse_out, *A_out;
+    const float *x_lse, *x_A;
+    void *out;
+    float *out_lse;
+};
+
+// Finishing pass over the split partials of AttnParams: writes the pair
+// (lse, A) and/or its merge with an extra (lse_x, A_x) pair.
+struct CombineParams {
+    const float *part_O;
+    const float2 *part_ml;
+    int Hq, G, Hkv, Tq, P, S, Rp;
+    float *lse_out, *A_out;              // nullable
+    const float *x_lse, *x_A;            // nullable (extra pair)
+    void *out;                           // nullable, typed by dtype
+    float *out_lse;                      // nullable
+};
+
+struct MlpParams {
+    const void *q, *W1, *W2t, *Ws, *ws2;
+    const float *b1, *bs, *b2, *bs2;
+    int Hq, G, Hkv, Rp, Ht, Hs, act;
+    // S hidden splits (chunk_t target units and chunk_s score units each);
+    // blocks of WR row groups x WS splits as in AttnParams; SB partials per row.
+    int S, chunk_t, chunk_s, RG, WR, WS, RB, SB;
+    float *part_O;   // [Hkv][SB][Rp][d]
+    float *part_s;   // [Hkv][SB][Rp]
+    float *a_out, *A_out;   // written directly when SB == 1
+};
+
+struct MlpReduceParams {
+    const float *part_O, *part_s, *b2, *bs2;
+    int Hq, G, Hkv, Rp, S;
+    float *a_out, *A_out;
+};
+
+struct MergeParams {
+    const float *a, *A, *lam, *A_loc;
+    void *out;
+    float *lse_out;
+    long rows;
+};
+
+// Row tiling of the MFMA kernels: rows per wave = 16 * rt.
+int row_tiles_for(int Rp);
+
+hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hipStream_t st);
+hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st);
+hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipStream_t st);
+hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st);
+hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st);
+
+}  // namespace nectar

@@ -1,0 +1,356 @@
+// C ABI of the Nectar hot path (declared in include/nectar.h): host-side
+// argument validation (before any HIP call, so every error path is testable
+// without a GPU), split planning, workspace sizing and kernel dispatch.
+#include "nectar.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.hpp"
+
+using namespace nectar;
+
+namespace {
+
+// Waves a split plan aims for: 256 CUs x 8 resident waves keeps every CU busy
+// with enough loads in flight to cover HBM latency.
+constexpr long kTargetWaves = 2048;
+constexpr long kTargetWavesMlp = 1024;
+constexpr int kTile = 32;
+
+inline long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+nectar_status check_desc(const nectar_attn_desc *d) {
+    if (!d) return NECTAR_EINVAL;
+    if (d->R < 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Hq % d->Hkv != 0) return NECTAR_EINVAL;
+    if (d->dtype != NECTAR_F32 && d->dtype != NECTAR_BF16) return NECTAR_EINVAL;
+    if (d->d <= 0) return NECTAR_EINVAL;
+    if (d->d != 64 && d->d != 128) return NECTAR_EUNSUPPORTED;
+    if (!std::isfinite(d->scale) || d->splits < 0) return NECTAR_EINVAL;
+    if ((long)d->R * d->Hq > 0x7fffffffL / 2) return NECTAR_EUNSUPPORTED;
+    return NECTAR_OK;
+}
+
+inline float score_scale(const nectar_attn_desc *d) {
+    return d->scale != 0.f ? d->scale : 1.0f / std::sqrt((float)d->d);
+}
+
+// Tensors read with 16-byte vector loads must be 16-byte aligned; fp32 scalars
+// and outputs written element-wise need their natural alignment.
+inline bool tensor_ok(const void *p) { return p && aligned(p, 16); }
+inline bool f32_ok(const void *p) { return p && aligned(p, 4); }
+inline bool out_ok(const void *p, int dtype) { return p && aligned(p, dtype == NECTAR_BF16 ? 2 : 4); }
+
+struct AttnPlan {
+    int P = 0, Rp = 0, RT = 0, RG = 0, S = 0, chunk = kTile;
+    int WR = 1, WS = 1, RB = 0, SB = 0;
+    size_t ws = 0;
+};
+
+// Block shape of the MFMA kernels: 4 waves as WR row groups x WS splits.
+void block_shape(int RG, int &WR, int &WS, int &RB) {
+    WR = RG >= 3 ? 4 : (RG == 2 ? 2 : 1);
+    WS = 4 / WR;
+    RB = (int)cdiv(RG, WR);
+}
+
+AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv) {
+    AttnPlan pl;
+    pl.P = P;
+    pl.Rp = Rp;
+    if (P == 0 || Rp == 0 || T_kv <= 0) return pl;    // nothing to attend: combine with S = 0
+    const long tiles = cdiv(T_kv, kTile);
+    const bool mfma = d->dtype == NECTAR_BF16;
+    long units;
+    if (mfma) {
+        pl.RT = row_tiles_for(Rp);
+        pl.RG = (int)cdiv(Rp, 16L * pl.RT);
+        block_shape(pl.RG, pl.WR, pl.WS, pl.RB);
+        units = (long)P * pl.RG;
+    } else {
+        pl.RG = Rp;
+        units = (long)P * Rp;
+    }
+    long S = d->splits > 0 ? d->splits : cdiv(kTargetWaves, units);
+    S = S < 1 ? 1 : (S > tiles ? tiles : S);
+    const long per = cdiv(tiles, S);
+    pl.chunk = (int)(per * kTile);
+    pl.S = (int)cdiv(tiles, per);
+    pl.SB = mfma ? (int)cdiv(pl.S, pl.WS) : pl.S;
+    pl.ws = pl.SB > 1 || !mfma ? (size_t)P * pl.SB * Rp * ((size_t)d->d * 4 + 8) : 0;
+    return pl;
+}
+
+struct MlpPlan {
+    int Rp = 0, RT = 0, RG = 0, S = 0, ct = kTile, cs = kTile;
+    int WR = 1, WS = 1, RB = 0, SB = 0;
+    size_t ws = 0;
+};
+
+MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs) {
+    MlpPlan pl;
+    pl.Rp = d->R * (d->Hq / d->Hkv);
+    if (pl.Rp == 0) return pl;
+    const bool mfma = d->dtype == NECTAR_BF16;
+    long units;
+    if (mfma) {
+        pl.RT = row_tiles_for(pl.Rp);
+        pl.RG = (int)cdiv(pl.Rp, 16L * pl.RT);
+        block_shape(pl.RG, pl.WR, pl.WS, pl.RB);
+        units = (long)d->Hkv * pl.RG;
+    } else {
+        pl.RG = pl.Rp;
+        units = (long)d->Hkv * pl.Rp;
+    }
+    const long tt = cdiv(Ht, kTile), ts = cdiv(Hs, kTile);
+    const long tmax = tt > ts ? (tt > 1 ? tt : 1) : (ts > 1 ? ts : 1);
+    long S = d->splits > 0 ? d->splits : cdiv(kTargetWavesMlp, units);
+    S = S < 1 ? 1 : (S > tmax ? tmax : S);
+    long pt = cdiv(tt, S), ps = cdiv(ts, S);
+    pt = pt < 1 ? 1 : pt;
+    ps = ps < 1 ? 1 : ps;
+    long Se = cdiv(tt, pt);
+    if (cdiv(ts, ps) > Se) Se = cdiv(ts, ps);
+    if (Se < 1) Se = 1;
+    pl.S = (int)Se;
+    pl.ct = (int)(pt * kTile);
+    pl.cs = (int)(ps * kTile);
+    pl.SB = mfma ? (int)cdiv(pl.S, pl.WS) : pl.S;
+    pl.ws = pl.SB > 1 || !mfma ? (size_t)d->Hkv * pl.SB * pl.Rp * ((size_t)d->d * 4 + 4) : 0;
+    return pl;
+}
+
+nectar_status check_ws(size_t need, const void *ws, size_t ws_bytes) {
+    if (need == 0) return NECTAR_OK;
+    if (ws_bytes < need) return NECTAR_EWORKSPACE;
+    return (ws && aligned(ws, 16)) ? NECTAR_OK : NECTAR_EINVAL;
+}
+
+nectar_status finish(hipError_t e, hipStream_t st) {
+    if (e != hipSuccess) return NECTAR_EHIP;
+    static const bool sync_check = [] {
+        const char *v = std::getenv("NECTAR_SYNC_CHECK");
+        return v && v[0] == '1';
+    }();
+    if (sync_check) {
+        if (hipStreamSynchronize(st) != hipSuccess) return NECTAR_EHIP;
+        if (hipGetLastError() != hipSuccess) return NECTAR_EHIP;
+    }
+    return NECTAR_OK;
+}
+
+// Attention over a batched cache, then (unless one block per row group covered
+// every key) the combine pass.
+hipError_t run_attention(const nectar_attn_desc *d, const AttnPlan &pl, const void *q, const void *k,
+                         const void *v, int64_t bstride, int64_t hstride, int B, int Tq, long T_kv,
+                         int causal, int q_offset, CombineParams cp, void *ws, hipStream_t st) {
+    float *part_O = (float *)ws;
+    float2 *part_ml = (float2 *)((char *)ws + (size_t)pl.P * pl.SB * pl.Rp * d->d * 4);
+    const bool mfma = d->dtype == NECTAR_BF16;
+    if (pl.S > 0) {
+        AttnParams a{};
+        a.q = q; a.k = k; a.v = v;
+        a.kv_bstride = bstride; a.kv_hstride = hstride;
+        a.Hq = d->Hq; a.G = d->Hq / d->Hkv; a.Hkv = d->Hkv; a.Tq = Tq; a.B = B; a.Rp = pl.Rp;
+        a.T_kv = (int)T_kv; a.causal = causal; a.q_offset = q_offset;
+        a.sl2 = score_scale(d) * 1.4426950408889634f;
+        a.P = pl.P; a.S = pl.S; a.chunk = pl.chunk; a.RG = pl.RG;
+        a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB;
+        a.part_O = part_O; a.part_ml = part_ml;
+        if (mfma && pl.SB == 1) {
+            a.lse_out = cp.lse_out; a.A_out = cp.A_out; a.x_lse = cp.x_lse; a.x_A = cp.x_A;
+            a.out = cp.out; a.out_lse = cp.out_lse;
+        }
+        hipError_t e = launch_attn_partial(a, d->dtype, d->d, pl.RT, st);
+        if (e != hipSuccess || (mfma && pl.SB == 1)) return e;
+    }
+    cp.part_O = part_O; cp.part_ml = part_ml;
+    cp.Hq = d->Hq; cp.G = d->Hq / d->Hkv; cp.Hkv = d->Hkv; cp.Tq = Tq;
+    cp.P = pl.P; cp.S = pl.SB; cp.Rp = pl.Rp;
+    return launch_attn_combine(cp, d->dtype, d->d, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int nectar_abi_version(void) { return NECTAR_ABI_VERSION; }
+
+const char *nectar_status_string(nectar_status s) {
+    switch (s) {
+        case NECTAR_OK: return "NECTAR_OK: success";
+        case NECTAR_EINVAL: return "NECTAR_EINVAL: invalid argument (null pointer, shape, alignment or enum)";
+        case NECTAR_EUNSUPPORTED: return "NECTAR_EUNSUPPORTED: valid arguments not supported by this build";
+        case NECTAR_EWORKSPACE: return "NECTAR_EWORKSPACE: workspace smaller than the size query requires";
+        case NECTAR_EHIP: return "NECTAR_EHIP: HIP launch or execution error";
+    }
+    return "unknown nectar_status";
+}
+
+size_t nectar_doc_attn_workspace_size(const nectar_attn_desc *desc, int64_t n) {
+    if (check_desc(desc) != NECTAR_OK || n < 0 || n > 0x7fffffffL - kTile) return 0;
+    return plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)n).ws;
+}
+
+nectar_status nectar_doc_attn_exact(const nectar_attn_desc *desc, int64_t n, const void *q,
+                                    const void *k, const void *v, float *alpha_out, float *A_out,
+                                    void *ws, size_t ws_bytes, void *stream) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if (n < 0) return NECTAR_EINVAL;
+    if (n > 0x7fffffffL - kTile) return NECTAR_EUNSUPPORTED;
+    if (desc->R == 0) return NECTAR_OK;
+    if (!tensor_ok(q) || !f32_ok(alpha_out) || !f32_ok(A_out)) return NECTAR_EINVAL;
+    if (n > 0 && (!tensor_ok(k) || !tensor_ok(v))) return NECTAR_EINVAL;
+    const AttnPlan pl = plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)n);
+    if ((s = check_ws(pl.ws, ws, ws_bytes)) != NECTAR_OK) return s;
+    CombineParams cp{};
+    cp.lse_out = alpha_out;
+    cp.A_out = A_out;
+    hipStream_t st = (hipStream_t)stream;
+    return finish(run_attention(desc, pl, q, k, v, 0, (int64_t)n * desc->d, 1, desc->R, (long)n, 0, 0,
+                                cp, ws, st), st);
+}
+
+static nectar_status check_module(const nectar_attn_desc *desc, const nectar_module *m) {
+    if (!m) return NECTAR_EINVAL;
+    if (m->kind == NECTAR_MODULE_MLP) {
+        if (m->act != NECTAR_ACT_GELU && m->act != NECTAR_ACT_SILU) return NECTAR_EINVAL;
+        if (m->Ht < 0 || m->Hs < 0) return NECTAR_EINVAL;
+        if (!m->b2 || !m->bs2 || !aligned(m->b2, 4) || !aligned(m->bs2, 4)) return NECTAR_EINVAL;
+        if (m->Ht > 0 && (!tensor_ok(m->W1) || !tensor_ok(m->W2t) || !m->b1 || !aligned(m->b1, 4)))
+            return NECTAR_EINVAL;
+        if (m->Hs > 0 && (!tensor_ok(m->Ws) || !m->ws2 || !aligned(m->ws2, desc->dtype ? 2 : 4) ||
+                          !m->bs || !aligned(m->bs, 4)))
+            return NECTAR_EINVAL;
+        return NECTAR_OK;
+    }
+    if (m->kind == NECTAR_MODULE_KVPAIR) {
+        if (m->p < 0) return NECTAR_EINVAL;
+        if (m->p > 0x7fffffffL - kTile) return NECTAR_EUNSUPPORTED;
+        if (m->p > 0 && (!tensor_ok(m->W) || !tensor_ok(m->Z))) return NECTAR_EINVAL;
+        return NECTAR_OK;
+    }
+    return NECTAR_EINVAL;
+}
+
+size_t nectar_module_workspace_size(const nectar_attn_desc *desc, const nectar_module *m) {
+    if (check_desc(desc) != NECTAR_OK || !m) return 0;
+    if (m->kind == NECTAR_MODULE_KVPAIR) {
+        if (m->p < 0 || m->p > 0x7fffffffL - kTile) return 0;
+        return plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)m->p).ws;
+    }
+    if (m->kind != NECTAR_MODULE_MLP || m->Ht < 0 || m->Hs < 0) return 0;
+    return plan_mlp(desc, m->Ht, m->Hs).ws;
+}
+
+nectar_status nectar_module_forward(const nectar_attn_desc *desc, const nectar_module *m,
+                                    const void *q, float *a_out, float *A_out, void *ws,
+                                    size_t ws_bytes, void *stream) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if ((s = check_module(desc, m)) != NECTAR_OK) return s;
+    if (desc->R == 0) return NECTAR_OK;
+    if (!tensor_ok(q) || !f32_ok(a_out) || !f32_ok(A_out)) return NECTAR_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    if (m->kind == NECTAR_MODULE_KVPAIR) {
+        const AttnPlan pl = plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)m->p);
+        if ((s = check_ws(pl.ws, ws, ws_bytes)) != NECTAR_OK) return s;
+        CombineParams cp{};
+        cp.lse_out = a_out;
+        cp.A_out = A_out;
+        return finish(run_attention(desc, pl, q, m->W, m->Z, 0, m->p * desc->d, 1, desc->R, (long)m->p,
+                                    0, 0, cp, ws, st), st);
+    }
+    const MlpPlan pl = plan_mlp(desc, m->Ht, m->Hs);
+    if ((s = check_ws(pl.ws, ws, ws_bytes)) != NECTAR_OK) return s;
+    float *part_O = (float *)ws;
+    float *part_s = (float *)((char *)ws + (size_t)desc->Hkv * pl.SB * pl.Rp * desc->d * 4);
+    const bool mfma = desc->dtype == NECTAR_BF16;
+    MlpParams a{};
+    a.q = q; a.W1 = m->W1; a.W2t = m->W2t; a.Ws = m->Ws; a.ws2 = m->ws2;
+    a.b1 = m->b1; a.bs = m->bs; a.b2 = m->b2; a.bs2 = m->bs2;
+    a.Hq = desc->Hq; a.G = desc->Hq / desc->Hkv; a.Hkv = desc->Hkv; a.Rp = pl.Rp;
+    a.Ht = m->Ht; a.Hs = m->Hs; a.act = m->act;
+    a.S = pl.S; a.chunk_t = pl.ct; a.chunk_s = pl.cs; a.RG = pl.RG;
+    a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB;
+    a.part_O = part_O; a.part_s = part_s;
+    a.a_out = a_out; a.A_out = A_out;
+    hipError_t e = launch_mlp_partial(a, desc->dtype, desc->d, pl.RT, st);
+    if (e == hipSuccess && !(mfma && pl.SB == 1)) {
+        MlpReduceParams r;
+        r.part_O = part_O; r.part_s = part_s; r.b2 = m->b2; r.bs2 = m->bs2;
+        r.Hq = desc->Hq; r.G = desc->Hq / desc->Hkv; r.Hkv = desc->Hkv; r.Rp = pl.Rp; r.S = pl.SB;
+        r.a_out = a_out; r.A_out = A_out;
+        e = launch_mlp_reduce(r, desc->d, st);
+    }
+    return finish(e, st);
+}
+
+static nectar_status check_local(const nectar_attn_desc *desc, const nectar_local_desc *loc) {
+    if (!loc) return NECTAR_EINVAL;
+    if (loc->B < 0 || loc->Tq < 0 || (long)loc->B * loc->Tq != desc->R) return NECTAR_EINVAL;
+    if (loc->T_loc < 0 || loc->T_cap < loc->T_loc || loc->q_offset < 0) return NECTAR_EINVAL;
+    if (loc->T_loc > 0x7fffffff - kTile) return NECTAR_EUNSUPPORTED;
+    return NECTAR_OK;
+}
+
+size_t nectar_local_workspace_size(const nectar_attn_desc *desc, const nectar_local_desc *loc) {
+    if (check_desc(desc) != NECTAR_OK || check_local(desc, loc) != NECTAR_OK) return 0;
+    return plan_attn(desc, loc->B * desc->Hkv, loc->Tq * (desc->Hq / desc->Hkv), loc->T_loc).ws;
+}
+
+nectar_status nectar_local_attn_lse(const nectar_attn_desc *desc, const nectar_local_desc *loc,
+                                    const void *q, const void *k_loc, const void *v_loc,
+                                    float *lse_out, float *A_out, const float *doc_lse,
+                                    const float *doc_A, void *out, float *out_lse, void *ws,
+                                    size_t ws_bytes, void *stream) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if ((s = check_local(desc, loc)) != NECTAR_OK) return s;
+    const bool want_merge = out || out_lse;
+    if (!lse_out && !A_out && !want_merge) return NECTAR_EINVAL;
+    if (want_merge != (doc_lse || doc_A)) return NECTAR_EINVAL;
+    if (want_merge && (!f32_ok(doc_lse) || !f32_ok(doc_A))) return NECTAR_EINVAL;
+    if ((lse_out && !f32_ok(lse_out)) || (A_out && !f32_ok(A_out)) || (out && !out_ok(out, desc->dtype)) ||
+        (out_lse && !f32_ok(out_lse)))
+        return NECTAR_EINVAL;
+    if (desc->R == 0) return NECTAR_OK;
+    if (!tensor_ok(q)) return NECTAR_EINVAL;
+    if (loc->T_loc > 0 && (!tensor_ok(k_loc) || !tensor_ok(v_loc))) return NECTAR_EINVAL;
+    const AttnPlan pl = plan_attn(desc, loc->B * desc->Hkv, loc->Tq * (desc->Hq / desc->Hkv), loc->T_loc);
+    if ((s = check_ws(pl.ws, ws, ws_bytes)) != NECTAR_OK) return s;
+    CombineParams cp{};
+    cp.lse_out = lse_out;
+    cp.A_out = A_out;
+    cp.x_lse = doc_lse;
+    cp.x_A = doc_A;
+    cp.out = out;
+    cp.out_lse = out_lse;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t hstride = (int64_t)loc->T_cap * desc->d;
+    return finish(run_attention(desc, pl, q, k_loc, v_loc, hstride * desc->Hkv, hstride, loc->B, loc->Tq,
+                                loc->T_loc, 1, loc->q_offset, cp, ws, st), st);
+}
+
+nectar_status nectar_merge(const nectar_attn_desc *desc, const float *a, const float *A, const float *lam,
+                           const float *A_loc, void *out, float *lse_out, void *stream) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if (desc->R == 0) return NECTAR_OK;
+    if (!f32_ok(a) || !f32_ok(A) || !f32_ok(lam) || !f32_ok(A_loc) || !out_ok(out, desc->dtype))
+        return NECTAR_EINVAL;
+    if (lse_out && !f32_ok(lse_out)) return NECTAR_EINVAL;
+    MergeParams p;
+    p.a = a; p.A = A; p.lam = lam; p.A_loc = A_loc; p.out = out; p.lse_out = lse_out;
+    p.rows = (long)desc->R * desc->Hq;
+    hipStream_t st = (hipStream_t)stream;
+    return finish(launch_merge(p, desc->dtype, desc->d, st), st);
+}
+
+}  // extern "C"

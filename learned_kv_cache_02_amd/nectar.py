@@ -1,0 +1,259 @@
+"""Thin ctypes binding of libnectar.so (the C ABI in include/nectar.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+Tensors are torch tensors on the GPU (contiguous); bf16 inputs may also be
+given as uint16 tensors holding bf16 bit patterns.  Calls are asynchronous on
+torch's current stream.  A missing library raises at import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnectar.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libnectar.so is not built (run __graft_entry__.build() or "
+                      "python learned_kv_cache_02_amd/build_native.py): no fallback path exists")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+F32, BF16 = 0, 1
+MLP, KVPAIR = 0, 1
+GELU, SILU = 0, 1
+STATUS = {0: "NECTAR_OK", 1: "NECTAR_EINVAL", 2: "NECTAR_EUNSUPPORTED", 3: "NECTAR_EWORKSPACE",
+          4: "NECTAR_EHIP"}
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("R", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("splits", ctypes.c_int32)]
+
+
+class LocalDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("T_loc", ctypes.c_int32),
+                ("T_cap", ctypes.c_int32), ("q_offset", ctypes.c_int32)]
+
+
+class Module(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("act", ctypes.c_int32), ("Ht", ctypes.c_int32),
+                ("Hs", ctypes.c_int32),
+                ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+                ("W2t", ctypes.c_void_p), ("b2", ctypes.c_void_p),
+                ("Ws", ctypes.c_void_p), ("bs", ctypes.c_void_p),
+                ("ws2", ctypes.c_void_p), ("bs2", ctypes.c_void_p),
+                ("p", ctypes.c_int64), ("W", ctypes.c_void_p), ("Z", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_D = ctypes.POINTER(AttnDesc)
+_lib.nectar_doc_attn_workspace_size.argtypes = [_D, ctypes.c_int64]
+_lib.nectar_doc_attn_workspace_size.restype = ctypes.c_size_t
+_lib.nectar_doc_attn_exact.argtypes = [_D, ctypes.c_int64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.nectar_module_workspace_size.argtypes = [_D, ctypes.POINTER(Module)]
+_lib.nectar_module_workspace_size.restype = ctypes.c_size_t
+_lib.nectar_module_forward.argtypes = [_D, ctypes.POINTER(Module), _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.nectar_local_workspace_size.argtypes = [_D, ctypes.POINTER(LocalDesc)]
+_lib.nectar_local_workspace_size.restype = ctypes.c_size_t
+_lib.nectar_local_attn_lse.argtypes = [_D, ctypes.POINTER(LocalDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, ctypes.c_size_t, _P]
+_lib.nectar_merge.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P]
+_lib.nectar_status_string.argtypes = [ctypes.c_int]
+_lib.nectar_status_string.restype = ctypes.c_char_p
+_lib.nectar_abi_version.restype = ctypes.c_int
+for _f in ("nectar_doc_attn_exact", "nectar_module_forward", "nectar_local_attn_lse", "nectar_merge"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+class NectarError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(_lib.nectar_status_string(code).decode())
+        self.code = code
+        self.status = STATUS.get(code, str(code))
+
+
+def _check(code: int):
+    if code != 0:
+        raise NectarError(code)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.uint16, torch.int16):
+        return BF16
+    raise TypeError("unsupported element type %s" % t.dtype)
+
+
+def desc(R, Hq, Hkv, d, dtype, scale=0.0, splits=0) -> AttnDesc:
+    return AttnDesc(int(R), int(Hq), int(Hkv), int(d), int(dtype), float(scale), int(splits))
+
+
+_ws_cache = {}
+
+
+def workspace(nbytes: int, device=None) -> Optional[torch.Tensor]:
+    """A cached scratch buffer of at least nbytes on the device (None for 0)."""
+    if nbytes == 0:
+        return None
+    dev = torch.device(device or "cuda")
+    key = (dev.type, dev.index)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _ws_args(nbytes, device):
+    buf = workspace(nbytes, device)
+    return (_ptr(buf), nbytes) if buf is not None else (None, 0)
+
+
+def doc_attn_workspace_size(dsc: AttnDesc, n: int) -> int:
+    return int(_lib.nectar_doc_attn_workspace_size(ctypes.byref(dsc), int(n)))
+
+
+def doc_attn_exact(q, k, v, Hkv, *, scale=0.0, splits=0, alpha_out=None, A_out=None):
+    """Exact document attention (alpha [R][Hq], A [R][Hq][d] fp32); q [R][Hq][d], k/v [Hkv][n][d]."""
+    R, Hq, d = q.shape
+    n = k.shape[-2] if k.dim() >= 2 else 0
+    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    if alpha_out is None:
+        alpha_out = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
+    if A_out is None:
+        A_out = torch.empty((R, Hq, d), dtype=torch.float32, device=q.device)
+    wp, wn = _ws_args(doc_attn_workspace_size(dsc, n), q.device)
+    _check(_lib.nectar_doc_attn_exact(ctypes.byref(dsc), n, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha_out),
+                                      _ptr(A_out), wp, wn, _stream()))
+    return alpha_out, A_out
+
+
+@dataclass
+class MLPModule:
+    """One-hidden-layer score/target module per KV head (tensors on the GPU)."""
+    W1: torch.Tensor
+    b1: torch.Tensor
+    W2t: torch.Tensor
+    b2: torch.Tensor
+    Ws: torch.Tensor
+    bs: torch.Tensor
+    ws2: torch.Tensor
+    bs2: torch.Tensor
+    act: int = GELU
+
+    def struct(self) -> Module:
+        m = Module()
+        m.kind, m.act = MLP, self.act
+        m.Ht, m.Hs = self.W1.shape[-2], self.Ws.shape[-2]
+        m.W1, m.b1, m.W2t, m.b2 = (_ptr(t) for t in (self.W1, self.b1, self.W2t, self.b2))
+        m.Ws, m.bs, m.ws2, m.bs2 = (_ptr(t) for t in (self.Ws, self.bs, self.ws2, self.bs2))
+        return m
+
+
+@dataclass
+class KVPairModule:
+    """Quadrature module: W, Z [Hkv][p][d]."""
+    W: torch.Tensor
+    Z: torch.Tensor
+
+    def struct(self) -> Module:
+        m = Module()
+        m.kind = KVPAIR
+        m.p = self.W.shape[-2]
+        m.W, m.Z = _ptr(self.W), _ptr(self.Z)
+        return m
+
+
+def module_workspace_size(dsc: AttnDesc, mod) -> int:
+    return int(_lib.nectar_module_workspace_size(ctypes.byref(dsc), ctypes.byref(mod.struct())))
+
+
+def module_forward(q, module, Hkv, *, scale=0.0, splits=0, a_out=None, A_out=None):
+    """(a [R][Hq], A [R][Hq][d]) fp32 of an MLPModule or KVPairModule."""
+    R, Hq, d = q.shape
+    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    m = module.struct()
+    if a_out is None:
+        a_out = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
+    if A_out is None:
+        A_out = torch.empty((R, Hq, d), dtype=torch.float32, device=q.device)
+    wp, wn = _ws_args(int(_lib.nectar_module_workspace_size(ctypes.byref(dsc), ctypes.byref(m))), q.device)
+    _check(_lib.nectar_module_forward(ctypes.byref(dsc), ctypes.byref(m), _ptr(q), _ptr(a_out),
+                                      _ptr(A_out), wp, wn, _stream()))
+    return a_out, A_out
+
+
+def local_workspace_size(dsc: AttnDesc, loc: LocalDesc) -> int:
+    return int(_lib.nectar_local_workspace_size(ctypes.byref(dsc), ctypes.byref(loc)))
+
+
+def local_attn_lse(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, scale=0.0, splits=0,
+                   want_pair=True, doc_lse=None, doc_A=None, out=None, out_lse=None,
+                   lse_out=None, A_out=None):
+    """Causal local attention.  k_loc/v_loc [B][Hkv][T_cap][d].
+
+    Returns (lse, A_local) when want_pair, and additionally (out, out_lse) when a
+    document pair (doc_lse, doc_A) is given: the merged output in q's dtype.
+    """
+    R, Hq, d = q.shape
+    T_cap = k_loc.shape[-2]
+    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    loc = LocalDesc(int(B), int(Tq), int(T_loc), int(T_cap), int(q_offset))
+    if want_pair:
+        if lse_out is None:
+            lse_out = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
+        if A_out is None:
+            A_out = torch.empty((R, Hq, d), dtype=torch.float32, device=q.device)
+    merge = doc_lse is not None
+    if merge:
+        if out is None:
+            out = torch.empty((R, Hq, d), dtype=q.dtype, device=q.device)
+        if out_lse is None:
+            out_lse = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
+    wp, wn = _ws_args(local_workspace_size(dsc, loc), q.device)
+    _check(_lib.nectar_local_attn_lse(ctypes.byref(dsc), ctypes.byref(loc), _ptr(q), _ptr(k_loc), _ptr(v_loc),
+                                      _ptr(lse_out), _ptr(A_out), _ptr(doc_lse), _ptr(doc_A), _ptr(out),
+                                      _ptr(out_lse), wp, wn, _stream()))
+    res = ()
+    if want_pair:
+        res += (lse_out, A_out)
+    if merge:
+        res += (out, out_lse)
+    return res
+
+
+def merge(a, A, lam, A_loc, *, Hkv, out_dtype, out=None, lse_out=None):
+    """Log-sum-exp merge of (a, A) with (lam, A_loc); out in out_dtype (fp32/bf16)."""
+    R, Hq, d = A.shape
+    code = F32 if out_dtype == torch.float32 else BF16
+    dsc = desc(R, Hq, Hkv, d, code)
+    if out is None:
+        out = torch.empty((R, Hq, d), dtype=out_dtype, device=A.device)
+    if lse_out is None:
+        lse_out = torch.empty((R, Hq), dtype=torch.float32, device=A.device)
+    _check(_lib.nectar_merge(ctypes.byref(dsc), _ptr(a), _ptr(A), _ptr(lam), _ptr(A_loc), _ptr(out),
+                             _ptr(lse_out), _stream()))
+    return out, lse_out
+
+
+def abi_version() -> int:
+    return int(_lib.nectar_abi_version())

@@ -43,8 +43,9 @@
  *   are propagated, not checked.
  * - Workspaces: the *_workspace_size functions return the exact number of
  *   bytes (0 allowed) the matching call needs for the same arguments; they
- *   need no GPU.  The workspace is scratch owned by the caller; its contents
- *   need no initialisation and are undefined afterwards.
+ *   need no GPU.  The workspace is caller-owned device scratch: its contents
+ *   need no initialisation and are undefined after a call.  Calls that may run
+ *   concurrently (different streams) need distinct workspaces.
  */
 #ifndef NECTAR_H
 #define NECTAR_H
@@ -83,8 +84,9 @@ typedef struct {
     int32_t dtype;   /* nectar_dtype of q, caches and module weights */
     float scale;     /* score scale; 0 selects 1/sqrt(d) */
     int32_t splits;  /* 0: automatic; > 0: requested number of key (or hidden)
-                        splits per head, clamped to [1, #32-wide tiles].  Results
-                        agree across split counts up to fp32 rounding. */
+                        splits per head, clamped to [1, number of key tiles]
+                        (64 keys per tile for bf16, 32 for fp32; 32 hidden units).
+                        Results agree across split counts up to rounding. */
 } nectar_attn_desc;
 
 /* The local (question + generated tokens) cache of nectar_local_attn_lse. */
@@ -180,6 +182,12 @@ NECTAR_API nectar_status nectar_local_attn_lse(const nectar_attn_desc *desc, con
 NECTAR_API nectar_status nectar_merge(const nectar_attn_desc *desc, const float *a, const float *A,
                            const float *lam, const float *A_loc, void *out, float *lse_out,
                            void *stream);
+
+/* Zero-fills ws_bytes of device memory on `stream` with a fill kernel (no
+ * memset node, so it can be captured in a graph); ws must be 16-byte aligned.
+ * Workspaces need no initialisation; this is a convenience for callers that
+ * want deterministic scratch contents. */
+NECTAR_API nectar_status nectar_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 NECTAR_API const char *nectar_status_string(nectar_status s);
 NECTAR_API int nectar_abi_version(void);

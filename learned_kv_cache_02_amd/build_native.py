@@ -20,33 +20,33 @@ def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
     objs = []
     inc = ["-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
     for src in SOURCES:
         obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + ".o")
-        cmd = [hipcc()] + HIPCC_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd.insert(1, "-x")
             cmd.insert(2, "hip")
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-        out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+        log = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
         if r.returncode != 0:
-            raise RuntimeError("hipcc failed for %s:\n%s" % (src, out))
-        if verbose and out.strip():
-            print(out)
+            raise RuntimeError("hipcc failed for %s:\n%s" % (src, log))
+        if verbose and log.strip():
+            print(log)
         objs.append(obj)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     for o in objs:
         os.remove(o)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

@@ -23,7 +23,9 @@
 // row group are folded in LDS (log-sum-exp rescale, then a sum), so each block
 // leaves one partial per row.  When one block spans the whole key range the
 // block finishes the rows itself (lse, read-out, optional merge); otherwise
-// attn_combine folds the per-block partials.
+// attn_combine folds the per-block partials.  (A last-arriving-block fold was
+// measured slower: the agent-scope fences it needs write back and invalidate
+// the XCD's L2 on every block.)
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -51,12 +53,12 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D> &T, const uint16_t *kb, c
         const int key = min(k0 + 16 * hh + c, kmax);
         const uint16_t *kp = kb + (size_t)key * D;
 #pragma unroll
-        for (int kt = 0; kt < KS; ++kt) T.k[hh][kt] = *(const u32x4 *)(kp + (4 * kt + g) * 8);
+        for (int kt = 0; kt < KS; ++kt) T.k[hh][kt] = stream_load((const u32x4 *)(kp + (4 * kt + g) * 8));
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int key = min(k0 + slot_key(g, j), kmax);
-        T.v[j] = *(const typename VRow<D>::T *)(vb + (size_t)key * D + c * DV);
+        T.v[j] = stream_load((const typename VRow<D>::T *)(vb + (size_t)key * D + c * DV));
     }
 }
 
@@ -167,8 +169,9 @@ __device__ __forceinline__ void finish_row_lanes(const AttnParams &a, size_t o, 
     }
 }
 
-template <int D, int RT, typename OutT>
-__global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams a) {
+// RT == 1: two waves per SIMD (8 per CU), each with a 32 KB batch in flight.
+template <int D, int RT, int SUB, typename OutT>
+__global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void attn_partial_mfma(AttnParams a) {
     constexpr int KS = D / 32, DV = D / 16;
     // Fold buffers (used when WS > 1, hence WR <= 2): per row group one f32x4
     // per (register, lane), lane-major so each wave access is conflict-free.
@@ -227,16 +230,20 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams a) {
     const int k_lo = s * a.chunk;
     const int k_hi = min(k_lo + a.chunk, wlim);
     if (k_lo < k_hi) {
+        // Batches of SUB 32-key tiles: every load of a batch (SUB x 16 KB) is
+        // issued before its first use, and the two waves sharing each SIMD keep
+        // the memory system busy while the other one computes.
         const int kmax = a.T_kv - 1;
-        KVTile<D> t0, t1;
-        load_kv_tile<D>(t0, kb, vb, k_lo, kmax, g, c);
-        for (int k0 = k_lo; k0 < k_hi; k0 += 64) {
-            const bool has1 = k0 + 32 < k_hi;
-            if (has1) load_kv_tile<D>(t1, kb, vb, k0 + 32, kmax, g, c);
-            attend_tile<D, RT>(t0, k0, qv, lim, a.sl2, g, O, m, l);
-            if (!has1) break;
-            if (k0 + 64 < k_hi) load_kv_tile<D>(t0, kb, vb, k0 + 64, kmax, g, c);
-            attend_tile<D, RT>(t1, k0 + 32, qv, lim, a.sl2, g, O, m, l);
+        int limw[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) limw[rt] = min(lim[rt], k_hi);
+        for (int k0 = k_lo; k0 < k_hi; k0 += 32 * SUB) {
+            KVTile<D> tl[SUB];
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) load_kv_tile<D>(tl[u], kb, vb, min(k0 + 32 * u, kmax), kmax, g, c);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) attend_tile<D, RT>(tl[u], k0 + 32 * u, qv, limw, a.sl2, g, O, m, l);
         }
     }
 #pragma unroll
@@ -271,20 +278,21 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams a) {
             }
             __syncthreads();
         }
-        if (ws != 0) return;
+        if (ws == 0) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            l[rt] += fold_l[wr][rt][lane];
+            for (int rt = 0; rt < RT; ++rt) {
+                l[rt] += fold_l[wr][rt][lane];
 #pragma unroll
-            for (int mm = 0; mm < DV; ++mm) O[rt][mm] += fold_O[wr][rt * DV + mm][lane];
+                for (int mm = 0; mm < DV; ++mm) O[rt][mm] += fold_O[wr][rt * DV + mm][lane];
+            }
         }
     }
-    if (rg >= a.RG) return;
+    const bool owner = (a.WS == 1 || ws == 0) && rg < a.RG;
 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int rho = (rg * RT + rt) * 16 + c;
-        if (rho >= a.Rp) continue;
+        if (!owner || rho >= a.Rp) continue;
         if (a.SB == 1) {
             finish_row_lanes<D, OutT>(a, out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq), g, m[rt], l[rt], O[rt]);
         } else {
@@ -300,6 +308,7 @@ __global__ __launch_bounds__(256) void attn_partial_mfma(AttnParams a) {
                 }
         }
     }
+
 }
 
 // fp32 path: one wave per (problem, row, split); lanes own head dimensions,
@@ -353,7 +362,7 @@ template <int D, typename OutT, int MAXI>
 __global__ __launch_bounds__(256) void attn_combine(CombineParams a) {
     constexpr int DQ = D / 4;            // float4 columns
     constexpr int NSG = 256 / DQ;        // split groups
-    __shared__ float red[256];
+    __shared__ float red[8];
     __shared__ f32x4 accs[NSG][DQ];
     const int idx = blockIdx.x;
     const int p = idx / a.Rp, rho = idx - p * a.Rp;
@@ -387,14 +396,11 @@ __global__ __launch_bounds__(256) void attn_combine(CombineParams a) {
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) mloc = fmaxf(mloc, st[i].x);
     for (int s = sg + MAXI * NSG; s < a.S; s += NSG) mloc = fmaxf(mloc, ml[(size_t)s * a.Rp].x);
-    red[tid] = mloc;
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o2, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = mloc;
     __syncthreads();
-    for (int k = 128; k > 0; k >>= 1) {
-        if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
-        __syncthreads();
-    }
-    const float M = red[0];
-    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const bool empty = (M == -INFINITY);
     float lloc = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -413,15 +419,14 @@ __global__ __launch_bounds__(256) void attn_combine(CombineParams a) {
         }
     }
     // every split's l is counted once: only the dq == 0 thread of a group adds it
-    red[tid] = (dq == 0) ? lloc : 0.f;
+    lloc = (dq == 0) ? lloc : 0.f;
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) lloc += __shfl_xor(lloc, o2, 64);
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = lloc;
     accs[sg][dq] = acc;
     __syncthreads();
-    for (int k = 128; k > 0; k >>= 1) {
-        if (tid < k) red[tid] += red[tid + k];
-        __syncthreads();
-    }
     if (tid >= DQ) return;
-    const float L = red[0];
+    const float L = (red[4] + red[5]) + (red[6] + red[7]);
     f32x4 O = accs[0][tid];
     for (int k = 1; k < NSG; ++k) O += accs[k][tid];
 
@@ -473,6 +478,19 @@ __global__ __launch_bounds__(256) void merge_pairs(MergeParams a) {
     if (a.lse_out && lane == 0) a.lse_out[r] = M + logf(den);
 }
 
+__global__ __launch_bounds__(256) void fill_zero(uint32_t *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
+    const size_t n = bytes / 4;
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(fill_zero, dim3((unsigned)blocks), dim3(256), 0, st, (uint32_t *)p, n);
+    return hipGetLastError();
+}
+
 int row_tiles_for(int Rp) { return Rp <= 16 ? 1 : 2; }
 
 static inline unsigned blocks_for_waves(long waves) { return (unsigned)((waves + 3) / 4); }
@@ -481,7 +499,7 @@ hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hi
     if (dtype == 1) {
         dim3 grid((unsigned)((long)p.P * p.RB * p.SB)), block(256);
 #define NECTAR_ATTN_CASE(DD, RR) \
-        if (d == DD && rt == RR) { hipLaunchKernelGGL((attn_partial_mfma<DD, RR, uint16_t>), grid, block, 0, st, p); return hipGetLastError(); }
+        if (d == DD && rt == RR) { hipLaunchKernelGGL((attn_partial_mfma<DD, RR, (RR == 1 ? 2 : 1), uint16_t>), grid, block, 0, st, p); return hipGetLastError(); }
         NECTAR_ATTN_CASE(128, 1) NECTAR_ATTN_CASE(128, 2)
         NECTAR_ATTN_CASE(64, 1) NECTAR_ATTN_CASE(64, 2)
 #undef NECTAR_ATTN_CASE

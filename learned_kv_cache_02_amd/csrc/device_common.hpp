@@ -25,6 +25,12 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f3
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Loads of data streamed once per call (document cache, module weights):
+// non-temporal, so the stream does not evict data that is reused.
+template <typename T> __device__ __forceinline__ T stream_load(const T *p) {
+    return __builtin_nontemporal_load(p);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

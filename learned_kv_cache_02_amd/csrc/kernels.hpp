@@ -22,7 +22,7 @@ struct AttnParams {
     int P, S, chunk, RG, WR, WS, RB, SB;
     float *part_O;       // [P][SB][Rp][d]    unnormalised read-out
     float2 *part_ml;     // [P][SB][Rp]       (running max in log2 units, sum)
-    // Finishing in place when SB == 1 (same meaning as in CombineParams).
+    // Row finishing in place when SB == 1 (same meaning as in CombineParams).
     float *lse_out, *A_out;
     const float *x_lse, *x_A;
     void *out;
@@ -74,5 +74,6 @@ hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStre
 hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipStream_t st);
 hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st);
 hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 
 }  // namespace nectar

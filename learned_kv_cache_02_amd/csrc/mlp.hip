@@ -44,7 +44,7 @@ __device__ __forceinline__ void load_rows(MTile<D> &T, const uint16_t *W, int j0
     for (int hh = 0; hh < 2; ++hh) {
         const uint16_t *wp = W + (size_t)min(j0 + 16 * hh + c, jmax) * D;
 #pragma unroll
-        for (int kt = 0; kt < KS; ++kt) T.w1[hh][kt] = *(const u32x4 *)(wp + (4 * kt + g) * 8);
+        for (int kt = 0; kt < KS; ++kt) T.w1[hh][kt] = stream_load((const u32x4 *)(wp + (4 * kt + g) * 8));
     }
 }
 
@@ -56,7 +56,7 @@ __device__ __forceinline__ void load_tgt(MTile<D> &T, const uint16_t *W1, const 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int u = min(j0 + hslot(g, j), jmax);
-        T.w2[j] = *(const typename WRow<D>::T *)(W2t + (size_t)u * D + c * DV);
+        T.w2[j] = stream_load((const typename WRow<D>::T *)(W2t + (size_t)u * D + c * DV));
         T.bias[j] = b1[u];
     }
 }
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256) void mlp_reduce(MlpReduceParams a) {
     constexpr int DQ = D / 4;
     constexpr int NSG = 256 / DQ;
     __shared__ f32x4 accs[NSG][DQ];
-    __shared__ float red[256];
+    __shared__ float red[4];
     const int idx = blockIdx.x;
     const int h = idx / a.Rp, rho = idx - h * a.Rp;
     const int tid = threadIdx.x;
@@ -351,17 +351,15 @@ __global__ __launch_bounds__(256) void mlp_reduce(MlpReduceParams a) {
         if (dq == 0) sacc += a.part_s[base + (size_t)s * a.Rp];
     }
     accs[sg][dq] = acc;
-    red[tid] = sacc;
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) sacc += __shfl_xor(sacc, o2, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = sacc;
     __syncthreads();
-    for (int k = 128; k > 0; k >>= 1) {
-        if (tid < k) red[tid] += red[tid + k];
-        __syncthreads();
-    }
     if (tid >= DQ) return;
     f32x4 O = *(const f32x4 *)(a.b2 + (size_t)h * D + 4 * tid);
     for (int k = 0; k < NSG; ++k) O += accs[k][tid];
     *(f32x4 *)(a.A_out + o * D + 4 * tid) = O;
-    if (tid == 0) a.a_out[o] = a.bs2[h] + red[0];
+    if (tid == 0) a.a_out[o] = a.bs2[h] + ((red[0] + red[1]) + (red[2] + red[3]));
 }
 
 static inline unsigned blocks_for_waves(long waves) { return (unsigned)((waves + 3) / 4); }

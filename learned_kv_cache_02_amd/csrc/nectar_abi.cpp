@@ -64,8 +64,10 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv) {
     pl.P = P;
     pl.Rp = Rp;
     if (P == 0 || Rp == 0 || T_kv <= 0) return pl;    // nothing to attend: combine with S = 0
-    const long tiles = cdiv(T_kv, kTile);
     const bool mfma = d->dtype == NECTAR_BF16;
+    // the MFMA kernel walks keys in batches of two 32-key tiles
+    const long gran = mfma ? 2 * kTile : kTile;
+    const long tiles = cdiv(T_kv, gran);
     long units;
     if (mfma) {
         pl.RT = row_tiles_for(Rp);
@@ -79,9 +81,11 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv) {
     long S = d->splits > 0 ? d->splits : cdiv(kTargetWaves, units);
     S = S < 1 ? 1 : (S > tiles ? tiles : S);
     const long per = cdiv(tiles, S);
-    pl.chunk = (int)(per * kTile);
+    pl.chunk = (int)(per * gran);
     pl.S = (int)cdiv(tiles, per);
     pl.SB = mfma ? (int)cdiv(pl.S, pl.WS) : pl.S;
+    // [read-outs][statistics] of every per-block partial; none when one block
+    // per row group covers all keys (MFMA path finishes rows in place)
     pl.ws = pl.SB > 1 || !mfma ? (size_t)P * pl.SB * Rp * ((size_t)d->d * 4 + 8) : 0;
     return pl;
 }
@@ -149,9 +153,9 @@ nectar_status finish(hipError_t e, hipStream_t st) {
 hipError_t run_attention(const nectar_attn_desc *d, const AttnPlan &pl, const void *q, const void *k,
                          const void *v, int64_t bstride, int64_t hstride, int B, int Tq, long T_kv,
                          int causal, int q_offset, CombineParams cp, void *ws, hipStream_t st) {
-    float *part_O = (float *)ws;
-    float2 *part_ml = (float2 *)((char *)ws + (size_t)pl.P * pl.SB * pl.Rp * d->d * 4);
     const bool mfma = d->dtype == NECTAR_BF16;
+    float *part_O = (float *)ws;
+    float2 *part_ml = (float2 *)((char *)part_O + (size_t)pl.P * pl.SB * pl.Rp * d->d * 4);
     if (pl.S > 0) {
         AttnParams a{};
         a.q = q; a.k = k; a.v = v;
@@ -180,6 +184,13 @@ hipError_t run_attention(const nectar_attn_desc *d, const AttnPlan &pl, const vo
 extern "C" {
 
 int nectar_abi_version(void) { return NECTAR_ABI_VERSION; }
+
+nectar_status nectar_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (ws_bytes == 0) return NECTAR_OK;
+    if (!ws || !aligned(ws, 16)) return NECTAR_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    return finish(launch_fill_zero(ws, ws_bytes, st), st);
+}
 
 const char *nectar_status_string(nectar_status s) {
     switch (s) {

@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnectar.so")
+# NECTAR_LIBRARY may name another build of the same library (e.g. a variant
+# compiled with different flags); default: the in-tree build.
+LIB_PATH = os.environ.get("NECTAR_LIBRARY", os.path.join(_HERE, "libnectar.so"))
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libnectar.so is not built (run __graft_entry__.build() or "
@@ -67,6 +69,8 @@ _lib.nectar_merge.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P]
 _lib.nectar_status_string.argtypes = [ctypes.c_int]
 _lib.nectar_status_string.restype = ctypes.c_char_p
 _lib.nectar_abi_version.restype = ctypes.c_int
+_lib.nectar_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
+_lib.nectar_workspace_init.restype = ctypes.c_int
 for _f in ("nectar_doc_attn_exact", "nectar_module_forward", "nectar_local_attn_lse", "nectar_merge"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -118,7 +122,8 @@ def workspace(nbytes: int, device=None) -> Optional[torch.Tensor]:
     key = (dev.type, dev.index)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        # zero-filled once: the library keeps its split counters zero afterwards
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf
 
@@ -253,6 +258,11 @@ def merge(a, A, lam, A_loc, *, Hkv, out_dtype, out=None, lse_out=None):
     _check(_lib.nectar_merge(ctypes.byref(dsc), _ptr(a), _ptr(A), _ptr(lam), _ptr(A_loc), _ptr(out),
                              _ptr(lse_out), _stream()))
     return out, lse_out
+
+
+def workspace_init(buf: torch.Tensor):
+    """Zero a caller-owned workspace tensor through the library."""
+    _check(_lib.nectar_workspace_init(_ptr(buf), buf.numel() * buf.element_size(), _stream()))
 
 
 def abi_version() -> int:

@@ -68,7 +68,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     assert lib.nectar_abi_version() == 1
@@ -186,6 +186,13 @@ def test_local_validation(lib):
     big = Local(4, 1, 5000, 5000, 4999)
     assert lib.nectar_local_workspace_size(ctypes.byref(d), ctypes.byref(big)) > 0
     assert call(big) == EWORKSPACE
+
+
+def test_workspace_init_validation(lib):
+    lib.nectar_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.nectar_workspace_init(None, 0, None) == OK          # nothing to do, no launch
+    assert lib.nectar_workspace_init(None, 64, None) == EINVAL
+    assert lib.nectar_workspace_init(MIS, 64, None) == EINVAL
 
 
 def test_merge_validation(lib):

@@ -63,13 +63,30 @@ def normal(key, rows: int, cols: int) -> np.ndarray:
     return out
 
 
-def rope(x: np.ndarray, pos, base: float) -> np.ndarray:
-    """Rotate-half RoPE of x [rows][d] (float64) at positions pos [rows], float64 math."""
-    d = x.shape[-1]
+def normal_rows(key, lo: int, hi: int, cols: int) -> np.ndarray:
+    """Rows [lo, hi) of normal(key, rows, cols); lo must be a multiple of CHUNK."""
+    assert lo % CHUNK == 0
+    out = np.empty((hi - lo, cols), dtype=np.float64)
+    for c in range(lo // CHUNK, (hi + CHUNK - 1) // CHUNK):
+        a, b = c * CHUNK, min(hi, (c + 1) * CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key) + [c])))
+        g.standard_normal(out=out[a - lo:b - lo])
+    return out
+
+
+def rope_tables(pos, d: int, base: float):
+    """cos/sin [rows][d/2] of the rotate-half RoPE angles pos * base^(-2i/d), float64."""
     half = d // 2
     inv = base ** (-2.0 * np.arange(half, dtype=np.float64) / d)
     ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
-    c, s = np.cos(ang), np.sin(ang)
+    return np.cos(ang), np.sin(ang)
+
+
+def rope(x: np.ndarray, pos, base: float, tables=None) -> np.ndarray:
+    """Rotate-half RoPE of x [rows][d] (float64) at positions pos [rows], float64 math."""
+    d = x.shape[-1]
+    half = d // 2
+    c, s = tables if tables is not None else rope_tables(pos, d, base)
     x1, x2 = x[:, :half], x[:, half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=1)
 
@@ -105,17 +122,23 @@ def _heads(cfg: Config, layer: int, tid: int, H: int, rows: int, pos=None, scale
            extra=()) -> np.ndarray:
     """[H][rows][d] stored tensor; optional RoPE at `pos` and scaling."""
     out = np.empty((H, rows, cfg.d), dtype=np.float32 if cfg.dtype == "f32" else np.uint16)
+    tables = rope_tables(pos, cfg.d, cfg.rope_base) if pos is not None else None
 
-    def one(h):
-        x = normal((cfg.seed, layer, tid, h) + tuple(extra), rows, cfg.d)
-        if pos is not None:
-            x = rope(x, pos, cfg.rope_base)
+    def one(h, lo, hi):
+        # rows [lo, hi) of head h; chunk-aligned, so values do not depend on the split
+        x = normal_rows((cfg.seed, layer, tid, h) + tuple(extra), lo, hi, cfg.d)
+        if tables is not None:
+            x = rope(x, None, cfg.rope_base, (tables[0][lo:hi], tables[1][lo:hi]))
         if scale != 1.0:
             x = x * scale
-        out[h] = store(x, cfg.dtype)
+        out[h, lo:hi] = store(x, cfg.dtype)
 
-    for h in range(H):
-        one(h)
+    jobs = [(h, lo, min(rows, lo + CHUNK)) for h in range(H) for lo in range(0, rows, CHUNK)]
+    if len(jobs) <= 1:
+        for j in jobs:
+            one(*j)
+    else:
+        list(_pool().map(lambda j: one(*j), jobs))
     return out
 
 

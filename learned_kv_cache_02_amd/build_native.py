@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnectar.so")
-SOURCES = ["attn.hip", "mlp.hip", "nectar_abi.cpp"]
+SOURCES = ["attn.hip", "mlp.hip", "mlp_prefill.hip", "nectar_abi.cpp"]
 
 # Packed fp32 VALU ops are kept out of every HIP object.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",

@@ -80,10 +80,42 @@ __device__ __forceinline__ float group4_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// GELU in the erf form, x * Phi(x) (HIP device erff).
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+// GELU in the erf form, x * Phi(x) with Phi(x) = (1 + erf(x / sqrt 2)) / 2 and
+// erf from Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26
+// (|error| <= 1.5e-7): erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2),
+// t = 1 / (1 + p z), z >= 0, odd extension.  Branch-free: one reciprocal, one
+// exponential and nine arithmetic operations.
+__device__ __forceinline__ float gelu_erf(float x) {
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
+    float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+    p = __builtin_fmaf(p, t, 1.421413741f);
+    p = __builtin_fmaf(p, t, -0.284496736f);
+    p = __builtin_fmaf(p, t, 0.254829592f);
+    const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+    const float erfc_half = 0.5f * (p * t) * e;                  // (1 - erf(z)) / 2
+    return x * (x >= 0.f ? 1.0f - erfc_half : erfc_half);        // x * Phi(x)
+}
+// SiLU, x * sigmoid(x) = x / (1 + e^-x) (hardware exp2 and reciprocal).
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+}
 
-__device__ __forceinline__ float activation(int act, float x) { return act == 1 ? silu(x) : gelu_erf(x); }
+// GELU in the tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) =
+// x * sigmoid(1.5957691 x (1 + 0.044715 x^2)) (Hendrycks & Gimpel's
+// approximation); it differs from the erf form by at most 4.8e-4.
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float v = x * __builtin_fmaf(x * x, -0.0713548162726f * kLog2e, -1.5957691216057308f * kLog2e);
+    return x * __builtin_amdgcn_rcpf(1.0f + fast_exp2(v));
+}
+
+// Activation fixed at compile time (0: GELU erf form, 1: SiLU, 2: GELU tanh
+// form, the values of nectar_act), so only one is evaluated.
+template <int ACT> __device__ __forceinline__ float act_fn(float x) {
+    return ACT == 1 ? silu(x) : (ACT == 2 ? gelu_tanh(x) : gelu_erf(x));
+}
+__device__ __forceinline__ float activation(int act, float x) {
+    return act == 1 ? silu(x) : (act == 2 ? gelu_tanh(x) : gelu_erf(x));
+}
 
 }  // namespace nectar

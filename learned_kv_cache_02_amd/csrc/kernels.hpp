@@ -73,6 +73,8 @@ hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hi
 hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipStream_t st);
 hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st);
+// Batched-prefill MLP (bf16, d = 128): one pass, no workspace.
+hipError_t launch_mlp_prefill(const MlpParams &p, hipStream_t st);
 hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 

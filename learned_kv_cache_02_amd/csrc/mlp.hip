@@ -86,8 +86,8 @@ __device__ __forceinline__ void transpose_w(const MTile<D> &T, u32x4 (&vt)[D / 1
     }
 }
 
-template <int D, int RT>
-__device__ __forceinline__ void tgt_tile(const MTile<D> &T, int j0, int Ht, int act,
+template <int D, int RT, int ACT>
+__device__ __forceinline__ void tgt_tile(const MTile<D> &T, int j0, int Ht,
                                          const u32x4 (&qv)[RT][D / 32], int g, f32x4 (&O)[RT][D / 16]) {
     constexpr int KS = D / 32, DV = D / 16;
     u32x4 vt[DV];
@@ -103,8 +103,8 @@ __device__ __forceinline__ void tgt_tile(const MTile<D> &T, int j0, int Ht, int 
         float hv[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            hv[r] = activation(act, z0[r] + T.bias[r]);
-            hv[4 + r] = activation(act, z1[r] + T.bias[4 + r]);
+            hv[r] = act_fn<ACT>(z0[r] + T.bias[r]);
+            hv[4 + r] = act_fn<ACT>(z1[r] + T.bias[4 + r]);
         }
         if (j0 + 32 > Ht) {
 #pragma unroll
@@ -118,8 +118,8 @@ __device__ __forceinline__ void tgt_tile(const MTile<D> &T, int j0, int Ht, int 
     }
 }
 
-template <int D, int RT>
-__device__ __forceinline__ void score_tile(const MTile<D> &T, int j0, int Hs, int act,
+template <int D, int RT, int ACT>
+__device__ __forceinline__ void score_tile(const MTile<D> &T, int j0, int Hs,
                                            const u32x4 (&qv)[RT][D / 32], int g, float (&sc)[RT]) {
     constexpr int KS = D / 32;
 #pragma unroll
@@ -134,7 +134,7 @@ __device__ __forceinline__ void score_tile(const MTile<D> &T, int j0, int Hs, in
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float z = (j < 4 ? z0[j] : z1[j - 4]) + T.bias[j];
-            float y = activation(act, z) * T.ws[j];
+            float y = act_fn<ACT>(z) * T.ws[j];
             if (j0 + hslot(g, j) >= Hs) y = 0.f;
             acc += y;
         }
@@ -142,7 +142,7 @@ __device__ __forceinline__ void score_tile(const MTile<D> &T, int j0, int Hs, in
     }
 }
 
-template <int D, int RT>
+template <int D, int RT, int ACT>
 __global__ __launch_bounds__(256) void mlp_partial_mfma(MlpParams a) {
     constexpr int KS = D / 32, DV = D / 16;
     __shared__ f32x4 fold_O[2][RT * DV][64];
@@ -200,8 +200,8 @@ __global__ __launch_bounds__(256) void mlp_partial_mfma(MlpParams a) {
         else load_score<D>(T, Ws, ws2, bs, js_lo + 32 * (i - ntt), a.Hs - 1, g, c);
     };
     auto run = [&](const MTile<D> &T, int i) {
-        if (i < ntt) tgt_tile<D, RT>(T, jt_lo + 32 * i, a.Ht, a.act, qv, g, O);
-        else score_tile<D, RT>(T, js_lo + 32 * (i - ntt), a.Hs, a.act, qv, g, sc);
+        if (i < ntt) tgt_tile<D, RT, ACT>(T, jt_lo + 32 * i, a.Ht, qv, g, O);
+        else score_tile<D, RT, ACT>(T, js_lo + 32 * (i - ntt), a.Hs, qv, g, sc);
     };
     if (ntiles > 0) {
         MTile<D> t0, t1;
@@ -368,7 +368,11 @@ hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipS
     if (dtype == 1) {
         dim3 grid((unsigned)((long)p.Hkv * p.RB * p.SB)), block(256);
 #define NECTAR_MLP_CASE(DD, RR) \
-        if (d == DD && rt == RR) { hipLaunchKernelGGL((mlp_partial_mfma<DD, RR>), grid, block, 0, st, p); return hipGetLastError(); }
+        if (d == DD && rt == RR) { \
+            if (p.act == 1) hipLaunchKernelGGL((mlp_partial_mfma<DD, RR, 1>), grid, block, 0, st, p); \
+            else if (p.act == 2) hipLaunchKernelGGL((mlp_partial_mfma<DD, RR, 2>), grid, block, 0, st, p); \
+            else hipLaunchKernelGGL((mlp_partial_mfma<DD, RR, 0>), grid, block, 0, st, p); \
+            return hipGetLastError(); }
         NECTAR_MLP_CASE(128, 1) NECTAR_MLP_CASE(128, 2)
         NECTAR_MLP_CASE(64, 1) NECTAR_MLP_CASE(64, 2)
 #undef NECTAR_MLP_CASE

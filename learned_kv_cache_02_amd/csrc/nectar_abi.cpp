@@ -93,13 +93,21 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv) {
 struct MlpPlan {
     int Rp = 0, RT = 0, RG = 0, S = 0, ct = kTile, cs = kTile;
     int WR = 1, WS = 1, RB = 0, SB = 0;
+    bool prefill = false;
     size_t ws = 0;
 };
+
+// Rows per KV head from which the LDS-staged batched kernel is used.
+constexpr int kPrefillRows = 2048;
 
 MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs) {
     MlpPlan pl;
     pl.Rp = d->R * (d->Hq / d->Hkv);
     if (pl.Rp == 0) return pl;
+    if (d->dtype == NECTAR_BF16 && d->d == 128 && pl.Rp >= kPrefillRows && d->splits == 0) {
+        pl.prefill = true;
+        return pl;
+    }
     const bool mfma = d->dtype == NECTAR_BF16;
     long units;
     if (mfma) {
@@ -231,7 +239,8 @@ nectar_status nectar_doc_attn_exact(const nectar_attn_desc *desc, int64_t n, con
 static nectar_status check_module(const nectar_attn_desc *desc, const nectar_module *m) {
     if (!m) return NECTAR_EINVAL;
     if (m->kind == NECTAR_MODULE_MLP) {
-        if (m->act != NECTAR_ACT_GELU && m->act != NECTAR_ACT_SILU) return NECTAR_EINVAL;
+        if (m->act != NECTAR_ACT_GELU && m->act != NECTAR_ACT_SILU && m->act != NECTAR_ACT_GELU_TANH)
+            return NECTAR_EINVAL;
         if (m->Ht < 0 || m->Hs < 0) return NECTAR_EINVAL;
         if (!m->b2 || !m->bs2 || !aligned(m->b2, 4) || !aligned(m->bs2, 4)) return NECTAR_EINVAL;
         if (m->Ht > 0 && (!tensor_ok(m->W1) || !tensor_ok(m->W2t) || !m->b1 || !aligned(m->b1, 4)))
@@ -280,6 +289,15 @@ nectar_status nectar_module_forward(const nectar_attn_desc *desc, const nectar_m
     }
     const MlpPlan pl = plan_mlp(desc, m->Ht, m->Hs);
     if ((s = check_ws(pl.ws, ws, ws_bytes)) != NECTAR_OK) return s;
+    if (pl.prefill) {
+        MlpParams a{};
+        a.q = q; a.W1 = m->W1; a.W2t = m->W2t; a.Ws = m->Ws; a.ws2 = m->ws2;
+        a.b1 = m->b1; a.bs = m->bs; a.b2 = m->b2; a.bs2 = m->bs2;
+        a.Hq = desc->Hq; a.G = desc->Hq / desc->Hkv; a.Hkv = desc->Hkv; a.Rp = pl.Rp;
+        a.Ht = m->Ht; a.Hs = m->Hs; a.act = m->act;
+        a.a_out = a_out; a.A_out = A_out;
+        return finish(launch_mlp_prefill(a, st), st);
+    }
     float *part_O = (float *)ws;
     float *part_s = (float *)((char *)ws + (size_t)desc->Hkv * pl.SB * pl.Rp * desc->d * 4);
     const bool mfma = desc->dtype == NECTAR_BF16;

@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16 = 0, 1
 MLP, KVPAIR = 0, 1
-GELU, SILU = 0, 1
+GELU, SILU, GELU_TANH = 0, 1, 2
 STATUS = {0: "NECTAR_OK", 1: "NECTAR_EINVAL", 2: "NECTAR_EUNSUPPORTED", 3: "NECTAR_EWORKSPACE",
           4: "NECTAR_EHIP"}
 

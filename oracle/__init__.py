@@ -22,7 +22,7 @@ _SRC = os.path.join(_HERE, "nectar_oracle.c")
 _LIB = os.path.join(_HERE, "libnectar_oracle.so")
 
 DT = {"f32": 0, "bf16": 1, "f64": 2}
-ACT = {"gelu": 0, "silu": 1}
+ACT = {"gelu": 0, "silu": 1, "gelu_tanh": 2}
 
 
 def build(force: bool = False) -> str:
@@ -55,6 +55,8 @@ def _L():
         lib.oracle_gelu.restype = D
         lib.oracle_silu.argtypes = [D]
         lib.oracle_silu.restype = D
+        lib.oracle_gelu_tanh.argtypes = [D]
+        lib.oracle_gelu_tanh.restype = D
         _lib = lib
     return _lib
 
@@ -188,3 +190,7 @@ def gelu(x: float) -> float:
 
 def silu(x: float) -> float:
     return _L().oracle_silu(float(x))
+
+
+def gelu_tanh(x: float) -> float:
+    return _L().oracle_gelu_tanh(float(x))

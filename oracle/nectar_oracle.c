@@ -20,7 +20,8 @@
  *     A = softmax(W q / sqrt(d))^T Z  -- exact attention over (W, Z, p).
  *   - section 2.4, Eq. (3.6): MLP form.  The workloads fix one hidden layer
  *     with GELU: A = W2 GELU(W1 q + b1) + b2, a = w2 . GELU(Ws q + bs) + bs2.
- *     SiLU is provided as the activation Eq. (3.6) itself names.
+ *     SiLU is provided as the activation Eq. (3.6) itself names, and the tanh
+ *     form of GELU as the common faster variant.
  *
  * Precision: every input element is widened exactly to double (bf16 bits are
  * shifted into an fp32 pattern; fp32 widens exactly); every sum is a plain
@@ -41,6 +42,7 @@
  *   b1 [Hkv][Ht], b2 [Hkv][d], bs [Hkv][Hs], bs2 [Hkv]  (double)
  *   query head hq reads KV head hq / (Hq / Hkv).
  */
+#define _DEFAULT_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -48,7 +50,7 @@
 #include <omp.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
-enum { OR_GELU = 0, OR_SILU = 1 };
+enum { OR_GELU = 0, OR_SILU = 1, OR_GELU_TANH = 2 };
 
 /* Read element i of an array of the given element type, widened to double. */
 static double ld(const void *p, int dt, size_t i)
@@ -70,8 +72,18 @@ static void set_threads(int nthreads)
 
 double oracle_gelu(double x) { return x * 0.5 * (1.0 + erf(x / sqrt(2.0))); }
 double oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+/* tanh form of GELU: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+double oracle_gelu_tanh(double x)
+{
+    return 0.5 * x * (1.0 + tanh(sqrt(2.0 / M_PI) * (x + 0.044715 * x * x * x)));
+}
 
-static double act_fn(int act, double x) { return act == OR_SILU ? oracle_silu(x) : oracle_gelu(x); }
+static double act_fn(int act, double x)
+{
+    if (act == OR_SILU) return oracle_silu(x);
+    if (act == OR_GELU_TANH) return oracle_gelu_tanh(x);
+    return oracle_gelu(x);
+}
 
 /*
  * Attention of one query vector over a set of key/value rows, returning the
@@ -261,7 +273,7 @@ int oracle_mlp(int dt, int R, int Hq, int Hkv, int d, int Ht, int Hs, int act,
                double *a_out, double *A_out, int nthreads)
 {
     if (!valid_dt(dt) || !shape_ok(R, Hq, Hkv, d) || Ht < 0 || Hs < 0) return 1;
-    if (act != OR_GELU && act != OR_SILU) return 1;
+    if (act != OR_GELU && act != OR_SILU && act != OR_GELU_TANH) return 1;
     if (!toks) ntok = R;
     const int G = Hq / Hkv;
     set_threads(nthreads);

@@ -14,6 +14,8 @@ from learned_kv_cache_02_amd import configs, synth
 
 pytestmark = pytest.mark.gpu
 
+ACTS = {"gelu": 0, "silu": 1, "gelu_tanh": 2}    # nectar_act values
+
 
 @pytest.fixture(scope="module")
 def nx(gpu):
@@ -139,7 +141,7 @@ def _mlp_oracle(q, P, dt, Hq, Hkv, act):
 
 @pytest.mark.parametrize("R,Hq,Hkv,Ht,Hs", [(5, 14, 2, 100, 70), (1, 32, 8, 256, 96), (20, 8, 2, 64, 33),
                                              (3, 4, 1, 0, 40), (3, 4, 1, 50, 0), (10, 16, 4, 300, 200)])
-@pytest.mark.parametrize("act", ["gelu", "silu"])
+@pytest.mark.parametrize("act", ["gelu", "silu", "gelu_tanh"])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_mlp_bf16(nx, R, Hq, Hkv, Ht, Hs, act, splits):
     d = 128
@@ -148,11 +150,27 @@ def test_mlp_bf16(nx, R, Hq, Hkv, Ht, Hs, act, splits):
     g = _rng(8, R, Hq, Ht, Hs)
     q = _bf(g.standard_normal((R, Hq, d)))
     P = _mlp_np(g, Hkv, d, Ht, Hs, "bf16")
-    a, A = nx.module_forward(dev(q), _mlp_dev(nx, P, nx.GELU if act == "gelu" else nx.SILU), Hkv,
-                             splits=splits)
+    a, A = nx.module_forward(dev(q), _mlp_dev(nx, P, ACTS[act]), Hkv, splits=splits)
     ea, eA = _mlp_oracle(q, P, "bf16", Hq, Hkv, act)
     check("a", host(a), ea, ATOL_LSE_BF16)
     check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu", "gelu_tanh"])
+@pytest.mark.parametrize("R,Hq,Hkv,Ht,Hs", [(300, 28, 4, 100, 70), (600, 32, 8, 256, 33), (520, 8, 2, 7680, 0)])
+def test_mlp_batched_prefill_bf16(nx, R, Hq, Hkv, Ht, Hs, act):
+    """Row counts large enough for the LDS-staged batched kernel (ragged rows and units)."""
+    d = 128
+    print("case mlp prefill R=%d Hq=%d Hkv=%d Ht=%d Hs=%d %s" % (R, Hq, Hkv, Ht, Hs, act), flush=True)
+    g = _rng(12, R, Hq, Ht, Hs)
+    q = _bf(g.standard_normal((R, Hq, d)))
+    P = _mlp_np(g, Hkv, d, Ht, Hs, "bf16")
+    a, A = nx.module_forward(dev(q), _mlp_dev(nx, P, ACTS[act]), Hkv)
+    toks = np.unique(np.concatenate([[0, R - 1], g.choice(R, 40, replace=False)])).astype(np.int32)
+    ea, eA = oracle.mlp(q, P["W1"], P["b1"], P["W2t"], P["b2"], P["Ws"], P["bs"], P["ws2"], P["bs2"],
+                        dt="bf16", Hq=Hq, Hkv=Hkv, toks=toks, act=act)
+    check("a", host(a)[toks], ea, ATOL_LSE_BF16)
+    check("A", host(A)[toks], eA, ATOL_OUT_BF16, REL_L2_BF16)
 
 
 def test_mlp_d64_and_f32(nx):

@@ -259,6 +259,21 @@ def test_p9_gelu_textbook_values():
     assert abs(oracle.gelu(-12.0)) < 1e-15
 
 
+def test_p9_gelu_tanh_form():
+    # the tanh form: odd part equals x/2, zero at zero, identity / zero tails, and within
+    # 4.8e-4 of the erf form everywhere (the known bound of this approximation)
+    xs = np.linspace(-8, 8, 4001)
+    for x in xs[::50]:
+        assert abs((oracle.gelu_tanh(x) - oracle.gelu_tanh(-x)) - x) < 1e-14
+    assert oracle.gelu_tanh(0.0) == 0.0
+    assert abs(oracle.gelu_tanh(10.0) - 10.0) < 1e-12 and abs(oracle.gelu_tanh(-10.0)) < 1e-12
+    dev = max(abs(oracle.gelu_tanh(x) - oracle.gelu(x)) for x in xs)
+    assert 1e-4 < dev < 4.8e-4
+    # tanh(1.5957691... * 1.044715 / 2) route at x = 1 against math.tanh written out
+    u = math.sqrt(2 / math.pi) * (1 + 0.044715)
+    assert abs(oracle.gelu_tanh(1.0) - 0.5 * (1 + math.tanh(u))) < 1e-15
+
+
 def test_p9_silu_textbook_values():
     assert oracle.silu(0.0) == 0.0
     assert abs(oracle.silu(1.0) - 0.7310585786300049) < 1e-15      # 1 / (1 + e^-1)

@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--only", choices=["step", "exact", "nectar", "doc"], default=None,
                     help="time only one graph (for profiling runs)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the batched-prefill MLP measurement")
     return ap.parse_args()
 
 
@@ -232,9 +234,61 @@ def main():
                                      "%d algorithmic bytes per launch" % (us, doc_bytes)}
         res["module_roofline_hint"] = {"bytes_per_launch": mlp_bytes}
 
+    if not args.no_prefill and args.only is None:
+        del reps, graphs
+        torch.cuda.empty_cache()
+        res["prefill_mlp"] = prefill_mlp(torch, np, nectar, configs, synth, dev)
+
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(cfg, q_h, K_h, V_h, Kl_h, Vl_h, P_h, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 flop/clk, dense
+
+
+def prefill_mlp(torch, np, nectar, configs, synth, dev):
+    """MFMA utilisation of the module forward at batched prefill: the 28-layer
+    Qwen2.5-7B-1M-shaped stack's 16 x 1,024 query tokens x 28 heads through the
+    rho = 10 % and 1 % MLPs (GELU erf form and tanh form), 4 layer replicas per graph."""
+    cfg = configs.C3
+
+    def up(x):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
+
+    q = up(synth.queries(cfg))
+    a = torch.empty((cfg.R, cfg.Hq), dtype=torch.float32, device=dev)
+    A = torch.empty((cfg.R, cfg.Hq, cfg.d), dtype=torch.float32, device=dev)
+    out = {}
+    for which in (1, 0):
+        P = synth.mlp_params(cfg, 0, which)
+        m = cfg.mlps[which]
+        flops = cfg.R * cfg.Hq * (4 * cfg.d * m.Ht + 2 * cfg.d * m.Hs + 2 * m.Hs)
+        for act, name in ((nectar.GELU, "gelu_erf"), (nectar.GELU_TANH, "gelu_tanh")):
+            mods = [nectar.MLPModule(*(up(P[k]) for k in ("W1", "b1", "W2t", "b2", "Ws", "bs", "ws2", "bs2")),
+                                     act=act) for _ in range(4)]
+            nectar.module_forward(q, mods[0], cfg.Hkv, a_out=a, A_out=A)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(8):
+                    nectar.module_forward(q, mods[i % 4], cfg.Hkv, a_out=a, A_out=A)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(2):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 16
+            tf = flops / ms / 1e9
+            out["rho%d_%s" % (10 if which == 1 else 1, name)] = {
+                "mlp": "%d/%d" % (m.Ht, m.Hs), "ms_per_layer": ms, "tflops": tf,
+                "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops_per_layer": flops}
+            del mods
+    return out
 
 
 def cpu_baseline(cfg, q, K, V, Kl, Vl, P, budget_s):

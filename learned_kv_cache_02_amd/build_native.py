@@ -9,7 +9,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnectar.so")
-SOURCES = ["attn.hip", "mlp.hip", "mlp_prefill.hip", "nectar_abi.cpp"]
+SOURCES = ["attn.hip", "attn_lds.hip", "mlp.hip", "mlp_prefill.hip", "nectar_abi.cpp"]
+# Per-source code-generation options: the LDS-staged attention keeps its MFMA
+# accumulators in ordinary VGPRs (with accumulation registers the compiler
+# copies them back and forth around the softmax on every tile).
+SOURCE_FLAGS = {"attn_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # Packed fp32 VALU ops are kept out of every HIP object.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
@@ -25,7 +29,8 @@ def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
     inc = ["-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
     for src in SOURCES:
         obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + ".o")
-        cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(src, []) + list(extra_flags) + inc +
+               ["-c", os.path.join(CSRC, src), "-o", obj])
         if src.endswith(".cpp"):
             cmd.insert(1, "-x")
             cmd.insert(2, "hip")

@@ -16,8 +16,13 @@
 //       load instruction reads four whole key rows.
 // The S^T layout puts one query row per lane column, so every row statistic
 // (max, sum, rescale) stays in the lane; only the tile max crosses the four
-// 16-lane groups.  Tiles are double-buffered in registers so the next tile's
-// 16 KB is in flight while the current one is computed.
+// 16-lane groups.  A wave issues the loads of a batch of SUB tiles before it
+// uses any of them, and at RT == 1 two waves share each SIMD, so one wave's
+// loads are in flight while the other computes.
+//
+// This register-direct form serves a few rows per KV head (decode); with more
+// rows (RT > 1 here) every row group re-streams the cache, which the
+// LDS-staged kernel in attn_lds.hip avoids for d = 128.
 //
 // A block's four waves cover WR row groups x WS key splits; the WS splits of a
 // row group are folded in LDS (log-sum-exp rescale, then a sum), so each block
@@ -26,8 +31,7 @@
 // attn_combine folds the per-block partials.  (A last-arriving-block fold was
 // measured slower: the agent-scope fences it needs write back and invalidate
 // the XCD's L2 on every block.)
-#include "device_common.hpp"
-#include "kernels.hpp"
+#include "attn_common.hpp"
 
 namespace nectar {
 
@@ -40,9 +44,6 @@ template <int D> struct KVTile {
     u32x4 k[2][KS];
     typename VRow<D>::T v[8];
 };
-
-// Key held by P slot j of lane group g within a 32-key tile.
-__device__ __forceinline__ int slot_key(int g, int j) { return 16 * (j >> 2) + 4 * g + (j & 3); }
 
 template <int D>
 __device__ __forceinline__ void load_kv_tile(KVTile<D> &T, const uint16_t *kb, const uint16_t *vb,
@@ -117,54 +118,6 @@ __device__ __forceinline__ void attend_tile(const KVTile<D> &T, int k0, const u3
         for (int mm = 0; mm < DV; ++mm) {
             O[rt][mm] *= alpha;
             O[rt][mm] = mfma16(vt[mm], P, O[rt][mm]);
-        }
-    }
-}
-
-// Output row index of row rho of problem p.
-__device__ __forceinline__ size_t out_row(int p, int rho, int Hkv, int G, int Tq, int Hq) {
-    const int b = p / Hkv, h = p - b * Hkv;
-    const int t = rho / G, gg = rho - t * G;
-    return (size_t)(b * Tq + t) * Hq + h * G + gg;
-}
-
-// Finish one row held in lane layout: lane (g, c) owns dims DV*(4g+r)+mm of the
-// row; m (log2 units) and l are the row's folded statistics.
-template <int D, typename OutT>
-__device__ __forceinline__ void finish_row_lanes(const AttnParams &a, size_t o, int g, float m, float l,
-                                                 const f32x4 (&O)[D / 16]) {
-    constexpr int DV = D / 16;
-    const bool empty = (m == -INFINITY);
-    const float inv = empty ? 0.f : 1.0f / l;
-    if (a.lse_out && g == 0) a.lse_out[o] = empty ? -INFINITY : (m + log2f(l)) * kLn2;
-    if (a.A_out) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int m4 = 0; m4 < DV; m4 += 4) {
-                f32x4 v = {O[m4][r] * inv, O[m4 + 1][r] * inv, O[m4 + 2][r] * inv, O[m4 + 3][r] * inv};
-                *(f32x4 *)(a.A_out + o * D + DV * (4 * g + r) + m4) = v;
-            }
-    }
-    if (a.x_lse) {
-        const float mx = a.x_lse[o] * kLog2e;
-        const float Mt = fmaxf(m, mx);
-        const bool none = (Mt == -INFINITY);
-        const float wl = (none || empty) ? 0.f : exp2f(m - Mt);
-        const float wx = none ? 0.f : exp2f(mx - Mt);
-        const float Lt = wl * l + wx;
-        const float it = none ? 0.f : 1.0f / Lt;
-        if (a.out_lse && g == 0) a.out_lse[o] = none ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
-        if (a.out) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float ov[DV];
-                const float *xa = a.x_A + o * D + DV * (4 * g + r);
-#pragma unroll
-                for (int mm = 0; mm < DV; ++mm) ov[mm] = none ? 0.f : (wl * O[mm][r] + wx * xa[mm]) * it;
-#pragma unroll
-                for (int mm = 0; mm < DV; ++mm) st_out<OutT>((OutT *)a.out, o * D + DV * (4 * g + r) + mm, ov[mm]);
-            }
         }
     }
 }

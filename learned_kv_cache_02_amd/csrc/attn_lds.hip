@@ -1,0 +1,270 @@
+// Split-K softmax attention for many query rows per KV head (d = 128, bf16):
+// the exact document path at batched decode and prefill (Eq. (3.1) of the
+// Nectar notes), the Quadrature module and the causal local part (section
+// 2.2) when a KV head serves more than 16 query rows.
+//
+// A block of NW waves owns 16 * NW * RT consecutive query rows of one problem
+// (KV head, and question for per-question caches) and one key range; every
+// wave holds RT tiles of 16 rows (NW = 8 puts two waves on each SIMD, so one
+// wave's softmax overlaps the other's matrix work).  The block streams its keys through LDS in
+// stages of 64 keys (16 KB of K, 16 KB of V), three stages in a ring: each
+// lane copies 16-byte pieces from HBM straight into LDS (global_load_lds, no
+// register staging), two stages ahead of use, so every key is read from HBM
+// once per block whatever the number of rows.
+//
+// LDS layout of a stage: one 256-byte row per key, the row's 16-byte piece j
+// stored at position j ^ (key & 15).  The MFMA operand reads below (16 lanes
+// reading the same piece of 16 consecutive keys, or 16 pieces of one key)
+// then touch 16 distinct positions, i.e. every bank once.
+//
+// Per 32-key tile a wave reads its operands from LDS once and reuses them for
+// its RT row tiles:
+//   S^T (32 keys x 16 rows) = K_tile . Q^T    (K rows as MFMA A operands)
+//   P = exp2(S * scale * log2e - m) -> bf16  (row statistics in the lane)
+//   O^T (128 x 16 rows) += V_tile^T . P^T    (V transposed inside the lane)
+// The running max is moved only when a score exceeds it by more than
+// kSlack (log2 units): until then the old reference stays, so the O rescale is
+// skipped; P <= 2^kSlack keeps every sum finite and the result is unchanged
+// (the same reference max is used for the numerator and the denominator).
+#include "attn_common.hpp"
+
+namespace nectar {
+
+namespace {
+
+constexpr int kD = 128, kKS = 4, kDV = 8;
+constexpr int kStageKeys = 64;
+constexpr int kStages = 3;
+constexpr int kPieces = kD * 2 / 16;            // 16-byte pieces per key row
+constexpr float kSlack = 8.0f;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt low bits [3:0], high bits [15:14]; expcnt and lgkmcnt at their maxima).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier that the compiler may not move memory operations across
+// (the bare builtin is not a memory barrier to the optimiser) and that adds
+// no waits of its own: the LDS copies are waited for explicitly above it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+}  // namespace
+
+template <int NW, int RT>
+__global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
+    constexpr int kKeysPerWave = kStageKeys / NW;       // keys of a stage one wave copies
+    constexpr int kCopies = kKeysPerWave / 4;           // copy instructions per wave, K and V each
+    static_assert(kCopies >= 1 && kCopies * 4 * NW == kStageKeys, "stage split");
+    // Three stage buffers, [0: K, 1: V][key * 16 + position].  They are
+    // separate variables (not one indexed array) so the compiler can tell the
+    // copies into one buffer from reads of another and does not make every
+    // read wait for all copies in flight.
+    __shared__ u32x4 kv_a[2][kStageKeys * kPieces], kv_b[2][kStageKeys * kPieces], kv_c[2][kStageKeys * kPieces];
+
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, c = lane & 15;
+    // Block -> (problem p, key split sb, row block rb).  Row blocks of one
+    // (p, sb) read the same keys; with xcd_group they are placed 8 ids apart,
+    // which the dispatcher sends to the same XCD (ids go round-robin over the
+    // 8 XCDs), so the second read of each stage hits that XCD's L2.
+    int u, rb;
+    if (a.xcd_group) {
+        const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+        rb = y % a.RB;
+        u = (y / a.RB) * 8 + x;
+    } else {
+        u = blockIdx.x / a.RB;
+        rb = blockIdx.x - u * a.RB;
+    }
+    const int p = u / a.SB, sb = u - p * a.SB;
+    const int b = p / a.Hkv, h = p - b * a.Hkv;
+    const uint16_t *kb = (const uint16_t *)a.k + b * a.kv_bstride + h * a.kv_hstride;
+    const uint16_t *vb = (const uint16_t *)a.v + b * a.kv_bstride + h * a.kv_hstride;
+    constexpr int kBlockRows = 16 * NW * RT;
+
+    u32x4 qv[RT][kKS];
+    int lim[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int rho = rb * kBlockRows + (w * RT + rt) * 16 + c;
+        if (rho < a.Rp) {
+            const int tk = rho / a.G, gg = rho - tk * a.G;
+            const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(b * a.Tq + tk) * a.Hq + h * a.G + gg) * kD;
+#pragma unroll
+            for (int kt = 0; kt < kKS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
+            int L = a.T_kv;
+            if (a.causal) L = min(L, a.q_offset + tk + 1);
+            lim[rt] = max(L, 0);
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < kKS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
+            lim[rt] = 0;
+        }
+    }
+    // Key limit of the whole block (uniform): the causal limit grows with the
+    // token, so the block's last valid row has the largest one.
+    int blim = a.T_kv;
+    if (a.causal) {
+        const int last = min(a.Rp, (rb + 1) * kBlockRows) - 1;
+        blim = min(blim, a.q_offset + last / a.G + 1);
+    }
+    blim = max(blim, 0);
+    const int k_lo = sb * a.chunk;
+    const int k_hi = min(k_lo + a.chunk, blim);
+    const int nst = k_hi > k_lo ? (k_hi - k_lo + kStageKeys - 1) / kStageKeys : 0;
+    const int kmax = a.T_kv - 1;
+
+    // Stage i: wave w copies its kKeysPerWave keys of K and of V, four keys
+    // (1 KB of LDS, lane order) per instruction; lane l fills position l & 15
+    // of key r = kKeysPerWave * w + 4u + (l >> 4) with that key's piece
+    // (l & 15) ^ (r & 15).
+    auto issue = [&](int i, u32x4 (&dst)[2][kStageKeys * kPieces]) {
+        const int key0 = k_lo + i * kStageKeys;
+#pragma unroll
+        for (int u = 0; u < kCopies; ++u) {
+            const int r0 = kKeysPerWave * w + 4 * u, r = r0 + (lane >> 4);
+            const int key = min(key0 + r, kmax);
+            const int piece = (lane & 15) ^ (r & 15);
+            const size_t off = (size_t)key * kD + piece * 8;
+            __builtin_amdgcn_global_load_lds((const void *)(kb + off), (lds_void *)&dst[0][r0 * kPieces],
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(vb + off), (lds_void *)&dst[1][r0 * kPieces],
+                                             16, 0, 0);
+        }
+    };
+
+    f32x4 O[RT][kDV];
+    float m[RT], l[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        m[rt] = -INFINITY;
+        l[rt] = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < kDV; ++mm) O[rt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Stage i is read from buffer i % 3; its copies are issued while stage
+    // i - 2 is computed (two stages ahead).
+    auto step = [&](int i, const u32x4 (&cur)[2][kStageKeys * kPieces], u32x4 (&ahead)[2][kStageKeys * kPieces]) {
+        // stage i has landed once at most the next stage's copies are pending
+        if (i + 1 < nst) wait_vmcnt<2 * kCopies>();
+        else wait_vmcnt<0>();
+        stage_barrier();
+        if (i + 2 < nst) issue(i + 2, ahead);
+        const u32x4 *Ks = cur[0];
+        const u32x4 *Vs = cur[1];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int kbase = k_lo + i * kStageKeys + 32 * sub;
+            u32x4 kop[2][kKS];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int r = 32 * sub + 16 * hh + c;
+#pragma unroll
+                for (int kt = 0; kt < kKS; ++kt) kop[hh][kt] = Ks[r * kPieces + ((4 * kt + g) ^ c)];
+            }
+            u32x4 vr[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = 32 * sub + slot_key(g, j);
+                vr[j] = Vs[r * kPieces + (c ^ (r & 15))];
+            }
+            // vt[mm] slot j = V[key(g, j)][8c + mm]
+            u32x4 vt[kDV];
+#pragma unroll
+            for (int mm = 0; mm < kDV; ++mm) {
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2) {
+                    const uint32_t a0 = vr[2 * q2][mm >> 1], a1 = vr[2 * q2 + 1][mm >> 1];
+                    vt[mm][q2] = (mm & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < kKS; ++kt) {
+                    s0 = mfma16(kop[0][kt], qv[rt][kt], s0);
+                    s1 = mfma16(kop[1][kt], qv[rt][kt], s1);
+                }
+                float sv[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) { sv[r] = s0[r] * a.sl2; sv[4 + r] = s1[r] * a.sl2; }
+                if (kbase + 32 > lim[rt]) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (kbase + slot_key(g, j) >= lim[rt]) sv[j] = -INFINITY;
+                }
+                float mt = sv[0];
+#pragma unroll
+                for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
+                // move the reference max only when some score passes it by kSlack
+                if (__ballot(mt > m[rt] + kSlack) != 0) {
+                    const float mnew = fmaxf(m[rt], group4_max(mt));
+                    const float sc = (m[rt] == -INFINITY) ? 0.f : fast_exp2(m[rt] - mnew);
+                    l[rt] *= sc;
+#pragma unroll
+                    for (int mm = 0; mm < kDV; ++mm) O[rt][mm] *= sc;
+                    m[rt] = mnew;
+                }
+                const float muse = (m[rt] == -INFINITY) ? 0.f : m[rt];
+                float pv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    pv[j] = fast_exp2(sv[j] - muse);
+                    l[rt] += pv[j];
+                }
+                const u32x4 P = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                                 pack_bf16(pv[6], pv[7])};
+#pragma unroll
+                for (int mm = 0; mm < kDV; ++mm) O[rt][mm] = mfma16(vt[mm], P, O[rt][mm]);
+            }
+        }
+    };
+    if (nst > 0) issue(0, kv_a);
+    if (nst > 1) issue(1, kv_b);
+    for (int i = 0; i < nst; i += kStages) {
+        step(i, kv_a, kv_c);
+        if (i + 1 >= nst) break;
+        step(i + 1, kv_b, kv_a);
+        if (i + 2 >= nst) break;
+        step(i + 2, kv_c, kv_b);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) l[rt] = group4_sum(l[rt]);
+
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int rho = rb * kBlockRows + (w * RT + rt) * 16 + c;
+        if (rho >= a.Rp) continue;
+        if (a.SB == 1) {
+            finish_row_lanes<kD, uint16_t>(a, out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq), g, m[rt], l[rt], O[rt]);
+        } else {
+            const size_t row = (size_t)(p * a.SB + sb) * a.Rp + rho;
+            if (g == 0) a.part_ml[row] = make_float2(m[rt], l[rt]);
+            float *op = a.part_O + row * kD;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int m4 = 0; m4 < kDV; m4 += 4) {
+                    f32x4 v = {O[rt][m4][r], O[rt][m4 + 1][r], O[rt][m4 + 2][r], O[rt][m4 + 3][r]};
+                    *(f32x4 *)(op + kDV * (4 * g + r) + m4) = v;
+                }
+        }
+    }
+}
+
+LdsShape lds_shape_for(int Rp) { return Rp <= 64 ? LdsShape{4, 1} : LdsShape{8, 1}; }
+
+hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st) {
+    dim3 grid((unsigned)((long)p.P * p.RB * p.SB)), block(sh.NW * 64);
+    if (sh.NW == 4 && sh.RT == 1) hipLaunchKernelGGL((attn_rows_lds<4, 1>), grid, block, 0, st, p);
+    else if (sh.NW == 8 && sh.RT == 1) hipLaunchKernelGGL((attn_rows_lds<8, 1>), grid, block, 0, st, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace nectar

@@ -20,6 +20,7 @@ struct AttnParams {
     // its WS splits together, leaving SB = ceil(S / WS) partials per row;
     // RB = ceil(RG / WR).  fp32 path: one wave per (row, split), SB = S.
     int P, S, chunk, RG, WR, WS, RB, SB;
+    int xcd_group;       // LDS-staged kernel: row blocks of a split share an XCD
     float *part_O;       // [P][SB][Rp][d]    unnormalised read-out
     float2 *part_ml;     // [P][SB][Rp]       (running max in log2 units, sum)
     // Row finishing in place when SB == 1 (same meaning as in CombineParams).
@@ -70,6 +71,13 @@ struct MergeParams {
 int row_tiles_for(int Rp);
 
 hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hipStream_t st);
+// LDS-staged attention for many rows per KV head (bf16, d = 128): NW waves of
+// RT row tiles per block, 16 * NW * RT rows.
+struct LdsShape {
+    int NW, RT;
+};
+LdsShape lds_shape_for(int Rp);
+hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st);
 hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipStream_t st);
 hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st);

@@ -19,6 +19,14 @@ namespace {
 // with enough loads in flight to cover HBM latency.
 constexpr long kTargetWaves = 2048;
 constexpr long kTargetWavesMlp = 1024;
+// Blocks a split plan of the LDS-staged kernel aims for: one per CU (a block
+// holds 96 KB of LDS, so one is resident per CU).
+constexpr long kTargetBlocksLds = 256;
+// Rows per KV head from which attention uses the LDS-staged kernel (bf16,
+// d = 128): beyond one 16-row tile the register-direct kernel would stream
+// the cache once per row group.
+constexpr int kLdsRows = 17;
+constexpr int kStageKeys = 64;
 constexpr int kTile = 32;
 
 inline long cdiv(long a, long b) { return (a + b - 1) / b; }
@@ -49,6 +57,8 @@ inline bool out_ok(const void *p, int dtype) { return p && aligned(p, dtype == N
 struct AttnPlan {
     int P = 0, Rp = 0, RT = 0, RG = 0, S = 0, chunk = kTile;
     int WR = 1, WS = 1, RB = 0, SB = 0;
+    bool lds = false, xcd = false;
+    LdsShape sh{0, 0};
     size_t ws = 0;
 };
 
@@ -65,6 +75,25 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv) {
     pl.Rp = Rp;
     if (P == 0 || Rp == 0 || T_kv <= 0) return pl;    // nothing to attend: combine with S = 0
     const bool mfma = d->dtype == NECTAR_BF16;
+    if (mfma && d->d == 128 && Rp >= kLdsRows) {
+        // LDS-staged kernel: blocks of 16 * NW * RT rows x key splits of whole
+        // 64-key stages; a block finishes its rows in place when S == 1
+        pl.lds = true;
+        pl.sh = lds_shape_for(Rp);
+        pl.RT = pl.sh.RT;
+        pl.WR = pl.sh.NW;
+        pl.RB = (int)cdiv(Rp, 16L * pl.sh.NW * pl.sh.RT);
+        pl.RG = (int)cdiv(Rp, 16L * pl.RT);
+        const long stages = cdiv(T_kv, kStageKeys);
+        long S = d->splits > 0 ? d->splits : cdiv(kTargetBlocksLds, (long)P * pl.RB);
+        S = S < 1 ? 1 : (S > stages ? stages : S);
+        const long per = cdiv(stages, S);
+        pl.chunk = (int)(per * kStageKeys);
+        pl.S = pl.SB = (int)cdiv(stages, per);
+        pl.xcd = pl.RB > 1 && pl.RB <= 8 && ((long)P * pl.S) % 8 == 0;
+        pl.ws = pl.SB > 1 ? (size_t)P * pl.SB * Rp * ((size_t)d->d * 4 + 8) : 0;
+        return pl;
+    }
     // the MFMA kernel walks keys in batches of two 32-key tiles
     const long gran = mfma ? 2 * kTile : kTile;
     const long tiles = cdiv(T_kv, gran);
@@ -173,12 +202,13 @@ hipError_t run_attention(const nectar_attn_desc *d, const AttnPlan &pl, const vo
         a.sl2 = score_scale(d) * 1.4426950408889634f;
         a.P = pl.P; a.S = pl.S; a.chunk = pl.chunk; a.RG = pl.RG;
         a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB;
+        a.xcd_group = pl.xcd ? 1 : 0;
         a.part_O = part_O; a.part_ml = part_ml;
         if (mfma && pl.SB == 1) {
             a.lse_out = cp.lse_out; a.A_out = cp.A_out; a.x_lse = cp.x_lse; a.x_A = cp.x_A;
             a.out = cp.out; a.out_lse = cp.out_lse;
         }
-        hipError_t e = launch_attn_partial(a, d->dtype, d->d, pl.RT, st);
+        hipError_t e = pl.lds ? launch_attn_rows_lds(a, pl.sh, st) : launch_attn_partial(a, d->dtype, d->d, pl.RT, st);
         if (e != hipSuccess || (mfma && pl.SB == 1)) return e;
     }
     cp.part_O = part_O; cp.part_ml = part_ml;

@@ -39,7 +39,7 @@ def _store(x, dt):
 
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("R,Hq,Hkv,n", [(1, 32, 8, 1000), (3, 28, 4, 777), (20, 8, 2, 96), (2, 4, 4, 33),
-                                        (10, 16, 4, 500)])
+                                        (10, 16, 4, 500), (70, 16, 4, 1000), (64, 32, 8, 3000)])
 @pytest.mark.parametrize("splits", [0, 1, 7])
 def test_doc_attn_bf16(nx, d, R, Hq, Hkv, n, splits):
     print("case doc_attn bf16 d=%d R=%d Hq=%d Hkv=%d n=%d splits=%d" % (d, R, Hq, Hkv, n, splits), flush=True)
@@ -190,7 +190,8 @@ def test_mlp_d64_and_f32(nx):
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,Tq,T_loc,T_cap,q_offset", [(2, 37, 37, 40, 0), (3, 1, 100, 128, 99),
                                                         (1, 1, 513, 513, 512), (2, 5, 20, 20, 10),
-                                                        (2, 1, 0, 8, 0)])
+                                                        (2, 1, 0, 8, 0), (2, 100, 100, 100, 0),
+                                                        (1, 70, 300, 320, 230)])
 def test_local_attn(nx, dt, B, Tq, T_loc, T_cap, q_offset):
     Hq, Hkv, d = 12, 4, 128
     print("case local %s B=%d Tq=%d T_loc=%d q_offset=%d" % (dt, B, Tq, T_loc, q_offset), flush=True)

@@ -33,7 +33,13 @@ namespace nectar {
 namespace {
 
 constexpr int kD = 128, kKS = 4, kDV = 8;
-constexpr int kStageKeys = 64;
+#ifndef NECTAR_LDS_STAGE_KEYS
+#define NECTAR_LDS_STAGE_KEYS 64
+#endif
+#ifndef NECTAR_LDS_WAVES_PER_SIMD
+#define NECTAR_LDS_WAVES_PER_SIMD 1
+#endif
+constexpr int kStageKeys = NECTAR_LDS_STAGE_KEYS;
 constexpr int kStages = 3;
 constexpr int kPieces = kD * 2 / 16;            // 16-byte pieces per key row
 constexpr float kSlack = 8.0f;
@@ -55,7 +61,7 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
 }  // namespace
 
 template <int NW, int RT>
-__global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
+__global__ __launch_bounds__(NW * 64, (NECTAR_LDS_WAVES_PER_SIMD * 4 / NW) > 1 ? NECTAR_LDS_WAVES_PER_SIMD * 4 / NW : 1) void attn_rows_lds(AttnParams a) {
     constexpr int kKeysPerWave = kStageKeys / NW;       // keys of a stage one wave copies
     constexpr int kCopies = kKeysPerWave / 4;           // copy instructions per wave, K and V each
     static_assert(kCopies >= 1 && kCopies * 4 * NW == kStageKeys, "stage split");
@@ -101,9 +107,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
         } else {
 #pragma unroll
             for (int kt = 0; kt < kKS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
-            lim[rt] = 0;
+            lim[rt] = 0x7fffffff;      // row past the end: computed unmasked, never written
         }
     }
+    // Scores are formed unscaled and the scale enters the exponent's FMA; a
+    // negative scale is carried by the query's sign (exact for bf16).
+    float sl2 = a.sl2;
+    if (sl2 < 0.f) {
+        sl2 = -sl2;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kt = 0; kt < kKS; ++kt) qv[rt][kt] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
+
     // Key limit of the whole block (uniform): the causal limit grows with the
     // token, so the block's last valid row has the largest one.
     int blim = a.T_kv;
@@ -157,7 +174,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
         const u32x4 *Ks = cur[0];
         const u32x4 *Vs = cur[1];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
+        for (int sub = 0; sub < kStageKeys / 32; ++sub) {
             const int kbase = k_lo + i * kStageKeys + 32 * sub;
             u32x4 kop[2][kKS];
 #pragma unroll
@@ -178,8 +195,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
             for (int mm = 0; mm < kDV; ++mm) {
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2) {
-                    const uint32_t a0 = vr[2 * q2][mm >> 1], a1 = vr[2 * q2 + 1][mm >> 1];
-                    vt[mm][q2] = (mm & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+                    // low or high halves of two keys' words: (a0 & 0xffff) | (a1 << 16)
+                    // or (a0 >> 16) | (a1 & 0xffff0000), one byte permute
+                    vt[mm][q2] = __builtin_amdgcn_perm(vr[2 * q2 + 1][mm >> 1], vr[2 * q2][mm >> 1],
+                                                       (mm & 1) ? 0x07060302u : 0x05040100u);
                 }
             }
 #pragma unroll
@@ -192,15 +211,17 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
                 }
                 float sv[8];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) { sv[r] = s0[r] * a.sl2; sv[4 + r] = s1[r] * a.sl2; }
+                for (int r = 0; r < 4; ++r) { sv[r] = s0[r]; sv[4 + r] = s1[r]; }
+                // per-lane test: the compiler turns it into selects that it can
+                // schedule with the matrix work (a wave-uniform branch here
+                // splits the block and measured slower)
                 if (kbase + 32 > lim[rt]) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
                         if (kbase + slot_key(g, j) >= lim[rt]) sv[j] = -INFINITY;
                 }
-                float mt = sv[0];
-#pragma unroll
-                for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
+                const float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]))) * sl2;
                 // move the reference max only when some score passes it by kSlack
                 if (__ballot(mt > m[rt] + kSlack) != 0) {
                     const float mnew = fmaxf(m[rt], group4_max(mt));
@@ -210,11 +231,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
                     for (int mm = 0; mm < kDV; ++mm) O[rt][mm] *= sc;
                     m[rt] = mnew;
                 }
-                const float muse = (m[rt] == -INFINITY) ? 0.f : m[rt];
+                const float nm = (m[rt] == -INFINITY) ? 0.f : -m[rt];
                 float pv[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    pv[j] = fast_exp2(sv[j] - muse);
+                    pv[j] = fast_exp2(__builtin_fmaf(sv[j], sl2, nm));
                     l[rt] += pv[j];
                 }
                 const u32x4 P = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),

@@ -21,12 +21,21 @@ constexpr long kTargetWaves = 2048;
 constexpr long kTargetWavesMlp = 1024;
 // Blocks a split plan of the LDS-staged kernel aims for: one per CU (a block
 // holds 96 KB of LDS, so one is resident per CU).
-constexpr long kTargetBlocksLds = 256;
+#ifndef NECTAR_LDS_TARGET_BLOCKS
+#define NECTAR_LDS_TARGET_BLOCKS 256
+#endif
+#ifndef NECTAR_LDS_MIN_ROWS
+#define NECTAR_LDS_MIN_ROWS 17
+#endif
+#ifndef NECTAR_LDS_STAGE_KEYS
+#define NECTAR_LDS_STAGE_KEYS 64
+#endif
+constexpr long kTargetBlocksLds = NECTAR_LDS_TARGET_BLOCKS;
 // Rows per KV head from which attention uses the LDS-staged kernel (bf16,
 // d = 128): beyond one 16-row tile the register-direct kernel would stream
 // the cache once per row group.
-constexpr int kLdsRows = 17;
-constexpr int kStageKeys = 64;
+constexpr int kLdsRows = NECTAR_LDS_MIN_ROWS;
+constexpr int kStageKeys = NECTAR_LDS_STAGE_KEYS;
 constexpr int kTile = 32;
 
 inline long cdiv(long a, long b) { return (a + b - 1) / b; }

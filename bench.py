@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--only", choices=["step", "exact", "nectar", "doc"], default=None,
                     help="time only one graph (for profiling runs)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-layer timings of the three larger workloads")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the batched-prefill MLP measurement")
     return ap.parse_args()
@@ -234,10 +236,13 @@ def main():
                                      "%d algorithmic bytes per launch" % (us, doc_bytes)}
         res["module_roofline_hint"] = {"bytes_per_launch": mlp_bytes}
 
-    if not args.no_prefill and args.only is None:
+    if args.only is None and not (args.no_prefill and args.no_workloads):
         del reps, graphs
         torch.cuda.empty_cache()
+    if not args.no_prefill and args.only is None:
         res["prefill_mlp"] = prefill_mlp(torch, np, nectar, configs, synth, dev)
+    if not args.no_workloads and args.only is None:
+        res["workloads"] = {c.name: workload_layer(torch, nectar, c, dev) for c in (configs.C4, configs.C5, configs.C3)}
 
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(cfg, q_h, K_h, V_h, Kl_h, Vl_h, P_h, args.cpu_seconds)
@@ -245,6 +250,102 @@ def main():
 
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 flop/clk, dense
+
+
+def workload_layer(torch, nectar, cfg, dev):
+    """One layer-step of a larger workload at its full per-layer shape: the exact
+    document part alone (against its HBM or MFMA roofline), the module alone, and
+    the Nectar and exact paths (document part + causal local part with the fused
+    merge).  Inputs are N(0, 1) draws from a seeded device generator in the
+    workload's shapes (module weights N(0, 1/fan_in)); two layer replicas when a
+    layer's cache is smaller than 2 GB, so consecutive calls do not reuse a
+    cache-resident copy.  Decode steps are timed as graphs, prefill eagerly."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 + cfg.seed)
+    bf = torch.bfloat16
+    d, Hkv, Hq, R, n = cfg.d, cfg.Hkv, cfg.Hq, cfg.R, cfg.n
+
+    def rn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device=dev) * std).to(bf)
+
+    doc_bytes = Hkv * n * 2 * d * 2
+    nrep = 1 if cfg.prefill or doc_bytes >= (2 << 30) else 2
+    q = rn(R, Hq, d)
+    KV = [(rn(Hkv, n, d), rn(Hkv, n, d)) for _ in range(nrep)]
+    Kl, Vl = rn(cfg.B, Hkv, cfg.T_cap, d), rn(cfg.B, Hkv, cfg.T_cap, d)
+    m = cfg.mlps[-1]
+    z = lambda *s: torch.zeros(*s, device=dev)
+    mod = nectar.MLPModule(rn(Hkv, m.Ht, d, std=d ** -0.5), z(Hkv, m.Ht), rn(Hkv, m.Ht, d, std=m.Ht ** -0.5),
+                           z(Hkv, d), rn(Hkv, m.Hs, d, std=d ** -0.5), z(Hkv, m.Hs),
+                           rn(Hkv, m.Hs, std=m.Hs ** -0.5), z(Hkv))
+    T, qoff = cfg.local_len(cfg.decode_steps - 1 if not cfg.prefill else 0), cfg.q_offset(cfg.decode_steps - 1 if not cfg.prefill else 0)
+    f32 = dict(dtype=torch.float32, device=dev)
+    al, Ax, a, Am = torch.empty((R, Hq), **f32), torch.empty((R, Hq, d), **f32), torch.empty((R, Hq), **f32), \
+        torch.empty((R, Hq, d), **f32)
+    out, olse = torch.empty((R, Hq, d), dtype=bf, device=dev), torch.empty((R, Hq), **f32)
+
+    def doc(i):
+        K, V = KV[i % nrep]
+        nectar.doc_attn_exact(q, K, V, Hkv, alpha_out=al, A_out=Ax)
+
+    def module(i):
+        nectar.module_forward(q, mod, Hkv, a_out=a, A_out=Am)
+
+    def local(i, x_lse, x_A):
+        nectar.local_attn_lse(q, Kl, Vl, Hkv, B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff, want_pair=False,
+                              doc_lse=x_lse, doc_A=x_A, out=out, out_lse=olse)
+
+    parts = {"exact_doc": doc, "module": module, "local_merge": lambda i: local(i, a, Am),
+             "nectar_path": lambda i: (module(i), local(i, a, Am)),
+             "exact_path": lambda i: (doc(i), local(i, al, Ax))}
+    for fn in parts.values():
+        fn(0)
+    torch.cuda.synchronize()
+    us = {}
+    for name, fn in parts.items():
+        if cfg.prefill:
+            reps = 3
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us[name] = e0.elapsed_time(e1) / reps * 1e3
+        else:
+            reps = 8 * nrep
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(reps):
+                    fn(i)
+            gr.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(4):
+                gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us[name] = e0.elapsed_time(e1) / (4 * reps) * 1e3
+            del gr
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite output in workload %s" % cfg.name)
+    res = {"layer_step": "prefill (16 x 1,024 causal tokens)" if cfg.prefill else
+           "decode step %d (batch %d, %d local keys)" % (cfg.decode_steps - 1, cfg.B, T),
+           "module": "MLP %d/%d" % (m.Ht, m.Hs), "us": us,
+           "qtok_s_layer": {"nectar": R / (us["nectar_path"] * 1e-6), "exact": R / (us["exact_path"] * 1e-6)},
+           "nectar_speedup_vs_exact": us["exact_path"] / us["nectar_path"]}
+    if cfg.prefill:
+        flops = R * Hq * n * 4 * d
+        res["exact_doc_roofline"] = {"bound": "mfma", "tflops": flops / us["exact_doc"] / 1e6,
+                                     "frac": flops / us["exact_doc"] / 1e6 / MFMA_BF16_PEAK_TFLOPS}
+    else:
+        res["exact_doc_roofline"] = {"bound": "hbm", "gbs": doc_bytes / us["exact_doc"] / 1e3,
+                                     "frac": doc_bytes / us["exact_doc"] / 1e3 / HBM_PEAK_GBS,
+                                     "bytes_per_launch": doc_bytes}
+    del KV, q, Kl, Vl, mod
+    torch.cuda.empty_cache()
+    return res
 
 
 def prefill_mlp(torch, np, nectar, configs, synth, dev):

@@ -7,7 +7,7 @@
 // (KV head, and question for per-question caches) and one key range; every
 // wave holds RT tiles of 16 rows (NW = 8 puts two waves on each SIMD, so one
 // wave's softmax overlaps the other's matrix work).  The block streams its keys through LDS in
-// stages of 64 keys (16 KB of K, 16 KB of V), three stages in a ring: each
+// stages of kStageKeys keys (64 keys: 16 KB of K, 16 KB of V), three stages in a ring: each
 // lane copies 16-byte pieces from HBM straight into LDS (global_load_lds, no
 // register staging), two stages ahead of use, so every key is read from HBM
 // once per block whatever the number of rows.
@@ -33,13 +33,6 @@ namespace nectar {
 namespace {
 
 constexpr int kD = 128, kKS = 4, kDV = 8;
-#ifndef NECTAR_LDS_STAGE_KEYS
-#define NECTAR_LDS_STAGE_KEYS 64
-#endif
-#ifndef NECTAR_LDS_WAVES_PER_SIMD
-#define NECTAR_LDS_WAVES_PER_SIMD 1
-#endif
-constexpr int kStageKeys = NECTAR_LDS_STAGE_KEYS;
 constexpr int kStages = 3;
 constexpr int kPieces = kD * 2 / 16;            // 16-byte pieces per key row
 constexpr float kSlack = 8.0f;
@@ -60,8 +53,8 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
 
 }  // namespace
 
-template <int NW, int RT>
-__global__ __launch_bounds__(NW * 64, (NECTAR_LDS_WAVES_PER_SIMD * 4 / NW) > 1 ? NECTAR_LDS_WAVES_PER_SIMD * 4 / NW : 1) void attn_rows_lds(AttnParams a) {
+template <int NW, int RT, int kStageKeys>
+__global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
     constexpr int kKeysPerWave = kStageKeys / NW;       // keys of a stage one wave copies
     constexpr int kCopies = kKeysPerWave / 4;           // copy instructions per wave, K and V each
     static_assert(kCopies >= 1 && kCopies * 4 * NW == kStageKeys, "stage split");
@@ -278,12 +271,15 @@ __global__ __launch_bounds__(NW * 64, (NECTAR_LDS_WAVES_PER_SIMD * 4 / NW) > 1 ?
     }
 }
 
-LdsShape lds_shape_for(int Rp) { return Rp <= 64 ? LdsShape{4, 1} : LdsShape{8, 1}; }
+// One wave per SIMD with 96-key stages (144 KB of LDS, two stages in flight)
+// when a block's four row tiles cover the problem; otherwise eight waves (two
+// per SIMD) with 64-key stages.
+LdsShape lds_shape_for(int Rp) { return Rp <= 64 ? LdsShape{4, 1, 96} : LdsShape{8, 1, 64}; }
 
 hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st) {
     dim3 grid((unsigned)((long)p.P * p.RB * p.SB)), block(sh.NW * 64);
-    if (sh.NW == 4 && sh.RT == 1) hipLaunchKernelGGL((attn_rows_lds<4, 1>), grid, block, 0, st, p);
-    else if (sh.NW == 8 && sh.RT == 1) hipLaunchKernelGGL((attn_rows_lds<8, 1>), grid, block, 0, st, p);
+    if (sh.NW == 4 && sh.RT == 1 && sh.SK == 96) hipLaunchKernelGGL((attn_rows_lds<4, 1, 96>), grid, block, 0, st, p);
+    else if (sh.NW == 8 && sh.RT == 1 && sh.SK == 64) hipLaunchKernelGGL((attn_rows_lds<8, 1, 64>), grid, block, 0, st, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

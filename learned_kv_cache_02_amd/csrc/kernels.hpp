@@ -72,9 +72,9 @@ int row_tiles_for(int Rp);
 
 hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hipStream_t st);
 // LDS-staged attention for many rows per KV head (bf16, d = 128): NW waves of
-// RT row tiles per block, 16 * NW * RT rows.
+// RT row tiles per block, 16 * NW * RT rows, keys staged SK at a time.
 struct LdsShape {
-    int NW, RT;
+    int NW, RT, SK;
 };
 LdsShape lds_shape_for(int Rp);
 hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st);

@@ -27,15 +27,11 @@ constexpr long kTargetWavesMlp = 1024;
 #ifndef NECTAR_LDS_MIN_ROWS
 #define NECTAR_LDS_MIN_ROWS 17
 #endif
-#ifndef NECTAR_LDS_STAGE_KEYS
-#define NECTAR_LDS_STAGE_KEYS 64
-#endif
 constexpr long kTargetBlocksLds = NECTAR_LDS_TARGET_BLOCKS;
 // Rows per KV head from which attention uses the LDS-staged kernel (bf16,
 // d = 128): beyond one 16-row tile the register-direct kernel would stream
 // the cache once per row group.
 constexpr int kLdsRows = NECTAR_LDS_MIN_ROWS;
-constexpr int kStageKeys = NECTAR_LDS_STAGE_KEYS;
 constexpr int kTile = 32;
 
 inline long cdiv(long a, long b) { return (a + b - 1) / b; }
@@ -67,7 +63,7 @@ struct AttnPlan {
     int P = 0, Rp = 0, RT = 0, RG = 0, S = 0, chunk = kTile;
     int WR = 1, WS = 1, RB = 0, SB = 0;
     bool lds = false, xcd = false;
-    LdsShape sh{0, 0};
+    LdsShape sh{0, 0, 0};
     size_t ws = 0;
 };
 
@@ -86,18 +82,18 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv) {
     const bool mfma = d->dtype == NECTAR_BF16;
     if (mfma && d->d == 128 && Rp >= kLdsRows) {
         // LDS-staged kernel: blocks of 16 * NW * RT rows x key splits of whole
-        // 64-key stages; a block finishes its rows in place when S == 1
+        // SK-key stages; a block finishes its rows in place when S == 1
         pl.lds = true;
         pl.sh = lds_shape_for(Rp);
         pl.RT = pl.sh.RT;
         pl.WR = pl.sh.NW;
         pl.RB = (int)cdiv(Rp, 16L * pl.sh.NW * pl.sh.RT);
         pl.RG = (int)cdiv(Rp, 16L * pl.RT);
-        const long stages = cdiv(T_kv, kStageKeys);
+        const long stages = cdiv(T_kv, pl.sh.SK);
         long S = d->splits > 0 ? d->splits : cdiv(kTargetBlocksLds, (long)P * pl.RB);
         S = S < 1 ? 1 : (S > stages ? stages : S);
         const long per = cdiv(stages, S);
-        pl.chunk = (int)(per * kStageKeys);
+        pl.chunk = (int)(per * pl.sh.SK);
         pl.S = pl.SB = (int)cdiv(stages, per);
         pl.xcd = pl.RB > 1 && pl.RB <= 8 && ((long)P * pl.S) % 8 == 0;
         pl.ws = pl.SB > 1 ? (size_t)P * pl.SB * Rp * ((size_t)d->d * 4 + 8) : 0;

@@ -122,9 +122,15 @@ __device__ __forceinline__ void attend_tile(const KVTile<D> &T, int k0, const u3
     }
 }
 
+#ifndef NECTAR_RT1_WAVES_PER_SIMD
+#define NECTAR_RT1_WAVES_PER_SIMD 2
+#endif
+#ifndef NECTAR_RT1_SUB
+#define NECTAR_RT1_SUB 2
+#endif
 // RT == 1: two waves per SIMD (8 per CU), each with a 32 KB batch in flight.
 template <int D, int RT, int SUB, typename OutT>
-__global__ __launch_bounds__(256, RT == 1 ? 2 : 1) void attn_partial_mfma(AttnParams a) {
+__global__ __launch_bounds__(256, RT == 1 ? NECTAR_RT1_WAVES_PER_SIMD : 1) void attn_partial_mfma(AttnParams a) {
     constexpr int KS = D / 32, DV = D / 16;
     // Fold buffers (used when WS > 1, hence WR <= 2): per row group one f32x4
     // per (register, lane), lane-major so each wave access is conflict-free.
@@ -452,7 +458,7 @@ hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hi
     if (dtype == 1) {
         dim3 grid((unsigned)((long)p.P * p.RB * p.SB)), block(256);
 #define NECTAR_ATTN_CASE(DD, RR) \
-        if (d == DD && rt == RR) { hipLaunchKernelGGL((attn_partial_mfma<DD, RR, (RR == 1 ? 2 : 1), uint16_t>), grid, block, 0, st, p); return hipGetLastError(); }
+        if (d == DD && rt == RR) { hipLaunchKernelGGL((attn_partial_mfma<DD, RR, (RR == 1 ? NECTAR_RT1_SUB : 1), uint16_t>), grid, block, 0, st, p); return hipGetLastError(); }
         NECTAR_ATTN_CASE(128, 1) NECTAR_ATTN_CASE(128, 2)
         NECTAR_ATTN_CASE(64, 1) NECTAR_ATTN_CASE(64, 2)
 #undef NECTAR_ATTN_CASE

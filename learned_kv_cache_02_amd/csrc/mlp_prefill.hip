@@ -12,10 +12,23 @@
 //   lane per operand), read-out rows are stored transposed and slot-ordered so
 //   a lane reads its W2t^T operand with one 16-byte read per 16 dimensions.
 // Per chunk and 16-row tile a wave runs
-//   Z^T = W1_chunk . Q^T (8 MFMAs) -> + b1 -> GELU -> bf16 -> O^T += W2t^T . H^T (8 MFMAs)
+//   Z^T = b1 + W1_chunk . Q^T (8 MFMAs, the bias is the accumulator's initial
+//   value) -> act -> bf16 -> O^T += W2t^T . H^T (8 MFMAs)
 // so the hidden activations never leave registers; score chunks run
-//   Zs^T = Ws_chunk . Q^T -> + bs -> GELU -> fp32 dot with ws2.
-// The block adds the output biases and writes (a, A).
+//   Zs^T = bs + Ws_chunk . Q^T -> act -> fp32 dot with ws2.
+//
+// The erf-form GELU is x * Phi(x).  Each block tabulates Phi in LDS at 2049
+// points over [-16, 16] (value and slope to the next point, evaluated in double
+// precision) and evaluates x * Phi(x) by linear interpolation, clamping outside
+// the range where Phi is 0 or 1 to within 1e-57: about seven VALU operations
+// and one 8-byte LDS read per hidden value instead of an exponential, a
+// reciprocal and a rational polynomial.  The interpolation error of Phi is at
+// most h^2 / 8 * max|Phi''| <= 7.4e-6 for h = 1/64.  SiLU and the tanh form are
+// cheaper to evaluate directly (one exponential and one reciprocal) and are
+// evaluated that way.
+// With one split (SB == 1) the block adds the output biases and writes (a, A);
+// with SB > 1 splits of the hidden units, block (h, row block, split) writes its
+// partial sums and mlp_reduce adds them in split order with the biases.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -24,6 +37,20 @@ namespace nectar {
 namespace {
 
 constexpr int kD = 128, kKS = 4, kDV = 8, kRTW = 2, kThreads = 512, kRows = kThreads / 64 * kRTW * 16;
+constexpr int kTabN = 2048;              // intervals of the activation table
+constexpr float kTabL = 16.0f;           // table range [-kTabL, kTabL]
+
+// Phi(x), the standard normal CDF, in double precision.
+__device__ double normal_cdf(double x) { return 0.5 * erfc(-x * 0.70710678118654752440); }
+
+// x * Phi(x) by linear interpolation in the table (value, slope) of Phi.
+__device__ __forceinline__ float gelu_table(const float2 *tab, float x) {
+    float t = __builtin_fmaf(x, kTabN / (2.0f * kTabL), kTabN / 2.0f);
+    t = __builtin_amdgcn_fmed3f(t, 0.0f, (float)kTabN);
+    const int i = (int)t;
+    const float2 e = tab[i];
+    return x * __builtin_fmaf(t - (float)i, e.y, e.x);
+}
 
 __device__ __forceinline__ int unit_of_slot(int g, int j) { return 16 * (j >> 2) + 4 * g + (j & 3); }
 
@@ -40,6 +67,7 @@ struct Smem {
     uint16_t w2t[2][4][8][16][8];   // [buf][g][mm][c][slot j]: W2t[unit(g, j)][8c + mm]
     float b[2][32];
     float s[2][32];
+    float2 tab[kTabN + 1];
 };
 
 __device__ __forceinline__ void stage_load(Stage &S, const uint16_t *W, const uint16_t *W2, const float *bias,
@@ -75,8 +103,18 @@ template <int ACT>
 __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
     __shared__ Smem sm;
     const int nrb = (a.Rp + kRows - 1) / kRows;
-    const int h = blockIdx.x / nrb, rb = blockIdx.x - h * nrb;
+    const int sb = blockIdx.x % a.SB, hr = blockIdx.x / a.SB;
+    const int h = hr / nrb, rb = hr - h * nrb;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, c = lane & 15;
+    // GELU table (the first barrier below orders it before any use)
+    if (ACT == 0) {
+        for (int i = t; i <= kTabN; i += kThreads) {
+            const double step = 2.0 * kTabL / kTabN, x0 = -kTabL + i * step;
+            const double g0 = normal_cdf(x0), g1 = i < kTabN ? normal_cdf(x0 + step) : g0;
+            sm.tab[i] = make_float2((float)g0, (float)(g1 - g0));
+        }
+    }
+    auto act = [&](float x) { return ACT == 0 ? gelu_table(sm.tab, x) : act_fn<ACT>(x); };
 
     u32x4 qv[kRTW][kKS];
 #pragma unroll
@@ -107,11 +145,15 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
     const uint16_t *Ws = (const uint16_t *)a.Ws + (size_t)h * a.Hs * kD;
     const uint16_t *ws2 = (const uint16_t *)a.ws2 + (size_t)h * a.Hs;
     const float *bs = a.bs + (size_t)h * a.Hs;
-    const int ntc = (a.Ht + 31) / 32, nch = ntc + (a.Hs + 31) / 32;
+    // this split's chunks: target chunks [t0, t0 + ntc), then score chunks [s0, s0 + nsc)
+    const int ttot = (a.Ht + 31) / 32, stot = (a.Hs + 31) / 32;
+    const int ctc = a.chunk_t / 32, csc = a.chunk_s / 32;
+    const int t0 = min(sb * ctc, ttot), s0 = min(sb * csc, stot);
+    const int ntc = min(ctc, ttot - t0), nch = ntc + min(csc, stot - s0);
 
     auto load_chunk = [&](Stage &S, int i) {
-        if (i < ntc) stage_load(S, W1, W2t, b1, nullptr, 32 * i, a.Ht, true, t);
-        else stage_load(S, Ws, nullptr, bs, ws2, 32 * (i - ntc), a.Hs, false, t);
+        if (i < ntc) stage_load(S, W1, W2t, b1, nullptr, 32 * (t0 + i), a.Ht, true, t);
+        else stage_load(S, Ws, nullptr, bs, ws2, 32 * (s0 + i - ntc), a.Hs, false, t);
     };
 
     auto compute = [&](int i) {
@@ -125,13 +167,13 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) bias[j] = sm.b[buf][unit_of_slot(g, j)];
         if (i < ntc) {
-            const int j0 = 32 * i;
+            const int j0 = 32 * (t0 + i);
             u32x4 vt[kDV];
 #pragma unroll
             for (int mm = 0; mm < kDV; ++mm) vt[mm] = *(const u32x4 *)&sm.w2t[buf][g][mm][c][0];
 #pragma unroll
             for (int rt = 0; rt < kRTW; ++rt) {
-                f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+                f32x4 z0 = {bias[0], bias[1], bias[2], bias[3]}, z1 = {bias[4], bias[5], bias[6], bias[7]};
 #pragma unroll
                 for (int kt = 0; kt < kKS; ++kt) {
                     z0 = mfma16(w1op[0][kt], qv[rt][kt], z0);
@@ -140,8 +182,8 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
                 float hv[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    hv[r] = act_fn<ACT>(z0[r] + bias[r]);
-                    hv[4 + r] = act_fn<ACT>(z1[r] + bias[4 + r]);
+                    hv[r] = act(z0[r]);
+                    hv[4 + r] = act(z1[r]);
                 }
                 if (j0 + 32 > a.Ht) {
 #pragma unroll
@@ -159,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
             for (int j = 0; j < 8; ++j) wsv[j] = sm.s[buf][unit_of_slot(g, j)];
 #pragma unroll
             for (int rt = 0; rt < kRTW; ++rt) {
-                f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+                f32x4 z0 = {bias[0], bias[1], bias[2], bias[3]}, z1 = {bias[4], bias[5], bias[6], bias[7]};
 #pragma unroll
                 for (int kt = 0; kt < kKS; ++kt) {
                     z0 = mfma16(w1op[0][kt], qv[rt][kt], z0);
@@ -168,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
                 float acc = 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j)      // units past Hs carry ws2 = 0
-                    acc += wsv[j] * act_fn<ACT>((j < 4 ? z0[j] : z1[j - 4]) + bias[j]);
+                    acc += wsv[j] * act(j < 4 ? z0[j] : z1[j - 4]);
                 sc[rt] += acc;
             }
         }
@@ -201,6 +243,19 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
         const float ssum = group4_sum(sc[rt]);
         const int rho = rb * kRows + (w * kRTW + rt) * 16 + c;
         if (rho >= a.Rp) continue;
+        if (a.SB > 1) {
+            const size_t row = (size_t)(h * a.SB + sb) * a.Rp + rho;
+            if (g == 0) a.part_s[row] = ssum;
+            float *op = a.part_O + row * kD;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int m4 = 0; m4 < kDV; m4 += 4) {
+                    f32x4 v = {O[rt][m4][r], O[rt][m4 + 1][r], O[rt][m4 + 2][r], O[rt][m4 + 3][r]};
+                    *(f32x4 *)(op + kDV * (4 * g + r) + m4) = v;
+                }
+            continue;
+        }
         const int tk = rho / a.G, gg = rho - tk * a.G;
         const size_t o = (size_t)tk * a.Hq + h * a.G + gg;
         if (g == 0) a.a_out[o] = a.bs2[h] + ssum;
@@ -219,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
 
 hipError_t launch_mlp_prefill(const MlpParams &p, hipStream_t st) {
     const long nrb = (p.Rp + kRows - 1) / kRows;
-    dim3 grid((unsigned)(p.Hkv * nrb)), block(kThreads);
+    dim3 grid((unsigned)(p.Hkv * nrb * p.SB)), block(kThreads);
     if (p.act == 1) hipLaunchKernelGGL(mlp_prefill_mfma<1>, grid, block, 0, st, p);
     else if (p.act == 2) hipLaunchKernelGGL(mlp_prefill_mfma<2>, grid, block, 0, st, p);
     else hipLaunchKernelGGL(mlp_prefill_mfma<0>, grid, block, 0, st, p);

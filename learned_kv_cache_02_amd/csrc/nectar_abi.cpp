@@ -17,7 +17,13 @@ namespace {
 
 // Waves a split plan aims for: 256 CUs x 8 resident waves keeps every CU busy
 // with enough loads in flight to cover HBM latency.
-constexpr long kTargetWaves = 2048;
+#ifndef NECTAR_TARGET_WAVES
+#define NECTAR_TARGET_WAVES 2048
+#endif
+#ifndef NECTAR_RT1_SUB
+#define NECTAR_RT1_SUB 2
+#endif
+constexpr long kTargetWaves = NECTAR_TARGET_WAVES;
 constexpr long kTargetWavesMlp = 1024;
 // Blocks a split plan of the LDS-staged kernel aims for: one per CU (a block
 // holds 96 KB of LDS, so one is resident per CU).
@@ -99,8 +105,8 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv) {
         pl.ws = pl.SB > 1 ? (size_t)P * pl.SB * Rp * ((size_t)d->d * 4 + 8) : 0;
         return pl;
     }
-    // the MFMA kernel walks keys in batches of two 32-key tiles
-    const long gran = mfma ? 2 * kTile : kTile;
+    // the MFMA kernel walks keys in batches of NECTAR_RT1_SUB 32-key tiles
+    const long gran = mfma ? NECTAR_RT1_SUB * kTile : kTile;
     const long tiles = cdiv(T_kv, gran);
     long units;
     if (mfma) {
@@ -131,15 +137,34 @@ struct MlpPlan {
     size_t ws = 0;
 };
 
-// Rows per KV head from which the LDS-staged batched kernel is used.
-constexpr int kPrefillRows = 2048;
+// Rows per KV head from which the LDS-staged batched kernel is used (bf16,
+// d = 128): beyond one 16-row tile the register-direct kernel would stream the
+// weights once per row group.
+constexpr int kPrefillRows = 17;
+constexpr int kPrefillBlockRows = 256;
+// Blocks a split plan of the batched kernel aims for (one 512-thread block per CU).
+constexpr long kTargetBlocksPrefill = 256;
 
 MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs) {
     MlpPlan pl;
     pl.Rp = d->R * (d->Hq / d->Hkv);
     if (pl.Rp == 0) return pl;
-    if (d->dtype == NECTAR_BF16 && d->d == 128 && pl.Rp >= kPrefillRows && d->splits == 0) {
+    const long tt = cdiv(Ht, kTile), ts = cdiv(Hs, kTile);
+    const long tmax = tt > ts ? (tt > 1 ? tt : 1) : (ts > 1 ? ts : 1);
+    if (d->dtype == NECTAR_BF16 && d->d == 128 && pl.Rp >= kPrefillRows) {
+        // batched kernel: 256-row blocks x hidden-unit splits of whole 32-unit chunks
         pl.prefill = true;
+        pl.RB = (int)cdiv(pl.Rp, kPrefillBlockRows);
+        long S = d->splits > 0 ? d->splits : cdiv(kTargetBlocksPrefill, (long)d->Hkv * pl.RB);
+        S = S < 1 ? 1 : (S > tmax ? tmax : S);
+        long pt = cdiv(tt, S), ps = cdiv(ts, S);
+        long Se = 1;
+        if (pt > 0 && cdiv(tt, pt) > Se) Se = cdiv(tt, pt);
+        if (ps > 0 && cdiv(ts, ps) > Se) Se = cdiv(ts, ps);
+        pl.S = pl.SB = (int)Se;
+        pl.ct = (int)(pt * kTile);
+        pl.cs = (int)(ps * kTile);
+        pl.ws = pl.SB > 1 ? (size_t)d->Hkv * pl.SB * pl.Rp * ((size_t)d->d * 4 + 4) : 0;
         return pl;
     }
     const bool mfma = d->dtype == NECTAR_BF16;
@@ -153,8 +178,6 @@ MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs) {
         pl.RG = pl.Rp;
         units = (long)d->Hkv * pl.Rp;
     }
-    const long tt = cdiv(Ht, kTile), ts = cdiv(Hs, kTile);
-    const long tmax = tt > ts ? (tt > 1 ? tt : 1) : (ts > 1 ? ts : 1);
     long S = d->splits > 0 ? d->splits : cdiv(kTargetWavesMlp, units);
     S = S < 1 ? 1 : (S > tmax ? tmax : S);
     long pt = cdiv(tt, S), ps = cdiv(ts, S);
@@ -324,17 +347,27 @@ nectar_status nectar_module_forward(const nectar_attn_desc *desc, const nectar_m
     }
     const MlpPlan pl = plan_mlp(desc, m->Ht, m->Hs);
     if ((s = check_ws(pl.ws, ws, ws_bytes)) != NECTAR_OK) return s;
+    float *part_O = (float *)ws;
+    float *part_s = (float *)((char *)ws + (size_t)desc->Hkv * pl.SB * pl.Rp * desc->d * 4);
     if (pl.prefill) {
         MlpParams a{};
         a.q = q; a.W1 = m->W1; a.W2t = m->W2t; a.Ws = m->Ws; a.ws2 = m->ws2;
         a.b1 = m->b1; a.bs = m->bs; a.b2 = m->b2; a.bs2 = m->bs2;
         a.Hq = desc->Hq; a.G = desc->Hq / desc->Hkv; a.Hkv = desc->Hkv; a.Rp = pl.Rp;
         a.Ht = m->Ht; a.Hs = m->Hs; a.act = m->act;
+        a.S = pl.S; a.SB = pl.SB; a.chunk_t = pl.ct; a.chunk_s = pl.cs; a.RB = pl.RB;
+        a.part_O = part_O; a.part_s = part_s;
         a.a_out = a_out; a.A_out = A_out;
-        return finish(launch_mlp_prefill(a, st), st);
+        hipError_t e = launch_mlp_prefill(a, st);
+        if (e == hipSuccess && pl.SB > 1) {
+            MlpReduceParams r;
+            r.part_O = part_O; r.part_s = part_s; r.b2 = m->b2; r.bs2 = m->bs2;
+            r.Hq = desc->Hq; r.G = desc->Hq / desc->Hkv; r.Hkv = desc->Hkv; r.Rp = pl.Rp; r.S = pl.SB;
+            r.a_out = a_out; r.A_out = A_out;
+            e = launch_mlp_reduce(r, desc->d, st);
+        }
+        return finish(e, st);
     }
-    float *part_O = (float *)ws;
-    float *part_s = (float *)((char *)ws + (size_t)desc->Hkv * pl.SB * pl.Rp * desc->d * 4);
     const bool mfma = desc->dtype == NECTAR_BF16;
     MlpParams a{};
     a.q = q; a.W1 = m->W1; a.W2t = m->W2t; a.Ws = m->Ws; a.ws2 = m->ws2;

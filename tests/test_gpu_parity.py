@@ -140,7 +140,8 @@ def _mlp_oracle(q, P, dt, Hq, Hkv, act):
 
 
 @pytest.mark.parametrize("R,Hq,Hkv,Ht,Hs", [(5, 14, 2, 100, 70), (1, 32, 8, 256, 96), (20, 8, 2, 64, 33),
-                                             (3, 4, 1, 0, 40), (3, 4, 1, 50, 0), (10, 16, 4, 300, 200)])
+                                             (3, 4, 1, 0, 40), (3, 4, 1, 50, 0), (10, 16, 4, 300, 200),
+                                             (64, 32, 8, 600, 300)])
 @pytest.mark.parametrize("act", ["gelu", "silu", "gelu_tanh"])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_mlp_bf16(nx, R, Hq, Hkv, Ht, Hs, act, splits):

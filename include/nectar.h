@@ -15,6 +15,7 @@
  *   nectar_local_attn_lse   causal local attention (log Z_local, A_local),
  *                           section 2.2, optionally merged with a document pair
  *   nectar_merge            the log-sum-exp merge of Eqs. (3.4)-(3.5)
+ *   nectar_layer_step       all of the above for one layer step, fused
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -185,6 +186,41 @@ NECTAR_API nectar_status nectar_local_attn_lse(const nectar_attn_desc *desc, con
 NECTAR_API nectar_status nectar_merge(const nectar_attn_desc *desc, const float *a, const float *A,
                            const float *lam, const float *A_loc, void *out, float *lse_out,
                            void *stream);
+
+/*
+ * One layer step of both paths, fused (sections 2.1-2.2; the step loop of a
+ * decode or prefill pass).  For every query row it computes the local pair over
+ * the causal local set (as nectar_local_attn_lse), the exact document pair
+ * (alpha, A) over k, v [Hkv][n][d] (as nectar_doc_attn_exact) when any exact
+ * output is requested, and the module pair (a, A) (as nectar_module_forward)
+ * when `module` is given, and merges each document-side pair with the local
+ * pair (Eqs. (3.4)-(3.5)).  The parts' split partials go to the workspace and
+ * one finishing pass folds them all, so the step takes (number of parts + 1)
+ * kernel launches.  Outputs (all optional; NULL skips, at least one given):
+ *   out_exact [R][Hq][d] (dtype), lse_exact [R][Hq]: exact path output;
+ *   alpha_out, A_out: the exact document pair (the regression targets);
+ *   out_nectar, lse_nectar: Nectar path output; a_out, Am_out: the module pair
+ *   (given iff module != NULL);
+ *   lam_out, Aloc_out: the local pair.
+ * k, v may be NULL when n == 0 or no exact output is requested.  `exact` of the
+ * size query says whether exact outputs will be requested.
+ */
+typedef struct {
+    void *out_exact;  float *lse_exact;
+    float *alpha_out; float *A_out;
+    void *out_nectar; float *lse_nectar;
+    float *a_out;     float *Am_out;
+    float *lam_out;   float *Aloc_out;
+} nectar_step_outputs;
+
+NECTAR_API size_t nectar_layer_step_workspace_size(const nectar_attn_desc *desc, int64_t n,
+                                                   const nectar_local_desc *loc, const nectar_module *module,
+                                                   int exact);
+NECTAR_API nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const nectar_local_desc *loc,
+                                           const void *q, const void *k, const void *v, const void *k_loc,
+                                           const void *v_loc, const nectar_module *module,
+                                           const nectar_step_outputs *outs, void *ws, size_t ws_bytes,
+                                           void *stream);
 
 /* Zero-fills ws_bytes of device memory on `stream` with a fill kernel (no
  * memset node, so it can be captured in a graph); ws must be 16-byte aligned.

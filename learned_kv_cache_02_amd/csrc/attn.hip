@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256, RT == 1 ? NECTAR_RT1_WAVES_PER_SIMD : 1) void 
     for (int rt = 0; rt < RT; ++rt) {
         const int rho = (rg * RT + rt) * 16 + c;
         if (!owner || rho >= a.Rp) continue;
-        if (a.SB == 1) {
+        if (a.SB == 1 && !a.defer) {
             finish_row_lanes<D, OutT>(a, out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq), g, m[rt], l[rt], O[rt]);
         } else {
             const size_t row = (size_t)(p * a.SB + sb) * a.Rp + rho;

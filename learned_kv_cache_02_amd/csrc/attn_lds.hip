@@ -254,7 +254,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
     for (int rt = 0; rt < RT; ++rt) {
         const int rho = rb * kBlockRows + (w * RT + rt) * 16 + c;
         if (rho >= a.Rp) continue;
-        if (a.SB == 1) {
+        if (a.SB == 1 && !a.defer) {
             finish_row_lanes<kD, uint16_t>(a, out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq), g, m[rt], l[rt], O[rt]);
         } else {
             const size_t row = (size_t)(p * a.SB + sb) * a.Rp + rho;

@@ -21,6 +21,7 @@ struct AttnParams {
     // RB = ceil(RG / WR).  fp32 path: one wave per (row, split), SB = S.
     int P, S, chunk, RG, WR, WS, RB, SB;
     int xcd_group;       // LDS-staged kernel: row blocks of a split share an XCD
+    int defer;           // write partials even when SB == 1 (a later pass finishes)
     float *part_O;       // [P][SB][Rp][d]    unnormalised read-out
     float2 *part_ml;     // [P][SB][Rp]       (running max in log2 units, sum)
     // Row finishing in place when SB == 1 (same meaning as in CombineParams).
@@ -51,7 +52,37 @@ struct MlpParams {
     int S, chunk_t, chunk_s, RG, WR, WS, RB, SB;
     float *part_O;   // [Hkv][SB][Rp][d]
     float *part_s;   // [Hkv][SB][Rp]
-    float *a_out, *A_out;   // written directly when SB == 1
+    float *a_out, *A_out;   // written directly when SB == 1 and !defer
+    int defer;              // write partials even when SB == 1 (a later pass finishes)
+};
+
+// One document-side part of a layer step, finished together with the local
+// part: split partials of the exact document attention or of a Quadrature
+// module (log-sum-exp form: ml != NULL) or of an MLP module (plain sums:
+// s != NULL, plus the output biases).  Rows are those of the document problems
+// ([Hkv][S][R * G]).
+struct FinishSet {
+    const float *O;          // [Hkv][S][Rp_doc][d]
+    const float2 *ml;        // [Hkv][S][Rp_doc] (max in log2 units, sum) or NULL
+    const float *s;          // [Hkv][S][Rp_doc] score partials or NULL
+    const float *b2, *bs2;   // MLP output biases (sum form)
+    int S;
+    float *lse_out, *A_out;  // the part's pair (nullable)
+    void *out;               // merge with the local pair, typed by dtype (nullable)
+    float *out_lse;          // (nullable)
+};
+
+// Finishing pass of a layer step: per local row, fold the local partials
+// ([P][S_loc][Rp] over problems p = b * Hkv + h) and up to two document-side
+// parts, write the pairs and the merged outputs.
+struct FinishParams {
+    const float *loc_O;
+    const float2 *loc_ml;
+    int S_loc;
+    float *lam_out, *Aloc_out;   // local pair (nullable)
+    FinishSet set[2];
+    int nsets;
+    int Hq, G, Hkv, Tq, P, Rp, Rp_doc;
 };
 
 struct MlpReduceParams {
@@ -85,5 +116,6 @@ hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st);
 hipError_t launch_mlp_prefill(const MlpParams &p, hipStream_t st);
 hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+hipError_t launch_finish(const FinishParams &p, int dtype, int d, hipStream_t st);
 
 }  // namespace nectar

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void mlp_partial_mfma(MlpParams a) {
     for (int rt = 0; rt < RT; ++rt) {
         const int rho = (rg * RT + rt) * 16 + c;
         if (rho >= a.Rp) continue;
-        if (a.SB == 1) {
+        if (a.SB == 1 && !a.defer) {
             const int t = rho / a.G, gg = rho - t * a.G;
             const size_t o = (size_t)t * a.Hq + h * a.G + gg;
             if (g == 0) a.a_out[o] = a.bs2[h] + sc[rt];

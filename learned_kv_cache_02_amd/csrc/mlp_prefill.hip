@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
         const float ssum = group4_sum(sc[rt]);
         const int rho = rb * kRows + (w * kRTW + rt) * 16 + c;
         if (rho >= a.Rp) continue;
-        if (a.SB > 1) {
+        if (a.SB > 1 || a.defer) {
             const size_t row = (size_t)(h * a.SB + sb) * a.Rp + rho;
             if (g == 0) a.part_s[row] = ssum;
             float *op = a.part_O + row * kD;

@@ -450,4 +450,172 @@ nectar_status nectar_merge(const nectar_attn_desc *desc, const float *a, const f
     return finish(launch_merge(p, desc->dtype, desc->d, st), st);
 }
 
+// ---------------------------------------------------------------------------
+// Whole layer step: deferred partials of every part, one finishing pass.
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Partial bytes of an attention plan when its finish is deferred.
+static size_t attn_partial_bytes(const nectar_attn_desc *d, const AttnPlan &pl) {
+    return pl.S > 0 ? (size_t)pl.P * pl.SB * pl.Rp * ((size_t)d->d * 4 + 8) : 0;
+}
+
+static size_t mlp_partial_bytes(const nectar_attn_desc *d, const MlpPlan &pl) {
+    return (size_t)d->Hkv * pl.SB * pl.Rp * ((size_t)d->d * 4 + 4);
+}
+
+struct StepPlan {
+    bool exact = false, mlp = false, kvp = false;
+    AttnPlan loc, doc, kvpl;
+    MlpPlan mlpl;
+    size_t off_doc = 0, off_mod = 0, bytes = 0;
+};
+
+static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_local_desc *loc,
+                          const nectar_module *m, bool exact) {
+    StepPlan sp;
+    const int G = d->Hq / d->Hkv, Rp_doc = d->R * G;
+    sp.loc = plan_attn(d, loc->B * d->Hkv, loc->Tq * G, loc->T_loc);
+    size_t off = align256(attn_partial_bytes(d, sp.loc));
+    sp.exact = exact;
+    if (exact) {
+        sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n);
+        sp.off_doc = off;
+        off += align256(attn_partial_bytes(d, sp.doc));
+    }
+    if (m && m->kind == NECTAR_MODULE_MLP) {
+        sp.mlp = true;
+        sp.mlpl = plan_mlp(d, m->Ht, m->Hs);
+        sp.off_mod = off;
+        off += align256(mlp_partial_bytes(d, sp.mlpl));
+    } else if (m) {
+        sp.kvp = true;
+        sp.kvpl = plan_attn(d, d->Hkv, Rp_doc, (long)m->p);
+        sp.off_mod = off;
+        off += align256(attn_partial_bytes(d, sp.kvpl));
+    }
+    sp.bytes = off;
+    return sp;
+}
+
+// Split partials of one attention plan into part (read-outs, then statistics).
+static hipError_t attn_partials(const nectar_attn_desc *d, const AttnPlan &pl, const void *q, const void *k,
+                                const void *v, int64_t bstride, int64_t hstride, int B, int Tq, long T_kv,
+                                int causal, int q_offset, void *part, hipStream_t st) {
+    if (pl.S == 0) return hipSuccess;
+    AttnParams a{};
+    a.q = q; a.k = k; a.v = v;
+    a.kv_bstride = bstride; a.kv_hstride = hstride;
+    a.Hq = d->Hq; a.G = d->Hq / d->Hkv; a.Hkv = d->Hkv; a.Tq = Tq; a.B = B; a.Rp = pl.Rp;
+    a.T_kv = (int)T_kv; a.causal = causal; a.q_offset = q_offset;
+    a.sl2 = score_scale(d) * 1.4426950408889634f;
+    a.P = pl.P; a.S = pl.S; a.chunk = pl.chunk; a.RG = pl.RG;
+    a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB;
+    a.xcd_group = pl.xcd ? 1 : 0;
+    a.defer = 1;
+    a.part_O = (float *)part;
+    a.part_ml = (float2 *)((char *)part + (size_t)pl.P * pl.SB * pl.Rp * d->d * 4);
+    return pl.lds ? launch_attn_rows_lds(a, pl.sh, st) : launch_attn_partial(a, d->dtype, d->d, pl.RT, st);
+}
+
+static hipError_t mlp_partials(const nectar_attn_desc *d, const MlpPlan &pl, const nectar_module *m,
+                               const void *q, void *part, hipStream_t st) {
+    MlpParams a{};
+    a.q = q; a.W1 = m->W1; a.W2t = m->W2t; a.Ws = m->Ws; a.ws2 = m->ws2;
+    a.b1 = m->b1; a.bs = m->bs; a.b2 = m->b2; a.bs2 = m->bs2;
+    a.Hq = d->Hq; a.G = d->Hq / d->Hkv; a.Hkv = d->Hkv; a.Rp = pl.Rp;
+    a.Ht = m->Ht; a.Hs = m->Hs; a.act = m->act;
+    a.S = pl.S; a.chunk_t = pl.ct; a.chunk_s = pl.cs; a.RG = pl.RG;
+    a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB;
+    a.defer = 1;
+    a.part_O = (float *)part;
+    a.part_s = (float *)((char *)part + (size_t)d->Hkv * pl.SB * pl.Rp * d->d * 4);
+    return pl.prefill ? launch_mlp_prefill(a, st) : launch_mlp_partial(a, d->dtype, d->d, pl.RT, st);
+}
+
+static bool exact_requested(const nectar_step_outputs *o) {
+    return o->out_exact || o->lse_exact || o->alpha_out || o->A_out;
+}
+
+size_t nectar_layer_step_workspace_size(const nectar_attn_desc *desc, int64_t n, const nectar_local_desc *loc,
+                                        const nectar_module *module, int exact) {
+    if (check_desc(desc) != NECTAR_OK || check_local(desc, loc) != NECTAR_OK) return 0;
+    if (n < 0 || n > 0x7fffffffL - kTile) return 0;
+    if (module && check_module(desc, module) != NECTAR_OK) return 0;
+    return plan_step(desc, n, loc, module, exact != 0).bytes;
+}
+
+nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const nectar_local_desc *loc,
+                                const void *q, const void *k, const void *v, const void *k_loc,
+                                const void *v_loc, const nectar_module *module,
+                                const nectar_step_outputs *outs, void *ws, size_t ws_bytes, void *stream) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if ((s = check_local(desc, loc)) != NECTAR_OK) return s;
+    if (!outs) return NECTAR_EINVAL;
+    if (module && (s = check_module(desc, module)) != NECTAR_OK) return s;
+    const bool exact = exact_requested(outs);
+    const bool nect = outs->out_nectar || outs->lse_nectar || outs->a_out || outs->Am_out;
+    if (nect != (module != nullptr)) return NECTAR_EINVAL;
+    if (!exact && !nect && !outs->lam_out && !outs->Aloc_out) return NECTAR_EINVAL;
+    if (n < 0) return NECTAR_EINVAL;
+    if (n > 0x7fffffffL - kTile) return NECTAR_EUNSUPPORTED;
+    const float *f32s[] = {outs->lse_exact, outs->alpha_out, outs->A_out, outs->lse_nectar, outs->a_out,
+                           outs->Am_out, outs->lam_out, outs->Aloc_out};
+    for (const float *f : f32s)
+        if (f && !f32_ok(f)) return NECTAR_EINVAL;
+    if ((outs->out_exact && !out_ok(outs->out_exact, desc->dtype)) ||
+        (outs->out_nectar && !out_ok(outs->out_nectar, desc->dtype)))
+        return NECTAR_EINVAL;
+    if (desc->R == 0) return NECTAR_OK;
+    if (!tensor_ok(q)) return NECTAR_EINVAL;
+    if (loc->T_loc > 0 && (!tensor_ok(k_loc) || !tensor_ok(v_loc))) return NECTAR_EINVAL;
+    if (exact && n > 0 && (!tensor_ok(k) || !tensor_ok(v))) return NECTAR_EINVAL;
+    const StepPlan sp = plan_step(desc, n, loc, module, exact);
+    if ((s = check_ws(sp.bytes, ws, ws_bytes)) != NECTAR_OK) return s;
+
+    hipStream_t st = (hipStream_t)stream;
+    char *w = (char *)ws;
+    const int G = desc->Hq / desc->Hkv;
+    FinishParams f{};
+    f.Hq = desc->Hq; f.G = G; f.Hkv = desc->Hkv; f.Tq = loc->Tq;
+    f.P = sp.loc.P; f.Rp = sp.loc.Rp; f.Rp_doc = desc->R * G;
+    f.lam_out = outs->lam_out; f.Aloc_out = outs->Aloc_out;
+    hipError_t e = hipSuccess;
+    if (sp.exact) {
+        e = attn_partials(desc, sp.doc, q, k, v, 0, n * desc->d, 1, desc->R, (long)n, 0, 0, w + sp.off_doc, st);
+        FinishSet &x = f.set[f.nsets++];
+        x.S = sp.doc.S > 0 ? sp.doc.SB : 0;
+        x.O = (const float *)(w + sp.off_doc);
+        x.ml = (const float2 *)(w + sp.off_doc + (size_t)sp.doc.P * sp.doc.SB * sp.doc.Rp * desc->d * 4);
+        x.lse_out = outs->alpha_out; x.A_out = outs->A_out; x.out = outs->out_exact; x.out_lse = outs->lse_exact;
+    }
+    if (e == hipSuccess && module) {
+        FinishSet &x = f.set[f.nsets++];
+        x.O = (const float *)(w + sp.off_mod);
+        x.lse_out = outs->a_out; x.A_out = outs->Am_out; x.out = outs->out_nectar; x.out_lse = outs->lse_nectar;
+        if (sp.mlp) {
+            e = mlp_partials(desc, sp.mlpl, module, q, w + sp.off_mod, st);
+            x.S = sp.mlpl.SB;
+            x.s = (const float *)(w + sp.off_mod + (size_t)desc->Hkv * sp.mlpl.SB * sp.mlpl.Rp * desc->d * 4);
+            x.b2 = module->b2; x.bs2 = module->bs2;
+        } else {
+            e = attn_partials(desc, sp.kvpl, q, module->W, module->Z, 0, module->p * desc->d, 1, desc->R,
+                              (long)module->p, 0, 0, w + sp.off_mod, st);
+            x.S = sp.kvpl.S > 0 ? sp.kvpl.SB : 0;
+            x.ml = (const float2 *)(w + sp.off_mod + (size_t)sp.kvpl.P * sp.kvpl.SB * sp.kvpl.Rp * desc->d * 4);
+        }
+    }
+    if (e == hipSuccess) {
+        const int64_t hstride = (int64_t)loc->T_cap * desc->d;
+        e = attn_partials(desc, sp.loc, q, k_loc, v_loc, hstride * desc->Hkv, hstride, loc->B, loc->Tq,
+                          loc->T_loc, 1, loc->q_offset, w, st);
+        f.S_loc = sp.loc.S > 0 ? sp.loc.SB : 0;
+        f.loc_O = (const float *)w;
+        f.loc_ml = (const float2 *)(w + (size_t)sp.loc.P * sp.loc.SB * sp.loc.Rp * desc->d * 4);
+    }
+    if (e == hipSuccess) e = launch_finish(f, desc->dtype, desc->d, st);
+    return finish(e, st);
+}
+
 }  // extern "C"

@@ -53,6 +53,11 @@ class Module(ctypes.Structure):
                 ("p", ctypes.c_int64), ("W", ctypes.c_void_p), ("Z", ctypes.c_void_p)]
 
 
+class StepOutputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("out_exact", "lse_exact", "alpha_out", "A_out", "out_nectar",
+                                                "lse_nectar", "a_out", "Am_out", "lam_out", "Aloc_out")]
+
+
 _P = ctypes.c_void_p
 _D = ctypes.POINTER(AttnDesc)
 _lib.nectar_doc_attn_workspace_size.argtypes = [_D, ctypes.c_int64]
@@ -66,12 +71,18 @@ _lib.nectar_local_workspace_size.restype = ctypes.c_size_t
 _lib.nectar_local_attn_lse.argtypes = [_D, ctypes.POINTER(LocalDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, ctypes.c_size_t, _P]
 _lib.nectar_merge.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P]
+_lib.nectar_layer_step_workspace_size.argtypes = [_D, ctypes.c_int64, ctypes.POINTER(LocalDesc),
+                                                  ctypes.POINTER(Module), ctypes.c_int]
+_lib.nectar_layer_step_workspace_size.restype = ctypes.c_size_t
+_lib.nectar_layer_step.argtypes = [_D, ctypes.c_int64, ctypes.POINTER(LocalDesc), _P, _P, _P, _P, _P,
+                                   ctypes.POINTER(Module), ctypes.POINTER(StepOutputs), _P, ctypes.c_size_t, _P]
 _lib.nectar_status_string.argtypes = [ctypes.c_int]
 _lib.nectar_status_string.restype = ctypes.c_char_p
 _lib.nectar_abi_version.restype = ctypes.c_int
 _lib.nectar_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.nectar_workspace_init.restype = ctypes.c_int
-for _f in ("nectar_doc_attn_exact", "nectar_module_forward", "nectar_local_attn_lse", "nectar_merge"):
+for _f in ("nectar_doc_attn_exact", "nectar_module_forward", "nectar_local_attn_lse", "nectar_merge",
+           "nectar_layer_step"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -258,6 +269,49 @@ def merge(a, A, lam, A_loc, *, Hkv, out_dtype, out=None, lse_out=None):
     _check(_lib.nectar_merge(ctypes.byref(dsc), _ptr(a), _ptr(A), _ptr(lam), _ptr(A_loc), _ptr(out),
                              _ptr(lse_out), _stream()))
     return out, lse_out
+
+
+def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, module=None,
+               exact=True, pairs=False, scale=0.0, splits=0, out=None):
+    """One fused layer step: exact path over k, v [Hkv][n][d] (when `exact`), Nectar path
+    through `module` (when given), both merged with causal local attention over
+    k_loc/v_loc [B][Hkv][T_cap][d].  Returns a dict of the outputs: out_exact,
+    lse_exact, out_nectar, lse_nectar, and with `pairs` also alpha, A, a, Am, lam, Aloc.
+    `out` may supply preallocated tensors under the same keys."""
+    R, Hq, d = q.shape
+    T_cap = k_loc.shape[-2]
+    n = k.shape[-2] if (exact and k is not None) else 0
+    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    loc = LocalDesc(int(B), int(Tq), int(T_loc), int(T_cap), int(q_offset))
+    o = dict(out or {})
+    f32 = dict(dtype=torch.float32, device=q.device)
+
+    def want(key, shape, dtype=None):
+        if key not in o:
+            o[key] = torch.empty(shape, dtype=dtype or torch.float32, device=q.device)
+
+    if exact:
+        want("out_exact", (R, Hq, d), q.dtype)
+        want("lse_exact", (R, Hq))
+        if pairs:
+            want("alpha", (R, Hq)); want("A", (R, Hq, d))
+    if module is not None:
+        want("out_nectar", (R, Hq, d), q.dtype)
+        want("lse_nectar", (R, Hq))
+        if pairs:
+            want("a", (R, Hq)); want("Am", (R, Hq, d))
+    if pairs:
+        want("lam", (R, Hq)); want("Aloc", (R, Hq, d))
+    so = StepOutputs(*(_ptr(o.get(key)) for key in ("out_exact", "lse_exact", "alpha", "A", "out_nectar",
+                                                    "lse_nectar", "a", "Am", "lam", "Aloc")))
+    m = module.struct() if module is not None else None
+    mp = ctypes.byref(m) if m is not None else None
+    nbytes = int(_lib.nectar_layer_step_workspace_size(ctypes.byref(dsc), n, ctypes.byref(loc), mp, int(exact)))
+    wp, wn = _ws_args(nbytes, q.device)
+    _check(_lib.nectar_layer_step(ctypes.byref(dsc), n, ctypes.byref(loc), _ptr(q), _ptr(k) if exact else None,
+                                  _ptr(v) if exact else None, _ptr(k_loc), _ptr(v_loc), mp, ctypes.byref(so),
+                                  wp, wn, _stream()))
+    return o
 
 
 def workspace_init(buf: torch.Tensor):

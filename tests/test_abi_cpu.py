@@ -35,6 +35,11 @@ class Module(ctypes.Structure):
                [("p", ctypes.c_int64), ("W", ctypes.c_void_p), ("Z", ctypes.c_void_p)]
 
 
+class StepOuts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("out_exact", "lse_exact", "alpha_out", "A_out", "out_nectar",
+                                                "lse_nectar", "a_out", "Am_out", "lam_out", "Aloc_out")]
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
@@ -52,6 +57,11 @@ def lib():
     L.nectar_local_workspace_size.restype = ctypes.c_size_t
     L.nectar_local_attn_lse.argtypes = [D, ctypes.POINTER(Local)] + [P] * 9 + [P, ctypes.c_size_t, P]
     L.nectar_merge.argtypes = [D] + [P] * 7
+    L.nectar_layer_step_workspace_size.argtypes = [D, ctypes.c_int64, ctypes.POINTER(Local),
+                                                    ctypes.POINTER(Module), ctypes.c_int]
+    L.nectar_layer_step_workspace_size.restype = ctypes.c_size_t
+    L.nectar_layer_step.argtypes = [D, ctypes.c_int64, ctypes.POINTER(Local), P, P, P, P, P,
+                                    ctypes.POINTER(Module), ctypes.POINTER(StepOuts), P, ctypes.c_size_t, P]
     L.nectar_status_string.argtypes = [ctypes.c_int]
     L.nectar_status_string.restype = ctypes.c_char_p
     return L
@@ -68,7 +78,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert lib.nectar_abi_version() == 1
@@ -213,3 +223,39 @@ def test_oracle_and_product_share_no_code():
     for f in ("nectar.py", "build_native.py", "__init__.py"):
         txt = open(os.path.join(ROOT, "learned_kv_cache_02_amd", f)).read()
         assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def test_layer_step_validation(lib):
+    d = Desc(1, 32, 8, 128, 1, 0.0, 0)
+    loc = Local(1, 1, 513, 513, 512)
+    m = _mlp_module(4608, 2944)
+
+    def call(outs, module=None, n=61440, ws=None, nbytes=0, q=A16, k=A16, lc=loc, desc=d):
+        return lib.nectar_layer_step(ctypes.byref(desc), n, ctypes.byref(lc) if lc else None, q, k, A16, A16,
+                                     A16, ctypes.byref(module) if module else None,
+                                     ctypes.byref(outs) if outs else None, ws, nbytes, None)
+
+    both = StepOuts(out_exact=A16, lse_exact=A16, out_nectar=A16, lse_nectar=A16)
+    exact_only = StepOuts(out_exact=A16, lse_exact=A16)
+    assert call(None) == EINVAL                                        # no output struct
+    assert call(StepOuts()) == EINVAL                                  # nothing requested
+    assert call(both) == EINVAL                                        # Nectar outputs without a module
+    assert call(exact_only, module=m) == EINVAL                        # module without Nectar outputs
+    assert call(both, module=m, lc=None) == EINVAL
+    assert call(both, module=m, lc=Local(2, 1, 513, 513, 512)) == EINVAL     # B * Tq != R
+    assert call(both, module=m, n=-1) == EINVAL
+    assert call(StepOuts(out_exact=A16 + 1), module=None) == EINVAL    # misaligned bf16 output
+    assert call(exact_only, q=MIS) == EINVAL
+    assert call(exact_only, k=None) == EINVAL                          # exact output needs the cache
+    bad = _mlp_module(); bad.act = 7
+    assert call(both, module=bad) == EINVAL
+    need = lib.nectar_layer_step_workspace_size(ctypes.byref(d), 61440, ctypes.byref(loc), ctypes.byref(m), 1)
+    # deferred partials of all three parts: the document's 60 and the local part's 3 blocks per
+    # head (4 rows x 520 B each), plus the module's split partials
+    assert need >= 8 * 60 * 4 * 520 + 8 * 3 * 4 * 520
+    assert call(both, module=m, ws=A16, nbytes=need - 1) == EWORKSPACE
+    only_loc = lib.nectar_layer_step_workspace_size(ctypes.byref(d), 61440, ctypes.byref(loc), None, 0)
+    assert 0 < only_loc < need
+    assert lib.nectar_layer_step_workspace_size(None, 61440, ctypes.byref(loc), None, 1) == 0
+    d0 = Desc(0, 32, 8, 128, 1, 0.0, 0)                                # R == 0: valid no-op
+    assert call(exact_only, desc=d0, lc=Local(0, 1, 513, 513, 512), q=None) == OK

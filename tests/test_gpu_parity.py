@@ -245,6 +245,77 @@ def test_worked_example_on_gpu(nx):
     assert np.allclose(host(out), 4.0, atol=1e-6) and abs(host(lse)[0, 0] - math.log(12.0)) < 1e-6
 
 
+# --- the fused layer step ----------------------------------------------------------------
+
+STEP_CASES = {
+    # name: (dt, d, B, Tq, T_loc, T_cap, q_offset, Hq, Hkv, n, module)
+    "decode_bf16": ("bf16", 128, 1, 1, 513, 513, 512, 32, 8, 3000, ("mlp", 256, 96)),
+    "batch64_bf16": ("bf16", 128, 64, 1, 300, 320, 299, 32, 8, 2000, ("mlp", 600, 300)),
+    "prefill_bf16": ("bf16", 128, 2, 100, 100, 100, 0, 28, 4, 1500, ("mlp", 300, 200)),
+    "kvpair_bf16": ("bf16", 128, 8, 1, 257, 384, 256, 28, 4, 5000, ("kvpair", 700)),
+    "tiny_f32_d64": ("f32", 64, 1, 16, 16, 16, 0, 2, 1, 512, ("mlp", 256, 256)),
+    "decode_bf16_d64": ("bf16", 64, 3, 1, 40, 48, 39, 8, 2, 777, ("mlp", 100, 70)),
+    "empty_doc_and_local": ("bf16", 128, 2, 1, 0, 8, 0, 8, 2, 0, ("mlp", 0, 40)),
+    "exact_only": ("bf16", 128, 4, 1, 50, 64, 49, 16, 4, 1000, None),
+    "module_only": ("bf16", 128, 4, 2, 30, 32, 28, 16, 4, None, ("mlp", 64, 32)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STEP_CASES))
+def test_layer_step(nx, name):
+    """nectar_layer_step against the oracle: every pair it writes and both merged
+    outputs; the exact output also against full attention over [document; local]."""
+    dt, d, B, Tq, T, T_cap, qoff, Hq, Hkv, n, mod = STEP_CASES[name]
+    print("case layer_step %s" % name, flush=True)
+    g = _rng(20, len(name), B, Tq, T)
+    R = B * Tq
+    q = _store(g.standard_normal((R, Hq, d)), dt)
+    Kl, Vl = (_store(g.standard_normal((B, Hkv, T_cap, d)), dt) for _ in range(2))
+    Klv, Vlv = (np.ascontiguousarray(x[:, :, :T]) for x in (Kl, Vl))
+    kw = dict(dt=dt, Hq=Hq, Hkv=Hkv)
+    lkw = dict(B=B, Tq=Tq, Tloc=T, q_offset=qoff, **kw)
+    exact = n is not None
+    k = v = None
+    if exact:
+        K, V = (_store(g.standard_normal((Hkv, n, d)), dt) for _ in range(2))
+        k, v = dev(K), dev(V)
+    module = None
+    if mod is not None and mod[0] == "mlp":
+        P = _mlp_np(g, Hkv, d, mod[1], mod[2], dt)
+        module = _mlp_dev(nx, P, nx.GELU)
+    elif mod is not None:
+        W, Z = (_store(g.standard_normal((Hkv, mod[1], d)), dt) for _ in range(2))
+        module = nx.KVPairModule(dev(W), dev(Z))
+    o = nx.layer_step(dev(q), dev(Kl), dev(Vl), Hkv, B=B, Tq=Tq, T_loc=T, q_offset=qoff, k=k, v=v,
+                      module=module, exact=exact, pairs=True)
+    o = {key: host(t) for key, t in o.items()}
+    if dt == "f32":
+        to = tl = ATOL_F32
+        rel = None
+    else:
+        to, tl, rel = ATOL_OUT_BF16, ATOL_LSE_BF16, REL_L2_BF16
+    el, eAl = oracle.local_attn(q, Klv, Vlv, **lkw)
+    check("lambda", o["lam"], el, tl)
+    check("A_local", o["Aloc"], eAl, to, rel)
+    if exact:
+        ea, eA = oracle.doc_attn(q, K, V, **kw)
+        check("alpha", o["alpha"], ea, tl)
+        check("A", o["A"], eA, to, rel)
+        flse, fout = oracle.full_attn(q, K, V, Klv, Vlv, **lkw)
+        check("exact out vs full attention", o["out_exact"], fout, to, rel)
+        check("exact lse vs full attention", o["lse_exact"], flse, tl)
+    if module is not None:
+        if mod[0] == "mlp":
+            em, eAm = _mlp_oracle(q, P, dt, Hq, Hkv, "gelu")
+        else:
+            em, eAm = oracle.kvpair(q, W, Z, **kw)
+        check("module a", o["a"], em, tl)
+        check("module A", o["Am"], eAm, to, rel)
+        eo, eol = oracle.merge(em, eAm, el, eAl)
+        check("nectar out", o["out_nectar"], eo, to, rel)
+        check("nectar lse", o["lse_nectar"], eol, tl)
+
+
 # --- workloads end to end -----------------------------------------------------------------
 
 def _run_layer(nx, cfg, inputs, step=0):

@@ -8,9 +8,14 @@ GELU).  A step is one decode step of one layer through the whole hot path:
 
   exact document attention (alpha, A) over the 61,440-key cache,
   the MLP module forward (a, A_theta),
-  causal local attention over the 513 local keys, merged with the module pair
-  (the Nectar output), and the merge of the exact pair with the local pair
-  (the exact output).
+  causal local attention over the 513 local keys (lambda, A_local),
+  and both merges: the module pair with the local pair (the Nectar output) and
+  the exact pair with the local pair (the exact output),
+
+through the fused layer-step entry point (the document, local and module
+partials in one launch, then one finishing launch that writes every pair and
+both outputs).  The same step through the four separate entry points is timed
+too (`paths.step_unfused_us`).
 
 Every step reads a distinct layer replica (its own document cache, module and
 local cache), so consecutive steps never hit a cache the previous step
@@ -135,13 +140,29 @@ def main():
         nectar.merge(o["alpha"], o["Ax"], o["lam"], o["Al"], Hkv=Hkv, out_dtype=torch.bfloat16,
                      out=o["out_x"], lse_out=o["lse_x"])
 
+    pair_out = {"out_exact": o["out_x"], "lse_exact": o["lse_x"], "alpha": o["alpha"], "A": o["Ax"],
+                "out_nectar": o["out_n"], "lse_nectar": o["lse_n"], "a": o["a"], "Am": o["Am"],
+                "lam": o["lam"], "Aloc": o["Al"]}
+
+    def fused(r, exact=True, nect=True):
+        x = reps[r]
+        keys = (["out_exact", "lse_exact", "alpha", "A"] if exact else []) + \
+               (["out_nectar", "lse_nectar", "a", "Am"] if nect else []) + ["lam", "Aloc"]
+        nectar.layer_step(x["q"], x["Kl"], x["Vl"], Hkv, B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff,
+                          k=x["K"] if exact else None, v=x["V"] if exact else None,
+                          module=x["mod"] if nect else None, exact=exact, pairs=True,
+                          out={k: pair_out[k] for k in keys})
+
     steps = {
-        "step": lambda r: (doc(r), module(r), local_nectar(r), merge_exact(r)),
-        "nectar": lambda r: (module(r), local_nectar(r)),
-        "exact": lambda r: (doc(r), local_pair(r), merge_exact(r)),
+        # the whole step of both paths through the fused layer-step entry point
+        "step": lambda r: fused(r),
+        "nectar": lambda r: fused(r, exact=False),
+        "exact": lambda r: fused(r, nect=False),
         "doc": lambda r: doc(r),
+        # the same step through the four separate entry points (seven launches)
+        "step_unfused": lambda r: (doc(r), module(r), local_nectar(r), merge_exact(r)),
     }
-    names = [args.only] if args.only else ["step", "nectar", "exact", "doc"]
+    names = [args.only] if args.only else ["step", "nectar", "exact", "doc", "step_unfused"]
 
     # warm every call once (allocates the binding's cached workspace outside capture)
     for fn in steps.values():
@@ -219,6 +240,8 @@ def main():
     if "nectar" in ms and "exact" in ms:
         paths["nectar_speedup_vs_exact"] = ms["exact"] / ms["nectar"]
         paths["module_rho"] = cfg.rho(cfg.mlps[0].params(d))
+    if "step_unfused" in ms:
+        paths["step_unfused_us"] = ms["step_unfused"] * 1e3
     res["paths"] = paths
     if "doc" in ms:
         us = ms["doc"] * 1e3
@@ -295,9 +318,20 @@ def workload_layer(torch, nectar, cfg, dev):
         nectar.local_attn_lse(q, Kl, Vl, Hkv, B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff, want_pair=False,
                               doc_lse=x_lse, doc_A=x_A, out=out, out_lse=olse)
 
+    so = {"out_exact": out, "lse_exact": olse, "out_nectar": out, "lse_nectar": olse}
+
+    def path(i, exact, mdl):
+        K, V = KV[i % nrep]
+        keys = ["out_exact", "lse_exact"] if exact else ["out_nectar", "lse_nectar"]
+        nectar.layer_step(q, Kl, Vl, Hkv, B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff, k=K if exact else None,
+                          v=V if exact else None, module=mdl, exact=exact, out={k: so[k] for k in keys})
+
     parts = {"exact_doc": doc, "module": module, "local_merge": lambda i: local(i, a, Am),
-             "nectar_path": lambda i: (module(i), local(i, a, Am)),
-             "exact_path": lambda i: (doc(i), local(i, al, Ax))}
+             "nectar_path": lambda i: path(i, False, mod),
+             "exact_path": lambda i: path(i, True, None)}
+    if cfg.kv_pairs:
+        kvp = nectar.KVPairModule(rn(Hkv, cfg.kv_pairs, d), rn(Hkv, cfg.kv_pairs, d))
+        parts["kvpair_path"] = lambda i: path(i, False, kvp)
     for fn in parts.values():
         fn(0)
     torch.cuda.synchronize()
@@ -335,6 +369,9 @@ def workload_layer(torch, nectar, cfg, dev):
            "module": "MLP %d/%d" % (m.Ht, m.Hs), "us": us,
            "qtok_s_layer": {"nectar": R / (us["nectar_path"] * 1e-6), "exact": R / (us["exact_path"] * 1e-6)},
            "nectar_speedup_vs_exact": us["exact_path"] / us["nectar_path"]}
+    if "kvpair_path" in us:
+        res["qtok_s_layer"]["kvpair"] = R / (us["kvpair_path"] * 1e-6)
+        res["kvpair_speedup_vs_exact"] = us["exact_path"] / us["kvpair_path"]
     if cfg.prefill:
         flops = R * Hq * n * 4 * d
         res["exact_doc_roofline"] = {"bound": "mfma", "tflops": flops / us["exact_doc"] / 1e6,
@@ -343,7 +380,7 @@ def workload_layer(torch, nectar, cfg, dev):
         res["exact_doc_roofline"] = {"bound": "hbm", "gbs": doc_bytes / us["exact_doc"] / 1e3,
                                      "frac": doc_bytes / us["exact_doc"] / 1e3 / HBM_PEAK_GBS,
                                      "bytes_per_launch": doc_bytes}
-    del KV, q, Kl, Vl, mod
+    del KV, q, Kl, Vl, mod, parts
     torch.cuda.empty_cache()
     return res
 

@@ -31,243 +31,16 @@
 // attn_combine folds the per-block partials.  (A last-arriving-block fold was
 // measured slower: the agent-scope fences it needs write back and invalidate
 // the XCD's L2 on every block.)
-#include "attn_common.hpp"
+#include "attn_body.hpp"
 
 namespace nectar {
 
-template <int D> struct VRow;
-template <> struct VRow<128> { typedef u32x4 T; };   // 8 bf16 per lane per key
-template <> struct VRow<64> { typedef u32x2 T; };    // 4 bf16 per lane per key
-
-template <int D> struct KVTile {
-    static constexpr int KS = D / 32;
-    u32x4 k[2][KS];
-    typename VRow<D>::T v[8];
-};
-
-template <int D>
-__device__ __forceinline__ void load_kv_tile(KVTile<D> &T, const uint16_t *kb, const uint16_t *vb,
-                                             int k0, int kmax, int g, int c) {
-    constexpr int KS = D / 32, DV = D / 16;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int key = min(k0 + 16 * hh + c, kmax);
-        const uint16_t *kp = kb + (size_t)key * D;
-#pragma unroll
-        for (int kt = 0; kt < KS; ++kt) T.k[hh][kt] = stream_load((const u32x4 *)(kp + (4 * kt + g) * 8));
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int key = min(k0 + slot_key(g, j), kmax);
-        T.v[j] = stream_load((const typename VRow<D>::T *)(vb + (size_t)key * D + c * DV));
-    }
-}
-
-// vt[mm] slot j = V[key(g, j)][c * DV + mm]: in-lane 8 x DV transpose of bf16.
-template <int D>
-__device__ __forceinline__ void transpose_v(const KVTile<D> &T, u32x4 (&vt)[D / 16]) {
-    constexpr int DV = D / 16;
-#pragma unroll
-    for (int mm = 0; mm < DV; ++mm) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t a0 = T.v[2 * w][mm >> 1], a1 = T.v[2 * w + 1][mm >> 1];
-            vt[mm][w] = (mm & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-        }
-    }
-}
-
-template <int D, int RT>
-__device__ __forceinline__ void attend_tile(const KVTile<D> &T, int k0, const u32x4 (&qv)[RT][D / 32],
-                                            const int (&lim)[RT], float sl2, int g,
-                                            f32x4 (&O)[RT][D / 16], float (&m)[RT], float (&l)[RT]) {
-    constexpr int KS = D / 32, DV = D / 16;
-    u32x4 vt[DV];
-    transpose_v<D>(T, vt);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kt = 0; kt < KS; ++kt) {
-            s0 = mfma16(T.k[0][kt], qv[rt][kt], s0);
-            s1 = mfma16(T.k[1][kt], qv[rt][kt], s1);
-        }
-        float sv[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { sv[r] = s0[r] * sl2; sv[4 + r] = s1[r] * sl2; }
-        if (k0 + 32 > lim[rt]) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (k0 + slot_key(g, j) >= lim[rt]) sv[j] = -INFINITY;
-        }
-        float mt = sv[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
-        mt = group4_max(mt);
-        const float mnew = fmaxf(m[rt], mt);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = fast_exp2(m[rt] - muse);
-        float pv[8], ps = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { pv[j] = fast_exp2(sv[j] - muse); ps += pv[j]; }
-        l[rt] = l[rt] * alpha + ps;
-        m[rt] = mnew;
-        const u32x4 P = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
-                         pack_bf16(pv[6], pv[7])};
-#pragma unroll
-        for (int mm = 0; mm < DV; ++mm) {
-            O[rt][mm] *= alpha;
-            O[rt][mm] = mfma16(vt[mm], P, O[rt][mm]);
-        }
-    }
-}
-
-#ifndef NECTAR_RT1_WAVES_PER_SIMD
-#define NECTAR_RT1_WAVES_PER_SIMD 2
-#endif
-#ifndef NECTAR_RT1_SUB
-#define NECTAR_RT1_SUB 2
-#endif
-// RT == 1: two waves per SIMD (8 per CU), each with a 32 KB batch in flight.
+// RT == 1: two waves per SIMD (8 per CU), each with a 32 KB batch in flight;
+// blocks [0, nb0) serve the first problem set, the rest the second.
 template <int D, int RT, int SUB, typename OutT>
-__global__ __launch_bounds__(256, RT == 1 ? NECTAR_RT1_WAVES_PER_SIMD : 1) void attn_partial_mfma(AttnParams a) {
-    constexpr int KS = D / 32, DV = D / 16;
-    // Fold buffers (used when WS > 1, hence WR <= 2): per row group one f32x4
-    // per (register, lane), lane-major so each wave access is conflict-free.
-    __shared__ f32x4 fold_O[2][RT * DV][64];
-    __shared__ float fold_l[2][RT][64];
-    __shared__ float fold_m[4][RT][16];
-
-    const int w = threadIdx.x >> 6;
-    const int wr = w % a.WR, ws = w / a.WR;
-    int blk = blockIdx.x;
-    const int sb = blk % a.SB;
-    blk /= a.SB;
-    const int rb = blk % a.RB;
-    const int p = blk / a.RB;
-    const int rg = rb * a.WR + wr;
-    const int s = sb * a.WS + ws;
-    const int b = p / a.Hkv, h = p - b * a.Hkv;
-    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    const uint16_t *kb = (const uint16_t *)a.k + b * a.kv_bstride + h * a.kv_hstride;
-    const uint16_t *vb = (const uint16_t *)a.v + b * a.kv_bstride + h * a.kv_hstride;
-
-    u32x4 qv[RT][KS];
-    int lim[RT];
-    int wlim = 0;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int rho = (rg * RT + rt) * 16 + c;
-        if (rg < a.RG && rho < a.Rp) {
-            const int t = rho / a.G, gg = rho - t * a.G;
-            const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(b * a.Tq + t) * a.Hq + h * a.G + gg) * D;
-#pragma unroll
-            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
-            int L = a.T_kv;
-            if (a.causal) L = min(L, a.q_offset + t + 1);
-            lim[rt] = max(L, 0);
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
-            lim[rt] = 0;
-        }
-        wlim = max(wlim, lim[rt]);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) wlim = max(wlim, __shfl_xor(wlim, o, 64));
-
-    f32x4 O[RT][DV];
-    float m[RT], l[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        m[rt] = -INFINITY;
-        l[rt] = 0.f;
-#pragma unroll
-        for (int mm = 0; mm < DV; ++mm) O[rt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const int k_lo = s * a.chunk;
-    const int k_hi = min(k_lo + a.chunk, wlim);
-    if (k_lo < k_hi) {
-        // Batches of SUB 32-key tiles: every load of a batch (SUB x 16 KB) is
-        // issued before its first use, and the two waves sharing each SIMD keep
-        // the memory system busy while the other one computes.
-        const int kmax = a.T_kv - 1;
-        int limw[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) limw[rt] = min(lim[rt], k_hi);
-        for (int k0 = k_lo; k0 < k_hi; k0 += 32 * SUB) {
-            KVTile<D> tl[SUB];
-#pragma unroll
-            for (int u = 0; u < SUB; ++u) load_kv_tile<D>(tl[u], kb, vb, min(k0 + 32 * u, kmax), kmax, g, c);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < SUB; ++u) attend_tile<D, RT>(tl[u], k0 + 32 * u, qv, limw, a.sl2, g, O, m, l);
-        }
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) l[rt] = group4_sum(l[rt]);
-
-    if (a.WS > 1) {
-        // Fold the WS splits of this row group: common max, rescale, sum.
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            if (g == 0) fold_m[w][rt][c] = m[rt];
-        __syncthreads();
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            float M = -INFINITY;
-            for (int k = 0; k < a.WS; ++k) M = fmaxf(M, fold_m[k * a.WR + wr][rt][c]);
-            const float sc = (m[rt] == -INFINITY) ? 0.f : exp2f(m[rt] - M);
-            l[rt] *= sc;
-#pragma unroll
-            for (int mm = 0; mm < DV; ++mm) O[rt][mm] *= sc;
-            m[rt] = M;
-        }
-        for (int k = a.WS - 1; k >= 1; --k) {
-            if (ws == k) {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    fold_l[wr][rt][lane] = (k == a.WS - 1) ? l[rt] : fold_l[wr][rt][lane] + l[rt];
-#pragma unroll
-                    for (int mm = 0; mm < DV; ++mm)
-                        fold_O[wr][rt * DV + mm][lane] =
-                            (k == a.WS - 1) ? O[rt][mm] : fold_O[wr][rt * DV + mm][lane] + O[rt][mm];
-                }
-            }
-            __syncthreads();
-        }
-        if (ws == 0) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                l[rt] += fold_l[wr][rt][lane];
-#pragma unroll
-                for (int mm = 0; mm < DV; ++mm) O[rt][mm] += fold_O[wr][rt * DV + mm][lane];
-            }
-        }
-    }
-    const bool owner = (a.WS == 1 || ws == 0) && rg < a.RG;
-
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int rho = (rg * RT + rt) * 16 + c;
-        if (!owner || rho >= a.Rp) continue;
-        if (a.SB == 1 && !a.defer) {
-            finish_row_lanes<D, OutT>(a, out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq), g, m[rt], l[rt], O[rt]);
-        } else {
-            const size_t row = (size_t)(p * a.SB + sb) * a.Rp + rho;
-            if (g == 0) a.part_ml[row] = make_float2(m[rt], l[rt]);
-            float *op = a.part_O + row * D;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int m4 = 0; m4 < DV; m4 += 4) {
-                    f32x4 v = {O[rt][m4][r], O[rt][m4 + 1][r], O[rt][m4 + 2][r], O[rt][m4 + 3][r]};
-                    *(f32x4 *)(op + DV * (4 * g + r) + m4) = v;
-                }
-        }
-    }
-
+__global__ __launch_bounds__(256, RT == 1 ? NECTAR_RT1_WAVES_PER_SIMD : 1) void attn_partial_mfma(AttnGroup gr) {
+    const int set = group_set(gr, (int)blockIdx.x);
+    attn_partial_body<D, RT, SUB, OutT>(gr.p[set], (int)blockIdx.x - (set ? gr.nb0 : 0));
 }
 
 // fp32 path: one wave per (problem, row, split); lanes own head dimensions,
@@ -454,15 +227,32 @@ int row_tiles_for(int Rp) { return Rp <= 16 ? 1 : 2; }
 
 static inline unsigned blocks_for_waves(long waves) { return (unsigned)((waves + 3) / 4); }
 
+static hipError_t launch_mfma_group(const AttnGroup &gr, long blocks, int d, int rt, hipStream_t st) {
+    dim3 grid((unsigned)blocks), block(256);
+#define NECTAR_ATTN_CASE(DD, RR) \
+    if (d == DD && rt == RR) { hipLaunchKernelGGL((attn_partial_mfma<DD, RR, (RR == 1 ? NECTAR_RT1_SUB : 1), uint16_t>), grid, block, 0, st, gr); return hipGetLastError(); }
+    NECTAR_ATTN_CASE(128, 1) NECTAR_ATTN_CASE(128, 2)
+    NECTAR_ATTN_CASE(64, 1) NECTAR_ATTN_CASE(64, 2)
+#undef NECTAR_ATTN_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_partial_pair(const AttnParams &p0, const AttnParams &p1, int d, int rt, hipStream_t st) {
+    AttnGroup gr;
+    gr.p[0] = p0;
+    gr.p[1] = p1;
+    gr.nb0 = (int)((long)p0.P * p0.RB * p0.SB);
+    return launch_mfma_group(gr, gr.nb0 + (long)p1.P * p1.RB * p1.SB, d, rt, st);
+}
+
 hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hipStream_t st) {
     if (dtype == 1) {
-        dim3 grid((unsigned)((long)p.P * p.RB * p.SB)), block(256);
-#define NECTAR_ATTN_CASE(DD, RR) \
-        if (d == DD && rt == RR) { hipLaunchKernelGGL((attn_partial_mfma<DD, RR, (RR == 1 ? NECTAR_RT1_SUB : 1), uint16_t>), grid, block, 0, st, p); return hipGetLastError(); }
-        NECTAR_ATTN_CASE(128, 1) NECTAR_ATTN_CASE(128, 2)
-        NECTAR_ATTN_CASE(64, 1) NECTAR_ATTN_CASE(64, 2)
-#undef NECTAR_ATTN_CASE
-        return hipErrorInvalidValue;
+        AttnGroup gr;
+        gr.p[0] = p;
+        gr.p[1] = p;
+        const long blocks = (long)p.P * p.RB * p.SB;
+        gr.nb0 = (int)blocks;
+        return launch_mfma_group(gr, blocks, d, rt, st);
     }
     const long waves = (long)p.P * p.S * p.Rp;
     dim3 grid(blocks_for_waves(waves)), block(256);

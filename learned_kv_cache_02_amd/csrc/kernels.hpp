@@ -31,6 +31,13 @@ struct AttnParams {
     float *out_lse;
 };
 
+// Two problem sets served by one launch of the register-direct attention
+// kernel (blocks [0, nb0) the first set); a single set repeats it.
+struct AttnGroup {
+    AttnParams p[2];
+    int nb0;
+};
+
 // Finishing pass over the split partials of AttnParams: writes the pair
 // (lse, A) and/or its merge with an extra (lse_x, A_x) pair.
 struct CombineParams {
@@ -109,6 +116,13 @@ struct LdsShape {
 };
 LdsShape lds_shape_for(int Rp);
 hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st);
+// One launch for two bf16 problem sets of the register-direct kernel with the same
+// head dimension and row tiling (independent blocks side by side).
+hipError_t launch_attn_partial_pair(const AttnParams &p0, const AttnParams &p1, int d, int rt, hipStream_t st);
+// One launch of register-direct bf16 attention blocks (one or two problem sets,
+// row tiling 1) and MLP module blocks (row tiling 1, decode kernel).
+hipError_t launch_step_partials(const AttnParams &p0, const AttnParams *p1, const MlpParams &m, int d,
+                                hipStream_t st);
 hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipStream_t st);
 hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st);

@@ -24,7 +24,10 @@ namespace {
 #define NECTAR_RT1_SUB 2
 #endif
 constexpr long kTargetWaves = NECTAR_TARGET_WAVES;
-constexpr long kTargetWavesMlp = 1024;
+#ifndef NECTAR_TARGET_WAVES_MLP
+#define NECTAR_TARGET_WAVES_MLP 1024
+#endif
+constexpr long kTargetWavesMlp = NECTAR_TARGET_WAVES_MLP;
 // Blocks a split plan of the LDS-staged kernel aims for: one per CU (a block
 // holds 96 KB of LDS, so one is resident per CU).
 #ifndef NECTAR_LDS_TARGET_BLOCKS
@@ -327,6 +330,33 @@ size_t nectar_module_workspace_size(const nectar_attn_desc *desc, const nectar_m
     return plan_mlp(desc, m->Ht, m->Hs).ws;
 }
 
+// The MLP module forward of a plan: partial kernel, then the split reduce
+// unless the partial kernel finished the rows itself.
+static hipError_t run_mlp(const nectar_attn_desc *desc, const MlpPlan &pl, const nectar_module *m, const void *q,
+                          float *a_out, float *A_out, void *ws, hipStream_t st) {
+    float *part_O = (float *)ws;
+    float *part_s = (float *)((char *)ws + (size_t)desc->Hkv * pl.SB * pl.Rp * desc->d * 4);
+    MlpParams a{};
+    a.q = q; a.W1 = m->W1; a.W2t = m->W2t; a.Ws = m->Ws; a.ws2 = m->ws2;
+    a.b1 = m->b1; a.bs = m->bs; a.b2 = m->b2; a.bs2 = m->bs2;
+    a.Hq = desc->Hq; a.G = desc->Hq / desc->Hkv; a.Hkv = desc->Hkv; a.Rp = pl.Rp;
+    a.Ht = m->Ht; a.Hs = m->Hs; a.act = m->act;
+    a.S = pl.S; a.chunk_t = pl.ct; a.chunk_s = pl.cs; a.RG = pl.RG;
+    a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB;
+    a.part_O = part_O; a.part_s = part_s;
+    a.a_out = a_out; a.A_out = A_out;
+    const bool in_place = pl.SB == 1 && (pl.prefill || desc->dtype == NECTAR_BF16);
+    hipError_t e = pl.prefill ? launch_mlp_prefill(a, st) : launch_mlp_partial(a, desc->dtype, desc->d, pl.RT, st);
+    if (e == hipSuccess && !in_place) {
+        MlpReduceParams r;
+        r.part_O = part_O; r.part_s = part_s; r.b2 = m->b2; r.bs2 = m->bs2;
+        r.Hq = desc->Hq; r.G = desc->Hq / desc->Hkv; r.Hkv = desc->Hkv; r.Rp = pl.Rp; r.S = pl.SB;
+        r.a_out = a_out; r.A_out = A_out;
+        e = launch_mlp_reduce(r, desc->d, st);
+    }
+    return e;
+}
+
 nectar_status nectar_module_forward(const nectar_attn_desc *desc, const nectar_module *m,
                                     const void *q, float *a_out, float *A_out, void *ws,
                                     size_t ws_bytes, void *stream) {
@@ -347,46 +377,7 @@ nectar_status nectar_module_forward(const nectar_attn_desc *desc, const nectar_m
     }
     const MlpPlan pl = plan_mlp(desc, m->Ht, m->Hs);
     if ((s = check_ws(pl.ws, ws, ws_bytes)) != NECTAR_OK) return s;
-    float *part_O = (float *)ws;
-    float *part_s = (float *)((char *)ws + (size_t)desc->Hkv * pl.SB * pl.Rp * desc->d * 4);
-    if (pl.prefill) {
-        MlpParams a{};
-        a.q = q; a.W1 = m->W1; a.W2t = m->W2t; a.Ws = m->Ws; a.ws2 = m->ws2;
-        a.b1 = m->b1; a.bs = m->bs; a.b2 = m->b2; a.bs2 = m->bs2;
-        a.Hq = desc->Hq; a.G = desc->Hq / desc->Hkv; a.Hkv = desc->Hkv; a.Rp = pl.Rp;
-        a.Ht = m->Ht; a.Hs = m->Hs; a.act = m->act;
-        a.S = pl.S; a.SB = pl.SB; a.chunk_t = pl.ct; a.chunk_s = pl.cs; a.RB = pl.RB;
-        a.part_O = part_O; a.part_s = part_s;
-        a.a_out = a_out; a.A_out = A_out;
-        hipError_t e = launch_mlp_prefill(a, st);
-        if (e == hipSuccess && pl.SB > 1) {
-            MlpReduceParams r;
-            r.part_O = part_O; r.part_s = part_s; r.b2 = m->b2; r.bs2 = m->bs2;
-            r.Hq = desc->Hq; r.G = desc->Hq / desc->Hkv; r.Hkv = desc->Hkv; r.Rp = pl.Rp; r.S = pl.SB;
-            r.a_out = a_out; r.A_out = A_out;
-            e = launch_mlp_reduce(r, desc->d, st);
-        }
-        return finish(e, st);
-    }
-    const bool mfma = desc->dtype == NECTAR_BF16;
-    MlpParams a{};
-    a.q = q; a.W1 = m->W1; a.W2t = m->W2t; a.Ws = m->Ws; a.ws2 = m->ws2;
-    a.b1 = m->b1; a.bs = m->bs; a.b2 = m->b2; a.bs2 = m->bs2;
-    a.Hq = desc->Hq; a.G = desc->Hq / desc->Hkv; a.Hkv = desc->Hkv; a.Rp = pl.Rp;
-    a.Ht = m->Ht; a.Hs = m->Hs; a.act = m->act;
-    a.S = pl.S; a.chunk_t = pl.ct; a.chunk_s = pl.cs; a.RG = pl.RG;
-    a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB;
-    a.part_O = part_O; a.part_s = part_s;
-    a.a_out = a_out; a.A_out = A_out;
-    hipError_t e = launch_mlp_partial(a, desc->dtype, desc->d, pl.RT, st);
-    if (e == hipSuccess && !(mfma && pl.SB == 1)) {
-        MlpReduceParams r;
-        r.part_O = part_O; r.part_s = part_s; r.b2 = m->b2; r.bs2 = m->bs2;
-        r.Hq = desc->Hq; r.G = desc->Hq / desc->Hkv; r.Hkv = desc->Hkv; r.Rp = pl.Rp; r.S = pl.SB;
-        r.a_out = a_out; r.A_out = A_out;
-        e = launch_mlp_reduce(r, desc->d, st);
-    }
-    return finish(e, st);
+    return finish(run_mlp(desc, pl, m, q, a_out, A_out, ws, st), st);
 }
 
 static nectar_status check_local(const nectar_attn_desc *desc, const nectar_local_desc *loc) {
@@ -466,43 +457,75 @@ static size_t mlp_partial_bytes(const nectar_attn_desc *d, const MlpPlan &pl) {
 
 struct StepPlan {
     bool exact = false, mlp = false, kvp = false;
+    // fused: deferred partials of every part, then one finishing launch (decode
+    // shapes, where every part is short); otherwise the parts finish in place
+    // or with their own combine and the local pass merges.
+    bool fused = false;
     AttnPlan loc, doc, kvpl;
     MlpPlan mlpl;
-    size_t off_doc = 0, off_mod = 0, bytes = 0;
+    size_t off_doc = 0, off_mod = 0;               // fused: partial regions
+    size_t off_px = 0, off_pm = 0, off_pl = 0;     // composed: scratch pairs
+    size_t off_po = 0;                             // composed: scratch merged output
+    size_t bytes = 0;
 };
+
+static size_t pair_bytes(const nectar_attn_desc *d) {
+    return align256((size_t)d->R * d->Hq * 4) + align256((size_t)d->R * d->Hq * d->d * 4);
+}
 
 static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_local_desc *loc,
                           const nectar_module *m, bool exact) {
     StepPlan sp;
     const int G = d->Hq / d->Hkv, Rp_doc = d->R * G;
     sp.loc = plan_attn(d, loc->B * d->Hkv, loc->Tq * G, loc->T_loc);
-    size_t off = align256(attn_partial_bytes(d, sp.loc));
     sp.exact = exact;
-    if (exact) {
-        sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n);
-        sp.off_doc = off;
-        off += align256(attn_partial_bytes(d, sp.doc));
-    }
+    if (exact) sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n);
     if (m && m->kind == NECTAR_MODULE_MLP) {
         sp.mlp = true;
         sp.mlpl = plan_mlp(d, m->Ht, m->Hs);
-        sp.off_mod = off;
-        off += align256(mlp_partial_bytes(d, sp.mlpl));
     } else if (m) {
         sp.kvp = true;
         sp.kvpl = plan_attn(d, d->Hkv, Rp_doc, (long)m->p);
-        sp.off_mod = off;
-        off += align256(attn_partial_bytes(d, sp.kvpl));
     }
-    sp.bytes = off;
+    auto decode = [](const AttnPlan &pl) { return pl.S == 0 || (!pl.lds && pl.RT == 1); };
+    sp.fused = d->dtype == NECTAR_F32 ||
+               (decode(sp.loc) && (!exact || decode(sp.doc)) && (!sp.mlp || (!sp.mlpl.prefill && sp.mlpl.RT == 1)) &&
+                (!sp.kvp || decode(sp.kvpl)));
+    if (sp.fused) {
+        size_t off = align256(attn_partial_bytes(d, sp.loc));
+        if (exact) {
+            sp.off_doc = off;
+            off += align256(attn_partial_bytes(d, sp.doc));
+        }
+        if (m) {
+            sp.off_mod = off;
+            off += align256(sp.mlp ? mlp_partial_bytes(d, sp.mlpl) : attn_partial_bytes(d, sp.kvpl));
+        }
+        sp.bytes = off;
+    } else {
+        size_t sub = sp.loc.ws;
+        if (exact && sp.doc.ws > sub) sub = sp.doc.ws;
+        if (sp.mlp && sp.mlpl.ws > sub) sub = sp.mlpl.ws;
+        if (sp.kvp && sp.kvpl.ws > sub) sub = sp.kvpl.ws;
+        size_t off = align256(sub);
+        sp.off_px = off;
+        off += exact ? pair_bytes(d) : 0;
+        sp.off_pm = off;
+        off += m ? pair_bytes(d) : 0;
+        sp.off_pl = off;
+        off += pair_bytes(d);
+        sp.off_po = off;
+        off += exact && m ? align256((size_t)d->R * d->Hq * d->d * 4) : 0;
+        sp.bytes = off;
+    }
     return sp;
 }
 
-// Split partials of one attention plan into part (read-outs, then statistics).
-static hipError_t attn_partials(const nectar_attn_desc *d, const AttnPlan &pl, const void *q, const void *k,
-                                const void *v, int64_t bstride, int64_t hstride, int B, int Tq, long T_kv,
-                                int causal, int q_offset, void *part, hipStream_t st) {
-    if (pl.S == 0) return hipSuccess;
+// Deferred-finish parameters of one attention plan writing into part
+// (read-outs, then statistics).
+static AttnParams attn_partial_params(const nectar_attn_desc *d, const AttnPlan &pl, const void *q, const void *k,
+                                      const void *v, int64_t bstride, int64_t hstride, int B, int Tq, long T_kv,
+                                      int causal, int q_offset, void *part) {
     AttnParams a{};
     a.q = q; a.k = k; a.v = v;
     a.kv_bstride = bstride; a.kv_hstride = hstride;
@@ -515,11 +538,22 @@ static hipError_t attn_partials(const nectar_attn_desc *d, const AttnPlan &pl, c
     a.defer = 1;
     a.part_O = (float *)part;
     a.part_ml = (float2 *)((char *)part + (size_t)pl.P * pl.SB * pl.Rp * d->d * 4);
+    return a;
+}
+
+static hipError_t launch_plan(const nectar_attn_desc *d, const AttnPlan &pl, const AttnParams &a, hipStream_t st) {
+    if (pl.S == 0) return hipSuccess;
     return pl.lds ? launch_attn_rows_lds(a, pl.sh, st) : launch_attn_partial(a, d->dtype, d->d, pl.RT, st);
 }
 
-static hipError_t mlp_partials(const nectar_attn_desc *d, const MlpPlan &pl, const nectar_module *m,
-                               const void *q, void *part, hipStream_t st) {
+// The register-direct bf16 kernel serves both plans in one launch when they
+// use the same row tiling.
+static bool pairable(const nectar_attn_desc *d, const AttnPlan &x, const AttnPlan &y) {
+    return d->dtype == NECTAR_BF16 && x.S > 0 && y.S > 0 && !x.lds && !y.lds && x.RT == y.RT;
+}
+
+static MlpParams mlp_partial_params(const nectar_attn_desc *d, const MlpPlan &pl, const nectar_module *m,
+                                    const void *q, void *part) {
     MlpParams a{};
     a.q = q; a.W1 = m->W1; a.W2t = m->W2t; a.Ws = m->Ws; a.ws2 = m->ws2;
     a.b1 = m->b1; a.bs = m->bs; a.b2 = m->b2; a.bs2 = m->bs2;
@@ -530,11 +564,73 @@ static hipError_t mlp_partials(const nectar_attn_desc *d, const MlpPlan &pl, con
     a.defer = 1;
     a.part_O = (float *)part;
     a.part_s = (float *)((char *)part + (size_t)d->Hkv * pl.SB * pl.Rp * d->d * 4);
-    return pl.prefill ? launch_mlp_prefill(a, st) : launch_mlp_partial(a, d->dtype, d->d, pl.RT, st);
+    return a;
 }
 
 static bool exact_requested(const nectar_step_outputs *o) {
     return o->out_exact || o->lse_exact || o->alpha_out || o->A_out;
+}
+
+// Composed layer step: each document-side part finishes itself into its pair
+// (the caller's pair outputs or scratch), the local pass merges one of them in
+// place and a merge launch handles the second.
+static hipError_t run_step_composed(const nectar_attn_desc *desc, const StepPlan &sp, int64_t n,
+                                    const nectar_local_desc *loc, const void *q, const void *k, const void *v,
+                                    const void *k_loc, const void *v_loc, const nectar_module *module,
+                                    const nectar_step_outputs *outs, char *w, hipStream_t st) {
+    const size_t lse_bytes = align256((size_t)desc->R * desc->Hq * 4);
+    auto pair = [&](size_t off, float *lse, float *A, float **pl, float **pA) {
+        *pl = lse ? lse : (float *)(w + off);
+        *pA = A ? A : (float *)(w + off + lse_bytes);
+    };
+    struct Merge { const float *lse, *A; void *out; float *out_lse; };
+    Merge mg[2];
+    int nm = 0;
+    hipError_t e = hipSuccess;
+    if (sp.exact) {
+        float *al, *Ax;
+        pair(sp.off_px, outs->alpha_out, outs->A_out, &al, &Ax);
+        CombineParams cp{};
+        cp.lse_out = al; cp.A_out = Ax;
+        e = run_attention(desc, sp.doc, q, k, v, 0, n * desc->d, 1, desc->R, (long)n, 0, 0, cp, w, st);
+        if (outs->out_exact || outs->lse_exact) mg[nm++] = Merge{al, Ax, outs->out_exact, outs->lse_exact};
+    }
+    if (e == hipSuccess && module) {
+        float *am, *Am;
+        pair(sp.off_pm, outs->a_out, outs->Am_out, &am, &Am);
+        if (sp.mlp) {
+            e = run_mlp(desc, sp.mlpl, module, q, am, Am, w, st);
+        } else {
+            CombineParams cp{};
+            cp.lse_out = am; cp.A_out = Am;
+            e = run_attention(desc, sp.kvpl, q, module->W, module->Z, 0, module->p * desc->d, 1, desc->R,
+                              (long)module->p, 0, 0, cp, w, st);
+        }
+        if (outs->out_nectar || outs->lse_nectar) mg[nm++] = Merge{am, Am, outs->out_nectar, outs->lse_nectar};
+    }
+    if (e != hipSuccess) return e;
+    // local pass: its pair (requested, or needed by a second merge) and the first merge in place
+    float *lam = outs->lam_out, *Aloc = outs->Aloc_out;
+    if (nm == 2) pair(sp.off_pl, outs->lam_out, outs->Aloc_out, &lam, &Aloc);
+    if (nm == 0 && !lam && !Aloc) return e;      // nothing needs the local part
+    CombineParams cp{};
+    cp.lse_out = lam; cp.A_out = Aloc;
+    if (nm > 0) {
+        cp.x_lse = mg[0].lse; cp.x_A = mg[0].A; cp.out = mg[0].out; cp.out_lse = mg[0].out_lse;
+    }
+    const int64_t hstride = (int64_t)loc->T_cap * desc->d;
+    e = run_attention(desc, sp.loc, q, k_loc, v_loc, hstride * desc->Hkv, hstride, loc->B, loc->Tq, loc->T_loc, 1,
+                      loc->q_offset, cp, w, st);
+    for (int i = 1; i < nm && e == hipSuccess; ++i) {
+        // out may be NULL (only the merged log-normaliser requested): write the output to scratch
+        MergeParams mp;
+        mp.a = mg[i].lse; mp.A = mg[i].A; mp.lam = lam; mp.A_loc = Aloc;
+        mp.out = mg[i].out ? mg[i].out : (void *)(w + sp.off_po);
+        mp.lse_out = mg[i].out_lse;
+        mp.rows = (long)desc->R * desc->Hq;
+        e = launch_merge(mp, desc->dtype, desc->d, st);
+    }
+    return e;
 }
 
 size_t nectar_layer_step_workspace_size(const nectar_attn_desc *desc, int64_t n, const nectar_local_desc *loc,
@@ -576,14 +672,39 @@ nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const n
 
     hipStream_t st = (hipStream_t)stream;
     char *w = (char *)ws;
+    if (!sp.fused) return finish(run_step_composed(desc, sp, n, loc, q, k, v, k_loc, v_loc, module, outs, w, st), st);
     const int G = desc->Hq / desc->Hkv;
     FinishParams f{};
     f.Hq = desc->Hq; f.G = G; f.Hkv = desc->Hkv; f.Tq = loc->Tq;
     f.P = sp.loc.P; f.Rp = sp.loc.Rp; f.Rp_doc = desc->R * G;
     f.lam_out = outs->lam_out; f.Aloc_out = outs->Aloc_out;
     hipError_t e = hipSuccess;
+    const int64_t hstride = (int64_t)loc->T_cap * desc->d;
+    const AttnParams ap_loc = attn_partial_params(desc, sp.loc, q, k_loc, v_loc, hstride * desc->Hkv, hstride,
+                                                  loc->B, loc->Tq, loc->T_loc, 1, loc->q_offset, w);
+    bool loc_done = false, mod_done = false;
+    const AttnParams ap_doc = attn_partial_params(desc, sp.doc, q, k, v, 0, n * desc->d, 1, desc->R, (long)n,
+                                                  0, 0, w + sp.off_doc);
+    MlpParams mp{};
+    if (sp.mlp) mp = mlp_partial_params(desc, sp.mlpl, module, q, w + sp.off_mod);
+    // decode shapes: the attention blocks and the module's blocks in one launch
+    const bool mlp_dec = sp.mlp && !sp.mlpl.prefill && desc->dtype == NECTAR_BF16 && sp.mlpl.RT == 1;
+    if (mlp_dec && sp.exact && pairable(desc, sp.doc, sp.loc) && sp.doc.RT == 1) {
+        e = launch_step_partials(ap_doc, &ap_loc, mp, desc->d, st);
+        loc_done = mod_done = true;
+    } else if (mlp_dec && !sp.exact && sp.loc.S > 0 && !sp.loc.lds && sp.loc.RT == 1) {
+        e = launch_step_partials(ap_loc, nullptr, mp, desc->d, st);
+        loc_done = mod_done = true;
+    }
     if (sp.exact) {
-        e = attn_partials(desc, sp.doc, q, k, v, 0, n * desc->d, 1, desc->R, (long)n, 0, 0, w + sp.off_doc, st);
+        if (loc_done) {
+            // already launched with the local and module blocks
+        } else if (pairable(desc, sp.doc, sp.loc)) {
+            e = launch_attn_partial_pair(ap_doc, ap_loc, desc->d, sp.doc.RT, st);
+            loc_done = true;
+        } else {
+            e = launch_plan(desc, sp.doc, ap_doc, st);
+        }
         FinishSet &x = f.set[f.nsets++];
         x.S = sp.doc.S > 0 ? sp.doc.SB : 0;
         x.O = (const float *)(w + sp.off_doc);
@@ -595,21 +716,22 @@ nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const n
         x.O = (const float *)(w + sp.off_mod);
         x.lse_out = outs->a_out; x.A_out = outs->Am_out; x.out = outs->out_nectar; x.out_lse = outs->lse_nectar;
         if (sp.mlp) {
-            e = mlp_partials(desc, sp.mlpl, module, q, w + sp.off_mod, st);
+            if (!mod_done)
+                e = sp.mlpl.prefill ? launch_mlp_prefill(mp, st)
+                                    : launch_mlp_partial(mp, desc->dtype, desc->d, sp.mlpl.RT, st);
             x.S = sp.mlpl.SB;
             x.s = (const float *)(w + sp.off_mod + (size_t)desc->Hkv * sp.mlpl.SB * sp.mlpl.Rp * desc->d * 4);
             x.b2 = module->b2; x.bs2 = module->bs2;
         } else {
-            e = attn_partials(desc, sp.kvpl, q, module->W, module->Z, 0, module->p * desc->d, 1, desc->R,
-                              (long)module->p, 0, 0, w + sp.off_mod, st);
+            e = launch_plan(desc, sp.kvpl, attn_partial_params(desc, sp.kvpl, q, module->W, module->Z, 0,
+                                                               module->p * desc->d, 1, desc->R, (long)module->p,
+                                                               0, 0, w + sp.off_mod), st);
             x.S = sp.kvpl.S > 0 ? sp.kvpl.SB : 0;
             x.ml = (const float2 *)(w + sp.off_mod + (size_t)sp.kvpl.P * sp.kvpl.SB * sp.kvpl.Rp * desc->d * 4);
         }
     }
     if (e == hipSuccess) {
-        const int64_t hstride = (int64_t)loc->T_cap * desc->d;
-        e = attn_partials(desc, sp.loc, q, k_loc, v_loc, hstride * desc->Hkv, hstride, loc->B, loc->Tq,
-                          loc->T_loc, 1, loc->q_offset, w, st);
+        if (!loc_done) e = launch_plan(desc, sp.loc, ap_loc, st);
         f.S_loc = sp.loc.S > 0 ? sp.loc.SB : 0;
         f.loc_O = (const float *)w;
         f.loc_ml = (const float2 *)(w + (size_t)sp.loc.P * sp.loc.SB * sp.loc.Rp * desc->d * 4);

@@ -316,6 +316,39 @@ def test_layer_step(nx, name):
         check("nectar lse", o["lse_nectar"], eol, tl)
 
 
+@pytest.mark.parametrize("name", ["batch64_bf16", "decode_bf16"])
+def test_layer_step_output_subsets(nx, name):
+    """Requesting only some outputs (here the two merged log-normalisers and the
+    exact pair) gives the same values as the full request, on both launch plans."""
+    import torch
+    dt, d, B, Tq, T, T_cap, qoff, Hq, Hkv, n, mod = STEP_CASES[name]
+    print("case layer_step subsets %s" % name, flush=True)
+    g = _rng(21, B, Tq, T)
+    R = B * Tq
+    q = dev(_store(g.standard_normal((R, Hq, d)), dt))
+    Kl, Vl = (dev(_store(g.standard_normal((B, Hkv, T_cap, d)), dt)) for _ in range(2))
+    k, v = (dev(_store(g.standard_normal((Hkv, n, d)), dt)) for _ in range(2))
+    module = _mlp_dev(nx, _mlp_np(g, Hkv, d, mod[1], mod[2], dt), nx.GELU)
+    kw = dict(B=B, Tq=Tq, T_loc=T, q_offset=qoff, k=k, v=v, module=module, exact=True)
+    full = nx.layer_step(q, Kl, Vl, Hkv, pairs=True, **kw)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    part = {"lse_exact": torch.empty((R, Hq), **f32), "lse_nectar": torch.empty((R, Hq), **f32),
+            "alpha": torch.empty((R, Hq), **f32), "A": torch.empty((R, Hq, d), **f32)}
+    from learned_kv_cache_02_amd.nectar import StepOutputs, _lib, _ptr, _stream, _ws_args, desc, LocalDesc, dtype_code
+    import ctypes
+    dsc = desc(R, Hq, Hkv, d, dtype_code(q))
+    loc = LocalDesc(B, Tq, T, T_cap, qoff)
+    so = StepOutputs(None, _ptr(part["lse_exact"]), _ptr(part["alpha"]), _ptr(part["A"]), None,
+                     _ptr(part["lse_nectar"]), None, None, None, None)
+    m = module.struct()
+    nbytes = int(_lib.nectar_layer_step_workspace_size(ctypes.byref(dsc), n, ctypes.byref(loc), ctypes.byref(m), 1))
+    wp, wn = _ws_args(nbytes, q.device)
+    assert _lib.nectar_layer_step(ctypes.byref(dsc), n, ctypes.byref(loc), _ptr(q), _ptr(k), _ptr(v), _ptr(Kl),
+                                  _ptr(Vl), ctypes.byref(m), ctypes.byref(so), wp, wn, _stream()) == 0
+    for key in part:
+        check("subset " + key, host(part[key]), host(full[key]).astype(np.float64), 1e-5)
+
+
 # --- workloads end to end -----------------------------------------------------------------
 
 def _run_layer(nx, cfg, inputs, step=0):

@@ -10,6 +10,7 @@
  * over the question's own tokens.  This library computes, on one GPU:
  *
  *   nectar_doc_attn_exact   exact (alpha, A) over the document cache, Eq. (3.1)
+ *   nectar_doc_attn_partials / nectar_doc_attn_combine   the same as two passes
  *   nectar_module_forward   (a, A) from the MLP form (Eq. (3.6), one hidden
  *                           layer) or the Quadrature KV-pair form (section 2.4)
  *   nectar_local_attn_lse   causal local attention (log Z_local, A_local),
@@ -148,6 +149,25 @@ NECTAR_API nectar_status nectar_doc_attn_exact(const nectar_attn_desc *desc, int
                                     const void *q, const void *k, const void *v,
                                     float *alpha_out, float *A_out,
                                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The same exact document attention as its two passes (the split-K partials
+ * and their log-sum-exp combine, Eq. (3.4) regrouped), for callers that place
+ * the passes themselves -- e.g. combining partials computed over several key
+ * ranges.  partials: caller-owned device buffer of nectar_doc_attn_partials_size
+ * bytes (16-byte aligned), written by the first call and read by the second
+ * with the same desc and n; its layout is private to the library.
+ * nectar_doc_attn_partials followed by nectar_doc_attn_combine writes the same
+ * (alpha_out, A_out) as nectar_doc_attn_exact up to rounding (bitwise the same
+ * whenever the plan splits the keys, i.e. whenever its workspace size is > 0).
+ */
+NECTAR_API size_t nectar_doc_attn_partials_size(const nectar_attn_desc *desc, int64_t n);
+NECTAR_API nectar_status nectar_doc_attn_partials(const nectar_attn_desc *desc, int64_t n,
+                                       const void *q, const void *k, const void *v,
+                                       void *partials, size_t bytes, void *stream);
+NECTAR_API nectar_status nectar_doc_attn_combine(const nectar_attn_desc *desc, int64_t n,
+                                      const void *partials, size_t bytes,
+                                      float *alpha_out, float *A_out, void *stream);
 
 /* Module forward: (a_out [R][Hq], A_out [R][Hq][d]) for every query row. */
 NECTAR_API size_t nectar_module_workspace_size(const nectar_attn_desc *desc, const nectar_module *m);

@@ -633,6 +633,52 @@ static hipError_t run_step_composed(const nectar_attn_desc *desc, const StepPlan
     return e;
 }
 
+// ---------------------------------------------------------------------------
+// The exact document attention as its two passes.
+
+size_t nectar_doc_attn_partials_size(const nectar_attn_desc *desc, int64_t n) {
+    if (check_desc(desc) != NECTAR_OK || n < 0 || n > 0x7fffffffL - kTile) return 0;
+    return attn_partial_bytes(desc, plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)n));
+}
+
+nectar_status nectar_doc_attn_partials(const nectar_attn_desc *desc, int64_t n, const void *q, const void *k,
+                                       const void *v, void *partials, size_t bytes, void *stream) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if (n < 0) return NECTAR_EINVAL;
+    if (n > 0x7fffffffL - kTile) return NECTAR_EUNSUPPORTED;
+    if (desc->R == 0) return NECTAR_OK;
+    if (!tensor_ok(q)) return NECTAR_EINVAL;
+    if (n > 0 && (!tensor_ok(k) || !tensor_ok(v))) return NECTAR_EINVAL;
+    const AttnPlan pl = plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)n);
+    if ((s = check_ws(attn_partial_bytes(desc, pl), partials, bytes)) != NECTAR_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    const AttnParams a = attn_partial_params(desc, pl, q, k, v, 0, n * desc->d, 1, desc->R, (long)n, 0, 0, partials);
+    return finish(launch_plan(desc, pl, a, st), st);
+}
+
+nectar_status nectar_doc_attn_combine(const nectar_attn_desc *desc, int64_t n, const void *partials, size_t bytes,
+                                      float *alpha_out, float *A_out, void *stream) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if (n < 0) return NECTAR_EINVAL;
+    if (n > 0x7fffffffL - kTile) return NECTAR_EUNSUPPORTED;
+    if (desc->R == 0) return NECTAR_OK;
+    if (!f32_ok(alpha_out) || !f32_ok(A_out)) return NECTAR_EINVAL;
+    const AttnPlan pl = plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)n);
+    const size_t need = attn_partial_bytes(desc, pl);
+    if (bytes < need) return NECTAR_EWORKSPACE;
+    if (need > 0 && (!partials || !aligned(partials, 16))) return NECTAR_EINVAL;
+    CombineParams cp{};
+    cp.lse_out = alpha_out; cp.A_out = A_out;
+    cp.part_O = (const float *)partials;
+    cp.part_ml = (const float2 *)((const char *)partials + (size_t)pl.P * pl.SB * pl.Rp * desc->d * 4);
+    cp.Hq = desc->Hq; cp.G = desc->Hq / desc->Hkv; cp.Hkv = desc->Hkv; cp.Tq = desc->R;
+    cp.P = desc->Hkv; cp.S = pl.S > 0 ? pl.SB : 0; cp.Rp = desc->R * (desc->Hq / desc->Hkv);
+    hipStream_t st = (hipStream_t)stream;
+    return finish(launch_attn_combine(cp, desc->dtype, desc->d, st), st);
+}
+
 size_t nectar_layer_step_workspace_size(const nectar_attn_desc *desc, int64_t n, const nectar_local_desc *loc,
                                         const nectar_module *module, int exact) {
     if (check_desc(desc) != NECTAR_OK || check_local(desc, loc) != NECTAR_OK) return 0;

@@ -71,6 +71,10 @@ _lib.nectar_local_workspace_size.restype = ctypes.c_size_t
 _lib.nectar_local_attn_lse.argtypes = [_D, ctypes.POINTER(LocalDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, ctypes.c_size_t, _P]
 _lib.nectar_merge.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P]
+_lib.nectar_doc_attn_partials_size.argtypes = [_D, ctypes.c_int64]
+_lib.nectar_doc_attn_partials_size.restype = ctypes.c_size_t
+_lib.nectar_doc_attn_partials.argtypes = [_D, ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.nectar_doc_attn_combine.argtypes = [_D, ctypes.c_int64, _P, ctypes.c_size_t, _P, _P, _P]
 _lib.nectar_layer_step_workspace_size.argtypes = [_D, ctypes.c_int64, ctypes.POINTER(LocalDesc),
                                                   ctypes.POINTER(Module), ctypes.c_int]
 _lib.nectar_layer_step_workspace_size.restype = ctypes.c_size_t
@@ -82,7 +86,7 @@ _lib.nectar_abi_version.restype = ctypes.c_int
 _lib.nectar_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.nectar_workspace_init.restype = ctypes.c_int
 for _f in ("nectar_doc_attn_exact", "nectar_module_forward", "nectar_local_attn_lse", "nectar_merge",
-           "nectar_layer_step"):
+           "nectar_layer_step", "nectar_doc_attn_partials", "nectar_doc_attn_combine"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -160,6 +164,37 @@ def doc_attn_exact(q, k, v, Hkv, *, scale=0.0, splits=0, alpha_out=None, A_out=N
     wp, wn = _ws_args(doc_attn_workspace_size(dsc, n), q.device)
     _check(_lib.nectar_doc_attn_exact(ctypes.byref(dsc), n, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha_out),
                                       _ptr(A_out), wp, wn, _stream()))
+    return alpha_out, A_out
+
+
+def doc_attn_partials_size(dsc: AttnDesc, n: int) -> int:
+    return int(_lib.nectar_doc_attn_partials_size(ctypes.byref(dsc), int(n)))
+
+
+def doc_attn_partials(q, k, v, Hkv, *, scale=0.0, splits=0, partials=None):
+    """First pass of the exact document attention: the split-K partials, into a
+    uint8 device tensor (allocated when not given).  Returns the tensor."""
+    R, Hq, d = q.shape
+    n = k.shape[-2]
+    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    nbytes = int(_lib.nectar_doc_attn_partials_size(ctypes.byref(dsc), n))
+    if partials is None:
+        partials = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(_lib.nectar_doc_attn_partials(ctypes.byref(dsc), n, _ptr(q), _ptr(k), _ptr(v), _ptr(partials),
+                                         partials.numel(), _stream()))
+    return partials
+
+
+def doc_attn_combine(partials, R, Hq, Hkv, d, n, dtype, *, scale=0.0, splits=0, alpha_out=None, A_out=None):
+    """Second pass: (alpha [R][Hq], A [R][Hq][d]) from the partials of the same shapes."""
+    dsc = desc(R, Hq, Hkv, d, dtype, scale, splits)
+    dev_ = partials.device
+    if alpha_out is None:
+        alpha_out = torch.empty((R, Hq), dtype=torch.float32, device=dev_)
+    if A_out is None:
+        A_out = torch.empty((R, Hq, d), dtype=torch.float32, device=dev_)
+    _check(_lib.nectar_doc_attn_combine(ctypes.byref(dsc), n, _ptr(partials), partials.numel(), _ptr(alpha_out),
+                                        _ptr(A_out), _stream()))
     return alpha_out, A_out
 
 

@@ -78,7 +78,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert lib.nectar_abi_version() == 1
@@ -259,3 +259,25 @@ def test_layer_step_validation(lib):
     assert lib.nectar_layer_step_workspace_size(None, 61440, ctypes.byref(loc), None, 1) == 0
     d0 = Desc(0, 32, 8, 128, 1, 0.0, 0)                                # R == 0: valid no-op
     assert call(exact_only, desc=d0, lc=Local(0, 1, 513, 513, 512), q=None) == OK
+
+
+def test_doc_attn_two_pass_validation(lib):
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(Desc)
+    lib.nectar_doc_attn_partials_size.argtypes = [D, ctypes.c_int64]
+    lib.nectar_doc_attn_partials_size.restype = ctypes.c_size_t
+    lib.nectar_doc_attn_partials.argtypes = [D, ctypes.c_int64, P, P, P, P, ctypes.c_size_t, P]
+    lib.nectar_doc_attn_combine.argtypes = [D, ctypes.c_int64, P, ctypes.c_size_t, P, P, P]
+    d = Desc(1, 32, 8, 128, 1, 0.0, 0)
+    # same plan as the one-call form: 60 partials per row, 4 rows per head, 520 B each
+    assert lib.nectar_doc_attn_partials_size(ctypes.byref(d), 61440) == 8 * 60 * 4 * 520
+    d1 = Desc(1, 32, 8, 128, 1, 0.0, 1)          # one split: still one partial per row
+    assert lib.nectar_doc_attn_partials_size(ctypes.byref(d1), 61440) == 8 * 1 * 4 * 520
+    assert lib.nectar_doc_attn_partials_size(ctypes.byref(d), 0) == 0
+    need = lib.nectar_doc_attn_partials_size(ctypes.byref(d), 61440)
+    assert lib.nectar_doc_attn_partials(ctypes.byref(d), 61440, A16, A16, A16, A16, need - 1, None) == EWORKSPACE
+    assert lib.nectar_doc_attn_partials(ctypes.byref(d), 61440, MIS, A16, A16, A16, need, None) == EINVAL
+    assert lib.nectar_doc_attn_partials(ctypes.byref(d), -1, A16, A16, A16, A16, need, None) == EINVAL
+    assert lib.nectar_doc_attn_combine(ctypes.byref(d), 61440, A16, need - 1, A16, A16, None) == EWORKSPACE
+    assert lib.nectar_doc_attn_combine(ctypes.byref(d), 61440, A16, need, None, A16, None) == EINVAL
+    assert lib.nectar_doc_attn_combine(ctypes.byref(d), 61440, MIS, need, A16, A16, None) == EINVAL

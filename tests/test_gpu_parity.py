@@ -76,6 +76,28 @@ def test_doc_attn_split_invariance_and_determinism(nx):
     assert np.array_equal(again[0], res[128][0]) and np.array_equal(again[1], res[128][1])
 
 
+@pytest.mark.parametrize("R,Hq,Hkv,n,splits", [(1, 32, 8, 61440, 0), (3, 28, 4, 777, 0), (64, 32, 8, 3000, 0),
+                                              (2, 16, 4, 5000, 1), (1, 8, 2, 0, 0)])
+def test_doc_attn_two_pass(nx, R, Hq, Hkv, n, splits):
+    """Partials then combine: the oracle's (alpha, A), and bitwise the one-call form
+    when that form splits the keys too."""
+    print("case doc two-pass R=%d Hq=%d Hkv=%d n=%d splits=%d" % (R, Hq, Hkv, n, splits), flush=True)
+    import torch
+    d = 128
+    g = _rng(12, R, n)
+    q, K, V = (_bf(g.standard_normal(s)) for s in ((R, Hq, d), (Hkv, n, d), (Hkv, n, d)))
+    qd, Kd, Vd = dev(q), dev(K), dev(V)
+    part = nx.doc_attn_partials(qd, Kd, Vd, Hkv, splits=splits)
+    a2, A2 = nx.doc_attn_combine(part, R, Hq, Hkv, d, n, nx.BF16, splits=splits)
+    a1, A1 = nx.doc_attn_exact(qd, Kd, Vd, Hkv, splits=splits)
+    ea, eA = oracle.doc_attn(q, K, V, dt="bf16", Hq=Hq, Hkv=Hkv)
+    check("alpha two-pass", host(a2), ea, ATOL_LSE_BF16)
+    check("A two-pass", host(A2), eA, ATOL_OUT_BF16, REL_L2_BF16)
+    dsc = nx.desc(R, Hq, Hkv, d, nx.BF16, 0.0, splits)
+    if nx.doc_attn_workspace_size(dsc, n) > 0:
+        assert torch.equal(a1, a2) and torch.equal(A1, A2)
+
+
 def test_scaled_query_stress(nx):
     # Large scores (peaky attention): the online max must keep exp2 in range.
     R, Hq, Hkv, n, d = 1, 8, 2, 2000, 128

@@ -271,15 +271,230 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 32 rows per wave: the same LDS ring with v_mfma_f32_32x32x16_bf16, so every
+// K and V operand read from LDS and every V transpose serves 32 query rows
+// (twice the 16-row kernel above), and a block of eight waves covers 256 rows.
+//
+// Per 32-key tile:
+//   S^T (32 keys x 32 rows) = sum over 8 slices of 16 dims of K_slice . Q^T_slice
+//       (lane l reads 16 bytes of key l % 32 in its half's 8 dims);
+//   row statistics: a lane holds 16 of its row's 32 scores, the other 16 sit
+//       in lane l ^ 32, so the row max and sum need one cross-lane step;
+//   O^T (128 dims x 32 rows) += V^T . P^T as 4 dim blocks x 2 key groups.
+// The accumulator layout of S puts key 8 (i / 4) + 4 h + i % 4 in register i of
+// a lane of half h; the P^T operand of key group t is simply registers
+// 8t .. 8t + 7 of that lane, provided the contraction slots of the V^T operand
+// follow the same key order: slot s of half h is key 16 t + 8 (s / 4) + 4 h + s % 4.
+// Lane l therefore reads, for each of those 8 keys, the 8 bytes holding dims
+// 4 (l % 32) .. + 3 and builds dim block mi's operand (dim 4 (l % 32) + mi)
+// with byte permutes; O^T row rho of block mi is dim 4 rho + mi.
+template <int NW, int kStageKeys>
+__global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
+    constexpr int kKeysPerWave = kStageKeys / NW;
+    constexpr int kCopies = kKeysPerWave / 4;
+    static_assert(kCopies >= 1 && kCopies * 4 * NW == kStageKeys, "stage split");
+    constexpr int kBlockRows = 32 * NW;
+    __shared__ u32x4 kv_a[2][kStageKeys * kPieces], kv_b[2][kStageKeys * kPieces], kv_c[2][kStageKeys * kPieces];
+
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, hf = lane >> 5, r = lane & 31;
+    int u, rb;
+    if (a.xcd_group) {
+        const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+        rb = y % a.RB;
+        u = (y / a.RB) * 8 + x;
+    } else {
+        u = blockIdx.x / a.RB;
+        rb = blockIdx.x - u * a.RB;
+    }
+    const int p = u / a.SB, sb = u - p * a.SB;
+    const int b = p / a.Hkv, h = p - b * a.Hkv;
+    const uint16_t *kb = (const uint16_t *)a.k + b * a.kv_bstride + h * a.kv_hstride;
+    const uint16_t *vb = (const uint16_t *)a.v + b * a.kv_bstride + h * a.kv_hstride;
+
+    // this lane's query row and its 8 B operands (dims 16 kt + 8 hf .. + 7)
+    const int rho = rb * kBlockRows + w * 32 + r;
+    u32x4 qv[8];
+    int lim;
+    if (rho < a.Rp) {
+        const int tk = rho / a.G, gg = rho - tk * a.G;
+        const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(b * a.Tq + tk) * a.Hq + h * a.G + gg) * kD;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) qv[kt] = *(const u32x4 *)(qp + 16 * kt + 8 * hf);
+        int L = a.T_kv;
+        if (a.causal) L = min(L, a.q_offset + tk + 1);
+        lim = max(L, 0);
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) qv[kt] = u32x4{0u, 0u, 0u, 0u};
+        lim = 0x7fffffff;
+    }
+    float sl2 = a.sl2;
+    if (sl2 < 0.f) {
+        sl2 = -sl2;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) qv[kt] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
+    int blim = a.T_kv;
+    if (a.causal) {
+        const int last = min(a.Rp, (rb + 1) * kBlockRows) - 1;
+        blim = min(blim, a.q_offset + last / a.G + 1);
+    }
+    blim = max(blim, 0);
+    const int k_lo = sb * a.chunk;
+    const int k_hi = min(k_lo + a.chunk, blim);
+    const int nst = k_hi > k_lo ? (k_hi - k_lo + kStageKeys - 1) / kStageKeys : 0;
+    const int kmax = a.T_kv - 1;
+
+    auto issue = [&](int i, u32x4 (&dst)[2][kStageKeys * kPieces]) {
+        const int key0 = k_lo + i * kStageKeys;
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) {
+            const int r0 = kKeysPerWave * w + 4 * c, rr = r0 + (lane >> 4);
+            const int key = min(key0 + rr, kmax);
+            const int piece = (lane & 15) ^ (rr & 15);
+            const size_t off = (size_t)key * kD + piece * 8;
+            __builtin_amdgcn_global_load_lds((const void *)(kb + off), (lds_void *)&dst[0][r0 * kPieces], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(vb + off), (lds_void *)&dst[1][r0 * kPieces], 16, 0, 0);
+        }
+    };
+
+    f32x16 O[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) O[mi] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+
+    auto step = [&](int i, const u32x4 (&cur)[2][kStageKeys * kPieces], u32x4 (&ahead)[2][kStageKeys * kPieces]) {
+        if (i + 1 < nst) wait_vmcnt<2 * kCopies>();
+        else wait_vmcnt<0>();
+        stage_barrier();
+        if (i + 2 < nst) issue(i + 2, ahead);
+        const u32x4 *Ks = cur[0];
+        const uint2 *Vs = (const uint2 *)cur[1];
+#pragma unroll
+        for (int sub = 0; sub < kStageKeys / 32; ++sub) {
+            const int kbase = k_lo + i * kStageKeys + 32 * sub;
+            f32x16 S = {};
+            const int kr = 32 * sub + r;                 // the key whose 16-dim slices this lane supplies
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) S = mfma32(Ks[kr * kPieces + ((2 * kt + hf) ^ (kr & 15))], qv[kt], S);
+            float sv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sv[j] = S[j];
+            if (kbase + 32 > lim) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (kbase + 8 * (j >> 2) + 4 * hf + (j & 3) >= lim) sv[j] = -INFINITY;
+            }
+            float mt = sv[0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sv[j]);
+            mt *= sl2;
+            if (__ballot(mt > m + kSlack) != 0) {
+                const float mnew = fmaxf(m, fmaxf(mt, __shfl_xor(mt, 32, 64)));
+                const float sc = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+                l *= sc;
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) O[mi] *= sc;
+                m = mnew;
+            }
+            const float nm = (m == -INFINITY) ? 0.f : -m;
+            float pv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                pv[j] = fast_exp2(__builtin_fmaf(sv[j], sl2, nm));
+                l += pv[j];
+            }
+#pragma unroll
+            for (int tg = 0; tg < 2; ++tg) {
+                const u32x4 P = {pack_bf16(pv[8 * tg + 0], pv[8 * tg + 1]), pack_bf16(pv[8 * tg + 2], pv[8 * tg + 3]),
+                                 pack_bf16(pv[8 * tg + 4], pv[8 * tg + 5]), pack_bf16(pv[8 * tg + 6], pv[8 * tg + 7])};
+                // dims 4r .. 4r + 3 of the 8 keys of slots s = 0..7
+                uint2 x[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int key = 32 * sub + 16 * tg + 8 * (s >> 2) + 4 * hf + (s & 3);
+                    x[s] = Vs[(key * kPieces + ((r >> 1) ^ (key & 15))) * 2 + (r & 1)];
+                }
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    u32x4 vt;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t w0 = (mi >> 1) ? x[2 * j].y : x[2 * j].x;
+                        const uint32_t w1 = (mi >> 1) ? x[2 * j + 1].y : x[2 * j + 1].x;
+                        vt[j] = __builtin_amdgcn_perm(w1, w0, (mi & 1) ? 0x07060302u : 0x05040100u);
+                    }
+                    O[mi] = mfma32(vt, P, O[mi]);
+                }
+            }
+        }
+    };
+    if (nst > 0) issue(0, kv_a);
+    if (nst > 1) issue(1, kv_b);
+    for (int i = 0; i < nst; i += kStages) {
+        step(i, kv_a, kv_c);
+        if (i + 1 >= nst) break;
+        step(i + 1, kv_b, kv_a);
+        if (i + 2 >= nst) break;
+        step(i + 2, kv_c, kv_b);
+    }
+    l += __shfl_xor(l, 32, 64);
+    if (rho >= a.Rp) return;
+
+    // register i of block mi holds dim 4 * rho_i + mi, rho_i = 8 (i / 4) + 4 hf + i % 4
+    const bool empty = (m == -INFINITY);
+    if (a.SB == 1 && !a.defer) {
+        const size_t o = out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq);
+        const float inv = empty ? 0.f : 1.0f / l;
+        if (a.lse_out && hf == 0) a.lse_out[o] = empty ? -INFINITY : (m + log2f(l)) * kLn2;
+        float wl = 0.f, wx = 0.f, it = 0.f;
+        bool none = true;
+        if (a.x_lse) {
+            const float mx = a.x_lse[o] * kLog2e;
+            const float Mt = fmaxf(m, mx);
+            none = (Mt == -INFINITY);
+            wl = (none || empty) ? 0.f : exp2f(m - Mt);
+            wx = none ? 0.f : exp2f(mx - Mt);
+            const float Lt = wl * l + wx;
+            it = none ? 0.f : 1.0f / Lt;
+            if (a.out_lse && hf == 0) a.out_lse[o] = none ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int dc = 4 * (8 * (i >> 2) + 4 * hf + (i & 3));
+            const f32x4 v = {O[0][i], O[1][i], O[2][i], O[3][i]};
+            if (a.A_out) *(f32x4 *)(a.A_out + o * kD + dc) = v * inv;
+            if (a.x_lse && a.out) {
+                const f32x4 xa = *(const f32x4 *)(a.x_A + o * kD + dc);
+                const f32x4 ov = (wl * v + wx * xa) * it;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st_out<uint16_t>((uint16_t *)a.out, o * kD + dc + e, none ? 0.f : ov[e]);
+            }
+        }
+    } else {
+        const size_t row = (size_t)(p * a.SB + sb) * a.Rp + rho;
+        if (hf == 0) a.part_ml[row] = make_float2(m, l);
+        float *op = a.part_O + row * kD;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int dc = 4 * (8 * (i >> 2) + 4 * hf + (i & 3));
+            *(f32x4 *)(op + dc) = f32x4{O[0][i], O[1][i], O[2][i], O[3][i]};
+        }
+    }
+}
+
 // One wave per SIMD with 96-key stages (144 KB of LDS, two stages in flight)
-// when a block's four row tiles cover the problem; otherwise eight waves (two
-// per SIMD) with 64-key stages.
-LdsShape lds_shape_for(int Rp) { return Rp <= 64 ? LdsShape{4, 1, 96} : LdsShape{8, 1, 64}; }
+// when a block's four row tiles cover the problem; otherwise the 32-row kernel
+// (eight waves, two per SIMD, 64-key stages).
+// RT == 2 selects the 32-row kernel (eight waves, 256 rows per block).
+LdsShape lds_shape_for(int Rp) { return Rp <= 64 ? LdsShape{4, 1, 96} : LdsShape{8, 2, 64}; }
 
 hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st) {
     dim3 grid((unsigned)((long)p.P * p.RB * p.SB)), block(sh.NW * 64);
     if (sh.NW == 4 && sh.RT == 1 && sh.SK == 96) hipLaunchKernelGGL((attn_rows_lds<4, 1, 96>), grid, block, 0, st, p);
     else if (sh.NW == 8 && sh.RT == 1 && sh.SK == 64) hipLaunchKernelGGL((attn_rows_lds<8, 1, 64>), grid, block, 0, st, p);
+    else if (sh.NW == 8 && sh.RT == 2 && sh.SK == 64) hipLaunchKernelGGL((attn_rows_lds32<8, 64>), grid, block, 0, st, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -9,11 +9,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnectar.so")
-SOURCES = ["attn.hip", "attn_lds.hip", "mlp.hip", "mlp_prefill.hip", "finish.hip", "step.hip", "nectar_abi.cpp"]
+SOURCES = ["attn.hip", "attn_lds.hip", "mlp.hip", "mlp_prefill.hip", "mlp_lds.hip", "finish.hip", "step.hip", "nectar_abi.cpp"]
 # Per-source code-generation options: the LDS-staged attention keeps its MFMA
 # accumulators in ordinary VGPRs (with accumulation registers the compiler
 # copies them back and forth around the softmax on every tile).
-SOURCE_FLAGS = {"attn_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"attn_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "mlp_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # Packed fp32 VALU ops are kept out of every HIP object.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",

@@ -27,6 +27,7 @@
 // skipped; P <= 2^kSlack keeps every sum finite and the result is unchanged
 // (the same reference max is used for the numerator and the denominator).
 #include "attn_common.hpp"
+#include "lds_common.hpp"
 
 namespace nectar {
 
@@ -36,20 +37,6 @@ constexpr int kD = 128, kKS = 4, kDV = 8;
 constexpr int kStages = 3;
 constexpr int kPieces = kD * 2 / 16;            // 16-byte pieces per key row
 constexpr float kSlack = 8.0f;
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt low bits [3:0], high bits [15:14]; expcnt and lgkmcnt at their maxima).
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Workgroup barrier that the compiler may not move memory operations across
-// (the bare builtin is not a memory barrier to the optimiser) and that adds
-// no waits of its own: the LDS copies are waited for explicitly above it.
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 }  // namespace
 

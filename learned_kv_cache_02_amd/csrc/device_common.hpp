@@ -120,6 +120,21 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 
 // Activation fixed at compile time (0: GELU erf form, 1: SiLU, 2: GELU tanh
 // form, the values of nectar_act), so only one is evaluated.
+// erf-form GELU for the VALU-bound batched MLP kernels: x * Phi(x) with Phi
+// written as sigmoid(p(x)), p an odd polynomial of degree 9 fitted to the
+// logit of Phi (fit_gelu_erf.py; max |Phi error| 1.5e-6, so |GELU error| <=
+// 6e-6 on |x| <= 9 and less beyond).  Coefficients below are c1..c9 times
+// -log2(e), so exp2 of p(x) x gives exp(-logit).  Five multiply-adds, one exp2
+// and one reciprocal, no table.
+__device__ __forceinline__ float gelu_erf_sigmoid(float x) {
+    const float u = x * x;
+    float p = __builtin_fmaf(u, -4.153249158e-06f, 1.066830016e-04f);
+    p = __builtin_fmaf(p, u, 2.487620203e-04f);
+    p = __builtin_fmaf(p, u, -1.049971051e-01f);
+    p = __builtin_fmaf(p, u, -2.302170342e+00f);
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p * x));
+}
+
 template <int ACT> __device__ __forceinline__ float act_fn(float x) {
     return ACT == 1 ? silu(x) : (ACT == 2 ? gelu_tanh(x) : gelu_erf(x));
 }

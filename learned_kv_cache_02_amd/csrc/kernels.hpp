@@ -126,6 +126,9 @@ hipError_t launch_step_partials(const AttnParams &p0, const AttnParams *p1, cons
 hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipStream_t st);
 hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st);
+// MLP on the 32x32 MFMA with LDS-staged weights (bf16, d = 128, Ht and Hs
+// multiples of 64); grid Hkv x ceil(Rp / 256) x SB, 64-unit split granularity.
+hipError_t launch_mlp_rows_lds32(const MlpParams &p, hipStream_t st);
 // Batched-prefill MLP (bf16, d = 128): one pass, no workspace.
 hipError_t launch_mlp_prefill(const MlpParams &p, hipStream_t st);
 hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st);

@@ -1,0 +1,219 @@
+// Nectar MLP module forward for many query rows (batched decode and prefill):
+// the one-hidden-layer score/target networks of Eq. (3.6) of the Nectar notes,
+//   target A = sum_j W2t[h][j] * act(W1[h][j] . q + b1[h][j]) + b2[h]
+//   score  a = sum_j ws2[h][j] * act(Ws[h][j] . q + bs[h][j]) + bs2[h],
+// on the 32x32x16 MFMA with the weights staged through LDS by direct copies.
+//
+// A block of eight waves (two per SIMD) owns 256 query rows of one KV head, 32
+// per wave, and one range of hidden units; the units stream through a
+// three-stage LDS ring of 64-unit stages (first-layer rows, read-out rows,
+// biases and score weights), copied HBM -> LDS two stages ahead with every
+// 256-byte row's 16-byte pieces XOR-swizzled by the unit (conflict-free operand
+// reads).  Per 32-unit chunk a wave runs
+//   Z^T (32 units x 32 rows) = b + sum over 8 slices of 16 dims of W1 . Q^T
+//       (the bias is the accumulator's initial value),
+//   H = act(Z), and for target chunks O^T (128 x 32) += W2t^T . H^T as
+//       4 dim blocks x 2 unit groups: H's accumulator registers 8t .. 8t + 7
+//       are the B operand of unit group t as they stand, and the read-out
+//       operand follows the same unit order (the attention kernel's V trick);
+//   for score chunks, a dot of H with ws2 in fp32.
+// The erf-form GELU is evaluated as x * sigmoid(p(x)) (gelu_erf_sigmoid).
+// The unit counts of both nets must be multiples of 64 (every workload's are;
+// other widths use mlp_prefill.hip).
+#include "lds_common.hpp"
+#include "kernels.hpp"
+
+namespace nectar {
+
+namespace {
+
+constexpr int kD = 128, kNW = 8, kThreads = 64 * kNW, kRows = 32 * kNW, kSU = 64, kPieces = 16;
+constexpr int kStages = 3;
+
+struct UnitStage {
+    u32x4 w1[kSU * kPieces];      // first-layer (or score first-layer) rows
+    u32x4 w2[kSU * kPieces];      // read-out rows (target stages)
+    float b[kSU];                 // b1 or bs
+    uint16_t ws2[kSU];            // score read-out weights (score stages)
+};
+
+}  // namespace
+
+template <int ACT>
+__global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
+    // separate variables, so the compiler tells copies into one stage from reads of another
+    __shared__ UnitStage st_a, st_b, st_c;
+
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, hf = lane >> 5, r = lane & 31;
+    const int nrb = (a.Rp + kRows - 1) / kRows;
+    const int sb = blockIdx.x % a.SB, hr = blockIdx.x / a.SB;
+    const int h = hr / nrb, rb = hr - h * nrb;
+
+    auto act = [&](float x) { return ACT == 0 ? gelu_erf_sigmoid(x) : act_fn<ACT>(x); };
+
+    const int rho = rb * kRows + w * 32 + r;
+    u32x4 qv[8];
+    if (rho < a.Rp) {
+        const int tk = rho / a.G, gg = rho - tk * a.G;
+        const uint16_t *qp = (const uint16_t *)a.q + ((size_t)tk * a.Hq + h * a.G + gg) * kD;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) qv[kt] = *(const u32x4 *)(qp + 16 * kt + 8 * hf);
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) qv[kt] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    const uint16_t *W1 = (const uint16_t *)a.W1 + (size_t)h * a.Ht * kD;
+    const uint16_t *W2t = (const uint16_t *)a.W2t + (size_t)h * a.Ht * kD;
+    const float *b1 = a.b1 + (size_t)h * a.Ht;
+    const uint16_t *Ws = (const uint16_t *)a.Ws + (size_t)h * a.Hs * kD;
+    const uint16_t *ws2 = (const uint16_t *)a.ws2 + (size_t)h * a.Hs;
+    const float *bs = a.bs + (size_t)h * a.Hs;
+    // this split's stages: target stages [t0, t0 + ntg), then score stages [s0, s0 + nsc)
+    const int ttot = a.Ht / kSU, stot = a.Hs / kSU;
+    const int cts = a.chunk_t / kSU, css = a.chunk_s / kSU;
+    const int t0 = min(sb * cts, ttot), s0 = min(sb * css, stot);
+    const int ntg = min(cts, ttot - t0), nst = ntg + min(css, stot - s0);
+
+    // Stage i: every wave copies 8 rows of each row table (two 1 KB copies
+    // each; score stages copy their first-layer rows twice so every wave issues
+    // the same count), wave 0 also the biases and score weights.
+    auto issue = [&](int i, UnitStage &dst) {
+        const bool tgt = i < ntg;
+        const int u0 = kSU * (tgt ? t0 + i : s0 + i - ntg);
+        const uint16_t *Wa = tgt ? W1 : Ws;
+        const uint16_t *Wb = tgt ? W2t : Ws;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int r0 = 8 * w + 4 * c, rr = r0 + (lane >> 4);
+            const int piece = (lane & 15) ^ (rr & 15);
+            const size_t off = (size_t)(u0 + rr) * kD + piece * 8;
+            __builtin_amdgcn_global_load_lds((const void *)(Wa + off), (lds_void *)&dst.w1[r0 * kPieces], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(Wb + off), (lds_void *)&dst.w2[r0 * kPieces], 16, 0, 0);
+        }
+        if (w == 0) {
+            // 64 biases = 16 pieces, 64 score weights = 8 pieces (score stages)
+            const float *bp = (tgt ? b1 : bs) + u0;
+            if (lane < 16)
+                __builtin_amdgcn_global_load_lds((const void *)(bp + 4 * lane), (lds_void *)dst.b, 16, 0, 0);
+            // target stages copy any valid 128 bytes (unused), so wave 0 always issues 6 copies
+            const void *sp = (!tgt) ? (const void *)(ws2 + u0 + 8 * lane)
+                                    : (a.Hs > 0 ? (const void *)(ws2 + 8 * lane) : (const void *)(bp + 4 * lane));
+            if (lane < 8) __builtin_amdgcn_global_load_lds(sp, (lds_void *)dst.ws2, 16, 0, 0);
+        }
+    };
+
+    f32x16 O[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) O[mi] = f32x16{};
+    float sc = 0.f;
+
+    auto step = [&](int i, const UnitStage &cur, UnitStage &ahead) {
+        // stage i has landed once at most the next stage's copies are pending
+        if (i + 1 < nst) {
+            if (w == 0) wait_vmcnt<6>();
+            else wait_vmcnt<4>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        stage_barrier();
+        if (i + 2 < nst) issue(i + 2, ahead);
+        const bool tgt = i < ntg;
+        const uint2 *W2s = (const uint2 *)cur.w2;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            // bias of the lane's 16 units 32c + 8q + 4hf + (0..3) as the accumulator's start
+            f32x16 Z;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 bq = *(const f32x4 *)&cur.b[32 * c + 8 * q + 4 * hf];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Z[4 * q + j] = bq[j];
+            }
+            const int ur = 32 * c + r;
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) Z = mfma32(cur.w1[ur * kPieces + ((2 * kt + hf) ^ (ur & 15))], qv[kt], Z);
+            float hv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) hv[j] = act(Z[j]);
+            if (tgt) {
+#pragma unroll
+                for (int tg = 0; tg < 2; ++tg) {
+                    const u32x4 H = {pack_bf16(hv[8 * tg + 0], hv[8 * tg + 1]), pack_bf16(hv[8 * tg + 2], hv[8 * tg + 3]),
+                                     pack_bf16(hv[8 * tg + 4], hv[8 * tg + 5]), pack_bf16(hv[8 * tg + 6], hv[8 * tg + 7])};
+                    uint2 x[8];
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const int u = 32 * c + 16 * tg + 8 * (s >> 2) + 4 * hf + (s & 3);
+                        x[s] = W2s[(u * kPieces + ((r >> 1) ^ (u & 15))) * 2 + (r & 1)];
+                    }
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi) {
+                        u32x4 vt;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t w0 = (mi >> 1) ? x[2 * j].y : x[2 * j].x;
+                            const uint32_t w1 = (mi >> 1) ? x[2 * j + 1].y : x[2 * j + 1].x;
+                            vt[j] = __builtin_amdgcn_perm(w1, w0, (mi & 1) ? 0x07060302u : 0x05040100u);
+                        }
+                        O[mi] = mfma32(vt, H, O[mi]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint2 wq = *(const uint2 *)&cur.ws2[32 * c + 8 * q + 4 * hf];
+                    sc = __builtin_fmaf(bf16lo(wq.x), hv[4 * q + 0], sc);
+                    sc = __builtin_fmaf(bf16hi(wq.x), hv[4 * q + 1], sc);
+                    sc = __builtin_fmaf(bf16lo(wq.y), hv[4 * q + 2], sc);
+                    sc = __builtin_fmaf(bf16hi(wq.y), hv[4 * q + 3], sc);
+                }
+            }
+        }
+    };
+    if (nst > 0) issue(0, st_a);
+    if (nst > 1) issue(1, st_b);
+    for (int i = 0; i < nst; i += kStages) {
+        step(i, st_a, st_c);
+        if (i + 1 >= nst) break;
+        step(i + 1, st_b, st_a);
+        if (i + 2 >= nst) break;
+        step(i + 2, st_c, st_b);
+    }
+    sc += __shfl_xor(sc, 32, 64);
+    if (rho >= a.Rp) return;
+
+    // register i of block mi holds dim 4 * rho_i + mi, rho_i = 8 (i / 4) + 4 hf + i % 4
+    if (a.SB > 1 || a.defer) {
+        const size_t row = (size_t)(h * a.SB + sb) * a.Rp + rho;
+        if (hf == 0) a.part_s[row] = sc;
+        float *op = a.part_O + row * kD;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int dc = 4 * (8 * (i >> 2) + 4 * hf + (i & 3));
+            *(f32x4 *)(op + dc) = f32x4{O[0][i], O[1][i], O[2][i], O[3][i]};
+        }
+        return;
+    }
+    const int tk = rho / a.G, gg = rho - tk * a.G;
+    const size_t o = (size_t)tk * a.Hq + h * a.G + gg;
+    if (hf == 0) a.a_out[o] = a.bs2[h] + sc;
+    const float *b2 = a.b2 + (size_t)h * kD;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int dc = 4 * (8 * (i >> 2) + 4 * hf + (i & 3));
+        const f32x4 bb = *(const f32x4 *)(b2 + dc);
+        *(f32x4 *)(a.A_out + o * kD + dc) = bb + f32x4{O[0][i], O[1][i], O[2][i], O[3][i]};
+    }
+}
+
+hipError_t launch_mlp_rows_lds32(const MlpParams &p, hipStream_t st) {
+    const long nrb = (p.Rp + kRows - 1) / kRows;
+    dim3 grid((unsigned)(p.Hkv * nrb * p.SB)), block(kThreads);
+    if (p.act == 1) hipLaunchKernelGGL(mlp_rows_lds32<1>, grid, block, 0, st, p);
+    else if (p.act == 2) hipLaunchKernelGGL(mlp_rows_lds32<2>, grid, block, 0, st, p);
+    else hipLaunchKernelGGL(mlp_rows_lds32<0>, grid, block, 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace nectar

@@ -1,6 +1,7 @@
 // Nectar MLP module forward for many query rows (batched prefill): the same
 // one-hidden-layer score/target networks as mlp.hip (Eq. (3.6) of the Nectar
-// notes with one hidden layer), tiled for the MFMA-bound regime.
+// notes with one hidden layer), tiled for the MFMA-bound regime.  This kernel
+// serves hidden widths that are not multiples of 64; mlp_lds.hip serves the rest.
 //
 // A block of 8 waves (two per SIMD, so one wave's activations overlap the
 // other's matrix work) owns 256 query rows of one KV head -- all G query heads
@@ -17,15 +18,7 @@
 // so the hidden activations never leave registers; score chunks run
 //   Zs^T = bs + Ws_chunk . Q^T -> act -> fp32 dot with ws2.
 //
-// The erf-form GELU is x * Phi(x).  Each block tabulates Phi in LDS at 2049
-// points over [-16, 16] (value and slope to the next point, evaluated in double
-// precision) and evaluates x * Phi(x) by linear interpolation, clamping outside
-// the range where Phi is 0 or 1 to within 1e-57: about seven VALU operations
-// and one 8-byte LDS read per hidden value instead of an exponential, a
-// reciprocal and a rational polynomial.  The interpolation error of Phi is at
-// most h^2 / 8 * max|Phi''| <= 7.4e-6 for h = 1/64.  SiLU and the tanh form are
-// cheaper to evaluate directly (one exponential and one reciprocal) and are
-// evaluated that way.
+// The erf-form GELU is evaluated as x * sigmoid(p(x)) (gelu_erf_sigmoid).
 // With one split (SB == 1) the block adds the output biases and writes (a, A);
 // with SB > 1 splits of the hidden units, block (h, row block, split) writes its
 // partial sums and mlp_reduce adds them in split order with the biases.
@@ -37,21 +30,6 @@ namespace nectar {
 namespace {
 
 constexpr int kD = 128, kKS = 4, kDV = 8, kRTW = 2, kThreads = 512, kRows = kThreads / 64 * kRTW * 16;
-constexpr int kTabN = 2048;              // intervals of the activation table
-constexpr float kTabL = 16.0f;           // table range [-kTabL, kTabL]
-
-// Phi(x), the standard normal CDF, in double precision.
-__device__ double normal_cdf(double x) { return 0.5 * erfc(-x * 0.70710678118654752440); }
-
-// x * Phi(x) by linear interpolation in the table (value, slope) of Phi.
-__device__ __forceinline__ float gelu_table(const float2 *tab, float x) {
-    float t = __builtin_fmaf(x, kTabN / (2.0f * kTabL), kTabN / 2.0f);
-    t = __builtin_amdgcn_fmed3f(t, 0.0f, (float)kTabN);
-    const int i = (int)t;
-    const float2 e = tab[i];
-    return x * __builtin_fmaf(t - (float)i, e.y, e.x);
-}
-
 __device__ __forceinline__ int unit_of_slot(int g, int j) { return 16 * (j >> 2) + 4 * g + (j & 3); }
 
 // One chunk's share of thread t: piece t of the 32 x 128 first-layer tile and
@@ -67,7 +45,6 @@ struct Smem {
     uint16_t w2t[2][4][8][16][8];   // [buf][g][mm][c][slot j]: W2t[unit(g, j)][8c + mm]
     float b[2][32];
     float s[2][32];
-    float2 tab[kTabN + 1];
 };
 
 __device__ __forceinline__ void stage_load(Stage &S, const uint16_t *W, const uint16_t *W2, const float *bias,
@@ -106,15 +83,7 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
     const int sb = blockIdx.x % a.SB, hr = blockIdx.x / a.SB;
     const int h = hr / nrb, rb = hr - h * nrb;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, c = lane & 15;
-    // GELU table (the first barrier below orders it before any use)
-    if (ACT == 0) {
-        for (int i = t; i <= kTabN; i += kThreads) {
-            const double step = 2.0 * kTabL / kTabN, x0 = -kTabL + i * step;
-            const double g0 = normal_cdf(x0), g1 = i < kTabN ? normal_cdf(x0 + step) : g0;
-            sm.tab[i] = make_float2((float)g0, (float)(g1 - g0));
-        }
-    }
-    auto act = [&](float x) { return ACT == 0 ? gelu_table(sm.tab, x) : act_fn<ACT>(x); };
+    auto act = [&](float x) { return ACT == 0 ? gelu_erf_sigmoid(x) : act_fn<ACT>(x); };
 
     u32x4 qv[kRTW][kKS];
 #pragma unroll

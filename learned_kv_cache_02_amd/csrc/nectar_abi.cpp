@@ -136,7 +136,8 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv) {
 struct MlpPlan {
     int Rp = 0, RT = 0, RG = 0, S = 0, ct = kTile, cs = kTile;
     int WR = 1, WS = 1, RB = 0, SB = 0;
-    bool prefill = false;
+    bool prefill = false;   // a batched kernel (LDS-staged weights)
+    bool lds32 = false;     // ... the 32x32 one (unit counts multiples of 64)
     size_t ws = 0;
 };
 
@@ -154,6 +155,24 @@ MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs) {
     if (pl.Rp == 0) return pl;
     const long tt = cdiv(Ht, kTile), ts = cdiv(Hs, kTile);
     const long tmax = tt > ts ? (tt > 1 ? tt : 1) : (ts > 1 ? ts : 1);
+    if (d->dtype == NECTAR_BF16 && d->d == 128 && pl.Rp >= kPrefillRows && Ht % 64 == 0 && Hs % 64 == 0) {
+        // 32x32 batched kernel: 256-row blocks x hidden-unit splits of whole 64-unit stages
+        pl.prefill = pl.lds32 = true;
+        pl.RB = (int)cdiv(pl.Rp, kPrefillBlockRows);
+        const long gt = cdiv(Ht, 64), gs = cdiv(Hs, 64);
+        const long gmax = gt > gs ? (gt > 1 ? gt : 1) : (gs > 1 ? gs : 1);
+        long S = d->splits > 0 ? d->splits : cdiv(kTargetBlocksPrefill, (long)d->Hkv * pl.RB);
+        S = S < 1 ? 1 : (S > gmax ? gmax : S);
+        const long pt = cdiv(gt, S), ps = cdiv(gs, S);
+        long Se = 1;
+        if (pt > 0 && cdiv(gt, pt) > Se) Se = cdiv(gt, pt);
+        if (ps > 0 && cdiv(gs, ps) > Se) Se = cdiv(gs, ps);
+        pl.S = pl.SB = (int)Se;
+        pl.ct = (int)(pt * 64);
+        pl.cs = (int)(ps * 64);
+        pl.ws = pl.SB > 1 ? (size_t)d->Hkv * pl.SB * pl.Rp * ((size_t)d->d * 4 + 4) : 0;
+        return pl;
+    }
     if (d->dtype == NECTAR_BF16 && d->d == 128 && pl.Rp >= kPrefillRows) {
         // batched kernel: 256-row blocks x hidden-unit splits of whole 32-unit chunks
         pl.prefill = true;
@@ -346,7 +365,8 @@ static hipError_t run_mlp(const nectar_attn_desc *desc, const MlpPlan &pl, const
     a.part_O = part_O; a.part_s = part_s;
     a.a_out = a_out; a.A_out = A_out;
     const bool in_place = pl.SB == 1 && (pl.prefill || desc->dtype == NECTAR_BF16);
-    hipError_t e = pl.prefill ? launch_mlp_prefill(a, st) : launch_mlp_partial(a, desc->dtype, desc->d, pl.RT, st);
+    hipError_t e = pl.lds32 ? launch_mlp_rows_lds32(a, st)
+                            : (pl.prefill ? launch_mlp_prefill(a, st) : launch_mlp_partial(a, desc->dtype, desc->d, pl.RT, st));
     if (e == hipSuccess && !in_place) {
         MlpReduceParams r;
         r.part_O = part_O; r.part_s = part_s; r.b2 = m->b2; r.bs2 = m->bs2;
@@ -763,8 +783,9 @@ nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const n
         x.lse_out = outs->a_out; x.A_out = outs->Am_out; x.out = outs->out_nectar; x.out_lse = outs->lse_nectar;
         if (sp.mlp) {
             if (!mod_done)
-                e = sp.mlpl.prefill ? launch_mlp_prefill(mp, st)
-                                    : launch_mlp_partial(mp, desc->dtype, desc->d, sp.mlpl.RT, st);
+                e = sp.mlpl.lds32 ? launch_mlp_rows_lds32(mp, st)
+                                  : (sp.mlpl.prefill ? launch_mlp_prefill(mp, st)
+                                                     : launch_mlp_partial(mp, desc->dtype, desc->d, sp.mlpl.RT, st));
             x.S = sp.mlpl.SB;
             x.s = (const float *)(w + sp.off_mod + (size_t)desc->Hkv * sp.mlpl.SB * sp.mlpl.Rp * desc->d * 4);
             x.b2 = module->b2; x.bs2 = module->bs2;

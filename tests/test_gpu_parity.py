@@ -163,7 +163,8 @@ def _mlp_oracle(q, P, dt, Hq, Hkv, act):
 
 @pytest.mark.parametrize("R,Hq,Hkv,Ht,Hs", [(5, 14, 2, 100, 70), (1, 32, 8, 256, 96), (20, 8, 2, 64, 33),
                                              (3, 4, 1, 0, 40), (3, 4, 1, 50, 0), (10, 16, 4, 300, 200),
-                                             (64, 32, 8, 600, 300)])
+                                             (64, 32, 8, 600, 300), (10, 16, 4, 256, 128), (64, 32, 8, 640, 320),
+                                             (20, 8, 2, 0, 64)])
 @pytest.mark.parametrize("act", ["gelu", "silu", "gelu_tanh"])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_mlp_bf16(nx, R, Hq, Hkv, Ht, Hs, act, splits):
@@ -180,7 +181,8 @@ def test_mlp_bf16(nx, R, Hq, Hkv, Ht, Hs, act, splits):
 
 
 @pytest.mark.parametrize("act", ["gelu", "silu", "gelu_tanh"])
-@pytest.mark.parametrize("R,Hq,Hkv,Ht,Hs", [(300, 28, 4, 100, 70), (600, 32, 8, 256, 33), (520, 8, 2, 7680, 0)])
+@pytest.mark.parametrize("R,Hq,Hkv,Ht,Hs", [(300, 28, 4, 100, 70), (600, 32, 8, 256, 33), (520, 8, 2, 7680, 0),
+                                             (400, 28, 4, 768, 512)])
 def test_mlp_batched_prefill_bf16(nx, R, Hq, Hkv, Ht, Hs, act):
     """Row counts large enough for the LDS-staged batched kernel (ragged rows and units)."""
     d = 128

@@ -389,3 +389,27 @@ def test_capacity_ratio_matches_table9():
             # module bytes = rho * doc KV bytes; the KV column is printed to 10 MB
             # (half-unit 5 MB) and the module column to 1 MB (half-unit 0.5 MB).
             assert abs(float(rho) * row["doc_kv_gb"] * 1000.0 - mb) <= float(rho) * 5.0 + 0.5 + 1e-9
+
+
+def test_batched_gelu_approximation_against_the_oracle():
+    """The batched MLP kernels evaluate the erf GELU as x * sigmoid(p(x)) with the
+    coefficients in csrc/device_common.hpp: pinned against the oracle's exact
+    x * Phi(x) (and the fit script's reported error) on a dense grid."""
+    import os
+    import re
+    import numpy as np
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "learned_kv_cache_02_amd", "csrc", "device_common.hpp")).read()
+    body = src[src.index("float gelu_erf_sigmoid(float x)"):]
+    body = body[:body.index("}")]
+    c = [float(v) for v in re.findall(r"([-+]?\d\.\d+e[-+]\d+)f", body)]
+    assert len(c) == 5                      # c9, c7, then c5, c3, c1 (times -log2 e)
+    c9, c7, c5, c3, c1 = c
+    xs = np.linspace(-12.0, 12.0, 4801)
+    worst = 0.0
+    for x in xs.tolist():
+        u = x * x
+        p = (((c9 * u + c7) * u + c5) * u + c3) * u + c1
+        approx = x / (1.0 + 2.0 ** min(p * x, 1000.0))
+        worst = max(worst, abs(approx - oracle.gelu(x)))
+    assert worst < 1e-5, worst

@@ -51,6 +51,8 @@ def _L():
         lib.oracle_mlp.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
         lib.oracle_merge.argtypes = [L, I, P, P, P, P, P, P]
         lib.oracle_merge.restype = None
+        lib.oracle_merge_k.argtypes = [L, I, I, P, P, P, P, P, P]
+        lib.oracle_merge_k.restype = None
         lib.oracle_gelu.argtypes = [D]
         lib.oracle_gelu.restype = D
         lib.oracle_silu.argtypes = [D]
@@ -181,6 +183,27 @@ def merge(a, A, lam, Aloc):
         raise ValueError("inconsistent merge shapes")
     out = np.empty(A.shape); lse = np.empty(a.shape)
     _L().oracle_merge(rows, d, _p(a), _p(A), _p(lam), _p(Aloc), _p(out), _p(lse))
+    return out, lse
+
+
+def merge_k(pairs, lam=None, Aloc=None):
+    """K-way merge of document-side pairs [(a_k, A_k)] with the optional local pair
+    (lam, Aloc).  Returns (out, lse) in float64."""
+    K = len(pairs)
+    a = np.ascontiguousarray(np.stack([_f64(p[0]) for p in pairs])) if K else np.zeros((0,))
+    A = np.ascontiguousarray(np.stack([_f64(p[1]) for p in pairs])) if K else np.zeros((0,))
+    shape_a = _f64(pairs[0][0]).shape if K else _f64(lam).shape
+    shape_A = _f64(pairs[0][1]).shape if K else _f64(Aloc).shape
+    d = shape_A[-1]
+    rows = int(np.prod(shape_a))
+    lam_a = _f64(lam) if lam is not None else None
+    Aloc_a = _f64(Aloc) if Aloc is not None else None
+    for p in pairs:
+        if _f64(p[0]).size != rows or _f64(p[1]).size != rows * d:
+            raise ValueError("inconsistent merge_k shapes")
+    out = np.empty(shape_A); lse = np.empty(shape_a)
+    _L().oracle_merge_k(rows, d, K, _p(a) if K else None, _p(A) if K else None, _p(lam_a), _p(Aloc_a),
+                        _p(out), _p(lse))
     return out, lse
 
 

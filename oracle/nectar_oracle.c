@@ -328,3 +328,42 @@ void oracle_merge(long rows, int d, const double *a, const double *A,
         lse[r] = M + log(wa + wl);
     }
 }
+
+/*
+ * K-way composition of document-side pairs with the local part: the pages'
+ * closing section proposes merging several context modules by one more
+ * softmax grouping over their (score, target) outputs, the virtual-logit form
+ * of Eqs. (3.4)-(3.5) with K virtual logits.  Per row:
+ *   out = (sum_k e^{a_k} A_k + e^{lam} A_loc) / (sum_k e^{a_k} + e^{lam}),
+ *   lse = log(sum_k e^{a_k} + e^{lam}),
+ * evaluated with the common maximum M of all logits; lam == NULL drops the local
+ * part; every logit -inf gives out = 0, lse = -inf.  a [K][rows], A [K][rows][d].
+ */
+void oracle_merge_k(long rows, int d, int K, const double *a, const double *A,
+                    const double *lam, const double *Aloc, double *out, double *lse)
+{
+    for (long r = 0; r < rows; ++r) {
+        double M = lam ? lam[r] : -INFINITY;
+        for (int k = 0; k < K; ++k)
+            if (a[(size_t)k * rows + r] > M) M = a[(size_t)k * rows + r];
+        double *o = &out[(size_t)r * d];
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        if (M == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double den = 0.0;
+        for (int k = 0; k < K; ++k) {
+            const double w = exp(a[(size_t)k * rows + r] - M);
+            den += w;
+            for (int c = 0; c < d; ++c) o[c] += w * A[((size_t)k * rows + r) * d + c];
+        }
+        if (lam) {
+            const double w = exp(lam[r] - M);
+            den += w;
+            for (int c = 0; c < d; ++c) o[c] += w * Aloc[(size_t)r * d + c];
+        }
+        for (int c = 0; c < d; ++c) o[c] /= den;
+        lse[r] = M + log(den);
+    }
+}

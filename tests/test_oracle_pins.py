@@ -198,6 +198,72 @@ def test_p5_split_invariance():
         assert np.max(np.abs(o - A)) < 1e-14 and np.max(np.abs(l - a)) < 1e-14
 
 
+# --- K-way composition (closing section: several context modules merged) -------
+
+@pytest.mark.parametrize("cuts", [(0, 11), (0, 4, 11), (0, 1, 5, 9, 11), (0, 3, 3, 7, 11)])
+def test_merge_k_chunked_document_equals_full_attention(cuts):
+    """Splitting the document into key ranges, taking each range's exact pair and
+    merging all of them with the local pair is one softmax over every key."""
+    B, Tq, Hq, Hkv, n, d, Tloc, qoff = 2, 3, 4, 2, 11, 8, 6, 2
+    R = B * Tq
+    q = _rand(R, Hq, d)
+    K, V = _rand(Hkv, n, d), _rand(Hkv, n, d)
+    Kl, Vl = _rand(B, Hkv, Tloc, d), _rand(B, Hkv, Tloc, d)
+    kw = dict(dt="f64", B=B, Tq=Tq, Hq=Hq, Hkv=Hkv, Tloc=Tloc, q_offset=qoff)
+    pairs = []
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        if hi > lo:
+            pairs.append(oracle.doc_attn(q, np.ascontiguousarray(K[:, lo:hi]),
+                                         np.ascontiguousarray(V[:, lo:hi]), dt="f64", Hq=Hq, Hkv=Hkv))
+        else:   # an empty range: the empty log-sum-exp pair
+            pairs.append((np.full((R, Hq), -np.inf), np.zeros((R, Hq, d))))
+    lam, Al = oracle.local_attn(q, Kl, Vl, **kw)
+    out, lse = oracle.merge_k(pairs, lam, Al)
+    flse, fout = oracle.full_attn(q, K, V, Kl, Vl, **kw)
+    assert np.max(np.abs(out - fout)) < 1e-12
+    assert np.max(np.abs(lse - flse)) < 1e-12
+    # without the local pair: attention over the document alone
+    a, A = oracle.doc_attn(q, K, V, dt="f64", Hq=Hq, Hkv=Hkv)
+    o2, l2 = oracle.merge_k(pairs)
+    assert np.max(np.abs(o2 - A)) < 1e-12 and np.max(np.abs(l2 - a)) < 1e-12
+
+
+def test_merge_k_special_cases():
+    rows, d = 5, 4
+    ps = [(_rand(rows), _rand(rows, d)) for _ in range(3)]
+    lam, Al = _rand(rows), _rand(rows, d)
+    o, l = oracle.merge_k(ps, lam, Al)
+    # order of the document-side pairs does not matter
+    o2, l2 = oracle.merge_k(ps[::-1], lam, Al)
+    assert np.max(np.abs(o - o2)) < 1e-14 and np.max(np.abs(l - l2)) < 1e-14
+    # one pair reduces to the two-way merge of Eqs. (3.4)-(3.5)
+    o1, l1 = oracle.merge_k(ps[:1], lam, Al)
+    om, lm = oracle.merge(ps[0][0], ps[0][1], lam, Al)
+    assert np.max(np.abs(o1 - om)) < 1e-15 and np.max(np.abs(l1 - lm)) < 1e-15
+    # no document-side pair: the local pair itself
+    o0, l0 = oracle.merge_k([], lam, Al)
+    assert np.max(np.abs(o0 - Al)) < 1e-15 and np.max(np.abs(l0 - lam)) < 1e-15
+    # the grouping is associative: merging the first two, then the rest, is the same
+    oa, la = oracle.merge(ps[0][0], ps[0][1], ps[1][0], ps[1][1])
+    ob, lb = oracle.merge_k([(la, oa), ps[2]], lam, Al)
+    assert np.max(np.abs(ob - o)) < 1e-14 and np.max(np.abs(lb - l)) < 1e-14
+    # equal scores give the plain mean of the read-outs, lse = score + log(K + 1)
+    s = np.full(rows, 0.7)
+    oe, le = oracle.merge_k([(s, p[1]) for p in ps], s, Al)
+    mean = (ps[0][1] + ps[1][1] + ps[2][1] + Al) / 4
+    assert np.max(np.abs(oe - mean)) < 1e-15 and np.max(np.abs(le - (0.7 + math.log(4)))) < 1e-15
+    # -inf logits drop out; every logit -inf gives (0, -inf)
+    ninf = np.full(rows, -np.inf)
+    od, ld = oracle.merge_k([ps[0], (ninf, _rand(rows, d))], ninf, _rand(rows, d))
+    assert np.max(np.abs(od - ps[0][1])) < 1e-15 and np.max(np.abs(ld - ps[0][0])) < 1e-15
+    oz, lz = oracle.merge_k([(ninf, _rand(rows, d))] * 2, ninf, Al)
+    assert np.all(oz == 0.0) and np.all(lz == -np.inf)
+    # large logits do not overflow (the common maximum is subtracted)
+    big = [(p[0] + 800.0, p[1]) for p in ps]
+    ob2, lb2 = oracle.merge_k(big, lam + 800.0, Al)
+    assert np.max(np.abs(ob2 - o)) < 1e-12 and np.max(np.abs(lb2 - (l + 800.0))) < 1e-12
+
+
 # --- P6: gradient identity of the log-normalizer (Appendix B) ------------------
 
 def test_p6_gradient_is_key_weighted_average():

@@ -137,7 +137,7 @@ def workspace(nbytes: int, device=None) -> Optional[torch.Tensor]:
     key = (dev.type, dev.index)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        # zero-filled once: the library keeps its split counters zero afterwards
+        # workspace contents need no initialisation; zeroed once for reproducible scratch
         buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf

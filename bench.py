@@ -280,6 +280,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_prefill and args.only is None:
         res["prefill_mlp"] = prefill_mlp(torch, np, nectar, configs, synth, dev)
+        res["merge_k"] = merge_k_prefill(torch, nectar, configs, dev)
     if not args.no_workloads and args.only is None:
         res["workloads"] = {c.name: workload_layer(torch, nectar, c, dev) for c in (configs.C4, configs.C5, configs.C3)}
 
@@ -443,6 +444,44 @@ def prefill_mlp(torch, np, nectar, configs, synth, dev):
                 "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops_per_layer": flops}
             del mods
     return out
+
+
+def merge_k_prefill(torch, nectar, configs, dev, K=4):
+    """HBM roofline of the K-way merge at the 16 x 1,024-token prefill shape
+    (28 query heads, d = 128): K document-side fp32 pairs and the local pair in,
+    the bf16 output and its log-normalizer out; N(0, 1) inputs from a seeded
+    device generator."""
+    cfg = configs.C3
+    R, Hq, d = cfg.R, cfg.Hq, cfg.d
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    f32 = dict(dtype=torch.float32, device=dev)
+    rn = lambda *s: torch.randn(*s, generator=g, **f32)
+    pairs = [(rn(R, Hq), rn(R, Hq, d)) for _ in range(K)]
+    lam, Al = rn(R, Hq), rn(R, Hq, d)
+    out = torch.empty((R, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((R, Hq), **f32)
+    call = lambda: nectar.merge_k(pairs, lam, Al, Hkv=cfg.Hkv, out_dtype=torch.bfloat16, out=out, lse_out=lse)
+    call()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(8):
+            call()
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(4):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 32 * 1e3
+    nbytes = R * Hq * ((K + 1) * (4 + 4 * d) + 2 * d + 4)
+    del gr, pairs, lam, Al, out, lse
+    torch.cuda.empty_cache()
+    return {"K": K, "rows": R * Hq, "us": us, "bytes_per_launch": nbytes, "gbs": nbytes / us / 1e3,
+            "frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "bound": "hbm"}
 
 
 def cpu_baseline(cfg, q, K, V, Kl, Vl, P, budget_s):

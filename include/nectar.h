@@ -16,6 +16,7 @@
  *   nectar_local_attn_lse   causal local attention (log Z_local, A_local),
  *                           section 2.2, optionally merged with a document pair
  *   nectar_merge            the log-sum-exp merge of Eqs. (3.4)-(3.5)
+ *   nectar_merge_k          the same over K document-side pairs
  *   nectar_layer_step       all of the above for one layer step, fused
  *
  * Conventions shared by every entry point
@@ -206,6 +207,31 @@ NECTAR_API nectar_status nectar_local_attn_lse(const nectar_attn_desc *desc, con
 NECTAR_API nectar_status nectar_merge(const nectar_attn_desc *desc, const float *a, const float *A,
                            const float *lam, const float *A_loc, void *out, float *lse_out,
                            void *stream);
+
+/*
+ * K-way log-sum-exp merge: the closing section of the Nectar notes proposes
+ * composing several context modules (documents, or pieces of one) by one more
+ * softmax grouping over their (score, target) pairs, the virtual-logit form of
+ * Eqs. (3.4)-(3.5) with K virtual logits.  Per row (R * Hq rows), with M the
+ * largest of a_0..a_{K-1} and lam:
+ *   out = (sum_k e^{a_k-M} A_k + e^{lam-M} A_loc) / (sum_k e^{a_k-M} + e^{lam-M}),
+ *   lse_out = M + log(sum_k e^{a_k-M} + e^{lam-M});
+ * every logit -inf gives out = 0, lse_out = -inf.  When the pairs are exact
+ * (alpha, A) over disjoint key ranges of one document, out is attention over
+ * their union (with the local keys when the local pair is given).
+ *   K          number of document-side pairs, 0..NECTAR_MERGE_K_MAX;
+ *   a, A       host arrays of K device pointers: a[k] [R][Hq] fp32 logits,
+ *              A[k] [R][Hq][d] fp32 read-outs; the host arrays are read during
+ *              the call only;
+ *   lam, A_loc the local pair ([R][Hq], [R][Hq][d] fp32), both or neither;
+ *   out        [R][Hq][d] in desc->dtype; lse_out [R][Hq] fp32, nullable.
+ * NECTAR_EINVAL for K out of range, lam without A_loc (or the reverse), no pair
+ * at all, or a misaligned pointer.
+ */
+#define NECTAR_MERGE_K_MAX 8
+NECTAR_API nectar_status nectar_merge_k(const nectar_attn_desc *desc, int K, const float *const *a,
+                             const float *const *A, const float *lam, const float *A_loc,
+                             void *out, float *lse_out, void *stream);
 
 /*
  * One layer step of both paths, fused (sections 2.1-2.2; the step loop of a

@@ -1,5 +1,5 @@
-// Split-K softmax attention with log-sum-exp partials, its combine, and the
-// log-sum-exp merge: the exact document path (Eq. (3.1) of the Nectar notes),
+// Split-K softmax attention with log-sum-exp partials and its combine: the
+// exact document path (Eq. (3.1) of the Nectar notes),
 // the Quadrature module (exact attention over p pairs) and the causal local
 // part (section 2.2), all as one kernel family.
 //
@@ -181,35 +181,6 @@ __global__ __launch_bounds__(256) void attn_combine(CombineParams a) {
     }
 }
 
-// Standalone merge of two (lse, A) pairs, one wave per row.
-template <int D, typename OutT>
-__global__ __launch_bounds__(256) void merge_pairs(MergeParams a) {
-    constexpr int NPL = D / 64;
-    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= a.rows) return;
-    const int lane = threadIdx.x & 63;
-    const float x = a.a[r], y = a.lam[r];
-    float va[NPL], vl[NPL];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const size_t e = (size_t)r * D + lane + 64 * i;
-        va[i] = a.A[e];
-        vl[i] = a.A_loc[e];
-    }
-    const float M = fmaxf(x, y);
-    if (M == -INFINITY) {
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) st_out<OutT>((OutT *)a.out, r * D + lane + 64 * i, 0.f);
-        if (a.lse_out && lane == 0) a.lse_out[r] = -INFINITY;
-        return;
-    }
-    const float wa = expf(x - M), wl = expf(y - M), den = wa + wl;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-        st_out<OutT>((OutT *)a.out, (size_t)r * D + lane + 64 * i, (wa * va[i] + wl * vl[i]) / den);
-    if (a.lse_out && lane == 0) a.lse_out[r] = M + logf(den);
-}
-
 __global__ __launch_bounds__(256) void fill_zero(uint32_t *p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }
@@ -268,16 +239,6 @@ hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStre
     else if (d == 128) hipLaunchKernelGGL((attn_combine<128, float, 8>), grid, block, 0, st, p);
     else if (d == 64 && dtype == 1) hipLaunchKernelGGL((attn_combine<64, uint16_t, 4>), grid, block, 0, st, p);
     else if (d == 64) hipLaunchKernelGGL((attn_combine<64, float, 4>), grid, block, 0, st, p);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
-}
-
-hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st) {
-    dim3 grid(blocks_for_waves(p.rows)), block(256);
-    if (d == 128 && dtype == 1) hipLaunchKernelGGL((merge_pairs<128, uint16_t>), grid, block, 0, st, p);
-    else if (d == 128) hipLaunchKernelGGL((merge_pairs<128, float>), grid, block, 0, st, p);
-    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((merge_pairs<64, uint16_t>), grid, block, 0, st, p);
-    else if (d == 64) hipLaunchKernelGGL((merge_pairs<64, float>), grid, block, 0, st, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -105,6 +105,17 @@ struct MergeParams {
     long rows;
 };
 
+// K-way merge: up to kMergeKMax document-side pairs and an optional local pair.
+constexpr int kMergeKMax = 8;
+struct MergeKParams {
+    const float *a[kMergeKMax], *A[kMergeKMax];
+    const float *lam, *A_loc;       // both null: no local pair
+    void *out;
+    float *lse_out;
+    long rows;
+    int K;
+};
+
 // Row tiling of the MFMA kernels: rows per wave = 16 * rt.
 int row_tiles_for(int Rp);
 
@@ -132,6 +143,7 @@ hipError_t launch_mlp_rows_lds32(const MlpParams &p, hipStream_t st);
 // Batched-prefill MLP (bf16, d = 128): one pass, no workspace.
 hipError_t launch_mlp_prefill(const MlpParams &p, hipStream_t st);
 hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st);
+hipError_t launch_merge_k(const MergeKParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 hipError_t launch_finish(const FinishParams &p, int dtype, int d, hipStream_t st);
 

@@ -11,6 +11,8 @@
 
 #include "kernels.hpp"
 
+static_assert(NECTAR_MERGE_K_MAX == nectar::kMergeKMax, "K-way merge limit");
+
 using namespace nectar;
 
 namespace {
@@ -66,7 +68,9 @@ inline float score_scale(const nectar_attn_desc *d) {
 // and outputs written element-wise need their natural alignment.
 inline bool tensor_ok(const void *p) { return p && aligned(p, 16); }
 inline bool f32_ok(const void *p) { return p && aligned(p, 4); }
-inline bool out_ok(const void *p, int dtype) { return p && aligned(p, dtype == NECTAR_BF16 ? 2 : 4); }
+// Arrays of d-vectors ([R][Hq][d] read-outs and outputs) are read and written
+// with vector accesses: 16-byte aligned like every tensor.
+inline bool rows_ok(const void *p) { return p && aligned(p, 16); }
 
 struct AttnPlan {
     int P = 0, Rp = 0, RT = 0, RG = 0, S = 0, chunk = kTile;
@@ -304,7 +308,7 @@ nectar_status nectar_doc_attn_exact(const nectar_attn_desc *desc, int64_t n, con
     if (n < 0) return NECTAR_EINVAL;
     if (n > 0x7fffffffL - kTile) return NECTAR_EUNSUPPORTED;
     if (desc->R == 0) return NECTAR_OK;
-    if (!tensor_ok(q) || !f32_ok(alpha_out) || !f32_ok(A_out)) return NECTAR_EINVAL;
+    if (!tensor_ok(q) || !f32_ok(alpha_out) || !rows_ok(A_out)) return NECTAR_EINVAL;
     if (n > 0 && (!tensor_ok(k) || !tensor_ok(v))) return NECTAR_EINVAL;
     const AttnPlan pl = plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)n);
     if ((s = check_ws(pl.ws, ws, ws_bytes)) != NECTAR_OK) return s;
@@ -384,7 +388,7 @@ nectar_status nectar_module_forward(const nectar_attn_desc *desc, const nectar_m
     if (s != NECTAR_OK) return s;
     if ((s = check_module(desc, m)) != NECTAR_OK) return s;
     if (desc->R == 0) return NECTAR_OK;
-    if (!tensor_ok(q) || !f32_ok(a_out) || !f32_ok(A_out)) return NECTAR_EINVAL;
+    if (!tensor_ok(q) || !f32_ok(a_out) || !rows_ok(A_out)) return NECTAR_EINVAL;
     hipStream_t st = (hipStream_t)stream;
     if (m->kind == NECTAR_MODULE_KVPAIR) {
         const AttnPlan pl = plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)m->p);
@@ -424,8 +428,8 @@ nectar_status nectar_local_attn_lse(const nectar_attn_desc *desc, const nectar_l
     const bool want_merge = out || out_lse;
     if (!lse_out && !A_out && !want_merge) return NECTAR_EINVAL;
     if (want_merge != (doc_lse || doc_A)) return NECTAR_EINVAL;
-    if (want_merge && (!f32_ok(doc_lse) || !f32_ok(doc_A))) return NECTAR_EINVAL;
-    if ((lse_out && !f32_ok(lse_out)) || (A_out && !f32_ok(A_out)) || (out && !out_ok(out, desc->dtype)) ||
+    if (want_merge && (!f32_ok(doc_lse) || !rows_ok(doc_A))) return NECTAR_EINVAL;
+    if ((lse_out && !f32_ok(lse_out)) || (A_out && !rows_ok(A_out)) || (out && !rows_ok(out)) ||
         (out_lse && !f32_ok(out_lse)))
         return NECTAR_EINVAL;
     if (desc->R == 0) return NECTAR_OK;
@@ -451,7 +455,7 @@ nectar_status nectar_merge(const nectar_attn_desc *desc, const float *a, const f
     nectar_status s = check_desc(desc);
     if (s != NECTAR_OK) return s;
     if (desc->R == 0) return NECTAR_OK;
-    if (!f32_ok(a) || !f32_ok(A) || !f32_ok(lam) || !f32_ok(A_loc) || !out_ok(out, desc->dtype))
+    if (!f32_ok(a) || !rows_ok(A) || !f32_ok(lam) || !rows_ok(A_loc) || !rows_ok(out))
         return NECTAR_EINVAL;
     if (lse_out && !f32_ok(lse_out)) return NECTAR_EINVAL;
     MergeParams p;
@@ -459,6 +463,32 @@ nectar_status nectar_merge(const nectar_attn_desc *desc, const float *a, const f
     p.rows = (long)desc->R * desc->Hq;
     hipStream_t st = (hipStream_t)stream;
     return finish(launch_merge(p, desc->dtype, desc->d, st), st);
+}
+
+nectar_status nectar_merge_k(const nectar_attn_desc *desc, int K, const float *const *a,
+                             const float *const *A, const float *lam, const float *A_loc, void *out,
+                             float *lse_out, void *stream) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if (K < 0 || K > NECTAR_MERGE_K_MAX) return NECTAR_EINVAL;
+    if ((lam == nullptr) != (A_loc == nullptr)) return NECTAR_EINVAL;
+    if (K == 0 && lam == nullptr) return NECTAR_EINVAL;
+    if (K > 0 && (a == nullptr || A == nullptr)) return NECTAR_EINVAL;
+    if (desc->R == 0) return NECTAR_OK;
+    MergeKParams p = {};
+    for (int k = 0; k < K; ++k) {
+        if (!f32_ok(a[k]) || !rows_ok(A[k])) return NECTAR_EINVAL;
+        p.a[k] = a[k];
+        p.A[k] = A[k];
+    }
+    if (lam && (!f32_ok(lam) || !rows_ok(A_loc))) return NECTAR_EINVAL;
+    if (!rows_ok(out)) return NECTAR_EINVAL;
+    if (lse_out && !f32_ok(lse_out)) return NECTAR_EINVAL;
+    p.lam = lam; p.A_loc = A_loc; p.out = out; p.lse_out = lse_out;
+    p.rows = (long)desc->R * desc->Hq;
+    p.K = K;
+    hipStream_t st = (hipStream_t)stream;
+    return finish(launch_merge_k(p, desc->dtype, desc->d, st), st);
 }
 
 // ---------------------------------------------------------------------------
@@ -684,7 +714,7 @@ nectar_status nectar_doc_attn_combine(const nectar_attn_desc *desc, int64_t n, c
     if (n < 0) return NECTAR_EINVAL;
     if (n > 0x7fffffffL - kTile) return NECTAR_EUNSUPPORTED;
     if (desc->R == 0) return NECTAR_OK;
-    if (!f32_ok(alpha_out) || !f32_ok(A_out)) return NECTAR_EINVAL;
+    if (!f32_ok(alpha_out) || !rows_ok(A_out)) return NECTAR_EINVAL;
     const AttnPlan pl = plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)n);
     const size_t need = attn_partial_bytes(desc, pl);
     if (bytes < need) return NECTAR_EWORKSPACE;
@@ -722,13 +752,12 @@ nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const n
     if (!exact && !nect && !outs->lam_out && !outs->Aloc_out) return NECTAR_EINVAL;
     if (n < 0) return NECTAR_EINVAL;
     if (n > 0x7fffffffL - kTile) return NECTAR_EUNSUPPORTED;
-    const float *f32s[] = {outs->lse_exact, outs->alpha_out, outs->A_out, outs->lse_nectar, outs->a_out,
-                           outs->Am_out, outs->lam_out, outs->Aloc_out};
+    const float *f32s[] = {outs->lse_exact, outs->alpha_out, outs->lse_nectar, outs->a_out, outs->lam_out};
     for (const float *f : f32s)
         if (f && !f32_ok(f)) return NECTAR_EINVAL;
-    if ((outs->out_exact && !out_ok(outs->out_exact, desc->dtype)) ||
-        (outs->out_nectar && !out_ok(outs->out_nectar, desc->dtype)))
-        return NECTAR_EINVAL;
+    const void *rows[] = {outs->A_out, outs->Am_out, outs->Aloc_out, outs->out_exact, outs->out_nectar};
+    for (const void *r : rows)
+        if (r && !rows_ok(r)) return NECTAR_EINVAL;
     if (desc->R == 0) return NECTAR_OK;
     if (!tensor_ok(q)) return NECTAR_EINVAL;
     if (loc->T_loc > 0 && (!tensor_ok(k_loc) || !tensor_ok(v_loc))) return NECTAR_EINVAL;

@@ -71,6 +71,7 @@ _lib.nectar_local_workspace_size.restype = ctypes.c_size_t
 _lib.nectar_local_attn_lse.argtypes = [_D, ctypes.POINTER(LocalDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, ctypes.c_size_t, _P]
 _lib.nectar_merge.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P]
+_lib.nectar_merge_k.argtypes = [_D, ctypes.c_int, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _P, _P, _P, _P]
 _lib.nectar_doc_attn_partials_size.argtypes = [_D, ctypes.c_int64]
 _lib.nectar_doc_attn_partials_size.restype = ctypes.c_size_t
 _lib.nectar_doc_attn_partials.argtypes = [_D, ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -86,7 +87,7 @@ _lib.nectar_abi_version.restype = ctypes.c_int
 _lib.nectar_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.nectar_workspace_init.restype = ctypes.c_int
 for _f in ("nectar_doc_attn_exact", "nectar_module_forward", "nectar_local_attn_lse", "nectar_merge",
-           "nectar_layer_step", "nectar_doc_attn_partials", "nectar_doc_attn_combine"):
+           "nectar_merge_k", "nectar_layer_step", "nectar_doc_attn_partials", "nectar_doc_attn_combine"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -303,6 +304,33 @@ def merge(a, A, lam, A_loc, *, Hkv, out_dtype, out=None, lse_out=None):
         lse_out = torch.empty((R, Hq), dtype=torch.float32, device=A.device)
     _check(_lib.nectar_merge(ctypes.byref(dsc), _ptr(a), _ptr(A), _ptr(lam), _ptr(A_loc), _ptr(out),
                              _ptr(lse_out), _stream()))
+    return out, lse_out
+
+
+MERGE_K_MAX = 8
+
+
+def merge_k(pairs, lam=None, A_loc=None, *, Hkv, out_dtype, out=None, lse_out=None):
+    """K-way log-sum-exp merge of the document-side pairs [(a_k, A_k)] with the
+    optional local pair (lam, A_loc); out in out_dtype (fp32/bf16)."""
+    ref = pairs[0][1] if pairs else A_loc
+    if ref is None:
+        raise ValueError("merge_k needs at least one pair")
+    R, Hq, d = ref.shape
+    code = F32 if out_dtype == torch.float32 else BF16
+    dsc = desc(R, Hq, Hkv, d, code)
+    for a, A in pairs:
+        if a.shape != (R, Hq) or A.shape != (R, Hq, d) or a.dtype != torch.float32 or A.dtype != torch.float32:
+            raise ValueError("merge_k: every pair is ([R][Hq], [R][Hq][d]) float32")
+    if out is None:
+        out = torch.empty((R, Hq, d), dtype=out_dtype, device=ref.device)
+    if lse_out is None:
+        lse_out = torch.empty((R, Hq), dtype=torch.float32, device=ref.device)
+    K = len(pairs)
+    pa = (_P * max(K, 1))(*[_ptr(a) for a, _ in pairs])
+    pA = (_P * max(K, 1))(*[_ptr(A) for _, A in pairs])
+    _check(_lib.nectar_merge_k(ctypes.byref(dsc), K, pa, pA, _ptr(lam), _ptr(A_loc), _ptr(out),
+                               _ptr(lse_out), _stream()))
     return out, lse_out
 
 

@@ -57,6 +57,7 @@ def lib():
     L.nectar_local_workspace_size.restype = ctypes.c_size_t
     L.nectar_local_attn_lse.argtypes = [D, ctypes.POINTER(Local)] + [P] * 9 + [P, ctypes.c_size_t, P]
     L.nectar_merge.argtypes = [D] + [P] * 7
+    L.nectar_merge_k.argtypes = [D, ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P)] + [P] * 5
     L.nectar_layer_step_workspace_size.argtypes = [D, ctypes.c_int64, ctypes.POINTER(Local),
                                                     ctypes.POINTER(Module), ctypes.c_int]
     L.nectar_layer_step_workspace_size.restype = ctypes.c_size_t
@@ -78,7 +79,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
     assert lib.nectar_abi_version() == 1
@@ -212,6 +213,27 @@ def test_merge_validation(lib):
     assert lib.nectar_merge(None, A16, A16, A16, A16, A16, None, None) == EINVAL
     d0 = Desc(0, 8, 2, 128, 1, 0.0, 0)
     assert lib.nectar_merge(ctypes.byref(d0), None, None, None, None, None, None, None) == OK
+
+
+def test_merge_k_validation(lib):
+    P = ctypes.c_void_p
+    d = Desc(2, 8, 2, 128, 1, 0.0, 0)
+    arr = lambda *v: (P * max(len(v), 1))(*v)
+    two = (arr(A16, A16), arr(A16, A16))
+    call = lambda K, pa, pA, lam, Al, out=A16, dd=d: lib.nectar_merge_k(
+        ctypes.byref(dd) if dd is not None else None, K, pa, pA, lam, Al, out, None, None)
+    assert call(2, *two, A16, A16, dd=None) == EINVAL
+    assert call(-1, *two, A16, A16) == EINVAL
+    assert call(9, arr(*[A16] * 9), arr(*[A16] * 9), A16, A16) == EINVAL     # above the maximum of 8
+    assert call(2, *two, A16, None) == EINVAL                                 # lam without A_loc
+    assert call(2, *two, None, A16) == EINVAL
+    assert call(0, None, None, None, None) == EINVAL                          # no pair at all
+    assert call(2, None, None, A16, A16) == EINVAL
+    assert call(2, arr(A16, A16 + 2), arr(A16, A16), A16, A16) == EINVAL     # misaligned logit
+    assert call(2, *two, A16, A16, out=A16 + 1) == EINVAL
+    assert call(2, *two, A16, A16, out=None) == EINVAL
+    d0 = Desc(0, 8, 2, 128, 1, 0.0, 0)
+    assert call(2, *two, None, None, out=None, dd=d0) == OK                  # no rows: a no-op
 
 
 def test_oracle_and_product_share_no_code():

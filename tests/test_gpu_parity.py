@@ -256,6 +256,62 @@ def test_merge_kernel(nx, out_dtype):
     assert np.all(host(out)[1, 2] == 0.0) and host(lse)[1, 2] == -np.inf
 
 
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("K,local", [(1, True), (3, True), (8, True), (5, False), (0, True)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_merge_k_kernel(nx, d, K, local, out_dtype):
+    import torch
+    print("case merge_k d=%d K=%d local=%s %s" % (d, K, local, out_dtype), flush=True)
+    R, Hq, Hkv = 9, 8, 2
+    g = _rng(12, d, K, int(local))
+    pairs = []
+    for k in range(K):
+        a = (g.standard_normal((R, Hq)) * 3).astype(np.float32)
+        a[0, k % Hq] = -np.inf                       # a pair that drops out of one row
+        a[3, :] = 60.0 + k                           # large logits
+        pairs.append((a, g.standard_normal((R, Hq, d)).astype(np.float32)))
+    lam = (g.standard_normal((R, Hq)) * 3).astype(np.float32) if local else None
+    Al = g.standard_normal((R, Hq, d)).astype(np.float32) if local else None
+    for a, _ in pairs:                               # row 1, head 2: every logit -inf
+        a[1, 2] = -np.inf
+    if local:
+        lam[1, 2] = -np.inf
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    out, lse = nx.merge_k([(dev(a), dev(A)) for a, A in pairs], dev(lam) if local else None,
+                          dev(Al) if local else None, Hkv=Hkv, out_dtype=tdt)
+    eo, el = oracle.merge_k(pairs, lam, Al)
+    check("merge_k out", host(out), eo, 1e-5 if out_dtype == "f32" else 1e-2)
+    check("merge_k lse", host(lse), el, 1e-5)
+    assert np.all(host(out)[1, 2] == 0.0) and host(lse)[1, 2] == -np.inf
+
+
+@pytest.mark.parametrize("cuts", [(0, 1000, 2300, 2301, 4000), (0, 4000), (0, 300, 300, 2000, 3333, 3334, 3900,
+                                                                           4000)])
+def test_merge_k_of_document_chunks_is_full_attention(nx, cuts):
+    """A document cut into key ranges: each range's exact pair on the GPU, the
+    local pair on the GPU, their K-way merge against full attention in the oracle."""
+    import torch
+    print("case merge_k chunks %s" % (cuts,), flush=True)
+    B, Tq, Hq, Hkv, d, T_loc, T_cap, qoff = 2, 3, 16, 4, 128, 50, 64, 47
+    R = B * Tq
+    n = cuts[-1]
+    g = _rng(13, len(cuts))
+    q = _bf(g.standard_normal((R, Hq, d)))
+    K, V = (_bf(g.standard_normal((Hkv, n, d))) for _ in range(2))
+    Kl, Vl = (_bf(g.standard_normal((B, Hkv, T_cap, d))) for _ in range(2))
+    qd, Kd, Vd = dev(q), dev(K), dev(V)
+    pairs = []
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        pairs.append(nx.doc_attn_exact(qd, Kd[:, lo:hi].contiguous(), Vd[:, lo:hi].contiguous(), Hkv))
+    lam, Al = nx.local_attn_lse(qd, dev(Kl), dev(Vl), Hkv, B=B, Tq=Tq, T_loc=T_loc, q_offset=qoff)
+    out, lse = nx.merge_k(pairs, lam, Al, Hkv=Hkv, out_dtype=torch.bfloat16)
+    flse, fout = oracle.full_attn(q, K, V, np.ascontiguousarray(Kl[:, :, :T_loc]),
+                                  np.ascontiguousarray(Vl[:, :, :T_loc]), dt="bf16", B=B, Tq=Tq, Hq=Hq,
+                                  Hkv=Hkv, Tloc=T_loc, q_offset=qoff)
+    check("chunked merge out", host(out), fout, ATOL_OUT_BF16)
+    check("chunked merge lse", host(lse), flse, 1e-3)
+
+
 def test_worked_example_on_gpu(nx):
     """The printed merge example of section 2.2 through the GPU merge kernel."""
     import math

@@ -49,6 +49,7 @@ def _L():
         lib.oracle_local_attn.argtypes = [I, I, I, I, I, I, I, I, D, P, P, P, P, I, P, P, I]
         lib.oracle_full_attn.argtypes = [I, I, I, I, I, I, L, I, I, D, P, P, P, P, P, P, I, P, P, I]
         lib.oracle_mlp.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
+        lib.oracle_deep_mlp.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
         lib.oracle_merge.argtypes = [L, I, P, P, P, P, P, P]
         lib.oracle_merge.restype = None
         lib.oracle_merge_k.argtypes = [L, I, I, P, P, P, P, P, P]
@@ -171,6 +172,55 @@ def mlp(q, W1, b1, W2t, b2, Ws, bs, ws2, bs2, *, dt, Hq, Hkv, act="gelu", toks=N
                          _p(Ws), _p(bs), _p(ws2), _p(bs2), _p(q), _p(t), nt, _p(a), _p(A), threads)
     if rc:
         raise ValueError("oracle_mlp failed (%d)" % rc)
+    return a, A
+
+
+def deep_mlp(q, P, *, dt, Hq, Hkv, act="silu", toks=None, threads=0):
+    """Deep MLP module with input re-injection (Eq. (3.6)) and an optional shared
+    backbone.  P holds "depth" (D_b, D_s, D_t), "width" (H_b, H_s, H_t), "layers"
+    (a list of (Wq, Wh or None, b) in the order backbone, score, target) and the
+    read-outs "ws_out", "bs_out", "Wt_out", "bt_out".
+    Returns (a [ntok][Hq], A [ntok][Hq][d]) in float64."""
+    q = _arr(q, dt)
+    d = q.shape[-1]
+    R = q.size // (Hq * d)
+    depth = np.ascontiguousarray(P["depth"], dtype=np.int32)
+    width = np.ascontiguousarray(P["width"], dtype=np.int32)
+    layers = P["layers"]
+    if len(layers) != int(depth.sum()):
+        raise ValueError("deep_mlp: %d layers for depths %s" % (len(layers), tuple(depth)))
+    Db, Ds, Dt = (int(x) for x in depth)
+    Hb, Hs, Ht = (int(x) for x in width)
+    keep = []
+    Wq_p, Wh_p, b_p = [], [], []
+    for l, (Wq, Wh, b) in enumerate(layers):
+        Wq = _arr(Wq, dt); b = _f64(b)
+        Wh = _arr(Wh, dt) if Wh is not None else None
+        part = 0 if l < Db else (1 if l < Db + Ds else 2)
+        first = (0, Db, Db + Ds)[part]
+        H = (Hb, Hs, Ht)[part]
+        H_in = H if l > first else (Hb if part > 0 and Db > 0 else 0)
+        if Wq.size != Hkv * H * d or b.size != Hkv * H or (Wh is None) != (H_in == 0) or \
+                (Wh is not None and Wh.size != Hkv * H * H_in):
+            raise ValueError("deep_mlp: layer %d has inconsistent shapes" % l)
+        keep += [Wq, Wh, b]
+        Wq_p.append(Wq.ctypes.data); Wh_p.append(Wh.ctypes.data if Wh is not None else None)
+        b_p.append(b.ctypes.data)
+    nl = max(len(layers), 1)
+    arrs = [(ctypes.c_void_p * nl)(*v) for v in (Wq_p, Wh_p, b_p)]
+    ws_out, Wt_out = _arr(P["ws_out"], dt), _arr(P["Wt_out"], dt)
+    bs_out, bt_out = _f64(P["bs_out"]), _f64(P["bt_out"])
+    Hs_last, Ht_last = (Hs if Ds else Hb), (Ht if Dt else Hb)
+    if ws_out.size != Hkv * Hs_last or Wt_out.size != Hkv * d * Ht_last or bs_out.size != Hkv or \
+            bt_out.size != Hkv * d:
+        raise ValueError("deep_mlp: inconsistent read-out shapes")
+    t, nt = _toks(toks, R)
+    a = np.empty((nt, Hq)); A = np.empty((nt, Hq, d))
+    rc = _L().oracle_deep_mlp(DT[dt], R, Hq, Hkv, d, ACT[act], _p(depth), _p(width), arrs[0], arrs[1],
+                              arrs[2], _p(ws_out), _p(bs_out), _p(Wt_out), _p(bt_out), _p(q), _p(t), nt,
+                              _p(a), _p(A), threads)
+    if rc:
+        raise ValueError("oracle_deep_mlp failed (%d)" % rc)
     return a, A
 
 

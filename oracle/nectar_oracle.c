@@ -21,7 +21,11 @@
  *   - section 2.4, Eq. (3.6): MLP form.  The workloads fix one hidden layer
  *     with GELU: A = W2 GELU(W1 q + b1) + b2, a = w2 . GELU(Ws q + bs) + bs2.
  *     SiLU is provided as the activation Eq. (3.6) itself names, and the tanh
- *     form of GELU as the common faster variant.
+ *     form of GELU as the common faster variant.  The deep form of Eq. (3.6)
+ *     (the query re-injected into every layer, optional shared backbone) is
+ *     oracle_deep_mlp.
+ *   - closing section: several context modules composed by one more softmax
+ *     grouping over their pairs (oracle_merge_k).
  *
  * Precision: every input element is widened exactly to double (bf16 bits are
  * shifted into an fp32 pattern; fp32 widens exactly); every sum is a plain
@@ -300,6 +304,110 @@ int oracle_mlp(int dt, int R, int Hq, int Hkv, int d, int Ht, int Hs, int act,
             a += ld(ws2, dt, (size_t)h * Hs + j) * act_fn(act, z + bs[(size_t)h * Hs + j]);
         }
         a_out[(size_t)i * Hq + hq] = a;
+    }
+    return 0;
+}
+
+/*
+ * Deep MLP module with input re-injection, Eq. (3.6) of section 2.4: the first
+ * layer of a network reads only the query, h_0 = act(U_0 q + b_0); every later
+ * layer reads the query again beside the previous layer's state,
+ * h_{k+1} = act(V_k q + U_k h_k + b_k).  Reading of the depth triple
+ * (D_b, D_s, D_t): an optional shared backbone of D_b such layers (width H_b)
+ * is followed by a score head of D_s layers (width H_s) and a target head of
+ * D_t layers (width H_t); a head's first layer reads the backbone's last state
+ * when there is a backbone (so it too has the re-injection form), else only the
+ * query.  Each head ends in a linear read-out of its last state (the
+ * backbone's when the head has no layer of its own):
+ *   a = ws_out . h_s + bs_out,      A_c = sum_j Wt_out[c][j] h_t,j + bt_out[c].
+ *
+ * Layers are listed backbone first, then score, then target.  Layer l has
+ *   Wq[l] [Hkv][H_l][d]        query weights (U_0 or V_k),
+ *   Wh[l] [Hkv][H_l][H_in]     state weights (U_k; NULL for a layer that reads
+ *                              only the query),
+ *   b[l]  [Hkv][H_l]           bias;
+ * ws_out [Hkv][H_s_last], bs_out [Hkv], Wt_out [Hkv][d][H_t_last], bt_out [Hkv][d].
+ * Every sum is plain fp64 in index order; hidden states are kept in fp64.
+ */
+#define OR_DEEP_MAX_LAYERS 64
+int oracle_deep_mlp(int dt, int R, int Hq, int Hkv, int d, int act,
+                    const int32_t *depth, const int32_t *width,
+                    const void *const *Wq, const void *const *Wh, const double *const *b,
+                    const void *ws_out, const double *bs_out, const void *Wt_out, const double *bt_out,
+                    const void *q, const int32_t *toks, int ntok,
+                    double *a_out, double *A_out, int nthreads)
+{
+    if (!valid_dt(dt) || !shape_ok(R, Hq, Hkv, d)) return 1;
+    if (act != OR_GELU && act != OR_SILU && act != OR_GELU_TANH) return 1;
+    for (int part = 0; part < 3; ++part)
+        if (depth[part] < 0 || (depth[part] > 0 && width[part] <= 0)) return 1;
+    const int Db = depth[0], Ds = depth[1], Dt = depth[2];
+    if (Db + Ds + Dt > OR_DEEP_MAX_LAYERS || Db + Ds < 1 || Db + Dt < 1) return 1;
+    /* width of the state each layer reads (0: the query only) */
+    int in_w[OR_DEEP_MAX_LAYERS], out_w[OR_DEEP_MAX_LAYERS];
+    int Hmax = 1;
+    for (int l = 0; l < Db + Ds + Dt; ++l) {
+        int part = l < Db ? 0 : (l < Db + Ds ? 1 : 2);
+        int first = part == 0 ? 0 : (part == 1 ? Db : Db + Ds);
+        out_w[l] = width[part];
+        in_w[l] = l > first ? width[part] : (part > 0 && Db > 0 ? width[0] : 0);
+        if ((in_w[l] > 0) != (Wh[l] != NULL) || !Wq[l] || !b[l]) return 1;
+        if (out_w[l] > Hmax) Hmax = out_w[l];
+    }
+    const int Hs_last = Ds > 0 ? width[1] : width[0];
+    const int Ht_last = Dt > 0 ? width[2] : width[0];
+    if (!toks) ntok = R;
+    const int G = Hq / Hkv;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *bb = (double *)calloc((size_t)Hmax, sizeof(double));
+        double *s0 = (double *)calloc((size_t)Hmax, sizeof(double));
+        double *s1 = (double *)calloc((size_t)Hmax, sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (long row = 0; row < (long)ntok * Hq; ++row) {
+            int i = (int)(row / Hq), hq = (int)(row % Hq);
+            int r = toks ? toks[i] : i;
+            int h = hq / G;
+            size_t qo = ((size_t)r * Hq + hq) * d;
+            /* run layers [l0, l1) starting from state `init` (width in_w[l0]); result in *res */
+            double *cur = s0, *nxt = s1;
+            for (int part = 0; part < 3; ++part) {
+                int l0 = part == 0 ? 0 : (part == 1 ? Db : Db + Ds);
+                int l1 = l0 + depth[part];
+                const double *state = part > 0 && Db > 0 ? bb : NULL;
+                for (int l = l0; l < l1; ++l) {
+                    for (int j = 0; j < out_w[l]; ++j) {
+                        size_t wo = ((size_t)h * out_w[l] + j) * d;
+                        double z = b[l][(size_t)h * out_w[l] + j];
+                        for (int c = 0; c < d; ++c) z += ld(Wq[l], dt, wo + c) * ld(q, dt, qo + c);
+                        if (in_w[l] > 0) {
+                            size_t ho = ((size_t)h * out_w[l] + j) * in_w[l];
+                            for (int k = 0; k < in_w[l]; ++k) z += ld(Wh[l], dt, ho + k) * state[k];
+                        }
+                        nxt[j] = act_fn(act, z);
+                    }
+                    double *t = cur; cur = nxt; nxt = t;
+                    state = cur;
+                }
+                if (part == 0) {
+                    for (int j = 0; j < width[0] && Db > 0; ++j) bb[j] = cur[j];
+                } else if (part == 1) {
+                    double a = bs_out[h];
+                    for (int j = 0; j < Hs_last; ++j) a += ld(ws_out, dt, (size_t)h * Hs_last + j) * state[j];
+                    a_out[(size_t)i * Hq + hq] = a;
+                } else {
+                    double *A = &A_out[((size_t)i * Hq + hq) * d];
+                    for (int c = 0; c < d; ++c) {
+                        double v = bt_out[(size_t)h * d + c];
+                        size_t wo = ((size_t)h * d + c) * Ht_last;
+                        for (int j = 0; j < Ht_last; ++j) v += ld(Wt_out, dt, wo + j) * state[j];
+                        A[c] = v;
+                    }
+                }
+            }
+        }
+        free(bb); free(s0); free(s1);
     }
     return 0;
 }

@@ -479,3 +479,150 @@ def test_batched_gelu_approximation_against_the_oracle():
         approx = x / (1.0 + 2.0 ** min(p * x, 1000.0))
         worst = max(worst, abs(approx - oracle.gelu(x)))
     assert worst < 1e-5, worst
+
+
+# --- Deep MLP with input re-injection, Eq. (3.6) ---------------------------------
+
+def _deep_params(Hkv, d, depth, width, bias=0.3, zero_state=False):
+    """Random fp64 parameters of a deep module (layers backbone, score, target)."""
+    Db, Ds, Dt = depth
+    Hb, Hs, Ht = width
+    layers = []
+    for part, D, H in ((0, Db, Hb), (1, Ds, Hs), (2, Dt, Ht)):
+        for l in range(D):
+            H_in = H if l > 0 else (Hb if part > 0 and Db > 0 else 0)
+            Wq = _rand(Hkv, H, d, scale=d ** -0.5)
+            Wh = None if H_in == 0 else (np.zeros((Hkv, H, H_in)) if zero_state
+                                         else _rand(Hkv, H, H_in, scale=H_in ** -0.5))
+            layers.append((Wq, Wh, _rand(Hkv, H, scale=bias)))
+    Hs_last = Hs if Ds else Hb
+    Ht_last = Ht if Dt else Hb
+    return dict(depth=depth, width=width, layers=layers, ws_out=_rand(Hkv, Hs_last, scale=Hs_last ** -0.5),
+                bs_out=_rand(Hkv, scale=bias), Wt_out=_rand(Hkv, d, Ht_last, scale=Ht_last ** -0.5),
+                bt_out=_rand(Hkv, d, scale=bias))
+
+
+def _deep(q, P, Hq, Hkv, act="silu"):
+    return oracle.deep_mlp(q, P, dt="f64", Hq=Hq, Hkv=Hkv, act=act)
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu"])
+def test_deep_mlp_depth_one_is_the_one_hidden_layer_module(act):
+    """Depths (0, 1, 1): one query-only layer per head is the one-hidden-layer
+    module (pinned by P10); the target read-out [d][H] is W2t transposed."""
+    Hq, Hkv, d, Hs, Ht = 6, 2, 8, 5, 7
+    P = _deep_params(Hkv, d, (0, 1, 1), (0, Hs, Ht))
+    q = _rand(4, Hq, d)
+    a, A = _deep(q, P, Hq, Hkv, act)
+    (Ws, _, bs), (W1, _, b1) = P["layers"]
+    e, E = oracle.mlp(q, W1, b1, np.ascontiguousarray(P["Wt_out"].transpose(0, 2, 1)), P["bt_out"], Ws, bs,
+                      P["ws_out"], P["bs_out"], dt="f64", Hq=Hq, Hkv=Hkv, act=act)
+    assert np.max(np.abs(a - e)) < 1e-13 and np.max(np.abs(A - E)) < 1e-13
+
+
+def test_deep_mlp_zero_state_weights_leave_the_last_layer():
+    """With every U_k = 0, h_{k+1} = act(V_k q + b_k): only each head's last layer
+    reaches the read-out, so the module equals the one-hidden-layer module built
+    from those layers."""
+    Hq, Hkv, d = 4, 2, 8
+    P = _deep_params(Hkv, d, (0, 2, 3), (0, 6, 5), zero_state=True)
+    q = _rand(3, Hq, d)
+    a, A = _deep(q, P, Hq, Hkv)
+    Ws, _, bs = P["layers"][1]
+    W1, _, b1 = P["layers"][4]
+    e, E = oracle.mlp(q, W1, b1, np.ascontiguousarray(P["Wt_out"].transpose(0, 2, 1)), P["bt_out"], Ws, bs,
+                      P["ws_out"], P["bs_out"], dt="f64", Hq=Hq, Hkv=Hkv, act="silu")
+    assert np.max(np.abs(a - e)) < 1e-13 and np.max(np.abs(A - E)) < 1e-13
+
+
+def test_deep_mlp_hidden_unit_permutation_invariance():
+    """Relabelling the hidden units of every layer (rows of that layer, columns of
+    the next) leaves the function unchanged; a transposed U_k or a state read from
+    the wrong layer breaks it."""
+    Hq, Hkv, d, H = 2, 1, 6, 5
+    for depth in ((0, 2, 3), (2, 1, 2), (1, 0, 2)):
+        width = (H if depth[0] else 0, H, H)
+        P = _deep_params(Hkv, d, depth, width)
+        q = _rand(3, Hq, d)
+        a, A = _deep(q, P, Hq, Hkv)
+        perms = [rng.permutation(H) for _ in P["layers"]]
+        Db, Ds, Dt = depth
+        newl = []
+        for l, (Wq, Wh, b) in enumerate(P["layers"]):
+            pi = perms[l]
+            part_first = 0 if l < Db else (Db if l < Db + Ds else Db + Ds)
+            prev = l - 1 if l > part_first else (Db - 1 if part_first > 0 and Db > 0 else None)
+            Wq2, b2 = Wq[:, pi], b[:, pi]
+            Wh2 = None if Wh is None else Wh[:, pi][:, :, perms[prev]]
+            newl.append((Wq2, Wh2, b2))
+        last_s = Db + Ds - 1
+        last_t = Db + Ds + Dt - 1 if Dt else Db - 1
+        P2 = dict(P, layers=newl, ws_out=P["ws_out"][:, perms[last_s]], Wt_out=P["Wt_out"][:, :, perms[last_t]])
+        a2, A2 = _deep(q, P2, Hq, Hkv)
+        assert np.max(np.abs(a2 - a)) < 1e-13 and np.max(np.abs(A2 - A)) < 1e-13, depth
+
+
+def test_deep_mlp_shared_backbone_equals_copied_backbone():
+    """A shared backbone layer is the same as giving each head its own copy of it:
+    (1, 1, 1) equals (0, 2, 2) with the backbone layer first in both heads."""
+    Hq, Hkv, d, Hb, Hs, Ht = 4, 2, 6, 5, 3, 4
+    P = _deep_params(Hkv, d, (1, 1, 1), (Hb, Hs, Ht))
+    q = _rand(3, Hq, d)
+    a, A = _deep(q, P, Hq, Hkv)
+    bb, sl, tl = P["layers"]
+    # as (0, 2, 2): every head's layers have one width, so pad the narrower layer
+    # with units whose outgoing weights are zero
+    H = max(Hb, Hs, Ht)
+
+    def pad_rows(Wq, Wh, b, H_in_new):
+        Hl = Wq.shape[1]
+        Wq2 = np.zeros((Hkv, H, d)); Wq2[:, :Hl] = Wq
+        b2 = np.zeros((Hkv, H)); b2[:, :Hl] = b
+        Wh2 = None
+        if Wh is not None:
+            Wh2 = np.zeros((Hkv, H, H_in_new)); Wh2[:, :Hl, :Wh.shape[2]] = Wh
+        return Wq2, Wh2, b2
+
+    layers = [pad_rows(*bb, 0), pad_rows(*sl, H), pad_rows(*bb, 0), pad_rows(*tl, H)]
+    ws = np.zeros((Hkv, H)); ws[:, :Hs] = P["ws_out"]
+    Wt = np.zeros((Hkv, d, H)); Wt[:, :, :Ht] = P["Wt_out"]
+    P2 = dict(depth=(0, 2, 2), width=(0, H, H), layers=layers, ws_out=ws, bs_out=P["bs_out"], Wt_out=Wt,
+              bt_out=P["bt_out"])
+    a2, A2 = _deep(q, P2, Hq, Hkv)
+    assert np.max(np.abs(a2 - a)) < 1e-13 and np.max(np.abs(A2 - A)) < 1e-13
+
+
+def test_deep_mlp_hand_worked_chain():
+    """d = 2, one head, depths (0, 2, 1), one unit per layer: z_0 = ln 3 gives
+    SiLU(z_0) = (3/4) ln 3; the second layer re-injects q (weight 1 on q_0 = 1)
+    and adds 2 * h_0, so z_1 = 1 + (3/2) ln 3; a = 10 * SiLU(z_1) - 1."""
+    L3 = math.log(3.0)
+    q = np.array([[[1.0, 0.0]]])
+    layers = [(np.array([[[L3, 5.0]]]), None, np.zeros((1, 1))),            # score layer 0
+              (np.array([[[1.0, 7.0]]]), np.array([[[2.0]]]), np.zeros((1, 1))),   # score layer 1
+              (np.array([[[0.0, 0.0]]]), None, np.array([[-1.0]]))]         # target layer 0: z = -1
+    P = dict(depth=(0, 2, 1), width=(0, 1, 1), layers=layers, ws_out=np.array([[10.0]]),
+             bs_out=np.array([-1.0]), Wt_out=np.array([[[1.0], [-2.0]]]), bt_out=np.array([[0.5, 0.0]]))
+    a, A = _deep(q, P, 1, 1)
+    z1 = 1.0 + 2.0 * 0.75 * L3
+    silu_z1 = z1 / (1.0 + math.exp(-z1))
+    assert abs(a[0, 0] - (10.0 * silu_z1 - 1.0)) < 1e-14
+    s_m1 = -1.0 / (1.0 + math.e)                      # SiLU(-1)
+    assert abs(A[0, 0, 0] - (s_m1 + 0.5)) < 1e-15 and abs(A[0, 0, 1] - (-2.0 * s_m1)) < 1e-15
+
+
+def test_deep_mlp_gqa_and_token_subset():
+    Hq, Hkv, d = 6, 2, 4
+    P = _deep_params(Hkv, d, (2, 1, 2), (5, 3, 4))
+    q = _rand(5, Hq, d)
+    a, A = _deep(q, P, Hq, Hkv)
+    # query heads 0..2 use KV head 0: the same query in head 1 and head 2 gives the same pair
+    q2 = q.copy(); q2[:, 2] = q2[:, 1]
+    a2, A2 = _deep(q2, P, Hq, Hkv)
+    assert np.all(a2[:, 1] == a2[:, 2]) and np.all(A2[:, 1] == A2[:, 2])
+    # ... but not across groups (head 3 belongs to KV head 1)
+    q3 = q.copy(); q3[:, 3] = q3[:, 1]
+    a3, _ = _deep(q3, P, Hq, Hkv)
+    assert np.max(np.abs(a3[:, 3] - a3[:, 1])) > 1e-6
+    at, At = oracle.deep_mlp(q, P, dt="f64", Hq=Hq, Hkv=Hkv, toks=[4, 1])
+    assert np.all(at[0] == a[4]) and np.all(At[1] == A[1])

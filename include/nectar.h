@@ -12,7 +12,8 @@
  *   nectar_doc_attn_exact   exact (alpha, A) over the document cache, Eq. (3.1)
  *   nectar_doc_attn_partials / nectar_doc_attn_combine   the same as two passes
  *   nectar_module_forward   (a, A) from the MLP form (Eq. (3.6), one hidden
- *                           layer) or the Quadrature KV-pair form (section 2.4)
+ *                           layer, or the deep re-injection form) or the
+ *                           Quadrature KV-pair form (section 2.4)
  *   nectar_local_attn_lse   causal local attention (log Z_local, A_local),
  *                           section 2.2, optionally merged with a document pair
  *   nectar_merge            the log-sum-exp merge of Eqs. (3.4)-(3.5)
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define NECTAR_ABI_VERSION 1
+#define NECTAR_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define NECTAR_API __attribute__((visibility("default")))
@@ -105,7 +106,7 @@ typedef struct {
                           Prefill of the whole local chunk: Tq = T_loc, 0. */
 } nectar_local_desc;
 
-typedef enum { NECTAR_MODULE_MLP = 0, NECTAR_MODULE_KVPAIR = 1 } nectar_module_kind;
+typedef enum { NECTAR_MODULE_MLP = 0, NECTAR_MODULE_KVPAIR = 1, NECTAR_MODULE_DEEP_MLP = 2 } nectar_module_kind;
 typedef enum { NECTAR_ACT_GELU = 0, NECTAR_ACT_SILU = 1, NECTAR_ACT_GELU_TANH = 2 } nectar_act;
 
 /*
@@ -124,7 +125,9 @@ typedef enum { NECTAR_ACT_GELU = 0, NECTAR_ACT_SILU = 1, NECTAR_ACT_GELU_TANH = 
  * KVPAIR (Quadrature): exact attention over p learnable pairs,
  *   a(q) = log sum_j exp(scale * W[h][j] . q),  A(q) = softmax(scale * W q)^T Z,
  *   W, Z [Hkv][p][d] (dtype), p >= 0 (p == 0 gives a = -inf, A = 0).
+ * DEEP_MLP: the deep form of Eq. (3.6), described by *deep (below).
  */
+typedef struct nectar_deep_mlp nectar_deep_mlp;
 typedef struct {
     int32_t kind;      /* nectar_module_kind */
     int32_t act;       /* nectar_act (MLP only) */
@@ -135,7 +138,46 @@ typedef struct {
     const void *ws2; const float *bs2;
     int64_t p;         /* KVPAIR pair count */
     const void *W;   const void *Z;
+    const nectar_deep_mlp *deep;   /* DEEP_MLP only */
 } nectar_module;
+
+/*
+ * Deep MLP module with input re-injection, Eq. (3.6) (section 2.4): a network's
+ * first layer reads the query, h_0 = act(U_0 q + b_0); each later layer reads
+ * the query again beside the previous state, h_{k+1} = act(V_k q + U_k h_k + b_k).
+ * The depth triple (D_b, D_s, D_t) of the notes: an optional shared backbone of
+ * D_b layers of width H_b, then a score head of D_s layers (width H_s) and a
+ * target head of D_t layers (width H_t).  A head's first layer reads the
+ * backbone's last state when D_b > 0 (so it has the re-injection form) and only
+ * the query otherwise.  Each head ends in a linear read-out of its last state
+ * (the backbone's when the head has no layer):
+ *   a = ws_out[h] . h_s + bs_out[h],   A[c] = Wt_out[h][c] . h_t + bt_out[h][c].
+ * Layers are listed backbone first, then score, then target (l < D_b + D_s + D_t):
+ *   Wq[l] [Hkv][H_l][d]     query weights (U_0, or V_k)            (dtype)
+ *   Wh[l] [Hkv][H_l][H_in]  state weights U_k; NULL exactly when the layer
+ *                           reads only the query                   (dtype)
+ *   b[l]  [Hkv][H_l]        bias                                   (fp32)
+ *   ws_out [Hkv][H_s last], Wt_out [Hkv][d][H_t last] (dtype); bs_out [Hkv],
+ *   bt_out [Hkv][d] (fp32).
+ * Constraints: D_b + D_s >= 1, D_b + D_t >= 1, D_b + D_s + D_t <=
+ * NECTAR_DEEP_MAX_LAYERS; the width of every part with layers is a positive
+ * multiple of 32 (NECTAR_EUNSUPPORTED otherwise).  On the bf16 path hidden
+ * states are stored in bf16 (round to nearest even) between layers, as the
+ * one-hidden-layer kernels round their hidden layer before the second product.
+ * The workspace (nectar_module_workspace_size) holds the hidden states:
+ * 2 * (H_b + H_s + H_t) * Hkv * R * (Hq / Hkv) elements of the storage type.
+ */
+#define NECTAR_DEEP_MAX_LAYERS 16
+struct nectar_deep_mlp {
+    int32_t depth[3];  /* D_b, D_s, D_t */
+    int32_t width[3];  /* H_b, H_s, H_t (ignored for a part with no layer) */
+    int32_t act;       /* nectar_act; NECTAR_ACT_SILU is the one Eq. (3.6) names */
+    const void *Wq[NECTAR_DEEP_MAX_LAYERS];
+    const void *Wh[NECTAR_DEEP_MAX_LAYERS];
+    const float *b[NECTAR_DEEP_MAX_LAYERS];
+    const void *ws_out; const float *bs_out;
+    const void *Wt_out; const float *bt_out;
+};
 
 /*
  * Exact document attention, Eq. (3.1) with GQA sharing (section 2.1):

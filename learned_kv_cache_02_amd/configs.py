@@ -29,6 +29,32 @@ class MLPShape:
 
 
 @dataclass(frozen=True)
+class DeepShape:
+    """Deep module of Eq. (3.6): depths (D_b, D_s, D_t) of the shared backbone,
+    score head and target head, and their widths (H_b, H_s, H_t)."""
+    depth: Tuple[int, int, int]
+    width: Tuple[int, int, int]
+
+    def layers(self):
+        """(width, input-state width) of every layer, backbone, score, target."""
+        Db, Ds, Dt = self.depth
+        out = []
+        for part, D in enumerate(self.depth):
+            H = self.width[part]
+            for l in range(D):
+                out.append((H, H if l > 0 else (self.width[0] if part > 0 and Db > 0 else 0)))
+        return out
+
+    def last_width(self, head: int) -> int:
+        return self.width[head] if self.depth[head] > 0 else self.width[0]
+
+    def params(self, d: int) -> int:
+        """Parameters per KV head including all biases."""
+        n = sum(H * d + H * H_in + H for H, H_in in self.layers())
+        return n + (self.last_width(1) + 1) + (d * self.last_width(2) + d)
+
+
+@dataclass(frozen=True)
 class Config:
     name: str
     seed: int
@@ -106,3 +132,8 @@ C5 = Config("c5_qwen25_7b_1m_decode", 4, "bf16", 28, 4, 28, 128, 1048576, 1e7, 8
 
 CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5)}
 BY_INDEX = [C1, C2, C3, C4, C5]
+
+# Deep modules of Eq. (3.6) in the two depth shapes the notes plot, (0, 2, 3) and
+# (2, 1, 2), sized to about the capacity of the Qwen3-4B-shaped layer's
+# one-hidden-layer module (rho ~ 10 %).
+DEEP_C2 = (DeepShape((0, 2, 3), (0, 576, 576)), DeepShape((2, 1, 2), (544, 544, 544)))

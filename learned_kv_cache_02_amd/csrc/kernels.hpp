@@ -63,6 +63,30 @@ struct MlpParams {
     int defer;              // write partials even when SB == 1 (a later pass finishes)
 };
 
+// One layer of the deep MLP module (Eq. (3.6)) for every KV head p and row rho
+// of its Rp = R * G query rows:
+//   Y[p][rho][n] = act(Wq[p][n] . q_row(p, rho) + Wh[p][n] . X[p][rho] + b[p][n]).
+// Wq == nullptr: the layer reads only the state (the linear read-outs);
+// Wh == nullptr: it reads only the query.  The result goes to the hidden-state
+// buffer Y ([Hkv][Rp][N], storage type) or, for a read-out, to the fp32 output
+// rows Yf[out_row * N + n].
+struct DeepLayer {
+    const void *Wq, *Wh, *X;
+    const float *b;
+    void *Y;
+    float *Yf;
+    int N, Kh, act;          // act < 0: none
+    long blocks;             // blocks of this layer in its launch
+};
+
+// One launch: one or two independent layers (the score and target heads run
+// side by side).
+struct DeepParams {
+    const void *q;
+    int Hq, G, Hkv, Rp, nl;
+    DeepLayer L0, L1;
+};
+
 // One document-side part of a layer step, finished together with the local
 // part: split partials of the exact document attention or of a Quadrature
 // module (log-sum-exp form: ml != NULL) or of an MLP module (plain sums:
@@ -144,6 +168,9 @@ hipError_t launch_mlp_rows_lds32(const MlpParams &p, hipStream_t st);
 hipError_t launch_mlp_prefill(const MlpParams &p, hipStream_t st);
 hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_merge_k(const MergeKParams &p, int dtype, int d, hipStream_t st);
+// Blocks of one deep-MLP layer for the launch shape of the given dtype.
+long deep_layer_blocks(int dtype, int Hkv, int Rp, int N);
+hipError_t launch_deep_layers(const DeepParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 hipError_t launch_finish(const FinishParams &p, int dtype, int d, hipStream_t st);
 

@@ -72,6 +72,8 @@ inline bool f32_ok(const void *p) { return p && aligned(p, 4); }
 // with vector accesses: 16-byte aligned like every tensor.
 inline bool rows_ok(const void *p) { return p && aligned(p, 16); }
 
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 struct AttnPlan {
     int P = 0, Rp = 0, RT = 0, RG = 0, S = 0, chunk = kTile;
     int WR = 1, WS = 1, RB = 0, SB = 0;
@@ -320,6 +322,121 @@ nectar_status nectar_doc_attn_exact(const nectar_attn_desc *desc, int64_t n, con
                                 cp, ws, st), st);
 }
 
+// ---------------------------------------------------------------------------
+// Deep MLP module (Eq. (3.6) with re-injection): layer bookkeeping.
+
+// Layer l's part (0 backbone, 1 score, 2 target), its width and the width of
+// the state it reads (0: the query only).
+struct DeepShape {
+    int D[3], H[3], nl;
+    int part(int l) const { return l < D[0] ? 0 : (l < D[0] + D[1] ? 1 : 2); }
+    int first(int part) const { return part == 0 ? 0 : (part == 1 ? D[0] : D[0] + D[1]); }
+    int in_width(int l) const {
+        const int pt = part(l);
+        return l > first(pt) ? H[pt] : (pt > 0 && D[0] > 0 ? H[0] : 0);
+    }
+    // width of the state a head's read-out reads
+    int last_width(int head) const { return D[head] > 0 ? H[head] : H[0]; }
+};
+
+static DeepShape deep_shape(const nectar_deep_mlp *m) {
+    DeepShape sh;
+    for (int i = 0; i < 3; ++i) {
+        sh.D[i] = m->depth[i];
+        sh.H[i] = m->depth[i] > 0 ? m->width[i] : 0;
+    }
+    sh.nl = sh.D[0] + sh.D[1] + sh.D[2];
+    return sh;
+}
+
+static nectar_status check_deep(const nectar_deep_mlp *m) {
+    if (!m) return NECTAR_EINVAL;
+    if (m->act != NECTAR_ACT_GELU && m->act != NECTAR_ACT_SILU && m->act != NECTAR_ACT_GELU_TANH)
+        return NECTAR_EINVAL;
+    for (int i = 0; i < 3; ++i)
+        if (m->depth[i] < 0 || (m->depth[i] > 0 && m->width[i] <= 0)) return NECTAR_EINVAL;
+    const DeepShape sh = deep_shape(m);
+    if (sh.D[0] + sh.D[1] < 1 || sh.D[0] + sh.D[2] < 1) return NECTAR_EINVAL;
+    if (sh.nl > NECTAR_DEEP_MAX_LAYERS) return NECTAR_EUNSUPPORTED;
+    for (int i = 0; i < 3; ++i)
+        if (sh.D[i] > 0 && (sh.H[i] % 32 != 0 || sh.H[i] > (1 << 20))) return NECTAR_EUNSUPPORTED;
+    for (int l = 0; l < sh.nl; ++l) {
+        if (!tensor_ok(m->Wq[l]) || !m->b[l] || !aligned(m->b[l], 4)) return NECTAR_EINVAL;
+        if ((sh.in_width(l) > 0) != (m->Wh[l] != nullptr)) return NECTAR_EINVAL;
+        if (m->Wh[l] && !tensor_ok(m->Wh[l])) return NECTAR_EINVAL;
+    }
+    if (!tensor_ok(m->ws_out) || !tensor_ok(m->Wt_out)) return NECTAR_EINVAL;
+    if (!m->bs_out || !aligned(m->bs_out, 4) || !m->bt_out || !aligned(m->bt_out, 4)) return NECTAR_EINVAL;
+    return NECTAR_OK;
+}
+
+// Workspace: two ping-pong hidden-state buffers per part, [Hkv][Rp][H] each.
+static size_t deep_buffer_bytes(const nectar_attn_desc *d, int H) {
+    const size_t esz = d->dtype == NECTAR_BF16 ? 2 : 4;
+    return align256((size_t)d->Hkv * d->R * (d->Hq / d->Hkv) * H * esz);
+}
+
+static size_t deep_ws_bytes(const nectar_attn_desc *d, const nectar_deep_mlp *m) {
+    const DeepShape sh = deep_shape(m);
+    size_t b = 0;
+    for (int i = 0; i < 3; ++i) b += 2 * deep_buffer_bytes(d, sh.H[i]);
+    return b;
+}
+
+static hipError_t run_deep(const nectar_attn_desc *desc, const nectar_deep_mlp *m, const void *q, float *a_out,
+                           float *A_out, void *ws, hipStream_t st) {
+    const DeepShape sh = deep_shape(m);
+    const int G = desc->Hq / desc->Hkv, Rp = desc->R * G;
+    char *buf[3][2];
+    char *w = (char *)ws;
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 2; ++j) {
+            buf[i][j] = w;
+            w += deep_buffer_bytes(desc, sh.H[i]);
+        }
+    DeepParams a{};
+    a.q = q; a.Hq = desc->Hq; a.G = G; a.Hkv = desc->Hkv; a.Rp = Rp;
+    auto layer = [&](int l, int step) {
+        const int pt = sh.part(l);
+        DeepLayer L{};
+        L.Wq = m->Wq[l]; L.Wh = m->Wh[l]; L.b = m->b[l];
+        L.N = sh.H[pt]; L.Kh = sh.in_width(l); L.act = m->act;
+        // the state read: the previous layer of the part, else the backbone's last
+        if (l > sh.first(pt)) L.X = buf[pt][(step - 1) & 1];
+        else if (L.Kh > 0) L.X = buf[0][(sh.D[0] - 1) & 1];
+        L.Y = buf[pt][step & 1];
+        L.blocks = deep_layer_blocks(desc->dtype, desc->Hkv, Rp, L.N);
+        return L;
+    };
+    auto head_state = [&](int head) -> const void * {
+        return sh.D[head] > 0 ? buf[head][(sh.D[head] - 1) & 1] : buf[0][(sh.D[0] - 1) & 1];
+    };
+    hipError_t e = hipSuccess;
+    for (int l = 0; l < sh.D[0] && e == hipSuccess; ++l) {
+        a.nl = 1;
+        a.L0 = layer(l, l);
+        e = launch_deep_layers(a, desc->dtype, desc->d, st);
+    }
+    const int Dh = sh.D[1] > sh.D[2] ? sh.D[1] : sh.D[2];
+    for (int j = 0; j < Dh && e == hipSuccess; ++j) {
+        a.nl = 0;
+        if (j < sh.D[1]) a.L0 = layer(sh.first(1) + j, j), a.nl = 1;
+        if (j < sh.D[2]) (a.nl ? a.L1 : a.L0) = layer(sh.first(2) + j, j), a.nl += 1;
+        e = launch_deep_layers(a, desc->dtype, desc->d, st);
+    }
+    if (e != hipSuccess) return e;
+    // the two linear read-outs in one launch
+    DeepLayer rs{}, rt{};
+    rs.Wh = m->ws_out; rs.b = m->bs_out; rs.X = head_state(1); rs.Yf = a_out;
+    rs.N = 1; rs.Kh = sh.last_width(1); rs.act = -1;
+    rs.blocks = deep_layer_blocks(desc->dtype, desc->Hkv, Rp, 1);
+    rt.Wh = m->Wt_out; rt.b = m->bt_out; rt.X = head_state(2); rt.Yf = A_out;
+    rt.N = desc->d; rt.Kh = sh.last_width(2); rt.act = -1;
+    rt.blocks = deep_layer_blocks(desc->dtype, desc->Hkv, Rp, desc->d);
+    a.nl = 2; a.L0 = rs; a.L1 = rt;
+    return launch_deep_layers(a, desc->dtype, desc->d, st);
+}
+
 static nectar_status check_module(const nectar_attn_desc *desc, const nectar_module *m) {
     if (!m) return NECTAR_EINVAL;
     if (m->kind == NECTAR_MODULE_MLP) {
@@ -340,6 +457,7 @@ static nectar_status check_module(const nectar_attn_desc *desc, const nectar_mod
         if (m->p > 0 && (!tensor_ok(m->W) || !tensor_ok(m->Z))) return NECTAR_EINVAL;
         return NECTAR_OK;
     }
+    if (m->kind == NECTAR_MODULE_DEEP_MLP) return check_deep(m->deep);
     return NECTAR_EINVAL;
 }
 
@@ -349,6 +467,7 @@ size_t nectar_module_workspace_size(const nectar_attn_desc *desc, const nectar_m
         if (m->p < 0 || m->p > 0x7fffffffL - kTile) return 0;
         return plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)m->p).ws;
     }
+    if (m->kind == NECTAR_MODULE_DEEP_MLP) return check_deep(m->deep) == NECTAR_OK ? deep_ws_bytes(desc, m->deep) : 0;
     if (m->kind != NECTAR_MODULE_MLP || m->Ht < 0 || m->Hs < 0) return 0;
     return plan_mlp(desc, m->Ht, m->Hs).ws;
 }
@@ -398,6 +517,10 @@ nectar_status nectar_module_forward(const nectar_attn_desc *desc, const nectar_m
         cp.A_out = A_out;
         return finish(run_attention(desc, pl, q, m->W, m->Z, 0, m->p * desc->d, 1, desc->R, (long)m->p,
                                     0, 0, cp, ws, st), st);
+    }
+    if (m->kind == NECTAR_MODULE_DEEP_MLP) {
+        if ((s = check_ws(deep_ws_bytes(desc, m->deep), ws, ws_bytes)) != NECTAR_OK) return s;
+        return finish(run_deep(desc, m->deep, q, a_out, A_out, ws, st), st);
     }
     const MlpPlan pl = plan_mlp(desc, m->Ht, m->Hs);
     if ((s = check_ws(pl.ws, ws, ws_bytes)) != NECTAR_OK) return s;
@@ -494,8 +617,6 @@ nectar_status nectar_merge_k(const nectar_attn_desc *desc, int K, const float *c
 // ---------------------------------------------------------------------------
 // Whole layer step: deferred partials of every part, one finishing pass.
 
-static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 // Partial bytes of an attention plan when its finish is deferred.
 static size_t attn_partial_bytes(const nectar_attn_desc *d, const AttnPlan &pl) {
     return pl.S > 0 ? (size_t)pl.P * pl.SB * pl.Rp * ((size_t)d->d * 4 + 8) : 0;
@@ -506,7 +627,8 @@ static size_t mlp_partial_bytes(const nectar_attn_desc *d, const MlpPlan &pl) {
 }
 
 struct StepPlan {
-    bool exact = false, mlp = false, kvp = false;
+    bool exact = false, mlp = false, kvp = false, deep = false;
+    size_t deep_ws = 0;
     // fused: deferred partials of every part, then one finishing launch (decode
     // shapes, where every part is short); otherwise the parts finish in place
     // or with their own combine and the local pass merges.
@@ -533,14 +655,17 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
     if (m && m->kind == NECTAR_MODULE_MLP) {
         sp.mlp = true;
         sp.mlpl = plan_mlp(d, m->Ht, m->Hs);
+    } else if (m && m->kind == NECTAR_MODULE_DEEP_MLP) {
+        sp.deep = true;
+        sp.deep_ws = deep_ws_bytes(d, m->deep);
     } else if (m) {
         sp.kvp = true;
         sp.kvpl = plan_attn(d, d->Hkv, Rp_doc, (long)m->p);
     }
     auto decode = [](const AttnPlan &pl) { return pl.S == 0 || (!pl.lds && pl.RT == 1); };
-    sp.fused = d->dtype == NECTAR_F32 ||
+    sp.fused = !sp.deep && (d->dtype == NECTAR_F32 ||
                (decode(sp.loc) && (!exact || decode(sp.doc)) && (!sp.mlp || (!sp.mlpl.prefill && sp.mlpl.RT == 1)) &&
-                (!sp.kvp || decode(sp.kvpl)));
+                (!sp.kvp || decode(sp.kvpl))));
     if (sp.fused) {
         size_t off = align256(attn_partial_bytes(d, sp.loc));
         if (exact) {
@@ -557,6 +682,7 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
         if (exact && sp.doc.ws > sub) sub = sp.doc.ws;
         if (sp.mlp && sp.mlpl.ws > sub) sub = sp.mlpl.ws;
         if (sp.kvp && sp.kvpl.ws > sub) sub = sp.kvpl.ws;
+        if (sp.deep && sp.deep_ws > sub) sub = sp.deep_ws;
         size_t off = align256(sub);
         sp.off_px = off;
         off += exact ? pair_bytes(d) : 0;
@@ -650,6 +776,8 @@ static hipError_t run_step_composed(const nectar_attn_desc *desc, const StepPlan
         pair(sp.off_pm, outs->a_out, outs->Am_out, &am, &Am);
         if (sp.mlp) {
             e = run_mlp(desc, sp.mlpl, module, q, am, Am, w, st);
+        } else if (sp.deep) {
+            e = run_deep(desc, module->deep, q, am, Am, w, st);
         } else {
             CombineParams cp{};
             cp.lse_out = am; cp.A_out = Am;

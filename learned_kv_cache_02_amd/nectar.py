@@ -26,7 +26,8 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16 = 0, 1
-MLP, KVPAIR = 0, 1
+MLP, KVPAIR, DEEP_MLP = 0, 1, 2
+DEEP_MAX_LAYERS = 16
 GELU, SILU, GELU_TANH = 0, 1, 2
 STATUS = {0: "NECTAR_OK", 1: "NECTAR_EINVAL", 2: "NECTAR_EUNSUPPORTED", 3: "NECTAR_EWORKSPACE",
           4: "NECTAR_EHIP"}
@@ -43,6 +44,14 @@ class LocalDesc(ctypes.Structure):
                 ("T_cap", ctypes.c_int32), ("q_offset", ctypes.c_int32)]
 
 
+class DeepMLP(ctypes.Structure):
+    _fields_ = [("depth", ctypes.c_int32 * 3), ("width", ctypes.c_int32 * 3), ("act", ctypes.c_int32),
+                ("Wq", ctypes.c_void_p * DEEP_MAX_LAYERS), ("Wh", ctypes.c_void_p * DEEP_MAX_LAYERS),
+                ("b", ctypes.c_void_p * DEEP_MAX_LAYERS),
+                ("ws_out", ctypes.c_void_p), ("bs_out", ctypes.c_void_p),
+                ("Wt_out", ctypes.c_void_p), ("bt_out", ctypes.c_void_p)]
+
+
 class Module(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("act", ctypes.c_int32), ("Ht", ctypes.c_int32),
                 ("Hs", ctypes.c_int32),
@@ -50,7 +59,8 @@ class Module(ctypes.Structure):
                 ("W2t", ctypes.c_void_p), ("b2", ctypes.c_void_p),
                 ("Ws", ctypes.c_void_p), ("bs", ctypes.c_void_p),
                 ("ws2", ctypes.c_void_p), ("bs2", ctypes.c_void_p),
-                ("p", ctypes.c_int64), ("W", ctypes.c_void_p), ("Z", ctypes.c_void_p)]
+                ("p", ctypes.c_int64), ("W", ctypes.c_void_p), ("Z", ctypes.c_void_p),
+                ("deep", ctypes.POINTER(DeepMLP))]
 
 
 class StepOutputs(ctypes.Structure):
@@ -235,12 +245,46 @@ class KVPairModule:
         return m
 
 
+@dataclass
+class DeepMLPModule:
+    """Deep MLP module with query re-injection (Eq. (3.6)): depth (D_b, D_s, D_t),
+    width (H_b, H_s, H_t); layers = [(Wq, Wh or None, b)] backbone first, then
+    score, then target (Wq [Hkv][H][d], Wh [Hkv][H][H_in], b [Hkv][H] fp32);
+    read-outs ws_out [Hkv][H_s last], bs_out [Hkv], Wt_out [Hkv][d][H_t last],
+    bt_out [Hkv][d]."""
+    depth: tuple
+    width: tuple
+    layers: list
+    ws_out: torch.Tensor
+    bs_out: torch.Tensor
+    Wt_out: torch.Tensor
+    bt_out: torch.Tensor
+    act: int = SILU
+
+    def struct(self) -> Module:
+        if len(self.layers) > DEEP_MAX_LAYERS:
+            raise ValueError("at most %d layers" % DEEP_MAX_LAYERS)
+        dm = DeepMLP()
+        dm.depth[:] = [int(x) for x in self.depth]
+        dm.width[:] = [int(x) for x in self.width]
+        dm.act = self.act
+        for l, (Wq, Wh, b) in enumerate(self.layers):
+            dm.Wq[l], dm.Wh[l], dm.b[l] = _ptr(Wq), _ptr(Wh), _ptr(b)
+        dm.ws_out, dm.bs_out, dm.Wt_out, dm.bt_out = (_ptr(t) for t in (self.ws_out, self.bs_out, self.Wt_out,
+                                                                         self.bt_out))
+        m = Module()
+        m.kind = DEEP_MLP
+        m.deep = ctypes.pointer(dm)
+        m._deep_keep = dm          # the pointed-to description lives as long as the struct
+        return m
+
+
 def module_workspace_size(dsc: AttnDesc, mod) -> int:
     return int(_lib.nectar_module_workspace_size(ctypes.byref(dsc), ctypes.byref(mod.struct())))
 
 
 def module_forward(q, module, Hkv, *, scale=0.0, splits=0, a_out=None, A_out=None):
-    """(a [R][Hq], A [R][Hq][d]) fp32 of an MLPModule or KVPairModule."""
+    """(a [R][Hq], A [R][Hq][d]) fp32 of an MLPModule, DeepMLPModule or KVPairModule."""
     R, Hq, d = q.shape
     dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
     m = module.struct()

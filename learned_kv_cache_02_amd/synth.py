@@ -13,7 +13,8 @@ inputs the method consumes.  The recipe:
   float64 at absolute positions: document keys at 0..n-1, local token i of a
   question at n + i, a query at its own token's position;
 * module weights are scaled to N(0, 1/fan_in) (fan_in = d for the first layer,
-  the hidden width for the read-out); biases are zero unless requested;
+  the hidden width for the read-out, d + the state width for a deep layer that
+  re-injects the query); biases are zero unless requested;
   Quadrature pairs W, Z are N(0, 1) without RoPE;
 * values are rounded float64 -> float32 (round to nearest even) and, for bf16,
   float32 -> bf16 (round to nearest even).  bf16 tensors are returned as their
@@ -34,6 +35,7 @@ CHUNK = 16384
 T_DOC_K, T_DOC_V, T_LOC_K, T_LOC_V, T_Q = 0, 1, 2, 3, 4
 T_MLP = 16          # + 16 * module index + parameter index
 T_KVP_W, T_KVP_Z = 8, 9
+T_DEEP = 1024      # + 4 * layer + parameter index; read-outs at T_DEEP + 512
 
 _POOL = None
 
@@ -205,3 +207,32 @@ def kv_pairs(cfg: Config, layer: int = 0, p: int | None = None):
     W = _heads(cfg, layer, T_KVP_W, cfg.Hkv, p)
     Z = _heads(cfg, layer, T_KVP_Z, cfg.Hkv, p)
     return W, Z
+
+
+def deep_mlp_params(seed: int, Hkv: int, d: int, shape, dtype: str, layer: int = 0, bias_std: float = 0.0):
+    """Deep module of Eq. (3.6) per KV head (``shape``: configs.DeepShape).
+
+    Returns dict with depth, width, layers [(Wq [Hkv][H][d], Wh [Hkv][H][H_in] or
+    None, b [Hkv][H])], ws_out [Hkv][H_s last], bs_out [Hkv], Wt_out [Hkv][d][H_t last],
+    bt_out [Hkv][d]; weights in the storage type, biases float32.  A layer that
+    reads the query and a state has fan_in d + H_in for both of its matrices."""
+    def w(tid, rows, cols, fan_in):
+        x = np.stack([normal((seed, layer, tid, h), rows, cols) for h in range(Hkv)]) * fan_in ** -0.5
+        return store(x, dtype)
+
+    def bias(tid, shape_):
+        if bias_std == 0.0:
+            return np.zeros(shape_, dtype=np.float32)
+        x = np.stack([normal((seed, layer, tid, h), 1, int(np.prod(shape_[1:])))[0] for h in range(Hkv)])
+        return (x * bias_std).astype(np.float32).reshape(shape_)
+
+    layers = []
+    for l, (H, H_in) in enumerate(shape.layers()):
+        t = T_DEEP + 4 * l
+        fan = d + H_in
+        layers.append((w(t, H, d, fan), w(t + 1, H, H_in, fan) if H_in else None, bias(t + 2, (Hkv, H))))
+    Hs, Ht = shape.last_width(1), shape.last_width(2)
+    t = T_DEEP + 512
+    return dict(depth=tuple(shape.depth), width=tuple(shape.width), layers=layers,
+                ws_out=w(t, 1, Hs, Hs).reshape(Hkv, Hs), bs_out=bias(t + 1, (Hkv,)).reshape(Hkv),
+                Wt_out=w(t + 2, d, Ht, Ht), bt_out=bias(t + 3, (Hkv, d)))

@@ -28,11 +28,22 @@ class Local(ctypes.Structure):
                 ("T_cap", ctypes.c_int32), ("q_offset", ctypes.c_int32)]
 
 
+DEEP_MAX = 16
+
+
+class Deep(ctypes.Structure):
+    _fields_ = [("depth", ctypes.c_int32 * 3), ("width", ctypes.c_int32 * 3), ("act", ctypes.c_int32),
+                ("Wq", ctypes.c_void_p * DEEP_MAX), ("Wh", ctypes.c_void_p * DEEP_MAX),
+                ("b", ctypes.c_void_p * DEEP_MAX)] + \
+               [(n, ctypes.c_void_p) for n in ("ws_out", "bs_out", "Wt_out", "bt_out")]
+
+
 class Module(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("act", ctypes.c_int32), ("Ht", ctypes.c_int32),
                 ("Hs", ctypes.c_int32)] + \
                [(n, ctypes.c_void_p) for n in ("W1", "b1", "W2t", "b2", "Ws", "bs", "ws2", "bs2")] + \
-               [("p", ctypes.c_int64), ("W", ctypes.c_void_p), ("Z", ctypes.c_void_p)]
+               [("p", ctypes.c_int64), ("W", ctypes.c_void_p), ("Z", ctypes.c_void_p),
+                ("deep", ctypes.POINTER(Deep))]
 
 
 class StepOuts(ctypes.Structure):
@@ -82,7 +93,7 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.nectar_abi_version() == 1
+    assert lib.nectar_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -204,6 +215,69 @@ def test_workspace_init_validation(lib):
     assert lib.nectar_workspace_init(None, 0, None) == OK          # nothing to do, no launch
     assert lib.nectar_workspace_init(None, 64, None) == EINVAL
     assert lib.nectar_workspace_init(MIS, 64, None) == EINVAL
+
+
+def _deep(depth, width, act=1):
+    """A well-formed deep module description with fake (aligned) pointers."""
+    dm = Deep()
+    dm.depth[:] = list(depth)
+    dm.width[:] = list(width)
+    dm.act = act
+    Db, Ds, Dt = depth
+    for l in range(min(sum(depth), DEEP_MAX)):
+        part = 0 if l < Db else (1 if l < Db + Ds else 2)
+        first = (0, Db, Db + Ds)[part]
+        reads_state = l > first or (part > 0 and Db > 0)
+        dm.Wq[l], dm.b[l] = A16, A16
+        dm.Wh[l] = A16 if reads_state else None
+    dm.ws_out = dm.bs_out = dm.Wt_out = dm.bt_out = A16
+    return dm
+
+
+def test_deep_module_validation_and_workspace(lib):
+    d = Desc(3, 8, 2, 128, 1, 0.0, 0)
+    Rp = 3 * 4
+
+    def fwd(dm, q=A16):
+        m = Module(kind=2)
+        m.deep = ctypes.pointer(dm) if dm is not None else None
+        return lib.nectar_module_forward(ctypes.byref(d), ctypes.byref(m), q, A16, A16, A16, 0, None)
+
+    def wsz(dm):
+        m = Module(kind=2)
+        m.deep = ctypes.pointer(dm)
+        return lib.nectar_module_workspace_size(ctypes.byref(d), ctypes.byref(m))
+
+    # two ping-pong bf16 state buffers per part: 2 * (H_b + H_s + H_t) * Hkv * Rp * 2 bytes
+    assert wsz(_deep((0, 2, 3), (0, 64, 96))) == 2 * (64 + 96) * 2 * Rp * 2
+    assert wsz(_deep((2, 1, 2), (128, 32, 64))) == 2 * (128 + 32 + 64) * 2 * Rp * 2
+    assert wsz(_deep((0, 2, 3), (7, 64, 96))) == 2 * (64 + 96) * 2 * Rp * 2    # backbone width unused
+    # a workspace below that size is refused before any launch
+    assert fwd(_deep((0, 2, 3), (0, 64, 96))) == EWORKSPACE
+    assert fwd(None) == EINVAL
+    assert fwd(_deep((0, 0, 3), (0, 64, 96))) == EINVAL             # no score network at all
+    assert fwd(_deep((0, 2, 0), (0, 64, 96))) == EINVAL             # no target network
+    assert fwd(_deep((0, 2, -1), (0, 64, 96))) == EINVAL
+    assert fwd(_deep((0, 2, 3), (0, 0, 96))) == EINVAL              # a part with layers needs a width
+    assert fwd(_deep((0, 2, 3), (0, 48, 96))) == EUNSUPPORTED       # widths are multiples of 32
+    assert fwd(_deep((8, 8, 8), (64, 64, 64))) == EUNSUPPORTED      # more than 16 layers
+    assert fwd(_deep((0, 2, 3), (0, 64, 96), act=9)) == EINVAL
+    dm = _deep((0, 2, 3), (0, 64, 96))
+    dm.Wh[0] = A16                                                  # the first layer reads only q
+    assert fwd(dm) == EINVAL
+    dm = _deep((0, 2, 3), (0, 64, 96))
+    dm.Wh[1] = None                                                 # the second reads the state
+    assert fwd(dm) == EINVAL
+    dm = _deep((2, 1, 2), (64, 32, 64))
+    dm.Wh[2] = None                                                 # a head after a backbone reads it
+    assert fwd(dm) == EINVAL
+    dm = _deep((0, 2, 3), (0, 64, 96))
+    dm.Wq[4] = MIS
+    assert fwd(dm) == EINVAL
+    dm = _deep((0, 2, 3), (0, 64, 96))
+    dm.bt_out = None
+    assert fwd(dm) == EINVAL
+    assert fwd(_deep((0, 2, 3), (0, 64, 96)), q=MIS) == EINVAL
 
 
 def test_merge_validation(lib):

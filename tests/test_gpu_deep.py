@@ -1,0 +1,148 @@
+"""GPU parity of the deep MLP module (Eq. (3.6) with query re-injection and an
+optional shared backbone) against the fp64 oracle: both depth shapes the notes
+plot, heads read from the backbone, several 16-row / 16-output tiles with
+ragged tails, both head dimensions, fp32 and bf16, the full-size modules of the
+Qwen3-4B-shaped decode layer, and the module inside the fused layer step.
+
+Tolerance: the bf16 bars of the other module tests (2e-2 on read-outs, 1e-2 on
+scores).  The kernels keep fp32 sums and store each hidden state in bf16 (a
+relative rounding of at most 2^-9 per layer), so with N(0, 1/fan_in) weights
+the output error grows roughly with the square root of the depth and stays
+near 1e-3 for the depths tested here.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import ATOL_F32, ATOL_LSE_BF16, ATOL_OUT_BF16, REL_L2_BF16, check, dev, host
+from learned_kv_cache_02_amd import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+ACTS = {"gelu": 0, "silu": 1, "gelu_tanh": 2}
+
+
+@pytest.fixture(scope="module")
+def nx(gpu):
+    from learned_kv_cache_02_amd import nectar
+    return nectar
+
+
+def _module(nx, P, act):
+    import torch
+
+    def t(x):
+        if x is None:
+            return None
+        return dev(x) if x.size else torch.empty(x.shape, dtype=torch.float32, device="cuda")
+
+    return nx.DeepMLPModule(P["depth"], P["width"], [(t(a), t(b), t(c)) for a, b, c in P["layers"]],
+                            t(P["ws_out"]), t(P["bs_out"]), t(P["Wt_out"]), t(P["bt_out"]), act=ACTS[act])
+
+
+def _q(seed, R, Hq, d, dt):
+    x = synth.normal((seed, 0, synth.T_Q, 0), R * Hq, d).reshape(R, Hq, d)
+    return synth.store(x, dt)
+
+
+SHAPES = [((0, 2, 3), (0, 64, 96)), ((2, 1, 2), (64, 32, 64)), ((1, 0, 2), (64, 0, 32)),
+          ((0, 1, 1), (0, 96, 32)), ((3, 2, 0), (32, 64, 0))]
+
+
+@pytest.mark.parametrize("depth,width", SHAPES)
+@pytest.mark.parametrize("R,Hq,Hkv", [(1, 32, 8), (3, 28, 4), (20, 8, 2)])
+def test_deep_mlp_bf16(nx, depth, width, R, Hq, Hkv):
+    d = 128
+    print("case deep bf16 depth=%s width=%s R=%d Hq=%d Hkv=%d" % (depth, width, R, Hq, Hkv), flush=True)
+    shape = configs.DeepShape(depth, width)
+    P = synth.deep_mlp_params(31 + R, Hkv, d, shape, "bf16", bias_std=0.3)
+    q = _q(32 + R, R, Hq, d, "bf16")
+    a, A = nx.module_forward(dev(q), _module(nx, P, "silu"), Hkv)
+    ea, eA = oracle.deep_mlp(q, P, dt="bf16", Hq=Hq, Hkv=Hkv, act="silu")
+    check("a", host(a), ea, ATOL_LSE_BF16)
+    check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
+def test_deep_mlp_other_activations_and_d64(nx, act):
+    R, Hq, Hkv, d = 5, 12, 3, 64
+    print("case deep bf16 d=64 %s" % act, flush=True)
+    shape = configs.DeepShape((1, 2, 2), (64, 32, 96))
+    P = synth.deep_mlp_params(40, Hkv, d, shape, "bf16", bias_std=0.3)
+    q = _q(41, R, Hq, d, "bf16")
+    a, A = nx.module_forward(dev(q), _module(nx, P, act), Hkv)
+    ea, eA = oracle.deep_mlp(q, P, dt="bf16", Hq=Hq, Hkv=Hkv, act=act)
+    check("a", host(a), ea, ATOL_LSE_BF16)
+    check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_deep_mlp_f32(nx, d):
+    R, Hq, Hkv = 4, 6, 2
+    print("case deep f32 d=%d" % d, flush=True)
+    shape = configs.DeepShape((1, 1, 2), (32, 64, 32))
+    P = synth.deep_mlp_params(50, Hkv, d, shape, "f32", bias_std=0.3)
+    q = _q(51, R, Hq, d, "f32")
+    a, A = nx.module_forward(dev(q), _module(nx, P, "silu"), Hkv)
+    ea, eA = oracle.deep_mlp(q, P, dt="f32", Hq=Hq, Hkv=Hkv, act="silu")
+    check("a", host(a), ea, ATOL_F32)
+    check("A", host(A), eA, ATOL_F32)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_deep_mlp_full_size_decode_layer(nx, which):
+    """The Qwen3-4B-shaped layer's deep modules at full width (rho ~ 10 %),
+    one decode token x 32 query heads, every row against the oracle."""
+    cfg = configs.C2
+    shape = configs.DEEP_C2[which]
+    print("case deep c2 %s" % (shape,), flush=True)
+    P = synth.deep_mlp_params(cfg.seed, cfg.Hkv, cfg.d, shape, "bf16")
+    q = synth.queries(cfg)
+    a, A = nx.module_forward(dev(q), _module(nx, P, "silu"), cfg.Hkv)
+    ea, eA = oracle.deep_mlp(q, P, dt="bf16", Hq=cfg.Hq, Hkv=cfg.Hkv, act="silu")
+    check("a", host(a), ea, ATOL_LSE_BF16)
+    check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
+
+
+def test_deep_mlp_many_rows_sampled(nx):
+    """A batched shape (1,000 tokens x 28 heads over 4 KV heads): sampled rows."""
+    R, Hq, Hkv, d = 1000, 28, 4, 128
+    print("case deep batched R=%d" % R, flush=True)
+    shape = configs.DeepShape((0, 2, 3), (0, 128, 160))
+    P = synth.deep_mlp_params(60, Hkv, d, shape, "bf16", bias_std=0.2)
+    q = _q(61, R, Hq, d, "bf16")
+    a, A = nx.module_forward(dev(q), _module(nx, P, "silu"), Hkv)
+    g = np.random.default_rng(62)
+    toks = np.unique(np.concatenate([[0, R - 1], g.choice(R, 40, replace=False)])).astype(np.int32)
+    ea, eA = oracle.deep_mlp(q, P, dt="bf16", Hq=Hq, Hkv=Hkv, act="silu", toks=toks)
+    check("a", host(a)[toks], ea, ATOL_LSE_BF16)
+    check("A", host(A)[toks], eA, ATOL_OUT_BF16, REL_L2_BF16)
+
+
+def test_deep_mlp_in_the_layer_step(nx):
+    """The Nectar path of a decode step through a deep module: its pair and the
+    merge with the causal local part, next to the exact path."""
+    import torch
+    B, Tq, T_loc, T_cap, qoff, Hq, Hkv, d, n = 2, 1, 200, 256, 199, 16, 4, 128, 1500
+    print("case deep layer step", flush=True)
+    R = B * Tq
+    g = np.random.default_rng(70)
+    bf = lambda *s: synth.to_bf16_bits(g.standard_normal(s))
+    q, K, V = bf(R, Hq, d), bf(Hkv, n, d), bf(Hkv, n, d)
+    Kl, Vl = bf(B, Hkv, T_cap, d), bf(B, Hkv, T_cap, d)
+    P = synth.deep_mlp_params(71, Hkv, d, configs.DeepShape((2, 1, 2), (64, 96, 64)), "bf16", bias_std=0.3)
+    o = nx.layer_step(dev(q), dev(Kl), dev(Vl), Hkv, B=B, Tq=Tq, T_loc=T_loc, q_offset=qoff, k=dev(K), v=dev(V),
+                      module=_module(nx, P, "silu"), exact=True, pairs=True)
+    Klv, Vlv = np.ascontiguousarray(Kl[:, :, :T_loc]), np.ascontiguousarray(Vl[:, :, :T_loc])
+    kw = dict(dt="bf16", B=B, Tq=Tq, Hq=Hq, Hkv=Hkv, Tloc=T_loc, q_offset=qoff)
+    ea, eA = oracle.deep_mlp(q, P, dt="bf16", Hq=Hq, Hkv=Hkv, act="silu")
+    el, eAl = oracle.local_attn(q, Kl[:, :, :T_loc].copy(), Vl[:, :, :T_loc].copy(), **kw)
+    eo, eol = oracle.merge(ea, eA, el, eAl)
+    check("a", host(o["a"]), ea, ATOL_LSE_BF16)
+    check("Am", host(o["Am"]), eA, ATOL_OUT_BF16)
+    check("out_nectar", host(o["out_nectar"]), eo, ATOL_OUT_BF16)
+    check("lse_nectar", host(o["lse_nectar"]), eol, ATOL_LSE_BF16)
+    flse, fout = oracle.full_attn(q, K, V, Klv, Vlv, **kw)
+    check("out_exact", host(o["out_exact"]), fout, ATOL_OUT_BF16)
+    check("lse_exact", host(o["lse_exact"]), flse, ATOL_LSE_BF16)
+    assert o["out_nectar"].dtype == torch.bfloat16

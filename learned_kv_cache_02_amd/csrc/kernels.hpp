@@ -168,9 +168,10 @@ hipError_t launch_mlp_rows_lds32(const MlpParams &p, hipStream_t st);
 hipError_t launch_mlp_prefill(const MlpParams &p, hipStream_t st);
 hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_merge_k(const MergeKParams &p, int dtype, int d, hipStream_t st);
-// Blocks of one deep-MLP layer for the launch shape of the given dtype.
-long deep_layer_blocks(int dtype, int Hkv, int Rp, int N);
-hipError_t launch_deep_layers(const DeepParams &p, int dtype, int d, hipStream_t st);
+// Blocks of one deep-MLP layer for the launch shape of the given dtype (lds:
+// the LDS-staged kernel for many rows per KV head).
+long deep_layer_blocks(int dtype, int lds, int Hkv, int Rp, int N);
+hipError_t launch_deep_layers(const DeepParams &p, int dtype, int d, int lds, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 hipError_t launch_finish(const FinishParams &p, int dtype, int d, hipStream_t st);
 

@@ -370,6 +370,12 @@ static nectar_status check_deep(const nectar_deep_mlp *m) {
     return NECTAR_OK;
 }
 
+// Rows per KV head from which a deep layer runs on the LDS-staged kernel.
+#ifndef NECTAR_DEEP_LDS_ROWS
+#define NECTAR_DEEP_LDS_ROWS 1024
+#endif
+static constexpr int kDeepLdsRows = NECTAR_DEEP_LDS_ROWS;
+
 // Workspace: two ping-pong hidden-state buffers per part, [Hkv][Rp][H] each.
 static size_t deep_buffer_bytes(const nectar_attn_desc *d, int H) {
     const size_t esz = d->dtype == NECTAR_BF16 ? 2 : 4;
@@ -396,6 +402,7 @@ static hipError_t run_deep(const nectar_attn_desc *desc, const nectar_deep_mlp *
         }
     DeepParams a{};
     a.q = q; a.Hq = desc->Hq; a.G = G; a.Hkv = desc->Hkv; a.Rp = Rp;
+    const int lds = desc->dtype == NECTAR_BF16 && Rp >= kDeepLdsRows;
     auto layer = [&](int l, int step) {
         const int pt = sh.part(l);
         DeepLayer L{};
@@ -405,7 +412,7 @@ static hipError_t run_deep(const nectar_attn_desc *desc, const nectar_deep_mlp *
         if (l > sh.first(pt)) L.X = buf[pt][(step - 1) & 1];
         else if (L.Kh > 0) L.X = buf[0][(sh.D[0] - 1) & 1];
         L.Y = buf[pt][step & 1];
-        L.blocks = deep_layer_blocks(desc->dtype, desc->Hkv, Rp, L.N);
+        L.blocks = deep_layer_blocks(desc->dtype, lds, desc->Hkv, Rp, L.N);
         return L;
     };
     auto head_state = [&](int head) -> const void * {
@@ -415,26 +422,26 @@ static hipError_t run_deep(const nectar_attn_desc *desc, const nectar_deep_mlp *
     for (int l = 0; l < sh.D[0] && e == hipSuccess; ++l) {
         a.nl = 1;
         a.L0 = layer(l, l);
-        e = launch_deep_layers(a, desc->dtype, desc->d, st);
+        e = launch_deep_layers(a, desc->dtype, desc->d, lds, st);
     }
     const int Dh = sh.D[1] > sh.D[2] ? sh.D[1] : sh.D[2];
     for (int j = 0; j < Dh && e == hipSuccess; ++j) {
         a.nl = 0;
         if (j < sh.D[1]) a.L0 = layer(sh.first(1) + j, j), a.nl = 1;
         if (j < sh.D[2]) (a.nl ? a.L1 : a.L0) = layer(sh.first(2) + j, j), a.nl += 1;
-        e = launch_deep_layers(a, desc->dtype, desc->d, st);
+        e = launch_deep_layers(a, desc->dtype, desc->d, lds, st);
     }
     if (e != hipSuccess) return e;
     // the two linear read-outs in one launch
     DeepLayer rs{}, rt{};
     rs.Wh = m->ws_out; rs.b = m->bs_out; rs.X = head_state(1); rs.Yf = a_out;
     rs.N = 1; rs.Kh = sh.last_width(1); rs.act = -1;
-    rs.blocks = deep_layer_blocks(desc->dtype, desc->Hkv, Rp, 1);
+    rs.blocks = deep_layer_blocks(desc->dtype, lds, desc->Hkv, Rp, 1);
     rt.Wh = m->Wt_out; rt.b = m->bt_out; rt.X = head_state(2); rt.Yf = A_out;
     rt.N = desc->d; rt.Kh = sh.last_width(2); rt.act = -1;
-    rt.blocks = deep_layer_blocks(desc->dtype, desc->Hkv, Rp, desc->d);
+    rt.blocks = deep_layer_blocks(desc->dtype, lds, desc->Hkv, Rp, desc->d);
     a.nl = 2; a.L0 = rs; a.L1 = rt;
-    return launch_deep_layers(a, desc->dtype, desc->d, st);
+    return launch_deep_layers(a, desc->dtype, desc->d, lds, st);
 }
 
 static nectar_status check_module(const nectar_attn_desc *desc, const nectar_module *m) {

@@ -104,13 +104,17 @@ def test_deep_mlp_full_size_decode_layer(nx, which):
     check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
 
 
-def test_deep_mlp_many_rows_sampled(nx):
-    """A batched shape (1,000 tokens x 28 heads over 4 KV heads): sampled rows."""
-    R, Hq, Hkv, d = 1000, 28, 4, 128
-    print("case deep batched R=%d" % R, flush=True)
-    shape = configs.DeepShape((0, 2, 3), (0, 128, 160))
-    P = synth.deep_mlp_params(60, Hkv, d, shape, "bf16", bias_std=0.2)
-    q = _q(61, R, Hq, d, "bf16")
+@pytest.mark.parametrize("R,Hq,Hkv,d,depth,width", [
+    (1000, 28, 4, 128, (0, 2, 3), (0, 128, 160)),
+    (150, 56, 8, 128, (2, 1, 2), (96, 64, 32)),       # 1,050 rows per KV head: a ragged 256-row block
+    (600, 16, 2, 64, (1, 1, 1), (544, 64, 96)),       # d = 64, contraction 608 = 9.5 stages
+    (300, 32, 8, 128, (0, 1, 1), (0, 32, 1024))])
+def test_deep_mlp_many_rows_sampled(nx, R, Hq, Hkv, d, depth, width):
+    """Batched shapes (the LDS-staged kernel from 1,024 rows per KV head): sampled rows."""
+    print("case deep batched R=%d Hq=%d Hkv=%d d=%d depth=%s width=%s" % (R, Hq, Hkv, d, depth, width), flush=True)
+    shape = configs.DeepShape(depth, width)
+    P = synth.deep_mlp_params(60 + R, Hkv, d, shape, "bf16", bias_std=0.2)
+    q = _q(61 + R, R, Hq, d, "bf16")
     a, A = nx.module_forward(dev(q), _module(nx, P, "silu"), Hkv)
     g = np.random.default_rng(62)
     toks = np.unique(np.concatenate([[0, R - 1], g.choice(R, 40, replace=False)])).astype(np.int32)

@@ -137,3 +137,41 @@ BY_INDEX = [C1, C2, C3, C4, C5]
 # (2, 1, 2), sized to about the capacity of the Qwen3-4B-shaped layer's
 # one-hidden-layer module (rho ~ 10 %).
 DEEP_C2 = (DeepShape((0, 2, 3), (0, 576, 576)), DeepShape((2, 1, 2), (544, 544, 544)))
+
+
+# Layer-wise capacity allocation (App. C.1, Table 10 of the notes): layer groups
+# [0, 9), [9, 15), [15, 27), [27, 28) of a 28-layer stack with multipliers
+# (1, 2, 5, 2), normalised so the total capacity stays that of the uniform
+# allocation.  The score/target study of App. C.2 uses (1, 2, 8, 12) on the same
+# groups.
+TABLE10_BOUNDS = (0, 9, 15, 27, 28)
+TABLE10_MULT = (1, 2, 5, 2)
+TABLE11_MULT = (1, 2, 8, 12)
+
+
+def layer_capacity_factors(bounds=TABLE10_BOUNDS, mult=TABLE10_MULT):
+    """Per-layer capacity factor m_l / mean(m): the group multiplier divided by its
+    layer-count-weighted mean (83/28 for Table 10), so the factors sum to the
+    layer count."""
+    sizes = [hi - lo for lo, hi in zip(bounds[:-1], bounds[1:])]
+    L = bounds[-1] - bounds[0]
+    mean = sum(n * m for n, m in zip(sizes, mult)) / L
+    return [m / mean for n, m in zip(sizes, mult) for _ in range(n)]
+
+
+def mlp_widths_for_budget(params: float, d: int, score_frac: float, multiple: int = 64):
+    """Hidden widths (Ht, Hs) of a one-hidden-layer module with about `params`
+    parameters per KV head, `score_frac` of them in the score net, each width
+    rounded to a multiple of `multiple` (at least one multiple)."""
+    def rnd(x):
+        return max(multiple, int(round(x / multiple)) * multiple)
+    pt, ps = params * (1.0 - score_frac), params * score_frac
+    return rnd((pt - d) / (2 * d + 1)), rnd((ps - 1) / (d + 2))
+
+
+def allocated_mlps(cfg: "Config", rho: float, score_frac: float, bounds=TABLE10_BOUNDS, mult=TABLE10_MULT):
+    """Per-layer module shapes of a stack at total capacity ratio `rho`
+    (|theta| / (2 n d) per layer and KV head on average), allocated by layer group."""
+    base = rho * 2.0 * cfg.n * cfg.d
+    return [MLPShape(*mlp_widths_for_budget(base * f, cfg.d, score_frac))
+            for f in layer_capacity_factors(bounds, mult)]

@@ -50,6 +50,7 @@ def _L():
         lib.oracle_full_attn.argtypes = [I, I, I, I, I, I, L, I, I, D, P, P, P, P, P, P, I, P, P, I]
         lib.oracle_mlp.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
         lib.oracle_deep_mlp.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
+        lib.oracle_fit_metrics.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
         lib.oracle_merge.argtypes = [L, I, P, P, P, P, P, P]
         lib.oracle_merge.restype = None
         lib.oracle_merge_k.argtypes = [L, I, I, P, P, P, P, P, P]
@@ -222,6 +223,24 @@ def deep_mlp(q, P, *, dt, Hq, Hkv, act="silu", toks=None, threads=0):
     if rc:
         raise ValueError("oracle_deep_mlp failed (%d)" % rc)
     return a, A
+
+
+def fit_metrics(q, a, A, alpha, Aex, *, dt, Hq, Hkv):
+    """Per-row (score squared error, target squared error, log RTE ratio)
+    [R][Hq][3] and their per-KV-head sums [Hkv][3], float64."""
+    q = _arr(q, dt)
+    d = q.shape[-1]
+    R = q.size // (Hq * d)
+    a, A, alpha, Aex = (_f64(x) for x in (a, A, alpha, Aex))
+    if a.size != R * Hq or alpha.size != R * Hq or A.size != R * Hq * d or Aex.size != R * Hq * d:
+        raise ValueError("fit_metrics: inconsistent shapes")
+    row = np.empty((R, Hq, 3)); head = np.empty((Hkv, 3))
+    with np.errstate(divide="ignore"):
+        rc = _L().oracle_fit_metrics(DT[dt], R, Hq, Hkv, d, _p(q), _p(a), _p(A), _p(alpha), _p(Aex), _p(row),
+                                     _p(head))
+    if rc:
+        raise ValueError("oracle_fit_metrics failed (%d)" % rc)
+    return row, head
 
 
 def merge(a, A, lam, Aloc):

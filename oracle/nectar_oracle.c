@@ -413,6 +413,43 @@ int oracle_deep_mlp(int dt, int R, int Hq, int Hkv, int d, int act,
 }
 
 /*
+ * Fit metrics of a module against the exact pair (the regression losses of
+ * Eqs. (3.2)-(3.3) and the RTE of Eq. (C.1), section 3.3 and App. C.4 of the
+ * notes).  For every token row r and query head h' (KV head h = h' / G):
+ *   row[0] = (a - alpha)^2                           score squared error
+ *   row[1] = || A_theta - A ||^2                     target squared error
+ *   row[2] = log( ||A_theta - A||^2 / ||q - A||^2 )  the RTE summand
+ * and per KV head the sums of each over its rows (all tokens, all its query
+ * heads): head[h][k] = sum row[k].  row [R][Hq][3], head [Hkv][3].  q is read in
+ * its storage type; the pairs are fp64.
+ */
+int oracle_fit_metrics(int dt, int R, int Hq, int Hkv, int d, const void *q,
+                       const double *a, const double *A, const double *alpha, const double *Aex,
+                       double *row, double *head)
+{
+    if (!valid_dt(dt) || !shape_ok(R, Hq, Hkv, d)) return 1;
+    const int G = Hq / Hkv;
+    for (int h = 0; h < Hkv; ++h) head[3 * h] = head[3 * h + 1] = head[3 * h + 2] = 0.0;
+    for (long r = 0; r < R; ++r)
+        for (int hq = 0; hq < Hq; ++hq) {
+            size_t i = (size_t)r * Hq + hq;
+            double es = (a[i] - alpha[i]) * (a[i] - alpha[i]);
+            double et = 0.0, eq = 0.0;
+            for (int c = 0; c < d; ++c) {
+                double x = A[i * d + c] - Aex[i * d + c];
+                double y = ld(q, dt, i * d + c) - Aex[i * d + c];
+                et += x * x;
+                eq += y * y;
+            }
+            double lr = log(et / eq);
+            row[3 * i] = es; row[3 * i + 1] = et; row[3 * i + 2] = lr;
+            int h = hq / G;
+            head[3 * h] += es; head[3 * h + 1] += et; head[3 * h + 2] += lr;
+        }
+    return 0;
+}
+
+/*
  * Log-sum-exp merge of two (lse, read-out) pairs, Eqs. (3.4)-(3.5): the first
  * pair is the document part (exact alpha, A or the module's a, A), used as one
  * extra "virtual logit" with value A beside the local part (lse_loc, A_loc):

@@ -626,3 +626,39 @@ def test_deep_mlp_gqa_and_token_subset():
     assert np.max(np.abs(a3[:, 3] - a3[:, 1])) > 1e-6
     at, At = oracle.deep_mlp(q, P, dt="f64", Hq=Hq, Hkv=Hkv, toks=[4, 1])
     assert np.all(at[0] == a[4]) and np.all(At[1] == A[1])
+
+
+# --- Fit metrics: Eqs. (3.2)-(3.3) squared errors and the RTE of Eq. (C.1) ---------
+
+def test_fit_metrics_hand_worked_and_closed_forms():
+    # d = 2, one head: q = (1, 0), exact A = (0, 0), module A = (0, 3): ||A_th - A||^2 = 9,
+    # ||q - A||^2 = 1, so the RTE summand is log 9; a = 1 against alpha = -1 gives 4.
+    row, head = oracle.fit_metrics(np.array([[[1.0, 0.0]]]), np.array([[1.0]]), np.array([[[0.0, 3.0]]]),
+                                   np.array([[-1.0]]), np.array([[[0.0, 0.0]]]), dt="f64", Hq=1, Hkv=1)
+    assert row[0, 0, 0] == 4.0 and row[0, 0, 1] == 9.0 and abs(row[0, 0, 2] - math.log(9.0)) < 1e-15
+    assert np.all(head[0] == row[0, 0])
+    R, Hq, Hkv, d = 5, 6, 2, 8
+    q = _rand(R, Hq, d)
+    Aex = _rand(R, Hq, d)
+    alpha = _rand(R, Hq)
+    # the query itself as the module's target: ratio 1, summand 0
+    row, _ = oracle.fit_metrics(q, alpha, q, alpha, Aex, dt="f64", Hq=Hq, Hkv=Hkv)
+    assert np.all(row[..., 0] == 0.0) and np.max(np.abs(row[..., 2])) < 1e-14
+    # A_th - A = c (q - A): summand 2 log |c|
+    for c in (0.5, -3.0):
+        row, _ = oracle.fit_metrics(q, alpha, Aex + c * (q - Aex), alpha, Aex, dt="f64", Hq=Hq, Hkv=Hkv)
+        assert np.max(np.abs(row[..., 2] - 2 * math.log(abs(c)))) < 1e-13
+    # an exact module: zero errors and a summand of -inf
+    row, _ = oracle.fit_metrics(q, alpha, Aex, alpha, Aex, dt="f64", Hq=Hq, Hkv=Hkv)
+    assert np.all(row[..., :2] == 0.0) and np.all(row[..., 2] == -np.inf)
+
+
+def test_fit_metrics_head_sums_follow_the_gqa_groups():
+    R, Hq, Hkv, d = 4, 6, 3, 4
+    q, A, Aex = _rand(R, Hq, d), _rand(R, Hq, d), _rand(R, Hq, d)
+    a, alpha = _rand(R, Hq), _rand(R, Hq)
+    row, head = oracle.fit_metrics(q, a, A, alpha, Aex, dt="f64", Hq=Hq, Hkv=Hkv)
+    for h in range(Hkv):
+        np.testing.assert_allclose(head[h], row[:, 2 * h:2 * h + 2].reshape(-1, 3).sum(0), rtol=1e-14)
+    # squared errors are sums over the dimensions (not means)
+    np.testing.assert_allclose(row[..., 1], ((A - Aex) ** 2).sum(-1), rtol=1e-14)

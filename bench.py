@@ -281,6 +281,8 @@ def main():
     if not args.no_prefill and args.only is None:
         res["prefill_mlp"] = prefill_mlp(torch, np, nectar, configs, synth, dev)
         res["merge_k"] = merge_k_prefill(torch, nectar, configs, dev)
+        res["fit_metrics"] = fit_metrics_prefill(torch, nectar, configs, dev)
+        res["deep_modules"] = deep_modules(torch, nectar, configs, dev)
     if not args.no_workloads and args.only is None:
         res["workloads"] = {c.name: workload_layer(torch, nectar, c, dev) for c in (configs.C4, configs.C5, configs.C3)}
 
@@ -482,6 +484,107 @@ def merge_k_prefill(torch, nectar, configs, dev, K=4):
     torch.cuda.empty_cache()
     return {"K": K, "rows": R * Hq, "us": us, "bytes_per_launch": nbytes, "gbs": nbytes / us / 1e3,
             "frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "bound": "hbm"}
+
+
+def _graph_us(torch, call, reps=8, replays=4):
+    call()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(reps):
+            call()
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * replays) * 1e3
+
+
+def deep_modules(torch, nectar, configs, dev):
+    """The deep re-injection modules of Eq. (3.6) in the depth shapes (0, 2, 3)
+    and (2, 1, 2) at about 10 % capacity of the Qwen3-4B-shaped layer: the
+    decode-step forward (one token x 32 heads; 16 module replicas rotate so the
+    weights stream from HBM; roofline = weight bytes) and the 16 x 1,024-token
+    prefill forward of the 7B-shaped layer (roofline = MFMA flops).  Weights
+    N(0, 1/fan_in) from a seeded device generator, zero biases, SiLU."""
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(79)
+
+    def module(Hkv, d, shape):
+        bf = lambda *s_, std: (torch.randn(*s_, generator=g, device=dev) * std).to(torch.bfloat16)
+        layers = [(bf(Hkv, H, d, std=(d + H_in) ** -0.5), bf(Hkv, H, H_in, std=(d + H_in) ** -0.5) if H_in else None,
+                   torch.zeros(Hkv, H, device=dev)) for H, H_in in shape.layers()]
+        Hs, Ht = shape.last_width(1), shape.last_width(2)
+        return nectar.DeepMLPModule(shape.depth, shape.width, layers, bf(Hkv, Hs, std=Hs ** -0.5),
+                                    torch.zeros(Hkv, device=dev), bf(Hkv, d, Ht, std=Ht ** -0.5),
+                                    torch.zeros(Hkv, d, device=dev))
+
+    for shape in configs.DEEP_C2:
+        key = "d%d%d%d" % tuple(shape.depth)
+        res = {"depth": list(shape.depth), "width": list(shape.width)}
+        for cfg, nrep in ((configs.C2, 16), (configs.C3, 1)):
+            d, Hkv, Hq, R = cfg.d, cfg.Hkv, cfg.Hq, cfg.R
+            q = torch.randn(R, Hq, d, generator=g, device=dev).to(torch.bfloat16)
+            a = torch.empty(R, Hq, device=dev)
+            A = torch.empty(R, Hq, d, device=dev)
+            mods = [module(Hkv, d, shape) for _ in range(nrep)]
+            i = [0]
+
+            def call():
+                nectar.module_forward(q, mods[i[0] % nrep], Hkv, a_out=a, A_out=A)
+                i[0] += 1
+            P = shape.params(d)
+            if cfg.prefill:
+                call()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(3):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / 3 * 1e3
+                tf = 2.0 * R * Hq * P / us / 1e6
+                res["prefill_c3"] = {"us": us, "tflops": tf, "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS, "bound": "mfma",
+                                     "flops": 2.0 * R * Hq * P}
+            else:
+                us = _graph_us(torch, call, reps=nrep, replays=4)
+                nb = Hkv * P * 2
+                res["decode_c2"] = {"us": us, "params_per_head": P, "rho": cfg.rho(P), "gbs": nb / us / 1e3,
+                                    "frac": nb / us / 1e3 / HBM_PEAK_GBS, "bound": "hbm", "bytes": nb}
+            del mods, q, a, A
+            torch.cuda.empty_cache()
+        out[key] = res
+    return out
+
+
+def fit_metrics_prefill(torch, nectar, configs, dev):
+    """HBM roofline of the fit metrics (squared errors and the RTE summand of a
+    module pair against the exact pair, with per-KV-head sums) at the
+    16 x 1,024-token prefill shape: q (bf16), both pairs (fp32) in, the per-row
+    values out."""
+    cfg = configs.C3
+    R, Hq, d = cfg.R, cfg.Hq, cfg.d
+    g = torch.Generator(device=dev)
+    g.manual_seed(78)
+    f32 = dict(dtype=torch.float32, device=dev)
+    rn = lambda *s: torch.randn(*s, generator=g, **f32)
+    q = rn(R, Hq, d).to(torch.bfloat16)
+    a, alpha, A, Aex = rn(R, Hq), rn(R, Hq), rn(R, Hq, d), rn(R, Hq, d)
+    row = torch.empty((R, Hq, 3), **f32)
+    head = torch.empty((cfg.Hkv, 3), dtype=torch.float64, device=dev)
+    us = _graph_us(torch, lambda: nectar.fit_metrics(q, a, A, alpha, Aex, cfg.Hkv, row_out=row, head_out=head))
+    nbytes = R * Hq * (2 * d + 2 * 4 * d + 2 * 4 + 3 * 4)
+    del q, a, alpha, A, Aex, row, head
+    torch.cuda.empty_cache()
+    return {"rows": R * Hq, "us": us, "bytes_per_call": nbytes, "gbs": nbytes / us / 1e3,
+            "frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "bound": "hbm",
+            "what": "nectar_fit_metrics: row pass + per-KV-head fp64 sums (three launches)"}
 
 
 def cpu_baseline(cfg, q, K, V, Kl, Vl, P, budget_s):

@@ -18,6 +18,8 @@
  *                           section 2.2, optionally merged with a document pair
  *   nectar_merge            the log-sum-exp merge of Eqs. (3.4)-(3.5)
  *   nectar_merge_k          the same over K document-side pairs
+ *   nectar_fit_metrics      squared errors and the RTE of a module against the
+ *                           exact pair (Eqs. (3.2)-(3.3), (C.1))
  *   nectar_layer_step       all of the above for one layer step, fused
  *
  * Conventions shared by every entry point
@@ -274,6 +276,33 @@ NECTAR_API nectar_status nectar_merge(const nectar_attn_desc *desc, const float 
 NECTAR_API nectar_status nectar_merge_k(const nectar_attn_desc *desc, int K, const float *const *a,
                              const float *const *A, const float *lam, const float *A_loc,
                              void *out, float *lse_out, void *stream);
+
+/*
+ * Fit metrics of a module pair (a, A_theta) against the exact pair (alpha, A):
+ * the squared errors whose sums over heads and tokens are the regression losses
+ * of Eqs. (3.2)-(3.3) (section 2.3 of the notes), and the summand of the
+ * relative target error of Eq. (C.1) (App. C.4), which measures the target
+ * error against the error of using the query itself as the target.  Per row
+ * (token r, query head h'):
+ *   row_out[r][h'][0] = (a - alpha)^2
+ *   row_out[r][h'][1] = ||A_theta - A||^2             (a sum over the d dimensions)
+ *   row_out[r][h'][2] = log(||A_theta - A||^2 / ||q - A||^2)
+ * (IEEE semantics: a zero target error gives -inf, q == A gives +inf).
+ * head_out[h][k] (fp64, nullable) = the sum of row_out[.][.][k] over the rows of
+ * KV head h (every token, every query head of its group), summed in a fixed
+ * order; the score and target MSE of a layer are these sums over the heads
+ * divided by the row count R * Hq, its RTE term is sum_h head_out[h][2] / (R * G).
+ *   q [R][Hq][d] (desc->dtype); a, alpha [R][Hq], A, A_exact [R][Hq][d] (fp32);
+ *   row_out [R][Hq][3] fp32: caller-owned, required (it also carries the
+ *   per-row values to the head sums);
+ *   ws: nectar_fit_metrics_workspace_size bytes (16-byte aligned) when head_out
+ *   is given, else unused.
+ */
+NECTAR_API size_t nectar_fit_metrics_workspace_size(const nectar_attn_desc *desc);
+NECTAR_API nectar_status nectar_fit_metrics(const nectar_attn_desc *desc, const void *q, const float *a,
+                                 const float *A, const float *alpha, const float *A_exact,
+                                 float *row_out, double *head_out, void *ws, size_t ws_bytes,
+                                 void *stream);
 
 /*
  * One layer step of both paths, fused (sections 2.1-2.2; the step loop of a

@@ -87,6 +87,19 @@ struct DeepParams {
     DeepLayer L0, L1;
 };
 
+// Fit metrics: per row (R * Hq rows) the score squared error, the target
+// squared error and the log RTE ratio, [rows][3]; per KV head their fp64 sums.
+constexpr int kFitParts = 64;      // partial sums per KV head
+struct FitParams {
+    const void *q;
+    const float *a, *A, *alpha, *Aex;
+    float *row;
+    double *head;      // nullable
+    double *part;      // [Hkv][kFitParts][3] workspace when head != nullptr
+    long rows;
+    int Hq, Hkv;
+};
+
 // One document-side part of a layer step, finished together with the local
 // part: split partials of the exact document attention or of a Quadrature
 // module (log-sum-exp form: ml != NULL) or of an MLP module (plain sums:
@@ -168,6 +181,7 @@ hipError_t launch_mlp_rows_lds32(const MlpParams &p, hipStream_t st);
 hipError_t launch_mlp_prefill(const MlpParams &p, hipStream_t st);
 hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_merge_k(const MergeKParams &p, int dtype, int d, hipStream_t st);
+hipError_t launch_fit_metrics(const FitParams &p, int dtype, int d, hipStream_t st);
 // Blocks of one deep-MLP layer for the launch shape of the given dtype (lds:
 // the LDS-staged kernel for many rows per KV head).
 long deep_layer_blocks(int dtype, int lds, int Hkv, int Rp, int N);

@@ -621,6 +621,32 @@ nectar_status nectar_merge_k(const nectar_attn_desc *desc, int K, const float *c
     return finish(launch_merge_k(p, desc->dtype, desc->d, st), st);
 }
 
+size_t nectar_fit_metrics_workspace_size(const nectar_attn_desc *desc) {
+    if (check_desc(desc) != NECTAR_OK) return 0;
+    return (size_t)desc->Hkv * kFitParts * 3 * sizeof(double);
+}
+
+nectar_status nectar_fit_metrics(const nectar_attn_desc *desc, const void *q, const float *a, const float *A,
+                                 const float *alpha, const float *A_exact, float *row_out, double *head_out,
+                                 void *ws, size_t ws_bytes, void *stream) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if (desc->R == 0) return NECTAR_OK;
+    if (!tensor_ok(q) || !f32_ok(a) || !f32_ok(alpha) || !rows_ok(A) || !rows_ok(A_exact) || !f32_ok(row_out))
+        return NECTAR_EINVAL;
+    if (head_out) {
+        if (!aligned(head_out, 8)) return NECTAR_EINVAL;
+        if ((s = check_ws(nectar_fit_metrics_workspace_size(desc), ws, ws_bytes)) != NECTAR_OK) return s;
+    }
+    FitParams p{};
+    p.q = q; p.a = a; p.A = A; p.alpha = alpha; p.Aex = A_exact;
+    p.row = row_out; p.head = head_out; p.part = (double *)ws;
+    p.rows = (long)desc->R * desc->Hq;
+    p.Hq = desc->Hq; p.Hkv = desc->Hkv;
+    hipStream_t st = (hipStream_t)stream;
+    return finish(launch_fit_metrics(p, desc->dtype, desc->d, st), st);
+}
+
 // ---------------------------------------------------------------------------
 // Whole layer step: deferred partials of every part, one finishing pass.
 

@@ -81,6 +81,9 @@ _lib.nectar_local_workspace_size.restype = ctypes.c_size_t
 _lib.nectar_local_attn_lse.argtypes = [_D, ctypes.POINTER(LocalDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, ctypes.c_size_t, _P]
 _lib.nectar_merge.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P]
+_lib.nectar_fit_metrics.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.nectar_fit_metrics_workspace_size.argtypes = [_D]
+_lib.nectar_fit_metrics_workspace_size.restype = ctypes.c_size_t
 _lib.nectar_merge_k.argtypes = [_D, ctypes.c_int, ctypes.POINTER(_P), ctypes.POINTER(_P), _P, _P, _P, _P, _P]
 _lib.nectar_doc_attn_partials_size.argtypes = [_D, ctypes.c_int64]
 _lib.nectar_doc_attn_partials_size.restype = ctypes.c_size_t
@@ -97,7 +100,7 @@ _lib.nectar_abi_version.restype = ctypes.c_int
 _lib.nectar_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.nectar_workspace_init.restype = ctypes.c_int
 for _f in ("nectar_doc_attn_exact", "nectar_module_forward", "nectar_local_attn_lse", "nectar_merge",
-           "nectar_merge_k", "nectar_layer_step", "nectar_doc_attn_partials", "nectar_doc_attn_combine"):
+           "nectar_merge_k", "nectar_fit_metrics", "nectar_layer_step", "nectar_doc_attn_partials", "nectar_doc_attn_combine"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -376,6 +379,21 @@ def merge_k(pairs, lam=None, A_loc=None, *, Hkv, out_dtype, out=None, lse_out=No
     _check(_lib.nectar_merge_k(ctypes.byref(dsc), K, pa, pA, _ptr(lam), _ptr(A_loc), _ptr(out),
                                _ptr(lse_out), _stream()))
     return out, lse_out
+
+
+def fit_metrics(q, a, A, alpha, A_exact, Hkv, *, row_out=None, head_out=None):
+    """Per row (a - alpha)^2, ||A - A_exact||^2, log(||A - A_exact||^2 / ||q - A_exact||^2)
+    ([R][Hq][3] fp32) and their per-KV-head sums ([Hkv][3] fp64)."""
+    R, Hq, d = q.shape
+    dsc = desc(R, Hq, Hkv, d, dtype_code(q))
+    if row_out is None:
+        row_out = torch.empty((R, Hq, 3), dtype=torch.float32, device=q.device)
+    if head_out is None:
+        head_out = torch.empty((Hkv, 3), dtype=torch.float64, device=q.device)
+    wp, wn = _ws_args(int(_lib.nectar_fit_metrics_workspace_size(ctypes.byref(dsc))), q.device)
+    _check(_lib.nectar_fit_metrics(ctypes.byref(dsc), _ptr(q), _ptr(a), _ptr(A), _ptr(alpha), _ptr(A_exact),
+                                   _ptr(row_out), _ptr(head_out), wp, wn, _stream()))
+    return row_out, head_out
 
 
 def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, module=None,

@@ -68,6 +68,9 @@ def lib():
     L.nectar_local_workspace_size.restype = ctypes.c_size_t
     L.nectar_local_attn_lse.argtypes = [D, ctypes.POINTER(Local)] + [P] * 9 + [P, ctypes.c_size_t, P]
     L.nectar_merge.argtypes = [D] + [P] * 7
+    L.nectar_fit_metrics.argtypes = [D] + [P] * 8 + [ctypes.c_size_t, P]
+    L.nectar_fit_metrics_workspace_size.argtypes = [D]
+    L.nectar_fit_metrics_workspace_size.restype = ctypes.c_size_t
     L.nectar_merge_k.argtypes = [D, ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P)] + [P] * 5
     L.nectar_layer_step_workspace_size.argtypes = [D, ctypes.c_int64, ctypes.POINTER(Local),
                                                     ctypes.POINTER(Module), ctypes.c_int]
@@ -90,7 +93,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
     assert lib.nectar_abi_version() == 2
@@ -308,6 +311,24 @@ def test_merge_k_validation(lib):
     assert call(2, *two, A16, A16, out=None) == EINVAL
     d0 = Desc(0, 8, 2, 128, 1, 0.0, 0)
     assert call(2, *two, None, None, out=None, dd=d0) == OK                  # no rows: a no-op
+
+
+def test_fit_metrics_validation(lib):
+    d = Desc(2, 8, 2, 128, 1, 0.0, 0)
+    call = lambda dd=d, q=A16, a=A16, A=A16, al=A16, Ae=A16, row=A16, head=A16, ws=A16, wsb=1 << 20: \
+        lib.nectar_fit_metrics(ctypes.byref(dd) if dd is not None else None, q, a, A, al, Ae, row, head, ws, wsb,
+                               None)
+    need = lib.nectar_fit_metrics_workspace_size(ctypes.byref(d))
+    assert need == 2 * 64 * 3 * 8
+    assert call(wsb=need - 1) == EWORKSPACE
+    assert call(dd=None) == EINVAL
+    assert call(q=MIS) == EINVAL
+    assert call(A=A16 + 4) == EINVAL            # d-vectors are 16-byte aligned
+    assert call(Ae=None) == EINVAL
+    assert call(row=None) == EINVAL
+    assert call(head=A16 + 4) == EINVAL          # fp64 sums
+    assert call(dd=Desc(2, 8, 2, 96, 1, 0.0, 0)) == EUNSUPPORTED
+    assert call(dd=Desc(0, 8, 2, 128, 1, 0.0, 0), q=None, a=None, A=None, al=None, Ae=None, row=None) == OK
 
 
 def test_oracle_and_product_share_no_code():

@@ -51,6 +51,11 @@ def _L():
         lib.oracle_mlp.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
         lib.oracle_deep_mlp.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
         lib.oracle_fit_metrics.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.oracle_act_grad.argtypes = [I, D]
+        lib.oracle_act_grad.restype = D
+        lib.oracle_mlp_loss_grad.argtypes = [I, I, I, I, I, I, I, I] + [P] * 11 + [D, D] + [P] * 9
+        lib.oracle_adamw.argtypes = [L, P, P, P, P, D, D, D, D, D, I, D]
+        lib.oracle_adamw.restype = None
         lib.oracle_merge.argtypes = [L, I, P, P, P, P, P, P]
         lib.oracle_merge.restype = None
         lib.oracle_merge_k.argtypes = [L, I, I, P, P, P, P, P, P]
@@ -241,6 +246,43 @@ def fit_metrics(q, a, A, alpha, Aex, *, dt, Hq, Hkv):
     if rc:
         raise ValueError("oracle_fit_metrics failed (%d)" % rc)
     return row, head
+
+
+MLP_PARAMS = ("W1", "b1", "W2t", "b2", "Ws", "bs", "ws2", "bs2")
+
+
+def mlp_loss_grad(q, P, alpha, A_target, *, dt, Hq, Hkv, act="gelu", lam_alpha=0.1, lam_A=1.0):
+    """Regression loss (L, L_alpha, L_A) of the one-hidden-layer module P (dict of
+    W1, b1, W2t, b2, Ws, bs, ws2, bs2) against the targets, and its gradient
+    (dict of float64 arrays with the parameters' shapes)."""
+    q = _arr(q, dt)
+    d = q.shape[-1]
+    R = q.size // (Hq * d)
+    W = {k: (_arr(P[k], dt) if k in ("W1", "W2t", "Ws", "ws2") else _f64(P[k])) for k in MLP_PARAMS}
+    Ht, Hs = W["W1"].size // (Hkv * d), W["Ws"].size // (Hkv * d)
+    alpha, A_target = _f64(alpha), _f64(A_target)
+    if alpha.size != R * Hq or A_target.size != R * Hq * d:
+        raise ValueError("mlp_loss_grad: inconsistent target shapes")
+    g = {k: np.zeros(np.shape(P[k])) for k in MLP_PARAMS}
+    loss = np.zeros(3)
+    rc = _L().oracle_mlp_loss_grad(DT[dt], R, Hq, Hkv, d, Ht, Hs, ACT[act], *[_p(W[k]) for k in MLP_PARAMS],
+                                   _p(q), _p(alpha), _p(A_target), float(lam_alpha), float(lam_A),
+                                   *[_p(g[k]) for k in MLP_PARAMS], _p(loss))
+    if rc:
+        raise ValueError("oracle_mlp_loss_grad failed (%d)" % rc)
+    return loss, g
+
+
+def act_grad(act: str, x: float) -> float:
+    return _L().oracle_act_grad(ACT[act], float(x))
+
+
+def adamw(theta, g, m, v, *, lr, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, step=1, scale=1.0):
+    """One AdamW step on float64 copies; returns (theta, m, v)."""
+    theta, m, v = (np.array(x, dtype=np.float64, copy=True) for x in (theta, m, v))
+    g = _f64(g)
+    _L().oracle_adamw(theta.size, _p(theta), _p(g), _p(m), _p(v), lr, b1, b2, eps, wd, int(step), scale)
+    return theta, m, v
 
 
 def merge(a, A, lam, Aloc):

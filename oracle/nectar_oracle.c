@@ -89,6 +89,25 @@ static double act_fn(int act, double x)
     return oracle_gelu(x);
 }
 
+/* Derivatives of the activations, written from their definitions:
+ *   GELU(x) = x Phi(x):           Phi(x) + x phi(x)
+ *   SiLU(x) = x s(x), s sigmoid:  s(x) (1 + x (1 - s(x)))
+ *   tanh form 0.5 x (1 + tanh u), u = c (x + k x^3):
+ *                                  0.5 (1 + tanh u) + 0.5 x (1 - tanh^2 u) c (1 + 3 k x^2) */
+double oracle_act_grad(int act, double x)
+{
+    if (act == OR_SILU) {
+        double sg = 1.0 / (1.0 + exp(-x));
+        return sg * (1.0 + x * (1.0 - sg));
+    }
+    if (act == OR_GELU_TANH) {
+        const double c = sqrt(2.0 / M_PI), k = 0.044715;
+        double t = tanh(c * (x + k * x * x * x));
+        return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * k * x * x);
+    }
+    return 0.5 * (1.0 + erf(x / sqrt(2.0))) + x * exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+}
+
 /*
  * Attention of one query vector over a set of key/value rows, returning the
  * log of the sum of exponentiated scores and the normalized read-out.
@@ -447,6 +466,127 @@ int oracle_fit_metrics(int dt, int R, int Hq, int Hkv, int d, const void *q,
             head[3 * h] += es; head[3 * h + 1] += et; head[3 * h + 2] += lr;
         }
     return 0;
+}
+
+/*
+ * Regression loss of the one-hidden-layer module and its gradient (section 2.3,
+ * Eqs. (3.2)-(3.3)): over the R token rows of one layer,
+ *   L_alpha = (1/R) sum_r sum_h' (a(q) - alpha)^2,
+ *   L_A     = (1/R) sum_r sum_h' ||A(q) - A_target||^2,
+ *   L       = lambda_alpha L_alpha + lambda_A L_A
+ * (the expectation over samples is the mean over tokens; the sum runs over the
+ * query heads).  loss[0..2] = L, L_alpha, L_A.  The gradient of L with respect
+ * to each parameter array (same layouts as oracle_mlp) is written to the fp64
+ * arrays gW1 .. gbs2, by the chain rule written out per row:
+ *   gA = 2 lambda_A (A - A_target) / R,  ga = 2 lambda_alpha (a - alpha) / R,
+ *   target unit j: dz_j = act'(z_j) sum_c W2t[j][c] gA_c; dW2t[j][c] += act(z_j) gA_c,
+ *                  dW1[j][c] += dz_j q_c, db1[j] += dz_j; db2 += gA;
+ *   score unit j:  dzs_j = act'(zs_j) ws2[j] ga; dws2[j] += act(zs_j) ga,
+ *                  dWs[j][c] += dzs_j q_c, dbs[j] += dzs_j; dbs2 += ga.
+ * Rows are accumulated in order (single thread), so the result is reproducible.
+ */
+int oracle_mlp_loss_grad(int dt, int R, int Hq, int Hkv, int d, int Ht, int Hs, int act,
+                         const void *W1, const double *b1, const void *W2t, const double *b2,
+                         const void *Ws, const double *bs, const void *ws2, const double *bs2,
+                         const void *q, const double *alpha, const double *Atgt,
+                         double lam_alpha, double lam_A,
+                         double *gW1, double *gb1, double *gW2t, double *gb2,
+                         double *gWs, double *gbs, double *gws2, double *gbs2, double *loss)
+{
+    if (!valid_dt(dt) || !shape_ok(R, Hq, Hkv, d) || Ht < 0 || Hs < 0 || R <= 0) return 1;
+    if (act != OR_GELU && act != OR_SILU && act != OR_GELU_TANH) return 1;
+    const int G = Hq / Hkv;
+    memset(gW1, 0, sizeof(double) * (size_t)Hkv * Ht * d);
+    memset(gb1, 0, sizeof(double) * (size_t)Hkv * Ht);
+    memset(gW2t, 0, sizeof(double) * (size_t)Hkv * Ht * d);
+    memset(gb2, 0, sizeof(double) * (size_t)Hkv * d);
+    memset(gWs, 0, sizeof(double) * (size_t)Hkv * Hs * d);
+    memset(gbs, 0, sizeof(double) * (size_t)Hkv * Hs);
+    memset(gws2, 0, sizeof(double) * (size_t)Hkv * Hs);
+    memset(gbs2, 0, sizeof(double) * (size_t)Hkv);
+    double *z = (double *)malloc(sizeof(double) * (size_t)(Ht > Hs ? Ht : Hs) + 8);
+    double *A = (double *)malloc(sizeof(double) * (size_t)d);
+    double *gA = (double *)malloc(sizeof(double) * (size_t)d);
+    double La = 0.0, LA = 0.0;
+    for (long r = 0; r < R; ++r)
+        for (int hq = 0; hq < Hq; ++hq) {
+            const int h = hq / G;
+            const size_t qo = ((size_t)r * Hq + hq) * d, i = (size_t)r * Hq + hq;
+            /* forward */
+            for (int c = 0; c < d; ++c) A[c] = b2[(size_t)h * d + c];
+            for (int j = 0; j < Ht; ++j) {
+                size_t wo = ((size_t)h * Ht + j) * d;
+                double zz = b1[(size_t)h * Ht + j];
+                for (int c = 0; c < d; ++c) zz += ld(W1, dt, wo + c) * ld(q, dt, qo + c);
+                z[j] = zz;
+                double y = act_fn(act, zz);
+                for (int c = 0; c < d; ++c) A[c] += ld(W2t, dt, wo + c) * y;
+            }
+            for (int c = 0; c < d; ++c) {
+                double e = A[c] - Atgt[i * d + c];
+                LA += e * e;
+                gA[c] = 2.0 * lam_A * e / R;
+            }
+            /* target backward */
+            for (int c = 0; c < d; ++c) gb2[(size_t)h * d + c] += gA[c];
+            for (int j = 0; j < Ht; ++j) {
+                size_t wo = ((size_t)h * Ht + j) * d;
+                double y = act_fn(act, z[j]), dy = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    dy += ld(W2t, dt, wo + c) * gA[c];
+                    gW2t[wo + c] += y * gA[c];
+                }
+                double dz = dy * oracle_act_grad(act, z[j]);
+                gb1[(size_t)h * Ht + j] += dz;
+                for (int c = 0; c < d; ++c) gW1[wo + c] += dz * ld(q, dt, qo + c);
+            }
+            /* score forward and backward */
+            double a = bs2[h];
+            for (int j = 0; j < Hs; ++j) {
+                size_t wo = ((size_t)h * Hs + j) * d;
+                double zz = bs[(size_t)h * Hs + j];
+                for (int c = 0; c < d; ++c) zz += ld(Ws, dt, wo + c) * ld(q, dt, qo + c);
+                z[j] = zz;
+                a += ld(ws2, dt, (size_t)h * Hs + j) * act_fn(act, zz);
+            }
+            double e = a - alpha[i];
+            La += e * e;
+            double ga = 2.0 * lam_alpha * e / R;
+            gbs2[h] += ga;
+            for (int j = 0; j < Hs; ++j) {
+                size_t wo = ((size_t)h * Hs + j) * d;
+                gws2[(size_t)h * Hs + j] += act_fn(act, z[j]) * ga;
+                double dz = ld(ws2, dt, (size_t)h * Hs + j) * ga * oracle_act_grad(act, z[j]);
+                gbs[(size_t)h * Hs + j] += dz;
+                for (int c = 0; c < d; ++c) gWs[wo + c] += dz * ld(q, dt, qo + c);
+            }
+        }
+    free(z); free(A); free(gA);
+    loss[1] = La / R;
+    loss[2] = LA / R;
+    loss[0] = lam_alpha * loss[1] + lam_A * loss[2];
+    return 0;
+}
+
+/*
+ * One AdamW step (Loshchilov & Hutter's decoupled weight decay; the notes'
+ * optimizer, App. A.2-A.5) on n parameters with the gradient scaled by `scale`
+ * (the global-norm clipping factor):
+ *   theta <- theta (1 - lr wd);  g' = scale g;
+ *   m <- b1 m + (1 - b1) g';  v <- b2 v + (1 - b2) g'^2;
+ *   theta <- theta - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps),  t = step >= 1.
+ */
+void oracle_adamw(long n, double *theta, const double *g, double *m, double *v, double lr, double b1,
+                  double b2, double eps, double wd, int step, double scale)
+{
+    const double c1 = 1.0 - pow(b1, step), c2 = 1.0 - pow(b2, step);
+    for (long i = 0; i < n; ++i) {
+        const double gi = scale * g[i];
+        theta[i] *= 1.0 - lr * wd;
+        m[i] = b1 * m[i] + (1.0 - b1) * gi;
+        v[i] = b2 * v[i] + (1.0 - b2) * gi * gi;
+        theta[i] -= lr * (m[i] / c1) / (sqrt(v[i] / c2) + eps);
+    }
 }
 
 /*

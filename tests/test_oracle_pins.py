@@ -662,3 +662,82 @@ def test_fit_metrics_head_sums_follow_the_gqa_groups():
         np.testing.assert_allclose(head[h], row[:, 2 * h:2 * h + 2].reshape(-1, 3).sum(0), rtol=1e-14)
     # squared errors are sums over the dimensions (not means)
     np.testing.assert_allclose(row[..., 1], ((A - Aex) ** 2).sum(-1), rtol=1e-14)
+
+
+# --- Training step: loss of Eqs. (3.2)-(3.3), its gradient, AdamW ----------------
+
+@pytest.mark.parametrize("act", ["gelu", "silu", "gelu_tanh"])
+def test_activation_derivatives_match_central_differences(act):
+    f = {"gelu": oracle.gelu, "silu": oracle.silu, "gelu_tanh": oracle.gelu_tanh}[act]
+    h = 1e-5
+    for x in (-6.0, -2.5, -1.0, -0.3, 0.0, 0.4, 1.0, 2.2, 7.0):
+        fd = (f(x + h) - f(x - h)) / (2 * h)
+        assert abs(oracle.act_grad(act, x) - fd) < 1e-9
+    assert abs(oracle.act_grad("gelu", 0.0) - 0.5) < 1e-15 and abs(oracle.act_grad("silu", 0.0) - 0.5) < 1e-15
+
+
+def _train_case(Hkv=2, Hq=4, d=6, Ht=5, Hs=3, R=3, bias=0.4):
+    P = dict(W1=_rand(Hkv, Ht, d, scale=d ** -0.5), b1=_rand(Hkv, Ht, scale=bias),
+             W2t=_rand(Hkv, Ht, d, scale=Ht ** -0.5), b2=_rand(Hkv, d, scale=bias),
+             Ws=_rand(Hkv, Hs, d, scale=d ** -0.5), bs=_rand(Hkv, Hs, scale=bias),
+             ws2=_rand(Hkv, Hs, scale=Hs ** -0.5), bs2=_rand(Hkv, scale=bias))
+    q = _rand(R, Hq, d)
+    alpha = _rand(R, Hq)
+    At = _rand(R, Hq, d)
+    return P, q, alpha, At
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+def test_loss_is_the_mean_over_tokens_of_the_summed_squared_errors(act):
+    Hkv, Hq = 2, 4
+    P, q, alpha, At = _train_case()
+    loss, _ = oracle.mlp_loss_grad(q, P, alpha, At, dt="f64", Hq=Hq, Hkv=Hkv, act=act, lam_alpha=0.1, lam_A=1.0)
+    a, A = _run_mlp(q, P, Hq, Hkv, act)          # the forward pinned by P10
+    R = q.shape[0]
+    La = ((a - alpha) ** 2).sum() / R
+    LA = ((A - At) ** 2).sum() / R
+    assert abs(loss[1] - La) < 1e-13 and abs(loss[2] - LA) < 1e-13
+    assert abs(loss[0] - (0.1 * La + LA)) < 1e-13
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu", "gelu_tanh"])
+def test_gradient_matches_central_differences_of_the_loss(act):
+    Hkv, Hq = 2, 4
+    P, q, alpha, At = _train_case()
+    _, g = oracle.mlp_loss_grad(q, P, alpha, At, dt="f64", Hq=Hq, Hkv=Hkv, act=act, lam_alpha=0.3, lam_A=0.7)
+    h = 1e-6
+    for k in oracle.MLP_PARAMS:
+        flat = P[k].reshape(-1)
+        for idx in rng.choice(flat.size, min(6, flat.size), replace=False):
+            Pp = {kk: vv.copy() for kk, vv in P.items()}
+            Pm = {kk: vv.copy() for kk, vv in P.items()}
+            Pp[k].reshape(-1)[idx] += h
+            Pm[k].reshape(-1)[idx] -= h
+            lp, _ = oracle.mlp_loss_grad(q, Pp, alpha, At, dt="f64", Hq=Hq, Hkv=Hkv, act=act, lam_alpha=0.3,
+                                         lam_A=0.7)
+            lm, _ = oracle.mlp_loss_grad(q, Pm, alpha, At, dt="f64", Hq=Hq, Hkv=Hkv, act=act, lam_alpha=0.3,
+                                         lam_A=0.7)
+            fd = (lp[0] - lm[0]) / (2 * h)
+            assert abs(g[k].reshape(-1)[idx] - fd) < 1e-7 * max(1.0, abs(fd)), (k, idx)
+
+
+def test_adamw_closed_forms():
+    g = np.array([0.3, -2.0, 1e-3, 0.0])
+    theta = np.array([1.0, -1.0, 0.5, 2.0])
+    z = np.zeros(4)
+    lr, eps = 1e-2, 1e-8
+    # first step: the bias-corrected moments are g and g^2, so each parameter moves lr * g / (|g| + eps)
+    t1, m1, v1 = oracle.adamw(theta, g, z, z, lr=lr, eps=eps)
+    np.testing.assert_allclose(t1, theta - lr * g / (np.abs(g) + eps), rtol=0, atol=1e-15)
+    # a constant gradient keeps that step size at every step
+    t, m, v = theta, z, z
+    for s in range(1, 6):
+        t, m, v = oracle.adamw(t, g, m, v, lr=lr, eps=eps, step=s)
+    np.testing.assert_allclose(t, theta - 5 * lr * g / (np.abs(g) + eps), rtol=0, atol=1e-12)
+    # decoupled weight decay shrinks theta by (1 - lr wd) before the step, gradient or not
+    t2, _, _ = oracle.adamw(theta, z, z, z, lr=lr, wd=0.1)
+    np.testing.assert_allclose(t2, theta * (1 - lr * 0.1), rtol=0, atol=1e-15)
+    # the clipping scale multiplies the gradient: the first step is unchanged up to eps
+    t3, m3, _ = oracle.adamw(theta, g, z, z, lr=lr, eps=eps, scale=0.25)
+    np.testing.assert_allclose(m3, 0.1 * 0.25 * g, rtol=1e-15)
+    np.testing.assert_allclose(t3[:2], t1[:2], rtol=0, atol=1e-9)

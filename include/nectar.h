@@ -20,6 +20,8 @@
  *   nectar_merge_k          the same over K document-side pairs
  *   nectar_fit_metrics      squared errors and the RTE of a module against the
  *                           exact pair (Eqs. (3.2)-(3.3), (C.1))
+ *   nectar_mlp_loss_grad / nectar_adamw_step / nectar_mlp_train_step
+ *                           the module's regression training step (section 2.3)
  *   nectar_layer_step       all of the above for one layer step, fused
  *
  * Conventions shared by every entry point
@@ -303,6 +305,62 @@ NECTAR_API nectar_status nectar_fit_metrics(const nectar_attn_desc *desc, const 
                                  const float *A, const float *alpha, const float *A_exact,
                                  float *row_out, double *head_out, void *ws, size_t ws_bytes,
                                  void *stream);
+
+/*
+ * Regression training of the one-hidden-layer MLP module (section 2.3 of the
+ * notes, Eqs. (3.2)-(3.3); App. A.2-A.5 for the optimizer).  Over the R query
+ * tokens of one layer, with targets (alpha, A_target) from the exact document
+ * attention (nectar_doc_attn_exact emits them in fp32, as the notes cache them):
+ *   L_alpha = (1/R) sum_r sum_h' (a(q) - alpha)^2,
+ *   L_A     = (1/R) sum_r sum_h' ||A(q) - A_target||^2,
+ *   L       = lambda_alpha L_alpha + lambda_A L_A     ((0.1, 1) for the MLP).
+ * The parameters are handled as one flat fp32 vector theta in the order
+ *   W1 [Hkv][Ht][d], b1 [Hkv][Ht], W2t [Hkv][Ht][d], b2 [Hkv][d],
+ *   Ws [Hkv][Hs][d], bs [Hkv][Hs], ws2 [Hkv][Hs], bs2 [Hkv]
+ * (nectar_mlp_param_count elements); gradients use the same layout.
+ * Supported: bf16 modules (desc->dtype == NECTAR_BF16), Ht and Hs positive
+ * multiples of 32, R >= 1.  The products run on bf16 operands with fp32
+ * accumulation (hidden values and back-propagated gradients rounded to bf16
+ * between products, as in the forward kernels); reductions are fixed-order, so
+ * a call is reproducible.
+ *
+ * nectar_mlp_loss_grad: grad (flat fp32) and loss[3] = (L, L_alpha, L_A) of the
+ *   module m (its bf16 weights and fp32 biases) on q [R][Hq][d] (bf16), alpha
+ *   [R][Hq], A_target [R][Hq][d] (fp32).
+ * nectar_adamw_step: one AdamW step on n fp32 parameters (decoupled weight
+ *   decay: theta *= 1 - lr wd; m = b1 m + (1 - b1) g; v = b2 v + (1 - b2) g^2;
+ *   theta -= lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)).
+ * nectar_mlp_train_step: the loss and gradient as above (grad is overwritten),
+ *   the global gradient norm, clipping by min(1, clip_norm / (norm + 1e-6))
+ *   when clip_norm > 0, the AdamW step on theta, adam_m, adam_v, and the
+ *   module's own arrays rewritten from theta (weights rounded to bf16, biases
+ *   copied) -- m's arrays are written although the struct declares them const.
+ *   loss [3] and gnorm [2] = (clipping factor, norm before clipping) are
+ *   optional fp32 device outputs.  theta must hold the module's current values
+ *   (the caller initialises it and the moments, zero, once).
+ * The learning-rate schedule (warm-up and cosine decay in the notes) is the
+ * caller's: pass each step's lr in hp.
+ */
+typedef struct {
+    float lambda_alpha, lambda_A;     /* loss weights */
+    float lr, beta1, beta2, eps, weight_decay;
+    float clip_norm;                  /* global gradient-norm clip; <= 0: none */
+    int32_t step;                     /* Adam step t >= 1 */
+} nectar_train_hparams;
+
+NECTAR_API int64_t nectar_mlp_param_count(const nectar_attn_desc *desc, const nectar_module *m);
+NECTAR_API size_t nectar_mlp_train_workspace_size(const nectar_attn_desc *desc, const nectar_module *m);
+NECTAR_API nectar_status nectar_mlp_loss_grad(const nectar_attn_desc *desc, const nectar_module *m,
+                                   const void *q, const float *alpha, const float *A_target,
+                                   float lambda_alpha, float lambda_A, float *grad, float *loss,
+                                   void *ws, size_t ws_bytes, void *stream);
+NECTAR_API nectar_status nectar_adamw_step(int64_t n, float *theta, const float *grad, float *adam_m,
+                                float *adam_v, const nectar_train_hparams *hp, void *stream);
+NECTAR_API nectar_status nectar_mlp_train_step(const nectar_attn_desc *desc, const nectar_module *m,
+                                    const void *q, const float *alpha, const float *A_target,
+                                    const nectar_train_hparams *hp, float *theta, float *adam_m,
+                                    float *adam_v, float *grad, float *loss, float *gnorm,
+                                    void *ws, size_t ws_bytes, void *stream);
 
 /*
  * One layer step of both paths, fused (sections 2.1-2.2; the step loop of a

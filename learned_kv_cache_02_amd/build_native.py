@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnectar.so")
-SOURCES = ["attn.hip", "attn_lds.hip", "merge.hip", "deep_mlp.hip", "metrics.hip", "mlp.hip", "mlp_prefill.hip", "mlp_lds.hip", "finish.hip", "step.hip", "nectar_abi.cpp"]
+SOURCES = ["attn.hip", "attn_lds.hip", "merge.hip", "deep_mlp.hip", "metrics.hip", "train.hip", "mlp.hip", "mlp_prefill.hip", "mlp_lds.hip", "finish.hip", "step.hip", "nectar_abi.cpp"]
 # Per-source code-generation options: the LDS-staged attention keeps its MFMA
 # accumulators in ordinary VGPRs (with accumulation registers the compiler
 # copies them back and forth around the softmax on every tile).

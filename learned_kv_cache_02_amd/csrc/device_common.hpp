@@ -135,6 +135,36 @@ __device__ __forceinline__ float gelu_erf_sigmoid(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p * x));
 }
 
+// Derivatives of the activations (the backward pass of the training step):
+//   GELU erf form: Phi(x) + x phi(x), Phi with the same 7.1.26 erf as gelu_erf;
+//   SiLU: s (1 + x (1 - s)), s = sigmoid(x);
+//   tanh form x sigmoid(v), v = 1.5957691 (x + 0.044715 x^3):
+//       sigmoid(v) + x sigmoid(v) (1 - sigmoid(v)) 1.5957691 (1 + 0.134145 x^2).
+__device__ __forceinline__ float gelu_erf_grad(float x) {
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
+    float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+    p = __builtin_fmaf(p, t, 1.421413741f);
+    p = __builtin_fmaf(p, t, -0.284496736f);
+    p = __builtin_fmaf(p, t, 0.254829592f);
+    const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);   // exp(-x^2 / 2)
+    const float erfc_half = 0.5f * (p * t) * e;
+    const float Phi = x >= 0.f ? 1.0f - erfc_half : erfc_half;
+    return Phi + x * e * 0.3989422804014327f;
+}
+__device__ __forceinline__ float silu_grad(float x) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+    return sg * (1.0f + x * (1.0f - sg));
+}
+__device__ __forceinline__ float gelu_tanh_grad(float x) {
+    const float v = 1.5957691216057308f * x * __builtin_fmaf(0.044715f, x * x, 1.0f);
+    const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e));
+    return sg + x * sg * (1.0f - sg) * 1.5957691216057308f * __builtin_fmaf(0.134145f, x * x, 1.0f);
+}
+template <int ACT> __device__ __forceinline__ float act_grad_fn(float x) {
+    return ACT == 1 ? silu_grad(x) : (ACT == 2 ? gelu_tanh_grad(x) : gelu_erf_grad(x));
+}
+
 template <int ACT> __device__ __forceinline__ float act_fn(float x) {
     return ACT == 1 ? silu(x) : (ACT == 2 ? gelu_tanh(x) : gelu_erf(x));
 }

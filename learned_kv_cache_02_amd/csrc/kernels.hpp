@@ -100,6 +100,98 @@ struct FitParams {
     int Hq, Hkv;
 };
 
+// --- training step of the one-hidden-layer module ---
+// C[p][m][n] = sum_k X[p][m][k] W[p][n][k] (+ bias[p * sb + n]); bf16 operands,
+// fp32 result; K a multiple of 16, leading dimensions multiples of 8.
+struct GemmParams {
+    const uint16_t *X, *W;
+    const float *bias;       // nullable
+    float *C;
+    long sx, sw, sb, sc;     // per-batch strides (elements)
+    int ldx, ldw, ldc;
+    int M, N, K, P;
+};
+// out[p][c][r] = in[p][r][c] for r < rows, zero for rows <= r < ldo.
+struct TransposeParams {
+    const uint16_t *in;
+    uint16_t *out;
+    long si, so;
+    int rows, cols, ldi, ldo, P;
+};
+struct GatherParams {        // Q[p][rho][:] = q row of rho in KV group p
+    const uint16_t *q;
+    uint16_t *Q;
+    int Hq, G, Hkv, Rp, d;
+};
+struct ActParams {           // mode 0: Y = act(Z); mode 1: Y = dY * act'(Z) (bf16 out)
+    const float *Z, *dY;
+    uint16_t *Y;
+    long n;
+    int mode;
+};
+struct ScoreRowParams {
+    const float *Zs;         // [Hkv][Rp][Hs] pre-activations (bias included)
+    const uint16_t *ws2;     // [Hkv][Hs]
+    const float *bs2, *alpha;
+    uint16_t *Ys, *dZs;      // [Hkv][Rp][Hs] bf16
+    float *ga, *err;         // [Hkv][Rp]
+    float coef;              // 2 lambda_alpha / R
+    int Hq, G, Hkv, Rp, Hs;
+};
+struct TargetRowParams {
+    const float *A, *Atgt;   // [Hkv][Rp][d] (bias included), [R][Hq][d]
+    uint16_t *gA;            // [Hkv][Rp][d]
+    float *err;              // [Hkv][Rp]
+    float coef;              // 2 lambda_A / R
+    int Hq, G, Hkv, Rp;
+};
+struct RowDotParams {        // out[p * so + j] = sum_k X[p][j][k] * (v ? v[p][k] : 1)
+    const void *X;
+    const float *v;
+    float *out;
+    long sx, sv, so;
+    int ldx, J, K, P;
+};
+struct SumParams {           // parts[part0 + b] = fixed-order fp64 sum of block b's range
+    const float *x;
+    double *parts;
+    long n;
+    int part0, square;
+};
+struct TrainScalars {
+    const double *parts;     // [3][nparts]: score errors, target errors, squared gradients
+    int nparts;
+    double R, lam_alpha, lam_A;
+    float clip;
+    float *loss;             // [3] or null
+    float *scale;            // [2]: clipping factor, gradient norm; or null
+    float *gnorm;            // caller's copy of scale (nullable)
+};
+struct AdamParams {
+    float *theta, *m, *v;
+    const float *g;
+    const float *scale;      // device clipping factor or null
+    long n;
+    float lr, b1, b2, eps, wd, ic1, ic2;   // ic = 1 / (1 - beta^t)
+};
+struct WriteParams {
+    const float *theta;
+    void *dst;
+    long n;
+    int bf16;
+};
+hipError_t launch_gemm_nt(const GemmParams &g, hipStream_t st);
+hipError_t launch_transpose_bf16(const TransposeParams &t, hipStream_t st);
+hipError_t launch_gather_q(const GatherParams &a, hipStream_t st);
+hipError_t launch_act_pass(const ActParams &a, int act, hipStream_t st);
+hipError_t launch_score_rows(const ScoreRowParams &a, int act, hipStream_t st);
+hipError_t launch_target_rows(const TargetRowParams &a, int d, hipStream_t st);
+hipError_t launch_row_dot(const RowDotParams &a, int fp32_in, hipStream_t st);
+hipError_t launch_sum_parts(const SumParams &a, int nparts, hipStream_t st);
+hipError_t launch_train_scalars(const TrainScalars &a, hipStream_t st);
+hipError_t launch_adamw(const AdamParams &a, hipStream_t st);
+hipError_t launch_write_params(const WriteParams &a, hipStream_t st);
+
 // One document-side part of a layer step, finished together with the local
 // part: split partials of the exact document attention or of a Quadrature
 // module (log-sum-exp form: ml != NULL) or of an MLP module (plain sums:

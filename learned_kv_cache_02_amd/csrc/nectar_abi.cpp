@@ -648,6 +648,266 @@ nectar_status nectar_fit_metrics(const nectar_attn_desc *desc, const void *q, co
 }
 
 // ---------------------------------------------------------------------------
+// Regression training step of the one-hidden-layer module.
+
+namespace {
+
+constexpr int kTrainParts = 64;
+
+struct TrainLayout {
+    int Rp = 0, Rpad = 0, Ht = 0, Hs = 0, d = 0, Hkv = 0;
+    // flat parameter offsets (elements): W1, b1, W2t, b2, Ws, bs, ws2, bs2, total
+    long off[9] = {};
+    // workspace offsets (bytes)
+    size_t Q, Qt, Zt, Yt, Ytt, W2tT, Aout, gA, gAt, dYt, Zs, Ys, Yst, dZs, dZst, ga, es, et, parts, scale, bytes;
+};
+
+TrainLayout train_layout(const nectar_attn_desc *d, const nectar_module *m) {
+    TrainLayout L;
+    const long H = d->Hkv;
+    L.Hkv = d->Hkv; L.d = d->d; L.Ht = m->Ht; L.Hs = m->Hs;
+    L.Rp = d->R * (d->Hq / d->Hkv);
+    L.Rpad = (L.Rp + 31) / 32 * 32;
+    const long sizes[8] = {H * L.Ht * L.d, H * L.Ht, H * L.Ht * L.d, H * L.d,
+                           H * L.Hs * L.d, H * L.Hs, H * L.Hs, H};
+    L.off[0] = 0;
+    for (int i = 0; i < 8; ++i) L.off[i + 1] = L.off[i] + sizes[i];
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+    const size_t R = (size_t)H * L.Rp, Rq = (size_t)H * L.Rpad;
+    L.Q = take(R * L.d * 2);
+    L.Qt = take(Rq * L.d * 2);
+    L.Zt = take(R * L.Ht * 4);
+    L.Yt = take(R * L.Ht * 2);
+    L.Ytt = take(Rq * L.Ht * 2);
+    L.W2tT = take((size_t)H * L.d * L.Ht * 2);
+    L.Aout = take(R * L.d * 4);
+    L.gA = take(R * L.d * 2);
+    L.gAt = take(Rq * L.d * 2);
+    L.dYt = take(R * L.Ht * 4);
+    L.Zs = take(R * L.Hs * 4);
+    L.Ys = take(R * L.Hs * 2);
+    L.Yst = take(Rq * L.Hs * 2);
+    L.dZs = take(R * L.Hs * 2);
+    L.dZst = take(Rq * L.Hs * 2);
+    L.ga = take(R * 4);
+    L.es = take(R * 4);
+    L.et = take(R * 4);
+    L.parts = take(3 * kTrainParts * 8);
+    L.scale = take(2 * 4);
+    L.bytes = o;
+    return L;
+}
+
+nectar_status check_train(const nectar_attn_desc *desc, const nectar_module *m) {
+    nectar_status s = check_desc(desc);
+    if (s != NECTAR_OK) return s;
+    if ((s = check_module(desc, m)) != NECTAR_OK) return s;
+    if (m->kind != NECTAR_MODULE_MLP) return NECTAR_EUNSUPPORTED;
+    if (desc->dtype != NECTAR_BF16) return NECTAR_EUNSUPPORTED;
+    if (m->Ht <= 0 || m->Hs <= 0 || m->Ht % 32 || m->Hs % 32) return NECTAR_EUNSUPPORTED;
+    if (desc->R <= 0) return NECTAR_EINVAL;
+    return NECTAR_OK;
+}
+
+GemmParams gemm(const void *X, long sx, int ldx, const void *W, long sw, int ldw, const float *bias, long sb,
+                float *C, long sc, int ldc, int M, int N, int K, int P) {
+    GemmParams g{};
+    g.X = (const uint16_t *)X; g.W = (const uint16_t *)W; g.bias = bias; g.C = C;
+    g.sx = sx; g.sw = sw; g.sb = sb; g.sc = sc; g.ldx = ldx; g.ldw = ldw; g.ldc = ldc;
+    g.M = M; g.N = N; g.K = K; g.P = P;
+    return g;
+}
+
+TransposeParams transpose(const void *in, long si, int ldi, void *out, long so, int ldo, int rows, int cols, int P) {
+    TransposeParams t{};
+    t.in = (const uint16_t *)in; t.out = (uint16_t *)out; t.si = si; t.so = so;
+    t.rows = rows; t.cols = cols; t.ldi = ldi; t.ldo = ldo; t.P = P;
+    return t;
+}
+
+RowDotParams rowdot(const void *X, long sx, int ldx, const float *v, long sv, float *out, long so, int J, int K, int P) {
+    RowDotParams r{};
+    r.X = X; r.sx = sx; r.ldx = ldx; r.v = v; r.sv = sv; r.out = out; r.so = so; r.J = J; r.K = K; r.P = P;
+    return r;
+}
+
+// Loss terms and gradient into grad (flat fp32, parameter order of TrainLayout).
+hipError_t run_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, const TrainLayout &L, const void *q,
+                         const float *alpha, const float *Atgt, float lam_alpha, float lam_A, float *grad,
+                         char *w, hipStream_t st) {
+    const int P = L.Hkv, Rp = L.Rp, Rq = L.Rpad, d = L.d, Ht = L.Ht, Hs = L.Hs;
+    auto B = [&](size_t off) { return (void *)(w + off); };
+    auto F = [&](size_t off) { return (float *)(w + off); };
+    hipError_t e = hipSuccess;
+    auto run = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+
+    GatherParams gq{};
+    gq.q = (const uint16_t *)q; gq.Q = (uint16_t *)B(L.Q);
+    gq.Hq = desc->Hq; gq.G = desc->Hq / desc->Hkv; gq.Hkv = P; gq.Rp = Rp; gq.d = d;
+    run(launch_gather_q(gq, st));
+    run(launch_transpose_bf16(transpose(B(L.Q), (long)Rp * d, d, B(L.Qt), (long)d * Rq, Rq, Rp, d, P), st));
+    // forward: pre-activations (bias included), hidden values, read-out
+    run(launch_gemm_nt(gemm(B(L.Q), (long)Rp * d, d, m->W1, (long)Ht * d, d, m->b1, Ht, F(L.Zt), (long)Rp * Ht, Ht,
+                            Rp, Ht, d, P), st));
+    run(launch_gemm_nt(gemm(B(L.Q), (long)Rp * d, d, m->Ws, (long)Hs * d, d, m->bs, Hs, F(L.Zs), (long)Rp * Hs, Hs,
+                            Rp, Hs, d, P), st));
+    ActParams ap{};
+    ap.Z = F(L.Zt); ap.Y = (uint16_t *)B(L.Yt); ap.n = (long)P * Rp * Ht; ap.mode = 0;
+    run(launch_act_pass(ap, m->act, st));
+    run(launch_transpose_bf16(transpose(B(L.Yt), (long)Rp * Ht, Ht, B(L.Ytt), (long)Ht * Rq, Rq, Rp, Ht, P), st));
+    run(launch_transpose_bf16(transpose(m->W2t, (long)Ht * d, d, B(L.W2tT), (long)d * Ht, Ht, Ht, d, P), st));
+    run(launch_gemm_nt(gemm(B(L.Yt), (long)Rp * Ht, Ht, B(L.W2tT), (long)d * Ht, Ht, m->b2, d, F(L.Aout),
+                            (long)Rp * d, d, Rp, d, Ht, P), st));
+    // loss terms and the output gradients
+    TargetRowParams tp{};
+    tp.A = F(L.Aout); tp.Atgt = Atgt; tp.gA = (uint16_t *)B(L.gA); tp.err = F(L.et);
+    tp.coef = 2.0f * lam_A / (float)desc->R;
+    tp.Hq = desc->Hq; tp.G = desc->Hq / desc->Hkv; tp.Hkv = P; tp.Rp = Rp;
+    run(launch_target_rows(tp, d, st));
+    ScoreRowParams sp{};
+    sp.Zs = F(L.Zs); sp.ws2 = (const uint16_t *)m->ws2; sp.bs2 = m->bs2; sp.alpha = alpha;
+    sp.Ys = (uint16_t *)B(L.Ys); sp.dZs = (uint16_t *)B(L.dZs); sp.ga = F(L.ga); sp.err = F(L.es);
+    sp.coef = 2.0f * lam_alpha / (float)desc->R;
+    sp.Hq = desc->Hq; sp.G = desc->Hq / desc->Hkv; sp.Hkv = P; sp.Rp = Rp; sp.Hs = Hs;
+    run(launch_score_rows(sp, m->act, st));
+    run(launch_transpose_bf16(transpose(B(L.gA), (long)Rp * d, d, B(L.gAt), (long)d * Rq, Rq, Rp, d, P), st));
+    run(launch_transpose_bf16(transpose(B(L.Ys), (long)Rp * Hs, Hs, B(L.Yst), (long)Hs * Rq, Rq, Rp, Hs, P), st));
+    run(launch_transpose_bf16(transpose(B(L.dZs), (long)Rp * Hs, Hs, B(L.dZst), (long)Hs * Rq, Rq, Rp, Hs, P), st));
+    // target read-out gradient, then back through it
+    float *gW1 = grad + L.off[0], *gb1 = grad + L.off[1], *gW2t = grad + L.off[2], *gb2 = grad + L.off[3];
+    float *gWs = grad + L.off[4], *gbs = grad + L.off[5], *gws2 = grad + L.off[6], *gbs2 = grad + L.off[7];
+    run(launch_gemm_nt(gemm(B(L.Ytt), (long)Ht * Rq, Rq, B(L.gAt), (long)d * Rq, Rq, nullptr, 0, gW2t, (long)Ht * d,
+                            d, Ht, d, Rq, P), st));
+    run(launch_gemm_nt(gemm(B(L.gA), (long)Rp * d, d, m->W2t, (long)Ht * d, d, nullptr, 0, F(L.dYt), (long)Rp * Ht,
+                            Ht, Rp, Ht, d, P), st));
+    ap.Z = F(L.Zt); ap.dY = F(L.dYt); ap.Y = (uint16_t *)B(L.Yt); ap.mode = 1;       // dZ_t over the hidden values
+    run(launch_act_pass(ap, m->act, st));
+    run(launch_transpose_bf16(transpose(B(L.Yt), (long)Rp * Ht, Ht, B(L.Ytt), (long)Ht * Rq, Rq, Rp, Ht, P), st));
+    // first-layer gradients (contractions over the rows)
+    run(launch_gemm_nt(gemm(B(L.Ytt), (long)Ht * Rq, Rq, B(L.Qt), (long)d * Rq, Rq, nullptr, 0, gW1, (long)Ht * d,
+                            d, Ht, d, Rq, P), st));
+    run(launch_gemm_nt(gemm(B(L.dZst), (long)Hs * Rq, Rq, B(L.Qt), (long)d * Rq, Rq, nullptr, 0, gWs, (long)Hs * d,
+                            d, Hs, d, Rq, P), st));
+    // bias and score read-out gradients: fixed-order row sums
+    run(launch_row_dot(rowdot(B(L.Ytt), (long)Ht * Rq, Rq, nullptr, 0, gb1, Ht, Ht, Rq, P), 0, st));
+    run(launch_row_dot(rowdot(B(L.gAt), (long)d * Rq, Rq, nullptr, 0, gb2, d, d, Rq, P), 0, st));
+    run(launch_row_dot(rowdot(B(L.dZst), (long)Hs * Rq, Rq, nullptr, 0, gbs, Hs, Hs, Rq, P), 0, st));
+    run(launch_row_dot(rowdot(B(L.Yst), (long)Hs * Rq, Rq, F(L.ga), Rp, gws2, Hs, Hs, Rp, P), 0, st));
+    run(launch_row_dot(rowdot(F(L.ga), Rp, Rp, nullptr, 0, gbs2, 1, 1, Rp, P), 1, st));
+    // loss sums
+    SumParams su{};
+    su.parts = (double *)B(L.parts);
+    su.x = F(L.es); su.n = (long)P * Rp; su.part0 = 0; su.square = 0;
+    run(launch_sum_parts(su, kTrainParts, st));
+    su.x = F(L.et); su.part0 = kTrainParts;
+    run(launch_sum_parts(su, kTrainParts, st));
+    return e;
+}
+
+}  // namespace
+
+int64_t nectar_mlp_param_count(const nectar_attn_desc *desc, const nectar_module *m) {
+    if (check_desc(desc) != NECTAR_OK || !m || m->kind != NECTAR_MODULE_MLP || m->Ht < 0 || m->Hs < 0) return 0;
+    const long H = desc->Hkv, d = desc->d;
+    return H * (2L * m->Ht * d + m->Ht + d + m->Hs * d + 2L * m->Hs + 1);
+}
+
+size_t nectar_mlp_train_workspace_size(const nectar_attn_desc *desc, const nectar_module *m) {
+    if (check_train(desc, m) != NECTAR_OK) return 0;
+    return train_layout(desc, m).bytes;
+}
+
+nectar_status nectar_mlp_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, const void *q,
+                                   const float *alpha, const float *A_target, float lambda_alpha, float lambda_A,
+                                   float *grad, float *loss, void *ws, size_t ws_bytes, void *stream) {
+    nectar_status s = check_train(desc, m);
+    if (s != NECTAR_OK) return s;
+    if (!tensor_ok(q) || !f32_ok(alpha) || !rows_ok(A_target) || !rows_ok(grad) || !f32_ok(loss))
+        return NECTAR_EINVAL;
+    if (!std::isfinite(lambda_alpha) || !std::isfinite(lambda_A)) return NECTAR_EINVAL;
+    const TrainLayout L = train_layout(desc, m);
+    if ((s = check_ws(L.bytes, ws, ws_bytes)) != NECTAR_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    char *w = (char *)ws;
+    hipError_t e = run_loss_grad(desc, m, L, q, alpha, A_target, lambda_alpha, lambda_A, grad, w, st);
+    if (e == hipSuccess) {
+        TrainScalars ts{};
+        ts.parts = (const double *)(w + L.parts); ts.nparts = kTrainParts;
+        ts.R = desc->R; ts.lam_alpha = lambda_alpha; ts.lam_A = lambda_A; ts.loss = loss;
+        e = launch_train_scalars(ts, st);
+    }
+    return finish(e, st);
+}
+
+static bool hparams_ok(const nectar_train_hparams *hp) {
+    return hp && hp->step >= 1 && std::isfinite(hp->lr) && hp->beta1 >= 0.f && hp->beta1 < 1.f && hp->beta2 >= 0.f &&
+           hp->beta2 < 1.f && hp->eps > 0.f && std::isfinite(hp->weight_decay) && std::isfinite(hp->clip_norm) &&
+           std::isfinite(hp->lambda_alpha) && std::isfinite(hp->lambda_A);
+}
+
+static AdamParams adam_params(const nectar_train_hparams *hp, float *theta, const float *g, float *m, float *v,
+                              long n, const float *scale) {
+    AdamParams a{};
+    a.theta = theta; a.g = g; a.m = m; a.v = v; a.n = n; a.scale = scale;
+    a.lr = hp->lr; a.b1 = hp->beta1; a.b2 = hp->beta2; a.eps = hp->eps; a.wd = hp->weight_decay;
+    a.ic1 = (float)(1.0 / (1.0 - std::pow((double)hp->beta1, hp->step)));
+    a.ic2 = (float)(1.0 / (1.0 - std::pow((double)hp->beta2, hp->step)));
+    return a;
+}
+
+nectar_status nectar_adamw_step(int64_t n, float *theta, const float *grad, float *adam_m, float *adam_v,
+                                const nectar_train_hparams *hp, void *stream) {
+    if (n < 0 || !hparams_ok(hp)) return NECTAR_EINVAL;
+    if (n == 0) return NECTAR_OK;
+    if (!f32_ok(theta) || !f32_ok(grad) || !f32_ok(adam_m) || !f32_ok(adam_v)) return NECTAR_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    return finish(launch_adamw(adam_params(hp, theta, grad, adam_m, adam_v, (long)n, nullptr), st), st);
+}
+
+nectar_status nectar_mlp_train_step(const nectar_attn_desc *desc, const nectar_module *m, const void *q,
+                                    const float *alpha, const float *A_target, const nectar_train_hparams *hp,
+                                    float *theta, float *adam_m, float *adam_v, float *grad, float *loss,
+                                    float *gnorm, void *ws, size_t ws_bytes, void *stream) {
+    nectar_status s = check_train(desc, m);
+    if (s != NECTAR_OK) return s;
+    if (!hparams_ok(hp)) return NECTAR_EINVAL;
+    if (!tensor_ok(q) || !f32_ok(alpha) || !rows_ok(A_target) || !rows_ok(grad) || !rows_ok(theta) ||
+        !rows_ok(adam_m) || !rows_ok(adam_v))
+        return NECTAR_EINVAL;
+    if ((loss && !f32_ok(loss)) || (gnorm && !f32_ok(gnorm))) return NECTAR_EINVAL;
+    const TrainLayout L = train_layout(desc, m);
+    if ((s = check_ws(L.bytes, ws, ws_bytes)) != NECTAR_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    char *w = (char *)ws;
+    hipError_t e = run_loss_grad(desc, m, L, q, alpha, A_target, hp->lambda_alpha, hp->lambda_A, grad, w, st);
+    const long n = L.off[8];
+    if (e == hipSuccess) {
+        SumParams su{};
+        su.parts = (double *)(w + L.parts); su.x = grad; su.n = n; su.part0 = 2 * kTrainParts; su.square = 1;
+        e = launch_sum_parts(su, kTrainParts, st);
+    }
+    float *scale = (float *)(w + L.scale);
+    if (e == hipSuccess) {
+        TrainScalars ts{};
+        ts.parts = (const double *)(w + L.parts); ts.nparts = kTrainParts;
+        ts.R = desc->R; ts.lam_alpha = hp->lambda_alpha; ts.lam_A = hp->lambda_A; ts.clip = hp->clip_norm;
+        ts.loss = loss; ts.scale = scale; ts.gnorm = gnorm;
+        e = launch_train_scalars(ts, st);
+    }
+    if (e == hipSuccess) e = launch_adamw(adam_params(hp, theta, grad, adam_m, adam_v, n, scale), st);
+    // the module's arrays from the updated master parameters
+    const void *dst[8] = {m->W1, m->b1, m->W2t, m->b2, m->Ws, m->bs, m->ws2, m->bs2};
+    for (int i = 0; i < 8 && e == hipSuccess; ++i) {
+        WriteParams wp{};
+        wp.theta = theta + L.off[i]; wp.dst = const_cast<void *>(dst[i]); wp.n = L.off[i + 1] - L.off[i];
+        wp.bf16 = (i == 0 || i == 2 || i == 4 || i == 6);
+        e = launch_write_params(wp, st);
+    }
+    return finish(e, st);
+}
+
+// ---------------------------------------------------------------------------
 // Whole layer step: deferred partials of every part, one finishing pass.
 
 // Partial bytes of an attention plan when its finish is deferred.

@@ -1,0 +1,396 @@
+// Regression training step of the one-hidden-layer module (section 2.3 of the
+// Nectar notes, Eqs. (3.2)-(3.3)): the forward with its pre-activations kept,
+// the loss lambda_alpha L_alpha + lambda_A L_A, the backward, global-norm
+// gradient clipping and AdamW on fp32 master parameters.
+//
+// Every dense contraction -- the two first layers, the target read-out, the
+// back-propagation through the read-out and the three weight gradients (whose
+// contraction runs over the query rows) -- is one batched "NT" product
+//   C[p][m][n] = sum_k X[p][m][k] W[p][n][k] (+ bias[p][n])
+// on the 32x32x16 bf16 MFMA (gemm_nt_lds32): both operands row-major with the
+// contraction innermost, so the products over rows read transposed copies
+// made by transpose_bf16 (64 x 64 tiles through LDS, the row count padded to a
+// multiple of 32 with zeros).  The elementwise passes (activation, its
+// derivative, the per-row score net and loss terms) and the bias gradients
+// (row sums of the transposed buffers, fixed order) are plain VALU kernels;
+// sums that feed the loss and the clipping norm are fixed-order, so a step is
+// reproducible.
+#include "attn_common.hpp"
+#include "lds_common.hpp"
+
+namespace nectar {
+
+namespace {
+
+constexpr int kBM = 256, kBN = 128, kBK = 32, kSl = kBK / 16, kWaves = 8, kXcd = 8;
+
+struct GemmStage {
+    u32x4 x[kSl * kBM * 2];   // [slice][row][half]
+    u32x4 w[kSl * kBN * 2];
+};
+
+}  // namespace
+
+// Tile: 256 rows of X x 128 rows of W per block of eight waves, 32-wide
+// contraction stages in a three-stage LDS ring filled by direct copies two
+// stages ahead (the layout and copy pattern of the deep-MLP layer kernel).
+__global__ __launch_bounds__(64 * kWaves, 4) void gemm_nt_lds32(GemmParams g) {
+    __shared__ GemmStage st_a, st_b, st_c;
+
+    const long blk = blockIdx.x;
+    const int NT = (g.N + kBN - 1) / kBN, nrb = (g.M + kBM - 1) / kBM;
+    const int xcd = (int)(blk % kXcd);
+    const long kq = blk / kXcd;
+    const int nt = (int)(kq % NT);
+    const int rgi = (int)(kq / NT) * kXcd + xcd;
+    if (rgi >= g.P * nrb) return;
+    const int p = rgi / nrb, m0 = (rgi - p * nrb) * kBM, n0 = nt * kBN;
+
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int wr = w & 3, wc = w >> 2;
+    const int nst = (g.K + kBK - 1) / kBK;
+    const int cs = w >> 2, half = (lane & 1) ^ ((lane >> 4) & 1);
+    const size_t lo = 16 * cs + 8 * half;
+    const int rA = min(m0 + (2 * (w & 3)) * 32 + (lane >> 1), g.M - 1);
+    const int rB = min(m0 + (2 * (w & 3) + 1) * 32 + (lane >> 1), g.M - 1);
+    const int rW = min(n0 + (w & 3) * 32 + (lane >> 1), g.N - 1);
+    const uint16_t *xA = g.X + p * g.sx + (size_t)rA * g.ldx + lo;
+    const uint16_t *xB = g.X + p * g.sx + (size_t)rB * g.ldx + lo;
+    const uint16_t *wR = g.W + p * g.sw + (size_t)rW * g.ldw + lo;
+
+    auto issue = [&](int i, GemmStage &dst) __attribute__((always_inline)) {
+        const int k0 = i * kBK;
+        const int kk = (k0 + 16 * cs < g.K) ? k0 : -16 * cs;   // past the end: slice 0 again (unused)
+        __builtin_amdgcn_global_load_lds((const void *)(xA + kk),
+                                         (lds_void *)&dst.x[(cs * kBM + (2 * (w & 3)) * 32) * 2], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(xB + kk),
+                                         (lds_void *)&dst.x[(cs * kBM + (2 * (w & 3) + 1) * 32) * 2], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(wR + kk), (lds_void *)&dst.w[(cs * kBN + (w & 3) * 32) * 2],
+                                         16, 0, 0);
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    const int r32 = lane & 31, hsel = (lane >> 5) ^ ((r32 >> 3) & 1);
+
+    auto step = [&](int i, const GemmStage &cur, GemmStage &ahead) __attribute__((always_inline)) {
+        if (i + 1 < nst) wait_vmcnt<3>();
+        else wait_vmcnt<0>();
+        stage_barrier();
+        if (i + 2 < nst) issue(i + 2, ahead);
+        const int k0 = i * kBK;
+#pragma unroll
+        for (int s = 0; s < kSl; ++s) {
+            if (k0 + 16 * s >= g.K) break;
+            u32x4 A[2], B[2];
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) A[ti] = cur.w[(s * kBN + wc * 64 + 32 * ti + r32) * 2 + hsel];
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj) B[tj] = cur.x[(s * kBM + wr * 64 + 32 * tj + r32) * 2 + hsel];
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = mfma32(A[ti], B[tj], acc[ti][tj]);
+        }
+    };
+    issue(0, st_a);
+    if (nst > 1) issue(1, st_b);
+    for (int i = 0; i < nst; i += 3) {
+        step(i, st_a, st_c);
+        if (i + 1 >= nst) break;
+        step(i + 1, st_b, st_a);
+        if (i + 2 >= nst) break;
+        step(i + 2, st_c, st_b);
+    }
+
+    // register 4 qq + r of tile (ti, tj): column n0 + 64 wc + 32 ti + 8 qq + 4 (lane / 32) + r,
+    // row m0 + 64 wr + 32 tj + lane % 32
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj) {
+        const int m = m0 + wr * 64 + 32 * tj + r32;
+        if (m >= g.M) continue;
+        float *crow = g.C + p * g.sc + (size_t)m * g.ldc;
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5);
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    y[r] = acc[ti][tj][4 * qq + r] + (g.bias && nb + r < g.N ? g.bias[p * g.sb + nb + r] : 0.f);
+                if (nb + 3 < g.N) {
+                    *(f32x4 *)(crow + nb) = f32x4{y[0], y[1], y[2], y[3]};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (nb + r < g.N) crow[nb + r] = y[r];
+                }
+            }
+    }
+}
+
+// out[p][c][r] = in[p][r][c] for r < rows, 0 for rows <= r < ldo (64 x 64 tiles).
+__global__ __launch_bounds__(256) void transpose_bf16(TransposeParams a) {
+    __shared__ uint16_t tile[64][66];
+    const int tc = (a.cols + 63) / 64, tr = (a.ldo + 63) / 64;
+    long b = blockIdx.x;
+    const int bc = (int)(b % tc);
+    b /= tc;
+    const int br = (int)(b % tr), p = (int)(b / tr);
+    const int r0 = br * 64, c0 = bc * 64;
+    const uint16_t *in = a.in + p * a.si;
+    uint16_t *out = a.out + p * a.so;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int rr = e >> 6, cc = e & 63;
+        const int r = r0 + rr, c = c0 + cc;
+        tile[rr][cc] = (r < a.rows && c < a.cols) ? in[(size_t)r * a.ldi + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int cc = e >> 6, rr = e & 63;
+        const int r = r0 + rr, c = c0 + cc;
+        if (c < a.cols && r < a.ldo) out[(size_t)c * a.ldo + r] = tile[rr][cc];
+    }
+}
+
+// Q[p][rho][:] = q row of (token rho / G, query head p G + rho % G).
+__global__ __launch_bounds__(256) void gather_q(GatherParams a) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;       // one 16-byte piece
+    const int pieces = a.d / 8;
+    const long n = (long)a.Hkv * a.Rp * pieces;
+    if (i >= n) return;
+    const int pc = (int)(i % pieces);
+    const long pr = i / pieces;
+    const int rho = (int)(pr % a.Rp), p = (int)(pr / a.Rp);
+    const size_t src = out_row(p, rho, a.Hkv, a.G, 0, a.Hq) * a.d + 8 * pc;
+    *(u32x4 *)(a.Q + (size_t)pr * a.d + 8 * pc) = *(const u32x4 *)(a.q + src);
+}
+
+// mode 0: Y = bf16(act(Z)); mode 1: Y = bf16(dY * act'(Z)).
+template <int ACT>
+__global__ __launch_bounds__(256) void act_pass(ActParams a) {
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (long)gridDim.x * 256) {
+        const float z = a.Z[i];
+        const float y = a.mode == 0 ? act_fn<ACT>(z) : a.dY[i] * act_grad_fn<ACT>(z);
+        a.Y[i] = f32_to_bf16(y);
+    }
+}
+
+// One wave per score row: hidden values, a, the score error and its gradient,
+// and the score net's back-propagated pre-activation gradient.
+template <int ACT>
+__global__ __launch_bounds__(256) void score_rows(ScoreRowParams a) {
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (long)a.Hkv * a.Rp) return;
+    const int lane = threadIdx.x & 63;
+    const int p = (int)(row / a.Rp), rho = (int)(row - (long)p * a.Rp);
+    const float *z = a.Zs + (size_t)row * a.Hs;
+    const uint16_t *ws2 = a.ws2 + (size_t)p * a.Hs;
+    float s = 0.f;
+    for (int j = lane; j < a.Hs; j += 64) s = __builtin_fmaf(bf16_to_f32(ws2[j]), act_fn<ACT>(z[j]), s);
+    s = wave_sum(s);
+    const size_t o = out_row(p, rho, a.Hkv, a.G, 0, a.Hq);
+    const float e = a.bs2[p] + s - a.alpha[o];
+    const float ga = a.coef * e;                   // 2 lambda_alpha e / R
+    for (int j = lane; j < a.Hs; j += 64) {
+        const float zj = z[j];
+        a.Ys[(size_t)row * a.Hs + j] = f32_to_bf16(act_fn<ACT>(zj));
+        a.dZs[(size_t)row * a.Hs + j] = f32_to_bf16(ga * bf16_to_f32(ws2[j]) * act_grad_fn<ACT>(zj));
+    }
+    if (lane == 0) {
+        a.ga[row] = ga;
+        a.err[row] = e * e;
+    }
+}
+
+// One wave per target row: e = A - A_target, ||e||^2 and gA = 2 lambda_A e / R (bf16).
+template <int D>
+__global__ __launch_bounds__(256) void target_rows(TargetRowParams a) {
+    constexpr int NPL = D / 64;
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (long)a.Hkv * a.Rp) return;
+    const int lane = threadIdx.x & 63;
+    const int p = (int)(row / a.Rp), rho = (int)(row - (long)p * a.Rp);
+    const size_t o = out_row(p, rho, a.Hkv, a.G, 0, a.Hq);
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+        const int c = lane * NPL + k;
+        const float e = a.A[(size_t)row * D + c] - a.Atgt[o * D + c];
+        s = __builtin_fmaf(e, e, s);
+        a.gA[(size_t)row * D + c] = f32_to_bf16(a.coef * e);
+    }
+    s = wave_sum(s);
+    if (lane == 0) a.err[row] = s;
+}
+
+// out[p * so + j] = sum_k X[p][j][k] * (v ? v[p][k] : 1), one wave per (p, j),
+// lane-strided partial sums then a fixed tree.
+template <typename T>
+__global__ __launch_bounds__(256) void row_dot(RowDotParams a) {
+    const long idx = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (idx >= (long)a.P * a.J) return;
+    const int lane = threadIdx.x & 63;
+    const int p = (int)(idx / a.J), j = (int)(idx - (long)p * a.J);
+    const T *x = (const T *)a.X + p * a.sx + (size_t)j * a.ldx;
+    const float *v = a.v ? a.v + p * a.sv : nullptr;
+    float s = 0.f;
+    for (int k = lane; k < a.K; k += 64) {
+        const float xv = Elem<T>::ld(x, k);
+        s = v ? __builtin_fmaf(xv, v[k], s) : s + xv;
+    }
+    s = wave_sum(s);
+    if (lane == 0) a.out[p * a.so + j] = s;
+}
+
+// Fixed-order fp64 sum of n floats (optionally squared) into parts[blockIdx.x].
+__global__ __launch_bounds__(256) void sum_parts(SumParams a) {
+    const long lo = a.n * blockIdx.x / gridDim.x, hi = a.n * (blockIdx.x + 1) / gridDim.x;
+    double s = 0.0;
+    for (long i = lo + threadIdx.x; i < hi; i += 256) {
+        const double x = a.x[i];
+        s += a.square ? x * x : x;
+    }
+    __shared__ double red[256];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) a.parts[a.part0 + blockIdx.x] = red[0];
+}
+
+// The loss and the clipping factor from the part sums (one thread).
+__global__ void train_scalars(TrainScalars a) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    double s[3] = {0.0, 0.0, 0.0};
+    for (int k = 0; k < 3; ++k)
+        for (int b = 0; b < a.nparts; ++b) s[k] += a.parts[k * a.nparts + b];
+    if (a.loss) {
+        a.loss[1] = (float)(s[0] / a.R);
+        a.loss[2] = (float)(s[1] / a.R);
+        a.loss[0] = (float)(a.lam_alpha * (s[0] / a.R) + a.lam_A * (s[1] / a.R));
+    }
+    if (a.scale) {
+        const double norm = sqrt(s[2]);
+        a.scale[0] = (a.clip > 0.f && norm > 0.0) ? (float)fmin(1.0, a.clip / (norm + 1e-6)) : 1.0f;
+        a.scale[1] = (float)norm;
+        if (a.gnorm) {
+            a.gnorm[0] = a.scale[0];
+            a.gnorm[1] = a.scale[1];
+        }
+    }
+}
+
+// AdamW: theta *= 1 - lr wd; g' = scale g; moments; bias-corrected step.
+__global__ __launch_bounds__(256) void adamw_kernel(AdamParams a) {
+    const float scale = a.scale ? a.scale[0] : 1.0f;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (long)gridDim.x * 256) {
+        const float gi = scale * a.g[i];
+        float th = a.theta[i] * (1.0f - a.lr * a.wd);
+        const float m = a.b1 * a.m[i] + (1.0f - a.b1) * gi;
+        const float v = a.b2 * a.v[i] + (1.0f - a.b2) * gi * gi;
+        a.m[i] = m;
+        a.v[i] = v;
+        th -= a.lr * (m * a.ic1) / (sqrtf(v * a.ic2) + a.eps);
+        a.theta[i] = th;
+    }
+}
+
+// Module arrays from the fp32 master parameters: weights to bf16 (RNE), biases copied.
+__global__ __launch_bounds__(256) void write_params(WriteParams a) {
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (long)gridDim.x * 256) {
+        const float x = a.theta[i];
+        if (a.bf16) ((uint16_t *)a.dst)[i] = f32_to_bf16(x);
+        else ((float *)a.dst)[i] = x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+
+static unsigned grid_for(long n, long per_block, long cap) {
+    long b = (n + per_block - 1) / per_block;
+    if (b > cap) b = cap;
+    return (unsigned)(b < 1 ? 1 : b);
+}
+
+hipError_t launch_gemm_nt(const GemmParams &g, hipStream_t st) {
+    if (g.M <= 0 || g.N <= 0 || g.P <= 0) return hipSuccess;
+    const long rg = (long)g.P * ((g.M + kBM - 1) / kBM);
+    const long blocks = (rg + kXcd - 1) / kXcd * kXcd * ((g.N + kBN - 1) / kBN);
+    hipLaunchKernelGGL(gemm_nt_lds32, dim3((unsigned)blocks), dim3(64 * kWaves), 0, st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const TransposeParams &t, hipStream_t st) {
+    const long blocks = (long)t.P * ((t.ldo + 63) / 64) * ((t.cols + 63) / 64);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)blocks), dim3(256), 0, st, t);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_q(const GatherParams &a, hipStream_t st) {
+    const long n = (long)a.Hkv * a.Rp * (a.d / 8);
+    hipLaunchKernelGGL(gather_q, dim3(grid_for(n, 256, 1L << 30)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_pass(const ActParams &a, int act, hipStream_t st) {
+    const dim3 grid(grid_for(a.n, 256, 8192)), block(256);
+    if (act == 1) hipLaunchKernelGGL(act_pass<1>, grid, block, 0, st, a);
+    else if (act == 2) hipLaunchKernelGGL(act_pass<2>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(act_pass<0>, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_score_rows(const ScoreRowParams &a, int act, hipStream_t st) {
+    const dim3 grid(grid_for((long)a.Hkv * a.Rp, 4, 1L << 30)), block(256);
+    if (act == 1) hipLaunchKernelGGL(score_rows<1>, grid, block, 0, st, a);
+    else if (act == 2) hipLaunchKernelGGL(score_rows<2>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(score_rows<0>, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_target_rows(const TargetRowParams &a, int d, hipStream_t st) {
+    const dim3 grid(grid_for((long)a.Hkv * a.Rp, 4, 1L << 30)), block(256);
+    if (d == 128) hipLaunchKernelGGL(target_rows<128>, grid, block, 0, st, a);
+    else if (d == 64) hipLaunchKernelGGL(target_rows<64>, grid, block, 0, st, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_row_dot(const RowDotParams &a, int fp32_in, hipStream_t st) {
+    const dim3 grid(grid_for((long)a.P * a.J, 4, 1L << 30)), block(256);
+    if (fp32_in) hipLaunchKernelGGL(row_dot<float>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(row_dot<uint16_t>, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_parts(const SumParams &a, int nparts, hipStream_t st) {
+    hipLaunchKernelGGL(sum_parts, dim3(nparts), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_train_scalars(const TrainScalars &a, hipStream_t st) {
+    hipLaunchKernelGGL(train_scalars, dim3(1), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamParams &a, hipStream_t st) {
+    if (a.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(a.n, 256, 8192)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_write_params(const WriteParams &a, hipStream_t st) {
+    if (a.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(write_params, dim3(grid_for(a.n, 256, 8192)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace nectar

@@ -8,6 +8,7 @@ torch's current stream.  A missing library raises at import.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -63,6 +64,12 @@ class Module(ctypes.Structure):
                 ("deep", ctypes.POINTER(DeepMLP))]
 
 
+class TrainHParams(ctypes.Structure):
+    _fields_ = [("lambda_alpha", ctypes.c_float), ("lambda_A", ctypes.c_float), ("lr", ctypes.c_float),
+                ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("clip_norm", ctypes.c_float), ("step", ctypes.c_int32)]
+
+
 class StepOutputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("out_exact", "lse_exact", "alpha_out", "A_out", "out_nectar",
                                                 "lse_nectar", "a_out", "Am_out", "lam_out", "Aloc_out")]
@@ -81,6 +88,15 @@ _lib.nectar_local_workspace_size.restype = ctypes.c_size_t
 _lib.nectar_local_attn_lse.argtypes = [_D, ctypes.POINTER(LocalDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, ctypes.c_size_t, _P]
 _lib.nectar_merge.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P]
+_lib.nectar_mlp_param_count.argtypes = [_D, ctypes.POINTER(Module)]
+_lib.nectar_mlp_param_count.restype = ctypes.c_int64
+_lib.nectar_mlp_train_workspace_size.argtypes = [_D, ctypes.POINTER(Module)]
+_lib.nectar_mlp_train_workspace_size.restype = ctypes.c_size_t
+_lib.nectar_mlp_loss_grad.argtypes = [_D, ctypes.POINTER(Module), _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P,
+                                      _P, ctypes.c_size_t, _P]
+_lib.nectar_adamw_step.argtypes = [ctypes.c_int64, _P, _P, _P, _P, ctypes.POINTER(TrainHParams), _P]
+_lib.nectar_mlp_train_step.argtypes = [_D, ctypes.POINTER(Module), _P, _P, _P, ctypes.POINTER(TrainHParams), _P, _P,
+                                       _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.nectar_fit_metrics.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.nectar_fit_metrics_workspace_size.argtypes = [_D]
 _lib.nectar_fit_metrics_workspace_size.restype = ctypes.c_size_t
@@ -100,7 +116,8 @@ _lib.nectar_abi_version.restype = ctypes.c_int
 _lib.nectar_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.nectar_workspace_init.restype = ctypes.c_int
 for _f in ("nectar_doc_attn_exact", "nectar_module_forward", "nectar_local_attn_lse", "nectar_merge",
-           "nectar_merge_k", "nectar_fit_metrics", "nectar_layer_step", "nectar_doc_attn_partials", "nectar_doc_attn_combine"):
+           "nectar_merge_k", "nectar_fit_metrics", "nectar_mlp_loss_grad", "nectar_adamw_step",
+           "nectar_mlp_train_step", "nectar_layer_step", "nectar_doc_attn_partials", "nectar_doc_attn_combine"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -394,6 +411,75 @@ def fit_metrics(q, a, A, alpha, A_exact, Hkv, *, row_out=None, head_out=None):
     _check(_lib.nectar_fit_metrics(ctypes.byref(dsc), _ptr(q), _ptr(a), _ptr(A), _ptr(alpha), _ptr(A_exact),
                                    _ptr(row_out), _ptr(head_out), wp, wn, _stream()))
     return row_out, head_out
+
+
+MLP_PARAMS = ("W1", "b1", "W2t", "b2", "Ws", "bs", "ws2", "bs2")
+
+
+def mlp_params_flat(module: "MLPModule") -> torch.Tensor:
+    """The module's parameters as one flat fp32 vector in the training order
+    W1, b1, W2t, b2, Ws, bs, ws2, bs2."""
+    return torch.cat([getattr(module, k).float().reshape(-1) for k in MLP_PARAMS])
+
+
+def mlp_grad_split(flat: torch.Tensor, module: "MLPModule") -> dict:
+    """Views of a flat vector in the module's parameter shapes."""
+    out, o = {}, 0
+    for k in MLP_PARAMS:
+        t = getattr(module, k)
+        out[k] = flat[o:o + t.numel()].view(t.shape)
+        o += t.numel()
+    return out
+
+
+def train_hparams(*, lr, step, lambda_alpha=0.1, lambda_A=1.0, beta1=0.9, beta2=0.999, eps=1e-8,
+                  weight_decay=0.0, clip_norm=1.0) -> TrainHParams:
+    return TrainHParams(lambda_alpha, lambda_A, lr, beta1, beta2, eps, weight_decay, clip_norm, int(step))
+
+
+def lr_at(step: int, peak: float, warmup: int, total: int) -> float:
+    """Warm-up then cosine decay to zero (the notes' schedule, peak 1e-4)."""
+    if step <= warmup:
+        return peak * step / max(1, warmup)
+    t = min(1.0, (step - warmup) / max(1, total - warmup))
+    return 0.5 * peak * (1.0 + math.cos(math.pi * t))
+
+
+def mlp_loss_grad(q, module: "MLPModule", alpha, A_target, Hkv, *, lambda_alpha=0.1, lambda_A=1.0):
+    """(grad flat fp32, loss [3] = (L, L_alpha, L_A)) of the regression loss."""
+    R, Hq, d = q.shape
+    dsc = desc(R, Hq, Hkv, d, dtype_code(q))
+    m = module.struct()
+    n = int(_lib.nectar_mlp_param_count(ctypes.byref(dsc), ctypes.byref(m)))
+    grad = torch.empty(n, dtype=torch.float32, device=q.device)
+    loss = torch.empty(3, dtype=torch.float32, device=q.device)
+    wp, wn = _ws_args(int(_lib.nectar_mlp_train_workspace_size(ctypes.byref(dsc), ctypes.byref(m))), q.device)
+    _check(_lib.nectar_mlp_loss_grad(ctypes.byref(dsc), ctypes.byref(m), _ptr(q), _ptr(alpha), _ptr(A_target),
+                                     lambda_alpha, lambda_A, _ptr(grad), _ptr(loss), wp, wn, _stream()))
+    return grad, loss
+
+
+def adamw_step(theta, grad, m, v, hp: TrainHParams):
+    _check(_lib.nectar_adamw_step(theta.numel(), _ptr(theta), _ptr(grad), _ptr(m), _ptr(v), ctypes.byref(hp),
+                                  _stream()))
+
+
+def mlp_train_step(q, module: "MLPModule", alpha, A_target, Hkv, hp: TrainHParams, theta, adam_m, adam_v, *,
+                   grad=None, loss=None, gnorm=None):
+    """One regression training step; updates theta, the moments and the module's
+    arrays in place.  Returns (grad, loss, gnorm)."""
+    R, Hq, d = q.shape
+    dsc = desc(R, Hq, Hkv, d, dtype_code(q))
+    m = module.struct()
+    f32 = dict(dtype=torch.float32, device=q.device)
+    grad = torch.empty(theta.numel(), **f32) if grad is None else grad
+    loss = torch.empty(3, **f32) if loss is None else loss
+    gnorm = torch.empty(2, **f32) if gnorm is None else gnorm
+    wp, wn = _ws_args(int(_lib.nectar_mlp_train_workspace_size(ctypes.byref(dsc), ctypes.byref(m))), q.device)
+    _check(_lib.nectar_mlp_train_step(ctypes.byref(dsc), ctypes.byref(m), _ptr(q), _ptr(alpha), _ptr(A_target),
+                                      ctypes.byref(hp), _ptr(theta), _ptr(adam_m), _ptr(adam_v), _ptr(grad),
+                                      _ptr(loss), _ptr(gnorm), wp, wn, _stream()))
+    return grad, loss, gnorm
 
 
 def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, module=None,

@@ -46,6 +46,11 @@ class Module(ctypes.Structure):
                 ("deep", ctypes.POINTER(Deep))]
 
 
+class HP(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_float) for n in ("lambda_alpha", "lambda_A", "lr", "beta1", "beta2", "eps",
+                                               "weight_decay", "clip_norm")] + [("step", ctypes.c_int32)]
+
+
 class StepOuts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("out_exact", "lse_exact", "alpha_out", "A_out", "out_nectar",
                                                 "lse_nectar", "a_out", "Am_out", "lam_out", "Aloc_out")]
@@ -70,6 +75,15 @@ def lib():
     L.nectar_merge.argtypes = [D] + [P] * 7
     L.nectar_fit_metrics.argtypes = [D] + [P] * 8 + [ctypes.c_size_t, P]
     L.nectar_fit_metrics_workspace_size.argtypes = [D]
+    L.nectar_mlp_param_count.argtypes = [D, ctypes.POINTER(Module)]
+    L.nectar_mlp_param_count.restype = ctypes.c_int64
+    L.nectar_mlp_train_workspace_size.argtypes = [D, ctypes.POINTER(Module)]
+    L.nectar_mlp_train_workspace_size.restype = ctypes.c_size_t
+    L.nectar_mlp_loss_grad.argtypes = [D, ctypes.POINTER(Module), P, P, P, ctypes.c_float, ctypes.c_float, P, P, P,
+                                       ctypes.c_size_t, P]
+    L.nectar_adamw_step.argtypes = [ctypes.c_int64, P, P, P, P, ctypes.POINTER(HP), P]
+    L.nectar_mlp_train_step.argtypes = [D, ctypes.POINTER(Module), P, P, P, ctypes.POINTER(HP), P, P, P, P, P, P, P,
+                                        ctypes.c_size_t, P]
     L.nectar_fit_metrics_workspace_size.restype = ctypes.c_size_t
     L.nectar_merge_k.argtypes = [D, ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P)] + [P] * 5
     L.nectar_layer_step_workspace_size.argtypes = [D, ctypes.c_int64, ctypes.POINTER(Local),
@@ -93,7 +107,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
     assert lib.nectar_abi_version() == 2
@@ -329,6 +343,40 @@ def test_fit_metrics_validation(lib):
     assert call(head=A16 + 4) == EINVAL          # fp64 sums
     assert call(dd=Desc(2, 8, 2, 96, 1, 0.0, 0)) == EUNSUPPORTED
     assert call(dd=Desc(0, 8, 2, 128, 1, 0.0, 0), q=None, a=None, A=None, al=None, Ae=None, row=None) == OK
+
+
+def test_training_entry_points_validation(lib):
+    d = Desc(5, 8, 2, 128, 1, 0.0, 0)
+    m = _mlp_module(96, 64)
+    n = lib.nectar_mlp_param_count(ctypes.byref(d), ctypes.byref(m))
+    assert n == 2 * (2 * 96 * 128 + 96 + 128 + 64 * 128 + 2 * 64 + 1)
+    ws = lib.nectar_mlp_train_workspace_size(ctypes.byref(d), ctypes.byref(m))
+    assert ws > 0
+    lg = lambda dd=d, mm=m, wsb=ws, grad=A16, la=0.1: lib.nectar_mlp_loss_grad(
+        ctypes.byref(dd), ctypes.byref(mm), A16, A16, A16, la, 1.0, grad, A16, A16, wsb, None)
+    assert lg(wsb=ws - 1) == EWORKSPACE
+    assert lg(grad=A16 + 4) == EINVAL
+    assert lg(la=float("nan")) == EINVAL
+    assert lg(dd=Desc(5, 8, 2, 128, 0, 0.0, 0)) == EUNSUPPORTED           # fp32 modules
+    assert lg(mm=_mlp_module(100, 64)) == EUNSUPPORTED                          # widths are multiples of 32
+    assert lg(mm=_mlp_module(96, 0)) == EUNSUPPORTED
+    assert lg(mm=Module(kind=1, p=10, W=A16, Z=A16)) == EUNSUPPORTED      # Quadrature: not this step
+    assert lg(dd=Desc(0, 8, 2, 128, 1, 0.0, 0)) == EINVAL                # needs rows
+    hp = HP(0.1, 1.0, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1.0, 1)
+    ad = lambda h, nn=10, th=A16: lib.nectar_adamw_step(nn, th, A16, A16, A16, ctypes.byref(h), None)
+    assert ad(hp, nn=0) == OK
+    assert ad(hp, nn=-1) == EINVAL
+    assert ad(hp, th=A16 + 2) == EINVAL
+    for bad in (HP(0.1, 1.0, 1e-4, 1.0, 0.999, 1e-8, 0.0, 1.0, 1), HP(0.1, 1.0, 1e-4, 0.9, 0.999, 0.0, 0.0, 1.0, 1),
+                HP(0.1, 1.0, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1.0, 0), HP(0.1, 1.0, float("inf"), 0.9, 0.999, 1e-8, 0.0,
+                                                                    1.0, 1)):
+        assert ad(bad) == EINVAL
+    ts = lambda h=hp, wsb=ws, th=A16: lib.nectar_mlp_train_step(
+        ctypes.byref(d), ctypes.byref(m), A16, A16, A16, ctypes.byref(h), th, A16, A16, A16, None, None, A16, wsb,
+        None)
+    assert ts(wsb=ws - 1) == EWORKSPACE
+    assert ts(th=A16 + 4) == EINVAL
+    assert ts(h=HP(0.1, 1.0, 1e-4, 0.9, 0.999, 1e-8, 0.0, 1.0, 0)) == EINVAL
 
 
 def test_oracle_and_product_share_no_code():

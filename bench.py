@@ -283,6 +283,7 @@ def main():
         res["merge_k"] = merge_k_prefill(torch, nectar, configs, dev)
         res["fit_metrics"] = fit_metrics_prefill(torch, nectar, configs, dev)
         res["deep_modules"] = deep_modules(torch, nectar, configs, dev)
+        res["train_step"] = train_step_bench(torch, nectar, configs, dev)
     if not args.no_workloads and args.only is None:
         res["workloads"] = {c.name: workload_layer(torch, nectar, c, dev) for c in (configs.C4, configs.C5, configs.C3)}
 
@@ -560,6 +561,57 @@ def deep_modules(torch, nectar, configs, dev):
             del mods, q, a, A
             torch.cuda.empty_cache()
         out[key] = res
+    return out
+
+
+def train_step_bench(torch, nectar, configs, dev, tokens=1024):
+    """One regression training step (loss, backward, clipping, AdamW) of the
+    Qwen3-4B-shaped layer's 4608/2944 module on a batch of 1,024 query tokens x
+    32 heads with fp32 targets; roofline = the MFMA flops of its seven products
+    (two first layers, the read-out, its back-propagation, three weight
+    gradients).  Inputs N(0, 1) from a seeded device generator."""
+    cfg = configs.C2
+    m = cfg.mlps[0]
+    d, Hkv, Hq = cfg.d, cfg.Hkv, cfg.Hq
+    g = torch.Generator(device=dev)
+    g.manual_seed(80)
+    bf = lambda *s_, std=1.0: (torch.randn(*s_, generator=g, device=dev) * std).to(torch.bfloat16)
+    z = lambda *s_: torch.zeros(*s_, device=dev)
+    mod = nectar.MLPModule(bf(Hkv, m.Ht, d, std=d ** -0.5), z(Hkv, m.Ht), bf(Hkv, m.Ht, d, std=m.Ht ** -0.5),
+                           z(Hkv, d), bf(Hkv, m.Hs, d, std=d ** -0.5), z(Hkv, m.Hs), bf(Hkv, m.Hs, std=m.Hs ** -0.5),
+                           z(Hkv))
+    q = bf(tokens, Hq, d)
+    alpha = torch.randn(tokens, Hq, generator=g, device=dev)
+    At = torch.randn(tokens, Hq, d, generator=g, device=dev) * 0.1
+    theta = nectar.mlp_params_flat(mod)
+    mm, vv = torch.zeros_like(theta), torch.zeros_like(theta)
+    grad = torch.empty_like(theta)
+    loss = torch.empty(3, device=dev)
+    gn = torch.empty(2, device=dev)
+    it = [0]
+
+    def call():
+        it[0] += 1
+        hp = nectar.train_hparams(lr=1e-4, step=it[0], clip_norm=1.0)
+        nectar.mlp_train_step(q, mod, alpha, At, Hkv, hp, theta, mm, vv, grad=grad, loss=loss, gnorm=gn)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 10 * 1e3
+    Rp = tokens * (Hq // Hkv)
+    Rq = (Rp + 31) // 32 * 32
+    flops = Hkv * 2.0 * d * (Rp * (3 * m.Ht + m.Hs) + Rq * (2 * m.Ht + m.Hs))
+    tf = flops / us / 1e6
+    out = {"tokens": tokens, "module": "MLP %d/%d" % (m.Ht, m.Hs), "us": us, "tflops": tf,
+           "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS, "bound": "mfma", "flops": flops,
+           "loss_after": float(loss[0]), "params": int(theta.numel())}
+    del mod, q, alpha, At, theta, mm, vv, grad
+    torch.cuda.empty_cache()
     return out
 
 

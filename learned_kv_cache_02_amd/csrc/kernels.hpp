@@ -103,13 +103,21 @@ struct FitParams {
 // --- training step of the one-hidden-layer module ---
 // C[p][m][n] = sum_k X[p][m][k] W[p][n][k] (+ bias[p * sb + n]); bf16 operands,
 // fp32 result; K a multiple of 16, leading dimensions multiples of 8.
+// Epilogues: 0 C = acc + bias (fp32); 1 Zo = bf16(acc + bias) and
+// Y = bf16(act(acc + bias)); 2 Y = bf16(acc * act'(Zi)), Zi bf16 in C's layout.
+// ksplit > 1 (epilogue 0 only): block ks sums K range ks and writes its partial
+// tile to Cpart[ks][p][m][n]; gemm_reduce then forms C = sum_ks + bias.
 struct GemmParams {
     const uint16_t *X, *W;
     const float *bias;       // nullable
     float *C;
+    uint16_t *Zo, *Y;
+    const uint16_t *Zi;
+    float *Cpart;
     long sx, sw, sb, sc;     // per-batch strides (elements)
     int ldx, ldw, ldc;
     int M, N, K, P;
+    int epi, act, ksplit, kchunk;
 };
 // out[p][c][r] = in[p][r][c] for r < rows, zero for rows <= r < ldo.
 struct TransposeParams {
@@ -122,12 +130,6 @@ struct GatherParams {        // Q[p][rho][:] = q row of rho in KV group p
     const uint16_t *q;
     uint16_t *Q;
     int Hq, G, Hkv, Rp, d;
-};
-struct ActParams {           // mode 0: Y = act(Z); mode 1: Y = dY * act'(Z) (bf16 out)
-    const float *Z, *dY;
-    uint16_t *Y;
-    long n;
-    int mode;
 };
 struct ScoreRowParams {
     const float *Zs;         // [Hkv][Rp][Hs] pre-activations (bias included)
@@ -152,6 +154,7 @@ struct RowDotParams {        // out[p * so + j] = sum_k X[p][j][k] * (v ? v[p][k
     long sx, sv, so;
     int ldx, J, K, P;
 };
+constexpr int kNormParts = 1024;   // blocks of the gradient-norm sum
 struct SumParams {           // parts[part0 + b] = fixed-order fp64 sum of block b's range
     const float *x;
     double *parts;
@@ -159,7 +162,7 @@ struct SumParams {           // parts[part0 + b] = fixed-order fp64 sum of block
     int part0, square;
 };
 struct TrainScalars {
-    const double *parts;     // [3][nparts]: score errors, target errors, squared gradients
+    const double *parts;     // [2][nparts] score and target errors, then [kNormParts] squared gradients
     int nparts;
     double R, lam_alpha, lam_A;
     float clip;
@@ -180,10 +183,10 @@ struct WriteParams {
     long n;
     int bf16;
 };
+long gemm_blocks(const GemmParams &g);
 hipError_t launch_gemm_nt(const GemmParams &g, hipStream_t st);
 hipError_t launch_transpose_bf16(const TransposeParams &t, hipStream_t st);
 hipError_t launch_gather_q(const GatherParams &a, hipStream_t st);
-hipError_t launch_act_pass(const ActParams &a, int act, hipStream_t st);
 hipError_t launch_score_rows(const ScoreRowParams &a, int act, hipStream_t st);
 hipError_t launch_target_rows(const TargetRowParams &a, int d, hipStream_t st);
 hipError_t launch_row_dot(const RowDotParams &a, int fp32_in, hipStream_t st);

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -652,14 +653,14 @@ nectar_status nectar_fit_metrics(const nectar_attn_desc *desc, const void *q, co
 
 namespace {
 
-constexpr int kTrainParts = 64;
+constexpr int kTrainParts = 64, kMaxSplit = 8;
 
 struct TrainLayout {
     int Rp = 0, Rpad = 0, Ht = 0, Hs = 0, d = 0, Hkv = 0;
     // flat parameter offsets (elements): W1, b1, W2t, b2, Ws, bs, ws2, bs2, total
     long off[9] = {};
     // workspace offsets (bytes)
-    size_t Q, Qt, Zt, Yt, Ytt, W2tT, Aout, gA, gAt, dYt, Zs, Ys, Yst, dZs, dZst, ga, es, et, parts, scale, bytes;
+    size_t Q, Qt, Zb, Yt, Ytt, W2tT, Aout, gA, gAt, Zs, Ys, Yst, dZs, dZst, ga, es, et, Cpart, parts, scale, bytes;
 };
 
 TrainLayout train_layout(const nectar_attn_desc *d, const nectar_module *m) {
@@ -677,14 +678,13 @@ TrainLayout train_layout(const nectar_attn_desc *d, const nectar_module *m) {
     const size_t R = (size_t)H * L.Rp, Rq = (size_t)H * L.Rpad;
     L.Q = take(R * L.d * 2);
     L.Qt = take(Rq * L.d * 2);
-    L.Zt = take(R * L.Ht * 4);
+    L.Zb = take(R * L.Ht * 2);
     L.Yt = take(R * L.Ht * 2);
     L.Ytt = take(Rq * L.Ht * 2);
     L.W2tT = take((size_t)H * L.d * L.Ht * 2);
     L.Aout = take(R * L.d * 4);
     L.gA = take(R * L.d * 2);
     L.gAt = take(Rq * L.d * 2);
-    L.dYt = take(R * L.Ht * 4);
     L.Zs = take(R * L.Hs * 4);
     L.Ys = take(R * L.Hs * 2);
     L.Yst = take(Rq * L.Hs * 2);
@@ -693,7 +693,8 @@ TrainLayout train_layout(const nectar_attn_desc *d, const nectar_module *m) {
     L.ga = take(R * 4);
     L.es = take(R * 4);
     L.et = take(R * 4);
-    L.parts = take(3 * kTrainParts * 8);
+    L.Cpart = take((size_t)kMaxSplit * H * std::max(std::max(L.Rp, L.Ht), L.Hs) * L.d * 4);
+    L.parts = take((2 * kTrainParts + kNormParts) * 8);
     L.scale = take(2 * 4);
     L.bytes = o;
     return L;
@@ -716,6 +717,23 @@ GemmParams gemm(const void *X, long sx, int ldx, const void *W, long sw, int ldw
     g.X = (const uint16_t *)X; g.W = (const uint16_t *)W; g.bias = bias; g.C = C;
     g.sx = sx; g.sw = sw; g.sb = sb; g.sc = sc; g.ldx = ldx; g.ldw = ldw; g.ldc = ldc;
     g.M = M; g.N = N; g.K = K; g.P = P;
+    g.ksplit = 1; g.kchunk = K;
+    return g;
+}
+
+// Split the contraction of a product whose tiles alone would leave most CUs
+// idle (partial tiles in Cpart, then a fixed-order reduce).
+GemmParams with_split(GemmParams g, float *Cpart) {
+    const long b = gemm_blocks(g);
+    if (b >= 512 || g.K < 1024 || g.N % 4) return g;
+    int ks = (int)std::min<long>(kMaxSplit, (512 + b - 1) / b);
+    const int kc = ((g.K + ks - 1) / ks + 31) / 32 * 32;
+    ks = (g.K + kc - 1) / kc;
+    if (ks > 1) {
+        g.ksplit = ks;
+        g.kchunk = kc;
+        g.Cpart = Cpart;
+    }
     return g;
 }
 
@@ -748,17 +766,16 @@ hipError_t run_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, c
     run(launch_gather_q(gq, st));
     run(launch_transpose_bf16(transpose(B(L.Q), (long)Rp * d, d, B(L.Qt), (long)d * Rq, Rq, Rp, d, P), st));
     // forward: pre-activations (bias included), hidden values, read-out
-    run(launch_gemm_nt(gemm(B(L.Q), (long)Rp * d, d, m->W1, (long)Ht * d, d, m->b1, Ht, F(L.Zt), (long)Rp * Ht, Ht,
-                            Rp, Ht, d, P), st));
+    GemmParams gz = gemm(B(L.Q), (long)Rp * d, d, m->W1, (long)Ht * d, d, m->b1, Ht, nullptr, (long)Rp * Ht, Ht,
+                         Rp, Ht, d, P);
+    gz.epi = 1; gz.act = m->act; gz.Zo = (uint16_t *)B(L.Zb); gz.Y = (uint16_t *)B(L.Yt);   // Z and act(Z), bf16
+    run(launch_gemm_nt(gz, st));
     run(launch_gemm_nt(gemm(B(L.Q), (long)Rp * d, d, m->Ws, (long)Hs * d, d, m->bs, Hs, F(L.Zs), (long)Rp * Hs, Hs,
                             Rp, Hs, d, P), st));
-    ActParams ap{};
-    ap.Z = F(L.Zt); ap.Y = (uint16_t *)B(L.Yt); ap.n = (long)P * Rp * Ht; ap.mode = 0;
-    run(launch_act_pass(ap, m->act, st));
     run(launch_transpose_bf16(transpose(B(L.Yt), (long)Rp * Ht, Ht, B(L.Ytt), (long)Ht * Rq, Rq, Rp, Ht, P), st));
     run(launch_transpose_bf16(transpose(m->W2t, (long)Ht * d, d, B(L.W2tT), (long)d * Ht, Ht, Ht, d, P), st));
-    run(launch_gemm_nt(gemm(B(L.Yt), (long)Rp * Ht, Ht, B(L.W2tT), (long)d * Ht, Ht, m->b2, d, F(L.Aout),
-                            (long)Rp * d, d, Rp, d, Ht, P), st));
+    run(launch_gemm_nt(with_split(gemm(B(L.Yt), (long)Rp * Ht, Ht, B(L.W2tT), (long)d * Ht, Ht, m->b2, d,
+                                       F(L.Aout), (long)Rp * d, d, Rp, d, Ht, P), F(L.Cpart)), st));
     // loss terms and the output gradients
     TargetRowParams tp{};
     tp.A = F(L.Aout); tp.Atgt = Atgt; tp.gA = (uint16_t *)B(L.gA); tp.err = F(L.et);
@@ -777,18 +794,19 @@ hipError_t run_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, c
     // target read-out gradient, then back through it
     float *gW1 = grad + L.off[0], *gb1 = grad + L.off[1], *gW2t = grad + L.off[2], *gb2 = grad + L.off[3];
     float *gWs = grad + L.off[4], *gbs = grad + L.off[5], *gws2 = grad + L.off[6], *gbs2 = grad + L.off[7];
-    run(launch_gemm_nt(gemm(B(L.Ytt), (long)Ht * Rq, Rq, B(L.gAt), (long)d * Rq, Rq, nullptr, 0, gW2t, (long)Ht * d,
-                            d, Ht, d, Rq, P), st));
-    run(launch_gemm_nt(gemm(B(L.gA), (long)Rp * d, d, m->W2t, (long)Ht * d, d, nullptr, 0, F(L.dYt), (long)Rp * Ht,
-                            Ht, Rp, Ht, d, P), st));
-    ap.Z = F(L.Zt); ap.dY = F(L.dYt); ap.Y = (uint16_t *)B(L.Yt); ap.mode = 1;       // dZ_t over the hidden values
-    run(launch_act_pass(ap, m->act, st));
+    run(launch_gemm_nt(with_split(gemm(B(L.Ytt), (long)Ht * Rq, Rq, B(L.gAt), (long)d * Rq, Rq, nullptr, 0, gW2t,
+                                       (long)Ht * d, d, Ht, d, Rq, P), F(L.Cpart)), st));
+    // dZ_t = (gA W2t) * act'(Z), bf16, into the hidden-value buffer (no longer needed)
+    GemmParams gd = gemm(B(L.gA), (long)Rp * d, d, m->W2t, (long)Ht * d, d, nullptr, 0, nullptr, (long)Rp * Ht, Ht,
+                         Rp, Ht, d, P);
+    gd.epi = 2; gd.act = m->act; gd.Zi = (const uint16_t *)B(L.Zb); gd.Y = (uint16_t *)B(L.Yt);
+    run(launch_gemm_nt(gd, st));
     run(launch_transpose_bf16(transpose(B(L.Yt), (long)Rp * Ht, Ht, B(L.Ytt), (long)Ht * Rq, Rq, Rp, Ht, P), st));
     // first-layer gradients (contractions over the rows)
-    run(launch_gemm_nt(gemm(B(L.Ytt), (long)Ht * Rq, Rq, B(L.Qt), (long)d * Rq, Rq, nullptr, 0, gW1, (long)Ht * d,
-                            d, Ht, d, Rq, P), st));
-    run(launch_gemm_nt(gemm(B(L.dZst), (long)Hs * Rq, Rq, B(L.Qt), (long)d * Rq, Rq, nullptr, 0, gWs, (long)Hs * d,
-                            d, Hs, d, Rq, P), st));
+    run(launch_gemm_nt(with_split(gemm(B(L.Ytt), (long)Ht * Rq, Rq, B(L.Qt), (long)d * Rq, Rq, nullptr, 0, gW1,
+                                       (long)Ht * d, d, Ht, d, Rq, P), F(L.Cpart)), st));
+    run(launch_gemm_nt(with_split(gemm(B(L.dZst), (long)Hs * Rq, Rq, B(L.Qt), (long)d * Rq, Rq, nullptr, 0, gWs,
+                                       (long)Hs * d, d, Hs, d, Rq, P), F(L.Cpart)), st));
     // bias and score read-out gradients: fixed-order row sums
     run(launch_row_dot(rowdot(B(L.Ytt), (long)Ht * Rq, Rq, nullptr, 0, gb1, Ht, Ht, Rq, P), 0, st));
     run(launch_row_dot(rowdot(B(L.gAt), (long)d * Rq, Rq, nullptr, 0, gb2, d, d, Rq, P), 0, st));
@@ -885,7 +903,7 @@ nectar_status nectar_mlp_train_step(const nectar_attn_desc *desc, const nectar_m
     if (e == hipSuccess) {
         SumParams su{};
         su.parts = (double *)(w + L.parts); su.x = grad; su.n = n; su.part0 = 2 * kTrainParts; su.square = 1;
-        e = launch_sum_parts(su, kTrainParts, st);
+        e = launch_sum_parts(su, kNormParts, st);
     }
     float *scale = (float *)(w + L.scale);
     if (e == hipSuccess) {

@@ -34,11 +34,14 @@ struct GemmStage {
 // Tile: 256 rows of X x 128 rows of W per block of eight waves, 32-wide
 // contraction stages in a three-stage LDS ring filled by direct copies two
 // stages ahead (the layout and copy pattern of the deep-MLP layer kernel).
+template <int EPI, int ACT>
 __global__ __launch_bounds__(64 * kWaves, 4) void gemm_nt_lds32(GemmParams g) {
     __shared__ GemmStage st_a, st_b, st_c;
 
-    const long blk = blockIdx.x;
     const int NT = (g.N + kBN - 1) / kBN, nrb = (g.M + kBM - 1) / kBM;
+    const long per_split = (long)((g.P * nrb + kXcd - 1) / kXcd * kXcd) * NT;
+    const int ks = (int)(blockIdx.x / per_split);
+    const long blk = blockIdx.x - (long)ks * per_split;
     const int xcd = (int)(blk % kXcd);
     const long kq = blk / kXcd;
     const int nt = (int)(kq % NT);
@@ -48,9 +51,11 @@ __global__ __launch_bounds__(64 * kWaves, 4) void gemm_nt_lds32(GemmParams g) {
 
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int wr = w & 3, wc = w >> 2;
-    const int nst = (g.K + kBK - 1) / kBK;
+    // this block's contraction range [kb, kb + Kc)
+    const int kb = ks * g.kchunk, Kc = min(g.K - kb, g.kchunk);
+    const int nst = (Kc + kBK - 1) / kBK;
     const int cs = w >> 2, half = (lane & 1) ^ ((lane >> 4) & 1);
-    const size_t lo = 16 * cs + 8 * half;
+    const size_t lo = kb + 16 * cs + 8 * half;
     const int rA = min(m0 + (2 * (w & 3)) * 32 + (lane >> 1), g.M - 1);
     const int rB = min(m0 + (2 * (w & 3) + 1) * 32 + (lane >> 1), g.M - 1);
     const int rW = min(n0 + (w & 3) * 32 + (lane >> 1), g.N - 1);
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void gemm_nt_lds32(GemmParams g) {
 
     auto issue = [&](int i, GemmStage &dst) __attribute__((always_inline)) {
         const int k0 = i * kBK;
-        const int kk = (k0 + 16 * cs < g.K) ? k0 : -16 * cs;   // past the end: slice 0 again (unused)
+        const int kk = (k0 + 16 * cs < Kc) ? k0 : -16 * cs;    // past the end: slice 0 again (unused)
         __builtin_amdgcn_global_load_lds((const void *)(xA + kk),
                                          (lds_void *)&dst.x[(cs * kBM + (2 * (w & 3)) * 32) * 2], 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void *)(xB + kk),
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void gemm_nt_lds32(GemmParams g) {
         const int k0 = i * kBK;
 #pragma unroll
         for (int s = 0; s < kSl; ++s) {
-            if (k0 + 16 * s >= g.K) break;
+            if (k0 + 16 * s >= Kc) break;
             u32x4 A[2], B[2];
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti) A[ti] = cur.w[(s * kBN + wc * 64 + 32 * ti + r32) * 2 + hsel];
@@ -107,35 +112,103 @@ __global__ __launch_bounds__(64 * kWaves, 4) void gemm_nt_lds32(GemmParams g) {
     }
 
     // register 4 qq + r of tile (ti, tj): column n0 + 64 wc + 32 ti + 8 qq + 4 (lane / 32) + r,
-    // row m0 + 64 wr + 32 tj + lane % 32
+    // row m0 + 64 wr + 32 tj + lane % 32.  Every load the epilogue needs (the
+    // lane's 32 biases, epilogue 2's pre-activations) is issued before the first use.
+    const bool part = g.ksplit > 1;
+    f32x4 bq[2][4];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5);
+            bq[ti][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!part && EPI != 2 && g.bias) {
+                if (nb + 3 < g.N) {
+                    bq[ti][qq] = *(const f32x4 *)(g.bias + p * g.sb + nb);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (nb + r < g.N) bq[ti][qq][r] = g.bias[p * g.sb + nb + r];
+                }
+            }
+        }
+    u32x2 zi[2][2][4];
+    if (EPI == 2) {
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) {
+            const int m = min(m0 + wr * 64 + 32 * tj + r32, g.M - 1);
+            const size_t row = p * g.sc + (size_t)m * g.ldc;
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int nb = min(n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5), g.N - 4);
+                    zi[tj][ti][qq] = *(const u32x2 *)(g.Zi + row + nb);
+                }
+        }
+    }
 #pragma unroll
     for (int tj = 0; tj < 2; ++tj) {
         const int m = m0 + wr * 64 + 32 * tj + r32;
         if (m >= g.M) continue;
-        float *crow = g.C + p * g.sc + (size_t)m * g.ldc;
+        const size_t row = part ? (((size_t)ks * g.P + p) * g.M + m) * g.N : p * g.sc + (size_t)m * g.ldc;
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
                 const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5);
+                if (nb >= g.N) continue;
                 float y[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    y[r] = acc[ti][tj][4 * qq + r] + (g.bias && nb + r < g.N ? g.bias[p * g.sb + nb + r] : 0.f);
-                if (nb + 3 < g.N) {
-                    *(f32x4 *)(crow + nb) = f32x4{y[0], y[1], y[2], y[3]};
-                } else {
+                for (int r = 0; r < 4; ++r) y[r] = acc[ti][tj][4 * qq + r] + bq[ti][qq][r];
+                if (EPI == 0) {
+                    float *c = (part ? g.Cpart : g.C) + row + nb;
+                    if (nb + 3 < g.N) {
+                        *(f32x4 *)c = f32x4{y[0], y[1], y[2], y[3]};
+                    } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (nb + r < g.N) crow[nb + r] = y[r];
+                        for (int r = 0; r < 4; ++r)
+                            if (nb + r < g.N) c[r] = y[r];
+                    }
+                } else {
+                    // bf16 outputs: widths are multiples of 32, the four columns are in range
+                    if (EPI == 1) {
+                        *(u32x2 *)(g.Zo + row + nb) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) y[r] = act_fn<ACT>(y[r]);
+                    } else {
+                        const u32x2 zz = zi[tj][ti][qq];
+                        y[0] *= act_grad_fn<ACT>(bf16lo(zz.x));
+                        y[1] *= act_grad_fn<ACT>(bf16hi(zz.x));
+                        y[2] *= act_grad_fn<ACT>(bf16lo(zz.y));
+                        y[3] *= act_grad_fn<ACT>(bf16hi(zz.y));
+                    }
+                    *(u32x2 *)(g.Y + row + nb) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
                 }
             }
     }
 }
 
-// out[p][c][r] = in[p][r][c] for r < rows, 0 for rows <= r < ldo (64 x 64 tiles).
+// C[p][m][n] = sum over the splits of the partial tiles + bias (fixed order).
+__global__ __launch_bounds__(256) void gemm_reduce(GemmParams g) {
+    const long n4 = (long)g.P * g.M * (g.N / 4);
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+        const int nq = (int)(i % (g.N / 4));
+        const long pm = i / (g.N / 4);
+        const int m = (int)(pm % g.M), p = (int)(pm / g.M);
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < g.ksplit; ++ks)
+            s += *(const f32x4 *)(g.Cpart + (((size_t)ks * g.P + p) * g.M + m) * g.N + 4 * nq);
+        if (g.bias) s += *(const f32x4 *)(g.bias + p * g.sb + 4 * nq);
+        *(f32x4 *)(g.C + p * g.sc + (size_t)m * g.ldc + 4 * nq) = s;
+    }
+}
+
+// out[p][c][r] = in[p][r][c] for r < rows, 0 for rows <= r < ldo (64 x 64
+// tiles through LDS; four elements per thread and access on both sides).
+// cols, ldi and ldo are multiples of 4.
 __global__ __launch_bounds__(256) void transpose_bf16(TransposeParams a) {
-    __shared__ uint16_t tile[64][66];
+    __shared__ uint16_t tile[64][68];
     const int tc = (a.cols + 63) / 64, tr = (a.ldo + 63) / 64;
     long b = blockIdx.x;
     const int bc = (int)(b % tc);
@@ -144,16 +217,29 @@ __global__ __launch_bounds__(256) void transpose_bf16(TransposeParams a) {
     const int r0 = br * 64, c0 = bc * 64;
     const uint16_t *in = a.in + p * a.si;
     uint16_t *out = a.out + p * a.so;
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int rr = e >> 6, cc = e & 63;
-        const int r = r0 + rr, c = c0 + cc;
-        tile[rr][cc] = (r < a.rows && c < a.cols) ? in[(size_t)r * a.ldi + c] : (uint16_t)0;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int e = threadIdx.x + 256 * it;            // 64 rows x 16 four-column groups
+        const int rr = e >> 4, cq = (e & 15) * 4;
+        const int r = r0 + rr, c = c0 + cq;
+        u32x2 v = {0u, 0u};
+        if (r < a.rows && c < a.cols) v = *(const u32x2 *)(in + (size_t)r * a.ldi + c);
+        tile[rr][cq + 0] = (uint16_t)(v.x & 0xffffu);
+        tile[rr][cq + 1] = (uint16_t)(v.x >> 16);
+        tile[rr][cq + 2] = (uint16_t)(v.y & 0xffffu);
+        tile[rr][cq + 3] = (uint16_t)(v.y >> 16);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int cc = e >> 6, rr = e & 63;
-        const int r = r0 + rr, c = c0 + cc;
-        if (c < a.cols && r < a.ldo) out[(size_t)c * a.ldo + r] = tile[rr][cc];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int e = threadIdx.x + 256 * it;            // 64 columns x 16 four-row groups
+        const int cc = e >> 4, rq = (e & 15) * 4;
+        const int r = r0 + rq, c = c0 + cc;
+        if (c < a.cols && r < a.ldo) {
+            const u32x2 v = {(uint32_t)tile[rq][cc] | ((uint32_t)tile[rq + 1][cc] << 16),
+                             (uint32_t)tile[rq + 2][cc] | ((uint32_t)tile[rq + 3][cc] << 16)};
+            *(u32x2 *)(out + (size_t)c * a.ldo + r) = v;
+        }
     }
 }
 
@@ -170,16 +256,6 @@ __global__ __launch_bounds__(256) void gather_q(GatherParams a) {
     *(u32x4 *)(a.Q + (size_t)pr * a.d + 8 * pc) = *(const u32x4 *)(a.q + src);
 }
 
-// mode 0: Y = bf16(act(Z)); mode 1: Y = bf16(dY * act'(Z)).
-template <int ACT>
-__global__ __launch_bounds__(256) void act_pass(ActParams a) {
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (long)gridDim.x * 256) {
-        const float z = a.Z[i];
-        const float y = a.mode == 0 ? act_fn<ACT>(z) : a.dY[i] * act_grad_fn<ACT>(z);
-        a.Y[i] = f32_to_bf16(y);
-    }
-}
-
 // One wave per score row: hidden values, a, the score error and its gradient,
 // and the score net's back-propagated pre-activation gradient.
 template <int ACT>
@@ -190,16 +266,59 @@ __global__ __launch_bounds__(256) void score_rows(ScoreRowParams a) {
     const int p = (int)(row / a.Rp), rho = (int)(row - (long)p * a.Rp);
     const float *z = a.Zs + (size_t)row * a.Hs;
     const uint16_t *ws2 = a.ws2 + (size_t)p * a.Hs;
+    // lane l owns units 4 l .. 4 l + 3 of every 256 (Hs is a multiple of 32: whole
+    // groups of four), loads issued four groups at a time
     float s = 0.f;
-    for (int j = lane; j < a.Hs; j += 64) s = __builtin_fmaf(bf16_to_f32(ws2[j]), act_fn<ACT>(z[j]), s);
+    for (int j0 = 4 * lane; j0 < a.Hs; j0 += 1024) {
+        f32x4 zv[4];
+        u32x2 wv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 256 * u;
+            if (j < a.Hs) {
+                zv[u] = *(const f32x4 *)(z + j);
+                wv[u] = *(const u32x2 *)(ws2 + j);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 256 * u;
+            if (j >= a.Hs) break;
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = act_fn<ACT>(zv[u][r]);
+            *(u32x2 *)(a.Ys + (size_t)row * a.Hs + j) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+            s = __builtin_fmaf(bf16lo(wv[u].x), y[0], s);
+            s = __builtin_fmaf(bf16hi(wv[u].x), y[1], s);
+            s = __builtin_fmaf(bf16lo(wv[u].y), y[2], s);
+            s = __builtin_fmaf(bf16hi(wv[u].y), y[3], s);
+        }
+    }
     s = wave_sum(s);
     const size_t o = out_row(p, rho, a.Hkv, a.G, 0, a.Hq);
     const float e = a.bs2[p] + s - a.alpha[o];
     const float ga = a.coef * e;                   // 2 lambda_alpha e / R
-    for (int j = lane; j < a.Hs; j += 64) {
-        const float zj = z[j];
-        a.Ys[(size_t)row * a.Hs + j] = f32_to_bf16(act_fn<ACT>(zj));
-        a.dZs[(size_t)row * a.Hs + j] = f32_to_bf16(ga * bf16_to_f32(ws2[j]) * act_grad_fn<ACT>(zj));
+    for (int j0 = 4 * lane; j0 < a.Hs; j0 += 1024) {
+        f32x4 zv[4];
+        u32x2 wv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 256 * u;
+            if (j < a.Hs) {
+                zv[u] = *(const f32x4 *)(z + j);
+                wv[u] = *(const u32x2 *)(ws2 + j);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 256 * u;
+            if (j >= a.Hs) break;
+            const float g0 = ga * bf16lo(wv[u].x) * act_grad_fn<ACT>(zv[u][0]);
+            const float g1 = ga * bf16hi(wv[u].x) * act_grad_fn<ACT>(zv[u][1]);
+            const float g2 = ga * bf16lo(wv[u].y) * act_grad_fn<ACT>(zv[u][2]);
+            const float g3 = ga * bf16hi(wv[u].y) * act_grad_fn<ACT>(zv[u][3]);
+            *(u32x2 *)(a.dZs + (size_t)row * a.Hs + j) = u32x2{pack_bf16(g0, g1), pack_bf16(g2, g3)};
+        }
     }
     if (lane == 0) {
         a.ga[row] = ga;
@@ -239,9 +358,26 @@ __global__ __launch_bounds__(256) void row_dot(RowDotParams a) {
     const T *x = (const T *)a.X + p * a.sx + (size_t)j * a.ldx;
     const float *v = a.v ? a.v + p * a.sv : nullptr;
     float s = 0.f;
-    for (int k = lane; k < a.K; k += 64) {
-        const float xv = Elem<T>::ld(x, k);
-        s = v ? __builtin_fmaf(xv, v[k], s) : s + xv;
+    if (sizeof(T) == 2 && a.K % 8 == 0 && a.ldx % 8 == 0) {
+        // eight bf16 per lane per iteration (16-byte loads)
+        for (int k = 8 * lane; k < a.K; k += 512) {
+            const u32x4 xv = *(const u32x4 *)((const uint16_t *)x + k);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float x0 = bf16lo(xv[u]), x1 = bf16hi(xv[u]);
+                if (v) {
+                    s = __builtin_fmaf(x0, v[k + 2 * u], s);
+                    s = __builtin_fmaf(x1, v[k + 2 * u + 1], s);
+                } else {
+                    s += x0 + x1;
+                }
+            }
+        }
+    } else {
+        for (int k = lane; k < a.K; k += 64) {
+            const float xv = Elem<T>::ld(x, k);
+            s = v ? __builtin_fmaf(xv, v[k], s) : s + xv;
+        }
     }
     s = wave_sum(s);
     if (lane == 0) a.out[p * a.so + j] = s;
@@ -269,8 +405,10 @@ __global__ __launch_bounds__(256) void sum_parts(SumParams a) {
 __global__ void train_scalars(TrainScalars a) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     double s[3] = {0.0, 0.0, 0.0};
-    for (int k = 0; k < 3; ++k)
+    for (int k = 0; k < 2; ++k)
         for (int b = 0; b < a.nparts; ++b) s[k] += a.parts[k * a.nparts + b];
+    if (a.scale)
+        for (int b = 0; b < kNormParts; ++b) s[2] += a.parts[2 * a.nparts + b];
     if (a.loss) {
         a.loss[1] = (float)(s[0] / a.R);
         a.loss[2] = (float)(s[1] / a.R);
@@ -319,11 +457,26 @@ static unsigned grid_for(long n, long per_block, long cap) {
     return (unsigned)(b < 1 ? 1 : b);
 }
 
+long gemm_blocks(const GemmParams &g) {
+    const long rg = (long)g.P * ((g.M + kBM - 1) / kBM);
+    return (rg + kXcd - 1) / kXcd * kXcd * ((g.N + kBN - 1) / kBN);
+}
+
 hipError_t launch_gemm_nt(const GemmParams &g, hipStream_t st) {
     if (g.M <= 0 || g.N <= 0 || g.P <= 0) return hipSuccess;
-    const long rg = (long)g.P * ((g.M + kBM - 1) / kBM);
-    const long blocks = (rg + kXcd - 1) / kXcd * kXcd * ((g.N + kBN - 1) / kBN);
-    hipLaunchKernelGGL(gemm_nt_lds32, dim3((unsigned)blocks), dim3(64 * kWaves), 0, st, g);
+    const dim3 grid((unsigned)(gemm_blocks(g) * (g.ksplit > 1 ? g.ksplit : 1))), block(64 * kWaves);
+#define NECTAR_GEMM(E, A) hipLaunchKernelGGL((gemm_nt_lds32<E, A>), grid, block, 0, st, g)
+    if (g.epi == 0) NECTAR_GEMM(0, 0);
+    else if (g.epi == 1 && g.act == 1) NECTAR_GEMM(1, 1);
+    else if (g.epi == 1 && g.act == 2) NECTAR_GEMM(1, 2);
+    else if (g.epi == 1) NECTAR_GEMM(1, 0);
+    else if (g.act == 1) NECTAR_GEMM(2, 1);
+    else if (g.act == 2) NECTAR_GEMM(2, 2);
+    else NECTAR_GEMM(2, 0);
+#undef NECTAR_GEMM
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || g.ksplit <= 1) return e;
+    hipLaunchKernelGGL(gemm_reduce, dim3(grid_for((long)g.P * g.M * (g.N / 4), 256, 8192)), dim3(256), 0, st, g);
     return hipGetLastError();
 }
 
@@ -337,14 +490,6 @@ hipError_t launch_transpose_bf16(const TransposeParams &t, hipStream_t st) {
 hipError_t launch_gather_q(const GatherParams &a, hipStream_t st) {
     const long n = (long)a.Hkv * a.Rp * (a.d / 8);
     hipLaunchKernelGGL(gather_q, dim3(grid_for(n, 256, 1L << 30)), dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_act_pass(const ActParams &a, int act, hipStream_t st) {
-    const dim3 grid(grid_for(a.n, 256, 8192)), block(256);
-    if (act == 1) hipLaunchKernelGGL(act_pass<1>, grid, block, 0, st, a);
-    else if (act == 2) hipLaunchKernelGGL(act_pass<2>, grid, block, 0, st, a);
-    else hipLaunchKernelGGL(act_pass<0>, grid, block, 0, st, a);
     return hipGetLastError();
 }
 

@@ -118,21 +118,22 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + fast_exp2(v));
 }
 
-// Activation fixed at compile time (0: GELU erf form, 1: SiLU, 2: GELU tanh
-// form, the values of nectar_act), so only one is evaluated.
-// erf-form GELU for the VALU-bound batched MLP kernels: x * Phi(x) with Phi
-// written as sigmoid(p(x)), p an odd polynomial of degree 9 fitted to the
-// logit of Phi (fit_gelu_erf.py; max |Phi error| 1.5e-6, so |GELU error| <=
-// 6e-6 on |x| <= 9 and less beyond).  Coefficients below are c1..c9 times
-// -log2(e), so exp2 of p(x) x gives exp(-logit).  Five multiply-adds, one exp2
-// and one reciprocal, no table.
-__device__ __forceinline__ float gelu_erf_sigmoid(float x) {
-    const float u = x * x;
-    float p = __builtin_fmaf(u, -4.153249158e-06f, 1.066830016e-04f);
-    p = __builtin_fmaf(p, u, 2.487620203e-04f);
-    p = __builtin_fmaf(p, u, -1.049971051e-01f);
-    p = __builtin_fmaf(p, u, -2.302170342e+00f);
-    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(p * x));
+// erf-form GELU for the VALU-bound batched MLP kernels: x * Phi(x) with
+// Phi(x) = 0.5 + c P(c^2), c = x clamped to [-4, 4], P of degree 7 fitted to
+// the odd part of Phi (fit_gelu_erf.py): max |Phi error| 5.3e-5, so |GELU
+// error| <= 5.3e-5 |x|.  Eleven multiply-add-class operations, no exponential
+// or reciprocal (four issue slots each on this part).
+__device__ __forceinline__ float gelu_erf_poly(float x) {
+    const float c = __builtin_amdgcn_fmed3f(x, -4.0f, 4.0f);
+    const float u = c * c;
+    float p = __builtin_fmaf(u, -1.58076696e-09f, 1.21709988e-07f);
+    p = __builtin_fmaf(p, u, -4.10084021e-06f);
+    p = __builtin_fmaf(p, u, 8.06670869e-05f);
+    p = __builtin_fmaf(p, u, -1.04820251e-03f);
+    p = __builtin_fmaf(p, u, 9.66486800e-03f);
+    p = __builtin_fmaf(p, u, -6.61753714e-02f);
+    p = __builtin_fmaf(p, u, 3.98847520e-01f);
+    return x * __builtin_fmaf(c, p, 0.5f);
 }
 
 // Derivatives of the activations (the backward pass of the training step):
@@ -165,6 +166,8 @@ template <int ACT> __device__ __forceinline__ float act_grad_fn(float x) {
     return ACT == 1 ? silu_grad(x) : (ACT == 2 ? gelu_tanh_grad(x) : gelu_erf_grad(x));
 }
 
+// Activation fixed at compile time (0: GELU erf form, 1: SiLU, 2: GELU tanh
+// form, the values of nectar_act), so only one is evaluated.
 template <int ACT> __device__ __forceinline__ float act_fn(float x) {
     return ACT == 1 ? silu(x) : (ACT == 2 ? gelu_tanh(x) : gelu_erf(x));
 }

@@ -17,7 +17,8 @@
 //       are the B operand of unit group t as they stand, and the read-out
 //       operand follows the same unit order (the attention kernel's V trick);
 //   for score chunks, a dot of H with ws2 in fp32.
-// The erf-form GELU is evaluated as x * sigmoid(p(x)) (gelu_erf_sigmoid).
+// The erf-form GELU is evaluated as x * (0.5 + c P(c^2)), c = clamp(x, -4, 4)
+// (gelu_erf_poly).
 // The unit counts of both nets must be multiples of 64 (every workload's are;
 // other widths use mlp_prefill.hip).
 #include "lds_common.hpp"
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
     const int sb = blockIdx.x % a.SB, hr = blockIdx.x / a.SB;
     const int h = hr / nrb, rb = hr - h * nrb;
 
-    auto act = [&](float x) { return ACT == 0 ? gelu_erf_sigmoid(x) : act_fn<ACT>(x); };
+    auto act = [&](float x) { return ACT == 0 ? gelu_erf_poly(x) : act_fn<ACT>(x); };
 
     const int rho = rb * kRows + w * 32 + r;
     u32x4 qv[8];

@@ -18,7 +18,8 @@
 // so the hidden activations never leave registers; score chunks run
 //   Zs^T = bs + Ws_chunk . Q^T -> act -> fp32 dot with ws2.
 //
-// The erf-form GELU is evaluated as x * sigmoid(p(x)) (gelu_erf_sigmoid).
+// The erf-form GELU is evaluated as x * (0.5 + c P(c^2)), c = clamp(x, -4, 4)
+// (gelu_erf_poly).
 // With one split (SB == 1) the block adds the output biases and writes (a, A);
 // with SB > 1 splits of the hidden units, block (h, row block, split) writes its
 // partial sums and mlp_reduce adds them in split order with the biases.
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void mlp_prefill_mfma(MlpParams a) {
     const int sb = blockIdx.x % a.SB, hr = blockIdx.x / a.SB;
     const int h = hr / nrb, rb = hr - h * nrb;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, c = lane & 15;
-    auto act = [&](float x) { return ACT == 0 ? gelu_erf_sigmoid(x) : act_fn<ACT>(x); };
+    auto act = [&](float x) { return ACT == 0 ? gelu_erf_poly(x) : act_fn<ACT>(x); };
 
     u32x4 qv[kRTW][kKS];
 #pragma unroll

@@ -26,10 +26,14 @@ many layers) are captured once in a HIP graph and replayed; timing uses HIP
 events on the replay stream around K steps (K rounded up to whole passes),
 bracketed by synchronizations.
 
-Prints one JSON line.  `value` is query-tokens/s/layer of the whole step;
-`paths` gives the Nectar and exact paths timed alone; `roofline` covers the
-dominant kernel (exact document attention, HBM-bound); `cpu_baseline` times the
-fp64 CPU oracle on a bounded sample of the same step.
+Prints one JSON line.  `value` is query-tokens/s/layer of the whole step (mean
+over the timed steps); `timing` gives the median and 10th/90th percentiles of
+the per-pass step times and the device clocks read while the step runs;
+`paths` gives the Nectar and exact paths timed alone, `components` the module,
+local attention and merge alone against their HBM rooflines; `roofline` covers
+the dominant kernel (exact document attention, HBM-bound); `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of the same step, multithreaded and on
+one thread, with the host's CPU model.
 """
 import argparse
 import hashlib
@@ -171,8 +175,13 @@ def main():
         "doc_partial": lambda r: doc_partial(r),
         # the same step through the four separate entry points (seven launches)
         "step_unfused": lambda r: (doc(r), module(r), local_nectar(r), merge_exact(r)),
+        # the components alone
+        "module": lambda r: module(r),
+        "local": lambda r: local_pair(r),
+        "merge": lambda r: merge_exact(r),
     }
-    names = [args.only] if args.only else ["step", "nectar", "exact", "doc", "doc_partial", "step_unfused"]
+    names = [args.only] if args.only else ["step", "nectar", "exact", "doc", "doc_partial", "step_unfused",
+                                           "module", "local", "merge"]
 
     # warm every call once (allocates the binding's cached workspace outside capture)
     for fn in steps.values():
@@ -214,6 +223,25 @@ def main():
 
     ms = {nm: timed(nm) for nm in names}
 
+    # spread of the step time: each pass of the step graph timed on its own
+    spread = None
+    if "step" in ms and not args.no_graph:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(passes + 1)]
+        ev[0].record()
+        for i in range(passes):
+            one_pass("step")
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) / NREP * 1e3 for i in range(passes))
+        pick = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+        spread = {"us_per_step_median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9), "passes": passes,
+                  "steps_per_pass": NREP}
+        # the clocks while the step runs: enqueue about a second of passes, then read them
+        for _ in range(max(1, int(1.0 / (ms["step"] * 1e-3 * NREP)))):
+            one_pass("step")
+        spread["clocks"] = gpu_clocks()
+        torch.cuda.synchronize()
+
     # Correctness spot check of the timed outputs against the oracle is the job of
     # the test suite; here only finite outputs are asserted.
     for k in ("out_n", "out_x"):
@@ -253,6 +281,20 @@ def main():
     if "step_unfused" in ms:
         paths["step_unfused_us"] = ms["step_unfused"] * 1e3
     res["paths"] = paths
+    if spread:
+        res["timing"] = spread
+    local_bytes = cfg.B * Hkv * T * 2 * d * 2
+    merge_bytes = R * Hq * (2 * 4 * (d + 1) + 2 * d + 4)
+    comp = {}
+    for nm, nb, what in (("module", mlp_bytes, "nectar_module_forward: MLP weights of the 8 KV heads, bf16"),
+                         ("local", local_bytes, "nectar_local_attn_lse: 513 causal local keys and values, bf16"),
+                         ("merge", merge_bytes, "nectar_merge: two fp32 pairs in, bf16 output and fp32 LSE out")):
+        if nm in ms:
+            us_c = ms[nm] * 1e3
+            comp[nm] = {"us": us_c, "bytes": nb, "gbs": nb / us_c / 1e3, "frac": nb / us_c / 1e3 / HBM_PEAK_GBS,
+                        "bound": "hbm", "what": what}
+    if comp:
+        res["components"] = comp
     if "doc_partial" in ms:
         us = ms["doc_partial"] * 1e3
         ach = doc_bytes / (us * 1e-6) / 1e9
@@ -273,7 +315,6 @@ def main():
         res["exact_doc_entry_point"] = {"us": us_e, "gbs": doc_bytes / (us_e * 1e-6) / 1e9,
                                         "frac": doc_bytes / (us_e * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                         "what": "nectar_doc_attn_exact: partial pass + combine launch"}
-        res["module_roofline_hint"] = {"bytes_per_launch": mlp_bytes}
 
     if args.only is None and not (args.no_prefill and args.no_workloads):
         del reps, graphs
@@ -639,31 +680,80 @@ def fit_metrics_prefill(torch, nectar, configs, dev):
             "what": "nectar_fit_metrics: row pass + per-KV-head fp64 sums (three launches)"}
 
 
+def gpu_clocks():
+    """The current shader, memory and fabric clock levels of the device as the
+    driver lists them (the entries marked current), read while work runs."""
+    import glob
+    out = {}
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_*clk")):
+        try:
+            with open(f) as fh:
+                cur = [ln.split(":", 1)[1].strip(" *\n") for ln in fh if ln.rstrip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            out["%s %s" % (f.split("/")[4], os.path.basename(f)[7:])] = cur[0]
+    if not out:
+        import subprocess
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+            for card, kv in json.loads(r.stdout).items():
+                for k, v in kv.items():
+                    if "clk" in k.lower():
+                        out["%s %s" % (card, k.strip(" :"))] = v
+        except (OSError, ValueError, AttributeError, subprocess.SubprocessError):
+            pass
+    return out or None
+
+
+def host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"nproc": usable, "cpu_count": os.cpu_count(), "model": model}
+
+
 def cpu_baseline(cfg, q, K, V, Kl, Vl, P, budget_s):
     """The fp64 oracle on the same step (both paths, one token), repeated until
-    the time budget is used; tokens per second per layer."""
+    the time budget is used; tokens per second per layer.  Two thirds of the
+    budget go to a run on up to 16 threads (the reported value), the rest to a
+    single-thread run."""
     import numpy as np
 
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    host = host_cpu()
+    threads = max(1, min(16, host["nproc"] or 1))
     T = cfg.local_len(0)
     Klv, Vlv = (np.ascontiguousarray(x[:, :, :T]) for x in (Kl, Vl))
-    kw = dict(dt="bf16", Hq=cfg.Hq, Hkv=cfg.Hkv, threads=threads)
-    n_tok = 0
-    t0 = time.time()
-    while True:
-        alpha, A = oracle.doc_attn(q, K, V, **kw)
-        a, Am = oracle.mlp(q, P["W1"], P["b1"], P["W2t"], P["b2"], P["Ws"], P["bs"], P["ws2"], P["bs2"], **kw)
-        lam, Al = oracle.local_attn(q, Klv, Vlv, B=cfg.B, Tq=cfg.Tq, Tloc=T, q_offset=cfg.q_offset(0), **kw)
-        oracle.merge(a, Am, lam, Al)
-        oracle.merge(alpha, A, lam, Al)
-        n_tok += cfg.R
-        el = time.time() - t0
-        if el >= budget_s:
-            break
+
+    def run(nthreads, budget):
+        kw = dict(dt="bf16", Hq=cfg.Hq, Hkv=cfg.Hkv, threads=nthreads)
+        n_tok = 0
+        t0 = time.time()
+        while True:
+            alpha, A = oracle.doc_attn(q, K, V, **kw)
+            a, Am = oracle.mlp(q, P["W1"], P["b1"], P["W2t"], P["b2"], P["Ws"], P["bs"], P["ws2"], P["bs2"], **kw)
+            lam, Al = oracle.local_attn(q, Klv, Vlv, B=cfg.B, Tq=cfg.Tq, Tloc=T, q_offset=cfg.q_offset(0), **kw)
+            oracle.merge(a, Am, lam, Al)
+            oracle.merge(alpha, A, lam, Al)
+            n_tok += cfg.R
+            el = time.time() - t0
+            if el >= budget:
+                return n_tok, el
+
+    n_tok, el = run(threads, budget_s * 2 / 3)
+    n1, el1 = run(1, budget_s / 3)
     return {"value": n_tok / el, "unit": "query-tokens/s/layer", "cores": threads, "kind": "oracle",
             "sample": "%d decode steps of the same layer (exact + Nectar paths, 1 query token x 32 heads "
-                      "each) in %.1f s" % (n_tok, el)}
+                      "each) in %.1f s" % (n_tok, el),
+            "single_core": {"value": n1 / el1, "sample": "%d steps in %.1f s" % (n1, el1)}, "host": host}
 
 
 if __name__ == "__main__":

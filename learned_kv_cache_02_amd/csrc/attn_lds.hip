@@ -263,8 +263,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
 
 // ---------------------------------------------------------------------------
 // 32 rows per wave: the same LDS ring with v_mfma_f32_32x32x16_bf16, so every
-// K and V operand read from LDS and every V transpose serves 32 query rows
-// (twice the 16-row kernel above), and a block of eight waves covers 256 rows.
+// K and V operand read from LDS serves 32 query rows (twice the 16-row kernel
+// above), and a block of eight waves covers 256 rows.
 //
 // Per 32-key tile:
 //   S^T (32 keys x 32 rows) = sum over 8 slices of 16 dims of K_slice . Q^T_slice
@@ -276,9 +276,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
 // a lane of half h; the P^T operand of key group t is simply registers
 // 8t .. 8t + 7 of that lane, provided the contraction slots of the V^T operand
 // follow the same key order: slot s of half h is key 16 t + 8 (s / 4) + 4 h + s % 4.
-// Lane l therefore reads, for each of those 8 keys, the 8 bytes holding dims
-// 4 (l % 32) .. + 3 and builds dim block mi's operand (dim 4 (l % 32) + mi)
-// with byte permutes; O^T row rho of block mi is dim 4 rho + mi.
+// Those operands come straight from the key-major V stage by gfx950's
+// transposing LDS read (ds_read_b64_tr_b16, four keys' values of one dim per
+// lane and read; no register permutes): O^T row m of block mi is dim 32 mi + m.
 template <int NW, int kStageKeys>
 __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
     constexpr int kKeysPerWave = kStageKeys / NW;
@@ -349,6 +349,25 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
         }
     };
 
+    // Byte offsets, within a 16-key block of a V stage, of the 8-byte slot this
+    // lane names for the transposing read of key half `hh` and dim block mi:
+    // key 8 hh + 4 (lane / 32) + (lane / 4) % 4, dims 32 mi + 16 ((lane / 16) % 2)
+    // + 4 (lane % 4) .. + 3 (the swizzled position of their 16-byte piece).
+    // Lane 32 h + m then receives dim 32 mi + m of keys 8 hh + 4 h + 0..3, the
+    // contraction order of the P^T operand.
+    uint32_t voff[2][4];
+    {
+        const int G = lane >> 4, aa = lane & 3, e = (lane >> 2) & 3;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const int key = 8 * hh + 4 * (G >> 1) + e;
+                const int piece = 4 * mi + 2 * (G & 1) + (aa >> 1);
+                voff[hh][mi] = (uint32_t)(key * kPieces * 16 + ((piece ^ key) * 16) + (aa & 1) * 8);
+            }
+    }
+
     f32x16 O[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) O[mi] = f32x16{};
@@ -360,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
         stage_barrier();
         if (i + 2 < nst) issue(i + 2, ahead);
         const u32x4 *Ks = cur[0];
-        const uint2 *Vs = (const uint2 *)cur[1];
+        const u32x4 *Vs = cur[1];
 #pragma unroll
         for (int sub = 0; sub < kStageKeys / 32; ++sub) {
             const int kbase = k_lo + i * kStageKeys + 32 * sub;
@@ -399,23 +418,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
             for (int tg = 0; tg < 2; ++tg) {
                 const u32x4 P = {pack_bf16(pv[8 * tg + 0], pv[8 * tg + 1]), pack_bf16(pv[8 * tg + 2], pv[8 * tg + 3]),
                                  pack_bf16(pv[8 * tg + 4], pv[8 * tg + 5]), pack_bf16(pv[8 * tg + 6], pv[8 * tg + 7])};
-                // dims 4r .. 4r + 3 of the 8 keys of slots s = 0..7
-                uint2 x[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const int key = 32 * sub + 16 * tg + 8 * (s >> 2) + 4 * hf + (s & 3);
-                    x[s] = Vs[(key * kPieces + ((r >> 1) ^ (key & 15))) * 2 + (r & 1)];
-                }
+                // V^T operand of dim block mi, straight from LDS by transposing reads
+                const char *vblk = (const char *)Vs + (32 * sub + 16 * tg) * (kPieces * 16);
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) {
-                    u32x4 vt;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t w0 = (mi >> 1) ? x[2 * j].y : x[2 * j].x;
-                        const uint32_t w1 = (mi >> 1) ? x[2 * j + 1].y : x[2 * j + 1].x;
-                        vt[j] = __builtin_amdgcn_perm(w1, w0, (mi & 1) ? 0x07060302u : 0x05040100u);
-                    }
-                    O[mi] = mfma32(vt, P, O[mi]);
+                    const u32x2 h0 = lds_read_tr16(vblk, voff[0][mi]), h1 = lds_read_tr16(vblk, voff[1][mi]);
+                    O[mi] = mfma32(u32x4{h0.x, h0.y, h1.x, h1.y}, P, O[mi]);
                 }
             }
         }
@@ -432,7 +440,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
     l += __shfl_xor(l, 32, 64);
     if (rho >= a.Rp) return;
 
-    // register i of block mi holds dim 4 * rho_i + mi, rho_i = 8 (i / 4) + 4 hf + i % 4
+    // registers 4q .. 4q + 3 of block mi hold dims 32 mi + 8 q + 4 hf + 0..3
     const bool empty = (m == -INFINITY);
     if (a.SB == 1 && !a.defer) {
         const size_t o = out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq);
@@ -452,8 +460,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int dc = 4 * (8 * (i >> 2) + 4 * hf + (i & 3));
-            const f32x4 v = {O[0][i], O[1][i], O[2][i], O[3][i]};
+            const int mi = i >> 2, q = i & 3;
+            const int dc = 32 * mi + 8 * q + 4 * hf;
+            const f32x4 v = {O[mi][4 * q], O[mi][4 * q + 1], O[mi][4 * q + 2], O[mi][4 * q + 3]};
             if (a.A_out) *(f32x4 *)(a.A_out + o * kD + dc) = v * inv;
             if (a.x_lse && a.out) {
                 const f32x4 xa = *(const f32x4 *)(a.x_A + o * kD + dc);
@@ -468,8 +477,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
         float *op = a.part_O + row * kD;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int dc = 4 * (8 * (i >> 2) + 4 * hf + (i & 3));
-            *(f32x4 *)(op + dc) = f32x4{O[0][i], O[1][i], O[2][i], O[3][i]};
+            const int mi = i >> 2, q = i & 3;
+            *(f32x4 *)(op + 32 * mi + 8 * q + 4 * hf) = f32x4{O[mi][4 * q], O[mi][4 * q + 1], O[mi][4 * q + 2], O[mi][4 * q + 3]};
         }
     }
 }

@@ -16,6 +16,19 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16): every lane names one 8-byte slot
+// of four 16-bit elements; in each group of 16 lanes, lane 4a + b receives
+// element b of the slots named by lanes a, a + 4, a + 8 and a + 12 of its
+// group, in that order.  `byte_off` is a byte offset from `base`.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void *base, uint32_t byte_off) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)((__attribute__((address_space(3))) char *)base + byte_off));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 // Workgroup barrier that the compiler may not move memory operations across
 // (the bare builtin is not a memory barrier to the optimiser) and that adds
 // no waits of its own: the LDS copies are waited for explicitly above it.

@@ -15,7 +15,8 @@
 //   H = act(Z), and for target chunks O^T (128 x 32) += W2t^T . H^T as
 //       4 dim blocks x 2 unit groups: H's accumulator registers 8t .. 8t + 7
 //       are the B operand of unit group t as they stand, and the read-out
-//       operand follows the same unit order (the attention kernel's V trick);
+//       operand, in the same unit order, comes from the unit-major read-out
+//       stage by transposing LDS reads (ds_read_b64_tr_b16);
 //   for score chunks, a dot of H with ws2 in fp32.
 // The erf-form GELU is evaluated as x * (0.5 + c P(c^2)), c = clamp(x, -4, 4)
 // (gelu_erf_poly).
@@ -104,6 +105,24 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
         }
     };
 
+    // Byte offsets, within a 16-unit block of a read-out stage, of the 8-byte
+    // slot this lane names for the transposing read of unit half `hh` and dim
+    // block mi: unit 8 hh + 4 (lane / 32) + (lane / 4) % 4, dims 32 mi + 16
+    // ((lane / 16) % 2) + 4 (lane % 4) .. + 3.  Lane 32 h + m then receives dim
+    // 32 mi + m of units 8 hh + 4 h + 0..3, the contraction order of H^T.
+    uint32_t woff[2][4];
+    {
+        const int G = lane >> 4, aa = lane & 3, e = (lane >> 2) & 3;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const int u = 8 * hh + 4 * (G >> 1) + e;
+                const int piece = 4 * mi + 2 * (G & 1) + (aa >> 1);
+                woff[hh][mi] = (uint32_t)(u * kPieces * 16 + ((piece ^ u) * 16) + (aa & 1) * 8);
+            }
+    }
+
     f32x16 O[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) O[mi] = f32x16{};
@@ -120,7 +139,6 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
         stage_barrier();
         if (i + 2 < nst) issue(i + 2, ahead);
         const bool tgt = i < ntg;
-        const uint2 *W2s = (const uint2 *)cur.w2;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             // bias of the lane's 16 units 32c + 8q + 4hf + (0..3) as the accumulator's start
@@ -142,22 +160,12 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
                 for (int tg = 0; tg < 2; ++tg) {
                     const u32x4 H = {pack_bf16(hv[8 * tg + 0], hv[8 * tg + 1]), pack_bf16(hv[8 * tg + 2], hv[8 * tg + 3]),
                                      pack_bf16(hv[8 * tg + 4], hv[8 * tg + 5]), pack_bf16(hv[8 * tg + 6], hv[8 * tg + 7])};
-                    uint2 x[8];
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const int u = 32 * c + 16 * tg + 8 * (s >> 2) + 4 * hf + (s & 3);
-                        x[s] = W2s[(u * kPieces + ((r >> 1) ^ (u & 15))) * 2 + (r & 1)];
-                    }
+                    // W2^T operand of dim block mi, straight from LDS by transposing reads
+                    const char *ublk = (const char *)cur.w2 + (32 * c + 16 * tg) * (kPieces * 16);
 #pragma unroll
                     for (int mi = 0; mi < 4; ++mi) {
-                        u32x4 vt;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t w0 = (mi >> 1) ? x[2 * j].y : x[2 * j].x;
-                            const uint32_t w1 = (mi >> 1) ? x[2 * j + 1].y : x[2 * j + 1].x;
-                            vt[j] = __builtin_amdgcn_perm(w1, w0, (mi & 1) ? 0x07060302u : 0x05040100u);
-                        }
-                        O[mi] = mfma32(vt, H, O[mi]);
+                        const u32x2 h0 = lds_read_tr16(ublk, woff[0][mi]), h1 = lds_read_tr16(ublk, woff[1][mi]);
+                        O[mi] = mfma32(u32x4{h0.x, h0.y, h1.x, h1.y}, H, O[mi]);
                     }
                 }
             } else {
@@ -184,15 +192,15 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
     sc += __shfl_xor(sc, 32, 64);
     if (rho >= a.Rp) return;
 
-    // register i of block mi holds dim 4 * rho_i + mi, rho_i = 8 (i / 4) + 4 hf + i % 4
+    // registers 4q .. 4q + 3 of block mi hold dims 32 mi + 8 q + 4 hf + 0..3
     if (a.SB > 1 || a.defer) {
         const size_t row = (size_t)(h * a.SB + sb) * a.Rp + rho;
         if (hf == 0) a.part_s[row] = sc;
         float *op = a.part_O + row * kD;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int dc = 4 * (8 * (i >> 2) + 4 * hf + (i & 3));
-            *(f32x4 *)(op + dc) = f32x4{O[0][i], O[1][i], O[2][i], O[3][i]};
+            const int mi = i >> 2, q = i & 3;
+            *(f32x4 *)(op + 32 * mi + 8 * q + 4 * hf) = f32x4{O[mi][4 * q], O[mi][4 * q + 1], O[mi][4 * q + 2], O[mi][4 * q + 3]};
         }
         return;
     }
@@ -202,9 +210,10 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
     const float *b2 = a.b2 + (size_t)h * kD;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int dc = 4 * (8 * (i >> 2) + 4 * hf + (i & 3));
+        const int mi = i >> 2, q = i & 3;
+        const int dc = 32 * mi + 8 * q + 4 * hf;
         const f32x4 bb = *(const f32x4 *)(b2 + dc);
-        *(f32x4 *)(a.A_out + o * kD + dc) = bb + f32x4{O[0][i], O[1][i], O[2][i], O[3][i]};
+        *(f32x4 *)(a.A_out + o * kD + dc) = bb + f32x4{O[mi][4 * q], O[mi][4 * q + 1], O[mi][4 * q + 2], O[mi][4 * q + 3]};
     }
 }
 

@@ -158,8 +158,14 @@ __device__ __forceinline__ void attn_partial_body(const AttnParams &a, int blk_i
         for (int mm = 0; mm < DV; ++mm) O[rt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int k_lo = s * a.chunk;
-    const int k_hi = min(k_lo + a.chunk, wlim);
+    int k_lo, k_hi;
+    if (a.tiles > 0) {
+        k_lo = (int)((long)s * a.tiles / a.S) * a.chunk;
+        k_hi = min((int)((long)(s + 1) * a.tiles / a.S) * a.chunk, wlim);
+    } else {
+        k_lo = s * a.chunk;
+        k_hi = min(k_lo + a.chunk, wlim);
+    }
     if (k_lo < k_hi) {
         // Batches of SUB 32-key tiles: every load of a batch (SUB x 16 KB) is
         // issued before its first use, and the two waves sharing each SIMD keep

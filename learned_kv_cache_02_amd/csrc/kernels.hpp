@@ -20,6 +20,9 @@ struct AttnParams {
     // its WS splits together, leaving SB = ceil(S / WS) partials per row;
     // RB = ceil(RG / WR).  fp32 path: one wave per (row, split), SB = S.
     int P, S, chunk, RG, WR, WS, RB, SB;
+    // > 0 (register-direct kernel): balanced splits, split s covering key tiles
+    // [s * tiles / S, (s + 1) * tiles / S) of `chunk` keys each
+    int tiles;
     int xcd_group;       // LDS-staged kernel: row blocks of a split share an XCD
     int defer;           // write partials even when SB == 1 (a later pass finishes)
     float *part_O;       // [P][SB][Rp][d]    unnormalised read-out

@@ -152,10 +152,11 @@ def test_doc_attn_validation(lib):
 
 def test_workspace_sizes(lib):
     # n = 61,440 document keys, 8 KV heads, 4 query heads per group, one token:
-    # 240 splits of 256 keys folded four per block -> 60 partials per row,
-    # 4 rows per head, (128 + 2) floats per row.
+    # 960 batches of 64 keys in 256 balanced splits (3 or 4 batches each)
+    # folded four per block -> 64 partials per row, 4 rows per head,
+    # (128 + 2) floats per row.
     d = Desc(1, 32, 8, 128, 1, 0.0, 0)
-    assert lib.nectar_doc_attn_workspace_size(ctypes.byref(d), 61440) == 8 * 60 * 4 * 520
+    assert lib.nectar_doc_attn_workspace_size(ctypes.byref(d), 61440) == 8 * 64 * 4 * 520
     assert lib.nectar_doc_attn_workspace_size(ctypes.byref(d), 0) == 0
     assert lib.nectar_doc_attn_workspace_size(None, 10) == 0
     d1 = Desc(1, 32, 8, 128, 1, 0.0, 1)          # one split: the block finishes rows in place
@@ -434,8 +435,8 @@ def test_doc_attn_two_pass_validation(lib):
     lib.nectar_doc_attn_partials.argtypes = [D, ctypes.c_int64, P, P, P, P, ctypes.c_size_t, P]
     lib.nectar_doc_attn_combine.argtypes = [D, ctypes.c_int64, P, ctypes.c_size_t, P, P, P]
     d = Desc(1, 32, 8, 128, 1, 0.0, 0)
-    # same plan as the one-call form: 60 partials per row, 4 rows per head, 520 B each
-    assert lib.nectar_doc_attn_partials_size(ctypes.byref(d), 61440) == 8 * 60 * 4 * 520
+    # same plan as the one-call form: 64 partials per row, 4 rows per head, 520 B each
+    assert lib.nectar_doc_attn_partials_size(ctypes.byref(d), 61440) == 8 * 64 * 4 * 520
     d1 = Desc(1, 32, 8, 128, 1, 0.0, 1)          # one split: still one partial per row
     assert lib.nectar_doc_attn_partials_size(ctypes.byref(d1), 61440) == 8 * 1 * 4 * 520
     assert lib.nectar_doc_attn_partials_size(ctypes.byref(d), 0) == 0

@@ -369,9 +369,13 @@ NECTAR_API nectar_status nectar_mlp_train_step(const nectar_attn_desc *desc, con
  * (alpha, A) over k, v [Hkv][n][d] (as nectar_doc_attn_exact) when any exact
  * output is requested, and the module pair (a, A) (as nectar_module_forward)
  * when `module` is given, and merges each document-side pair with the local
- * pair (Eqs. (3.4)-(3.5)).  The parts' split partials go to the workspace and
- * one finishing pass folds them all, so the step takes (number of parts + 1)
- * kernel launches.  Outputs (all optional; NULL skips, at least one given):
+ * pair (Eqs. (3.4)-(3.5)).  On fp32, and on bf16 at decode shapes (at most 16
+ * query rows per KV head, one-hidden-layer or KV-pair module), every part's
+ * split partials come from one launch and one finishing launch folds them all
+ * and writes every pair and merged output (two launches); otherwise (more rows,
+ * or a deep module) each part runs its own kernels and the local pass merges
+ * in place.
+ * Outputs (all optional; NULL skips, at least one given):
  *   out_exact [R][Hq][d] (dtype), lse_exact [R][Hq]: exact path output;
  *   alpha_out, A_out: the exact document pair (the regression targets);
  *   out_nectar, lse_nectar: Nectar path output; a_out, Am_out: the module pair

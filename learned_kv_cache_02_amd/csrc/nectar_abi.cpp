@@ -102,7 +102,8 @@ void block_shape(int RG, int &WR, int &WS, int &RB) {
 // batches each (every CU gets the same share: the 4B document's 960 batches in
 // 256 splits = 512 blocks, two per CU, instead of 240 splits of 4 = 480 blocks);
 // otherwise every split but the last covers the same whole number of batches.
-AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv, bool balanced = true) {
+AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv, bool balanced = true,
+                   long target_waves = kTargetWaves) {
     AttnPlan pl;
     pl.P = P;
     pl.Rp = Rp;
@@ -140,7 +141,7 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv, bool bal
         pl.RG = Rp;
         units = (long)P * Rp;
     }
-    long S = d->splits > 0 ? d->splits : cdiv(kTargetWaves, units);
+    long S = d->splits > 0 ? d->splits : cdiv(target_waves, units);
     S = S < 1 ? 1 : (S > tiles ? tiles : S);
     if (mfma && balanced && d->splits <= 0) {
         pl.chunk = (int)gran;
@@ -997,11 +998,12 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
                 (!sp.kvp || decode(sp.kvpl))));
     if (sp.fused) {
         if (sp.mlp && exact) sp.mlpl = plan_mlp(d, m->Ht, m->Hs, kTargetWavesMlpShared);
-        // with a module in the same launch the document keeps a few block slots
-        // free from the start (480 of 512 at the 4B layer), so the module's
-        // blocks run beside the document's instead of after them (balanced
-        // splits here measured 59.7 -> 61.2 us for the 4B step)
-        if (exact && m) sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n, false);
+        // with a module in the same launch the document leaves 64 of the 512
+        // two-per-CU block slots free from the start, so the module's blocks run
+        // beside the document's instead of after them (4B step: all 512 slots
+        // to the document 61.2 us, 480 in whole-batch splits 59.8 us, 448
+        // balanced 59.2 us)
+        if (exact && m) sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n, true, kTargetWaves - 256);
         size_t off = align256(attn_partial_bytes(d, sp.loc));
         if (exact) {
             sp.off_doc = off;

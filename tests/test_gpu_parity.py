@@ -51,6 +51,25 @@ def test_doc_attn_bf16(nx, d, R, Hq, Hkv, n, splits):
     check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
 
 
+@pytest.mark.parametrize("n", [19217, 61457])
+def test_doc_attn_balanced_splits(nx, n):
+    """Decode rows (4 per KV head): the automatic plan spreads the 64-key batches
+    over 256 splits per head unevenly (301 batches: one or two per split; 961:
+    three or four) with a ragged last batch."""
+    R, Hq, Hkv, d = 1, 32, 8, 128
+    print("case doc_attn balanced splits n=%d" % n, flush=True)
+    g = _rng(3, n)
+    q, K, V = (_bf(g.standard_normal(s)) for s in ((R, Hq, d), (Hkv, n, d), (Hkv, n, d)))
+    a, A = nx.doc_attn_exact(dev(q), dev(K), dev(V), Hkv)
+    ea, eA = oracle.doc_attn(q, K, V, dt="bf16", Hq=Hq, Hkv=Hkv)
+    check("alpha", host(a), ea, 1e-3)
+    check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
+    # the two-pass form follows the same plan and agrees bit for bit
+    part = nx.doc_attn_partials(dev(q), dev(K), dev(V), Hkv)
+    a2, A2 = nx.doc_attn_combine(part, R, Hq, Hkv, d, n, nx.BF16)
+    assert np.array_equal(host(a2), host(a)) and np.array_equal(host(A2), host(A))
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_doc_attn_f32(nx, d):
     R, Hq, Hkv, n = 5, 6, 2, 300

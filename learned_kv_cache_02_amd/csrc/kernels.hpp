@@ -121,6 +121,10 @@ struct GemmParams {
     int ldx, ldw, ldc;
     int M, N, K, P;
     int epi, act, ksplit, kchunk;
+    // TN products only (nullable): xsum[p * sxs + m] = sum_k X[p][k][m], with
+    // per-split partials in xsum_part [ksplit][P][M] when the contraction is split
+    float *xsum, *xsum_part;
+    long sxs;
 };
 // out[p][c][r] = in[p][r][c] for r < rows, zero for rows <= r < ldo.
 struct TransposeParams {
@@ -157,6 +161,14 @@ struct RowDotParams {        // out[p * so + j] = sum_k X[p][j][k] * (v ? v[p][k
     long sx, sv, so;
     int ldx, J, K, P;
 };
+struct ColSumParams {         // out[p * so + col] = sum_row X[p][row][col] * (v ? v[p][row] : 1)
+    const uint16_t *X;
+    const float *v;
+    float *parts;            // [P][ceil(rows / 64)][cols] fixed-order partial sums
+    float *out;
+    long sx, sv, so;
+    int ldx, rows, cols, P;
+};
 constexpr int kNormParts = 1024;   // blocks of the gradient-norm sum
 struct SumParams {           // parts[part0 + b] = fixed-order fp64 sum of block b's range
     const float *x;
@@ -188,6 +200,8 @@ struct WriteParams {
 };
 long gemm_blocks(const GemmParams &g);
 hipError_t launch_gemm_nt(const GemmParams &g, hipStream_t st);
+hipError_t launch_gemm_tn(const GemmParams &g, hipStream_t st);
+hipError_t launch_col_sum(const ColSumParams &a, hipStream_t st);
 hipError_t launch_transpose_bf16(const TransposeParams &t, hipStream_t st);
 hipError_t launch_gather_q(const GatherParams &a, hipStream_t st);
 hipError_t launch_score_rows(const ScoreRowParams &a, int act, hipStream_t st);

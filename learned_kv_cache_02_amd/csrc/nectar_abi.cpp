@@ -675,11 +675,11 @@ namespace {
 constexpr int kTrainParts = 64, kMaxSplit = 8;
 
 struct TrainLayout {
-    int Rp = 0, Rpad = 0, Ht = 0, Hs = 0, d = 0, Hkv = 0;
+    int Rp = 0, Ht = 0, Hs = 0, d = 0, Hkv = 0;
     // flat parameter offsets (elements): W1, b1, W2t, b2, Ws, bs, ws2, bs2, total
     long off[9] = {};
     // workspace offsets (bytes)
-    size_t Q, Qt, Zb, Yt, Ytt, W2tT, Aout, gA, gAt, Zs, Ys, Yst, dZs, dZst, ga, es, et, Cpart, parts, scale, bytes;
+    size_t Q, Zb, Yt, W2tT, Aout, gA, Zs, Ys, dZs, ga, es, et, Cpart, xsp, csp, parts, scale, bytes;
 };
 
 TrainLayout train_layout(const nectar_attn_desc *d, const nectar_module *m) {
@@ -687,32 +687,28 @@ TrainLayout train_layout(const nectar_attn_desc *d, const nectar_module *m) {
     const long H = d->Hkv;
     L.Hkv = d->Hkv; L.d = d->d; L.Ht = m->Ht; L.Hs = m->Hs;
     L.Rp = d->R * (d->Hq / d->Hkv);
-    L.Rpad = (L.Rp + 31) / 32 * 32;
     const long sizes[8] = {H * L.Ht * L.d, H * L.Ht, H * L.Ht * L.d, H * L.d,
                            H * L.Hs * L.d, H * L.Hs, H * L.Hs, H};
     L.off[0] = 0;
     for (int i = 0; i < 8; ++i) L.off[i + 1] = L.off[i] + sizes[i];
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
-    const size_t R = (size_t)H * L.Rp, Rq = (size_t)H * L.Rpad;
+    const size_t R = (size_t)H * L.Rp;
     L.Q = take(R * L.d * 2);
-    L.Qt = take(Rq * L.d * 2);
     L.Zb = take(R * L.Ht * 2);
     L.Yt = take(R * L.Ht * 2);
-    L.Ytt = take(Rq * L.Ht * 2);
     L.W2tT = take((size_t)H * L.d * L.Ht * 2);
     L.Aout = take(R * L.d * 4);
     L.gA = take(R * L.d * 2);
-    L.gAt = take(Rq * L.d * 2);
     L.Zs = take(R * L.Hs * 4);
     L.Ys = take(R * L.Hs * 2);
-    L.Yst = take(Rq * L.Hs * 2);
     L.dZs = take(R * L.Hs * 2);
-    L.dZst = take(Rq * L.Hs * 2);
     L.ga = take(R * 4);
     L.es = take(R * 4);
     L.et = take(R * 4);
     L.Cpart = take((size_t)kMaxSplit * H * std::max(std::max(L.Rp, L.Ht), L.Hs) * L.d * 4);
+    L.xsp = take((size_t)kMaxSplit * H * std::max(L.Ht, L.Hs) * 4);
+    L.csp = take((size_t)H * ((L.Rp + 63) / 64) * std::max(L.Hs, L.d) * 4);
     L.parts = take((2 * kTrainParts + kNormParts) * 8);
     L.scale = take(2 * 4);
     L.bytes = o;
@@ -773,7 +769,7 @@ RowDotParams rowdot(const void *X, long sx, int ldx, const float *v, long sv, fl
 hipError_t run_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, const TrainLayout &L, const void *q,
                          const float *alpha, const float *Atgt, float lam_alpha, float lam_A, float *grad,
                          char *w, hipStream_t st) {
-    const int P = L.Hkv, Rp = L.Rp, Rq = L.Rpad, d = L.d, Ht = L.Ht, Hs = L.Hs;
+    const int P = L.Hkv, Rp = L.Rp, d = L.d, Ht = L.Ht, Hs = L.Hs;
     auto B = [&](size_t off) { return (void *)(w + off); };
     auto F = [&](size_t off) { return (float *)(w + off); };
     hipError_t e = hipSuccess;
@@ -783,7 +779,6 @@ hipError_t run_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, c
     gq.q = (const uint16_t *)q; gq.Q = (uint16_t *)B(L.Q);
     gq.Hq = desc->Hq; gq.G = desc->Hq / desc->Hkv; gq.Hkv = P; gq.Rp = Rp; gq.d = d;
     run(launch_gather_q(gq, st));
-    run(launch_transpose_bf16(transpose(B(L.Q), (long)Rp * d, d, B(L.Qt), (long)d * Rq, Rq, Rp, d, P), st));
     // forward: pre-activations (bias included), hidden values, read-out
     GemmParams gz = gemm(B(L.Q), (long)Rp * d, d, m->W1, (long)Ht * d, d, m->b1, Ht, nullptr, (long)Rp * Ht, Ht,
                          Rp, Ht, d, P);
@@ -791,7 +786,6 @@ hipError_t run_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, c
     run(launch_gemm_nt(gz, st));
     run(launch_gemm_nt(gemm(B(L.Q), (long)Rp * d, d, m->Ws, (long)Hs * d, d, m->bs, Hs, F(L.Zs), (long)Rp * Hs, Hs,
                             Rp, Hs, d, P), st));
-    run(launch_transpose_bf16(transpose(B(L.Yt), (long)Rp * Ht, Ht, B(L.Ytt), (long)Ht * Rq, Rq, Rp, Ht, P), st));
     run(launch_transpose_bf16(transpose(m->W2t, (long)Ht * d, d, B(L.W2tT), (long)d * Ht, Ht, Ht, d, P), st));
     run(launch_gemm_nt(with_split(gemm(B(L.Yt), (long)Rp * Ht, Ht, B(L.W2tT), (long)d * Ht, Ht, m->b2, d,
                                        F(L.Aout), (long)Rp * d, d, Rp, d, Ht, P), F(L.Cpart)), st));
@@ -807,30 +801,37 @@ hipError_t run_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, c
     sp.coef = 2.0f * lam_alpha / (float)desc->R;
     sp.Hq = desc->Hq; sp.G = desc->Hq / desc->Hkv; sp.Hkv = P; sp.Rp = Rp; sp.Hs = Hs;
     run(launch_score_rows(sp, m->act, st));
-    run(launch_transpose_bf16(transpose(B(L.gA), (long)Rp * d, d, B(L.gAt), (long)d * Rq, Rq, Rp, d, P), st));
-    run(launch_transpose_bf16(transpose(B(L.Ys), (long)Rp * Hs, Hs, B(L.Yst), (long)Hs * Rq, Rq, Rp, Hs, P), st));
-    run(launch_transpose_bf16(transpose(B(L.dZs), (long)Rp * Hs, Hs, B(L.dZst), (long)Hs * Rq, Rq, Rp, Hs, P), st));
-    // target read-out gradient, then back through it
+    // weight gradients: contractions over the rows of the row-major buffers
+    // (TN products), bias gradients as fixed-order column sums
     float *gW1 = grad + L.off[0], *gb1 = grad + L.off[1], *gW2t = grad + L.off[2], *gb2 = grad + L.off[3];
     float *gWs = grad + L.off[4], *gbs = grad + L.off[5], *gws2 = grad + L.off[6], *gbs2 = grad + L.off[7];
-    run(launch_gemm_nt(with_split(gemm(B(L.Ytt), (long)Ht * Rq, Rq, B(L.gAt), (long)d * Rq, Rq, nullptr, 0, gW2t,
-                                       (long)Ht * d, d, Ht, d, Rq, P), F(L.Cpart)), st));
+    auto colsum = [&](const void *X, long sx, int ldx, int cols, const float *v, float *out, long so) {
+        ColSumParams c{};
+        c.X = (const uint16_t *)X; c.v = v; c.parts = F(L.csp); c.out = out;
+        c.sx = sx; c.sv = Rp; c.so = so; c.ldx = ldx; c.rows = Rp; c.cols = cols; c.P = P;
+        run(launch_col_sum(c, st));
+    };
+    // target read-out: dW2t = Y^T gA (before Y's buffer takes dZ_t), db2 = column sums of gA
+    run(launch_gemm_tn(with_split(gemm(B(L.Yt), (long)Rp * Ht, Ht, B(L.gA), (long)Rp * d, d, nullptr, 0, gW2t,
+                                       (long)Ht * d, d, Ht, d, Rp, P), F(L.Cpart)), st));
+    colsum(B(L.gA), (long)Rp * d, d, d, nullptr, gb2, d);
     // dZ_t = (gA W2t) * act'(Z), bf16, into the hidden-value buffer (no longer needed)
     GemmParams gd = gemm(B(L.gA), (long)Rp * d, d, m->W2t, (long)Ht * d, d, nullptr, 0, nullptr, (long)Rp * Ht, Ht,
                          Rp, Ht, d, P);
     gd.epi = 2; gd.act = m->act; gd.Zi = (const uint16_t *)B(L.Zb); gd.Y = (uint16_t *)B(L.Yt);
     run(launch_gemm_nt(gd, st));
-    run(launch_transpose_bf16(transpose(B(L.Yt), (long)Rp * Ht, Ht, B(L.Ytt), (long)Ht * Rq, Rq, Rp, Ht, P), st));
-    // first-layer gradients (contractions over the rows)
-    run(launch_gemm_nt(with_split(gemm(B(L.Ytt), (long)Ht * Rq, Rq, B(L.Qt), (long)d * Rq, Rq, nullptr, 0, gW1,
-                                       (long)Ht * d, d, Ht, d, Rq, P), F(L.Cpart)), st));
-    run(launch_gemm_nt(with_split(gemm(B(L.dZst), (long)Hs * Rq, Rq, B(L.Qt), (long)d * Rq, Rq, nullptr, 0, gWs,
-                                       (long)Hs * d, d, Hs, d, Rq, P), F(L.Cpart)), st));
-    // bias and score read-out gradients: fixed-order row sums
-    run(launch_row_dot(rowdot(B(L.Ytt), (long)Ht * Rq, Rq, nullptr, 0, gb1, Ht, Ht, Rq, P), 0, st));
-    run(launch_row_dot(rowdot(B(L.gAt), (long)d * Rq, Rq, nullptr, 0, gb2, d, d, Rq, P), 0, st));
-    run(launch_row_dot(rowdot(B(L.dZst), (long)Hs * Rq, Rq, nullptr, 0, gbs, Hs, Hs, Rq, P), 0, st));
-    run(launch_row_dot(rowdot(B(L.Yst), (long)Hs * Rq, Rq, F(L.ga), Rp, gws2, Hs, Hs, Rp, P), 0, st));
+    // first layers: dW1 = dZ_t^T Q, dWs = dZ_s^T Q; their biases; the score read-out
+    // (the bias gradients db1, dbs are the column sums of the X operands, formed
+    // inside the same products)
+    auto with_xsum = [&](GemmParams g, float *xsum, long sxs) {
+        g.xsum = xsum; g.xsum_part = F(L.xsp); g.sxs = sxs;
+        return g;
+    };
+    run(launch_gemm_tn(with_xsum(with_split(gemm(B(L.Yt), (long)Rp * Ht, Ht, B(L.Q), (long)Rp * d, d, nullptr, 0,
+                                                 gW1, (long)Ht * d, d, Ht, d, Rp, P), F(L.Cpart)), gb1, Ht), st));
+    run(launch_gemm_tn(with_xsum(with_split(gemm(B(L.dZs), (long)Rp * Hs, Hs, B(L.Q), (long)Rp * d, d, nullptr, 0,
+                                                 gWs, (long)Hs * d, d, Hs, d, Rp, P), F(L.Cpart)), gbs, Hs), st));
+    colsum(B(L.Ys), (long)Rp * Hs, Hs, Hs, F(L.ga), gws2, Hs);
     run(launch_row_dot(rowdot(F(L.ga), Rp, Rp, nullptr, 0, gbs2, 1, 1, Rp, P), 1, st));
     // loss sums
     SumParams su{};

@@ -3,18 +3,19 @@
 // the loss lambda_alpha L_alpha + lambda_A L_A, the backward, global-norm
 // gradient clipping and AdamW on fp32 master parameters.
 //
-// Every dense contraction -- the two first layers, the target read-out, the
-// back-propagation through the read-out and the three weight gradients (whose
-// contraction runs over the query rows) -- is one batched "NT" product
-//   C[p][m][n] = sum_k X[p][m][k] W[p][n][k] (+ bias[p][n])
-// on the 32x32x16 bf16 MFMA (gemm_nt_lds32): both operands row-major with the
-// contraction innermost, so the products over rows read transposed copies
-// made by transpose_bf16 (64 x 64 tiles through LDS, the row count padded to a
-// multiple of 32 with zeros).  The elementwise passes (activation, its
+// The dense contractions run on the 32x32x16 bf16 MFMA in two batched forms:
+// the two first layers, the target read-out and the back-propagation through
+// it are "NT" products
+//   C[p][m][n] = sum_k X[p][m][k] W[p][n][k] (+ bias[p][n])   (gemm_nt_lds32)
+// with both operands row-major and the contraction innermost (the read-out's
+// weights go through one small transposed copy, transpose_bf16); the three
+// weight gradients, whose contraction runs over the query rows, are "TN"
+// products C[p][m][n] = sum_k X[p][k][m] W[p][k][n] (gemm_tn_lds32) that read
+// the row-major hidden values and gradients as they are, their MFMA operands
+// formed by transposing LDS reads.  The elementwise passes (activation, its
 // derivative, the per-row score net and loss terms) and the bias gradients
-// (row sums of the transposed buffers, fixed order) are plain VALU kernels;
-// sums that feed the loss and the clipping norm are fixed-order, so a step is
-// reproducible.
+// (fixed-order column sums) are plain VALU kernels; sums that feed the loss and
+// the clipping norm are fixed-order, so a step is reproducible.
 #include "attn_common.hpp"
 #include "lds_common.hpp"
 
@@ -189,8 +190,237 @@ __global__ __launch_bounds__(64 * kWaves, 4) void gemm_nt_lds32(GemmParams g) {
     }
 }
 
-// C[p][m][n] = sum over the splits of the partial tiles + bias (fixed order).
+// "TN" product for the contractions over the query rows (the weight
+// gradients): C[p][m][n] = sum_k X[p][k][m] W[p][k][n], both operands stored
+// row-major with the contraction OUTERMOST (the hidden values or gradients
+// [rows][units], the queries or output gradients [rows][d]), fp32 out (or
+// split partials).  The same tiling and three-stage ring as gemm_nt_lds32, but
+// a stage holds 32 contraction rows of each operand as they lie in memory and
+// the MFMA operands (eight consecutive contraction indices of one column per
+// lane) come out of it by gfx950's transposing LDS read, so no transposed copy
+// is ever written.  Each 16-byte piece p of a stage row k sits at position
+// p ^ 2 (k % 4): the four rows one transposing read touches then fill distinct
+// banks.  Rows past the contraction end are zeroed in LDS before use.
+__global__ __launch_bounds__(64 * kWaves, 4) void gemm_tn_lds32(GemmParams g) {
+    struct Stage {
+        u32x4 x[kBK * kBM / 8];   // [k][256 columns]: 32 pieces per row
+        u32x4 w[kBK * kBN / 8];   // [k][128 columns]: 16 pieces per row
+    };
+    __shared__ Stage st_a, st_b, st_c;
+
+    const int NT = (g.N + kBN - 1) / kBN, nrb = (g.M + kBM - 1) / kBM;
+    const long per_split = (long)((g.P * nrb + kXcd - 1) / kXcd * kXcd) * NT;
+    const int ks = (int)(blockIdx.x / per_split);
+    const long blk = blockIdx.x - (long)ks * per_split;
+    const int xcd = (int)(blk % kXcd);
+    const long kq = blk / kXcd;
+    const int nt = (int)(kq % NT);
+    const int rgi = (int)(kq / NT) * kXcd + xcd;
+    if (rgi >= g.P * nrb) return;
+    const int p = rgi / nrb, m0 = (rgi - p * nrb) * kBM, n0 = nt * kBN;
+
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int wr = w & 3, wc = w >> 2;
+    const int kb = ks * g.kchunk, Kc = min(g.K - kb, g.kchunk);
+    const int nst = (Kc + kBK - 1) / kBK;
+    const uint16_t *X = g.X + p * g.sx, *W = g.W + p * g.sw;
+
+    // copies: wave w fills X rows 2w, 2w + 1 and 2w + 16, 2w + 17 (32 pieces
+    // each, one row per 32 lanes) and W rows 4w .. 4w + 3 (16 pieces each)
+    auto issue = [&](int i, Stage &dst) __attribute__((always_inline)) {
+        const int k0 = kb + i * kBK;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int r = 2 * w + 16 * c + (lane >> 5), pos = lane & 31;
+            const int k = min(k0 + r, g.K - 1);
+            const int col = min(m0 + 8 * (pos ^ (2 * (r & 3))), g.M - 8);
+            __builtin_amdgcn_global_load_lds((const void *)(X + (size_t)k * g.ldx + col),
+                                             (lds_void *)&dst.x[(2 * w + 16 * c) * 32], 16, 0, 0);
+        }
+        const int r = 4 * w + (lane >> 4), pos = lane & 15;
+        const int k = min(k0 + r, g.K - 1);
+        const int col = min(n0 + 8 * (pos ^ (2 * (r & 3))), g.N - 8);
+        __builtin_amdgcn_global_load_lds((const void *)(W + (size_t)k * g.ldw + col),
+                                         (lds_void *)&dst.w[(4 * w) * 16], 16, 0, 0);
+    };
+
+    // per-lane byte offsets (within a 16-row slice) of the slot this lane names
+    // for the transposing reads: rows 8 (lane / 32) + 4 h + (lane / 4) % 4,
+    // columns 16 ((lane / 16) % 2) + 4 (lane % 4) .. + 3 of the wave's tiles
+    const int G = lane >> 4, aa = lane & 3, e = (lane >> 2) & 3;
+    uint32_t wo[2][2], xo[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = 8 * (G >> 1) + 4 * h + e;
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            const int pw = 8 * wc + ((4 * ti + 2 * (G & 1) + (aa >> 1)) ^ (2 * e));
+            wo[ti][h] = (uint32_t)(r * 256 + pw * 16 + (aa & 1) * 8);
+            const int px = 8 * wr + ((4 * ti + 2 * (G & 1) + (aa >> 1)) ^ (2 * e));
+            xo[ti][h] = (uint32_t)(r * 512 + px * 16 + (aa & 1) * 8);
+        }
+    }
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    // optional column sums of X over this block's contraction range (the bias
+    // gradient of the same product): the waves of the first column half add
+    // up the eight contraction values of each of their X operands
+    const bool xs_on = g.xsum != nullptr && wc == 0;
+    float xs[2] = {0.f, 0.f};
+
+    auto step = [&](int i, Stage &cur, Stage &ahead) __attribute__((always_inline)) {
+        if (i + 1 < nst) wait_vmcnt<3>();
+        else wait_vmcnt<0>();
+        stage_barrier();
+        const int k0 = i * kBK;
+        if (k0 + kBK > Kc) {
+            // rows past the contraction end: zero in both operands
+            const int kv = Kc - k0;
+            for (int u = t; u < kBK * 48; u += 64 * kWaves) {
+                const int r = u / 48, pc = u - r * 48;
+                if (r < kv) continue;
+                if (pc < 32) cur.x[r * 32 + pc] = u32x4{0u, 0u, 0u, 0u};
+                else cur.w[r * 16 + pc - 32] = u32x4{0u, 0u, 0u, 0u};
+            }
+            __syncthreads();
+        }
+        if (i + 2 < nst) issue(i + 2, ahead);
+#pragma unroll
+        for (int sl = 0; sl < kBK / 16; ++sl) {
+            if (k0 + 16 * sl >= Kc) break;
+            u32x4 A[2], B[2];
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) {
+                const u32x2 a0 = lds_read_tr16(cur.w, sl * 16 * 256 + wo[ti][0]);
+                const u32x2 a1 = lds_read_tr16(cur.w, sl * 16 * 256 + wo[ti][1]);
+                A[ti] = u32x4{a0.x, a0.y, a1.x, a1.y};
+                const u32x2 b0 = lds_read_tr16(cur.x, sl * 16 * 512 + xo[ti][0]);
+                const u32x2 b1 = lds_read_tr16(cur.x, sl * 16 * 512 + xo[ti][1]);
+                B[ti] = u32x4{b0.x, b0.y, b1.x, b1.y};
+            }
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = mfma32(A[ti], B[tj], acc[ti][tj]);
+            if (xs_on) {
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) xs[tj] += bf16lo(B[tj][u]) + bf16hi(B[tj][u]);
+            }
+        }
+    };
+    issue(0, st_a);
+    if (nst > 1) issue(1, st_b);
+    for (int i = 0; i < nst; i += 3) {
+        step(i, st_a, st_c);
+        if (i + 1 >= nst) break;
+        step(i + 1, st_b, st_a);
+        if (i + 2 >= nst) break;
+        step(i + 2, st_c, st_b);
+    }
+
+    // register 4 qq + r of tile (ti, tj): column n0 + 64 wc + 32 ti + 8 qq + 4 (lane / 32) + r,
+    // row m0 + 64 wr + 32 tj + lane % 32 (the layout of gemm_nt_lds32)
+    const bool part = g.ksplit > 1;
+    const int r32 = lane & 31;
+    if (g.xsum != nullptr && nt == 0) {
+        // lanes l and l ^ 32 hold the two contraction halves of column l % 32
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) xs[tj] += __shfl_xor(xs[tj], 32, 64);
+        const int m = m0 + wr * 64 + 32 * (lane >> 5) + r32;     // lane half h writes tile tj = h
+        const float v = (lane >> 5) ? xs[1] : xs[0];
+        if (wc == 0 && m < g.M) {
+            if (part) g.xsum_part[((size_t)ks * g.P + p) * g.M + m] = v;
+            else g.xsum[p * g.sxs + m] = v;
+        }
+    }
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj) {
+        const int m = m0 + wr * 64 + 32 * tj + r32;
+        if (m >= g.M) continue;
+        const size_t row = part ? (((size_t)ks * g.P + p) * g.M + m) * g.N : p * g.sc + (size_t)m * g.ldc;
+        float *c = (part ? g.Cpart : g.C) + row;
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5);
+                if (nb >= g.N) continue;
+                *(f32x4 *)(c + nb) = f32x4{acc[ti][tj][4 * qq], acc[ti][tj][4 * qq + 1], acc[ti][tj][4 * qq + 2],
+                                           acc[ti][tj][4 * qq + 3]};
+            }
+    }
+}
+
+// Column sums over the rows, fixed order: parts[p][c][col] = the sum of rows
+// [64 c, 64 c + 64) of X[p][row][col] * (v ? v[p][row] : 1) (four columns per
+// thread, 16 rows' loads in flight), then out[p][col] = the parts summed in
+// chunk order.
+__global__ __launch_bounds__(256) void col_sum_parts(ColSumParams a) {
+    const int nch = (a.rows + 63) / 64, cq = a.cols / 4;
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)a.P * nch * cq) return;
+    const int q = (int)(i % cq);
+    const long pc = i / cq;
+    const int c = (int)(pc % nch), p = (int)(pc / nch);
+    const int r0 = 64 * c, r1 = min(r0 + 64, a.rows);
+    const uint16_t *x = a.X + p * a.sx + 4 * q;
+    const float *v = a.v ? a.v + p * a.sv : nullptr;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int rb = r0; rb < r1; rb += 16) {
+        u32x2 xv[16];
+        float vr[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int r = min(rb + u, r1 - 1);
+            xv[u] = *(const u32x2 *)(x + (size_t)r * a.ldx);
+            vr[u] = (rb + u < r1) ? (v ? v[r] : 1.f) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            s[0] = __builtin_fmaf(bf16lo(xv[u].x), vr[u], s[0]);
+            s[1] = __builtin_fmaf(bf16hi(xv[u].x), vr[u], s[1]);
+            s[2] = __builtin_fmaf(bf16lo(xv[u].y), vr[u], s[2]);
+            s[3] = __builtin_fmaf(bf16hi(xv[u].y), vr[u], s[3]);
+        }
+    }
+    *(f32x4 *)(a.parts + ((size_t)p * nch + c) * a.cols + 4 * q) = s;
+}
+
+__global__ __launch_bounds__(256) void col_sum_final(ColSumParams a) {
+    const int nch = (a.rows + 63) / 64, cq = a.cols / 4;
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)a.P * cq) return;
+    const int q = (int)(i % cq), p = (int)(i / cq);
+    const float *pp = a.parts + (size_t)p * nch * a.cols + 4 * q;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nch; c0 += 16) {
+        f32x4 pv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            pv[u] = (c0 + u < nch) ? *(const f32x4 *)(pp + (size_t)(c0 + u) * a.cols) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += pv[u];
+    }
+    *(f32x4 *)(a.out + p * a.so + 4 * q) = s;
+}
+
+// C[p][m][n] = sum over the splits of the partial tiles + bias (fixed order);
+// with xsum, also xsum[p][m] = the sum over the splits of its partials.
 __global__ __launch_bounds__(256) void gemm_reduce(GemmParams g) {
+    if (g.xsum) {
+        for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < (long)g.P * g.M; i += (long)gridDim.x * 256) {
+            const int m = (int)(i % g.M), p = (int)(i / g.M);
+            float s = 0.f;
+            for (int ks = 0; ks < g.ksplit; ++ks) s += g.xsum_part[((size_t)ks * g.P + p) * g.M + m];
+            g.xsum[p * g.sxs + m] = s;
+        }
+    }
     const long n4 = (long)g.P * g.M * (g.N / 4);
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
         const int nq = (int)(i % (g.N / 4));
@@ -477,6 +707,28 @@ hipError_t launch_gemm_nt(const GemmParams &g, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.ksplit <= 1) return e;
     hipLaunchKernelGGL(gemm_reduce, dim3(grid_for((long)g.P * g.M * (g.N / 4), 256, 8192)), dim3(256), 0, st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_tn(const GemmParams &g, hipStream_t st) {
+    if (g.M <= 0 || g.N <= 0 || g.P <= 0) return hipSuccess;
+    if (g.M % 8 || g.N % 8 || g.ldx % 8 || g.ldw % 8 || g.K <= 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(gemm_blocks(g) * (g.ksplit > 1 ? g.ksplit : 1))), block(64 * kWaves);
+    hipLaunchKernelGGL(gemm_tn_lds32, grid, block, 0, st, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || g.ksplit <= 1) return e;
+    hipLaunchKernelGGL(gemm_reduce, dim3(grid_for((long)g.P * g.M * (g.N / 4), 256, 8192)), dim3(256), 0, st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_col_sum(const ColSumParams &a, hipStream_t st) {
+    if (a.P <= 0 || a.cols <= 0) return hipSuccess;
+    if (a.cols % 4 || a.ldx % 4 || a.rows <= 0) return hipErrorInvalidValue;
+    const long nch = (a.rows + 63) / 64, cq = a.cols / 4;
+    hipLaunchKernelGGL(col_sum_parts, dim3(grid_for((long)a.P * nch * cq, 256, 1L << 30)), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(col_sum_final, dim3(grid_for((long)a.P * cq, 256, 1L << 30)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -645,8 +645,7 @@ def train_step_bench(torch, nectar, configs, dev, tokens=1024):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / 10 * 1e3
     Rp = tokens * (Hq // Hkv)
-    Rq = (Rp + 31) // 32 * 32
-    flops = Hkv * 2.0 * d * (Rp * (3 * m.Ht + m.Hs) + Rq * (2 * m.Ht + m.Hs))
+    flops = Hkv * 2.0 * d * Rp * (5 * m.Ht + 2 * m.Hs)
     tf = flops / us / 1e6
     out = {"tokens": tokens, "module": "MLP %d/%d" % (m.Ht, m.Hs), "us": us, "tflops": tf,
            "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS, "bound": "mfma", "flops": flops,

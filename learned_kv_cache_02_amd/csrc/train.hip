@@ -133,60 +133,100 @@ __global__ __launch_bounds__(64 * kWaves, 4) void gemm_nt_lds32(GemmParams g) {
                 }
             }
         }
-    u32x2 zi[2][2][4];
+    // epilogue 2's pre-activations: whole 128-byte row segments of the wave's
+    // 32 x 64 tiles (eight lanes per row), staged through LDS below
+    u32x4 zin[2][4];
     if (EPI == 2) {
 #pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int idx = 64 * it + lane, rr = idx >> 3, pc = idx & 7;
+                const int m = min(m0 + wr * 64 + 32 * tj + rr, g.M - 1);
+                const int col = min(n0 + wc * 64 + 8 * pc, g.N - 8);
+                zin[tj][it] = *(const u32x4 *)(g.Zi + p * g.sc + (size_t)m * g.ldc + col);
+            }
+    }
+    if (EPI == 0) {
+#pragma unroll
         for (int tj = 0; tj < 2; ++tj) {
-            const int m = min(m0 + wr * 64 + 32 * tj + r32, g.M - 1);
-            const size_t row = p * g.sc + (size_t)m * g.ldc;
+            const int m = m0 + wr * 64 + 32 * tj + r32;
+            if (m >= g.M) continue;
+            const size_t row = part ? (((size_t)ks * g.P + p) * g.M + m) * g.N : p * g.sc + (size_t)m * g.ldc;
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
-                    const int nb = min(n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5), g.N - 4);
-                    zi[tj][ti][qq] = *(const u32x2 *)(g.Zi + row + nb);
-                }
-        }
-    }
-#pragma unroll
-    for (int tj = 0; tj < 2; ++tj) {
-        const int m = m0 + wr * 64 + 32 * tj + r32;
-        if (m >= g.M) continue;
-        const size_t row = part ? (((size_t)ks * g.P + p) * g.M + m) * g.N : p * g.sc + (size_t)m * g.ldc;
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5);
-                if (nb >= g.N) continue;
-                float y[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) y[r] = acc[ti][tj][4 * qq + r] + bq[ti][qq][r];
-                if (EPI == 0) {
+                    const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5);
+                    if (nb >= g.N) continue;
                     float *c = (part ? g.Cpart : g.C) + row + nb;
+                    const f32x4 y = {acc[ti][tj][4 * qq] + bq[ti][qq][0], acc[ti][tj][4 * qq + 1] + bq[ti][qq][1],
+                                     acc[ti][tj][4 * qq + 2] + bq[ti][qq][2], acc[ti][tj][4 * qq + 3] + bq[ti][qq][3]};
                     if (nb + 3 < g.N) {
-                        *(f32x4 *)c = f32x4{y[0], y[1], y[2], y[3]};
+                        *(f32x4 *)c = y;
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             if (nb + r < g.N) c[r] = y[r];
                     }
-                } else {
-                    // bf16 outputs: widths are multiples of 32, the four columns are in range
-                    if (EPI == 1) {
-                        *(u32x2 *)(g.Zo + row + nb) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) y[r] = act_fn<ACT>(y[r]);
-                    } else {
-                        const u32x2 zz = zi[tj][ti][qq];
-                        y[0] *= act_grad_fn<ACT>(bf16lo(zz.x));
-                        y[1] *= act_grad_fn<ACT>(bf16hi(zz.x));
-                        y[2] *= act_grad_fn<ACT>(bf16lo(zz.y));
-                        y[3] *= act_grad_fn<ACT>(bf16hi(zz.y));
-                    }
-                    *(u32x2 *)(g.Y + row + nb) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
                 }
+        }
+        return;
+    }
+
+    // bf16 outputs (EPI 1: pre-activation and activation; EPI 2: the gradient
+    // times act'): a lane holds four columns of one row per register group, so
+    // each wave stages its 32 x 64 tile through LDS (the stage ring, free now)
+    // and stores whole 128-byte row segments.  Widths are multiples of 32.
+    __syncthreads();
+    char *reg = (w < 3 ? (char *)&st_a : (w < 6 ? (char *)&st_b : (char *)&st_c)) + (w % 3) * 8192;
+    uint16_t *zs = (uint16_t *)reg, *ys = (uint16_t *)(reg + 4096);   // [32 rows][8 pieces][8], swizzled
+    const int hh = lane >> 5;
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj) {
+        if (EPI == 2) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int idx = 64 * it + lane, rr = idx >> 3, pc = idx & 7;
+                *(u32x4 *)(zs + rr * 64 + ((pc ^ (rr & 7)) * 8)) = zin[tj][it];
             }
+        }
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] = acc[ti][tj][4 * qq + r] + bq[ti][qq][r];
+                const int off = r32 * 64 + (((4 * ti + qq) ^ (r32 & 7)) * 8) + 4 * hh;
+                if (EPI == 1) {
+                    *(u32x2 *)(zs + off) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) y[r] = act_fn<ACT>(y[r]);
+                } else {
+                    const u32x2 zz = *(const u32x2 *)(zs + off);
+                    y[0] *= act_grad_fn<ACT>(bf16lo(zz.x));
+                    y[1] *= act_grad_fn<ACT>(bf16hi(zz.x));
+                    y[2] *= act_grad_fn<ACT>(bf16lo(zz.y));
+                    y[3] *= act_grad_fn<ACT>(bf16hi(zz.y));
+                }
+                *(u32x2 *)(ys + off) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+            }
+        // 32 rows x 8 pieces of 16 bytes, four per lane, eight lanes per row
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int idx = 64 * it + lane, rr = idx >> 3, pc = idx & 7;
+            const int m = m0 + wr * 64 + 32 * tj + rr, col = n0 + wc * 64 + 8 * pc;
+            const int src = rr * 64 + ((pc ^ (rr & 7)) * 8);
+            const u32x4 yv = *(const u32x4 *)(ys + src);
+            u32x4 zv;
+            if (EPI == 1) zv = *(const u32x4 *)(zs + src);
+            if (m < g.M && col < g.N) {
+                const size_t o = p * g.sc + (size_t)m * g.ldc + col;
+                if (EPI == 1) *(u32x4 *)(g.Zo + o) = zv;
+                *(u32x4 *)(g.Y + o) = yv;
+            }
+        }
     }
 }
 

@@ -124,6 +124,8 @@ struct DeepStage {
     u32x4 x[kSl * kBM * 2];   // [slice][row][half]: input rows (query or state)
     u32x4 w[kSl * kBN * 2];   // [slice][row][half]: weight rows (outputs)
 };
+// the bf16 epilogue stages three waves' 32 x 64 tiles (8 KB each) in one stage buffer
+static_assert(sizeof(DeepStage) >= 3 * 8192, "epilogue staging");
 
 }  // namespace
 
@@ -220,33 +222,64 @@ __global__ __launch_bounds__(64 * kLdsWaves, 4) void deep_layer_lds32(DeepParams
 
     // register 4 qq + r of tile (ti, tj): output n0 + 64 wc + 32 ti + 8 qq + 4 (lane / 32) + r,
     // row rho0 + 64 wr + 32 tj + lane % 32
+    if (!L.Y) {
+        // the linear read-outs: fp32 rows of the output layout
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) {
+            const int rho = rho0 + wr * 64 + 32 * tj + r32;
+            if (rho >= a.Rp) continue;
+            const size_t o = out_row(p, rho, a.Hkv, a.G, 0, a.Hq) * L.N;
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5);
+                    float y[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        y[r] = acc[ti][tj][4 * qq + r] + (nb + r < L.N ? L.b[(size_t)p * L.N + nb + r] : 0.f);
+                        if (ACT >= 0) y[r] = act_fn<ACT>(y[r]);
+                    }
+                    if (nb + 3 < L.N) {
+                        *(f32x4 *)(L.Yf + o + nb) = f32x4{y[0], y[1], y[2], y[3]};
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (nb + r < L.N) L.Yf[o + nb + r] = y[r];
+                    }
+                }
+        }
+        return;
+    }
+    // hidden states (bf16; widths are multiples of 32): each wave stages its
+    // 32 x 64 tiles through the free stage ring so the stores write whole
+    // 128-byte row segments (a lane holds four columns of one row)
+    __syncthreads();
+    uint16_t *ys = (uint16_t *)((w < 3 ? (char *)&st_a : (w < 6 ? (char *)&st_b : (char *)&st_c)) + (w % 3) * 8192);
+    const int hh = lane >> 5;
 #pragma unroll
     for (int tj = 0; tj < 2; ++tj) {
-        const int rho = rho0 + wr * 64 + 32 * tj + r32;
-        if (rho >= a.Rp) continue;
-        const size_t o = L.Y ? ((size_t)p * a.Rp + rho) * L.N : out_row(p, rho, a.Hkv, a.G, 0, a.Hq) * L.N;
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-                const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5);
+                const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * hh;
                 float y[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     y[r] = acc[ti][tj][4 * qq + r] + (nb + r < L.N ? L.b[(size_t)p * L.N + nb + r] : 0.f);
                     if (ACT >= 0) y[r] = act_fn<ACT>(y[r]);
                 }
-                if (L.Y) {
-                    if (nb < L.N)    // hidden widths are multiples of 32: all four in range
-                        *(u32x2 *)((uint16_t *)L.Y + o + nb) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
-                } else if (nb + 3 < L.N) {
-                    *(f32x4 *)(L.Yf + o + nb) = f32x4{y[0], y[1], y[2], y[3]};
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (nb + r < L.N) L.Yf[o + nb + r] = y[r];
-                }
+                *(u32x2 *)(ys + r32 * 64 + (((4 * ti + qq) ^ (r32 & 7)) * 8) + 4 * hh) =
+                    u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
             }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int idx = 64 * it + lane, rr = idx >> 3, pc = idx & 7;
+            const int rho = rho0 + wr * 64 + 32 * tj + rr, col = n0 + wc * 64 + 8 * pc;
+            const u32x4 yv = *(const u32x4 *)(ys + rr * 64 + ((pc ^ (rr & 7)) * 8));
+            if (rho < a.Rp && col < L.N) *(u32x4 *)((uint16_t *)L.Y + ((size_t)p * a.Rp + rho) * L.N + col) = yv;
+        }
     }
 }
 

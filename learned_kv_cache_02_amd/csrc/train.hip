@@ -29,6 +29,8 @@ struct GemmStage {
     u32x4 x[kSl * kBM * 2];   // [slice][row][half]
     u32x4 w[kSl * kBN * 2];
 };
+// the bf16 epilogue stages three waves' 32 x 64 tiles (8 KB each) in one stage buffer
+static_assert(sizeof(GemmStage) >= 3 * 8192, "epilogue staging");
 
 }  // namespace
 

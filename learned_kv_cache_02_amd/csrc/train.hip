@@ -149,41 +149,49 @@ __global__ __launch_bounds__(64 * kWaves, 4) void gemm_nt_lds32(GemmParams g) {
                 zin[tj][it] = *(const u32x4 *)(g.Zi + p * g.sc + (size_t)m * g.ldc + col);
             }
     }
+    // Outputs go through the stage ring (free after the loop): each wave
+    // stages its 32 x 64 tiles in its own 8 KB so the stores write whole
+    // row segments (a lane holds four columns of one row per register group).
+    __syncthreads();
+    char *reg = (w < 3 ? (char *)&st_a : (w < 6 ? (char *)&st_b : (char *)&st_c)) + (w % 3) * 8192;
+    const int hh = lane >> 5;
     if (EPI == 0) {
+        // fp32 (or split partials): [32 rows][16 pieces of four columns], swizzled
+        float *cs = (float *)reg;
 #pragma unroll
         for (int tj = 0; tj < 2; ++tj) {
-            const int m = m0 + wr * 64 + 32 * tj + r32;
-            if (m >= g.M) continue;
-            const size_t row = part ? (((size_t)ks * g.P + p) * g.M + m) * g.N : p * g.sc + (size_t)m * g.ldc;
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
-                    const int nb = n0 + wc * 64 + 32 * ti + 8 * qq + 4 * (lane >> 5);
-                    if (nb >= g.N) continue;
-                    float *c = (part ? g.Cpart : g.C) + row + nb;
-                    const f32x4 y = {acc[ti][tj][4 * qq] + bq[ti][qq][0], acc[ti][tj][4 * qq + 1] + bq[ti][qq][1],
-                                     acc[ti][tj][4 * qq + 2] + bq[ti][qq][2], acc[ti][tj][4 * qq + 3] + bq[ti][qq][3]};
-                    if (nb + 3 < g.N) {
-                        *(f32x4 *)c = y;
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (nb + r < g.N) c[r] = y[r];
-                    }
+                    const int pc = 8 * ti + 2 * qq + hh;
+                    *(f32x4 *)(cs + r32 * 64 + ((pc ^ (r32 & 15)) * 4)) =
+                        f32x4{acc[ti][tj][4 * qq] + bq[ti][qq][0], acc[ti][tj][4 * qq + 1] + bq[ti][qq][1],
+                              acc[ti][tj][4 * qq + 2] + bq[ti][qq][2], acc[ti][tj][4 * qq + 3] + bq[ti][qq][3]};
                 }
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int idx = 64 * it + lane, rr = idx >> 4, pc = idx & 15;
+                const int m = m0 + wr * 64 + 32 * tj + rr, col = n0 + wc * 64 + 4 * pc;
+                const f32x4 v = *(const f32x4 *)(cs + rr * 64 + ((pc ^ (rr & 15)) * 4));
+                if (m >= g.M || col >= g.N) continue;
+                float *c = (part ? g.Cpart + (((size_t)ks * g.P + p) * g.M + m) * g.N
+                                 : g.C + p * g.sc + (size_t)m * g.ldc) + col;
+                if (col + 3 < g.N) {
+                    *(f32x4 *)c = v;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (col + r < g.N) c[r] = v[r];
+                }
+            }
         }
         return;
     }
 
     // bf16 outputs (EPI 1: pre-activation and activation; EPI 2: the gradient
-    // times act'): a lane holds four columns of one row per register group, so
-    // each wave stages its 32 x 64 tile through LDS (the stage ring, free now)
-    // and stores whole 128-byte row segments.  Widths are multiples of 32.
-    __syncthreads();
-    char *reg = (w < 3 ? (char *)&st_a : (w < 6 ? (char *)&st_b : (char *)&st_c)) + (w % 3) * 8192;
+    // times act'), 128-byte row segments.  Widths are multiples of 32.
     uint16_t *zs = (uint16_t *)reg, *ys = (uint16_t *)(reg + 4096);   // [32 rows][8 pieces][8], swizzled
-    const int hh = lane >> 5;
 #pragma unroll
     for (int tj = 0; tj < 2; ++tj) {
         if (EPI == 2) {
@@ -598,6 +606,61 @@ __global__ __launch_bounds__(256) void score_rows(ScoreRowParams a) {
     }
 }
 
+// The same with the row's pre-activations and score weights held in registers
+// (Hs <= 256 * MAXG): Zs is read once instead of twice.  Lane l owns units
+// 4 l .. 4 l + 3 of every 256; the sums run in the order of score_rows.
+template <int ACT, int MAXG>
+__global__ __launch_bounds__(256) void score_rows_reg(ScoreRowParams a) {
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (long)a.Hkv * a.Rp) return;
+    const int lane = threadIdx.x & 63;
+    const int p = (int)(row / a.Rp), rho = (int)(row - (long)p * a.Rp);
+    const float *z = a.Zs + (size_t)row * a.Hs;
+    const uint16_t *ws2 = a.ws2 + (size_t)p * a.Hs;
+    f32x4 zv[MAXG];
+    u32x2 wv[MAXG];
+#pragma unroll
+    for (int u = 0; u < MAXG; ++u) {
+        const int j = 4 * lane + 256 * u;
+        if (j < a.Hs) {
+            zv[u] = *(const f32x4 *)(z + j);
+            wv[u] = *(const u32x2 *)(ws2 + j);
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < MAXG; ++u) {
+        const int j = 4 * lane + 256 * u;
+        if (j >= a.Hs) break;
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = act_fn<ACT>(zv[u][r]);
+        *(u32x2 *)(a.Ys + (size_t)row * a.Hs + j) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+        s = __builtin_fmaf(bf16lo(wv[u].x), y[0], s);
+        s = __builtin_fmaf(bf16hi(wv[u].x), y[1], s);
+        s = __builtin_fmaf(bf16lo(wv[u].y), y[2], s);
+        s = __builtin_fmaf(bf16hi(wv[u].y), y[3], s);
+    }
+    s = wave_sum(s);
+    const size_t o = out_row(p, rho, a.Hkv, a.G, 0, a.Hq);
+    const float e = a.bs2[p] + s - a.alpha[o];
+    const float ga = a.coef * e;                   // 2 lambda_alpha e / R
+#pragma unroll
+    for (int u = 0; u < MAXG; ++u) {
+        const int j = 4 * lane + 256 * u;
+        if (j >= a.Hs) break;
+        const float g0 = ga * bf16lo(wv[u].x) * act_grad_fn<ACT>(zv[u][0]);
+        const float g1 = ga * bf16hi(wv[u].x) * act_grad_fn<ACT>(zv[u][1]);
+        const float g2 = ga * bf16lo(wv[u].y) * act_grad_fn<ACT>(zv[u][2]);
+        const float g3 = ga * bf16hi(wv[u].y) * act_grad_fn<ACT>(zv[u][3]);
+        *(u32x2 *)(a.dZs + (size_t)row * a.Hs + j) = u32x2{pack_bf16(g0, g1), pack_bf16(g2, g3)};
+    }
+    if (lane == 0) {
+        a.ga[row] = ga;
+        a.err[row] = e * e;
+    }
+}
+
 // One wave per target row: e = A - A_target, ||e||^2 and gA = 2 lambda_A e / R (bf16).
 template <int D>
 __global__ __launch_bounds__(256) void target_rows(TargetRowParams a) {
@@ -789,6 +852,12 @@ hipError_t launch_gather_q(const GatherParams &a, hipStream_t st) {
 
 hipError_t launch_score_rows(const ScoreRowParams &a, int act, hipStream_t st) {
     const dim3 grid(grid_for((long)a.Hkv * a.Rp, 4, 1L << 30)), block(256);
+    if (a.Hs <= 256 * 16) {
+        if (act == 1) hipLaunchKernelGGL((score_rows_reg<1, 16>), grid, block, 0, st, a);
+        else if (act == 2) hipLaunchKernelGGL((score_rows_reg<2, 16>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((score_rows_reg<0, 16>), grid, block, 0, st, a);
+        return hipGetLastError();
+    }
     if (act == 1) hipLaunchKernelGGL(score_rows<1>, grid, block, 0, st, a);
     else if (act == 2) hipLaunchKernelGGL(score_rows<2>, grid, block, 0, st, a);
     else hipLaunchKernelGGL(score_rows<0>, grid, block, 0, st, a);

@@ -2,7 +2,7 @@
 // regression losses, Eqs. (3.2)-(3.3) of the Nectar notes, and the summand of
 // the relative target error of Eq. (C.1), log(||A_theta - A||^2 / ||q - A||^2).
 //
-// Pass 1: one wave per (token, query head) row; lane l owns the D/64
+// Pass 1: one wave per four (token, query head) rows; lane l owns the D/64
 // consecutive dimensions from l * D/64, so each of the three d-vectors is one
 // coalesced wave load; the two squared norms are wave sums.  Passes 2 and 3:
 // the per-KV-head sums in fp64, each head's rows cut into kFitParts contiguous
@@ -14,30 +14,47 @@
 
 namespace nectar {
 
-template <int D, typename T>
+// RPW rows per wave, every load of all of them issued before the first sum.
+template <int D, typename T, int RPW>
 __global__ __launch_bounds__(256) void fit_rows(FitParams a) {
     constexpr int NPL = D / 64;
-    const long i = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (i >= a.rows) return;
+    const long i0 = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
+    if (i0 >= a.rows) return;
     const int lane = threadIdx.x & 63;
-    const size_t e = (size_t)i * D + lane * NPL;
-    float et = 0.f, eq = 0.f;
+    float ex[RPW][NPL], av[RPW][NPL], qv[RPW][NPL], sa[RPW], sb[RPW];
 #pragma unroll
-    for (int k = 0; k < NPL; ++k) {
-        const float ex = a.Aex[e + k];
-        const float x = a.A[e + k] - ex;
-        const float y = Elem<T>::ld((const T *)a.q, e + k) - ex;
-        et = __builtin_fmaf(x, x, et);
-        eq = __builtin_fmaf(y, y, eq);
+    for (int u = 0; u < RPW; ++u) {
+        const long i = min(i0 + u, a.rows - 1);
+        const size_t e = (size_t)i * D + lane * NPL;
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+            ex[u][k] = a.Aex[e + k];
+            av[u][k] = a.A[e + k];
+            qv[u][k] = Elem<T>::ld((const T *)a.q, e + k);
+        }
+        sa[u] = a.a[i];
+        sb[u] = a.alpha[i];
     }
-    et = wave_sum(et);
-    eq = wave_sum(eq);
-    if (lane == 0) {
-        const float ds = a.a[i] - a.alpha[i];
-        float *o = a.row + 3 * (size_t)i;
-        o[0] = ds * ds;
-        o[1] = et;
-        o[2] = logf(et / eq);
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) {
+        const long i = i0 + u;
+        float et = 0.f, eq = 0.f;
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+            const float x = av[u][k] - ex[u][k];
+            const float y = qv[u][k] - ex[u][k];
+            et = __builtin_fmaf(x, x, et);
+            eq = __builtin_fmaf(y, y, eq);
+        }
+        et = wave_sum(et);
+        eq = wave_sum(eq);
+        if (lane == 0 && i < a.rows) {
+            const float ds = sa[u] - sb[u];
+            float *o = a.row + 3 * (size_t)i;
+            o[0] = ds * ds;
+            o[1] = et;
+            o[2] = logf(et / eq);
+        }
     }
 }
 
@@ -79,11 +96,12 @@ __global__ __launch_bounds__(64) void fit_head_sums(FitParams a) {
 }
 
 hipError_t launch_fit_metrics(const FitParams &p, int dtype, int d, hipStream_t st) {
-    dim3 grid((unsigned)((p.rows + 3) / 4)), block(256);
-    if (d == 128 && dtype == 1) hipLaunchKernelGGL((fit_rows<128, uint16_t>), grid, block, 0, st, p);
-    else if (d == 128) hipLaunchKernelGGL((fit_rows<128, float>), grid, block, 0, st, p);
-    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((fit_rows<64, uint16_t>), grid, block, 0, st, p);
-    else if (d == 64) hipLaunchKernelGGL((fit_rows<64, float>), grid, block, 0, st, p);
+    constexpr int kRows = 4;   // rows per wave
+    dim3 grid((unsigned)((p.rows + 4 * kRows - 1) / (4 * kRows))), block(256);
+    if (d == 128 && dtype == 1) hipLaunchKernelGGL((fit_rows<128, uint16_t, kRows>), grid, block, 0, st, p);
+    else if (d == 128) hipLaunchKernelGGL((fit_rows<128, float, kRows>), grid, block, 0, st, p);
+    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((fit_rows<64, uint16_t, kRows>), grid, block, 0, st, p);
+    else if (d == 64) hipLaunchKernelGGL((fit_rows<64, float, kRows>), grid, block, 0, st, p);
     else return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.head) return e;

@@ -36,10 +36,10 @@ __global__ __launch_bounds__(256) void merge_pairs(MergeParams a) {
 }
 
 // K-way merge (the closing section's composition of several context modules):
-// one wave per row, lane l owning the D/64 contiguous dimensions from l * D/64,
-// so each pair's read-out row is one coalesced wave load.  Every pair's logit
-// and read-out are loaded before the common maximum is taken, and the pairs are
-// folded in index order, the local pair last.
+// one wave per two rows, lane l owning the D/64 contiguous dimensions from
+// l * D/64, so each pair's read-out row is one coalesced wave load.  Every
+// pair's logit and read-out of both rows are loaded before the first common
+// maximum is taken, and the pairs are folded in index order, the local pair last.
 template <int NPL> struct RowVec;
 template <> struct RowVec<1> {
     static __device__ __forceinline__ void load(const float *p, float *v) { v[0] = *p; }
@@ -58,49 +58,60 @@ template <> struct RowVec<2> {
     }
 };
 
-template <int D, typename OutT>
+template <int D, typename OutT, int RPW>
 __global__ __launch_bounds__(256) void merge_k_pairs(MergeKParams a) {
     constexpr int NPL = D / 64;
     using RV = RowVec<NPL>;
-    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= a.rows) return;
-    const size_t e = (size_t)r * D + (threadIdx.x & 63) * NPL;
+    const long r0 = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
+    if (r0 >= a.rows) return;
     const bool lane0 = (threadIdx.x & 63) == 0;
-    float x[kMergeKMax + 1], v[kMergeKMax + 1][NPL];
+    // RPW rows per wave: every pair of all of them loaded before the first maximum
+    float x[RPW][kMergeKMax + 1], v[RPW][kMergeKMax + 1][NPL];
 #pragma unroll
-    for (int k = 0; k <= kMergeKMax; ++k) {
-        const bool loc = (k == kMergeKMax);
-        const float *ps = loc ? a.lam : (k < a.K ? a.a[k] : nullptr);
-        const float *pv = loc ? a.A_loc : (k < a.K ? a.A[k] : nullptr);
-        x[k] = ps ? ps[r] : -INFINITY;
+    for (int u = 0; u < RPW; ++u) {
+        const long r = min(r0 + u, a.rows - 1);
+        const size_t e = (size_t)r * D + (threadIdx.x & 63) * NPL;
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) v[k][i] = 0.f;
-        if (pv) RV::load(pv + e, v[k]);
+        for (int k = 0; k <= kMergeKMax; ++k) {
+            const bool loc = (k == kMergeKMax);
+            const float *ps = loc ? a.lam : (k < a.K ? a.a[k] : nullptr);
+            const float *pv = loc ? a.A_loc : (k < a.K ? a.A[k] : nullptr);
+            x[u][k] = ps ? ps[r] : -INFINITY;
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) v[u][k][i] = 0.f;
+            if (pv) RV::load(pv + e, v[u][k]);
+        }
     }
-    float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k <= kMergeKMax; ++k) M = fmaxf(M, x[k]);
-    float acc[NPL];
+    for (int u = 0; u < RPW; ++u) {
+        const long r = r0 + u;
+        if (r >= a.rows) break;
+        const size_t e = (size_t)r * D + (threadIdx.x & 63) * NPL;
+        float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) acc[i] = 0.f;
-    if (M == -INFINITY) {
+        for (int k = 0; k <= kMergeKMax; ++k) M = fmaxf(M, x[u][k]);
+        float acc[NPL];
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) acc[i] = 0.f;
+        if (M == -INFINITY) {
+            RV::store((OutT *)a.out + e, acc);
+            if (a.lse_out && lane0) a.lse_out[r] = -INFINITY;
+            continue;
+        }
+        float den = 0.f;
+#pragma unroll
+        for (int k = 0; k <= kMergeKMax; ++k) {
+            const float w = x[u][k] == -INFINITY ? 0.f : expf(x[u][k] - M);
+            den += w;
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) acc[i] += w * v[u][k][i];
+        }
+        const float inv = 1.0f / den;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) acc[i] *= inv;
         RV::store((OutT *)a.out + e, acc);
-        if (a.lse_out && lane0) a.lse_out[r] = -INFINITY;
-        return;
+        if (a.lse_out && lane0) a.lse_out[r] = M + logf(den);
     }
-    float den = 0.f;
-#pragma unroll
-    for (int k = 0; k <= kMergeKMax; ++k) {
-        const float w = x[k] == -INFINITY ? 0.f : expf(x[k] - M);
-        den += w;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) acc[i] += w * v[k][i];
-    }
-    const float inv = 1.0f / den;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) acc[i] *= inv;
-    RV::store((OutT *)a.out + e, acc);
-    if (a.lse_out && lane0) a.lse_out[r] = M + logf(den);
 }
 
 static inline unsigned blocks_for_waves(long waves) { return (unsigned)((waves + 3) / 4); }
@@ -116,11 +127,12 @@ hipError_t launch_merge(const MergeParams &p, int dtype, int d, hipStream_t st) 
 }
 
 hipError_t launch_merge_k(const MergeKParams &p, int dtype, int d, hipStream_t st) {
-    dim3 grid(blocks_for_waves(p.rows)), block(256);
-    if (d == 128 && dtype == 1) hipLaunchKernelGGL((merge_k_pairs<128, uint16_t>), grid, block, 0, st, p);
-    else if (d == 128) hipLaunchKernelGGL((merge_k_pairs<128, float>), grid, block, 0, st, p);
-    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((merge_k_pairs<64, uint16_t>), grid, block, 0, st, p);
-    else if (d == 64) hipLaunchKernelGGL((merge_k_pairs<64, float>), grid, block, 0, st, p);
+    constexpr int kRows = 2;   // rows per wave
+    dim3 grid(blocks_for_waves((p.rows + kRows - 1) / kRows)), block(256);
+    if (d == 128 && dtype == 1) hipLaunchKernelGGL((merge_k_pairs<128, uint16_t, kRows>), grid, block, 0, st, p);
+    else if (d == 128) hipLaunchKernelGGL((merge_k_pairs<128, float, kRows>), grid, block, 0, st, p);
+    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((merge_k_pairs<64, uint16_t, kRows>), grid, block, 0, st, p);
+    else if (d == 64) hipLaunchKernelGGL((merge_k_pairs<64, float, kRows>), grid, block, 0, st, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -85,33 +85,34 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams a) {
     for (int i = 0; i < NPL; ++i) a.part_O[row * D + lane + 64 * i] = acc[i];
 }
 
-// One block per (problem, row): log-sum-exp fold of the S partials, fixed
-// order, then the optional merge with an extra (lse, A) pair (Eq. (3.5)).
-// Thread (sg, dq) owns 4 dims of the splits sg, sg + NSG, ...; it issues every
-// load it needs (statistics, read-outs, the extra pair) before the first
-// reduction, so the block pays one memory round trip.
-template <int D, typename OutT, int MAXI>
-__global__ __launch_bounds__(256) void attn_combine(CombineParams a) {
-    constexpr int DQ = D / 4;            // float4 columns
-    constexpr int NSG = 256 / DQ;        // split groups
-    __shared__ float red[8];
-    __shared__ f32x4 accs[NSG][DQ];
-    const int idx = blockIdx.x;
-    const int p = idx / a.Rp, rho = idx - p * a.Rp;
-    const int tid = threadIdx.x;
+// One wave per (problem, row, slice of NC float4 columns): log-sum-exp fold of
+// the S partials in a fixed order, then the optional merge with an extra
+// (lse, A) pair (Eq. (3.5)).  Lane (g, c) owns four dims of the splits g,
+// g + NG, ... (NG = 64 / NC) and issues every load it needs (statistics,
+// read-outs, the extra pair) before the first reduction, so a row costs one
+// memory round trip; the split groups are folded within the wave.
+template <int D, typename OutT, int NC, int MAXI>
+__global__ __launch_bounds__(64) void attn_combine(CombineParams a) {
+    constexpr int NB = D / 4 / NC;       // waves per row
+    constexpr int NG = 64 / NC;          // split groups
+    int row, cb;
+    slice_of_block<NB>(row, cb);
+    if (row >= a.P * a.Rp) return;
+    const int p = row / a.Rp, rho = row - p * a.Rp;
+    const int lane = threadIdx.x, sg = lane / NC;
+    const int dc = 4 * (cb * NC + (lane - sg * NC));
     const size_t o = out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq);
     const float2 *ml = a.part_ml + (size_t)p * a.S * a.Rp + rho;   // stride Rp over splits
     const float *po = a.part_O + ((size_t)p * a.S * a.Rp + rho) * D;
-    const int sg = tid / DQ, dq = tid - sg * DQ;
 
     float2 st[MAXI];
     f32x4 ov[MAXI];
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-        const int s = sg + i * NSG;
+        const int s = sg + i * NG;
         if (s < a.S) {
             st[i] = ml[(size_t)s * a.Rp];
-            ov[i] = *(const f32x4 *)(po + (size_t)s * a.Rp * D + 4 * dq);
+            ov[i] = *(const f32x4 *)(po + (size_t)s * a.Rp * D + dc);
         } else {
             st[i] = make_float2(-INFINITY, 0.f);
             ov[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -121,18 +122,14 @@ __global__ __launch_bounds__(256) void attn_combine(CombineParams a) {
     f32x4 xa = {0.f, 0.f, 0.f, 0.f};
     if (a.x_lse) {
         mx = a.x_lse[o] * kLog2e;
-        if (a.out && tid < DQ) xa = *(const f32x4 *)(a.x_A + o * D + 4 * tid);
+        if (a.out && sg == 0) xa = *(const f32x4 *)(a.x_A + o * D + dc);
     }
-    // splits beyond MAXI * NSG (very long split lists) are folded serially
+    // splits beyond MAXI * NG (very long split lists) are folded serially
     float mloc = -INFINITY;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) mloc = fmaxf(mloc, st[i].x);
-    for (int s = sg + MAXI * NSG; s < a.S; s += NSG) mloc = fmaxf(mloc, ml[(size_t)s * a.Rp].x);
-#pragma unroll
-    for (int o2 = 32; o2 >= 1; o2 >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o2, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = mloc;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    for (int s = sg + MAXI * NG; s < a.S; s += NG) mloc = fmaxf(mloc, ml[(size_t)s * a.Rp].x);
+    const float M = splits_max<NC>(mloc);
     const bool empty = (M == -INFINITY);
     float lloc = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -143,28 +140,21 @@ __global__ __launch_bounds__(256) void attn_combine(CombineParams a) {
             lloc += w * st[i].y;
             acc += w * ov[i];
         }
-        for (int s = sg + MAXI * NSG; s < a.S; s += NSG) {
+        for (int s = sg + MAXI * NG; s < a.S; s += NG) {
             const float2 v = ml[(size_t)s * a.Rp];
             const float w = exp2f(v.x - M);
             lloc += w * v.y;
-            acc += w * *(const f32x4 *)(po + (size_t)s * a.Rp * D + 4 * dq);
+            acc += w * *(const f32x4 *)(po + (size_t)s * a.Rp * D + dc);
         }
     }
-    // every split's l is counted once: only the dq == 0 thread of a group adds it
-    lloc = (dq == 0) ? lloc : 0.f;
-#pragma unroll
-    for (int o2 = 32; o2 >= 1; o2 >>= 1) lloc += __shfl_xor(lloc, o2, 64);
-    if ((tid & 63) == 0) red[4 + (tid >> 6)] = lloc;
-    accs[sg][dq] = acc;
-    __syncthreads();
-    if (tid >= DQ) return;
-    const float L = (red[4] + red[5]) + (red[6] + red[7]);
-    f32x4 O = accs[0][tid];
-    for (int k = 1; k < NSG; ++k) O += accs[k][tid];
+    const float L = splits_sum<NC>(lloc);
+    const f32x4 O = splits_sum4<NC>(acc);
+    if (sg != 0) return;
+    const bool lead = (cb == 0 && lane == 0);   // writes the row's scalars
 
     const float inv = empty ? 0.f : 1.0f / L;
-    if (a.lse_out && tid == 0) a.lse_out[o] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
-    if (a.A_out) *(f32x4 *)(a.A_out + o * D + 4 * tid) = O * inv;
+    if (a.lse_out && lead) a.lse_out[o] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+    if (a.A_out) *(f32x4 *)(a.A_out + o * D + dc) = O * inv;
     if (a.x_lse) {
         const float Mt = fmaxf(M, mx);
         const bool none = (Mt == -INFINITY);
@@ -172,11 +162,11 @@ __global__ __launch_bounds__(256) void attn_combine(CombineParams a) {
         const float wx = none ? 0.f : exp2f(mx - Mt);
         const float Lt = wl * L + wx;
         const float it = none ? 0.f : 1.0f / Lt;
-        if (a.out_lse && tid == 0) a.out_lse[o] = none ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
+        if (a.out_lse && lead) a.out_lse[o] = none ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
         if (a.out) {
             const f32x4 r = (wl * O + wx * xa) * it;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st_out<OutT>((OutT *)a.out, o * D + 4 * tid + i, none ? 0.f : r[i]);
+            for (int i = 0; i < 4; ++i) st_out<OutT>((OutT *)a.out, o * D + dc + i, none ? 0.f : r[i]);
         }
     }
 }
@@ -233,14 +223,22 @@ hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hi
     return hipGetLastError();
 }
 
+// Few rows (decode): d / 16 waves per row, 16 dims each, 64 splits loaded up
+// front; many rows: one wave per row over all dims, 8 (d = 128) or 32 (d = 64)
+// splits up front.
 hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st) {
-    dim3 grid((unsigned)((long)p.P * p.Rp)), block(256);
-    if (d == 128 && dtype == 1) hipLaunchKernelGGL((attn_combine<128, uint16_t, 8>), grid, block, 0, st, p);
-    else if (d == 128) hipLaunchKernelGGL((attn_combine<128, float, 8>), grid, block, 0, st, p);
-    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((attn_combine<64, uint16_t, 4>), grid, block, 0, st, p);
-    else if (d == 64) hipLaunchKernelGGL((attn_combine<64, float, 4>), grid, block, 0, st, p);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    const long rows = (long)p.P * p.Rp;
+    const bool sliced = rows * (d / 4 / kSliceCols) <= kReduceSliceWaves;
+    dim3 grid((unsigned)slice_grid(rows, sliced ? d / 4 / kSliceCols : 1)), block(64);
+#define NECTAR_COMBINE_CASE(DD, T) \
+    if (d == DD) { \
+        if (sliced) hipLaunchKernelGGL((attn_combine<DD, T, kSliceCols, kSliceCols>), grid, block, 0, st, p); \
+        else hipLaunchKernelGGL((attn_combine<DD, T, DD / 4, 64 * 8 / DD>), grid, block, 0, st, p); \
+        return hipGetLastError(); }
+    if (dtype == 1) { NECTAR_COMBINE_CASE(128, uint16_t) NECTAR_COMBINE_CASE(64, uint16_t) }
+    else { NECTAR_COMBINE_CASE(128, float) NECTAR_COMBINE_CASE(64, float) }
+#undef NECTAR_COMBINE_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace nectar

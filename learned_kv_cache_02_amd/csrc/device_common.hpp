@@ -87,6 +87,45 @@ __device__ __forceinline__ float group4_max(float v) {
     return v;
 }
 
+// Block -> (row, slice) of a split reduction with NB waves per row: the NB
+// slices of a row share blockIdx % 8, which the dispatcher sends to one XCD
+// (block ids go round-robin over the eight), so the cache lines the slices
+// split are fetched into a single L2.  The grid covers the rows rounded up to
+// a multiple of 8; `row` may pass the last row.
+template <int NB> __device__ __forceinline__ void slice_of_block(int &row, int &cb) {
+    if (NB == 1) {
+        row = blockIdx.x;
+        cb = 0;
+    } else {
+        const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+        cb = y % NB;
+        row = (y / NB) * 8 + x;
+    }
+}
+static inline long slice_grid(long rows, int nb) { return nb == 1 ? rows : (rows + 7) / 8 * 8 * nb; }
+
+// Folds over the split groups of a wave whose lane (g, c) = (lane / NC, lane %
+// NC) holds column c of the splits of group g: lanes that differ only in the
+// bits from NC up are combined in a fixed butterfly order and every lane ends
+// with the total of its column.
+template <int NC> __device__ __forceinline__ float splits_max(float v) {
+#pragma unroll
+    for (int o = NC; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+template <int NC> __device__ __forceinline__ float splits_sum(float v) {
+#pragma unroll
+    for (int o = NC; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+template <int NC> __device__ __forceinline__ f32x4 splits_sum4(f32x4 v) {
+#pragma unroll
+    for (int o = NC; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], o, 64);
+    return v;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // GELU in the erf form, x * Phi(x) with Phi(x) = (1 + erf(x / sqrt 2)) / 2 and

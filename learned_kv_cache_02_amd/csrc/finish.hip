@@ -5,10 +5,12 @@
 // plus output biases) -- is folded into its pair (alpha, A) or (a, A); and each
 // pair is merged with the local one as the virtual logit of Eqs. (3.4)-(3.5).
 //
-// One block per local row.  Thread (sg, dq) owns four dimensions of the splits
-// sg, sg + NSG, ... of every part and issues all of its loads (statistics,
-// read-outs, of all parts) before the first reduction, so a row costs one
-// memory round trip; the splits are folded in a fixed order.
+// One wave per (local row, slice of NC float4 columns): lane (g, c) owns column
+// c of the slice for the splits g, g + NG, ... of every part (NG = 64 / NC) and
+// issues all of its loads (statistics, read-outs, of all parts) before the
+// first reduction, so a row costs one memory round trip; the split groups are
+// folded by butterfly exchanges within the wave (no barriers), in a fixed
+// order, so every lane ends with the same totals.
 #include "attn_common.hpp"
 
 namespace nectar {
@@ -17,38 +19,23 @@ namespace {
 
 constexpr int kMaxSets = 3;   // local part + two document-side parts
 
-// Block-wide reductions of one value per thread over the four waves.
-__device__ __forceinline__ float block_max(float v, float *red) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-__device__ __forceinline__ float block_sum(float v, float *red) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
 }  // namespace
 
-template <int D, typename OutT, int MAXI>
-__global__ __launch_bounds__(256) void attn_finish(FinishParams a) {
-    constexpr int DQ = D / 4;          // float4 columns
-    constexpr int NSG = 256 / DQ;      // split groups
-    __shared__ float red[kMaxSets][2][4];
-    __shared__ f32x4 accs[kMaxSets][NSG][DQ];
+template <int D, typename OutT, int NC>
+__global__ __launch_bounds__(64) void attn_finish(FinishParams a) {
+    constexpr int NB = D / 4 / NC;     // waves per row
+    constexpr int NG = 64 / NC;        // split groups
+    constexpr int MAXI = 64 / NG;      // splits per lane loaded up front (64 per part)
 
-    const int idx = blockIdx.x;
-    const int p = idx / a.Rp, rho = idx - p * a.Rp;
+    int row, cb;
+    slice_of_block<NB>(row, cb);
+    if (row >= a.P * a.Rp) return;
+    const int p = row / a.Rp, rho = row - p * a.Rp;
     const int b = p / a.Hkv, h = p - b * a.Hkv;
     const size_t o = out_row(p, rho, a.Hkv, a.G, a.Tq, a.Hq);
     const int rho_doc = b * a.Tq * a.G + rho;      // the same query row in the document problems
-    const int tid = threadIdx.x, sg = tid / DQ, dq = tid - sg * DQ;
+    const int lane = threadIdx.x, sg = lane / NC;
+    const int dc = 4 * (cb * NC + (lane - sg * NC));  // first of this lane's four dims
     const int nparts = 1 + a.nsets;
 
     // part k: base pointers with split stride `stride` rows
@@ -80,31 +67,33 @@ __global__ __launch_bounds__(256) void attn_finish(FinishParams a) {
     for (int k = 0; k < kMaxSets; ++k)
 #pragma unroll
         for (int i = 0; i < MAXI; ++i) {
-            const int s = sg + i * NSG;
+            const int s = sg + i * NG;
             // absent splits: an empty log-sum-exp partial, or a zero sum
             st[k][i] = make_float2(pml[k] ? -INFINITY : 0.f, 0.f);
             ov[k][i] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (k < nparts && s < S[k]) {
                 if (pml[k]) st[k][i] = pml[k][s * stride[k]];
                 else st[k][i] = make_float2(ps[k][s * stride[k]], 0.f);
-                ov[k][i] = *(const f32x4 *)(pO[k] + s * stride[k] * D + 4 * dq);
+                ov[k][i] = *(const f32x4 *)(pO[k] + s * stride[k] * D + dc);
             }
         }
 
     // per part: (M in log2 units, L, O) with the read-out unnormalised by L
     float M[kMaxSets], L[kMaxSets];
+    f32x4 O[kMaxSets];
 #pragma unroll
     for (int k = 0; k < kMaxSets; ++k) {
         M[k] = -INFINITY;
         L[k] = 0.f;
+        O[k] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (k >= nparts) continue;             // uniform
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (pml[k]) {
             float mloc = -INFINITY;
 #pragma unroll
             for (int i = 0; i < MAXI; ++i) mloc = fmaxf(mloc, st[k][i].x);
-            for (int s = sg + MAXI * NSG; s < S[k]; s += NSG) mloc = fmaxf(mloc, pml[k][s * stride[k]].x);
-            const float Mk = block_max(mloc, red[k][0]);
+            for (int s = sg + MAXI * NG; s < S[k]; s += NG) mloc = fmaxf(mloc, pml[k][s * stride[k]].x);
+            const float Mk = splits_max<NC>(mloc);
             float lloc = 0.f;
             if (Mk != -INFINITY) {
 #pragma unroll
@@ -113,15 +102,14 @@ __global__ __launch_bounds__(256) void attn_finish(FinishParams a) {
                     lloc += w * st[k][i].y;
                     acc += w * ov[k][i];
                 }
-                for (int s = sg + MAXI * NSG; s < S[k]; s += NSG) {
+                for (int s = sg + MAXI * NG; s < S[k]; s += NG) {
                     const float2 v = pml[k][s * stride[k]];
                     const float w = exp2f(v.x - Mk);
                     lloc += w * v.y;
-                    acc += w * *(const f32x4 *)(pO[k] + s * stride[k] * D + 4 * dq);
+                    acc += w * *(const f32x4 *)(pO[k] + s * stride[k] * D + dc);
                 }
             }
-            // each split's l counted once: only the dq == 0 thread of a group adds it
-            L[k] = block_sum(dq == 0 ? lloc : 0.f, red[k][1]);
+            L[k] = splits_sum<NC>(lloc);
             M[k] = Mk;
         } else {
             // MLP module: a = bs2 + sum of score partials, A = b2 + sum of read-out partials
@@ -131,34 +119,25 @@ __global__ __launch_bounds__(256) void attn_finish(FinishParams a) {
                 sloc += st[k][i].x;
                 acc += ov[k][i];
             }
-            for (int s = sg + MAXI * NSG; s < S[k]; s += NSG) {
+            for (int s = sg + MAXI * NG; s < S[k]; s += NG) {
                 sloc += ps[k][s * stride[k]];
-                acc += *(const f32x4 *)(pO[k] + s * stride[k] * D + 4 * dq);
+                acc += *(const f32x4 *)(pO[k] + s * stride[k] * D + dc);
             }
-            const float asum = block_sum(dq == 0 ? sloc : 0.f, red[k][1]);
+            const float asum = splits_sum<NC>(sloc);
             M[k] = (a.set[k - 1].bs2[h] + asum) * kLog2e;   // the pair's log-normaliser, log2 units
             L[k] = 1.f;
         }
-        accs[k][sg][dq] = acc;
+        O[k] = splits_sum4<NC>(acc);
+        if (k > 0 && !pml[k]) O[k] += *(const f32x4 *)(a.set[k - 1].b2 + (size_t)h * D + dc);
     }
-    __syncthreads();
-    if (tid >= DQ) return;
-
-    f32x4 O[kMaxSets];
-#pragma unroll
-    for (int k = 0; k < kMaxSets; ++k) {
-        O[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (k >= nparts) continue;
-#pragma unroll
-        for (int j = 0; j < NSG; ++j) O[k] += accs[k][j][tid];
-        if (k > 0 && !pml[k]) O[k] += *(const f32x4 *)(a.set[k - 1].b2 + (size_t)h * D + 4 * tid);
-    }
+    if (sg != 0) return;
+    const bool lead = (cb == 0 && lane == 0);   // writes the row's scalars
 
     // the pairs
     auto write_pair = [&](int k, float *lse_out, float *A_out) {
         const bool empty = (M[k] == -INFINITY);
-        if (lse_out && tid == 0) lse_out[o] = empty ? -INFINITY : (M[k] + log2f(L[k])) * kLn2;
-        if (A_out) *(f32x4 *)(A_out + o * D + 4 * tid) = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : O[k] * (1.0f / L[k]);
+        if (lse_out && lead) lse_out[o] = empty ? -INFINITY : (M[k] + log2f(L[k])) * kLn2;
+        if (A_out) *(f32x4 *)(A_out + o * D + dc) = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : O[k] * (1.0f / L[k]);
     };
     write_pair(0, a.lam_out, a.Aloc_out);
 #pragma unroll
@@ -173,21 +152,24 @@ __global__ __launch_bounds__(256) void attn_finish(FinishParams a) {
         const float wk = (none || M[k] == -INFINITY) ? 0.f : exp2f(M[k] - Mt);
         const float Lt = wl * L[0] + wk * L[k];
         const float it = none ? 0.f : 1.0f / Lt;
-        if (f.out_lse && tid == 0) f.out_lse[o] = none ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
+        if (f.out_lse && lead) f.out_lse[o] = none ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
         if (f.out) {
             const f32x4 r = (wl * O[0] + wk * O[k]) * it;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st_out<OutT>((OutT *)f.out, o * D + 4 * tid + i, none ? 0.f : r[i]);
+            for (int i = 0; i < 4; ++i) st_out<OutT>((OutT *)f.out, o * D + dc + i, none ? 0.f : r[i]);
         }
     }
 }
 
 hipError_t launch_finish(const FinishParams &p, int dtype, int d, hipStream_t st) {
-    dim3 grid((unsigned)((long)p.P * p.Rp)), block(256);
-    if (d == 128 && dtype == 1) hipLaunchKernelGGL((attn_finish<128, uint16_t, 8>), grid, block, 0, st, p);
-    else if (d == 128) hipLaunchKernelGGL((attn_finish<128, float, 8>), grid, block, 0, st, p);
-    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((attn_finish<64, uint16_t, 4>), grid, block, 0, st, p);
-    else if (d == 64) hipLaunchKernelGGL((attn_finish<64, float, 4>), grid, block, 0, st, p);
+    // float4 columns per wave: 8 waves per row at d = 128, 4 at d = 64 (4B decode
+    // step: 2 columns 56.5 us, 4 columns 55.9 us, 8 columns 56.6 us)
+    constexpr int kCols = 4;
+    dim3 grid((unsigned)slice_grid((long)p.P * p.Rp, d / 4 / kCols)), block(64);
+    if (d == 128 && dtype == 1) hipLaunchKernelGGL((attn_finish<128, uint16_t, kCols>), grid, block, 0, st, p);
+    else if (d == 128) hipLaunchKernelGGL((attn_finish<128, float, kCols>), grid, block, 0, st, p);
+    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((attn_finish<64, uint16_t, kCols>), grid, block, 0, st, p);
+    else if (d == 64) hipLaunchKernelGGL((attn_finish<64, float, kCols>), grid, block, 0, st, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -67,49 +67,46 @@ __global__ __launch_bounds__(256) void mlp_partial_valu(MlpParams a) {
     for (int i = 0; i < NPL; ++i) a.part_O[row * D + lane + 64 * i] = acc[i];
 }
 
-// One block per (KV head, row): output bias plus the split partials, summed in
-// a fixed order.  Every load is issued before the first reduction.
-template <int D, int MAXI>
-__global__ __launch_bounds__(256) void mlp_reduce(MlpReduceParams a) {
-    constexpr int DQ = D / 4;
-    constexpr int NSG = 256 / DQ;
-    __shared__ f32x4 accs[NSG][DQ];
-    __shared__ float red[4];
-    const int idx = blockIdx.x;
-    const int h = idx / a.Rp, rho = idx - h * a.Rp;
-    const int tid = threadIdx.x;
+// One wave per (KV head, row, slice of NC float4 columns): output bias plus the
+// split partials, folded in a fixed order.  Lane (g, c) owns four dims of the
+// splits g, g + NG, ... (NG = 64 / NC); every load is issued before the first
+// reduction.
+template <int D, int NC, int MAXI>
+__global__ __launch_bounds__(64) void mlp_reduce(MlpReduceParams a) {
+    constexpr int NB = D / 4 / NC;       // waves per row
+    constexpr int NG = 64 / NC;          // split groups
+    int row, cb;
+    slice_of_block<NB>(row, cb);
+    if (row >= a.Hkv * a.Rp) return;
+    const int h = row / a.Rp, rho = row - h * a.Rp;
+    const int lane = threadIdx.x, sg = lane / NC;
+    const int dc = 4 * (cb * NC + (lane - sg * NC));
     const int t = rho / a.G, gg = rho - t * a.G;
     const size_t o = (size_t)t * a.Hq + h * a.G + gg;
     const size_t base = (size_t)h * a.S * a.Rp + rho;      // row of split 0; stride Rp per split
-    const int sg = tid / DQ, dq = tid - sg * DQ;
 
     f32x4 ov[MAXI];
     float sv[MAXI];
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-        const int s = sg + i * NSG;
+        const int s = sg + i * NG;
         const bool in = s < a.S;
-        ov[i] = in ? *(const f32x4 *)(a.part_O + (base + (size_t)s * a.Rp) * D + 4 * dq) : f32x4{0.f, 0.f, 0.f, 0.f};
-        sv[i] = (in && dq == 0) ? a.part_s[base + (size_t)s * a.Rp] : 0.f;
+        ov[i] = in ? *(const f32x4 *)(a.part_O + (base + (size_t)s * a.Rp) * D + dc) : f32x4{0.f, 0.f, 0.f, 0.f};
+        sv[i] = in ? a.part_s[base + (size_t)s * a.Rp] : 0.f;
     }
     f32x4 acc = ov[0];
     float sacc = sv[0];
 #pragma unroll
     for (int i = 1; i < MAXI; ++i) { acc += ov[i]; sacc += sv[i]; }
-    for (int s = sg + MAXI * NSG; s < a.S; s += NSG) {
-        acc += *(const f32x4 *)(a.part_O + (base + (size_t)s * a.Rp) * D + 4 * dq);
-        if (dq == 0) sacc += a.part_s[base + (size_t)s * a.Rp];
+    for (int s = sg + MAXI * NG; s < a.S; s += NG) {
+        acc += *(const f32x4 *)(a.part_O + (base + (size_t)s * a.Rp) * D + dc);
+        sacc += a.part_s[base + (size_t)s * a.Rp];
     }
-    accs[sg][dq] = acc;
-#pragma unroll
-    for (int o2 = 32; o2 >= 1; o2 >>= 1) sacc += __shfl_xor(sacc, o2, 64);
-    if ((tid & 63) == 0) red[tid >> 6] = sacc;
-    __syncthreads();
-    if (tid >= DQ) return;
-    f32x4 O = *(const f32x4 *)(a.b2 + (size_t)h * D + 4 * tid);
-    for (int k = 0; k < NSG; ++k) O += accs[k][tid];
-    *(f32x4 *)(a.A_out + o * D + 4 * tid) = O;
-    if (tid == 0) a.a_out[o] = a.bs2[h] + ((red[0] + red[1]) + (red[2] + red[3]));
+    const f32x4 O = splits_sum4<NC>(acc);
+    const float ssum = splits_sum<NC>(sacc);
+    if (sg != 0) return;
+    *(f32x4 *)(a.A_out + o * D + dc) = O + *(const f32x4 *)(a.b2 + (size_t)h * D + dc);
+    if (cb == 0 && lane == 0) a.a_out[o] = a.bs2[h] + ssum;
 }
 
 static inline unsigned blocks_for_waves(long waves) { return (unsigned)((waves + 3) / 4); }
@@ -137,9 +134,13 @@ hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipS
 }
 
 hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st) {
-    dim3 grid((unsigned)((long)p.Hkv * p.Rp)), block(256);
-    if (d == 128) hipLaunchKernelGGL((mlp_reduce<128, 8>), grid, block, 0, st, p);
-    else if (d == 64) hipLaunchKernelGGL((mlp_reduce<64, 4>), grid, block, 0, st, p);
+    const long rows = (long)p.Hkv * p.Rp;
+    const bool sliced = rows * (d / 4 / kSliceCols) <= kReduceSliceWaves;
+    dim3 grid((unsigned)slice_grid(rows, sliced ? d / 4 / kSliceCols : 1)), block(64);
+    if (d == 128 && sliced) hipLaunchKernelGGL((mlp_reduce<128, kSliceCols, kSliceCols>), grid, block, 0, st, p);
+    else if (d == 128) hipLaunchKernelGGL((mlp_reduce<128, 32, 4>), grid, block, 0, st, p);
+    else if (d == 64 && sliced) hipLaunchKernelGGL((mlp_reduce<64, kSliceCols, kSliceCols>), grid, block, 0, st, p);
+    else if (d == 64) hipLaunchKernelGGL((mlp_reduce<64, 16, 8>), grid, block, 0, st, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

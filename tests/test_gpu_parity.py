@@ -51,6 +51,20 @@ def test_doc_attn_bf16(nx, d, R, Hq, Hkv, n, splits):
     check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
 
 
+@pytest.mark.parametrize("d,R,n,splits", [(128, 300, 700, 7), (128, 300, 700, 0), (64, 520, 300, 5)])
+def test_doc_attn_many_rows(nx, d, R, n, splits):
+    """Over 8,192 rows (d = 128) or 16,384 rows (d = 64): the split-K combine
+    runs one wave per row over all dims instead of 16-dim row slices."""
+    Hq, Hkv = 32, 8
+    print("case doc_attn many rows d=%d R=%d n=%d splits=%d" % (d, R, n, splits), flush=True)
+    g = _rng(30, d, R, n, splits)
+    q, K, V = (_bf(g.standard_normal(s)) for s in ((R, Hq, d), (Hkv, n, d), (Hkv, n, d)))
+    a, A = nx.doc_attn_exact(dev(q), dev(K), dev(V), Hkv, splits=splits)
+    ea, eA = oracle.doc_attn(q, K, V, dt="bf16", Hq=Hq, Hkv=Hkv)
+    check("alpha", host(a), ea, 1e-3)
+    check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
+
+
 @pytest.mark.parametrize("n", [19217, 61457])
 def test_doc_attn_balanced_splits(nx, n):
     """Decode rows (4 per KV head): the automatic plan spreads the 64-key batches
@@ -178,6 +192,21 @@ def _mlp_dev(nx, P, act):
 def _mlp_oracle(q, P, dt, Hq, Hkv, act):
     return oracle.mlp(q, P["W1"], P["b1"], P["W2t"], P["b2"], P["Ws"], P["bs"], P["ws2"], P["bs2"],
                       dt=dt, Hq=Hq, Hkv=Hkv, act=act)
+
+
+@pytest.mark.parametrize("d,R,Ht,Hs,splits", [(128, 300, 256, 128, 3), (128, 300, 320, 192, 0), (64, 520, 100, 70, 4)])
+def test_mlp_many_rows(nx, d, R, Ht, Hs, splits):
+    """Over 8,192 rows (d = 128) or 16,384 rows (d = 64) with several hidden-unit
+    splits: the split reduce runs one wave per row over all dims."""
+    Hq, Hkv = 32, 8
+    print("case mlp many rows d=%d R=%d Ht=%d Hs=%d splits=%d" % (d, R, Ht, Hs, splits), flush=True)
+    g = _rng(31, d, R, Ht, Hs, splits)
+    q = _bf(g.standard_normal((R, Hq, d)))
+    P = _mlp_np(g, Hkv, d, Ht, Hs, "bf16")
+    a, A = nx.module_forward(dev(q), _mlp_dev(nx, P, nx.GELU), Hkv, splits=splits)
+    ea, eA = _mlp_oracle(q, P, "bf16", Hq, Hkv, "gelu")
+    check("a", host(a), ea, ATOL_LSE_BF16)
+    check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
 
 
 @pytest.mark.parametrize("R,Hq,Hkv,Ht,Hs", [(5, 14, 2, 100, 70), (1, 32, 8, 256, 96), (20, 8, 2, 64, 33),
@@ -364,8 +393,19 @@ STEP_CASES = {
 def test_layer_step(nx, name):
     """nectar_layer_step against the oracle: every pair it writes and both merged
     outputs; the exact output also against full attention over [document; local]."""
+    _check_layer_step(nx, name, 0)
+
+
+@pytest.mark.parametrize("name,splits", [("decode_bf16", 100), ("batch64_bf16", 70), ("decode_bf16_d64", 90)])
+def test_layer_step_many_splits(nx, name, splits):
+    """More than 64 key splits per part: the finishing pass and the split-K
+    combine fold the splits past the 64 they load up front in a serial tail."""
+    _check_layer_step(nx, name, splits)
+
+
+def _check_layer_step(nx, name, splits):
     dt, d, B, Tq, T, T_cap, qoff, Hq, Hkv, n, mod = STEP_CASES[name]
-    print("case layer_step %s" % name, flush=True)
+    print("case layer_step %s splits=%d" % (name, splits), flush=True)
     g = _rng(20, len(name), B, Tq, T)
     R = B * Tq
     q = _store(g.standard_normal((R, Hq, d)), dt)
@@ -386,7 +426,7 @@ def test_layer_step(nx, name):
         W, Z = (_store(g.standard_normal((Hkv, mod[1], d)), dt) for _ in range(2))
         module = nx.KVPairModule(dev(W), dev(Z))
     o = nx.layer_step(dev(q), dev(Kl), dev(Vl), Hkv, B=B, Tq=Tq, T_loc=T, q_offset=qoff, k=k, v=v,
-                      module=module, exact=exact, pairs=True)
+                      module=module, exact=exact, pairs=True, splits=splits)
     o = {key: host(t) for key, t in o.items()}
     if dt == "f32":
         to = tl = ATOL_F32

@@ -223,16 +223,14 @@ hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hi
     return hipGetLastError();
 }
 
-// Few rows (decode): d / 16 waves per row, 16 dims each, 64 splits loaded up
-// front; many rows: one wave per row over all dims, 8 (d = 128) or 32 (d = 64)
-// splits up front.
 hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st) {
     const long rows = (long)p.P * p.Rp;
-    const bool sliced = rows * (d / 4 / kSliceCols) <= kReduceSliceWaves;
-    dim3 grid((unsigned)slice_grid(rows, sliced ? d / 4 / kSliceCols : 1)), block(64);
+    const int nc = reduce_cols(rows, d, false);
+    dim3 grid((unsigned)slice_grid(rows, d / 4 / nc)), block(64);
+    // splits loaded up front: 64 for 16-dim slices, 8 (d = 128) or 32 (d = 64) for whole rows
 #define NECTAR_COMBINE_CASE(DD, T) \
     if (d == DD) { \
-        if (sliced) hipLaunchKernelGGL((attn_combine<DD, T, kSliceCols, kSliceCols>), grid, block, 0, st, p); \
+        if (nc == 4) hipLaunchKernelGGL((attn_combine<DD, T, 4, 4>), grid, block, 0, st, p); \
         else hipLaunchKernelGGL((attn_combine<DD, T, DD / 4, 64 * 8 / DD>), grid, block, 0, st, p); \
         return hipGetLastError(); }
     if (dtype == 1) { NECTAR_COMBINE_CASE(128, uint16_t) NECTAR_COMBINE_CASE(64, uint16_t) }

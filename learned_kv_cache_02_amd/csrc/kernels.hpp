@@ -43,12 +43,21 @@ struct AttnGroup {
 
 // Finishing pass over the split partials of AttnParams: writes the pair
 // (lse, A) and/or its merge with an extra (lse_x, A_x) pair.
-// Split reductions (combine, MLP reduce) run one wave per 16-dim slice of a row
-// while that takes at most this many waves, else one wave per row.
+// Split reductions (combine, MLP reduce): one wave per slice of a row, of
+// reduce_cols(...) float4 columns -- 16 dims (the most waves: the decode shapes
+// are latency-bound), 32 dims (whole 128-byte lines per split) for the plain
+// sums of the MLP reduce past kReduceFewRows rows, or the whole row when
+// slices would take more than kReduceSliceWaves waves.  Batch-64 decode
+// (2,048 rows, 32 splits), 32-dim against 16-dim slices: MLP module forward
+// 45.2 against 46.5 us, exact document pass with its combine 360.4 against
+// 356.6 us, so only the MLP reduce takes the wider slices.
 constexpr long kReduceSliceWaves = 65536;
-// float4 columns per slice wave (16 dims; 32-dim slices measured slower at the
-// 4B exact entry point: 50.3 against 48.2 us)
-constexpr int kSliceCols = 4;
+constexpr long kReduceFewRows = 512;
+inline int reduce_cols(long rows, int d, bool lines) {
+    if (rows * (d / 16) <= kReduceSliceWaves && (!lines || rows <= kReduceFewRows)) return 4;
+    if (lines && rows * (d / 32) <= kReduceSliceWaves) return 8;
+    return d / 4;
+}
 
 struct CombineParams {
     const float *part_O;

@@ -135,14 +135,17 @@ hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipS
 
 hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st) {
     const long rows = (long)p.Hkv * p.Rp;
-    const bool sliced = rows * (d / 4 / kSliceCols) <= kReduceSliceWaves;
-    dim3 grid((unsigned)slice_grid(rows, sliced ? d / 4 / kSliceCols : 1)), block(64);
-    if (d == 128 && sliced) hipLaunchKernelGGL((mlp_reduce<128, kSliceCols, kSliceCols>), grid, block, 0, st, p);
-    else if (d == 128) hipLaunchKernelGGL((mlp_reduce<128, 32, 4>), grid, block, 0, st, p);
-    else if (d == 64 && sliced) hipLaunchKernelGGL((mlp_reduce<64, kSliceCols, kSliceCols>), grid, block, 0, st, p);
-    else if (d == 64) hipLaunchKernelGGL((mlp_reduce<64, 16, 8>), grid, block, 0, st, p);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    const int nc = reduce_cols(rows, d, true);
+    dim3 grid((unsigned)slice_grid(rows, d / 4 / nc)), block(64);
+#define NECTAR_REDUCE_CASE(DD) \
+    if (d == DD) { \
+        if (nc == 4) hipLaunchKernelGGL((mlp_reduce<DD, 4, 4>), grid, block, 0, st, p); \
+        else if (nc == 8) hipLaunchKernelGGL((mlp_reduce<DD, 8, 8>), grid, block, 0, st, p); \
+        else hipLaunchKernelGGL((mlp_reduce<DD, DD / 4, 64 * 8 / DD>), grid, block, 0, st, p); \
+        return hipGetLastError(); }
+    NECTAR_REDUCE_CASE(128) NECTAR_REDUCE_CASE(64)
+#undef NECTAR_REDUCE_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace nectar

@@ -129,7 +129,9 @@ __global__ __launch_bounds__(64) void attn_combine(CombineParams a) {
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) mloc = fmaxf(mloc, st[i].x);
     for (int s = sg + MAXI * NG; s < a.S; s += NG) mloc = fmaxf(mloc, ml[(size_t)s * a.Rp].x);
-    const float M = splits_max<NC>(mloc);
+    float mred[1] = {mloc};
+    splits_fold<NC, true>(mred);
+    const float M = mred[0];
     const bool empty = (M == -INFINITY);
     float lloc = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -147,8 +149,10 @@ __global__ __launch_bounds__(64) void attn_combine(CombineParams a) {
             acc += w * *(const f32x4 *)(po + (size_t)s * a.Rp * D + dc);
         }
     }
-    const float L = splits_sum<NC>(lloc);
-    const f32x4 O = splits_sum4<NC>(acc);
+    float red[5] = {lloc, acc[0], acc[1], acc[2], acc[3]};
+    splits_fold<NC, false>(red);
+    const float L = red[0];
+    const f32x4 O = {red[1], red[2], red[3], red[4]};
     if (sg != 0) return;
     const bool lead = (cb == 0 && lane == 0);   // writes the row's scalars
 

@@ -106,24 +106,29 @@ static inline long slice_grid(long rows, int nb) { return nb == 1 ? rows : (rows
 
 // Folds over the split groups of a wave whose lane (g, c) = (lane / NC, lane %
 // NC) holds column c of the splits of group g: lanes that differ only in the
-// bits from NC up are combined in a fixed butterfly order and every lane ends
-// with the total of its column.
-template <int NC> __device__ __forceinline__ float splits_max(float v) {
-#pragma unroll
-    for (int o = NC; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+// bits from NC up are combined, N independent values at a time, and every lane
+// ends with the total of its column.  The steps inside a row of 16 lanes are
+// DPP row rotations (a rotation by o, then by 2o, ..., sums each lane with every
+// lane of its row that agrees with it modulo o); the steps across rows are
+// lane exchanges.  The order is fixed, so the totals are reproducible and equal
+// in every lane of a column.
+template <int OFF> __device__ __forceinline__ float row_rotate(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + OFF, 0xf, 0xf, false));
 }
-template <int NC> __device__ __forceinline__ float splits_sum(float v) {
+template <int NC, bool MAX, int N> __device__ __forceinline__ void splits_fold(float (&v)[N]) {
+    auto fold = [&](auto get) {
 #pragma unroll
-    for (int o = NC; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-template <int NC> __device__ __forceinline__ f32x4 splits_sum4(f32x4 v) {
-#pragma unroll
-    for (int o = NC; o < 64; o <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], o, 64);
-    return v;
+        for (int i = 0; i < N; ++i) {
+            const float o = get(v[i]);
+            v[i] = MAX ? fmaxf(v[i], o) : v[i] + o;
+        }
+    };
+    if constexpr (NC <= 1) fold([](float x) { return row_rotate<1>(x); });
+    if constexpr (NC <= 2) fold([](float x) { return row_rotate<2>(x); });
+    if constexpr (NC <= 4) fold([](float x) { return row_rotate<4>(x); });
+    if constexpr (NC <= 8) fold([](float x) { return row_rotate<8>(x); });
+    if constexpr (NC <= 16) fold([](float x) { return __shfl_xor(x, 16, 64); });
+    if constexpr (NC <= 32) fold([](float x) { return __shfl_xor(x, 32, 64); });
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

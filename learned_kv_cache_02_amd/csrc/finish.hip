@@ -78,23 +78,28 @@ __global__ __launch_bounds__(64) void attn_finish(FinishParams a) {
             }
         }
 
-    // per part: (M in log2 units, L, O) with the read-out unnormalised by L
-    float M[kMaxSets], L[kMaxSets];
-    f32x4 O[kMaxSets];
+    // per part: (M in log2 units, L, O) with the read-out unnormalised by L.
+    // The maxima of all parts are folded together, then every sum of all parts.
+    float mx[kMaxSets];
 #pragma unroll
     for (int k = 0; k < kMaxSets; ++k) {
-        M[k] = -INFINITY;
-        L[k] = 0.f;
-        O[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mx[k] = -INFINITY;
+        if (k >= nparts || !pml[k]) continue;   // uniform
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) mx[k] = fmaxf(mx[k], st[k][i].x);
+        for (int s = sg + MAXI * NG; s < S[k]; s += NG) mx[k] = fmaxf(mx[k], pml[k][s * stride[k]].x);
+    }
+    splits_fold<NC, true>(mx);
+    float red[kMaxSets * 5];                    // per part: the scalar sum, then four read-out sums
+#pragma unroll
+    for (int i = 0; i < kMaxSets * 5; ++i) red[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxSets; ++k) {
         if (k >= nparts) continue;             // uniform
+        float lloc = 0.f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (pml[k]) {
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < MAXI; ++i) mloc = fmaxf(mloc, st[k][i].x);
-            for (int s = sg + MAXI * NG; s < S[k]; s += NG) mloc = fmaxf(mloc, pml[k][s * stride[k]].x);
-            const float Mk = splits_max<NC>(mloc);
-            float lloc = 0.f;
+            const float Mk = mx[k];
             if (Mk != -INFINITY) {
 #pragma unroll
                 for (int i = 0; i < MAXI; ++i) {
@@ -109,26 +114,39 @@ __global__ __launch_bounds__(64) void attn_finish(FinishParams a) {
                     acc += w * *(const f32x4 *)(pO[k] + s * stride[k] * D + dc);
                 }
             }
-            L[k] = splits_sum<NC>(lloc);
-            M[k] = Mk;
         } else {
             // MLP module: a = bs2 + sum of score partials, A = b2 + sum of read-out partials
-            float sloc = 0.f;
 #pragma unroll
             for (int i = 0; i < MAXI; ++i) {
-                sloc += st[k][i].x;
+                lloc += st[k][i].x;
                 acc += ov[k][i];
             }
             for (int s = sg + MAXI * NG; s < S[k]; s += NG) {
-                sloc += ps[k][s * stride[k]];
+                lloc += ps[k][s * stride[k]];
                 acc += *(const f32x4 *)(pO[k] + s * stride[k] * D + dc);
             }
-            const float asum = splits_sum<NC>(sloc);
-            M[k] = (a.set[k - 1].bs2[h] + asum) * kLog2e;   // the pair's log-normaliser, log2 units
-            L[k] = 1.f;
         }
-        O[k] = splits_sum4<NC>(acc);
-        if (k > 0 && !pml[k]) O[k] += *(const f32x4 *)(a.set[k - 1].b2 + (size_t)h * D + dc);
+        red[5 * k] = lloc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[5 * k + 1 + e] = acc[e];
+    }
+    splits_fold<NC, false>(red);
+    float M[kMaxSets], L[kMaxSets];
+    f32x4 O[kMaxSets];
+#pragma unroll
+    for (int k = 0; k < kMaxSets; ++k) {
+        O[k] = f32x4{red[5 * k + 1], red[5 * k + 2], red[5 * k + 3], red[5 * k + 4]};
+        if (k >= nparts) {
+            M[k] = -INFINITY;
+            L[k] = 0.f;
+        } else if (pml[k]) {
+            M[k] = mx[k];
+            L[k] = red[5 * k];
+        } else {
+            M[k] = (a.set[k - 1].bs2[h] + red[5 * k]) * kLog2e;   // the pair's log-normaliser, log2 units
+            L[k] = 1.f;
+            O[k] += *(const f32x4 *)(a.set[k - 1].b2 + (size_t)h * D + dc);
+        }
     }
     if (sg != 0) return;
     const bool lead = (cb == 0 && lane == 0);   // writes the row's scalars

@@ -102,8 +102,10 @@ __global__ __launch_bounds__(64) void mlp_reduce(MlpReduceParams a) {
         acc += *(const f32x4 *)(a.part_O + (base + (size_t)s * a.Rp) * D + dc);
         sacc += a.part_s[base + (size_t)s * a.Rp];
     }
-    const f32x4 O = splits_sum4<NC>(acc);
-    const float ssum = splits_sum<NC>(sacc);
+    float red[5] = {sacc, acc[0], acc[1], acc[2], acc[3]};
+    splits_fold<NC, false>(red);
+    const float ssum = red[0];
+    const f32x4 O = {red[1], red[2], red[3], red[4]};
     if (sg != 0) return;
     *(f32x4 *)(a.A_out + o * D + dc) = O + *(const f32x4 *)(a.b2 + (size_t)h * D + dc);
     if (cb == 0 && lane == 0) a.a_out[o] = a.bs2[h] + ssum;

@@ -310,7 +310,7 @@ const char *nectar_status_string(nectar_status s) {
     switch (s) {
         case NECTAR_OK: return "NECTAR_OK: success";
         case NECTAR_EINVAL: return "NECTAR_EINVAL: invalid argument (null pointer, shape, alignment or enum)";
-        case NECTAR_EUNSUPPORTED: return "NECTAR_EUNSUPPORTED: valid arguments not supported by this build";
+        case NECTAR_EUNSUPPORTED: return "NECTAR_EUNSUPPORTED: valid arguments not supported by this library";
         case NECTAR_EWORKSPACE: return "NECTAR_EWORKSPACE: workspace smaller than the size query requires";
         case NECTAR_EHIP: return "NECTAR_EHIP: HIP launch or execution error";
     }

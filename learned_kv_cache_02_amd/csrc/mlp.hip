@@ -20,9 +20,11 @@
 
 namespace nectar {
 
+// Two weight tiles in registers (4B decode module: 13.4 us; three 13.4 us, four
+// 13.7 us).
 template <int D, int RT, int ACT>
 __global__ __launch_bounds__(256) void mlp_partial_mfma(MlpParams a) {
-    mlp_partial_body<D, RT, ACT>(a, (int)blockIdx.x);
+    mlp_partial_body<D, RT, ACT, 2>(a, (int)blockIdx.x);
 }
 
 // fp32 path: one wave per (KV head, row, split); lanes own output dimensions.

@@ -129,9 +129,10 @@ __device__ __forceinline__ void score_tile(const MTile<D> &T, int j0, int Hs,
 }
 
 // Block blk_id of the MLP partial grid (Hkv x RB x SB blocks of 4 waves).
-// DBUF: double-buffer the weight tiles (one tile in flight while the previous
-// one is computed); without it the body needs about 80 fewer registers.
-template <int D, int RT, int ACT, bool DBUF = true>
+// NBUF: weight tiles held in registers at once -- NBUF - 1 tiles in flight while
+// one is computed (about 80 registers per tile); 1 loads each tile just before
+// its use.
+template <int D, int RT, int ACT, int NBUF = 2>
 __device__ __forceinline__ void mlp_partial_body(const MlpParams &a, int blk_id) {
     constexpr int KS = D / 32, DV = D / 16;
     __shared__ f32x4 fold_O[2][RT * DV][64];
@@ -192,22 +193,27 @@ __device__ __forceinline__ void mlp_partial_body(const MlpParams &a, int blk_id)
         if (i < ntt) tgt_tile<D, RT, ACT>(T, jt_lo + 32 * i, a.Ht, qv, g, O);
         else score_tile<D, RT, ACT>(T, js_lo + 32 * (i - ntt), a.Hs, qv, g, sc);
     };
-    if (!DBUF) {
+    if (NBUF == 1) {
         for (int i = 0; i < ntiles; ++i) {
             MTile<D> t0;
             load(t0, i);
             run(t0, i);
         }
     } else if (ntiles > 0) {
-        MTile<D> t0, t1;
-        load(t0, 0);
-        for (int i = 0; i < ntiles; i += 2) {
-            const bool has1 = i + 1 < ntiles;
-            if (has1) load(t1, i + 1);
-            run(t0, i);
-            if (!has1) break;
-            if (i + 2 < ntiles) load(t0, i + 2);
-            run(t1, i + 1);
+        // ring of NBUF tiles: before tile i is computed, tile i + NBUF - 1 is
+        // issued into the slot tile i - 1 has just left (static slot indices)
+        MTile<D> t[NBUF];
+#pragma unroll
+        for (int k = 0; k < NBUF - 1; ++k)
+            if (k < ntiles) load(t[k], k);
+        for (int i0 = 0; i0 < ntiles; i0 += NBUF) {
+#pragma unroll
+            for (int k = 0; k < NBUF; ++k) {
+                const int i = i0 + k;
+                if (i >= ntiles) break;
+                if (i + NBUF - 1 < ntiles) load(t[(k + NBUF - 1) % NBUF], i + NBUF - 1);
+                run(t[k], i);
+            }
         }
     }
 #pragma unroll

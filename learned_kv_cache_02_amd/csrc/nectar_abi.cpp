@@ -999,12 +999,13 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
                 (!sp.kvp || decode(sp.kvpl))));
     if (sp.fused) {
         if (sp.mlp && exact) sp.mlpl = plan_mlp(d, m->Ht, m->Hs, kTargetWavesMlpShared);
-        // with a module in the same launch the document leaves 64 of the 512
+        // with a module in the same launch the document leaves 48 of the 512
         // two-per-CU block slots free from the start, so the module's blocks run
-        // beside the document's instead of after them (4B step: all 512 slots
-        // to the document 61.2 us, 480 in whole-batch splits 59.8 us, 448
-        // balanced 59.2 us)
-        if (exact && m) sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n, true, kTargetWaves - 256);
+        // beside the document's instead of after them (4B step, waves left free
+        // 96 / 128 / 160 / 192 / 256 / 352: 56.8 / 56.0 / 55.0 / 54.8 / 55.5 /
+        // 56.9 us; all 512 slots to the document was 61.2 us with the earlier
+        // finishing pass)
+        if (exact && m) sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n, true, kTargetWaves - 192);
         // exact path alone: the document leaves the local part's blocks their
         // slots, so both fill the 512 two-per-CU slots in one wave of blocks
         // (4B exact path 49.4 -> 48.5 us)

@@ -416,10 +416,10 @@ def test_layer_step_validation(lib):
     bad = _mlp_module(); bad.act = 7
     assert call(both, module=bad) == EINVAL
     need = lib.nectar_layer_step_workspace_size(ctypes.byref(d), 61440, ctypes.byref(loc), ctypes.byref(m), 1)
-    # deferred partials of all three parts: the document's 56 blocks per head (448 of the 512
+    # deferred partials of all three parts: the document's 58 blocks per head (464 of the 512
     # two-per-CU block slots, leaving room for the module's blocks) and the local part's 3
     # (4 rows x 520 B each), plus the module's split partials
-    assert need >= 8 * 56 * 4 * 520 + 8 * 3 * 4 * 520
+    assert need >= 8 * 58 * 4 * 520 + 8 * 3 * 4 * 520
     assert call(both, module=m, ws=A16, nbytes=need - 1) == EWORKSPACE
     only_loc = lib.nectar_layer_step_workspace_size(ctypes.byref(d), 61440, ctypes.byref(loc), None, 0)
     assert 0 < only_loc < need

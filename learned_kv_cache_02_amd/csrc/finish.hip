@@ -180,9 +180,10 @@ __global__ __launch_bounds__(64) void attn_finish(FinishParams a) {
 }
 
 hipError_t launch_finish(const FinishParams &p, int dtype, int d, hipStream_t st) {
-    // float4 columns per wave: 8 waves per row at d = 128, 4 at d = 64 (4B decode
-    // step: 2 columns 56.5 us, 4 columns 55.9 us, 8 columns 56.6 us)
-    constexpr int kCols = 4;
+    // float4 columns per wave: 16 waves per row at d = 128, 8 at d = 64 (4B decode
+    // step with the batched folds: 2 columns 54.5 us, 4 columns 54.8 us, 8 columns
+    // 56.1 us)
+    constexpr int kCols = 2;
     dim3 grid((unsigned)slice_grid((long)p.P * p.Rp, d / 4 / kCols)), block(64);
     if (d == 128 && dtype == 1) hipLaunchKernelGGL((attn_finish<128, uint16_t, kCols>), grid, block, 0, st, p);
     else if (d == 128) hipLaunchKernelGGL((attn_finish<128, float, kCols>), grid, block, 0, st, p);

@@ -229,12 +229,16 @@ hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hi
 
 hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st) {
     const long rows = (long)p.P * p.Rp;
-    const int nc = reduce_cols(rows, d, false);
+    // 8-dim slices for the fewest rows (4B exact entry point, 32 rows: 48.0 ->
+    // 47.4 us; at 224 rows 16-dim slices stay faster, 10.7 against 11.0 us)
+    const int nc0 = reduce_cols(rows, d, false);
+    const int nc = (nc0 == 4 && rows <= 64) ? 2 : nc0;
     dim3 grid((unsigned)slice_grid(rows, d / 4 / nc)), block(64);
     // splits loaded up front: 64 for 16-dim slices, 8 (d = 128) or 32 (d = 64) for whole rows
 #define NECTAR_COMBINE_CASE(DD, T) \
     if (d == DD) { \
-        if (nc == 4) hipLaunchKernelGGL((attn_combine<DD, T, 4, 4>), grid, block, 0, st, p); \
+        if (nc == 2) hipLaunchKernelGGL((attn_combine<DD, T, 2, 2>), grid, block, 0, st, p); \
+        else if (nc == 4) hipLaunchKernelGGL((attn_combine<DD, T, 4, 4>), grid, block, 0, st, p); \
         else hipLaunchKernelGGL((attn_combine<DD, T, DD / 4, 64 * 8 / DD>), grid, block, 0, st, p); \
         return hipGetLastError(); }
     if (dtype == 1) { NECTAR_COMBINE_CASE(128, uint16_t) NECTAR_COMBINE_CASE(64, uint16_t) }

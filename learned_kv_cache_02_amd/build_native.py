@@ -4,6 +4,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -25,25 +26,31 @@ def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
-    objs = []
+def _compile(src: str, extra_flags, verbose: bool, tag: str) -> str:
     inc = ["-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
-    for src in SOURCES:
-        obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + ".o")
-        cmd = ([hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(src, []) + list(extra_flags) + inc +
-               ["-c", os.path.join(CSRC, src), "-o", obj])
-        if src.endswith(".cpp"):
-            cmd.insert(1, "-x")
-            cmd.insert(2, "hip")
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-        log = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
-        if r.returncode != 0:
-            raise RuntimeError("hipcc failed for %s:\n%s" % (src, log))
-        if verbose and log.strip():
+    obj = os.path.join(CSRC, "%s.%s.o" % (src.rsplit(".", 1)[0], tag))
+    cmd = ([hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(src, []) + list(extra_flags) + inc +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
+    if src.endswith(".cpp"):
+        cmd.insert(1, "-x")
+        cmd.insert(2, "hip")
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    log = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, log))
+    if verbose:
+        print(" ".join(cmd), flush=True)
+        if log.strip():
             print(log)
-        objs.append(obj)
+    return obj
+
+
+def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
+    # the sources compile independently: one hipcc per source, in parallel
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    tag = "b%d" % os.getpid()
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda src: _compile(src, extra_flags, verbose, tag), SOURCES))
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -1211,10 +1211,13 @@ size_t nectar_layer_step_workspace_size(const nectar_attn_desc *desc, int64_t n,
     return plan_step(desc, n, loc, module, exact != 0).bytes;
 }
 
-nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const nectar_local_desc *loc,
-                                const void *q, const void *k, const void *v, const void *k_loc,
-                                const void *v_loc, const nectar_module *module,
-                                const nectar_step_outputs *outs, void *ws, size_t ws_bytes, void *stream) {
+// Every argument check of the layer step (no HIP call); on NECTAR_OK *sp holds
+// the plan, unless R == 0 (*noop: nothing to launch).
+static nectar_status check_layer_step(const nectar_attn_desc *desc, int64_t n, const nectar_local_desc *loc,
+                                      const void *q, const void *k, const void *v, const void *k_loc,
+                                      const void *v_loc, const nectar_module *module,
+                                      const nectar_step_outputs *outs, StepPlan *sp, bool *noop) {
+    *noop = false;
     nectar_status s = check_desc(desc);
     if (s != NECTAR_OK) return s;
     if ((s = check_local(desc, loc)) != NECTAR_OK) return s;
@@ -1232,16 +1235,23 @@ nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const n
     const void *rows[] = {outs->A_out, outs->Am_out, outs->Aloc_out, outs->out_exact, outs->out_nectar};
     for (const void *r : rows)
         if (r && !rows_ok(r)) return NECTAR_EINVAL;
-    if (desc->R == 0) return NECTAR_OK;
+    if (desc->R == 0) {
+        *noop = true;
+        return NECTAR_OK;
+    }
     if (!tensor_ok(q)) return NECTAR_EINVAL;
     if (loc->T_loc > 0 && (!tensor_ok(k_loc) || !tensor_ok(v_loc))) return NECTAR_EINVAL;
     if (exact && n > 0 && (!tensor_ok(k) || !tensor_ok(v))) return NECTAR_EINVAL;
-    const StepPlan sp = plan_step(desc, n, loc, module, exact);
-    if ((s = check_ws(sp.bytes, ws, ws_bytes)) != NECTAR_OK) return s;
+    *sp = plan_step(desc, n, loc, module, exact);
+    return NECTAR_OK;
+}
 
-    hipStream_t st = (hipStream_t)stream;
-    char *w = (char *)ws;
-    if (!sp.fused) return finish(run_step_composed(desc, sp, n, loc, q, k, v, k_loc, v_loc, module, outs, w, st), st);
+// The launches of a checked layer step on workspace w (at least sp.bytes).
+static hipError_t run_layer_step(const nectar_attn_desc *desc, const StepPlan &sp, int64_t n,
+                                 const nectar_local_desc *loc, const void *q, const void *k, const void *v,
+                                 const void *k_loc, const void *v_loc, const nectar_module *module,
+                                 const nectar_step_outputs *outs, char *w, hipStream_t st) {
+    if (!sp.fused) return run_step_composed(desc, sp, n, loc, q, k, v, k_loc, v_loc, module, outs, w, st);
     const int G = desc->Hq / desc->Hkv;
     FinishParams f{};
     f.Hq = desc->Hq; f.G = G; f.Hkv = desc->Hkv; f.Tq = loc->Tq;
@@ -1307,7 +1317,20 @@ nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const n
         f.loc_ml = (const float2 *)(w + (size_t)sp.loc.P * sp.loc.SB * sp.loc.Rp * desc->d * 4);
     }
     if (e == hipSuccess) e = launch_finish(f, desc->dtype, desc->d, st);
-    return finish(e, st);
+    return e;
+}
+
+nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const nectar_local_desc *loc,
+                                const void *q, const void *k, const void *v, const void *k_loc,
+                                const void *v_loc, const nectar_module *module,
+                                const nectar_step_outputs *outs, void *ws, size_t ws_bytes, void *stream) {
+    StepPlan sp;
+    bool noop;
+    nectar_status s = check_layer_step(desc, n, loc, q, k, v, k_loc, v_loc, module, outs, &sp, &noop);
+    if (s != NECTAR_OK || noop) return s;
+    if ((s = check_ws(sp.bytes, ws, ws_bytes)) != NECTAR_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    return finish(run_layer_step(desc, sp, n, loc, q, k, v, k_loc, v_loc, module, outs, (char *)ws, st), st);
 }
 
 }  // extern "C"

@@ -540,3 +540,46 @@ def test_workload_layer_end_to_end(nx, cfg):
     check("exact merged lse vs full", lse_x, flse, tl)
     check("nectar merged out", out_n, eon, to, rel)
     check("nectar merged lse", lse_n, eln, tl)
+
+
+def test_c2_layer_step_as_timed(nx):
+    """The Qwen3-4B-shaped decode layer at full size (n = 61,440, 513 local keys,
+    MLP 4608/2944) through nectar_layer_step exactly as the benchmark calls it:
+    both paths in one call with every pair requested (the document's balanced
+    splits share the launch with the module's blocks, then one finishing pass),
+    then each path alone.  Every pair and both merged outputs against the oracle."""
+    cfg = configs.C2
+    print("case c2 layer step as timed", flush=True)
+    q = synth.queries(cfg)
+    K, V = synth.doc_kv(cfg)
+    Kl, Vl = synth.local_kv(cfg)
+    P = synth.mlp_params(cfg)
+    T, qoff = cfg.local_len(0), cfg.q_offset(0)
+    qd, Kd, Vd, Kld, Vld = dev(q), dev(K), dev(V), dev(Kl), dev(Vl)
+    mod = _mlp_dev(nx, P, nx.GELU)
+    kw = dict(dt="bf16", Hq=cfg.Hq, Hkv=cfg.Hkv)
+    Klv, Vlv = (np.ascontiguousarray(x[:, :, :T]) for x in (Kl, Vl))
+    ea, eA = oracle.doc_attn(q, K, V, **kw)
+    em, eAm = _mlp_oracle(q, P, "bf16", cfg.Hq, cfg.Hkv, "gelu")
+    el, eAl = oracle.local_attn(q, Klv, Vlv, B=cfg.B, Tq=cfg.Tq, Tloc=T, q_offset=qoff, **kw)
+    flse, fout = oracle.full_attn(q, K, V, Klv, Vlv, B=cfg.B, Tq=cfg.Tq, Tloc=T, q_offset=qoff, **kw)
+    eon, eln = oracle.merge(em, eAm, el, eAl)
+    to, tl, rel = ATOL_OUT_BF16, ATOL_LSE_BF16, REL_L2_BF16
+    skw = dict(B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff, pairs=True)
+    for name, exact, module in (("both paths", True, mod), ("nectar path", False, mod),
+                                ("exact path", True, None)):
+        o = nx.layer_step(qd, Kld, Vld, cfg.Hkv, k=Kd if exact else None, v=Vd if exact else None,
+                          module=module, exact=exact, **skw)
+        o = {key: host(t) for key, t in o.items()}
+        check(name + ": lambda", o["lam"], el, tl)
+        check(name + ": A_local", o["Aloc"], eAl, to, rel)
+        if exact:
+            check(name + ": alpha", o["alpha"], ea, tl)
+            check(name + ": A", o["A"], eA, to, rel)
+            check(name + ": exact out vs full attention", o["out_exact"], fout, to, rel)
+            check(name + ": exact lse vs full attention", o["lse_exact"], flse, tl)
+        if module is not None:
+            check(name + ": module a", o["a"], em, tl)
+            check(name + ": module A", o["Am"], eAm, to, rel)
+            check(name + ": nectar out", o["out_nectar"], eon, to, rel)
+            check(name + ": nectar lse", o["lse_nectar"], eln, tl)

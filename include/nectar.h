@@ -30,7 +30,8 @@
  *   (innermost index last), 16-byte aligned.  The library never allocates,
  *   frees or synchronizes; every call is asynchronous on `stream` (a
  *   hipStream_t; NULL = the null stream).  Outputs are complete when later work
- *   on that stream runs.  No global mutable state: calls are thread-safe;
+ *   on that stream runs.  No global mutable state (the one exception is the
+ *   device scratch of nectar_layer_step_static): calls are thread-safe;
  *   concurrent calls must use distinct workspaces.
  * - Query layout q[R][Hq][d] (token-major).  Query head h' reads KV head
  *   h = h' / (Hq / Hkv) (contiguous GQA groups; the group's query heads share
@@ -400,6 +401,30 @@ NECTAR_API nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t
                                            const void *v_loc, const nectar_module *module,
                                            const nectar_step_outputs *outs, void *ws, size_t ws_bytes,
                                            void *stream);
+
+/*
+ * nectar_layer_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Arguments, outputs and results are those
+ * of nectar_layer_step (the same plan and kernels, so the same bits).  The
+ * split partials go to a scratch array the library holds in device memory, one
+ * copy per GPU it runs on, NECTAR_STATIC_SCRATCH_BYTES long, kept until the
+ * process ends; its address is looked up on the first call on each device.
+ * The call allocates nothing, and nothing in the scratch needs to start at zero.
+ * Errors: NECTAR_EWORKSPACE (nothing launched) when the plan needs more scratch
+ * than NECTAR_STATIC_SCRATCH_BYTES (nectar_layer_step_workspace_size gives the
+ * need: every decode shape of the 4B, 8B and 1M-token layers fits; the
+ * 16 x 1,024-token prefill does not); NECTAR_EHIP when the scratch address
+ * cannot be obtained.  Every call on one GPU uses that GPU's one scratch array:
+ * calls that may overlap on the same GPU (other streams, other threads) race,
+ * and must be ordered by the caller.
+ */
+#define NECTAR_STATIC_SCRATCH_BYTES (64u << 20)
+NECTAR_API nectar_status nectar_layer_step_static(const nectar_attn_desc *desc, int64_t n,
+                                                  const nectar_local_desc *loc, const void *q, const void *k,
+                                                  const void *v, const void *k_loc, const void *v_loc,
+                                                  const nectar_module *module, const nectar_step_outputs *outs,
+                                                  void *stream);
 
 /* Zero-fills ws_bytes of device memory on `stream` with a fill kernel (no
  * memset node, so it can be captured in a graph); ws must be 16-byte aligned.

@@ -9,8 +9,15 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
+
+// Device scratch of nectar_layer_step_static: one copy per GPU the library is
+// loaded on, held until the process ends.  Host code never passes this name to
+// a kernel (on the host it is only a stand-in for the symbol): it uses the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[NECTAR_STATIC_SCRATCH_BYTES];
 
 static_assert(NECTAR_MERGE_K_MAX == nectar::kMergeKMax, "K-way merge limit");
 
@@ -1331,6 +1338,45 @@ nectar_status nectar_layer_step(const nectar_attn_desc *desc, int64_t n, const n
     if ((s = check_ws(sp.bytes, ws, ws_bytes)) != NECTAR_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     return finish(run_layer_step(desc, sp, n, loc, q, k, v, k_loc, v_loc, module, outs, (char *)ws, st), st);
+}
+
+// Device address of `scratch` on the device of `stream` (the current device for
+// the null stream), looked up once per device with that device current.
+static nectar_status static_scratch(hipStream_t st, char **out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *ptr[kMaxDevices] = {};
+    int cur = -1, dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return NECTAR_EHIP;
+    dev = cur;
+    if (st && hipStreamGetDevice(st, &dev) != hipSuccess) return NECTAR_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return NECTAR_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return NECTAR_EHIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return NECTAR_EHIP;
+        if (e != hipSuccess || !p) return NECTAR_EHIP;
+        ptr[dev] = p;
+    }
+    *out = (char *)ptr[dev];
+    return NECTAR_OK;
+}
+
+nectar_status nectar_layer_step_static(const nectar_attn_desc *desc, int64_t n, const nectar_local_desc *loc,
+                                       const void *q, const void *k, const void *v, const void *k_loc,
+                                       const void *v_loc, const nectar_module *module,
+                                       const nectar_step_outputs *outs, void *stream) {
+    StepPlan sp;
+    bool noop;
+    nectar_status s = check_layer_step(desc, n, loc, q, k, v, k_loc, v_loc, module, outs, &sp, &noop);
+    if (s != NECTAR_OK || noop) return s;
+    if (sp.bytes > (size_t)NECTAR_STATIC_SCRATCH_BYTES) return NECTAR_EWORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    char *w = nullptr;
+    if (sp.bytes > 0 && (s = static_scratch(st, &w)) != NECTAR_OK) return s;
+    return finish(run_layer_step(desc, sp, n, loc, q, k, v, k_loc, v_loc, module, outs, w, st), st);
 }
 
 }  // extern "C"

@@ -110,6 +110,8 @@ _lib.nectar_layer_step_workspace_size.argtypes = [_D, ctypes.c_int64, ctypes.POI
 _lib.nectar_layer_step_workspace_size.restype = ctypes.c_size_t
 _lib.nectar_layer_step.argtypes = [_D, ctypes.c_int64, ctypes.POINTER(LocalDesc), _P, _P, _P, _P, _P,
                                    ctypes.POINTER(Module), ctypes.POINTER(StepOutputs), _P, ctypes.c_size_t, _P]
+_lib.nectar_layer_step_static.argtypes = [_D, ctypes.c_int64, ctypes.POINTER(LocalDesc), _P, _P, _P, _P, _P,
+                                          ctypes.POINTER(Module), ctypes.POINTER(StepOutputs), _P]
 _lib.nectar_status_string.argtypes = [ctypes.c_int]
 _lib.nectar_status_string.restype = ctypes.c_char_p
 _lib.nectar_abi_version.restype = ctypes.c_int
@@ -117,7 +119,8 @@ _lib.nectar_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.nectar_workspace_init.restype = ctypes.c_int
 for _f in ("nectar_doc_attn_exact", "nectar_module_forward", "nectar_local_attn_lse", "nectar_merge",
            "nectar_merge_k", "nectar_fit_metrics", "nectar_mlp_loss_grad", "nectar_adamw_step",
-           "nectar_mlp_train_step", "nectar_layer_step", "nectar_doc_attn_partials", "nectar_doc_attn_combine"):
+           "nectar_mlp_train_step", "nectar_layer_step", "nectar_layer_step_static", "nectar_doc_attn_partials",
+           "nectar_doc_attn_combine"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -483,12 +486,13 @@ def mlp_train_step(q, module: "MLPModule", alpha, A_target, Hkv, hp: TrainHParam
 
 
 def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, module=None,
-               exact=True, pairs=False, scale=0.0, splits=0, out=None):
+               exact=True, pairs=False, scale=0.0, splits=0, out=None, no_alloc=False):
     """One fused layer step: exact path over k, v [Hkv][n][d] (when `exact`), Nectar path
     through `module` (when given), both merged with causal local attention over
     k_loc/v_loc [B][Hkv][T_cap][d].  Returns a dict of the outputs: out_exact,
     lse_exact, out_nectar, lse_nectar, and with `pairs` also alpha, A, a, Am, lam, Aloc.
-    `out` may supply preallocated tensors under the same keys."""
+    `out` may supply preallocated tensors under the same keys.  `no_alloc` calls the
+    allocation-free entry point (the library's own device scratch, no workspace)."""
     R, Hq, d = q.shape
     T_cap = k_loc.shape[-2]
     n = k.shape[-2] if (exact and k is not None) else 0
@@ -517,6 +521,11 @@ def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, 
                                                     "lse_nectar", "a", "Am", "lam", "Aloc")))
     m = module.struct() if module is not None else None
     mp = ctypes.byref(m) if m is not None else None
+    if no_alloc:
+        _check(_lib.nectar_layer_step_static(ctypes.byref(dsc), n, ctypes.byref(loc), _ptr(q),
+                                             _ptr(k) if exact else None, _ptr(v) if exact else None, _ptr(k_loc),
+                                             _ptr(v_loc), mp, ctypes.byref(so), _stream()))
+        return o
     nbytes = int(_lib.nectar_layer_step_workspace_size(ctypes.byref(dsc), n, ctypes.byref(loc), mp, int(exact)))
     wp, wn = _ws_args(nbytes, q.device)
     _check(_lib.nectar_layer_step(ctypes.byref(dsc), n, ctypes.byref(loc), _ptr(q), _ptr(k) if exact else None,

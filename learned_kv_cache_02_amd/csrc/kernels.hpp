@@ -80,7 +80,14 @@ struct MlpParams {
     float *part_s;   // [Hkv][SB][Rp]
     float *a_out, *A_out;   // written directly when SB == 1 and !defer
     int defer;              // write partials even when SB == 1 (a later pass finishes)
+    // decode kernel (mlp_decode.hpp): per (KV head, row group) nwt target waves
+    // and nws score waves, in SB blocks of four waves (RB == RG, WS == 4)
+    int nwt, nws;
 };
+
+// Largest number of 32-unit target tiles a wave of the decode MLP kernel
+// holds (a score wave holds twice as many score tiles).
+constexpr int kDecTiles = 2;
 
 // One layer of the deep MLP module (Eq. (3.6)) for every KV head p and row rho
 // of its Rp = R * G query rows:
@@ -283,6 +290,8 @@ struct MergeKParams {
 
 // Row tiling of the MFMA kernels: rows per wave = 16 * rt.
 int row_tiles_for(int Rp);
+// ... of the register-direct MLP kernel (up to 64 rows per wave).
+int mlp_row_tiles(int Rp);
 
 hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hipStream_t st);
 // LDS-staged attention for many rows per KV head (bf16, d = 128): NW waves of
@@ -297,11 +306,13 @@ hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st
 hipError_t launch_attn_partial_pair(const AttnParams &p0, const AttnParams &p1, int d, int rt, hipStream_t st);
 // One launch of register-direct bf16 attention blocks (one or two problem sets,
 // row tiling 1) and MLP module blocks (row tiling 1, decode kernel).
-hipError_t launch_step_partials(const AttnParams &p0, const AttnParams *p1, const MlpParams &m, int d,
+hipError_t launch_step_partials(const AttnParams &p0, const AttnParams *p1, const MlpParams &m, int d, int mlp_rt,
                                 hipStream_t st);
 hipError_t launch_attn_combine(const CombineParams &p, int dtype, int d, hipStream_t st);
 hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipStream_t st);
 hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st);
+// Decode-shape MLP (bf16, up to 16 * rt rows per wave): grid Hkv x RG x SB.
+hipError_t launch_mlp_decode(const MlpParams &p, int d, int rt, hipStream_t st);
 // MLP on the 32x32 MFMA with LDS-staged weights (bf16, d = 128, Ht and Hs
 // multiples of 64); grid Hkv x ceil(Rp / 256) x SB, 64-unit split granularity.
 hipError_t launch_mlp_rows_lds32(const MlpParams &p, hipStream_t st);

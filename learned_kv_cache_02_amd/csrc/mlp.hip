@@ -17,8 +17,16 @@
 // biases and writes (a, A) itself, otherwise mlp_reduce adds the partials in
 // split order.
 #include "mlp_body.hpp"
+#include "mlp_decode.hpp"
 
 namespace nectar {
+
+// Decode shapes (up to 64 rows per KV head): target and score waves, every
+// tile load issued up front, block fold through LDS (mlp_decode.hpp).
+template <int D, int RT, int ACT>
+__global__ __launch_bounds__(256, 1) void mlp_decode_mfma(MlpParams a) {
+    mlp_decode_body<D, RT, ACT, kDecTiles>(a, (int)blockIdx.x);
+}
 
 // Two weight tiles in registers (4B decode module: 13.4 us; three 13.4 us, four
 // 13.7 us).
@@ -115,6 +123,8 @@ __global__ __launch_bounds__(64) void mlp_reduce(MlpReduceParams a) {
 
 static inline unsigned blocks_for_waves(long waves) { return (unsigned)((waves + 3) / 4); }
 
+int mlp_row_tiles(int Rp) { return Rp <= 16 ? 1 : (Rp <= 32 ? 2 : 4); }
+
 hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipStream_t st) {
     if (dtype == 1) {
         dim3 grid((unsigned)((long)p.Hkv * p.RB * p.SB)), block(256);
@@ -135,6 +145,20 @@ hipError_t launch_mlp_partial(const MlpParams &p, int dtype, int d, int rt, hipS
     else if (d == 64) hipLaunchKernelGGL((mlp_partial_valu<64, float>), grid, block, 0, st, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+hipError_t launch_mlp_decode(const MlpParams &p, int d, int rt, hipStream_t st) {
+    dim3 grid((unsigned)((long)p.Hkv * p.RG * p.SB)), block(256);
+#define NECTAR_DEC_CASE(DD, RR) \
+    if (d == DD && rt == RR) { \
+        if (p.act == 1) hipLaunchKernelGGL((mlp_decode_mfma<DD, RR, 1>), grid, block, 0, st, p); \
+        else if (p.act == 2) hipLaunchKernelGGL((mlp_decode_mfma<DD, RR, 2>), grid, block, 0, st, p); \
+        else hipLaunchKernelGGL((mlp_decode_mfma<DD, RR, 0>), grid, block, 0, st, p); \
+        return hipGetLastError(); }
+    NECTAR_DEC_CASE(128, 1) NECTAR_DEC_CASE(128, 2) NECTAR_DEC_CASE(128, 4)
+    NECTAR_DEC_CASE(64, 1) NECTAR_DEC_CASE(64, 2) NECTAR_DEC_CASE(64, 4)
+#undef NECTAR_DEC_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_mlp_reduce(const MlpReduceParams &p, int d, hipStream_t st) {

@@ -1,0 +1,315 @@
+// Device code of the decode-shape MLP module kernel (up to 64 query rows per
+// KV head per wave), shared by the standalone module launch and the fused
+// decode-step launch.
+//
+// At decode the module forward streams every weight of the module once
+// (|theta| * 2 bytes per KV head) and does little arithmetic per byte, so the
+// kernel is built around one memory round trip per wave:
+//  * a wave is either a target wave (the 32-unit target tiles
+//    [t0, t1): W1 and W2t rows) or a score wave (32-unit score tiles: Ws rows
+//    and ws2); the host sizes both wave sets so every wave reads about the
+//    same number of bytes (a target tile is 16 KB at d = 128, a score tile
+//    8 KB, so score waves take up to twice as many tiles);
+//  * a wave issues the loads of all its tiles (at most NT target or 2 NT score
+//    tiles, indices clamped to its range) before its first product, in
+//    straight-line code, so every wait is for exactly the tile in use;
+//  * products as in the register-direct kernel: Z^T = W1_tile . Q^T on the
+//    16x16x32 MFMA with the query rows as B columns, bias + activation on the
+//    fp32 accumulators, the hidden tile rounded to bf16 and fed back as the B
+//    operand of O^T += W2t_tile^T . H^T (W2t rows transposed inside the lane);
+//    score hidden values stay fp32 and are dotted with ws2 on the VALU;
+//  * the block's four waves fold through LDS (one barrier) and the block writes
+//    one partial per row as whole rows (coalesced), or -- when one block covers
+//    every tile -- the outputs with their biases.
+#pragma once
+
+#include "lds_common.hpp"
+#include "mlp_body.hpp"
+
+namespace nectar {
+
+// GELU (erf form) evaluated without transcendentals in the decode kernels too:
+// the degree-7 polynomial of gelu_erf_poly (|GELU error| <= 5.3e-5 |x|).
+template <int ACT> __device__ __forceinline__ float act_dec(float x) {
+    return ACT == 1 ? silu(x) : (ACT == 2 ? gelu_tanh(x) : gelu_erf_poly(x));
+}
+
+template <int D, int RT, int ACT>
+__device__ __forceinline__ void dec_tgt_tile(const MTile<D> &T, int j0, int Ht, const u32x4 (&qv)[RT][D / 32],
+                                             int g, f32x4 (&O)[RT][D / 16]) {
+    constexpr int KS = D / 32, DV = D / 16;
+    u32x4 vt[DV];
+    transpose_w<D>(T, vt);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        f32x4 z0 = {T.bias[0], T.bias[1], T.bias[2], T.bias[3]};
+        f32x4 z1 = {T.bias[4], T.bias[5], T.bias[6], T.bias[7]};
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) {
+            z0 = mfma16(T.w1[0][kt], qv[rt][kt], z0);
+            z1 = mfma16(T.w1[1][kt], qv[rt][kt], z1);
+        }
+        float hv[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            hv[r] = act_dec<ACT>(z0[r]);
+            hv[4 + r] = act_dec<ACT>(z1[r]);
+        }
+        if (j0 + 32 > Ht) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j0 + hslot(g, j) >= Ht) hv[j] = 0.f;
+        }
+        const u32x4 H = {pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3]), pack_bf16(hv[4], hv[5]),
+                         pack_bf16(hv[6], hv[7])};
+#pragma unroll
+        for (int mm = 0; mm < DV; ++mm) O[rt][mm] = mfma16(vt[mm], H, O[rt][mm]);
+    }
+}
+
+template <int D, int RT, int ACT>
+__device__ __forceinline__ void dec_score_tile(const MTile<D> &T, int j0, int Hs, const u32x4 (&qv)[RT][D / 32],
+                                               int g, float (&sc)[RT]) {
+    constexpr int KS = D / 32;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        f32x4 z0 = {T.bias[0], T.bias[1], T.bias[2], T.bias[3]};
+        f32x4 z1 = {T.bias[4], T.bias[5], T.bias[6], T.bias[7]};
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) {
+            z0 = mfma16(T.w1[0][kt], qv[rt][kt], z0);
+            z1 = mfma16(T.w1[1][kt], qv[rt][kt], z1);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float y = act_dec<ACT>(j < 4 ? z0[j] : z1[j - 4]) * T.ws[j];
+            if (j0 + hslot(g, j) >= Hs) y = 0.f;
+            acc += y;
+        }
+        sc[rt] += acc;
+    }
+}
+
+// LDS of the block fold: per wave, its rows' read-outs [16 RT][D + 4] (rows
+// padded by four floats so the sixteen rows of one store land in different
+// banks) and score sums [16 RT].
+template <int D, int RT> struct DecFold {
+    static constexpr int ROWS = 16 * RT, LD = D + 4;
+    float O[4][ROWS * LD];
+    float s[4][ROWS];
+};
+
+// d = 128: a wave's weight rows are copied HBM -> LDS (global_load_lds, whole
+// 256-byte rows, four rows per copy) into its own region -- NT target tiles of
+// [W1 rows | W2t rows] or 2 NT score tiles of Ws rows, 16 KB per target tile --
+// with the sixteen 16-byte pieces of row r stored at piece ^ (r % 16), so the
+// operand reads of sixteen rows fall in distinct banks.  The fold reuses the
+// same LDS after a barrier.
+template <int D, int RT, int NT> union DecLds {
+    u32x4 tiles[4][NT * 2 * 32 * (D / 8)];
+    DecFold<D, RT> fold;
+};
+
+// Copy rows u0 .. u0 + 31 (clamped to umax) of W into LDS rows 0..31 at dst.
+__device__ __forceinline__ void stage_rows128(u32x4 *dst, const uint16_t *W, int u0, int umax, int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rr = 4 * i + (lane >> 4);
+        const int piece = (lane & 15) ^ (rr & 15);
+        const uint16_t *src = W + (size_t)min(u0 + rr, umax) * 128 + piece * 8;
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + 64 * i), 16, 0, 0);
+    }
+}
+
+// MFMA operands of one tile from its LDS rows (the layout of load_rows / load_tgt).
+__device__ __forceinline__ void lds_rows128(MTile<128> &T, const u32x4 *rows, int g, int c) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int r = 16 * hh + c;
+            T.w1[hh][kt] = rows[r * 16 + ((4 * kt + g) ^ (r & 15))];
+        }
+}
+__device__ __forceinline__ void lds_w2_128(MTile<128> &T, const u32x4 *rows, int g, int c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = hslot(g, j);
+        T.w2[j] = rows[r * 16 + (c ^ (r & 15))];
+    }
+}
+
+// Block blk_id of the grid Hkv x RG x SB (blocks of 4 waves).  Wave w of block
+// sb of (KV head h, row group rg) is wave i = 4 sb + w of that group: target
+// wave i < nwt, score wave i - nwt < nws, idle otherwise.
+template <int D, int RT, int ACT, int NT>
+__device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) {
+    constexpr int KS = D / 32, DV = D / 16;
+    __shared__ DecLds<D, RT, NT> lds;
+    DecFold<D, RT> &fold = lds.fold;
+
+    const int w = threadIdx.x >> 6;
+    int blk = blk_id;
+    const int sb = blk % a.SB;
+    blk /= a.SB;
+    const int rg = blk % a.RG;
+    const int h = blk / a.RG;
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    const int wi = 4 * sb + w;
+
+    f32x4 O[RT][DV];
+    float sc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        sc[rt] = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < DV; ++mm) O[rt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const bool tgt = wi < a.nwt, scw = !tgt && wi < a.nwt + a.nws;
+    if (tgt || scw) {
+        u32x4 qv[RT][KS];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int rho = (rg * RT + rt) * 16 + c;
+            if (rho < a.Rp) {
+                const int t = rho / a.G, gg = rho - t * a.G;
+                const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.Hq + h * a.G + gg) * D;
+#pragma unroll
+                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        if (tgt) {
+            const int Tt = (a.Ht + 31) / 32;
+            const int t0 = (int)((long)wi * Tt / a.nwt), n = (int)((long)(wi + 1) * Tt / a.nwt) - t0;
+            const uint16_t *W1 = (const uint16_t *)a.W1 + (size_t)h * a.Ht * D;
+            const uint16_t *W2t = (const uint16_t *)a.W2t + (size_t)h * a.Ht * D;
+            const float *b1 = a.b1 + (size_t)h * a.Ht;
+            if constexpr (D == 128) {
+                u32x4 *buf = lds.tiles[w];
+                float bias[NT][8];
+#pragma unroll
+                for (int k = 0; k < NT; ++k) {
+                    const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
+                    stage_rows128(buf + k * 1024, W1, u0, a.Ht - 1, lane);
+                    stage_rows128(buf + k * 1024 + 512, W2t, u0, a.Ht - 1, lane);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) bias[k][j] = b1[min(u0 + hslot(g, j), a.Ht - 1)];
+                }
+                wait_vmcnt<0>();
+                asm volatile("" ::: "memory");   // the copies landed: LDS reads stay below
+#pragma unroll
+                for (int k = 0; k < NT; ++k)
+                    if (k < n) {
+                        MTile<D> T;
+                        lds_rows128(T, buf + k * 1024, g, c);
+                        lds_w2_128(T, buf + k * 1024 + 512, g, c);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) T.bias[j] = bias[k][j];
+                        dec_tgt_tile<D, RT, ACT>(T, 32 * (t0 + k), a.Ht, qv, g, O);
+                    }
+            } else {
+                MTile<D> T[NT];
+#pragma unroll
+                for (int k = 0; k < NT; ++k)
+                    load_tgt<D>(T[k], W1, W2t, b1, 32 * (t0 + max(min(k, n - 1), 0)), a.Ht - 1, g, c);
+#pragma unroll
+                for (int k = 0; k < NT; ++k)
+                    if (k < n) dec_tgt_tile<D, RT, ACT>(T[k], 32 * (t0 + k), a.Ht, qv, g, O);
+            }
+        } else {
+            const int si = wi - a.nwt, Ts = (a.Hs + 31) / 32;
+            const int t0 = (int)((long)si * Ts / a.nws), n = (int)((long)(si + 1) * Ts / a.nws) - t0;
+            const uint16_t *Ws = (const uint16_t *)a.Ws + (size_t)h * a.Hs * D;
+            const uint16_t *ws2 = (const uint16_t *)a.ws2 + (size_t)h * a.Hs;
+            const float *bs = a.bs + (size_t)h * a.Hs;
+            if constexpr (D == 128) {
+                u32x4 *buf = lds.tiles[w];
+                float bias[2 * NT][8], wsv[2 * NT][8];
+#pragma unroll
+                for (int k = 0; k < 2 * NT; ++k) {
+                    const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
+                    stage_rows128(buf + k * 512, Ws, u0, a.Hs - 1, lane);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int u = min(u0 + hslot(g, j), a.Hs - 1);
+                        bias[k][j] = bs[u];
+                        wsv[k][j] = bf16_to_f32(ws2[u]);
+                    }
+                }
+                wait_vmcnt<0>();
+                asm volatile("" ::: "memory");   // the copies landed: LDS reads stay below
+#pragma unroll
+                for (int k = 0; k < 2 * NT; ++k)
+                    if (k < n) {
+                        MTile<D> T;
+                        lds_rows128(T, buf + k * 512, g, c);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            T.bias[j] = bias[k][j];
+                            T.ws[j] = wsv[k][j];
+                        }
+                        dec_score_tile<D, RT, ACT>(T, 32 * (t0 + k), a.Hs, qv, g, sc);
+                    }
+            } else {
+                MTile<D> T[2 * NT];
+#pragma unroll
+                for (int k = 0; k < 2 * NT; ++k)
+                    load_score<D>(T[k], Ws, ws2, bs, 32 * (t0 + max(min(k, n - 1), 0)), a.Hs - 1, g, c);
+#pragma unroll
+                for (int k = 0; k < 2 * NT; ++k)
+                    if (k < n) dec_score_tile<D, RT, ACT>(T[k], 32 * (t0 + k), a.Hs, qv, g, sc);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sc[rt] = group4_sum(sc[rt]);
+        }
+    }
+
+    // fold the four waves: every wave stores its rows (in the LDS the tiles
+    // used, once every wave is past them), one barrier, then the block's
+    // threads sum the four and write whole rows
+    constexpr int LD = DecFold<D, RT>::LD, ROWS = DecFold<D, RT>::ROWS;
+    if constexpr (D == 128) stage_barrier();
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        float *op = fold.O[w] + (rt * 16 + c) * LD;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int m4 = 0; m4 < DV; m4 += 4)
+                *(f32x4 *)(op + DV * (4 * g + r) + m4) = f32x4{O[rt][m4][r], O[rt][m4 + 1][r], O[rt][m4 + 2][r],
+                                                              O[rt][m4 + 3][r]};
+        if (g == 0) fold.s[w][rt * 16 + c] = sc[rt];
+    }
+    __syncthreads();
+    const bool direct = a.SB == 1 && !a.defer;
+    constexpr int CPR = D / 4;                // float4 columns per row
+    constexpr int RPI = 256 / CPR;            // rows per pass of the block
+    const int col = (threadIdx.x % CPR) * 4;
+#pragma unroll
+    for (int r0 = 0; r0 < ROWS; r0 += RPI) {
+        const int rr = r0 + (int)threadIdx.x / CPR;
+        const int rho = rg * ROWS + rr;
+        if (rr >= ROWS || rho >= a.Rp) continue;
+        f32x4 v = *(const f32x4 *)(fold.O[0] + rr * LD + col);
+#pragma unroll
+        for (int k = 1; k < 4; ++k) v += *(const f32x4 *)(fold.O[k] + rr * LD + col);
+        const bool lead = col == 0;
+        const float s = lead ? ((fold.s[0][rr] + fold.s[1][rr]) + (fold.s[2][rr] + fold.s[3][rr])) : 0.f;
+        if (direct) {
+            const int t = rho / a.G, gg = rho - t * a.G;
+            const size_t o = (size_t)t * a.Hq + h * a.G + gg;
+            *(f32x4 *)(a.A_out + o * D + col) = v + *(const f32x4 *)(a.b2 + (size_t)h * D + col);
+            if (lead) a.a_out[o] = a.bs2[h] + s;
+        } else {
+            const size_t row = (size_t)(h * a.SB + sb) * a.Rp + rho;
+            *(f32x4 *)(a.part_O + row * D + col) = v;
+            if (lead) a.part_s[row] = s;
+        }
+    }
+}
+
+}  // namespace nectar

@@ -35,7 +35,7 @@ namespace {
 #endif
 constexpr long kTargetWaves = NECTAR_TARGET_WAVES;
 #ifndef NECTAR_TARGET_WAVES_MLP
-#define NECTAR_TARGET_WAVES_MLP 1024
+#define NECTAR_TARGET_WAVES_MLP 512
 #endif
 constexpr long kTargetWavesMlp = NECTAR_TARGET_WAVES_MLP;
 // ... when the module's blocks share one launch with the exact document's (the
@@ -171,18 +171,22 @@ struct MlpPlan {
     int WR = 1, WS = 1, RB = 0, SB = 0;
     bool prefill = false;   // a batched kernel (LDS-staged weights)
     bool lds32 = false;     // ... the 32x32 one (unit counts multiples of 64)
+    bool dec = false;       // the decode kernel (target and score waves)
+    int Wt = 0, Ws = 0;     // ... its waves per (KV head, row group)
     size_t ws = 0;
 };
 
-// Rows per KV head from which the LDS-staged batched kernel is used (bf16,
-// d = 128): beyond one 16-row tile the register-direct kernel would stream the
-// weights once per row group.
-constexpr int kPrefillRows = 17;
+// Rows per KV head up to which the register-direct kernel serves the module
+// (bf16): one wave holds up to 64 rows (four 16-row tiles), so the weights
+// stream once; beyond, the LDS-staged batched kernels (d = 128) share each
+// weight tile between more rows.
+constexpr int kPrefillRows = 65;
 constexpr int kPrefillBlockRows = 256;
 // Blocks a split plan of the batched kernel aims for (one 512-thread block per CU).
 constexpr long kTargetBlocksPrefill = 256;
 
-MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs, long target_waves = kTargetWavesMlp) {
+MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs, long target_waves = kTargetWavesMlp,
+                 bool shared = false) {
     MlpPlan pl;
     pl.Rp = d->R * (d->Hq / d->Hkv);
     if (pl.Rp == 0) return pl;
@@ -223,6 +227,43 @@ MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs, long target_waves = 
         return pl;
     }
     const bool mfma = d->dtype == NECTAR_BF16;
+    if (mfma && !shared) {
+        // decode kernel: per (KV head, row group) Wt target waves and Ws score
+        // waves, sized so every wave reads about the same number of bytes (a
+        // target tile streams twice the bytes of a score tile) and holds at most
+        // kDecTiles target or 2 kDecTiles score tiles; target_waves is the wave
+        // budget of the launch
+        pl.dec = true;
+        pl.RT = mlp_row_tiles(pl.Rp);
+        pl.RG = pl.RB = (int)cdiv(pl.Rp, 16L * pl.RT);
+        pl.WR = 1;
+        pl.WS = 4;
+        const long per = (long)d->Hkv * pl.RG;
+        const long Wa = std::max(1L, d->splits > 0 ? (long)d->splits : cdiv(target_waves, per));
+        auto clampl = [](long x, long lo, long hi) { return std::min(std::max(x, lo), hi); };
+#ifndef NECTAR_DEC_SCORE_CAP
+#define NECTAR_DEC_SCORE_CAP 1
+#endif
+        const long smax = kDecTiles * (pl.RT > 1 ? NECTAR_DEC_SCORE_CAP : 2);   // score tiles per wave
+        long Wt = 0, Ws = 0;
+        if (tt > 0 && ts > 0) {
+            Wt = clampl(std::lround((double)Wa * 2.0 * tt / (2.0 * tt + ts)), cdiv(tt, kDecTiles), tt);
+            Ws = clampl(Wa - Wt, cdiv(ts, smax), ts);
+        } else if (tt > 0) {
+            Wt = clampl(Wa, cdiv(tt, kDecTiles), tt);
+        } else if (ts > 0) {
+            Ws = clampl(Wa, cdiv(ts, smax), ts);
+        }
+        pl.Wt = (int)Wt;
+        pl.Ws = (int)Ws;
+        pl.S = (int)(Wt + Ws);
+        pl.SB = (int)std::max(1L, cdiv(Wt + Ws, 4));
+        pl.ws = pl.SB > 1 ? (size_t)d->Hkv * pl.SB * pl.Rp * ((size_t)d->d * 4 + 4) : 0;
+        return pl;
+    }
+    // register-direct body one tile at a time (beside the document in the fused
+    // decode step; RT == 1 there) and the fp32 path: S splits of pt target and
+    // ps score tiles each
     long units;
     if (mfma) {
         pl.RT = row_tiles_for(pl.Rp);
@@ -518,12 +559,14 @@ static hipError_t run_mlp(const nectar_attn_desc *desc, const MlpPlan &pl, const
     a.Hq = desc->Hq; a.G = desc->Hq / desc->Hkv; a.Hkv = desc->Hkv; a.Rp = pl.Rp;
     a.Ht = m->Ht; a.Hs = m->Hs; a.act = m->act;
     a.S = pl.S; a.chunk_t = pl.ct; a.chunk_s = pl.cs; a.RG = pl.RG;
-    a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB;
+    a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB; a.nwt = pl.Wt; a.nws = pl.Ws;
     a.part_O = part_O; a.part_s = part_s;
     a.a_out = a_out; a.A_out = A_out;
     const bool in_place = pl.SB == 1 && (pl.prefill || desc->dtype == NECTAR_BF16);
-    hipError_t e = pl.lds32 ? launch_mlp_rows_lds32(a, st)
-                            : (pl.prefill ? launch_mlp_prefill(a, st) : launch_mlp_partial(a, desc->dtype, desc->d, pl.RT, st));
+    hipError_t e = pl.dec ? launch_mlp_decode(a, desc->d, pl.RT, st)
+                          : pl.lds32 ? launch_mlp_rows_lds32(a, st)
+                                     : (pl.prefill ? launch_mlp_prefill(a, st)
+                                                   : launch_mlp_partial(a, desc->dtype, desc->d, pl.RT, st));
     if (e == hipSuccess && !in_place) {
         MlpReduceParams r;
         r.part_O = part_O; r.part_s = part_s; r.b2 = m->b2; r.bs2 = m->bs2;
@@ -1001,11 +1044,13 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
         sp.kvpl = plan_attn(d, d->Hkv, Rp_doc, (long)m->p);
     }
     auto decode = [](const AttnPlan &pl) { return pl.S == 0 || (!pl.lds && pl.RT == 1); };
+    // (with the document in the same launch the module has at most 16 rows per
+    // KV head too, so both run one row tile)
     sp.fused = !sp.deep && (d->dtype == NECTAR_F32 ||
-               (decode(sp.loc) && (!exact || decode(sp.doc)) && (!sp.mlp || (!sp.mlpl.prefill && sp.mlpl.RT == 1)) &&
+               (decode(sp.loc) && (!exact || decode(sp.doc)) && (!sp.mlp || !sp.mlpl.prefill) &&
                 (!sp.kvp || decode(sp.kvpl))));
     if (sp.fused) {
-        if (sp.mlp && exact) sp.mlpl = plan_mlp(d, m->Ht, m->Hs, kTargetWavesMlpShared);
+        if (sp.mlp && exact) sp.mlpl = plan_mlp(d, m->Ht, m->Hs, kTargetWavesMlpShared, true);
         // with a module in the same launch the document leaves 48 of the 512
         // two-per-CU block slots free from the start, so the module's blocks run
         // beside the document's instead of after them (4B step, waves left free
@@ -1089,7 +1134,7 @@ static MlpParams mlp_partial_params(const nectar_attn_desc *d, const MlpPlan &pl
     a.Hq = d->Hq; a.G = d->Hq / d->Hkv; a.Hkv = d->Hkv; a.Rp = pl.Rp;
     a.Ht = m->Ht; a.Hs = m->Hs; a.act = m->act;
     a.S = pl.S; a.chunk_t = pl.ct; a.chunk_s = pl.cs; a.RG = pl.RG;
-    a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB;
+    a.WR = pl.WR; a.WS = pl.WS; a.RB = pl.RB; a.SB = pl.SB; a.nwt = pl.Wt; a.nws = pl.Ws;
     a.defer = 1;
     a.part_O = (float *)part;
     a.part_s = (float *)((char *)part + (size_t)d->Hkv * pl.SB * pl.Rp * d->d * 4);
@@ -1274,12 +1319,12 @@ static hipError_t run_layer_step(const nectar_attn_desc *desc, const StepPlan &s
     MlpParams mp{};
     if (sp.mlp) mp = mlp_partial_params(desc, sp.mlpl, module, q, w + sp.off_mod);
     // decode shapes: the attention blocks and the module's blocks in one launch
-    const bool mlp_dec = sp.mlp && !sp.mlpl.prefill && desc->dtype == NECTAR_BF16 && sp.mlpl.RT == 1;
-    if (mlp_dec && sp.exact && pairable(desc, sp.doc, sp.loc) && sp.doc.RT == 1) {
-        e = launch_step_partials(ap_doc, &ap_loc, mp, desc->d, st);
+    const bool mlp_dec = sp.mlp && !sp.mlpl.prefill && desc->dtype == NECTAR_BF16;
+    if (mlp_dec && sp.mlpl.RT == 1 && sp.exact && pairable(desc, sp.doc, sp.loc) && sp.doc.RT == 1) {
+        e = launch_step_partials(ap_doc, &ap_loc, mp, desc->d, 1, st);
         loc_done = mod_done = true;
     } else if (mlp_dec && !sp.exact && sp.loc.S > 0 && !sp.loc.lds && sp.loc.RT == 1) {
-        e = launch_step_partials(ap_loc, nullptr, mp, desc->d, st);
+        e = launch_step_partials(ap_loc, nullptr, mp, desc->d, sp.mlpl.RT, st);
         loc_done = mod_done = true;
     }
     if (sp.exact) {
@@ -1303,9 +1348,11 @@ static hipError_t run_layer_step(const nectar_attn_desc *desc, const StepPlan &s
         x.lse_out = outs->a_out; x.A_out = outs->Am_out; x.out = outs->out_nectar; x.out_lse = outs->lse_nectar;
         if (sp.mlp) {
             if (!mod_done)
-                e = sp.mlpl.lds32 ? launch_mlp_rows_lds32(mp, st)
-                                  : (sp.mlpl.prefill ? launch_mlp_prefill(mp, st)
-                                                     : launch_mlp_partial(mp, desc->dtype, desc->d, sp.mlpl.RT, st));
+                e = sp.mlpl.dec ? launch_mlp_decode(mp, desc->d, sp.mlpl.RT, st)
+                                : sp.mlpl.lds32 ? launch_mlp_rows_lds32(mp, st)
+                                                : (sp.mlpl.prefill ? launch_mlp_prefill(mp, st)
+                                                                   : launch_mlp_partial(mp, desc->dtype, desc->d,
+                                                                                        sp.mlpl.RT, st));
             x.S = sp.mlpl.SB;
             x.s = (const float *)(w + sp.off_mod + (size_t)desc->Hkv * sp.mlpl.SB * sp.mlpl.Rp * desc->d * 4);
             x.b2 = module->b2; x.bs2 = module->bs2;

@@ -212,7 +212,7 @@ def test_mlp_many_rows(nx, d, R, Ht, Hs, splits):
 @pytest.mark.parametrize("R,Hq,Hkv,Ht,Hs", [(5, 14, 2, 100, 70), (1, 32, 8, 256, 96), (20, 8, 2, 64, 33),
                                              (3, 4, 1, 0, 40), (3, 4, 1, 50, 0), (10, 16, 4, 300, 200),
                                              (64, 32, 8, 600, 300), (10, 16, 4, 256, 128), (64, 32, 8, 640, 320),
-                                             (20, 8, 2, 0, 64)])
+                                             (20, 8, 2, 0, 64), (16, 16, 4, 1000, 500), (11, 12, 4, 96, 40)])
 @pytest.mark.parametrize("act", ["gelu", "silu", "gelu_tanh"])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_mlp_bf16(nx, R, Hq, Hkv, Ht, Hs, act, splits):
@@ -386,6 +386,10 @@ STEP_CASES = {
     "empty_doc_and_local": ("bf16", 128, 2, 1, 0, 8, 0, 8, 2, 0, ("mlp", 0, 40)),
     "exact_only": ("bf16", 128, 4, 1, 50, 64, 49, 16, 4, 1000, None),
     "module_only": ("bf16", 128, 4, 2, 30, 32, 28, 16, 4, None, ("mlp", 64, 32)),
+    # 56 document rows per KV head (the 1M-token decode's shape): the Nectar path fuses
+    # the 64-row module blocks with the local blocks; with the exact part the plan is composed
+    "nectar_rows56": ("bf16", 128, 8, 1, 300, 320, 299, 28, 4, None, ("mlp", 704, 450)),
+    "both_rows56": ("bf16", 128, 8, 1, 300, 320, 299, 28, 4, 3000, ("mlp", 704, 450)),
 }
 
 
@@ -396,7 +400,8 @@ def test_layer_step(nx, name):
     _check_layer_step(nx, name, 0)
 
 
-@pytest.mark.parametrize("name,splits", [("decode_bf16", 100), ("batch64_bf16", 70), ("decode_bf16_d64", 90)])
+@pytest.mark.parametrize("name,splits", [("decode_bf16", 100), ("batch64_bf16", 70), ("decode_bf16_d64", 90),
+                                         ("nectar_rows56", 80)])
 def test_layer_step_many_splits(nx, name, splits):
     """More than 64 key splits per part: the finishing pass and the split-K
     combine fold the splits past the 64 they load up front in a serial tail."""

@@ -1,39 +1,45 @@
 #!/usr/bin/env python3
 """Benchmark of the Nectar attention hot path on one MI355X.
 
-Workload: the Qwen3-4B-shaped decode layer (8 KV heads, 32 query heads, d=128,
-bf16; document n = 61,440 keys; local cache 512 prompt tokens + the decode
-token; Nectar MLP 128->4608->128 target and 128->2944->1 score per KV head,
-GELU).  A step is one decode step of one layer through the whole hot path:
+Headline workload: the Qwen2.5-7B-1M-shaped 28-layer stack with a 1M-token
+document (4 KV heads, 28 query heads, d = 128, bf16; n = 1,048,576 document
+keys per layer and KV head, 60 GB of document cache resident in HBM; 8
+questions decoding one token each, 256 prompt tokens then 128 decode steps).
+A step is one decode step of the whole stack, every layer in turn, through the
+three forms of the document part:
 
-  exact document attention (alpha, A) over the 61,440-key cache,
-  the MLP module forward (a, A_theta),
-  causal local attention over the 513 local keys (lambda, A_local),
-  and both merges: the module pair with the local pair (the Nectar output) and
-  the exact pair with the local pair (the exact output),
+  Nectar (the headline `value`): per layer the MLP module forward (target
+      128->5120->128, score 128->3072->1, GELU) and causal local attention over
+      the question's own tokens, merged by log-sum-exp (Eqs. (3.4)-(3.5));
+  Quadrature: the same with the learnable-KV-pair module (p = 10,486 pairs);
+  exact: exact attention over all 1,048,576 document keys, merged likewise.
 
-through the fused layer-step entry point (the document, local and module
-partials in one launch, then one finishing launch that writes every pair and
-both outputs).  The same step through the four separate entry points is timed
-too (`paths.step_unfused_us`).
+Each path of each decode step is one HIP graph of its 28 layer steps (the
+layers' caches, modules and queries are their own), replayed on the current
+stream; HIP events between the paths of every step give the per-step times.
+`--warmup` steps run untimed, then exactly `--steps` steps are timed; decode
+step s of the stack sees 257 + s local keys (s = step index modulo 128).
+`value` = query tokens per second per layer of the Nectar path (8 tokens x 28
+layers per step over the Nectar share of the step time); `paths` gives all
+three; `timing` the per-step median and 10th/90th percentiles and the device
+clocks read while steps run.  Inputs are resident in HBM before timing (the
+boundary takes device buffers, so there is no host-transfer rate to report).
+The stack's tensors are N(0, 1) draws from a seeded device generator (modules
+N(0, 1/fan_in)): a rotation leaves an N(0, 1) key N(0, 1), so RoPE'd keys and
+these draws have the same distribution.
 
-Every step reads a distinct layer replica (its own document cache, module and
-local cache), so consecutive steps never hit a cache the previous step
-warmed; the replicas together exceed the 256 MB Infinity Cache many times.
-Inputs are resident in HBM before timing.  The launches of one pass over all
-replicas (one step per replica, like a decode step through a stack of that
-many layers) are captured once in a HIP graph and replayed; timing uses HIP
-events on the replay stream around K steps (K rounded up to whole passes),
-bracketed by synchronizations.
-
-Prints one JSON line.  `value` is query-tokens/s/layer of the whole step (mean
-over the timed steps); `timing` gives the median and 10th/90th percentiles of
-the per-pass step times and the device clocks read while the step runs;
-`paths` gives the Nectar and exact paths timed alone, `components` the module,
-local attention and merge alone against their HBM rooflines; `roofline` covers
-the dominant kernel (exact document attention, HBM-bound); `cpu_baseline` times
-the fp64 CPU oracle on a bounded sample of the same step, multithreaded and on
-one thread, with the host's CPU model.
+`roofline` covers the exact path's dominant kernel, the split-K partial pass
+of the document attention over a layer's 1,048,576 keys (one launch per layer:
+Hkv x n x 2 x d x 2 = 2,147,483,648 algorithmic bytes), timed alone over the
+28 layers' caches with HIP events; `traffic` comes from the counter summary in
+profiles/ while the kernel's sources are unchanged.  `cpu_baseline` times the
+fp64 CPU oracle on the host cores: the Nectar path on one decode step of one
+layer, and slices of every workload and form (exact, MLP, Quadrature, local
+attention, merge).  `pages_context` quotes the only timing figures the pages
+give (end-to-end generation, hardware not stated).  Extras: the
+Qwen3-4B-shaped decode layer (fused step, each path, components, its own
+document-pass roofline), per-layer timings of the batch-64 decode and prefill
+workloads, the batched-prefill MLP against the MFMA peak, and the NEXT kernels.
 """
 import argparse
 import hashlib
@@ -46,33 +52,62 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-SOURCES_FOR_TRAFFIC = ["learned_kv_cache_02_amd/csrc/" + f for f in
-                       ("attn.hip", "attn_body.hpp", "attn_common.hpp", "device_common.hpp", "kernels.hpp")]
+# sources of the document-attention partial pass (the traffic figures are valid
+# while these hash to the value stored with them)
+ATTN_SOURCES = ["learned_kv_cache_02_amd/csrc/" + f for f in
+                ("attn.hip", "attn_body.hpp", "attn_common.hpp", "attn_lds.hip", "lds_common.hpp",
+                 "device_common.hpp", "kernels.hpp")]
+CALIB_BYTES = 1 << 30   # runtime copies of this many bytes (the largest of a profiling run) calibrate the counters
+
+# The pages' own timing figures (Nectar notes, section 4.8, App. D, Table 12):
+# end-to-end generation, base model with the full document in context versus
+# Nectar; the hardware is not stated.  Context only.
+PAGES_TABLE12 = {
+    "source": "Nectar notes, section 4.8 / App. D, Table 12 (end-to-end generation; hardware not stated)",
+    "rows": [
+        {"model": "Qwen3-1.7B", "doc_tokens": 40022, "ttft_base": "183,000 (unit garbled; ms)",
+         "ttft_nectar_ms": 26.4, "decode_tok_s": [9.5, 44.2], "peak_mem_gb": [24.9, 7.7]},
+        {"model": "Qwen3-1.7B", "doc_tokens": 122466, "ttft_base": "299,900 (unit garbled; ms)",
+         "ttft_nectar_ms": 29.3, "decode_tok_s": [4.4, 37.7], "peak_mem_gb": [60.4, 8.2]},
+        {"model": "Qwen3-4B", "doc_tokens": 40022, "ttft_base": "347,900 (unit garbled; ms)",
+         "ttft_nectar_ms": 44.6, "decode_tok_s": [6.3, 18.4], "peak_mem_gb": [38.6, 16.7]},
+        {"model": "Qwen3-4B", "doc_tokens": 122466, "ttft_base": "557,600 (unit garbled; ms)",
+         "ttft_nectar_ms": 50.1, "decode_tok_s": [1.5, 15.7], "peak_mem_gb": [84.2, 17.1]},
+    ],
+    "hardware": "not stated",
+}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=240)
-    ap.add_argument("--warmup", type=int, default=24)
-    ap.add_argument("--replicas", type=int, default=24)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0: skip)")
-    ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--only", choices=["step", "exact", "nectar", "doc", "doc_partial"], default=None,
-                    help="time only one graph (for profiling runs)")
-    ap.add_argument("--no-workloads", action="store_true",
-                    help="skip the per-layer timings of the three larger workloads")
-    ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the batched-prefill MLP measurement")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="CPU oracle budget of the headline sample (0: skip every CPU leg)")
+    ap.add_argument("--only", default=None,
+                    choices=["stack", "c5_doc_partial", "c4_doc_partial", "c3_mlp10", "c2_doc_partial"],
+                    help="time one leg only (profiling runs): the stack, or one kernel's launches")
+    ap.add_argument("--no-extras", action="store_true", help="skip the extra workloads and kernels")
     return ap.parse_args()
 
 
 def source_hash():
     h = hashlib.sha256()
-    for f in SOURCES_FOR_TRAFFIC:
+    for f in ATTN_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM bytes per launch of a profiled kernel, if its sources are unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        tj = json.load(fh)
+    return tj.get("hbm_bytes_per_launch") if tj.get("source_hash") == source_hash() else None
 
 
 def main():
@@ -87,52 +122,270 @@ def main():
 
     from learned_kv_cache_02_amd import configs, nectar, synth
 
-    cfg = configs.C2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    NREP = args.replicas
+    if args.only in ("c4_doc_partial", "c3_mlp10", "c2_doc_partial"):
+        print(json.dumps(profile_leg(torch, np, nectar, configs, synth, dev, args)), flush=True)
+        return
+
+    res = {
+        "metric": "query-tokens/s/layer, Nectar vs exact cache attn; % of HBM / MFMA roofline",
+        "unit": "query-tokens/s/layer",
+        "higher_is_better": True,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    st = stack_c5(torch, nectar, configs, dev, args)
+    res.update(st.pop("line"))
+    res.update(st)
+    if args.only:
+        print(json.dumps(res), flush=True)
+        return
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        res["c2_layer"] = c2_layer(torch, np, nectar, configs, synth, dev)
+        torch.cuda.empty_cache()
+        res["prefill_mlp"] = prefill_mlp(torch, np, nectar, configs, synth, dev)
+        res["merge_k"] = merge_k_prefill(torch, nectar, configs, dev)
+        res["fit_metrics"] = fit_metrics_prefill(torch, nectar, configs, dev)
+        res["deep_modules"] = deep_modules(torch, nectar, configs, dev)
+        res["train_step"] = train_step_bench(torch, nectar, configs, dev)
+        res["workloads"] = {c.name: workload_layer(torch, nectar, c, dev) for c in (configs.C4, configs.C3)}
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(np, configs, synth, args.cpu_seconds)
+    res["pages_context"] = PAGES_TABLE12
+    print(json.dumps(res), flush=True)
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _pct(xs, f):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]
+
+
+def stack_c5(torch, nectar, configs, dev, args):
+    """The 28-layer 1M-token decode stack: every layer's document cache (60 GB),
+    MLP and Quadrature modules, local caches and per-step queries on the device;
+    per-step graphs of the three paths; the timed steps; the roofline kernel."""
+    cfg = configs.C5
+    L, Hkv, Hq, d, n, B, R = cfg.layers, cfg.Hkv, cfg.Hq, cfg.d, cfg.n, cfg.B, cfg.R
+    m = cfg.mlps[0]
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(2000 + cfg.seed)
+    only = args.only
+
+    def rn(*shape, std=1.0):
+        # N(0, std^2) in bf16, drawn in chunks of 2^27 elements (bounded fp32 scratch)
+        out = torch.empty(shape, dtype=bf, device=dev)
+        flat = out.view(-1)
+        for lo in range(0, flat.numel(), 1 << 27):
+            hi = min(flat.numel(), lo + (1 << 27))
+            flat[lo:hi] = (torch.randn(hi - lo, generator=g, device=dev) * std).to(bf)
+        return out
+
+    t0 = time.time()
+    K = [rn(Hkv, n, d) for _ in range(L)]
+    V = [rn(Hkv, n, d) for _ in range(L)]
+    steps_total = args.warmup + args.steps
+    z = lambda *s: torch.zeros(*s, device=dev)
+    layers = []
+    if only != "c5_doc_partial":
+        for l in range(L):
+            layers.append(dict(
+                q=[rn(R, Hq, d) for _ in range(steps_total)],
+                Kl=rn(B, Hkv, cfg.T_cap, d), Vl=rn(B, Hkv, cfg.T_cap, d),
+                mlp=nectar.MLPModule(rn(Hkv, m.Ht, d, std=d ** -0.5), z(Hkv, m.Ht), rn(Hkv, m.Ht, d, std=m.Ht ** -0.5),
+                                     z(Hkv, d), rn(Hkv, m.Hs, d, std=d ** -0.5), z(Hkv, m.Hs),
+                                     rn(Hkv, m.Hs, std=m.Hs ** -0.5), z(Hkv)),
+                kvp=nectar.KVPairModule(rn(Hkv, cfg.kv_pairs, d), rn(Hkv, cfg.kv_pairs, d))))
+    torch.cuda.synchronize()
+    print("stack: %d layers generated in %.1f s" % (L, time.time() - t0), file=sys.stderr, flush=True)
+    doc_bytes = Hkv * n * 2 * d * 2
+    line = {}
+    extra = {}
+
+    # --- the roofline kernel: the document partial pass of every layer (one launch each)
+    dsc = nectar.desc(R, Hq, Hkv, d, nectar.BF16)
+    part = torch.empty(max(16, nectar.doc_attn_partials_size(dsc, n)), dtype=torch.uint8, device=dev)
+    q0 = rn(R, Hq, d)
+
+    def doc_partials():
+        for l in range(L):
+            nectar.doc_attn_partials(q0, K[l], V[l], Hkv, partials=part)
+    if only == "c5_doc_partial":
+        # runtime copies of a known size in the same run calibrate the traffic counters
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        for _ in range(4):
+            src.clone()
+    doc_partials()
+    torch.cuda.synchronize()
+    gdoc = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gdoc):
+        doc_partials()
+    reps = max(1, args.steps // 4) if only == "c5_doc_partial" else 3
+    gdoc.replay()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for _ in range(reps):
+        gdoc.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us_doc = e0.elapsed_time(e1) / (reps * L) * 1e3
+    ach = doc_bytes / (us_doc * 1e-6) / 1e9
+    extra["roofline"] = {
+        "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+        "traffic": load_traffic("doc_attn_c5"),
+        "kernel": "split-K partial pass of the exact document attention over one layer's 1,048,576 keys "
+                  "(nectar_doc_attn_partials: attn_rows_lds, one launch per layer), %.2f us per launch "
+                  "(%d launches over the 28 layers' caches), %d algorithmic bytes per launch"
+                  % (us_doc, reps * L, doc_bytes)}
+    del gdoc
+    if only == "c5_doc_partial":
+        line["config"] = {"workload": "c5_qwen25_7b_1m_decode: document partial pass alone, 28 layer caches"}
+        return dict(extra, line=line)
+
+    # --- per-step graphs of the three paths through the stack
+    f32 = dict(dtype=torch.float32, device=dev)
+    outs = {"nectar": {"out_nectar": torch.empty(R, Hq, d, dtype=bf, device=dev), "lse_nectar": torch.empty(R, Hq, **f32)},
+            "kvpair": {"out_nectar": torch.empty(R, Hq, d, dtype=bf, device=dev), "lse_nectar": torch.empty(R, Hq, **f32)},
+            "exact": {"out_exact": torch.empty(R, Hq, d, dtype=bf, device=dev), "lse_exact": torch.empty(R, Hq, **f32)}}
+
+    def path(name, s):
+        ds = s % cfg.decode_steps
+        kw = dict(B=B, Tq=1, T_loc=cfg.local_len(ds), q_offset=cfg.q_offset(ds), out=outs[name])
+        for l, ly in enumerate(layers):
+            if name == "exact":
+                nectar.layer_step(ly["q"][s], ly["Kl"], ly["Vl"], Hkv, k=K[l], v=V[l], module=None, exact=True, **kw)
+            else:
+                nectar.layer_step(ly["q"][s], ly["Kl"], ly["Vl"], Hkv, module=ly["mlp" if name == "nectar" else "kvp"],
+                                  exact=False, **kw)
+
+    names = ["nectar", "kvpair", "exact"]
+    for nm in names:                 # eager once: the binding's workspace outside any capture
+        path(nm, steps_total - 1)
+    torch.cuda.synchronize()
+    graphs = {nm: [] for nm in names}
+    for s in range(steps_total):
+        for nm in names:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                path(nm, s)
+            graphs[nm].append(gr)
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        for nm in names:
+            graphs[nm][s].replay()
+    torch.cuda.synchronize()
+    ev = _events(torch, 1 + 3 * args.steps)
+    ev[0].record()
+    for i in range(args.steps):
+        s = args.warmup + i
+        for j, nm in enumerate(names):
+            graphs[nm][s].replay()
+            ev[1 + 3 * i + j].record()
+    torch.cuda.synchronize()
+    per = {nm: [] for nm in names}
+    for i in range(args.steps):
+        for j, nm in enumerate(names):
+            per[nm].append(ev[3 * i + j].elapsed_time(ev[1 + 3 * i + j]))     # ms
+    total_ms = ev[0].elapsed_time(ev[3 * args.steps])
+    # the clocks while steps run: about a second of Nectar steps enqueued, then read
+    for _ in range(max(1, int(1.0 / max(1e-6, sum(per["nectar"]) / len(per["nectar"]) * 1e-3)))):
+        graphs["nectar"][args.warmup].replay()
+    clocks = gpu_clocks()
+    torch.cuda.synchronize()
+    for nm in ("out_nectar", "out_exact"):
+        for o in outs.values():
+            if nm in o and not torch.isfinite(o[nm].float()).all():
+                raise RuntimeError("non-finite output in %s" % nm)
+    tokens = R * L                    # query tokens per step through the stack
+    mean = lambda xs: sum(xs) / len(xs)
+    paths = {}
+    for nm in names:
+        ms = mean(per[nm])
+        paths[nm] = {"qtok_s_layer": tokens / (ms * 1e-3), "ms_per_step": ms, "us_per_layer": ms * 1e3 / L,
+                     "ms_per_step_median": _pct(per[nm], 0.5), "p10": _pct(per[nm], 0.1), "p90": _pct(per[nm], 0.9)}
+    paths["nectar"]["form"] = "MLP 5120/3072 GELU (rho = %.4f)" % cfg.rho(m.params(d))
+    paths["kvpair"]["form"] = "Quadrature, p = %d pairs (rho = %.4f)" % (cfg.kv_pairs, cfg.rho(2 * cfg.kv_pairs * d))
+    paths["exact"]["form"] = "exact attention over 1,048,576 document keys"
+    paths["nectar_speedup_vs_exact"] = paths["exact"]["ms_per_step"] / paths["nectar"]["ms_per_step"]
+    paths["kvpair_speedup_vs_exact"] = paths["exact"]["ms_per_step"] / paths["kvpair"]["ms_per_step"]
+    line["value"] = paths["nectar"]["qtok_s_layer"]
+    line["ms_per_step"] = total_ms / args.steps
+    line["config"] = {"workload": "c5_qwen25_7b_1m_decode: Qwen2.5-7B-1M-shaped 28-layer stack, bf16, Hkv=4 Hq=28 "
+                                  "d=128, 1,048,576 document keys per layer (60 GB resident), decode batch 8, "
+                                  "257..384 local keys; one step = one decode step of all 28 layers through the "
+                                  "Nectar (MLP 5120/3072), Quadrature (p=10,486) and exact paths; value = Nectar path",
+                      "global_batch": B, "seq_len": n + cfg.T_cap, "layers": L, "parallelism": "single-gpu",
+                      "graph": "one HIP graph per path and decode step"}
+    extra["paths"] = paths
+    extra["timing"] = {"ms_per_step": "all three paths (Nectar, Quadrature, exact) of one decode step of the stack",
+                       "nectar_ms_per_step_median": paths["nectar"]["ms_per_step_median"],
+                       "nectar_p10": paths["nectar"]["p10"], "nectar_p90": paths["nectar"]["p90"],
+                       "timed_steps": args.steps, "warmup_steps": args.warmup,
+                       "decode_steps": [args.warmup % cfg.decode_steps,
+                                        (args.warmup + args.steps - 1) % cfg.decode_steps],
+                       "clocks": clocks}
+    del graphs
+    return dict(extra, line=line)
+
+
+def c2_layer(torch, np, nectar, configs, synth, dev, nrep=24, passes=10):
+    """The Qwen3-4B-shaped decode layer (n = 61,440, 513 local keys, MLP 4608/2944):
+    24 layer replicas (each its own 252 MB cache, module and local cache) rotate
+    so no call reads what the previous one warmed; each measurement is one graph
+    of one call per replica, replayed `passes` times.  The fused step of both
+    paths, each path alone, the same step through the separate entry points, the
+    components alone, and the document partial pass with its HBM roofline."""
+    cfg = configs.C2
+    Hkv, Hq, d, R = cfg.Hkv, cfg.Hq, cfg.d, cfg.R
+    T, qoff = cfg.local_len(0), cfg.q_offset(0)
 
     def up(x):
         t = torch.from_numpy(np.ascontiguousarray(x))
         return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
 
-    t0 = time.time()
-    q_h = synth.queries(cfg)
-    K_h, V_h = synth.doc_kv(cfg)
-    Kl_h, Vl_h = synth.local_kv(cfg)
-    P_h = synth.mlp_params(cfg)
-    gen_s = time.time() - t0
-    print("generated inputs in %.1fs" % gen_s, file=sys.stderr, flush=True)
-
-    q0, K0, V0, Kl0, Vl0 = up(q_h), up(K_h), up(V_h), up(Kl_h), up(Vl_h)
-    mod0 = [up(P_h[k]) for k in ("W1", "b1", "W2t", "b2", "Ws", "bs", "ws2", "bs2")]
-    reps = []
-    for r in range(NREP):
-        reps.append(dict(q=q0.clone(), K=K0.clone(), V=V0.clone(), Kl=Kl0.clone(), Vl=Vl0.clone(),
-                         mod=nectar.MLPModule(*(t.clone() for t in mod0))))
+    q0, K0, V0 = up(synth.queries(cfg)), *(up(x) for x in synth.doc_kv(cfg))
+    Kl0, Vl0 = (up(x) for x in synth.local_kv(cfg))
+    P = synth.mlp_params(cfg)
+    mod0 = [up(P[k]) for k in ("W1", "b1", "W2t", "b2", "Ws", "bs", "ws2", "bs2")]
+    reps = [dict(q=q0.clone(), K=K0.clone(), V=V0.clone(), Kl=Kl0.clone(), Vl=Vl0.clone(),
+                 mod=nectar.MLPModule(*(t.clone() for t in mod0))) for _ in range(nrep)]
     del K0, V0
-    torch.cuda.synchronize()
-
-    Hkv, Hq, d, R = cfg.Hkv, cfg.Hq, cfg.d, cfg.R
-    T, qoff = cfg.local_len(0), cfg.q_offset(0)
     f32 = dict(dtype=torch.float32, device=dev)
     o = dict(alpha=torch.empty((R, Hq), **f32), Ax=torch.empty((R, Hq, d), **f32),
              a=torch.empty((R, Hq), **f32), Am=torch.empty((R, Hq, d), **f32),
              lam=torch.empty((R, Hq), **f32), Al=torch.empty((R, Hq, d), **f32),
              out_n=torch.empty((R, Hq, d), dtype=torch.bfloat16, device=dev), lse_n=torch.empty((R, Hq), **f32),
              out_x=torch.empty((R, Hq, d), dtype=torch.bfloat16, device=dev), lse_x=torch.empty((R, Hq), **f32))
+    part_buf = torch.empty(max(16, nectar.doc_attn_partials_size(nectar.desc(R, Hq, Hkv, d, nectar.BF16), cfg.n)),
+                           dtype=torch.uint8, device=dev)
+    pair_out = {"out_exact": o["out_x"], "lse_exact": o["lse_x"], "alpha": o["alpha"], "A": o["Ax"],
+                "out_nectar": o["out_n"], "lse_nectar": o["lse_n"], "a": o["a"], "Am": o["Am"],
+                "lam": o["lam"], "Aloc": o["Al"]}
+    lkw = dict(B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff)
+
+    def fused(r, exact=True, nect=True):
+        x = reps[r]
+        keys = (["out_exact", "lse_exact", "alpha", "A"] if exact else []) + \
+               (["out_nectar", "lse_nectar", "a", "Am"] if nect else []) + ["lam", "Aloc"]
+        nectar.layer_step(x["q"], x["Kl"], x["Vl"], Hkv, k=x["K"] if exact else None, v=x["V"] if exact else None,
+                          module=x["mod"] if nect else None, exact=exact, pairs=True,
+                          out={k: pair_out[k] for k in keys}, **lkw)
 
     def doc(r):
         x = reps[r]
         nectar.doc_attn_exact(x["q"], x["K"], x["V"], Hkv, alpha_out=o["alpha"], A_out=o["Ax"])
-
-    part_dsc = nectar.desc(R, Hq, Hkv, d, nectar.BF16)
-    part_buf = torch.empty(max(16, nectar.doc_attn_partials_size(part_dsc, cfg.n)), dtype=torch.uint8, device=dev)
-
-    def doc_partial(r):
-        # the split-K partial pass alone: the dominant kernel of the step
-        x = reps[r]
-        nectar.doc_attn_partials(x["q"], x["K"], x["V"], Hkv, partials=part_buf)
 
     def module(r):
         x = reps[r]
@@ -140,197 +393,228 @@ def main():
 
     def local_nectar(r):
         x = reps[r]
-        nectar.local_attn_lse(x["q"], x["Kl"], x["Vl"], Hkv, B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff,
-                              lse_out=o["lam"], A_out=o["Al"], doc_lse=o["a"], doc_A=o["Am"],
-                              out=o["out_n"], out_lse=o["lse_n"])
+        nectar.local_attn_lse(x["q"], x["Kl"], x["Vl"], Hkv, lse_out=o["lam"], A_out=o["Al"], doc_lse=o["a"],
+                              doc_A=o["Am"], out=o["out_n"], out_lse=o["lse_n"], **lkw)
 
     def local_pair(r):
         x = reps[r]
-        nectar.local_attn_lse(x["q"], x["Kl"], x["Vl"], Hkv, B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff,
-                              lse_out=o["lam"], A_out=o["Al"])
+        nectar.local_attn_lse(x["q"], x["Kl"], x["Vl"], Hkv, lse_out=o["lam"], A_out=o["Al"], **lkw)
 
     def merge_exact(r):
         nectar.merge(o["alpha"], o["Ax"], o["lam"], o["Al"], Hkv=Hkv, out_dtype=torch.bfloat16,
                      out=o["out_x"], lse_out=o["lse_x"])
 
-    pair_out = {"out_exact": o["out_x"], "lse_exact": o["lse_x"], "alpha": o["alpha"], "A": o["Ax"],
-                "out_nectar": o["out_n"], "lse_nectar": o["lse_n"], "a": o["a"], "Am": o["Am"],
-                "lam": o["lam"], "Aloc": o["Al"]}
-
-    def fused(r, exact=True, nect=True):
+    def doc_partial(r):
         x = reps[r]
-        keys = (["out_exact", "lse_exact", "alpha", "A"] if exact else []) + \
-               (["out_nectar", "lse_nectar", "a", "Am"] if nect else []) + ["lam", "Aloc"]
-        nectar.layer_step(x["q"], x["Kl"], x["Vl"], Hkv, B=cfg.B, Tq=cfg.Tq, T_loc=T, q_offset=qoff,
-                          k=x["K"] if exact else None, v=x["V"] if exact else None,
-                          module=x["mod"] if nect else None, exact=exact, pairs=True,
-                          out={k: pair_out[k] for k in keys})
+        nectar.doc_attn_partials(x["q"], x["K"], x["V"], Hkv, partials=part_buf)
 
-    steps = {
-        # the whole step of both paths through the fused layer-step entry point
-        "step": lambda r: fused(r),
-        "nectar": lambda r: fused(r, exact=False),
-        "exact": lambda r: fused(r, nect=False),
-        "doc": lambda r: doc(r),
-        "doc_partial": lambda r: doc_partial(r),
-        # the same step through the four separate entry points (seven launches)
-        "step_unfused": lambda r: (doc(r), module(r), local_nectar(r), merge_exact(r)),
-        # the components alone
-        "module": lambda r: module(r),
-        "local": lambda r: local_pair(r),
-        "merge": lambda r: merge_exact(r),
-    }
-    names = [args.only] if args.only else ["step", "nectar", "exact", "doc", "doc_partial", "step_unfused",
-                                           "module", "local", "merge"]
-
-    # warm every call once (allocates the binding's cached workspace outside capture)
-    for fn in steps.values():
+    calls = {"step": fused, "nectar": lambda r: fused(r, exact=False), "exact": lambda r: fused(r, nect=False),
+             "step_unfused": lambda r: (doc(r), module(r), local_nectar(r), merge_exact(r)),
+             "module": module, "local": local_pair, "merge": merge_exact, "doc": doc, "doc_partial": doc_partial}
+    for fn in calls.values():
         fn(0)
     torch.cuda.synchronize()
-
-    graphs = {}
-    if not args.no_graph:
-        for nm in names:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for r in range(NREP):
-                    steps[nm](r)
-            graphs[nm] = g
+    us = {}
+    for nm, fn in calls.items():
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for r in range(nrep):
+                fn(r)
+        gr.replay()
         torch.cuda.synchronize()
-
-    passes = max(1, -(-args.steps // NREP))
-    wpasses = max(1, -(-args.warmup // NREP))
-    n_steps, n_warm = passes * NREP, wpasses * NREP
-
-    def one_pass(nm):
-        if args.no_graph:
-            for r in range(NREP):
-                steps[nm](r)
-        else:
-            graphs[nm].replay()
-
-    def timed(nm):
-        for _ in range(wpasses):
-            one_pass(nm)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(passes):
-            one_pass(nm)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n_steps   # ms per step
-
-    ms = {nm: timed(nm) for nm in names}
-
-    # spread of the step time: each pass of the step graph timed on its own
-    spread = None
-    if "step" in ms and not args.no_graph:
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(passes + 1)]
+        ev = _events(torch, passes + 1)
         ev[0].record()
         for i in range(passes):
-            one_pass("step")
+            gr.replay()
             ev[i + 1].record()
         torch.cuda.synchronize()
-        per = sorted(ev[i].elapsed_time(ev[i + 1]) / NREP * 1e3 for i in range(passes))
-        pick = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
-        spread = {"us_per_step_median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9), "passes": passes,
-                  "steps_per_pass": NREP}
-        # the clocks while the step runs: enqueue about a second of passes, then read them
-        for _ in range(max(1, int(1.0 / (ms["step"] * 1e-3 * NREP)))):
-            one_pass("step")
-        spread["clocks"] = gpu_clocks()
-        torch.cuda.synchronize()
-
-    # Correctness spot check of the timed outputs against the oracle is the job of
-    # the test suite; here only finite outputs are asserted.
+        per = [ev[i].elapsed_time(ev[i + 1]) / nrep * 1e3 for i in range(passes)]
+        us[nm] = {"us": sum(per) / passes, "median": _pct(per, 0.5), "p10": _pct(per, 0.1), "p90": _pct(per, 0.9)}
+        del gr
     for k in ("out_n", "out_x"):
         if not torch.isfinite(o[k].float()).all():
             raise RuntimeError("non-finite output in %s" % k)
-
-    layer_tokens = R * 1   # one layer per step
     doc_bytes = Hkv * cfg.n * 2 * d * 2
     mlp_bytes = Hkv * cfg.mlps[0].params(d) * 2
-    res = {
-        "metric": "query-tokens/s/layer, Nectar vs exact cache attn; % of HBM / MFMA roofline",
-        "unit": "query-tokens/s/layer",
-        "higher_is_better": True,
-        "n_gpus": 1,
-        "steps": n_steps,
-        "warmup": n_warm,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-    }
-    if "step" in ms:
-        res["value"] = layer_tokens / (ms["step"] / 1e3)
-        res["ms_per_step"] = ms["step"]
-    res["config"] = {"workload": "%s: Hkv=8 Hq=32 d=128 bf16, n=61440 document keys, 513 local keys, "
-                                 "decode batch 1, MLP 4608/2944 GELU; one layer replica per step, %d replicas"
-                                 % (cfg.name, NREP),
-                     "global_batch": cfg.B, "seq_len": cfg.n + T, "parallelism": "single-gpu",
-                     "graph": not args.no_graph}
-    paths = {}
-    for nm in ("nectar", "exact"):
-        if nm in ms:
-            paths[nm] = {"qtok_s_layer": layer_tokens / (ms[nm] / 1e3), "us_per_layer": ms[nm] * 1e3}
-    if "nectar" in ms and "exact" in ms:
-        paths["nectar_speedup_vs_exact"] = ms["exact"] / ms["nectar"]
-        paths["module_rho"] = cfg.rho(cfg.mlps[0].params(d))
-    if "step_unfused" in ms:
-        paths["step_unfused_us"] = ms["step_unfused"] * 1e3
-    res["paths"] = paths
-    if spread:
-        res["timing"] = spread
     local_bytes = cfg.B * Hkv * T * 2 * d * 2
     merge_bytes = R * Hq * (2 * 4 * (d + 1) + 2 * d + 4)
+    res = {"workload": "c2_qwen3_4b_decode: Hkv=8 Hq=32 d=128 bf16, n=61,440, 513 local keys, decode batch 1, "
+                       "MLP 4608/2944 GELU; %d layer replicas per graph, %d passes" % (nrep, passes),
+           "step_both_paths": dict(us["step"], qtok_s_layer=R / (us["step"]["us"] * 1e-6)),
+           "paths": {"nectar": dict(us["nectar"], qtok_s_layer=R / (us["nectar"]["us"] * 1e-6)),
+                     "exact": dict(us["exact"], qtok_s_layer=R / (us["exact"]["us"] * 1e-6)),
+                     "nectar_speedup_vs_exact": us["exact"]["us"] / us["nectar"]["us"],
+                     "module_rho": cfg.rho(cfg.mlps[0].params(d))},
+           "step_unfused_us": us["step_unfused"]["us"]}
     comp = {}
     for nm, nb, what in (("module", mlp_bytes, "nectar_module_forward: MLP weights of the 8 KV heads, bf16"),
                          ("local", local_bytes, "nectar_local_attn_lse: 513 causal local keys and values, bf16"),
                          ("merge", merge_bytes, "nectar_merge: two fp32 pairs in, bf16 output and fp32 LSE out")):
-        if nm in ms:
-            us_c = ms[nm] * 1e3
-            comp[nm] = {"us": us_c, "bytes": nb, "gbs": nb / us_c / 1e3, "frac": nb / us_c / 1e3 / HBM_PEAK_GBS,
-                        "bound": "hbm", "what": what}
-    if comp:
-        res["components"] = comp
-    if "doc_partial" in ms:
-        us = ms["doc_partial"] * 1e3
-        ach = doc_bytes / (us * 1e-6) / 1e9
-        traffic = None
-        tf = os.path.join(ROOT, "profiles", "traffic_doc_attn_c2.json")
-        if os.path.exists(tf):
-            with open(tf) as fh:
-                tj = json.load(fh)
-            if tj.get("source_hash") == source_hash():
-                traffic = tj.get("hbm_bytes_per_launch")
-        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
-                           "kernel": "split-K partial pass of the exact document attention "
-                                     "(nectar_doc_attn_partials: attn_partial_mfma, one launch), %.2f us per launch, "
-                                     "%d algorithmic bytes per launch" % (us, doc_bytes)}
-    if "doc" in ms:
-        us_e = ms["doc"] * 1e3
-        res["exact_doc_entry_point"] = {"us": us_e, "gbs": doc_bytes / (us_e * 1e-6) / 1e9,
-                                        "frac": doc_bytes / (us_e * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                        "what": "nectar_doc_attn_exact: partial pass + combine launch"}
+        u = us[nm]["us"]
+        comp[nm] = {"us": u, "bytes": nb, "gbs": nb / u / 1e3, "frac": nb / u / 1e3 / HBM_PEAK_GBS, "bound": "hbm",
+                    "what": what}
+    res["components"] = comp
+    u = us["doc_partial"]["us"]
+    ach = doc_bytes / (u * 1e-6) / 1e9
+    res["doc_partial_roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic("doc_attn_c2"),
+                                   "kernel": "nectar_doc_attn_partials (attn_partial_mfma), %.2f us per launch, "
+                                             "%d algorithmic bytes per launch" % (u, doc_bytes)}
+    ue = us["doc"]["us"]
+    res["exact_doc_entry_point"] = {"us": ue, "gbs": doc_bytes / (ue * 1e-6) / 1e9,
+                                    "frac": doc_bytes / (ue * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                    "what": "nectar_doc_attn_exact: partial pass + combine launch"}
+    del reps
+    torch.cuda.empty_cache()
+    return res
 
-    if args.only is None and not (args.no_prefill and args.no_workloads):
-        del reps, graphs
-        torch.cuda.empty_cache()
-    if not args.no_prefill and args.only is None:
-        res["prefill_mlp"] = prefill_mlp(torch, np, nectar, configs, synth, dev)
-        res["merge_k"] = merge_k_prefill(torch, nectar, configs, dev)
-        res["fit_metrics"] = fit_metrics_prefill(torch, nectar, configs, dev)
-        res["deep_modules"] = deep_modules(torch, nectar, configs, dev)
-        res["train_step"] = train_step_bench(torch, nectar, configs, dev)
-    if not args.no_workloads and args.only is None:
-        res["workloads"] = {c.name: workload_layer(torch, nectar, c, dev) for c in (configs.C4, configs.C5, configs.C3)}
 
-    if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(cfg, q_h, K_h, V_h, Kl_h, Vl_h, P_h, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+def profile_leg(torch, np, nectar, configs, synth, dev, args):
+    """One kernel's launches alone, for counter runs: the batch-64 decode layer's
+    document partial pass (LDS-staged 32-row kernel), the prefill workload's
+    rho = 10 % MLP (erf GELU), or the 4B layer's document partial pass."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    bf = torch.bfloat16
+    rn = lambda *s, std=1.0: (torch.randn(*s, generator=g, device=dev) * std).to(bf)
+    n_launch = max(1, args.steps)
+    if args.only == "c4_doc_partial":
+        cfg = configs.C4
+        q = rn(cfg.R, cfg.Hq, cfg.d)
+        KV = [(rn(cfg.Hkv, cfg.n, cfg.d), rn(cfg.Hkv, cfg.n, cfg.d)) for _ in range(2)]
+        part = torch.empty(max(16, nectar.doc_attn_partials_size(nectar.desc(cfg.R, cfg.Hq, cfg.Hkv, cfg.d, nectar.BF16),
+                                                                  cfg.n)), dtype=torch.uint8, device=dev)
+        call = lambda i: nectar.doc_attn_partials(q, KV[i % 2][0], KV[i % 2][1], cfg.Hkv, partials=part)
+        nbytes, what = cfg.Hkv * cfg.n * 2 * cfg.d * 2, "batch-64 decode layer document partial pass"
+    elif args.only == "c2_doc_partial":
+        cfg = configs.C2
+        q = rn(cfg.R, cfg.Hq, cfg.d)
+        KV = [(rn(cfg.Hkv, cfg.n, cfg.d), rn(cfg.Hkv, cfg.n, cfg.d)) for _ in range(16)]
+        part = torch.empty(max(16, nectar.doc_attn_partials_size(nectar.desc(cfg.R, cfg.Hq, cfg.Hkv, cfg.d, nectar.BF16),
+                                                                  cfg.n)), dtype=torch.uint8, device=dev)
+        call = lambda i: nectar.doc_attn_partials(q, KV[i % 16][0], KV[i % 16][1], cfg.Hkv, partials=part)
+        nbytes, what = cfg.Hkv * cfg.n * 2 * cfg.d * 2, "4B decode layer document partial pass"
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        for _ in range(4):
+            src.clone()                # calibration copies of a known size
+    else:
+        cfg = configs.C3
+        m = cfg.mlps[1]
+        q = rn(cfg.R, cfg.Hq, cfg.d)
+        z = lambda *s: torch.zeros(*s, device=dev)
+        mod = nectar.MLPModule(rn(cfg.Hkv, m.Ht, cfg.d, std=cfg.d ** -0.5), z(cfg.Hkv, m.Ht),
+                               rn(cfg.Hkv, m.Ht, cfg.d, std=m.Ht ** -0.5), z(cfg.Hkv, cfg.d),
+                               rn(cfg.Hkv, m.Hs, cfg.d, std=cfg.d ** -0.5), z(cfg.Hkv, m.Hs),
+                               rn(cfg.Hkv, m.Hs, std=m.Hs ** -0.5), z(cfg.Hkv))
+        a = torch.empty(cfg.R, cfg.Hq, device=dev)
+        A = torch.empty(cfg.R, cfg.Hq, cfg.d, device=dev)
+        call = lambda i: nectar.module_forward(q, mod, cfg.Hkv, a_out=a, A_out=A)
+        nbytes = cfg.R * cfg.Hq * (4 * cfg.d * m.Ht + 2 * cfg.d * m.Hs + 2 * m.Hs)   # flops
+        what = "prefill workload rho = 10 % MLP 7680/5120 (erf GELU), 458,752 rows"
+    call(0)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for i in range(n_launch):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n_launch * 1e3
+    out = {"leg": args.only, "what": what, "launches": n_launch, "us_per_call": us}
+    if args.only == "c3_mlp10":
+        out.update(tflops=nbytes / us / 1e6, mfma_frac=nbytes / us / 1e6 / MFMA_BF16_PEAK_TFLOPS)
+    else:
+        out.update(gbs=nbytes / us / 1e3, frac=nbytes / us / 1e3 / HBM_PEAK_GBS)
+    return out
+
+
+def cpu_baseline(np, configs, synth, budget_s):
+    """The fp64 oracle (test infrastructure, never tuned) on the host cores.
+    `value`: the Nectar path (MLP module, local attention, merge) on one decode
+    step of one layer of the 1M-token stack (8 query tokens x 28 heads),
+    repeated for the budget, on up to 16 threads; the same on one thread.
+    `slices`: every workload and form once -- exact document attention, each MLP
+    module, the Quadrature module, local attention, merge -- on a bounded token
+    sample of one layer (the oracle's cost is linear in tokens, so tokens /
+    seconds is its query-tokens/s/layer)."""
+    import oracle
+    host = host_cpu()
+    threads = max(1, min(16, host["nproc"] or 1))
+    kwargs = lambda cfg, nt: dict(dt=cfg.dtype, Hq=cfg.Hq, Hkv=cfg.Hkv, threads=nt)
+
+    def timed(fn):
+        t0 = time.time()
+        fn()
+        return time.time() - t0
+
+    cfg = configs.C5
+    step = cfg.decode_steps - 1
+    T, qoff = cfg.local_len(step), cfg.q_offset(step)
+    q = synth.queries(cfg, 0, step)
+    Kl, Vl = synth.local_kv(cfg)
+    Klv, Vlv = (np.ascontiguousarray(x[:, :, :T]) for x in (Kl, Vl))
+    P = synth.mlp_params(cfg)
+
+    def nectar_step(nt):
+        kw = kwargs(cfg, nt)
+        a, Am = oracle.mlp(q, P["W1"], P["b1"], P["W2t"], P["b2"], P["Ws"], P["bs"], P["ws2"], P["bs2"], **kw)
+        lam, Al = oracle.local_attn(q, Klv, Vlv, B=cfg.B, Tq=1, Tloc=T, q_offset=qoff, **kw)
+        oracle.merge(a, Am, lam, Al)
+
+    def run(nt, budget):
+        n_tok, t0 = 0, time.time()
+        while True:
+            nectar_step(nt)
+            n_tok += cfg.R
+            el = time.time() - t0
+            if el >= budget:
+                return n_tok, el
+
+    n_tok, el = run(threads, budget_s * 2 / 3)
+    n1, el1 = run(1, budget_s / 3)
+    res = {"value": n_tok / el, "unit": "query-tokens/s/layer", "cores": threads, "kind": "oracle",
+           "sample": "%d tokens: decode step %d of one layer of the 1M-token stack through the Nectar path "
+                     "(MLP 5120/3072, %d local keys, merge), 8 tokens x 28 heads per pass, in %.1f s"
+                     % (n_tok, step, T, el),
+           "single_core": {"value": n1 / el1, "sample": "%d tokens in %.1f s" % (n1, el1)}, "host": host}
+
+    # slices of every workload and form
+    slices = []
+
+    def add(cfg_, form, ntok, secs):
+        slices.append({"workload": cfg_.name, "form": form, "tokens": int(ntok), "seconds": secs,
+                       "qtok_s_layer": ntok / secs, "threads": threads})
+
+    for cfg_ in configs.BY_INDEX:
+        step_ = 0 if cfg_.prefill else cfg_.decode_steps - 1
+        T_, qoff_ = cfg_.local_len(step_), cfg_.q_offset(step_)
+        q_ = synth.queries(cfg_, 0, step_)
+        # token sample: every token (tiny workload), else one query token, else one per question up to 8
+        toks = np.arange(cfg_.R, dtype=np.int32) if cfg_.R <= 16 else \
+            (np.array([0], dtype=np.int32) if cfg_.prefill else np.arange(min(cfg_.B, 8), dtype=np.int32))
+        kw = dict(kwargs(cfg_, threads), toks=toks)
+        K_, V_ = synth.doc_kv(cfg_)
+        ex_toks = toks if cfg_.n <= 131072 else toks[:1]       # the longest documents: one token
+        add(cfg_, "exact", len(ex_toks), timed(lambda: oracle.doc_attn(q_, K_, V_, **dict(kw, toks=ex_toks))))
+        del K_, V_
+        for which, mshape in enumerate(cfg_.mlps):
+            P_ = synth.mlp_params(cfg_, 0, which)
+            add(cfg_, "mlp %d/%d" % (mshape.Ht, mshape.Hs), len(toks),
+                timed(lambda: oracle.mlp(q_, P_["W1"], P_["b1"], P_["W2t"], P_["b2"], P_["Ws"], P_["bs"], P_["ws2"],
+                                         P_["bs2"], **kw)))
+        if cfg_.kv_pairs:
+            W_, Z_ = synth.kv_pairs(cfg_)
+            add(cfg_, "quadrature p=%d" % cfg_.kv_pairs, len(toks), timed(lambda: oracle.kvpair(q_, W_, Z_, **kw)))
+        Kl_, Vl_ = synth.local_kv(cfg_)
+        Klv_, Vlv_ = (np.ascontiguousarray(x[:, :, :T_]) for x in (Kl_, Vl_))
+        lk = dict(B=cfg_.B, Tq=cfg_.Tq, Tloc=T_, q_offset=qoff_, **kw)
+        add(cfg_, "local", len(toks), timed(lambda: oracle.local_attn(q_, Klv_, Vlv_, **lk)))
+        rows = cfg_.R * cfg_.Hq
+        a_, lam_ = np.zeros((cfg_.R, cfg_.Hq)), np.ones((cfg_.R, cfg_.Hq))
+        A_ = np.zeros((cfg_.R, cfg_.Hq, cfg_.d))
+        add(cfg_, "merge (all %d rows)" % rows, cfg_.R, timed(lambda: oracle.merge(a_, A_, lam_, A_)))
+    res["slices"] = slices
+    return res
 
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 flop/clk, dense
@@ -717,42 +1001,6 @@ def host_cpu():
         pass
     usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {"nproc": usable, "cpu_count": os.cpu_count(), "model": model}
-
-
-def cpu_baseline(cfg, q, K, V, Kl, Vl, P, budget_s):
-    """The fp64 oracle on the same step (both paths, one token), repeated until
-    the time budget is used; tokens per second per layer.  Two thirds of the
-    budget go to a run on up to 16 threads (the reported value), the rest to a
-    single-thread run."""
-    import numpy as np
-
-    import oracle
-    host = host_cpu()
-    threads = max(1, min(16, host["nproc"] or 1))
-    T = cfg.local_len(0)
-    Klv, Vlv = (np.ascontiguousarray(x[:, :, :T]) for x in (Kl, Vl))
-
-    def run(nthreads, budget):
-        kw = dict(dt="bf16", Hq=cfg.Hq, Hkv=cfg.Hkv, threads=nthreads)
-        n_tok = 0
-        t0 = time.time()
-        while True:
-            alpha, A = oracle.doc_attn(q, K, V, **kw)
-            a, Am = oracle.mlp(q, P["W1"], P["b1"], P["W2t"], P["b2"], P["Ws"], P["bs"], P["ws2"], P["bs2"], **kw)
-            lam, Al = oracle.local_attn(q, Klv, Vlv, B=cfg.B, Tq=cfg.Tq, Tloc=T, q_offset=cfg.q_offset(0), **kw)
-            oracle.merge(a, Am, lam, Al)
-            oracle.merge(alpha, A, lam, Al)
-            n_tok += cfg.R
-            el = time.time() - t0
-            if el >= budget:
-                return n_tok, el
-
-    n_tok, el = run(threads, budget_s * 2 / 3)
-    n1, el1 = run(1, budget_s / 3)
-    return {"value": n_tok / el, "unit": "query-tokens/s/layer", "cores": threads, "kind": "oracle",
-            "sample": "%d decode steps of the same layer (exact + Nectar paths, 1 query token x 32 heads "
-                      "each) in %.1f s" % (n_tok, el),
-            "single_core": {"value": n1 / el1, "sample": "%d steps in %.1f s" % (n1, el1)}, "host": host}
 
 
 if __name__ == "__main__":

@@ -164,13 +164,23 @@ _ws_cache = {}
 
 
 def workspace(nbytes: int, device=None) -> Optional[torch.Tensor]:
-    """A cached scratch buffer of at least nbytes on the device (None for 0)."""
+    """A cached scratch buffer of at least nbytes on the device (None for 0).
+
+    One buffer per device, shared by every call of this binding: calls issued on
+    different streams must not overlap in time (the caller orders them; the C ABI
+    itself takes a workspace per call).  The buffer only grows, and it may not
+    grow while a graph is being captured -- graphs captured earlier would keep
+    the released buffer's address -- so run the largest call once before
+    capturing."""
     if nbytes == 0:
         return None
     dev = torch.device(device or "cuda")
     key = (dev.type, dev.index)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
+        if buf is not None and torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("the binding's workspace would grow (to %d bytes) during graph capture: run the "
+                               "largest call once before capturing" % nbytes)
         # workspace contents need no initialisation; zeroed once for reproducible scratch
         buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf

@@ -156,6 +156,50 @@ def dtype_code(t: torch.Tensor) -> int:
     raise TypeError("unsupported element type %s" % t.dtype)
 
 
+_STORAGE = (torch.float32, torch.bfloat16, torch.uint16, torch.int16)
+F32T = torch.float32
+
+
+def _arg(x, name, shape, dtype):
+    """Shape and element type of a tensor argument, checked on the host before any
+    library call (the C ABI receives bare pointers and cannot see sizes).  `shape`
+    entries of None are free; `dtype` is a storage code (F32 / BF16: fp32, or
+    bf16 as bfloat16 or 16-bit integer bits) or a torch dtype."""
+    if not isinstance(x, torch.Tensor):
+        raise ValueError("%s must be a torch tensor, got %s" % (name, type(x).__name__))
+    if x.dim() != len(shape) or any(e is not None and int(a) != int(e) for a, e in zip(x.shape, shape)):
+        want = "[" + "][".join("*" if e is None else str(int(e)) for e in shape) + "]"
+        raise ValueError("%s has shape %s, expected %s" % (name, list(x.shape), want))
+    if isinstance(dtype, int):
+        if x.dtype not in _STORAGE or dtype_code(x) != dtype:
+            raise ValueError("%s has element type %s, expected %s" % (name, x.dtype, "fp32" if dtype == F32 else "bf16"))
+    elif x.dtype != dtype:
+        raise ValueError("%s has element type %s, expected %s" % (name, x.dtype, dtype))
+    return x
+
+
+def _on_gpu(ref, *named):
+    """Every given tensor on the GPU device of `ref` and contiguous (after the shape
+    and type checks, so those are reported first)."""
+    dev = ref.device
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("%s must be in GPU device memory, got a tensor on %s" % (name, t.device))
+        if t.device != dev:
+            raise ValueError("%s is on %s, the call's tensors are on %s" % (name, t.device, dev))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _q(q, name="q"):
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("%s must be a [R][Hq][d] tensor" % name)
+    _arg(q, name, (None, None, None), F32 if q.dtype == torch.float32 else BF16)
+    return q.shape[0], q.shape[1], q.shape[2], dtype_code(q)
+
+
 def desc(R, Hq, Hkv, d, dtype, scale=0.0, splits=0) -> AttnDesc:
     return AttnDesc(int(R), int(Hq), int(Hkv), int(d), int(dtype), float(scale), int(splits))
 
@@ -198,9 +242,16 @@ def doc_attn_workspace_size(dsc: AttnDesc, n: int) -> int:
 
 def doc_attn_exact(q, k, v, Hkv, *, scale=0.0, splits=0, alpha_out=None, A_out=None):
     """Exact document attention (alpha [R][Hq], A [R][Hq][d] fp32); q [R][Hq][d], k/v [Hkv][n][d]."""
-    R, Hq, d = q.shape
-    n = k.shape[-2] if k.dim() >= 2 else 0
-    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    R, Hq, d, code = _q(q)
+    _arg(k, "k", (Hkv, None, d), code)
+    n = k.shape[1]
+    _arg(v, "v", (Hkv, n, d), code)
+    if alpha_out is not None:
+        _arg(alpha_out, "alpha_out", (R, Hq), F32T)
+    if A_out is not None:
+        _arg(A_out, "A_out", (R, Hq, d), F32T)
+    _on_gpu(q, ("q", q), ("k", k), ("v", v), ("alpha_out", alpha_out), ("A_out", A_out))
+    dsc = desc(R, Hq, Hkv, d, code, scale, splits)
     if alpha_out is None:
         alpha_out = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
     if A_out is None:
@@ -218,9 +269,14 @@ def doc_attn_partials_size(dsc: AttnDesc, n: int) -> int:
 def doc_attn_partials(q, k, v, Hkv, *, scale=0.0, splits=0, partials=None):
     """First pass of the exact document attention: the split-K partials, into a
     uint8 device tensor (allocated when not given).  Returns the tensor."""
-    R, Hq, d = q.shape
-    n = k.shape[-2]
-    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    R, Hq, d, code = _q(q)
+    _arg(k, "k", (Hkv, None, d), code)
+    n = k.shape[1]
+    _arg(v, "v", (Hkv, n, d), code)
+    if partials is not None:
+        _arg(partials, "partials", (None,), torch.uint8)
+    _on_gpu(q, ("q", q), ("k", k), ("v", v), ("partials", partials))
+    dsc = desc(R, Hq, Hkv, d, code, scale, splits)
     nbytes = int(_lib.nectar_doc_attn_partials_size(ctypes.byref(dsc), n))
     if partials is None:
         partials = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
@@ -231,6 +287,12 @@ def doc_attn_partials(q, k, v, Hkv, *, scale=0.0, splits=0, partials=None):
 
 def doc_attn_combine(partials, R, Hq, Hkv, d, n, dtype, *, scale=0.0, splits=0, alpha_out=None, A_out=None):
     """Second pass: (alpha [R][Hq], A [R][Hq][d]) from the partials of the same shapes."""
+    _arg(partials, "partials", (None,), torch.uint8)
+    if alpha_out is not None:
+        _arg(alpha_out, "alpha_out", (R, Hq), F32T)
+    if A_out is not None:
+        _arg(A_out, "A_out", (R, Hq, d), F32T)
+    _on_gpu(partials, ("partials", partials), ("alpha_out", alpha_out), ("A_out", A_out))
     dsc = desc(R, Hq, Hkv, d, dtype, scale, splits)
     dev_ = partials.device
     if alpha_out is None:
@@ -255,6 +317,20 @@ class MLPModule:
     bs2: torch.Tensor
     act: int = GELU
 
+    def check(self, Hkv: int, d: int, code: int):
+        """Shapes and element types against the call's KV heads, head dimension and
+        storage type (weights in the storage type, biases fp32)."""
+        Ht, Hs = int(self.W1.shape[-2]) if self.W1.dim() == 3 else -1, int(self.Ws.shape[-2]) if self.Ws.dim() == 3 else -1
+        _arg(self.W1, "W1", (Hkv, Ht, d), code)
+        _arg(self.W2t, "W2t", (Hkv, Ht, d), code)
+        _arg(self.Ws, "Ws", (Hkv, Hs, d), code)
+        _arg(self.ws2, "ws2", (Hkv, Hs), code)
+        _arg(self.b1, "b1", (Hkv, Ht), F32T)
+        _arg(self.b2, "b2", (Hkv, d), F32T)
+        _arg(self.bs, "bs", (Hkv, Hs), F32T)
+        _arg(self.bs2, "bs2", (Hkv,), F32T)
+        return [(k, getattr(self, k)) for k in ("W1", "b1", "W2t", "b2", "Ws", "bs", "ws2", "bs2")]
+
     def struct(self) -> Module:
         m = Module()
         m.kind, m.act = MLP, self.act
@@ -269,6 +345,11 @@ class KVPairModule:
     """Quadrature module: W, Z [Hkv][p][d]."""
     W: torch.Tensor
     Z: torch.Tensor
+
+    def check(self, Hkv: int, d: int, code: int):
+        _arg(self.W, "W", (Hkv, None, d), code)
+        _arg(self.Z, "Z", (Hkv, self.W.shape[1], d), code)
+        return [("W", self.W), ("Z", self.Z)]
 
     def struct(self) -> Module:
         m = Module()
@@ -294,6 +375,34 @@ class DeepMLPModule:
     bt_out: torch.Tensor
     act: int = SILU
 
+    def check(self, Hkv: int, d: int, code: int):
+        depth = [int(x) for x in self.depth]
+        width = [int(x) if depth[i] > 0 else 0 for i, x in enumerate(self.width)]
+        if len(self.layers) != sum(depth):
+            raise ValueError("deep module: %d layers for depths %s" % (len(self.layers), depth))
+        named, l = [], 0
+        for part in range(3):
+            for j in range(depth[part]):
+                Wq, Wh, b = self.layers[l]
+                H = width[part]
+                H_in = H if j > 0 else (width[0] if part > 0 and depth[0] > 0 else 0)
+                _arg(Wq, "layer %d Wq" % l, (Hkv, H, d), code)
+                if H_in:
+                    _arg(Wh, "layer %d Wh" % l, (Hkv, H, H_in), code)
+                elif Wh is not None:
+                    raise ValueError("layer %d reads only the query: Wh must be None" % l)
+                _arg(b, "layer %d b" % l, (Hkv, H), F32T)
+                named += [("layer %d Wq" % l, Wq), ("layer %d Wh" % l, Wh), ("layer %d b" % l, b)]
+                l += 1
+        Hs = width[1] if depth[1] > 0 else width[0]
+        Ht = width[2] if depth[2] > 0 else width[0]
+        _arg(self.ws_out, "ws_out", (Hkv, Hs), code)
+        _arg(self.bs_out, "bs_out", (Hkv,), F32T)
+        _arg(self.Wt_out, "Wt_out", (Hkv, d, Ht), code)
+        _arg(self.bt_out, "bt_out", (Hkv, d), F32T)
+        return named + [("ws_out", self.ws_out), ("bs_out", self.bs_out), ("Wt_out", self.Wt_out),
+                        ("bt_out", self.bt_out)]
+
     def struct(self) -> Module:
         if len(self.layers) > DEEP_MAX_LAYERS:
             raise ValueError("at most %d layers" % DEEP_MAX_LAYERS)
@@ -318,8 +427,14 @@ def module_workspace_size(dsc: AttnDesc, mod) -> int:
 
 def module_forward(q, module, Hkv, *, scale=0.0, splits=0, a_out=None, A_out=None):
     """(a [R][Hq], A [R][Hq][d]) fp32 of an MLPModule, DeepMLPModule or KVPairModule."""
-    R, Hq, d = q.shape
-    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    R, Hq, d, code = _q(q)
+    named = module.check(Hkv, d, code)
+    if a_out is not None:
+        _arg(a_out, "a_out", (R, Hq), F32T)
+    if A_out is not None:
+        _arg(A_out, "A_out", (R, Hq, d), F32T)
+    _on_gpu(q, ("q", q), ("a_out", a_out), ("A_out", A_out), *named)
+    dsc = desc(R, Hq, Hkv, d, code, scale, splits)
     m = module.struct()
     if a_out is None:
         a_out = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
@@ -343,9 +458,18 @@ def local_attn_lse(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, scale=0.0, s
     Returns (lse, A_local) when want_pair, and additionally (out, out_lse) when a
     document pair (doc_lse, doc_A) is given: the merged output in q's dtype.
     """
-    R, Hq, d = q.shape
-    T_cap = k_loc.shape[-2]
-    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    R, Hq, d, code = _q(q)
+    _arg(k_loc, "k_loc", (B, Hkv, None, d), code)
+    T_cap = k_loc.shape[2]
+    _arg(v_loc, "v_loc", (B, Hkv, T_cap, d), code)
+    for name, t, shape, dt in (("lse_out", lse_out, (R, Hq), F32T), ("A_out", A_out, (R, Hq, d), F32T),
+                               ("doc_lse", doc_lse, (R, Hq), F32T), ("doc_A", doc_A, (R, Hq, d), F32T),
+                               ("out", out, (R, Hq, d), code), ("out_lse", out_lse, (R, Hq), F32T)):
+        if t is not None:
+            _arg(t, name, shape, dt)
+    _on_gpu(q, ("q", q), ("k_loc", k_loc), ("v_loc", v_loc), ("lse_out", lse_out), ("A_out", A_out),
+            ("doc_lse", doc_lse), ("doc_A", doc_A), ("out", out), ("out_lse", out_lse))
+    dsc = desc(R, Hq, Hkv, d, code, scale, splits)
     loc = LocalDesc(int(B), int(Tq), int(T_loc), int(T_cap), int(q_offset))
     if want_pair:
         if lse_out is None:
@@ -372,7 +496,16 @@ def local_attn_lse(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, scale=0.0, s
 
 def merge(a, A, lam, A_loc, *, Hkv, out_dtype, out=None, lse_out=None):
     """Log-sum-exp merge of (a, A) with (lam, A_loc); out in out_dtype (fp32/bf16)."""
+    _arg(A, "A", (None, None, None), F32T)
     R, Hq, d = A.shape
+    _arg(a, "a", (R, Hq), F32T)
+    _arg(lam, "lam", (R, Hq), F32T)
+    _arg(A_loc, "A_loc", (R, Hq, d), F32T)
+    if out is not None:
+        _arg(out, "out", (R, Hq, d), F32 if out_dtype == torch.float32 else BF16)
+    if lse_out is not None:
+        _arg(lse_out, "lse_out", (R, Hq), F32T)
+    _on_gpu(A, ("a", a), ("A", A), ("lam", lam), ("A_loc", A_loc), ("out", out), ("lse_out", lse_out))
     code = F32 if out_dtype == torch.float32 else BF16
     dsc = desc(R, Hq, Hkv, d, code)
     if out is None:
@@ -399,6 +532,18 @@ def merge_k(pairs, lam=None, A_loc=None, *, Hkv, out_dtype, out=None, lse_out=No
     for a, A in pairs:
         if a.shape != (R, Hq) or A.shape != (R, Hq, d) or a.dtype != torch.float32 or A.dtype != torch.float32:
             raise ValueError("merge_k: every pair is ([R][Hq], [R][Hq][d]) float32")
+    if (lam is None) != (A_loc is None):
+        raise ValueError("merge_k: give both lam and A_loc, or neither")
+    if lam is not None:
+        _arg(lam, "lam", (R, Hq), F32T)
+        _arg(A_loc, "A_loc", (R, Hq, d), F32T)
+    if out is not None:
+        _arg(out, "out", (R, Hq, d), F32 if out_dtype == torch.float32 else BF16)
+    if lse_out is not None:
+        _arg(lse_out, "lse_out", (R, Hq), F32T)
+    _on_gpu(ref, *[("a[%d]" % i, a) for i, (a, _) in enumerate(pairs)],
+            *[("A[%d]" % i, A) for i, (_, A) in enumerate(pairs)], ("lam", lam), ("A_loc", A_loc), ("out", out),
+            ("lse_out", lse_out))
     if out is None:
         out = torch.empty((R, Hq, d), dtype=out_dtype, device=ref.device)
     if lse_out is None:
@@ -414,8 +559,15 @@ def merge_k(pairs, lam=None, A_loc=None, *, Hkv, out_dtype, out=None, lse_out=No
 def fit_metrics(q, a, A, alpha, A_exact, Hkv, *, row_out=None, head_out=None):
     """Per row (a - alpha)^2, ||A - A_exact||^2, log(||A - A_exact||^2 / ||q - A_exact||^2)
     ([R][Hq][3] fp32) and their per-KV-head sums ([Hkv][3] fp64)."""
-    R, Hq, d = q.shape
-    dsc = desc(R, Hq, Hkv, d, dtype_code(q))
+    R, Hq, d, code = _q(q)
+    for name, t, shape, dt in (("a", a, (R, Hq), F32T), ("A", A, (R, Hq, d), F32T), ("alpha", alpha, (R, Hq), F32T),
+                               ("A_exact", A_exact, (R, Hq, d), F32T), ("row_out", row_out, (R, Hq, 3), F32T),
+                               ("head_out", head_out, (Hkv, 3), torch.float64)):
+        if t is not None:
+            _arg(t, name, shape, dt)
+    _on_gpu(q, ("q", q), ("a", a), ("A", A), ("alpha", alpha), ("A_exact", A_exact), ("row_out", row_out),
+            ("head_out", head_out))
+    dsc = desc(R, Hq, Hkv, d, code)
     if row_out is None:
         row_out = torch.empty((R, Hq, 3), dtype=torch.float32, device=q.device)
     if head_out is None:
@@ -460,8 +612,12 @@ def lr_at(step: int, peak: float, warmup: int, total: int) -> float:
 
 def mlp_loss_grad(q, module: "MLPModule", alpha, A_target, Hkv, *, lambda_alpha=0.1, lambda_A=1.0):
     """(grad flat fp32, loss [3] = (L, L_alpha, L_A)) of the regression loss."""
-    R, Hq, d = q.shape
-    dsc = desc(R, Hq, Hkv, d, dtype_code(q))
+    R, Hq, d, code = _q(q)
+    named = module.check(Hkv, d, code)
+    _arg(alpha, "alpha", (R, Hq), F32T)
+    _arg(A_target, "A_target", (R, Hq, d), F32T)
+    _on_gpu(q, ("q", q), ("alpha", alpha), ("A_target", A_target), *named)
+    dsc = desc(R, Hq, Hkv, d, code)
     m = module.struct()
     n = int(_lib.nectar_mlp_param_count(ctypes.byref(dsc), ctypes.byref(m)))
     grad = torch.empty(n, dtype=torch.float32, device=q.device)
@@ -473,6 +629,10 @@ def mlp_loss_grad(q, module: "MLPModule", alpha, A_target, Hkv, *, lambda_alpha=
 
 
 def adamw_step(theta, grad, m, v, hp: TrainHParams):
+    _arg(theta, "theta", (None,), F32T)
+    for name, t in (("grad", grad), ("m", m), ("v", v)):
+        _arg(t, name, (theta.numel(),), F32T)
+    _on_gpu(theta, ("theta", theta), ("grad", grad), ("m", m), ("v", v))
     _check(_lib.nectar_adamw_step(theta.numel(), _ptr(theta), _ptr(grad), _ptr(m), _ptr(v), ctypes.byref(hp),
                                   _stream()))
 
@@ -481,9 +641,22 @@ def mlp_train_step(q, module: "MLPModule", alpha, A_target, Hkv, hp: TrainHParam
                    grad=None, loss=None, gnorm=None):
     """One regression training step; updates theta, the moments and the module's
     arrays in place.  Returns (grad, loss, gnorm)."""
-    R, Hq, d = q.shape
-    dsc = desc(R, Hq, Hkv, d, dtype_code(q))
+    R, Hq, d, code = _q(q)
+    named = module.check(Hkv, d, code)
+    _arg(alpha, "alpha", (R, Hq), F32T)
+    _arg(A_target, "A_target", (R, Hq, d), F32T)
+    dsc = desc(R, Hq, Hkv, d, code)
     m = module.struct()
+    nparams = int(_lib.nectar_mlp_param_count(ctypes.byref(dsc), ctypes.byref(m)))
+    for name, t in (("theta", theta), ("adam_m", adam_m), ("adam_v", adam_v), ("grad", grad)):
+        if t is not None:
+            _arg(t, name, (nparams,), F32T)
+    if loss is not None:
+        _arg(loss, "loss", (3,), F32T)
+    if gnorm is not None:
+        _arg(gnorm, "gnorm", (2,), F32T)
+    _on_gpu(q, ("q", q), ("alpha", alpha), ("A_target", A_target), ("theta", theta), ("adam_m", adam_m),
+            ("adam_v", adam_v), ("grad", grad), ("loss", loss), ("gnorm", gnorm), *named)
     f32 = dict(dtype=torch.float32, device=q.device)
     grad = torch.empty(theta.numel(), **f32) if grad is None else grad
     loss = torch.empty(3, **f32) if loss is None else loss
@@ -503,10 +676,26 @@ def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, 
     lse_exact, out_nectar, lse_nectar, and with `pairs` also alpha, A, a, Am, lam, Aloc.
     `out` may supply preallocated tensors under the same keys.  `no_alloc` calls the
     allocation-free entry point (the library's own device scratch, no workspace)."""
-    R, Hq, d = q.shape
-    T_cap = k_loc.shape[-2]
-    n = k.shape[-2] if (exact and k is not None) else 0
-    dsc = desc(R, Hq, Hkv, d, dtype_code(q), scale, splits)
+    R, Hq, d, code = _q(q)
+    _arg(k_loc, "k_loc", (B, Hkv, None, d), code)
+    T_cap = k_loc.shape[2]
+    _arg(v_loc, "v_loc", (B, Hkv, T_cap, d), code)
+    n = 0
+    if exact and k is not None:
+        _arg(k, "k", (Hkv, None, d), code)
+        n = k.shape[1]
+        _arg(v, "v", (Hkv, n, d), code)
+    named = module.check(Hkv, d, code) if module is not None else []
+    shapes = {"out_exact": ((R, Hq, d), code), "lse_exact": ((R, Hq), F32T), "alpha": ((R, Hq), F32T),
+              "A": ((R, Hq, d), F32T), "out_nectar": ((R, Hq, d), code), "lse_nectar": ((R, Hq), F32T),
+              "a": ((R, Hq), F32T), "Am": ((R, Hq, d), F32T), "lam": ((R, Hq), F32T), "Aloc": ((R, Hq, d), F32T)}
+    for key, t in (out or {}).items():
+        if key not in shapes:
+            raise ValueError("layer_step: unknown output %r" % key)
+        _arg(t, "out[%r]" % key, *shapes[key])
+    _on_gpu(q, ("q", q), ("k_loc", k_loc), ("v_loc", v_loc), ("k", k if exact else None), ("v", v if exact else None),
+            *named, *[("out[%r]" % key, t) for key, t in (out or {}).items()])
+    dsc = desc(R, Hq, Hkv, d, code, scale, splits)
     loc = LocalDesc(int(B), int(Tq), int(T_loc), int(T_cap), int(q_offset))
     o = dict(out or {})
     f32 = dict(dtype=torch.float32, device=q.device)
@@ -546,6 +735,7 @@ def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, 
 
 def workspace_init(buf: torch.Tensor):
     """Zero a caller-owned workspace tensor through the library."""
+    _on_gpu(buf, ("buf", buf))
     _check(_lib.nectar_workspace_init(_ptr(buf), buf.numel() * buf.element_size(), _stream()))
 
 

@@ -1,0 +1,97 @@
+"""The binding checks shapes, element types, devices and contiguity of every
+tensor argument on the host and raises ValueError before any library call
+(the C ABI receives bare pointers and cannot see sizes).  CPU only: wrong
+shapes and types are reported first; correct ones on the CPU are refused as
+not being in GPU memory."""
+import pytest
+import torch
+
+from learned_kv_cache_02_amd import nectar as nx
+
+R, Hq, Hkv, d, n = 3, 8, 2, 128, 100
+bf = torch.bfloat16
+
+
+def t(*shape, dtype=bf):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def mlp(Ht=64, Hs=32, **over):
+    parts = dict(W1=t(Hkv, Ht, d), b1=t(Hkv, Ht, dtype=torch.float32), W2t=t(Hkv, Ht, d),
+                 b2=t(Hkv, d, dtype=torch.float32), Ws=t(Hkv, Hs, d), bs=t(Hkv, Hs, dtype=torch.float32),
+                 ws2=t(Hkv, Hs), bs2=t(Hkv, dtype=torch.float32))
+    parts.update(over)
+    return nx.MLPModule(**parts)
+
+
+def raises(match, fn, *a, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*a, **kw)
+
+
+def test_doc_attn_checks():
+    raises("k has shape", nx.doc_attn_exact, t(R, Hq, d), t(3, n, d), t(3, n, d), Hkv)          # wrong KV heads
+    raises("v has shape", nx.doc_attn_exact, t(R, Hq, d), t(Hkv, n, d), t(Hkv, n + 1, d), Hkv)
+    raises("k has element type", nx.doc_attn_exact, t(R, Hq, d), t(Hkv, n, d, dtype=torch.float32),
+           t(Hkv, n, d, dtype=torch.float32), Hkv)                                              # fp32 cache, bf16 q
+    raises("A_out has shape", nx.doc_attn_exact, t(R, Hq, d), t(Hkv, n, d), t(Hkv, n, d), Hkv,
+           A_out=t(R, Hq, d - 1, dtype=torch.float32))                                          # short output
+    raises("alpha_out has element type", nx.doc_attn_exact, t(R, Hq, d), t(Hkv, n, d), t(Hkv, n, d), Hkv,
+           alpha_out=t(R, Hq))
+    raises("GPU device memory", nx.doc_attn_exact, t(R, Hq, d), t(Hkv, n, d), t(Hkv, n, d), Hkv)
+    raises("q must be", nx.doc_attn_exact, t(R, d), t(Hkv, n, d), t(Hkv, n, d), Hkv)
+    raises("partials has element type", nx.doc_attn_partials, t(R, Hq, d), t(Hkv, n, d), t(Hkv, n, d), Hkv,
+           partials=t(64, dtype=torch.float32))
+
+
+def test_module_checks():
+    q = t(R, Hq, d)
+    raises("b1 has element type", nx.module_forward, q, mlp(b1=t(Hkv, 64)), Hkv)                  # bf16 bias
+    raises("W2t has shape", nx.module_forward, q, mlp(W2t=t(Hkv, 65, d)), Hkv)
+    raises("W1 has shape", nx.module_forward, q, mlp(), 4)                                         # wrong Hkv
+    raises("ws2 has element type", nx.module_forward, q, mlp(ws2=t(Hkv, 32, dtype=torch.float32)), Hkv)
+    raises("a_out has shape", nx.module_forward, q, mlp(), Hkv, a_out=t(R, Hq + 1, dtype=torch.float32))
+    raises("Z has shape", nx.module_forward, q, nx.KVPairModule(t(Hkv, 50, d), t(Hkv, 49, d)), Hkv)
+    raises("GPU device memory", nx.module_forward, q, mlp(), Hkv)
+    deep = nx.DeepMLPModule((0, 1, 1), (0, 64, 64), [(t(Hkv, 64, d), None, t(Hkv, 64, dtype=torch.float32)),
+                                                      (t(Hkv, 64, d), t(Hkv, 64, 64), t(Hkv, 64, dtype=torch.float32))],
+                            t(Hkv, 64), t(Hkv, dtype=torch.float32), t(Hkv, d, 64), t(Hkv, d, dtype=torch.float32))
+    raises("reads only the query", nx.module_forward, q, deep, Hkv)
+
+
+def test_local_merge_fit_checks():
+    q = t(R, Hq, d)
+    raises("k_loc has shape", nx.local_attn_lse, q, t(R, 3, 40, d), t(R, 3, 40, d), Hkv, B=R, Tq=1, T_loc=40,
+           q_offset=39)
+    raises("doc_A has element type", nx.local_attn_lse, q, t(R, Hkv, 40, d), t(R, Hkv, 40, d), Hkv, B=R, Tq=1,
+           T_loc=40, q_offset=39, doc_lse=t(R, Hq, dtype=torch.float32), doc_A=t(R, Hq, d))
+    f = lambda *s: t(*s, dtype=torch.float32)
+    raises("lam has shape", nx.merge, f(R, Hq), f(R, Hq, d), f(R, Hq + 1), f(R, Hq, d), Hkv=Hkv, out_dtype=bf)
+    raises("out has element type", nx.merge, f(R, Hq), f(R, Hq, d), f(R, Hq), f(R, Hq, d), Hkv=Hkv, out_dtype=bf,
+           out=f(R, Hq, d))
+    raises("lam and A_loc", nx.merge_k, [(f(R, Hq), f(R, Hq, d))], f(R, Hq), None, Hkv=Hkv, out_dtype=bf)
+    raises("row_out has shape", nx.fit_metrics, q, f(R, Hq), f(R, Hq, d), f(R, Hq), f(R, Hq, d), Hkv,
+           row_out=f(R, Hq, 2))
+    raises("GPU device memory", nx.fit_metrics, q, f(R, Hq), f(R, Hq, d), f(R, Hq), f(R, Hq, d), Hkv)
+
+
+def test_layer_step_and_training_checks():
+    q = t(R, Hq, d)
+    kw = dict(B=R, Tq=1, T_loc=40, q_offset=39)
+    raises("v has shape", nx.layer_step, q, t(R, Hkv, 40, d), t(R, Hkv, 40, d), Hkv, k=t(Hkv, n, d),
+           v=t(Hkv, n, 64), **kw)
+    raises("unknown output", nx.layer_step, q, t(R, Hkv, 40, d), t(R, Hkv, 40, d), Hkv, k=t(Hkv, n, d),
+           v=t(Hkv, n, d), out={"bogus": t(1)}, **kw)
+    raises("out\\['lse_exact'\\] has shape", nx.layer_step, q, t(R, Hkv, 40, d), t(R, Hkv, 40, d), Hkv,
+           k=t(Hkv, n, d), v=t(Hkv, n, d), out={"lse_exact": t(R, Hq + 2, dtype=torch.float32)}, **kw)
+    raises("bs2 has shape", nx.layer_step, q, t(R, Hkv, 40, d), t(R, Hkv, 40, d), Hkv, module=mlp(bs2=t(Hkv + 1, dtype=torch.float32)),
+           exact=False, **kw)
+    raises("GPU device memory", nx.layer_step, q, t(R, Hkv, 40, d), t(R, Hkv, 40, d), Hkv, k=t(Hkv, n, d),
+           v=t(Hkv, n, d), **kw)
+    f = lambda *s: t(*s, dtype=torch.float32)
+    raises("A_target has shape", nx.mlp_loss_grad, q, mlp(), f(R, Hq), f(R, Hq, d + 1), Hkv)
+    raises("grad has shape", nx.adamw_step, f(100), f(99), f(100), f(100), nx.train_hparams(lr=1e-3, step=1))
+    m = mlp()
+    nparams = int(nx.mlp_params_flat(m).numel())
+    raises("theta has shape", nx.mlp_train_step, q, m, f(R, Hq), f(R, Hq, d), Hkv, nx.train_hparams(lr=1e-3, step=1),
+           f(nparams - 1), f(nparams), f(nparams))

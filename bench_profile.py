@@ -6,6 +6,13 @@ average of the last N launches of kernel K (the timed window of a bench leg
 whose earlier launches are its warm-up).
 
     python3 bench_profile.py <trace.csv> [--kernel attn_rows_lds --last 56]
+
+With ``--counters`` the file is a counter_collection.csv (``rocprofv3 --pmc``):
+per dispatch of kernel K (its most frequent launch shape) every counter is
+summed over its instances, and the table gives the average per dispatch; MFMA
+utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1,024 SIMDs).
+
+    python3 bench_profile.py <counter_collection.csv> --counters --kernel attn_rows_lds32
 """
 import argparse
 import csv
@@ -18,7 +25,10 @@ def main():
     ap.add_argument("--kernel", default=None)
     ap.add_argument("--last", type=int, default=0)
     ap.add_argument("--skip", default="at::native", help="kernels whose name contains this are left out")
+    ap.add_argument("--counters", action="store_true")
     args = ap.parse_args()
+    if args.counters:
+        return counters(args)
     rows = list(csv.DictReader(open(args.trace)))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     agg = OrderedDict()
@@ -43,6 +53,32 @@ def main():
         tail = named[-args.last:]
         print("\nlast %d launches of %s: average %.2f us (min %.2f, max %.2f)"
               % (len(tail), args.kernel, sum(tail) / len(tail), min(tail), max(tail)))
+
+
+def counters(args):
+    from collections import defaultdict
+    per = defaultdict(lambda: defaultdict(float))     # dispatch -> counter -> sum over instances
+    grid = {}
+    for r in csv.DictReader(open(args.trace)):
+        if args.kernel not in r.get("Kernel_Name", ""):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        grid[key] = r.get("Grid_Size", "")
+    shapes = defaultdict(int)
+    for k in per:
+        shapes[grid[k]] += 1
+    timed = max(shapes, key=shapes.get)
+    keys = [k for k in per if grid[k] == timed]
+    names = sorted({c for k in keys for c in per[k]})
+    print("%d dispatches of %s (grid %s)\n" % (len(keys), args.kernel, timed))
+    print("| counter | average per dispatch |")
+    print("|---|---|")
+    avg = {c: sum(per[k][c] for k in keys) / len(keys) for c in names}
+    for c in names:
+        print("| %s | %.6g |" % (c, avg[c]))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+        print("\nMFMA utilisation: %.3f" % (avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] * 1024)))
 
 
 if __name__ == "__main__":

@@ -180,17 +180,30 @@ __global__ __launch_bounds__(64) void attn_finish(FinishParams a) {
 }
 
 hipError_t launch_finish(const FinishParams &p, int dtype, int d, hipStream_t st) {
-    // float4 columns per wave: 16 waves per row at d = 128, 8 at d = 64 (4B decode
-    // step with the batched folds: 2 columns 54.5 us, 4 columns 54.8 us, 8 columns
-    // 56.1 us)
+    // float4 columns per wave: 2 (16 waves per row at d = 128) for few rows; from
+    // 128 rows on, 4 (1M-token decode stack with 224 rows per layer: 6.6 -> 5.9 us
+    // per layer; the 4B decode step with the batched folds is flat, 54.5-54.8 us)
+#ifndef NECTAR_FINISH_COLS_MANY
+#define NECTAR_FINISH_COLS_MANY 4
+#endif
+#ifndef NECTAR_FINISH_MANY_ROWS
+#define NECTAR_FINISH_MANY_ROWS 128
+#endif
     constexpr int kCols = 2;
-    dim3 grid((unsigned)slice_grid((long)p.P * p.Rp, d / 4 / kCols)), block(64);
-    if (d == 128 && dtype == 1) hipLaunchKernelGGL((attn_finish<128, uint16_t, kCols>), grid, block, 0, st, p);
-    else if (d == 128) hipLaunchKernelGGL((attn_finish<128, float, kCols>), grid, block, 0, st, p);
-    else if (d == 64 && dtype == 1) hipLaunchKernelGGL((attn_finish<64, uint16_t, kCols>), grid, block, 0, st, p);
-    else if (d == 64) hipLaunchKernelGGL((attn_finish<64, float, kCols>), grid, block, 0, st, p);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    const long rows = (long)p.P * p.Rp;
+    const int nc = rows >= NECTAR_FINISH_MANY_ROWS ? NECTAR_FINISH_COLS_MANY : kCols;
+    dim3 grid((unsigned)slice_grid(rows, d / 4 / nc)), block(64);
+#define NECTAR_FINISH_CASE(NC) \
+    if (nc == NC) { \
+        if (d == 128 && dtype == 1) hipLaunchKernelGGL((attn_finish<128, uint16_t, NC>), grid, block, 0, st, p); \
+        else if (d == 128) hipLaunchKernelGGL((attn_finish<128, float, NC>), grid, block, 0, st, p); \
+        else if (d == 64 && dtype == 1) hipLaunchKernelGGL((attn_finish<64, uint16_t, NC>), grid, block, 0, st, p); \
+        else if (d == 64) hipLaunchKernelGGL((attn_finish<64, float, NC>), grid, block, 0, st, p); \
+        else return hipErrorInvalidValue; \
+        return hipGetLastError(); }
+    NECTAR_FINISH_CASE(2) NECTAR_FINISH_CASE(4) NECTAR_FINISH_CASE(8)
+#undef NECTAR_FINISH_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace nectar

@@ -279,6 +279,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
 // Those operands come straight from the key-major V stage by gfx950's
 // transposing LDS read (ds_read_b64_tr_b16, four keys' values of one dim per
 // lane and read; no register permutes): O^T row m of block mi is dim 32 mi + m.
+// This kernel's V stages place piece j of key r at position j ^ tr_swizzle(r),
+// so those reads are conflict-free too (K stages keep j ^ (r & 15)).  The
+// batch-64 decode layer's document pass: 369 -> 352 us.
 template <int NW, int kStageKeys>
 __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
     constexpr int kKeysPerWave = kStageKeys / NW;
@@ -342,17 +345,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
         for (int c = 0; c < kCopies; ++c) {
             const int r0 = kKeysPerWave * w + 4 * c, rr = r0 + (lane >> 4);
             const int key = min(key0 + rr, kmax);
-            const int piece = (lane & 15) ^ (rr & 15);
-            const size_t off = (size_t)key * kD + piece * 8;
-            __builtin_amdgcn_global_load_lds((const void *)(kb + off), (lds_void *)&dst[0][r0 * kPieces], 16, 0, kStreamPolicy);
-            __builtin_amdgcn_global_load_lds((const void *)(vb + off), (lds_void *)&dst[1][r0 * kPieces], 16, 0, kStreamPolicy);
+            // K rows swizzled by the key (conflict-free 16-byte reads), V rows by
+            // tr_swizzle (conflict-free transposing reads)
+            const size_t row = (size_t)key * kD;
+            const int kpiece = (lane & 15) ^ (rr & 15), vpiece = (lane & 15) ^ tr_swizzle(rr);
+            __builtin_amdgcn_global_load_lds((const void *)(kb + row + kpiece * 8), (lds_void *)&dst[0][r0 * kPieces], 16, 0, kStreamPolicy);
+            __builtin_amdgcn_global_load_lds((const void *)(vb + row + vpiece * 8), (lds_void *)&dst[1][r0 * kPieces], 16, 0, kStreamPolicy);
         }
     };
 
     // Byte offsets, within a 16-key block of a V stage, of the 8-byte slot this
     // lane names for the transposing read of key half `hh` and dim block mi:
     // key 8 hh + 4 (lane / 32) + (lane / 4) % 4, dims 32 mi + 16 ((lane / 16) % 2)
-    // + 4 (lane % 4) .. + 3 (the swizzled position of their 16-byte piece).
+    // + 4 (lane % 4) .. + 3 (their 16-byte piece at its tr_swizzle position).
     // Lane 32 h + m then receives dim 32 mi + m of keys 8 hh + 4 h + 0..3, the
     // contraction order of the P^T operand.
     uint32_t voff[2][4];
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
             for (int mi = 0; mi < 4; ++mi) {
                 const int key = 8 * hh + 4 * (G >> 1) + e;
                 const int piece = 4 * mi + 2 * (G & 1) + (aa >> 1);
-                voff[hh][mi] = (uint32_t)(key * kPieces * 16 + ((piece ^ key) * 16) + (aa & 1) * 8);
+                voff[hh][mi] = (uint32_t)(key * kPieces * 16 + ((piece ^ tr_swizzle(key)) * 16) + (aa & 1) * 8);
             }
     }
 

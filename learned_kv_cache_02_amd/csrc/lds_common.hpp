@@ -29,6 +29,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *base, uint32_t byte_o
     return __builtin_bit_cast(u32x2, v);
 }
 
+// Swizzle of stages read by transposing reads (lds_read_tr16).  Piece j of row r is
+// stored at position j ^ tr_swizzle(r).  A transposing read of four rows
+// 4k .. 4k + 3 and four consecutive pieces 4i .. 4i + 3 (two per 16-lane group)
+// then touches sixteen distinct positions, and any 16 lanes eight distinct
+// positions mod 8: every bank once per 256 bytes.  (With the plain r & 15 the
+// sixteen fall on four positions, a four-way bank conflict.)
+__device__ __forceinline__ int tr_swizzle(int r) { return ((r & 1) * 10) ^ ((r & 2) << 1) ^ ((r >> 2) & 1); }
+
 // Workgroup barrier that the compiler may not move memory operations across
 // (the bare builtin is not a memory barrier to the optimiser) and that adds
 // no waits of its own: the LDS copies are waited for explicitly above it.

@@ -8,8 +8,9 @@
 // per wave, and one range of hidden units; the units stream through a
 // three-stage LDS ring of 64-unit stages (first-layer rows, read-out rows,
 // biases and score weights), copied HBM -> LDS two stages ahead with every
-// 256-byte row's 16-byte pieces XOR-swizzled by the unit (conflict-free operand
-// reads).  Per 32-unit chunk a wave runs
+// 256-byte row's 16-byte pieces XOR-swizzled by the unit (first-layer rows:
+// by unit & 15; read-out rows: by tr_swizzle), so the operand reads are
+// conflict-free.  Per 32-unit chunk a wave runs
 //   Z^T (32 units x 32 rows) = b + sum over 8 slices of 16 dims of W1 . Q^T
 //       (the bias is the accumulator's initial value),
 //   H = act(Z), and for target chunks O^T (128 x 32) += W2t^T . H^T as
@@ -88,10 +89,12 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int r0 = 8 * w + 4 * c, rr = r0 + (lane >> 4);
-            const int piece = (lane & 15) ^ (rr & 15);
-            const size_t off = (size_t)(u0 + rr) * kD + piece * 8;
-            __builtin_amdgcn_global_load_lds((const void *)(Wa + off), (lds_void *)&dst.w1[r0 * kPieces], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(Wb + off), (lds_void *)&dst.w2[r0 * kPieces], 16, 0, 0);
+            // first-layer rows swizzled by the unit (16-byte reads), read-out rows
+            // by tr_swizzle (transposing reads)
+            const size_t row = (size_t)(u0 + rr) * kD;
+            const int piece1 = (lane & 15) ^ (rr & 15), piece2 = (lane & 15) ^ tr_swizzle(rr);
+            __builtin_amdgcn_global_load_lds((const void *)(Wa + row + piece1 * 8), (lds_void *)&dst.w1[r0 * kPieces], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(Wb + row + piece2 * 8), (lds_void *)&dst.w2[r0 * kPieces], 16, 0, 0);
         }
         if (w == 0) {
             // 64 biases = 16 pieces, 64 score weights = 8 pieces (score stages)
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
             for (int mi = 0; mi < 4; ++mi) {
                 const int u = 8 * hh + 4 * (G >> 1) + e;
                 const int piece = 4 * mi + 2 * (G & 1) + (aa >> 1);
-                woff[hh][mi] = (uint32_t)(u * kPieces * 16 + ((piece ^ u) * 16) + (aa & 1) * 8);
+                woff[hh][mi] = (uint32_t)(u * kPieces * 16 + ((piece ^ tr_swizzle(u)) * 16) + (aa & 1) * 8);
             }
     }
 
@@ -127,6 +130,58 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) O[mi] = f32x16{};
     float sc = 0.f;
+
+    // Chunk c of a stage: Z^T = b + W1 . Q^T (the bias as the accumulator's start) ...
+    auto preact = [&](const UnitStage &cur, int c) {
+        f32x16 Z;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // bias of the lane's 16 units 32c + 8q + 4hf + (0..3)
+            const f32x4 bq = *(const f32x4 *)&cur.b[32 * c + 8 * q + 4 * hf];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Z[4 * q + j] = bq[j];
+        }
+        const int ur = 32 * c + r;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) Z = mfma32(cur.w1[ur * kPieces + ((2 * kt + hf) ^ (ur & 15))], qv[kt], Z);
+        return Z;
+    };
+    // ... then H = act(Z) and its read-out
+    auto readout = [&](const UnitStage &cur, bool tgt, int c, const f32x16 &Z) {
+        float hv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) hv[j] = act(Z[j]);
+        if (tgt) {
+#pragma unroll
+            for (int tg = 0; tg < 2; ++tg) {
+                const u32x4 H = {pack_bf16(hv[8 * tg + 0], hv[8 * tg + 1]), pack_bf16(hv[8 * tg + 2], hv[8 * tg + 3]),
+                                 pack_bf16(hv[8 * tg + 4], hv[8 * tg + 5]), pack_bf16(hv[8 * tg + 6], hv[8 * tg + 7])};
+                // W2^T operand of dim block mi, straight from LDS by transposing reads
+                const char *ublk = (const char *)cur.w2 + (32 * c + 16 * tg) * (kPieces * 16);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const u32x2 h0 = lds_read_tr16(ublk, woff[0][mi]), h1 = lds_read_tr16(ublk, woff[1][mi]);
+                    O[mi] = mfma32(u32x4{h0.x, h0.y, h1.x, h1.y}, H, O[mi]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint2 wq = *(const uint2 *)&cur.ws2[32 * c + 8 * q + 4 * hf];
+                sc = __builtin_fmaf(bf16lo(wq.x), hv[4 * q + 0], sc);
+                sc = __builtin_fmaf(bf16hi(wq.x), hv[4 * q + 1], sc);
+                sc = __builtin_fmaf(bf16lo(wq.y), hv[4 * q + 2], sc);
+                sc = __builtin_fmaf(bf16hi(wq.y), hv[4 * q + 3], sc);
+            }
+        }
+    };
+    // The two waves of a SIMD (w and w + 4) take a stage's chunks in different
+    // orders -- the first half chunk by chunk, the second half both chunks'
+    // first-layer products first -- so one wave's activations (vector work)
+    // tend to meet the other's matrix products rather than both waves issuing
+    // the same kind of work after every barrier (rho = 10 % prefill MLP: 3.11
+    // -> 3.05 ms).  The sums run in the same order either way.
+    const bool skew = w >= kNW / 2;
 
     auto step = [&](int i, const UnitStage &cur, UnitStage &ahead) {
         // stage i has landed once at most the next stage's copies are pending
@@ -139,45 +194,13 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_rows_lds32(MlpParams a) {
         stage_barrier();
         if (i + 2 < nst) issue(i + 2, ahead);
         const bool tgt = i < ntg;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            // bias of the lane's 16 units 32c + 8q + 4hf + (0..3) as the accumulator's start
-            f32x16 Z;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 bq = *(const f32x4 *)&cur.b[32 * c + 8 * q + 4 * hf];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Z[4 * q + j] = bq[j];
-            }
-            const int ur = 32 * c + r;
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt) Z = mfma32(cur.w1[ur * kPieces + ((2 * kt + hf) ^ (ur & 15))], qv[kt], Z);
-            float hv[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) hv[j] = act(Z[j]);
-            if (tgt) {
-#pragma unroll
-                for (int tg = 0; tg < 2; ++tg) {
-                    const u32x4 H = {pack_bf16(hv[8 * tg + 0], hv[8 * tg + 1]), pack_bf16(hv[8 * tg + 2], hv[8 * tg + 3]),
-                                     pack_bf16(hv[8 * tg + 4], hv[8 * tg + 5]), pack_bf16(hv[8 * tg + 6], hv[8 * tg + 7])};
-                    // W2^T operand of dim block mi, straight from LDS by transposing reads
-                    const char *ublk = (const char *)cur.w2 + (32 * c + 16 * tg) * (kPieces * 16);
-#pragma unroll
-                    for (int mi = 0; mi < 4; ++mi) {
-                        const u32x2 h0 = lds_read_tr16(ublk, woff[0][mi]), h1 = lds_read_tr16(ublk, woff[1][mi]);
-                        O[mi] = mfma32(u32x4{h0.x, h0.y, h1.x, h1.y}, H, O[mi]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint2 wq = *(const uint2 *)&cur.ws2[32 * c + 8 * q + 4 * hf];
-                    sc = __builtin_fmaf(bf16lo(wq.x), hv[4 * q + 0], sc);
-                    sc = __builtin_fmaf(bf16hi(wq.x), hv[4 * q + 1], sc);
-                    sc = __builtin_fmaf(bf16lo(wq.y), hv[4 * q + 2], sc);
-                    sc = __builtin_fmaf(bf16hi(wq.y), hv[4 * q + 3], sc);
-                }
-            }
+        if (skew) {
+            const f32x16 Z0 = preact(cur, 0), Z1 = preact(cur, 1);
+            readout(cur, tgt, 0, Z0);
+            readout(cur, tgt, 1, Z1);
+        } else {
+            readout(cur, tgt, 0, preact(cur, 0));
+            readout(cur, tgt, 1, preact(cur, 1));
         }
     };
     if (nst > 0) issue(0, st_a);

@@ -18,8 +18,10 @@
 //    fp32 accumulators, the hidden tile rounded to bf16 and fed back as the B
 //    operand of O^T += W2t_tile^T . H^T (W2t rows transposed inside the lane);
 //    score hidden values stay fp32 and are dotted with ws2 on the VALU;
-//  * the block's four waves fold through LDS (one barrier) and the block writes
-//    one partial per row as whole rows (coalesced), or -- when one block covers
+//  * a block has four tile slots; at d = 128 with up to 64 rows two waves share
+//    a slot's tiles (staged in LDS) and take 32 rows each (eight waves, two per
+//    SIMD); the slots fold through LDS (one barrier) and the block writes one
+//    partial per row as whole rows (coalesced), or -- when one block covers
 //    every tile -- the outputs with their biases.
 #pragma once
 
@@ -111,10 +113,12 @@ template <int D, int RT, int NT> union DecLds {
     DecFold<D, RT> fold;
 };
 
-// Copy rows u0 .. u0 + 31 (clamped to umax) of W into LDS rows 0..31 at dst.
-__device__ __forceinline__ void stage_rows128(u32x4 *dst, const uint16_t *W, int u0, int umax, int lane) {
+// Copy rows u0 .. u0 + 31 (clamped to umax) of W into LDS rows 0..31 at dst:
+// eight copies of four rows; the wave takes copies i0, i0 + 1, ..., i0 + n - 1.
+__device__ __forceinline__ void stage_rows128(u32x4 *dst, const uint16_t *W, int u0, int umax, int lane, int i0 = 0,
+                                              int n = 8) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = i0; i < i0 + n; ++i) {
         const int rr = 4 * i + (lane >> 4);
         const int piece = (lane & 15) ^ (rr & 15);
         const uint16_t *src = W + (size_t)min(u0 + rr, umax) * 128 + piece * 8;
@@ -122,34 +126,50 @@ __device__ __forceinline__ void stage_rows128(u32x4 *dst, const uint16_t *W, int
     }
 }
 
-// MFMA operands of one tile from its LDS rows (the layout of load_rows / load_tgt).
-__device__ __forceinline__ void lds_rows128(MTile<128> &T, const u32x4 *rows, int g, int c) {
+// MFMA operands of one tile from its LDS rows (the layout of load_rows /
+// load_tgt); d = 128 only (the d = 64 kernels load tiles into registers).
+template <int D> __device__ __forceinline__ void lds_rows128(MTile<D> &T, const u32x4 *rows, int g, int c) {
+    if constexpr (D == 128) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const int r = 16 * hh + c;
-            T.w1[hh][kt] = rows[r * 16 + ((4 * kt + g) ^ (r & 15))];
-        }
+            for (int kt = 0; kt < 4; ++kt) {
+                const int r = 16 * hh + c;
+                T.w1[hh][kt] = rows[r * 16 + ((4 * kt + g) ^ (r & 15))];
+            }
+    }
 }
-__device__ __forceinline__ void lds_w2_128(MTile<128> &T, const u32x4 *rows, int g, int c) {
+template <int D> __device__ __forceinline__ void lds_w2_128(MTile<D> &T, const u32x4 *rows, int g, int c) {
+    if constexpr (D == 128) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = hslot(g, j);
-        T.w2[j] = rows[r * 16 + (c ^ (r & 15))];
+        for (int j = 0; j < 8; ++j) {
+            const int r = hslot(g, j);
+            T.w2[j] = rows[r * 16 + (c ^ (r & 15))];
+        }
     }
 }
 
-// Block blk_id of the grid Hkv x RG x SB (blocks of 4 waves).  Wave w of block
-// sb of (KV head h, row group rg) is wave i = 4 sb + w of that group: target
-// wave i < nwt, score wave i - nwt < nws, idle otherwise.
+// Waves per tile slot: at d = 128 with four 16-row tiles (up to 64 rows per KV
+// head) two waves share each slot's weight tiles in LDS and take 32 rows each,
+// so a block has eight waves, two per SIMD, each with half the registers of a
+// 64-row wave; one wave per slot otherwise (at d = 64 the tiles sit in
+// registers, and a second wave would read them again).
+template <int D, int RT> constexpr int dec_wps() { return D == 128 && RT == 4 ? 2 : 1; }
+template <int D, int RT> constexpr int dec_threads() { return 256 * dec_wps<D, RT>(); }
+
+// Block blk_id of the grid Hkv x RG x SB (blocks of 4 tile slots, WPS waves
+// each: wave v takes slot v % 4 and row tiles (v / 4) * RT / WPS ...).  Slot w
+// of block sb of (KV head h, row group rg) is slot i = 4 sb + w of that group:
+// target slot i < nwt, score slot i - nwt < nws, idle otherwise.
 template <int D, int RT, int ACT, int NT>
 __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) {
     constexpr int KS = D / 32, DV = D / 16;
+    constexpr int WPS = dec_wps<D, RT>(), RTW = RT / WPS;   // waves per slot, row tiles per wave
     __shared__ DecLds<D, RT, NT> lds;
     DecFold<D, RT> &fold = lds.fold;
 
-    const int w = threadIdx.x >> 6;
+    const int v = threadIdx.x >> 6;
+    const int w = v & 3, part = v >> 2;       // tile slot, row part of this wave
     int blk = blk_id;
     const int sb = blk % a.SB;
     blk /= a.SB;
@@ -157,156 +177,185 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
     const int h = blk / a.RG;
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     const int wi = 4 * sb + w;
+    const int rt0 = part * RTW;                // first row tile of this wave within the block's RT
 
-    f32x4 O[RT][DV];
-    float sc[RT];
+    f32x4 O[RTW][DV];
+    float sc[RTW];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RTW; ++rt) {
         sc[rt] = 0.f;
 #pragma unroll
         for (int mm = 0; mm < DV; ++mm) O[rt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const bool tgt = wi < a.nwt, scw = !tgt && wi < a.nwt + a.nws;
-    if (tgt || scw) {
-        u32x4 qv[RT][KS];
+    u32x4 qv[RTW][KS];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int rho = (rg * RT + rt) * 16 + c;
-            if (rho < a.Rp) {
-                const int t = rho / a.G, gg = rho - t * a.G;
-                const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.Hq + h * a.G + gg) * D;
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int rho = (rg * RT + rt0 + rt) * 16 + c;
+        if ((tgt || scw) && rho < a.Rp) {
+            const int t = rho / a.G, gg = rho - t * a.G;
+            const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.Hq + h * a.G + gg) * D;
 #pragma unroll
-                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-        if (tgt) {
-            const int Tt = (a.Ht + 31) / 32;
-            const int t0 = (int)((long)wi * Tt / a.nwt), n = (int)((long)(wi + 1) * Tt / a.nwt) - t0;
-            const uint16_t *W1 = (const uint16_t *)a.W1 + (size_t)h * a.Ht * D;
-            const uint16_t *W2t = (const uint16_t *)a.W2t + (size_t)h * a.Ht * D;
-            const float *b1 = a.b1 + (size_t)h * a.Ht;
-            if constexpr (D == 128) {
-                u32x4 *buf = lds.tiles[w];
-                float bias[NT][8];
-#pragma unroll
-                for (int k = 0; k < NT; ++k) {
-                    const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
-                    stage_rows128(buf + k * 1024, W1, u0, a.Ht - 1, lane);
-                    stage_rows128(buf + k * 1024 + 512, W2t, u0, a.Ht - 1, lane);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) bias[k][j] = b1[min(u0 + hslot(g, j), a.Ht - 1)];
-                }
-                wait_vmcnt<0>();
-                asm volatile("" ::: "memory");   // the copies landed: LDS reads stay below
-#pragma unroll
-                for (int k = 0; k < NT; ++k)
-                    if (k < n) {
-                        MTile<D> T;
-                        lds_rows128(T, buf + k * 1024, g, c);
-                        lds_w2_128(T, buf + k * 1024 + 512, g, c);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) T.bias[j] = bias[k][j];
-                        dec_tgt_tile<D, RT, ACT>(T, 32 * (t0 + k), a.Ht, qv, g, O);
-                    }
-            } else {
-                MTile<D> T[NT];
-#pragma unroll
-                for (int k = 0; k < NT; ++k)
-                    load_tgt<D>(T[k], W1, W2t, b1, 32 * (t0 + max(min(k, n - 1), 0)), a.Ht - 1, g, c);
-#pragma unroll
-                for (int k = 0; k < NT; ++k)
-                    if (k < n) dec_tgt_tile<D, RT, ACT>(T[k], 32 * (t0 + k), a.Ht, qv, g, O);
-            }
+            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
         } else {
-            const int si = wi - a.nwt, Ts = (a.Hs + 31) / 32;
-            const int t0 = (int)((long)si * Ts / a.nws), n = (int)((long)(si + 1) * Ts / a.nws) - t0;
-            const uint16_t *Ws = (const uint16_t *)a.Ws + (size_t)h * a.Hs * D;
-            const uint16_t *ws2 = (const uint16_t *)a.ws2 + (size_t)h * a.Hs;
-            const float *bs = a.bs + (size_t)h * a.Hs;
-            if constexpr (D == 128) {
-                u32x4 *buf = lds.tiles[w];
-                float bias[2 * NT][8], wsv[2 * NT][8];
 #pragma unroll
-                for (int k = 0; k < 2 * NT; ++k) {
-                    const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
-                    stage_rows128(buf + k * 512, Ws, u0, a.Hs - 1, lane);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int u = min(u0 + hslot(g, j), a.Hs - 1);
-                        bias[k][j] = bs[u];
-                        wsv[k][j] = bf16_to_f32(ws2[u]);
-                    }
-                }
-                wait_vmcnt<0>();
-                asm volatile("" ::: "memory");   // the copies landed: LDS reads stay below
-#pragma unroll
-                for (int k = 0; k < 2 * NT; ++k)
-                    if (k < n) {
-                        MTile<D> T;
-                        lds_rows128(T, buf + k * 512, g, c);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            T.bias[j] = bias[k][j];
-                            T.ws[j] = wsv[k][j];
-                        }
-                        dec_score_tile<D, RT, ACT>(T, 32 * (t0 + k), a.Hs, qv, g, sc);
-                    }
-            } else {
-                MTile<D> T[2 * NT];
-#pragma unroll
-                for (int k = 0; k < 2 * NT; ++k)
-                    load_score<D>(T[k], Ws, ws2, bs, 32 * (t0 + max(min(k, n - 1), 0)), a.Hs - 1, g, c);
-#pragma unroll
-                for (int k = 0; k < 2 * NT; ++k)
-                    if (k < n) dec_score_tile<D, RT, ACT>(T[k], 32 * (t0 + k), a.Hs, qv, g, sc);
-            }
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) sc[rt] = group4_sum(sc[rt]);
+            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
         }
     }
+    // this slot's tile range
+    const int Tt = (a.Ht + 31) / 32, Ts = (a.Hs + 31) / 32;
+    const int si = wi - a.nwt;
+    const int t0 = tgt ? (int)((long)wi * Tt / a.nwt) : (scw ? (int)((long)si * Ts / a.nws) : 0);
+    const int n = tgt ? (int)((long)(wi + 1) * Tt / a.nwt) - t0 : (scw ? (int)((long)(si + 1) * Ts / a.nws) - t0 : 0);
+    const uint16_t *W1 = (const uint16_t *)a.W1 + (size_t)h * a.Ht * D;
+    const uint16_t *W2t = (const uint16_t *)a.W2t + (size_t)h * a.Ht * D;
+    const float *b1 = a.b1 + (size_t)h * a.Ht;
+    const uint16_t *Ws = (const uint16_t *)a.Ws + (size_t)h * a.Hs * D;
+    const uint16_t *ws2 = (const uint16_t *)a.ws2 + (size_t)h * a.Hs;
+    const float *bs = a.bs + (size_t)h * a.Hs;
 
-    // fold the four waves: every wave stores its rows (in the LDS the tiles
+    // d = 128: the slot's weight rows are staged in LDS (lds.tiles[w]), every
+    // copy and bias load first, then one wait before the first product.
+    u32x4 *buf = lds.tiles[w];
+    auto tgt_issue = [&](auto &bias, int i0, int ni) {
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
+            stage_rows128(buf + k * 1024, W1, u0, a.Ht - 1, lane, i0, ni);
+            stage_rows128(buf + k * 1024 + 512, W2t, u0, a.Ht - 1, lane, i0, ni);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bias[k][j] = b1[min(u0 + hslot(g, j), a.Ht - 1)];
+        }
+    };
+    auto tgt_compute = [&](const auto &bias) {
+#pragma unroll
+        for (int k = 0; k < NT; ++k)
+            if (k < n) {
+                MTile<D> T;
+                lds_rows128(T, buf + k * 1024, g, c);
+                lds_w2_128(T, buf + k * 1024 + 512, g, c);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) T.bias[j] = bias[k][j];
+                dec_tgt_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Ht, qv, g, O);
+            }
+    };
+    auto sc_issue = [&](auto &bias, auto &wsv, int i0, int ni) {
+#pragma unroll
+        for (int k = 0; k < 2 * NT; ++k) {
+            const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
+            stage_rows128(buf + k * 512, Ws, u0, a.Hs - 1, lane, i0, ni);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int u = min(u0 + hslot(g, j), a.Hs - 1);
+                bias[k][j] = bs[u];
+                wsv[k][j] = bf16_to_f32(ws2[u]);
+            }
+        }
+    };
+    auto sc_compute = [&](const auto &bias, const auto &wsv) {
+#pragma unroll
+        for (int k = 0; k < 2 * NT; ++k)
+            if (k < n) {
+                MTile<D> T;
+                lds_rows128(T, buf + k * 512, g, c);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    T.bias[j] = bias[k][j];
+                    T.ws[j] = wsv[k][j];
+                }
+                dec_score_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Hs, qv, g, sc);
+            }
+    };
+    if constexpr (D == 128 && WPS > 1) {
+        // two waves per slot share the copies (four of the eight per 32-row
+        // table each); a block barrier, taken by every wave (idle ones too),
+        // makes the other wave's copies visible before the first product
+        constexpr int CI = 8 / WPS;
+        float tb[NT][8], sbias[2 * NT][8], swsv[2 * NT][8];
+        if (tgt) tgt_issue(tb, part * CI, CI);
+        else if (scw) sc_issue(sbias, swsv, part * CI, CI);
+        wait_vmcnt<0>();
+        stage_barrier();
+        asm volatile("" ::: "memory");   // the copies landed: LDS reads stay below
+        if (tgt) tgt_compute(tb);
+        else if (scw) sc_compute(sbias, swsv);
+    } else if constexpr (D == 128) {
+        if (tgt) {
+            float tb[NT][8];
+            tgt_issue(tb, 0, 8);
+            wait_vmcnt<0>();
+            asm volatile("" ::: "memory");   // the copies landed: LDS reads stay below
+            tgt_compute(tb);
+        } else if (scw) {
+            float sbias[2 * NT][8], swsv[2 * NT][8];
+            sc_issue(sbias, swsv, 0, 8);
+            wait_vmcnt<0>();
+            asm volatile("" ::: "memory");
+            sc_compute(sbias, swsv);
+        }
+    } else {
+        if (tgt) {
+            MTile<D> T[NT];
+#pragma unroll
+            for (int k = 0; k < NT; ++k)
+                load_tgt<D>(T[k], W1, W2t, b1, 32 * (t0 + max(min(k, n - 1), 0)), a.Ht - 1, g, c);
+#pragma unroll
+            for (int k = 0; k < NT; ++k)
+                if (k < n) dec_tgt_tile<D, RTW, ACT>(T[k], 32 * (t0 + k), a.Ht, qv, g, O);
+        } else if (scw) {
+            MTile<D> T[2 * NT];
+#pragma unroll
+            for (int k = 0; k < 2 * NT; ++k)
+                load_score<D>(T[k], Ws, ws2, bs, 32 * (t0 + max(min(k, n - 1), 0)), a.Hs - 1, g, c);
+#pragma unroll
+            for (int k = 0; k < 2 * NT; ++k)
+                if (k < n) dec_score_tile<D, RTW, ACT>(T[k], 32 * (t0 + k), a.Hs, qv, g, sc);
+        }
+    }
+    if (scw) {
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) sc[rt] = group4_sum(sc[rt]);
+    }
+
+    // fold the four slots: every wave stores its rows (in the LDS the tiles
     // used, once every wave is past them), one barrier, then the block's
     // threads sum the four and write whole rows
     constexpr int LD = DecFold<D, RT>::LD, ROWS = DecFold<D, RT>::ROWS;
     if constexpr (D == 128) stage_barrier();
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        float *op = fold.O[w] + (rt * 16 + c) * LD;
+    for (int rt = 0; rt < RTW; ++rt) {
+        float *op = fold.O[w] + ((rt0 + rt) * 16 + c) * LD;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int m4 = 0; m4 < DV; m4 += 4)
                 *(f32x4 *)(op + DV * (4 * g + r) + m4) = f32x4{O[rt][m4][r], O[rt][m4 + 1][r], O[rt][m4 + 2][r],
                                                               O[rt][m4 + 3][r]};
-        if (g == 0) fold.s[w][rt * 16 + c] = sc[rt];
+        if (g == 0) fold.s[w][(rt0 + rt) * 16 + c] = sc[rt];
     }
     __syncthreads();
     const bool direct = a.SB == 1 && !a.defer;
-    constexpr int CPR = D / 4;                // float4 columns per row
-    constexpr int RPI = 256 / CPR;            // rows per pass of the block
+    constexpr int CPR = D / 4;                       // float4 columns per row
+    constexpr int RPI = dec_threads<D, RT>() / CPR;  // rows per pass of the block
     const int col = (threadIdx.x % CPR) * 4;
 #pragma unroll
     for (int r0 = 0; r0 < ROWS; r0 += RPI) {
         const int rr = r0 + (int)threadIdx.x / CPR;
         const int rho = rg * ROWS + rr;
         if (rr >= ROWS || rho >= a.Rp) continue;
-        f32x4 v = *(const f32x4 *)(fold.O[0] + rr * LD + col);
+        f32x4 v4 = *(const f32x4 *)(fold.O[0] + rr * LD + col);
 #pragma unroll
-        for (int k = 1; k < 4; ++k) v += *(const f32x4 *)(fold.O[k] + rr * LD + col);
+        for (int k = 1; k < 4; ++k) v4 += *(const f32x4 *)(fold.O[k] + rr * LD + col);
         const bool lead = col == 0;
         const float s = lead ? ((fold.s[0][rr] + fold.s[1][rr]) + (fold.s[2][rr] + fold.s[3][rr])) : 0.f;
         if (direct) {
             const int t = rho / a.G, gg = rho - t * a.G;
             const size_t o = (size_t)t * a.Hq + h * a.G + gg;
-            *(f32x4 *)(a.A_out + o * D + col) = v + *(const f32x4 *)(a.b2 + (size_t)h * D + col);
+            *(f32x4 *)(a.A_out + o * D + col) = v4 + *(const f32x4 *)(a.b2 + (size_t)h * D + col);
             if (lead) a.a_out[o] = a.bs2[h] + s;
         } else {
             const size_t row = (size_t)(h * a.SB + sb) * a.Rp + rho;
-            *(f32x4 *)(a.part_O + row * D + col) = v;
+            *(f32x4 *)(a.part_O + row * D + col) = v4;
             if (lead) a.part_s[row] = s;
         }
     }

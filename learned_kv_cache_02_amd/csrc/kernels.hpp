@@ -85,9 +85,12 @@ struct MlpParams {
     int nwt, nws;
 };
 
-// Largest number of 32-unit target tiles a wave of the decode MLP kernel
-// holds (a score wave holds twice as many score tiles).
+// Largest number of 32-unit target tiles a wave (tile slot) of the decode MLP
+// kernel holds; a score slot holds up to dec_score_tiles(rt) score tiles (a
+// score tile streams half the bytes of a target tile: twice as many with one
+// 16-row tile, as many with more rows, where the activations dominate).
 constexpr int kDecTiles = 2;
+constexpr int dec_score_tiles(int rt) { return kDecTiles * (rt > 1 ? 1 : 2); }
 
 // One layer of the deep MLP module (Eq. (3.6)) for every KV head p and row rho
 // of its Rp = R * G query rows:

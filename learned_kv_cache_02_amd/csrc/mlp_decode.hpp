@@ -10,9 +10,9 @@
 //    and ws2); the host sizes both wave sets so every wave reads about the
 //    same number of bytes (a target tile is 16 KB at d = 128, a score tile
 //    8 KB, so score waves take up to twice as many tiles);
-//  * a wave issues the loads of all its tiles (at most NT target or 2 NT score
-//    tiles, indices clamped to its range) before its first product, in
-//    straight-line code, so every wait is for exactly the tile in use;
+//  * a wave issues the loads of all its tiles (at most NT target or
+//    dec_score_tiles(RT) score tiles, indices clamped to its range) before its
+//    first product, in straight-line code;
 //  * products as in the register-direct kernel: Z^T = W1_tile . Q^T on the
 //    16x16x32 MFMA with the query rows as B columns, bias + activation on the
 //    fp32 accumulators, the hidden tile rounded to bf16 and fed back as the B
@@ -104,7 +104,7 @@ template <int D, int RT> struct DecFold {
 
 // d = 128: a wave's weight rows are copied HBM -> LDS (global_load_lds, whole
 // 256-byte rows, four rows per copy) into its own region -- NT target tiles of
-// [W1 rows | W2t rows] or 2 NT score tiles of Ws rows, 16 KB per target tile --
+// [W1 rows | W2t rows] or up to 2 NT score tiles of Ws rows, 16 KB per target tile --
 // with the sixteen 16-byte pieces of row r stored at piece ^ (r % 16), so the
 // operand reads of sixteen rows fall in distinct banks.  The fold reuses the
 // same LDS after a barrier.
@@ -165,6 +165,7 @@ template <int D, int RT, int ACT, int NT>
 __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) {
     constexpr int KS = D / 32, DV = D / 16;
     constexpr int WPS = dec_wps<D, RT>(), RTW = RT / WPS;   // waves per slot, row tiles per wave
+    constexpr int NS = dec_score_tiles(RT);                 // score tiles per score slot
     __shared__ DecLds<D, RT, NT> lds;
     DecFold<D, RT> &fold = lds.fold;
 
@@ -217,81 +218,126 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
     // d = 128: the slot's weight rows are staged in LDS (lds.tiles[w]), every
     // copy and bias load first, then one wait before the first product.
     u32x4 *buf = lds.tiles[w];
-    auto tgt_issue = [&](auto &bias, int i0, int ni) {
+    auto tgt_bias = [&](auto &bias) {
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bias[k][j] = b1[min(u0 + hslot(g, j), a.Ht - 1)];
+        }
+    };
+    auto tgt_copies = [&](int i0, int ni) {
 #pragma unroll
         for (int k = 0; k < NT; ++k) {
             const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
             stage_rows128(buf + k * 1024, W1, u0, a.Ht - 1, lane, i0, ni);
             stage_rows128(buf + k * 1024 + 512, W2t, u0, a.Ht - 1, lane, i0, ni);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bias[k][j] = b1[min(u0 + hslot(g, j), a.Ht - 1)];
         }
     };
-    auto tgt_compute = [&](const auto &bias) {
+    auto tgt_tile = [&](const auto &bias, int k) {
+        MTile<D> T;
+        lds_rows128(T, buf + k * 1024, g, c);
+        lds_w2_128(T, buf + k * 1024 + 512, g, c);
 #pragma unroll
-        for (int k = 0; k < NT; ++k)
-            if (k < n) {
-                MTile<D> T;
-                lds_rows128(T, buf + k * 1024, g, c);
-                lds_w2_128(T, buf + k * 1024 + 512, g, c);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) T.bias[j] = bias[k][j];
-                dec_tgt_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Ht, qv, g, O);
-            }
+        for (int j = 0; j < 8; ++j) T.bias[j] = bias[k][j];
+        dec_tgt_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Ht, qv, g, O);
     };
-    auto sc_issue = [&](auto &bias, auto &wsv, int i0, int ni) {
+    auto sc_bias = [&](auto &bias, auto &wsv) {
 #pragma unroll
-        for (int k = 0; k < 2 * NT; ++k) {
+        for (int k = 0; k < NS; ++k) {
             const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
-            stage_rows128(buf + k * 512, Ws, u0, a.Hs - 1, lane, i0, ni);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int u = min(u0 + hslot(g, j), a.Hs - 1);
                 bias[k][j] = bs[u];
-                wsv[k][j] = bf16_to_f32(ws2[u]);
+                wsv[k][j] = ws2[u];            // bf16 bits, widened at use (no wait here)
             }
         }
     };
-    auto sc_compute = [&](const auto &bias, const auto &wsv) {
+    auto sc_copies = [&](int i0, int ni) {
 #pragma unroll
-        for (int k = 0; k < 2 * NT; ++k)
-            if (k < n) {
-                MTile<D> T;
-                lds_rows128(T, buf + k * 512, g, c);
+        for (int k = 0; k < NS; ++k) {
+            const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
+            stage_rows128(buf + k * 512, Ws, u0, a.Hs - 1, lane, i0, ni);
+        }
+    };
+    auto sc_tile = [&](const auto &bias, const auto &wsv, int k) {
+        MTile<D> T;
+        lds_rows128(T, buf + k * 512, g, c);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    T.bias[j] = bias[k][j];
-                    T.ws[j] = wsv[k][j];
-                }
-                dec_score_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Hs, qv, g, sc);
-            }
+        for (int j = 0; j < 8; ++j) {
+            T.bias[j] = bias[k][j];
+            T.ws[j] = __uint_as_float(wsv[k][j] << 16);
+        }
+        dec_score_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Hs, qv, g, sc);
     };
     if constexpr (D == 128 && WPS > 1) {
-        // two waves per slot share the copies (four of the eight per 32-row
-        // table each); a block barrier, taken by every wave (idle ones too),
-        // makes the other wave's copies visible before the first product
+        // Two waves per slot share the copies (four of the eight per 32-row
+        // table each).  Loads complete in the order issued.  Target slots load
+        // their biases, then tile 0's copies, then tile 1's: once at most tile
+        // 1's copies are pending, tile 0 has landed, and its products run while
+        // tile 1 is still in flight.  Score slots issue their copies first and
+        // their biases and read-out weights after (those are widened from bf16
+        // as they arrive, which waits for everything issued before): at most CI
+        // pending operations are then bias loads, every copy has landed.  A
+        // block barrier per tile (every wave takes the same two, idle ones too)
+        // makes the other wave's half of the copies visible.
+        static_assert(NT == 2 && NS == 2, "two tiles per slot, one barrier each");
         constexpr int CI = 8 / WPS;
-        float tb[NT][8], sbias[2 * NT][8], swsv[2 * NT][8];
-        if (tgt) tgt_issue(tb, part * CI, CI);
-        else if (scw) sc_issue(sbias, swsv, part * CI, CI);
-        wait_vmcnt<0>();
-        stage_barrier();
-        asm volatile("" ::: "memory");   // the copies landed: LDS reads stay below
-        if (tgt) tgt_compute(tb);
-        else if (scw) sc_compute(sbias, swsv);
+        // each role runs its whole sequence in its own branch, so the
+        // compiler's wait analysis sees straight-line code (a join before the
+        // products would make it wait for every load)
+        if (tgt) {
+            float tb[NT][8];
+            tgt_bias(tb);
+            asm volatile("" ::: "memory");   // the bias loads stay ahead of the copies
+            tgt_copies(part * CI, CI);
+            wait_vmcnt<2 * CI>();            // tile 1's copies of both tables may be pending
+            stage_barrier();
+            asm volatile("" ::: "memory");   // tile 0's LDS reads stay below
+            if (n > 0) tgt_tile(tb, 0);
+            wait_vmcnt<0>();
+            stage_barrier();
+            asm volatile("" ::: "memory");
+            if (n > 1) tgt_tile(tb, 1);
+        } else if (scw) {
+            float sbias[NS][8];
+            uint32_t swsv[NS][8];
+            sc_copies(part * CI, CI);
+            asm volatile("" ::: "memory");
+            sc_bias(sbias, swsv);
+            wait_vmcnt<CI>();
+            stage_barrier();
+            asm volatile("" ::: "memory");
+            if (n > 0) sc_tile(sbias, swsv, 0);
+            wait_vmcnt<0>();
+            stage_barrier();
+            asm volatile("" ::: "memory");
+            if (n > 1) sc_tile(sbias, swsv, 1);
+        } else {
+            stage_barrier();
+            stage_barrier();
+        }
     } else if constexpr (D == 128) {
         if (tgt) {
             float tb[NT][8];
-            tgt_issue(tb, 0, 8);
+            tgt_bias(tb);
+            tgt_copies(0, 8);
             wait_vmcnt<0>();
             asm volatile("" ::: "memory");   // the copies landed: LDS reads stay below
-            tgt_compute(tb);
+#pragma unroll
+            for (int k = 0; k < NT; ++k)
+                if (k < n) tgt_tile(tb, k);
         } else if (scw) {
-            float sbias[2 * NT][8], swsv[2 * NT][8];
-            sc_issue(sbias, swsv, 0, 8);
+            float sbias[NS][8];
+            uint32_t swsv[NS][8];
+            sc_bias(sbias, swsv);
+            sc_copies(0, 8);
             wait_vmcnt<0>();
             asm volatile("" ::: "memory");
-            sc_compute(sbias, swsv);
+#pragma unroll
+            for (int k = 0; k < NS; ++k)
+                if (k < n) sc_tile(sbias, swsv, k);
         }
     } else {
         if (tgt) {
@@ -303,12 +349,12 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
             for (int k = 0; k < NT; ++k)
                 if (k < n) dec_tgt_tile<D, RTW, ACT>(T[k], 32 * (t0 + k), a.Ht, qv, g, O);
         } else if (scw) {
-            MTile<D> T[2 * NT];
+            MTile<D> T[NS];
 #pragma unroll
-            for (int k = 0; k < 2 * NT; ++k)
+            for (int k = 0; k < NS; ++k)
                 load_score<D>(T[k], Ws, ws2, bs, 32 * (t0 + max(min(k, n - 1), 0)), a.Hs - 1, g, c);
 #pragma unroll
-            for (int k = 0; k < 2 * NT; ++k)
+            for (int k = 0; k < NS; ++k)
                 if (k < n) dec_score_tile<D, RTW, ACT>(T[k], 32 * (t0 + k), a.Hs, qv, g, sc);
         }
     }

@@ -235,8 +235,8 @@ MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs, long target_waves = 
         // decode kernel: per (KV head, row group) Wt target waves and Ws score
         // waves, sized so every wave reads about the same number of bytes (a
         // target tile streams twice the bytes of a score tile) and holds at most
-        // kDecTiles target or 2 kDecTiles score tiles; target_waves is the wave
-        // budget of the launch
+        // kDecTiles target or dec_score_tiles(RT) score tiles; target_waves is
+        // the wave budget of the launch
         pl.dec = true;
         pl.RT = mlp_row_tiles(pl.Rp);
         pl.RG = pl.RB = (int)cdiv(pl.Rp, 16L * pl.RT);
@@ -245,10 +245,7 @@ MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs, long target_waves = 
         const long per = (long)d->Hkv * pl.RG;
         const long Wa = std::max(1L, d->splits > 0 ? (long)d->splits : cdiv(target_waves, per));
         auto clampl = [](long x, long lo, long hi) { return std::min(std::max(x, lo), hi); };
-#ifndef NECTAR_DEC_SCORE_CAP
-#define NECTAR_DEC_SCORE_CAP 1
-#endif
-        const long smax = kDecTiles * (pl.RT > 1 ? NECTAR_DEC_SCORE_CAP : 2);   // score tiles per wave
+        const long smax = dec_score_tiles(pl.RT);   // score tiles per wave
         long Wt = 0, Ws = 0;
         if (tt > 0 && ts > 0) {
             Wt = clampl(std::lround((double)Wa * 2.0 * tt / (2.0 * tt + ts)), cdiv(tt, kDecTiles), tt);

@@ -162,21 +162,20 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + fast_exp2(v));
 }
 
-// erf-form GELU for the VALU-bound batched MLP kernels: x * Phi(x) with
-// Phi(x) = 0.5 + c P(c^2), c = x clamped to [-4, 4], P of degree 7 fitted to
-// the odd part of Phi (fit_gelu_erf.py): max |Phi error| 5.3e-5, so |GELU
-// error| <= 5.3e-5 |x|.  Eleven multiply-add-class operations, no exponential
-// or reciprocal (four issue slots each on this part).
+// erf-form GELU for the VALU-bound batched and decode MLP kernels: x * Phi(x)
+// with Phi(x) = 0.5 + c P(c^2), c = x clamped to [-3.71875, 3.71875], P of
+// degree 6 fitted to the odd part of Phi (fit_gelu_erf.py): max |Phi error|
+// 5.2e-5, so |GELU error| <= 5.2e-5 |x|.  Ten multiply-add-class operations, no
+// exponential or reciprocal (four issue slots each on this part).
 __device__ __forceinline__ float gelu_erf_poly(float x) {
-    const float c = __builtin_amdgcn_fmed3f(x, -4.0f, 4.0f);
+    const float c = __builtin_amdgcn_fmed3f(x, -3.71875f, 3.71875f);
     const float u = c * c;
-    float p = __builtin_fmaf(u, -1.58076696e-09f, 1.21709988e-07f);
-    p = __builtin_fmaf(p, u, -4.10084021e-06f);
-    p = __builtin_fmaf(p, u, 8.06670869e-05f);
-    p = __builtin_fmaf(p, u, -1.04820251e-03f);
-    p = __builtin_fmaf(p, u, 9.66486800e-03f);
-    p = __builtin_fmaf(p, u, -6.61753714e-02f);
-    p = __builtin_fmaf(p, u, 3.98847520e-01f);
+    float p = __builtin_fmaf(u, 4.07418810e-08f, -2.44288435e-06f);
+    p = __builtin_fmaf(p, u, 6.33929594e-05f);
+    p = __builtin_fmaf(p, u, -9.51952359e-04f);
+    p = __builtin_fmaf(p, u, 9.39021632e-03f);
+    p = __builtin_fmaf(p, u, -6.58312142e-02f);
+    p = __builtin_fmaf(p, u, 3.98723632e-01f);
     return x * __builtin_fmaf(c, p, 0.5f);
 }
 

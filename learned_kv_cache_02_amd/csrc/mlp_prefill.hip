@@ -18,8 +18,8 @@
 // so the hidden activations never leave registers; score chunks run
 //   Zs^T = bs + Ws_chunk . Q^T -> act -> fp32 dot with ws2.
 //
-// The erf-form GELU is evaluated as x * (0.5 + c P(c^2)), c = clamp(x, -4, 4)
-// (gelu_erf_poly).
+// The erf-form GELU is evaluated as x * (0.5 + c P(c^2)), c = x clamped to
+// [-3.71875, 3.71875], P of degree 6 (gelu_erf_poly).
 // With one split (SB == 1) the block adds the output biases and writes (a, A);
 // with SB > 1 splits of the hidden units, block (h, row block, split) writes its
 // partial sums and mlp_reduce adds them in split order with the biases.

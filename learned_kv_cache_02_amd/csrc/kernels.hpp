@@ -91,6 +91,21 @@ struct MlpParams {
 // 16-row tile, as many with more rows, where the activations dominate).
 constexpr int kDecTiles = 2;
 constexpr int dec_score_tiles(int rt) { return kDecTiles * (rt > 1 ? 1 : 2); }
+// Waves per tile slot and tile slots per block of the decode MLP kernel: at
+// d = 128 with four 16-row tiles (up to 64 rows per KV head) two waves share a
+// slot's weight tiles in LDS and take 32 rows each, and a block holds
+// NECTAR_DEC_SLOTS_PAIRED slots; otherwise one wave per slot and four slots.
+// (Two paired slots per block -- 256 blocks at the 1M-token layer -- measured
+// slower: twice the partials, and beside the local blocks a second round of
+// blocks; 1M-token Nectar path 17.55 -> 23.4 us.)
+#ifndef NECTAR_DEC_SLOTS_PAIRED
+#define NECTAR_DEC_SLOTS_PAIRED 4
+#endif
+constexpr int dec_wps(int d, int rt) { return d == 128 && rt == 4 ? 2 : 1; }
+constexpr int dec_slots(int d, int rt) { return dec_wps(d, rt) > 1 ? NECTAR_DEC_SLOTS_PAIRED : 4; }
+constexpr int dec_threads(int d, int rt) { return 64 * dec_slots(d, rt) * dec_wps(d, rt); }
+// blocks per compute unit the paired kernels are compiled for (two waves per SIMD)
+constexpr int dec_min_blocks(int d, int rt) { return dec_wps(d, rt) > 1 ? 8 / (dec_slots(d, rt) * dec_wps(d, rt)) : 1; }
 
 // One layer of the deep MLP module (Eq. (3.6)) for every KV head p and row rho
 // of its Rp = R * G query rows:

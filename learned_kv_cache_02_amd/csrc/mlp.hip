@@ -24,7 +24,7 @@ namespace nectar {
 // Decode shapes (up to 64 rows per KV head): target and score waves, every
 // tile load issued up front, block fold through LDS (mlp_decode.hpp).
 template <int D, int RT, int ACT>
-__global__ __launch_bounds__((dec_threads<D, RT>()), 1) void mlp_decode_mfma(MlpParams a) {
+__global__ __launch_bounds__((dec_threads(D, RT)), (dec_min_blocks(D, RT))) void mlp_decode_mfma(MlpParams a) {
     mlp_decode_body<D, RT, ACT, kDecTiles>(a, (int)blockIdx.x);
 }
 
@@ -151,7 +151,7 @@ hipError_t launch_mlp_decode(const MlpParams &p, int d, int rt, hipStream_t st) 
     dim3 grid((unsigned)((long)p.Hkv * p.RG * p.SB));
 #define NECTAR_DEC_CASE(DD, RR) \
     if (d == DD && rt == RR) { \
-        const dim3 block((dec_threads<DD, RR>())); \
+        const dim3 block((dec_threads(DD, RR))); \
         if (p.act == 1) hipLaunchKernelGGL((mlp_decode_mfma<DD, RR, 1>), grid, block, 0, st, p); \
         else if (p.act == 2) hipLaunchKernelGGL((mlp_decode_mfma<DD, RR, 2>), grid, block, 0, st, p); \
         else hipLaunchKernelGGL((mlp_decode_mfma<DD, RR, 0>), grid, block, 0, st, p); \

@@ -96,10 +96,10 @@ __device__ __forceinline__ void dec_score_tile(const MTile<D> &T, int j0, int Hs
 // LDS of the block fold: per wave, its rows' read-outs [16 RT][D + 4] (rows
 // padded by four floats so the sixteen rows of one store land in different
 // banks) and score sums [16 RT].
-template <int D, int RT> struct DecFold {
+template <int D, int RT, int SL> struct DecFold {
     static constexpr int ROWS = 16 * RT, LD = D + 4;
-    float O[4][ROWS * LD];
-    float s[4][ROWS];
+    float O[SL][ROWS * LD];
+    float s[SL][ROWS];
 };
 
 // d = 128: a wave's weight rows are copied HBM -> LDS (global_load_lds, whole
@@ -108,9 +108,9 @@ template <int D, int RT> struct DecFold {
 // with the sixteen 16-byte pieces of row r stored at piece ^ (r % 16), so the
 // operand reads of sixteen rows fall in distinct banks.  The fold reuses the
 // same LDS after a barrier.
-template <int D, int RT, int NT> union DecLds {
-    u32x4 tiles[4][NT * 2 * 32 * (D / 8)];
-    DecFold<D, RT> fold;
+template <int D, int RT, int NT, int SL> union DecLds {
+    u32x4 tiles[SL][NT * 2 * 32 * (D / 8)];
+    DecFold<D, RT, SL> fold;
 };
 
 // Copy rows u0 .. u0 + 31 (clamped to umax) of W into LDS rows 0..31 at dst:
@@ -149,35 +149,28 @@ template <int D> __device__ __forceinline__ void lds_w2_128(MTile<D> &T, const u
     }
 }
 
-// Waves per tile slot: at d = 128 with four 16-row tiles (up to 64 rows per KV
-// head) two waves share each slot's weight tiles in LDS and take 32 rows each,
-// so a block has eight waves, two per SIMD, each with half the registers of a
-// 64-row wave; one wave per slot otherwise (at d = 64 the tiles sit in
-// registers, and a second wave would read them again).
-template <int D, int RT> constexpr int dec_wps() { return D == 128 && RT == 4 ? 2 : 1; }
-template <int D, int RT> constexpr int dec_threads() { return 256 * dec_wps<D, RT>(); }
-
-// Block blk_id of the grid Hkv x RG x SB (blocks of 4 tile slots, WPS waves
-// each: wave v takes slot v % 4 and row tiles (v / 4) * RT / WPS ...).  Slot w
-// of block sb of (KV head h, row group rg) is slot i = 4 sb + w of that group:
-// target slot i < nwt, score slot i - nwt < nws, idle otherwise.
+// Block blk_id of the grid Hkv x RG x SB: blocks of SL = dec_slots(D, RT) tile
+// slots of WPS = dec_wps(D, RT) waves each (wave v takes slot v % SL and row
+// tiles (v / SL) * RT / WPS ...).  Slot w of block sb of (KV head h, row group
+// rg) is slot i = SL sb + w of that group: target slot i < nwt, score slot
+// i - nwt < nws, idle otherwise.
 template <int D, int RT, int ACT, int NT>
 __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) {
     constexpr int KS = D / 32, DV = D / 16;
-    constexpr int WPS = dec_wps<D, RT>(), RTW = RT / WPS;   // waves per slot, row tiles per wave
+    constexpr int WPS = dec_wps(D, RT), SL = dec_slots(D, RT), RTW = RT / WPS;   // waves per slot, slots, row tiles per wave
     constexpr int NS = dec_score_tiles(RT);                 // score tiles per score slot
-    __shared__ DecLds<D, RT, NT> lds;
-    DecFold<D, RT> &fold = lds.fold;
+    __shared__ DecLds<D, RT, NT, SL> lds;
+    DecFold<D, RT, SL> &fold = lds.fold;
 
     const int v = threadIdx.x >> 6;
-    const int w = v & 3, part = v >> 2;       // tile slot, row part of this wave
+    const int w = v % SL, part = v / SL;      // tile slot, row part of this wave
     int blk = blk_id;
     const int sb = blk % a.SB;
     blk /= a.SB;
     const int rg = blk % a.RG;
     const int h = blk / a.RG;
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    const int wi = 4 * sb + w;
+    const int wi = SL * sb + w;
     const int rt0 = part * RTW;                // first row tile of this wave within the block's RT
 
     f32x4 O[RTW][DV];
@@ -363,10 +356,10 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
         for (int rt = 0; rt < RTW; ++rt) sc[rt] = group4_sum(sc[rt]);
     }
 
-    // fold the four slots: every wave stores its rows (in the LDS the tiles
+    // fold the slots: every wave stores its rows (in the LDS the tiles
     // used, once every wave is past them), one barrier, then the block's
-    // threads sum the four and write whole rows
-    constexpr int LD = DecFold<D, RT>::LD, ROWS = DecFold<D, RT>::ROWS;
+    // threads sum the slots and write whole rows
+    constexpr int LD = DecFold<D, RT, SL>::LD, ROWS = DecFold<D, RT, SL>::ROWS;
     if constexpr (D == 128) stage_barrier();
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
@@ -382,7 +375,7 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
     __syncthreads();
     const bool direct = a.SB == 1 && !a.defer;
     constexpr int CPR = D / 4;                       // float4 columns per row
-    constexpr int RPI = dec_threads<D, RT>() / CPR;  // rows per pass of the block
+    constexpr int RPI = dec_threads(D, RT) / CPR;   // rows per pass of the block
     const int col = (threadIdx.x % CPR) * 4;
 #pragma unroll
     for (int r0 = 0; r0 < ROWS; r0 += RPI) {
@@ -391,9 +384,16 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
         if (rr >= ROWS || rho >= a.Rp) continue;
         f32x4 v4 = *(const f32x4 *)(fold.O[0] + rr * LD + col);
 #pragma unroll
-        for (int k = 1; k < 4; ++k) v4 += *(const f32x4 *)(fold.O[k] + rr * LD + col);
+        for (int k = 1; k < SL; ++k) v4 += *(const f32x4 *)(fold.O[k] + rr * LD + col);
         const bool lead = col == 0;
-        const float s = lead ? ((fold.s[0][rr] + fold.s[1][rr]) + (fold.s[2][rr] + fold.s[3][rr])) : 0.f;
+        float s = 0.f;
+        if (lead) {
+            if constexpr (SL == 4) s = (fold.s[0][rr] + fold.s[1][rr]) + (fold.s[2][rr] + fold.s[3][rr]);
+            else {
+#pragma unroll
+                for (int k = 0; k < SL; ++k) s += fold.s[k][rr];
+            }
+        }
         if (direct) {
             const int t = rho / a.G, gg = rho - t * a.G;
             const size_t o = (size_t)t * a.Hq + h * a.G + gg;

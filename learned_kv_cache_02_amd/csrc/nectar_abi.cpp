@@ -241,7 +241,7 @@ MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs, long target_waves = 
         pl.RT = mlp_row_tiles(pl.Rp);
         pl.RG = pl.RB = (int)cdiv(pl.Rp, 16L * pl.RT);
         pl.WR = 1;
-        pl.WS = 4;
+        // WS: tile slots per block, set below
         const long per = (long)d->Hkv * pl.RG;
         const long Wa = std::max(1L, d->splits > 0 ? (long)d->splits : cdiv(target_waves, per));
         auto clampl = [](long x, long lo, long hi) { return std::min(std::max(x, lo), hi); };
@@ -258,7 +258,8 @@ MlpPlan plan_mlp(const nectar_attn_desc *d, int Ht, int Hs, long target_waves = 
         pl.Wt = (int)Wt;
         pl.Ws = (int)Ws;
         pl.S = (int)(Wt + Ws);
-        pl.SB = (int)std::max(1L, cdiv(Wt + Ws, 4));
+        pl.WS = dec_slots(d->d, pl.RT);
+        pl.SB = (int)std::max(1L, cdiv(Wt + Ws, (long)pl.WS));
         pl.ws = pl.SB > 1 ? (size_t)d->Hkv * pl.SB * pl.Rp * ((size_t)d->d * 4 + 4) : 0;
         return pl;
     }

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256, NECTAR_RT1_WAVES_PER_SIMD) void step_partials(
 // 64-row blocks at d = 128 (then the attention blocks' extra four waves end at
 // once: the attention body is written for four).
 template <int D, int ACT, int RTM>
-__global__ __launch_bounds__((dec_threads<D, RTM>()), 1) void step_partials_dec(AttnGroup gr, int nb_attn, MlpParams m) {
+__global__ __launch_bounds__((dec_threads(D, RTM)), 1) void step_partials_dec(AttnGroup gr, int nb_attn, MlpParams m) {
     const int b = (int)blockIdx.x;
     if (b < nb_attn) {
         if (threadIdx.x >= 256) return;
@@ -59,9 +59,9 @@ hipError_t launch_step_partials(const AttnParams &p0, const AttnParams *p1, cons
     if (d == DD && m.act == AA) { \
         if (shared && mlp_rt == 1) hipLaunchKernelGGL((step_partials<DD, AA>), grid, block, 0, st, gr, (int)nb_attn, m); \
         else if (shared) return hipErrorInvalidValue; \
-        else if (mlp_rt == 1) hipLaunchKernelGGL((step_partials_dec<DD, AA, 1>), grid, dim3((dec_threads<DD, 1>())), 0, st, gr, (int)nb_attn, m); \
-        else if (mlp_rt == 2) hipLaunchKernelGGL((step_partials_dec<DD, AA, 2>), grid, dim3((dec_threads<DD, 2>())), 0, st, gr, (int)nb_attn, m); \
-        else if (mlp_rt == 4) hipLaunchKernelGGL((step_partials_dec<DD, AA, 4>), grid, dim3((dec_threads<DD, 4>())), 0, st, gr, (int)nb_attn, m); \
+        else if (mlp_rt == 1) hipLaunchKernelGGL((step_partials_dec<DD, AA, 1>), grid, dim3((dec_threads(DD, 1))), 0, st, gr, (int)nb_attn, m); \
+        else if (mlp_rt == 2) hipLaunchKernelGGL((step_partials_dec<DD, AA, 2>), grid, dim3((dec_threads(DD, 2))), 0, st, gr, (int)nb_attn, m); \
+        else if (mlp_rt == 4) hipLaunchKernelGGL((step_partials_dec<DD, AA, 4>), grid, dim3((dec_threads(DD, 4))), 0, st, gr, (int)nb_attn, m); \
         else return hipErrorInvalidValue; \
         return hipGetLastError(); }
     NECTAR_STEP_CASE(128, 0) NECTAR_STEP_CASE(128, 1) NECTAR_STEP_CASE(128, 2)

@@ -1046,20 +1046,24 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
         sp.kvpl = plan_attn(d, d->Hkv, Rp_doc, (long)m->p);
     }
     auto decode = [](const AttnPlan &pl) { return pl.S == 0 || (!pl.lds && pl.RT == 1); };
+    // A document-side attention may also be LDS-staged (many rows per KV head
+    // beside a decode-shaped local part): its deferred partials go to the one
+    // finishing pass, which saves its own combine launch and the merge.
+    auto doc_side = [&](const AttnPlan &pl) { return decode(pl) || pl.lds; };
     // (with the document in the same launch the module has at most 16 rows per
     // KV head too, so both run one row tile)
     sp.fused = !sp.deep && (d->dtype == NECTAR_F32 ||
-               (decode(sp.loc) && (!exact || decode(sp.doc)) && (!sp.mlp || !sp.mlpl.prefill) &&
-                (!sp.kvp || decode(sp.kvpl))));
+               (decode(sp.loc) && (!exact || doc_side(sp.doc)) && (!sp.mlp || !sp.mlpl.prefill) &&
+                (!sp.kvp || doc_side(sp.kvpl))));
     if (sp.fused) {
-        if (sp.mlp && exact) sp.mlpl = plan_mlp(d, m->Ht, m->Hs, kTargetWavesMlpShared, true);
+        if (sp.mlp && exact && !sp.doc.lds) sp.mlpl = plan_mlp(d, m->Ht, m->Hs, kTargetWavesMlpShared, true);
         // with a module in the same launch the document leaves 48 of the 512
         // two-per-CU block slots free from the start, so the module's blocks run
         // beside the document's instead of after them (4B step, waves left free
         // 96 / 128 / 160 / 192 / 256 / 352: 56.8 / 56.0 / 55.0 / 54.8 / 55.5 /
         // 56.9 us; all 512 slots to the document was 61.2 us with the earlier
         // finishing pass)
-        if (exact && m) sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n, true, kTargetWaves - 192);
+        if (exact && m && !sp.doc.lds) sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n, true, kTargetWaves - 192);
         // exact path alone: the document leaves the local part's blocks their
         // slots, so both fill the 512 two-per-CU slots in one wave of blocks
         // (4B exact path 49.4 -> 48.5 us)

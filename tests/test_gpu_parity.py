@@ -387,7 +387,8 @@ STEP_CASES = {
     "exact_only": ("bf16", 128, 4, 1, 50, 64, 49, 16, 4, 1000, None),
     "module_only": ("bf16", 128, 4, 2, 30, 32, 28, 16, 4, None, ("mlp", 64, 32)),
     # 56 document rows per KV head (the 1M-token decode's shape): the Nectar path fuses
-    # the 64-row module blocks with the local blocks; with the exact part the plan is composed
+    # the 64-row module blocks with the local blocks; with the exact part the LDS-staged
+    # document pass and the module defer their partials to the same finishing pass
     "nectar_rows56": ("bf16", 128, 8, 1, 300, 320, 299, 28, 4, None, ("mlp", 704, 450)),
     "both_rows56": ("bf16", 128, 8, 1, 300, 320, 299, 28, 4, 3000, ("mlp", 704, 450)),
 }
@@ -401,7 +402,7 @@ def test_layer_step(nx, name):
 
 
 @pytest.mark.parametrize("name,splits", [("decode_bf16", 100), ("batch64_bf16", 70), ("decode_bf16_d64", 90),
-                                         ("nectar_rows56", 80)])
+                                         ("nectar_rows56", 80), ("both_rows56", 80), ("kvpair_bf16", 40)])
 def test_layer_step_many_splits(nx, name, splits):
     """More than 64 key splits per part: the finishing pass and the split-K
     combine fold the splits past the 64 they load up front in a serial tail."""

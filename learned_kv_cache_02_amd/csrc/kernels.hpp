@@ -174,10 +174,36 @@ struct TransposeParams {
     long si, so;
     int rows, cols, ldi, ldo, P;
 };
-struct GatherParams {        // Q[p][rho][:] = q row of rho in KV group p
+struct GatherParams {        // Q[p][rho][:] = q row of rho in KV group p; zero for Rp <= rho < Rpad
     const uint16_t *q;
     uint16_t *Q;
     int Hq, G, Hkv, Rp, d;
+    int Rpad;                // rows per group in Q (0: Rp)
+};
+// Per query row of the fused training pass (d = 128): the loss residuals of the
+// module's forward outputs and the gradients that the backward contracts, in
+// row-padded group layout (rows Rp <= rho < Rpad zero).
+struct LossRowParams {
+    const float *a, *A;      // module forward [R][Hq], [R][Hq][d] (output biases included)
+    const float *alpha, *Atgt;
+    uint16_t *gA;            // [Hkv][Rpad][d] bf16: coefA (A - Atgt)
+    float *ga;               // [Hkv][Rpad]: coefa (a - alpha)
+    float *es, *et;          // [Hkv][Rp]: (a - alpha)^2, ||A - Atgt||^2
+    float coefa, coefA;      // 2 lambda_alpha / R, 2 lambda_A / R
+    int Hq, G, Hkv, Rp, Rpad;
+};
+// Fused backward of the one-hidden-layer module (d = 128): blocks of four waves
+// own 128 target or score units of one KV group and run over all its rows,
+// recomputing the pre-activations; the weight, bias and score read-out
+// gradients of their units are written once, with no partial sums.
+struct TrainBwdParams {
+    const uint16_t *Q, *gA;  // [Hkv][Rpad][d] bf16 (padding rows zero)
+    const float *ga;         // [Hkv][Rpad] (padding rows zero)
+    const uint16_t *W1, *W2t, *Ws, *ws2;
+    const float *b1, *bs;
+    float *gW1, *gb1, *gW2t, *gWs, *gbs, *gws2;
+    int Hkv, Rpad, Ht, Hs;
+    int nut, nus, items;     // target / score unit blocks per group, items = Hkv (nut + nus)
 };
 struct ScoreRowParams {
     const float *Zs;         // [Hkv][Rp][Hs] pre-activations (bias included)
@@ -248,6 +274,8 @@ hipError_t launch_gather_q(const GatherParams &a, hipStream_t st);
 hipError_t launch_score_rows(const ScoreRowParams &a, int act, hipStream_t st);
 hipError_t launch_target_rows(const TargetRowParams &a, int d, hipStream_t st);
 hipError_t launch_row_dot(const RowDotParams &a, int fp32_in, hipStream_t st);
+hipError_t launch_loss_rows(const LossRowParams &a, hipStream_t st);
+hipError_t launch_train_bwd(const TrainBwdParams &a, int act, hipStream_t st);
 hipError_t launch_sum_parts(const SumParams &a, int nparts, hipStream_t st);
 hipError_t launch_train_scalars(const TrainScalars &a, hipStream_t st);
 hipError_t launch_adamw(const AdamParams &a, hipStream_t st);

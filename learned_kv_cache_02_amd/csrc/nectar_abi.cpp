@@ -728,10 +728,17 @@ constexpr int kTrainParts = 64, kMaxSplit = 8;
 
 struct TrainLayout {
     int Rp = 0, Ht = 0, Hs = 0, d = 0, Hkv = 0;
+    // fused (d = 128): the module's forward kernels, then one backward launch
+    // that recomputes the pre-activations (rows padded to Rpad per group);
+    // otherwise stored pre-activations and hidden values between products
+    bool fused = false;
+    int Rpad = 0;
+    MlpPlan fwd;
     // flat parameter offsets (elements): W1, b1, W2t, b2, Ws, bs, ws2, bs2, total
     long off[9] = {};
     // workspace offsets (bytes)
     size_t Q, Zb, Yt, W2tT, Aout, gA, Zs, Ys, dZs, ga, es, et, Cpart, xsp, csp, parts, scale, bytes;
+    size_t am, Am, fws;      // fused: the forward's (a, A) and its workspace
 };
 
 TrainLayout train_layout(const nectar_attn_desc *d, const nectar_module *m) {
@@ -745,6 +752,25 @@ TrainLayout train_layout(const nectar_attn_desc *d, const nectar_module *m) {
     for (int i = 0; i < 8; ++i) L.off[i + 1] = L.off[i] + sizes[i];
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+    L.fused = d->d == 128 && d->dtype == NECTAR_BF16;
+    if (L.fused) {
+        L.Rpad = (int)cdiv(L.Rp, 32) * 32;
+        L.fwd = plan_mlp(d, L.Ht, L.Hs);
+        const size_t Rq = (size_t)d->R * d->Hq, Rr = (size_t)H * L.Rp, Rd = (size_t)H * L.Rpad;
+        L.Q = take(Rd * L.d * 2);
+        L.gA = take(Rd * L.d * 2);
+        L.ga = take(Rd * 4);
+        L.es = take(Rr * 4);
+        L.et = take(Rr * 4);
+        L.am = take(Rq * 4);
+        L.Am = take(Rq * L.d * 4);
+        L.fws = take(L.fwd.ws);
+        L.csp = take((size_t)H * ((L.Rp + 63) / 64) * L.d * 4);
+        L.parts = take((2 * kTrainParts + kNormParts) * 8);
+        L.scale = take(2 * 4);
+        L.bytes = o;
+        return L;
+    }
     const size_t R = (size_t)H * L.Rp;
     L.Q = take(R * L.d * 2);
     L.Zb = take(R * L.Ht * 2);
@@ -817,6 +843,52 @@ RowDotParams rowdot(const void *X, long sx, int ldx, const float *v, long sv, fl
     return r;
 }
 
+// Fused loss and gradient (d = 128): (a, A) from the module's forward kernels,
+// the residual rows, one backward launch for every weight, hidden-bias and
+// score read-out gradient, then the output-bias gradients as fixed-order sums.
+hipError_t run_loss_grad_fused(const nectar_attn_desc *desc, const nectar_module *m, const TrainLayout &L,
+                               const void *q, const float *alpha, const float *Atgt, float lam_alpha, float lam_A,
+                               float *grad, char *w, hipStream_t st) {
+    const int P = L.Hkv, Rp = L.Rp, Rpad = L.Rpad, d = L.d;
+    auto F = [&](size_t off) { return (float *)(w + off); };
+    hipError_t e = hipSuccess;
+    auto run = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+    GatherParams gq{};
+    gq.q = (const uint16_t *)q; gq.Q = (uint16_t *)(w + L.Q);
+    gq.Hq = desc->Hq; gq.G = desc->Hq / desc->Hkv; gq.Hkv = P; gq.Rp = Rp; gq.d = d; gq.Rpad = Rpad;
+    run(launch_gather_q(gq, st));
+    if (e == hipSuccess) e = run_mlp(desc, L.fwd, m, q, F(L.am), F(L.Am), w + L.fws, st);
+    LossRowParams lr{};
+    lr.a = F(L.am); lr.A = F(L.Am); lr.alpha = alpha; lr.Atgt = Atgt;
+    lr.gA = (uint16_t *)(w + L.gA); lr.ga = F(L.ga); lr.es = F(L.es); lr.et = F(L.et);
+    lr.coefa = 2.0f * lam_alpha / (float)desc->R;
+    lr.coefA = 2.0f * lam_A / (float)desc->R;
+    lr.Hq = desc->Hq; lr.G = desc->Hq / desc->Hkv; lr.Hkv = P; lr.Rp = Rp; lr.Rpad = Rpad;
+    run(launch_loss_rows(lr, st));
+    TrainBwdParams tb{};
+    tb.Q = (const uint16_t *)(w + L.Q); tb.gA = (const uint16_t *)(w + L.gA); tb.ga = F(L.ga);
+    tb.W1 = (const uint16_t *)m->W1; tb.W2t = (const uint16_t *)m->W2t; tb.Ws = (const uint16_t *)m->Ws;
+    tb.ws2 = (const uint16_t *)m->ws2; tb.b1 = m->b1; tb.bs = m->bs;
+    tb.gW1 = grad + L.off[0]; tb.gb1 = grad + L.off[1]; tb.gW2t = grad + L.off[2];
+    tb.gWs = grad + L.off[4]; tb.gbs = grad + L.off[5]; tb.gws2 = grad + L.off[6];
+    tb.Hkv = P; tb.Rpad = Rpad; tb.Ht = L.Ht; tb.Hs = L.Hs;
+    tb.nut = (int)cdiv(L.Ht, 128); tb.nus = (int)cdiv(L.Hs, 128); tb.items = P * (tb.nut + tb.nus);
+    run(launch_train_bwd(tb, m->act, st));
+    // db2 = column sums of gA, dbs2 = sums of ga
+    ColSumParams c{};
+    c.X = (const uint16_t *)(w + L.gA); c.v = nullptr; c.parts = F(L.csp); c.out = grad + L.off[3];
+    c.sx = (long)Rpad * d; c.sv = Rpad; c.so = d; c.ldx = d; c.rows = Rp; c.cols = d; c.P = P;
+    run(launch_col_sum(c, st));
+    run(launch_row_dot(rowdot(F(L.ga), Rpad, Rpad, nullptr, 0, grad + L.off[7], 1, 1, Rp, P), 1, st));
+    SumParams su{};
+    su.parts = (double *)(w + L.parts);
+    su.x = F(L.es); su.n = (long)P * Rp; su.part0 = 0; su.square = 0;
+    run(launch_sum_parts(su, kTrainParts, st));
+    su.x = F(L.et); su.part0 = kTrainParts;
+    run(launch_sum_parts(su, kTrainParts, st));
+    return e;
+}
+
 // Loss terms and gradient into grad (flat fp32, parameter order of TrainLayout).
 hipError_t run_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, const TrainLayout &L, const void *q,
                          const float *alpha, const float *Atgt, float lam_alpha, float lam_A, float *grad,
@@ -826,6 +898,7 @@ hipError_t run_loss_grad(const nectar_attn_desc *desc, const nectar_module *m, c
     auto F = [&](size_t off) { return (float *)(w + off); };
     hipError_t e = hipSuccess;
     auto run = [&](hipError_t x) { if (e == hipSuccess) e = x; };
+    if (L.fused) return run_loss_grad_fused(desc, m, L, q, alpha, Atgt, lam_alpha, lam_A, grad, w, st);
 
     GatherParams gq{};
     gq.q = (const uint16_t *)q; gq.Q = (uint16_t *)B(L.Q);
@@ -1052,6 +1125,10 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
     auto doc_side = [&](const AttnPlan &pl) { return decode(pl) || pl.lds; };
     // (with the document in the same launch the module has at most 16 rows per
     // KV head too, so both run one row tile)
+    // A batched module (the LDS-staged kernels, 65+ rows per KV head) finishes
+    // with its own split fold: its many split partials per row make the finishing
+    // pass slower than that fold plus a merge (batch-64 decode layer, Nectar path:
+    // 63.5 us composed, 72 us fused).
     sp.fused = !sp.deep && (d->dtype == NECTAR_F32 ||
                (decode(sp.loc) && (!exact || doc_side(sp.doc)) && (!sp.mlp || !sp.mlpl.prefill) &&
                 (!sp.kvp || doc_side(sp.kvpl))));

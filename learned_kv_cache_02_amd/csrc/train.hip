@@ -527,13 +527,15 @@ __global__ __launch_bounds__(256) void transpose_bf16(TransposeParams a) {
 __global__ __launch_bounds__(256) void gather_q(GatherParams a) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;       // one 16-byte piece
     const int pieces = a.d / 8;
-    const long n = (long)a.Hkv * a.Rp * pieces;
+    const int Rs = a.Rpad > 0 ? a.Rpad : a.Rp;
+    const long n = (long)a.Hkv * Rs * pieces;
     if (i >= n) return;
     const int pc = (int)(i % pieces);
     const long pr = i / pieces;
-    const int rho = (int)(pr % a.Rp), p = (int)(pr / a.Rp);
-    const size_t src = out_row(p, rho, a.Hkv, a.G, 0, a.Hq) * a.d + 8 * pc;
-    *(u32x4 *)(a.Q + (size_t)pr * a.d + 8 * pc) = *(const u32x4 *)(a.q + src);
+    const int rho = (int)(pr % Rs), p = (int)(pr / Rs);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (rho < a.Rp) v = *(const u32x4 *)(a.q + out_row(p, rho, a.Hkv, a.G, 0, a.Hq) * a.d + 8 * pc);
+    *(u32x4 *)(a.Q + (size_t)pr * a.d + 8 * pc) = v;
 }
 
 // One wave per score row: hidden values, a, the score error and its gradient,
@@ -845,7 +847,7 @@ hipError_t launch_transpose_bf16(const TransposeParams &t, hipStream_t st) {
 }
 
 hipError_t launch_gather_q(const GatherParams &a, hipStream_t st) {
-    const long n = (long)a.Hkv * a.Rp * (a.d / 8);
+    const long n = (long)a.Hkv * (a.Rpad > 0 ? a.Rpad : a.Rp) * (a.d / 8);
     hipLaunchKernelGGL(gather_q, dim3(grid_for(n, 256, 1L << 30)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -898,6 +900,300 @@ hipError_t launch_adamw(const AdamParams &a, hipStream_t st) {
 hipError_t launch_write_params(const WriteParams &a, hipStream_t st) {
     if (a.n <= 0) return hipSuccess;
     hipLaunchKernelGGL(write_params, dim3(grid_for(a.n, 256, 8192)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused loss and backward (d = 128): the forward outputs come from the module's
+// own forward kernels; the backward recomputes every pre-activation from the
+// staged query rows instead of storing hidden-sized arrays.
+
+// One wave per padded row: residuals, their squared norms, and the gradients
+// the backward contracts (zero on padding rows).
+__global__ __launch_bounds__(256) void loss_rows128(LossRowParams a) {
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (long)a.Hkv * a.Rpad) return;
+    const int lane = threadIdx.x & 63;
+    const int p = (int)(row / a.Rpad), rho = (int)(row - (long)p * a.Rpad);
+    uint32_t *gA = (uint32_t *)(a.gA + (size_t)row * 128);      // lane: dims 2 lane, 2 lane + 1
+    if (rho >= a.Rp) {
+        gA[lane] = 0u;
+        if (lane == 0) a.ga[row] = 0.f;
+        return;
+    }
+    const size_t o = out_row(p, rho, a.Hkv, a.G, 0, a.Hq);
+    const float2 Av = *(const float2 *)(a.A + o * 128 + 2 * lane);
+    const float2 Tv = *(const float2 *)(a.Atgt + o * 128 + 2 * lane);
+    const float e0 = Av.x - Tv.x, e1 = Av.y - Tv.y;
+    gA[lane] = pack_bf16(a.coefA * e0, a.coefA * e1);
+    const float s = wave_sum(__builtin_fmaf(e1, e1, e0 * e0));
+    if (lane == 0) {
+        const long fr = (long)p * a.Rp + rho;
+        const float es = a.a[o] - a.alpha[o];
+        a.et[fr] = s;
+        a.es[fr] = es * es;
+        a.ga[row] = a.coefa * es;
+    }
+}
+
+namespace {
+
+constexpr int kBwdRows = 32;                  // query rows per stage
+constexpr int kBwdWaves = 4;                  // a wave owns 32 units
+
+struct BwdStage {
+    u32x4 q[kBwdRows * 16];     // query rows: piece j of row r at j ^ tr_swizzle(r)
+    u32x4 g[kBwdRows * 16];     // read-out gradient rows (target blocks), same layout
+    float ga[kBwdRows];         // score gradients of the rows (score blocks)
+};
+
+}  // namespace
+
+// act(x) and act'(x) together; the erf form shares its erf and exponential.
+template <int ACT> __device__ __forceinline__ void act_pair(float x, float &y, float &dy) {
+    if constexpr (ACT == 0) {
+        const float z = fabsf(x) * 0.70710678118654752f;
+        const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
+        float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+        p = __builtin_fmaf(p, t, 1.421413741f);
+        p = __builtin_fmaf(p, t, -0.284496736f);
+        p = __builtin_fmaf(p, t, 0.254829592f);
+        const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);   // exp(-x^2 / 2)
+        const float erfc_half = 0.5f * (p * t) * e;
+        const float Phi = x >= 0.f ? 1.0f - erfc_half : erfc_half;
+        y = x * Phi;
+        dy = __builtin_fmaf(x * e, 0.3989422804014327f, Phi);
+    } else {
+        y = act_fn<ACT>(x);
+        dy = act_grad_fn<ACT>(x);
+    }
+}
+
+// One item: the 128 units [u0, u0 + 128) of group h, target (TGT) or score.
+// Wave w owns units u0 + 32 w .. + 31; lane (n, half) = (lane % 32, lane / 32)
+// holds unit n's weights as the B operand of the 32x32x16 MFMA and, per stage
+// of 32 rows, computes
+//   Z (32 rows x 32 units) = Q . W^T + b               (A: query rows from LDS)
+//   target: dH = gA . W2t^T, dZ = dH act'(Z), H = act(Z),
+//           dW2t^T (128 x 32) += gA^T . H,  dW1^T += Q^T . dZ,  db1 += sum dZ
+//   score:  dZ = ga ws2 act'(Z),  dWs^T += Q^T . dZ,  dbs += sum dZ,
+//           dws2 += sum ga act(Z)
+// The accumulator of Z holds unit n in every lane and rows 8 (i / 4) + 4 half
+// + i % 4 in register i, so registers 8 t .. 8 t + 7 of H or dZ are the B
+// operand of row step t as they stand, provided the transposed A operands
+// (gA^T, Q^T: dims x rows) take their rows in that order: transposing LDS
+// reads (ds_read_b64_tr_b16) of the row-major stage give it.
+template <int ACT, bool TGT>
+__device__ __forceinline__ void train_bwd_item(const TrainBwdParams &a, int h, int u0, BwdStage &st_a,
+                                               BwdStage &st_b, BwdStage &st_c) {
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, hf = lane >> 5, r = lane & 31;
+    const int H = TGT ? a.Ht : a.Hs;
+    const bool live = u0 + 32 * w < H;        // H is a multiple of 32: whole waves
+    const int n = min(u0 + 32 * w + r, H - 1);
+    const size_t un = (size_t)h * H + n;
+
+    u32x4 wa[8], wb[8];
+    const uint16_t *Wa = (TGT ? a.W1 : a.Ws) + un * 128;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) wa[kt] = *(const u32x4 *)(Wa + 16 * kt + 8 * hf);
+    if constexpr (TGT) {
+        const uint16_t *Wb = a.W2t + un * 128;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) wb[kt] = *(const u32x4 *)(Wb + 16 * kt + 8 * hf);
+    }
+    const float bias = TGT ? a.b1[un] : a.bs[un];
+    const float wsc = TGT ? 0.f : bf16_to_f32(a.ws2[un]);
+
+    // transposing-read offsets in a 16-row block of a stage: lane 32 hf + m
+    // receives dim 32 mi + m of rows 8 hh + 4 hf + 0..3
+    uint32_t woff[2][4];
+    {
+        const int G = lane >> 4, aa = lane & 3, e = (lane >> 2) & 3;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const int u = 8 * hh + 4 * (G >> 1) + e;
+                const int piece = 4 * mi + 2 * (G & 1) + (aa >> 1);
+                woff[hh][mi] = (uint32_t)(u * 256 + ((piece ^ tr_swizzle(u)) * 16) + (aa & 1) * 8);
+            }
+    }
+    const int trs = tr_swizzle(r);
+
+    f32x16 gX[4], gY[4];          // target: dW2t^T, dW1^T; score: dWs^T (gX unused)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        gX[mi] = f32x16{};
+        gY[mi] = f32x16{};
+    }
+    float db = 0.f, dw = 0.f;
+
+    const uint16_t *Qh = a.Q + (size_t)h * a.Rpad * 128;
+    const uint16_t *Gh = a.gA + (size_t)h * a.Rpad * 128;
+    const float *gah = a.ga + (size_t)h * a.Rpad;
+    const int nst = a.Rpad / kBwdRows;
+
+    // Stage i: rows 32 i .. 32 i + 31; every wave copies 8 rows of each table
+    // (two 1 KB copies per table), score blocks' wave 0 also the 32 gradients.
+    auto issue = [&](int i, BwdStage &dst) {
+        const int row0 = kBwdRows * i;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int r0 = 8 * w + 4 * c, rr = r0 + (lane >> 4);
+            const size_t off = (size_t)(row0 + rr) * 128 + ((lane & 15) ^ tr_swizzle(rr)) * 8;
+            __builtin_amdgcn_global_load_lds((const void *)(Qh + off), (lds_void *)&dst.q[r0 * 16], 16, 0, 0);
+            if constexpr (TGT)
+                __builtin_amdgcn_global_load_lds((const void *)(Gh + off), (lds_void *)&dst.g[r0 * 16], 16, 0, 0);
+        }
+        if constexpr (!TGT) {
+            if (w == 0 && lane < 8)
+                __builtin_amdgcn_global_load_lds((const void *)(gah + row0 + 4 * lane), (lds_void *)dst.ga, 16, 0, 0);
+        }
+    };
+
+    auto compute = [&](const BwdStage &cur) {
+        f32x16 Z, dH;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            Z[i] = bias;
+            dH[i] = 0.f;
+        }
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+            const int pos = r * 16 + ((2 * kt + hf) ^ trs);
+            Z = mfma32(cur.q[pos], wa[kt], Z);
+            if constexpr (TGT) dH = mfma32(cur.g[pos], wb[kt], dH);
+        }
+        float hv[16], dz[16];
+        if constexpr (TGT) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float y, dy;
+                act_pair<ACT>(Z[i], y, dy);
+                hv[i] = y;
+                dz[i] = dH[i] * dy;
+                db += dz[i];
+            }
+        } else {
+            float gr[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 g4 = *(const f32x4 *)&cur.ga[8 * q + 4 * hf];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) gr[4 * q + j] = g4[j];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float y, dy;
+                act_pair<ACT>(Z[i], y, dy);
+                dw = __builtin_fmaf(gr[i], y, dw);
+                dz[i] = gr[i] * wsc * dy;
+                db += dz[i];
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const u32x4 Db = {pack_bf16(dz[8 * tt + 0], dz[8 * tt + 1]), pack_bf16(dz[8 * tt + 2], dz[8 * tt + 3]),
+                              pack_bf16(dz[8 * tt + 4], dz[8 * tt + 5]), pack_bf16(dz[8 * tt + 6], dz[8 * tt + 7])};
+            const char *qb = (const char *)cur.q + tt * 16 * 256;
+            if constexpr (TGT) {
+                const u32x4 Hb = {pack_bf16(hv[8 * tt + 0], hv[8 * tt + 1]), pack_bf16(hv[8 * tt + 2], hv[8 * tt + 3]),
+                                  pack_bf16(hv[8 * tt + 4], hv[8 * tt + 5]), pack_bf16(hv[8 * tt + 6], hv[8 * tt + 7])};
+                const char *gb = (const char *)cur.g + tt * 16 * 256;
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const u32x2 g0 = lds_read_tr16(gb, woff[0][mi]), g1 = lds_read_tr16(gb, woff[1][mi]);
+                    gX[mi] = mfma32(u32x4{g0.x, g0.y, g1.x, g1.y}, Hb, gX[mi]);
+                }
+            }
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const u32x2 q0 = lds_read_tr16(qb, woff[0][mi]), q1 = lds_read_tr16(qb, woff[1][mi]);
+                gY[mi] = mfma32(u32x4{q0.x, q0.y, q1.x, q1.y}, Db, gY[mi]);
+            }
+        }
+    };
+
+    // stage i has landed once at most the next stage's copies are pending
+    auto step = [&](int i, const BwdStage &cur, BwdStage &ahead) {
+        if (i + 1 < nst) {
+            if constexpr (TGT) wait_vmcnt<4>();
+            else {
+                if (w == 0) wait_vmcnt<3>();
+                else wait_vmcnt<2>();
+            }
+        } else {
+            wait_vmcnt<0>();
+        }
+        stage_barrier();
+        if (i + 2 < nst) issue(i + 2, ahead);
+        if (live) compute(cur);
+    };
+    if (nst > 0) issue(0, st_a);
+    if (nst > 1) issue(1, st_b);
+    for (int i = 0; i < nst; i += 3) {
+        step(i, st_a, st_c);
+        if (i + 1 >= nst) break;
+        step(i + 1, st_b, st_a);
+        if (i + 2 >= nst) break;
+        step(i + 2, st_c, st_b);
+    }
+
+    // unit n's sums over both row halves; register i of block mi is dim
+    // 32 mi + 8 (i / 4) + 4 hf + i % 4
+    db += __shfl_xor(db, 32, 64);
+    dw += __shfl_xor(dw, 32, 64);
+    if (!live) return;
+    float *gy = (TGT ? a.gW1 : a.gWs) + un * 128;
+    float *gx = a.gW2t + un * 128;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int dc = 32 * mi + 8 * q + 4 * hf;
+            *(f32x4 *)(gy + dc) = f32x4{gY[mi][4 * q], gY[mi][4 * q + 1], gY[mi][4 * q + 2], gY[mi][4 * q + 3]};
+            if constexpr (TGT)
+                *(f32x4 *)(gx + dc) = f32x4{gX[mi][4 * q], gX[mi][4 * q + 1], gX[mi][4 * q + 2], gX[mi][4 * q + 3]};
+        }
+    if (hf == 0) {
+        if constexpr (TGT) {
+            a.gb1[un] = db;
+        } else {
+            a.gbs[un] = db;
+            a.gws2[un] = dw;
+        }
+    }
+}
+
+// Items (group, role, unit block) in group-major order, a contiguous range per
+// XCD (block ids go round-robin over the eight), so each XCD's L2 holds few
+// groups' staged rows.
+template <int ACT>
+__global__ __launch_bounds__(64 * kBwdWaves, 1) void train_bwd_lds32(TrainBwdParams a) {
+    __shared__ BwdStage st_a, st_b, st_c;
+    const int per = (a.items + 7) / 8;
+    const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (item >= a.items) return;
+    const int ipg = a.nut + a.nus;
+    const int h = item / ipg, ri = item - h * ipg;
+    if (ri < a.nut) train_bwd_item<ACT, true>(a, h, 128 * ri, st_a, st_b, st_c);
+    else train_bwd_item<ACT, false>(a, h, 128 * (ri - a.nut), st_a, st_b, st_c);
+}
+
+hipError_t launch_loss_rows(const LossRowParams &a, hipStream_t st) {
+    const long rows = (long)a.Hkv * a.Rpad;
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(loss_rows128, dim3(grid_for(rows, 4, 1L << 30)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_train_bwd(const TrainBwdParams &a, int act, hipStream_t st) {
+    if (a.items <= 0) return hipSuccess;
+    if (a.Rpad % kBwdRows || a.Ht % 32 || a.Hs % 32) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(8 * ((a.items + 7) / 8))), block(64 * kBwdWaves);
+    if (act == 1) hipLaunchKernelGGL(train_bwd_lds32<1>, grid, block, 0, st, a);
+    else if (act == 2) hipLaunchKernelGGL(train_bwd_lds32<2>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(train_bwd_lds32<0>, grid, block, 0, st, a);
     return hipGetLastError();
 }
 

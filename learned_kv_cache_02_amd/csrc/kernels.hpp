@@ -202,6 +202,7 @@ struct TrainBwdParams {
     const uint16_t *W1, *W2t, *Ws, *ws2;
     const float *b1, *bs;
     float *gW1, *gb1, *gW2t, *gWs, *gbs, *gws2;
+    float *gbs2;             // [Hkv]: sum of ga (each group's first score item)
     int Hkv, Rpad, Ht, Hs;
     int nut, nus, items;     // target / score unit blocks per group, items = Hkv (nut + nus)
 };
@@ -258,12 +259,11 @@ struct AdamParams {
     const float *scale;      // device clipping factor or null
     long n;
     float lr, b1, b2, eps, wd, ic1, ic2;   // ic = 1 / (1 - beta^t)
-};
-struct WriteParams {
-    const float *theta;
-    void *dst;
-    long n;
-    int bf16;
+    // optional copies of the updated theta: elements [off[k], off[k + 1]) to
+    // dst[k] (bf16 where bit k of bf16 is set, else fp32); nseg = 0: none
+    int nseg, bf16;
+    long off[9];
+    void *dst[8];
 };
 long gemm_blocks(const GemmParams &g);
 hipError_t launch_gemm_nt(const GemmParams &g, hipStream_t st);
@@ -279,7 +279,6 @@ hipError_t launch_train_bwd(const TrainBwdParams &a, int act, hipStream_t st);
 hipError_t launch_sum_parts(const SumParams &a, int nparts, hipStream_t st);
 hipError_t launch_train_scalars(const TrainScalars &a, hipStream_t st);
 hipError_t launch_adamw(const AdamParams &a, hipStream_t st);
-hipError_t launch_write_params(const WriteParams &a, hipStream_t st);
 
 // One document-side part of a layer step, finished together with the local
 // part: split partials of the exact document attention or of a Quadrature

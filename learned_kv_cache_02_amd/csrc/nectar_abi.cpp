@@ -754,7 +754,7 @@ TrainLayout train_layout(const nectar_attn_desc *d, const nectar_module *m) {
     auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
     L.fused = d->d == 128 && d->dtype == NECTAR_BF16;
     if (L.fused) {
-        L.Rpad = (int)cdiv(L.Rp, 32) * 32;
+        L.Rpad = (int)cdiv(L.Rp, 64) * 64;      // whole 64-row stages of the backward
         L.fwd = plan_mlp(d, L.Ht, L.Hs);
         const size_t Rq = (size_t)d->R * d->Hq, Rr = (size_t)H * L.Rp, Rd = (size_t)H * L.Rpad;
         L.Q = take(Rd * L.d * 2);
@@ -870,16 +870,15 @@ hipError_t run_loss_grad_fused(const nectar_attn_desc *desc, const nectar_module
     tb.W1 = (const uint16_t *)m->W1; tb.W2t = (const uint16_t *)m->W2t; tb.Ws = (const uint16_t *)m->Ws;
     tb.ws2 = (const uint16_t *)m->ws2; tb.b1 = m->b1; tb.bs = m->bs;
     tb.gW1 = grad + L.off[0]; tb.gb1 = grad + L.off[1]; tb.gW2t = grad + L.off[2];
-    tb.gWs = grad + L.off[4]; tb.gbs = grad + L.off[5]; tb.gws2 = grad + L.off[6];
+    tb.gWs = grad + L.off[4]; tb.gbs = grad + L.off[5]; tb.gws2 = grad + L.off[6]; tb.gbs2 = grad + L.off[7];
     tb.Hkv = P; tb.Rpad = Rpad; tb.Ht = L.Ht; tb.Hs = L.Hs;
     tb.nut = (int)cdiv(L.Ht, 128); tb.nus = (int)cdiv(L.Hs, 128); tb.items = P * (tb.nut + tb.nus);
     run(launch_train_bwd(tb, m->act, st));
-    // db2 = column sums of gA, dbs2 = sums of ga
+    // db2 = column sums of gA (dbs2, the sums of ga, come from the backward)
     ColSumParams c{};
     c.X = (const uint16_t *)(w + L.gA); c.v = nullptr; c.parts = F(L.csp); c.out = grad + L.off[3];
     c.sx = (long)Rpad * d; c.sv = Rpad; c.so = d; c.ldx = d; c.rows = Rp; c.cols = d; c.P = P;
     run(launch_col_sum(c, st));
-    run(launch_row_dot(rowdot(F(L.ga), Rpad, Rpad, nullptr, 0, grad + L.off[7], 1, 1, Rp, P), 1, st));
     SumParams su{};
     su.parts = (double *)(w + L.parts);
     su.x = F(L.es); su.n = (long)P * Rp; su.part0 = 0; su.square = 0;
@@ -1058,15 +1057,15 @@ nectar_status nectar_mlp_train_step(const nectar_attn_desc *desc, const nectar_m
         ts.loss = loss; ts.scale = scale; ts.gnorm = gnorm;
         e = launch_train_scalars(ts, st);
     }
-    if (e == hipSuccess) e = launch_adamw(adam_params(hp, theta, grad, adam_m, adam_v, n, scale), st);
-    // the module's arrays from the updated master parameters
+    // AdamW, writing the module's arrays from the updated master parameters in
+    // the same pass (weights rounded to bf16, biases copied)
+    AdamParams ap = adam_params(hp, theta, grad, adam_m, adam_v, n, scale);
     const void *dst[8] = {m->W1, m->b1, m->W2t, m->b2, m->Ws, m->bs, m->ws2, m->bs2};
-    for (int i = 0; i < 8 && e == hipSuccess; ++i) {
-        WriteParams wp{};
-        wp.theta = theta + L.off[i]; wp.dst = const_cast<void *>(dst[i]); wp.n = L.off[i + 1] - L.off[i];
-        wp.bf16 = (i == 0 || i == 2 || i == 4 || i == 6);
-        e = launch_write_params(wp, st);
-    }
+    ap.nseg = 8;
+    ap.bf16 = (1 << 0) | (1 << 2) | (1 << 4) | (1 << 6);
+    for (int i = 0; i < 9; ++i) ap.off[i] = L.off[i];
+    for (int i = 0; i < 8; ++i) ap.dst[i] = const_cast<void *>(dst[i]);
+    if (e == hipSuccess) e = launch_adamw(ap, st);
     return finish(e, st);
 }
 

@@ -739,13 +739,20 @@ __global__ __launch_bounds__(256) void sum_parts(SumParams a) {
 }
 
 // The loss and the clipping factor from the part sums (one thread).
-__global__ void train_scalars(TrainScalars a) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// One wave: lane l sums parts l, l + 64, ... of each array in order, then a
+// fixed butterfly folds the lanes (every lane ends with the same totals).
+__global__ __launch_bounds__(64) void train_scalars(TrainScalars a) {
+    const int lane = threadIdx.x;
     double s[3] = {0.0, 0.0, 0.0};
     for (int k = 0; k < 2; ++k)
-        for (int b = 0; b < a.nparts; ++b) s[k] += a.parts[k * a.nparts + b];
+        for (int b = lane; b < a.nparts; b += 64) s[k] += a.parts[k * a.nparts + b];
     if (a.scale)
-        for (int b = 0; b < kNormParts; ++b) s[2] += a.parts[2 * a.nparts + b];
+        for (int b = lane; b < kNormParts; b += 64) s[2] += a.parts[2 * a.nparts + b];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) s[k] += __shfl_xor(s[k], o, 64);
+    if (lane != 0) return;
     if (a.loss) {
         a.loss[1] = (float)(s[0] / a.R);
         a.loss[2] = (float)(s[1] / a.R);
@@ -761,8 +768,6 @@ __global__ void train_scalars(TrainScalars a) {
         }
     }
 }
-
-// AdamW: theta *= 1 - lr wd; g' = scale g; moments; bias-corrected step.
 __global__ __launch_bounds__(256) void adamw_kernel(AdamParams a) {
     const float scale = a.scale ? a.scale[0] : 1.0f;
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (long)gridDim.x * 256) {
@@ -774,18 +779,17 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamParams a) {
         a.v[i] = v;
         th -= a.lr * (m * a.ic1) / (sqrtf(v * a.ic2) + a.eps);
         a.theta[i] = th;
+        if (a.nseg > 0) {
+            int k = 0;
+            while (k + 1 < a.nseg && i >= a.off[k + 1]) ++k;
+            const long j = i - a.off[k];
+            if ((a.bf16 >> k) & 1) ((uint16_t *)a.dst[k])[j] = f32_to_bf16(th);
+            else ((float *)a.dst[k])[j] = th;
+        }
     }
 }
 
 // Module arrays from the fp32 master parameters: weights to bf16 (RNE), biases copied.
-__global__ __launch_bounds__(256) void write_params(WriteParams a) {
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (long)gridDim.x * 256) {
-        const float x = a.theta[i];
-        if (a.bf16) ((uint16_t *)a.dst)[i] = f32_to_bf16(x);
-        else ((float *)a.dst)[i] = x;
-    }
-}
-
 // ---------------------------------------------------------------------------
 
 static unsigned grid_for(long n, long per_block, long cap) {
@@ -897,12 +901,6 @@ hipError_t launch_adamw(const AdamParams &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_write_params(const WriteParams &a, hipStream_t st) {
-    if (a.n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(write_params, dim3(grid_for(a.n, 256, 8192)), dim3(256), 0, st, a);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // Fused loss and backward (d = 128): the forward outputs come from the module's
 // own forward kernels; the backward recomputes every pre-activation from the
@@ -938,29 +936,46 @@ __global__ __launch_bounds__(256) void loss_rows128(LossRowParams a) {
 
 namespace {
 
-constexpr int kBwdRows = 32;                  // query rows per stage
-constexpr int kBwdWaves = 4;                  // a wave owns 32 units
+constexpr int kBwdRows = 64;                  // query rows per stage (two halves of 32)
+constexpr int kBwdWaves = 8;                  // 4 unit groups of 32 x 2 row halves
+constexpr int kBwdUnits = 128;                // units per item
 
 struct BwdStage {
     u32x4 q[kBwdRows * 16];     // query rows: piece j of row r at j ^ tr_swizzle(r)
-    u32x4 g[kBwdRows * 16];     // read-out gradient rows (target blocks), same layout
-    float ga[kBwdRows];         // score gradients of the rows (score blocks)
+    u32x4 g[kBwdRows * 16];     // read-out gradient rows (target items), same layout
 };
+// 160 KB: the item's first-layer rows, its read-out rows (target) or the
+// stages' row gradients (score), and a three-stage ring of 64 query rows
+struct BwdLds {
+    u32x4 w1[kBwdUnits * 16];   // W1[u] (target) or Ws[u] (score): piece j at j ^ (u & 15)
+    union {
+        u32x4 w2[kBwdUnits * 16];   // W2t[u], same layout
+        float ga[3][kBwdRows];
+    } x;
+    BwdStage st[3];
+};
+// the final fold of the two row halves reuses the LDS: four waves' 16 f32x4 per
+// lane, then their two scalar sums per unit
+static_assert(sizeof(BwdLds) >= 4 * 16 * 64 * 16 + (4 * 2 * 32 + 1) * 4, "fold space");
+static_assert(sizeof(BwdLds) <= 160 * 1024, "LDS of one workgroup");
 
 }  // namespace
 
-// act(x) and act'(x) together; the erf form shares its erf and exponential.
+// act(x) and act'(x) together.  Erf form: Phi by the polynomial of
+// gelu_erf_poly (|Phi error| <= 5.2e-5, the module forward's own), phi(x) =
+// exp(-x^2 / 2) / sqrt(2 pi), GELU' = Phi + x phi.
 template <int ACT> __device__ __forceinline__ void act_pair(float x, float &y, float &dy) {
     if constexpr (ACT == 0) {
-        const float z = fabsf(x) * 0.70710678118654752f;
-        const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
-        float p = __builtin_fmaf(1.061405429f, t, -1.453152027f);
-        p = __builtin_fmaf(p, t, 1.421413741f);
-        p = __builtin_fmaf(p, t, -0.284496736f);
-        p = __builtin_fmaf(p, t, 0.254829592f);
-        const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);   // exp(-x^2 / 2)
-        const float erfc_half = 0.5f * (p * t) * e;
-        const float Phi = x >= 0.f ? 1.0f - erfc_half : erfc_half;
+        const float c = __builtin_amdgcn_fmed3f(x, -3.71875f, 3.71875f);
+        const float u = c * c;
+        float p = __builtin_fmaf(u, 4.07418810e-08f, -2.44288435e-06f);
+        p = __builtin_fmaf(p, u, 6.33929594e-05f);
+        p = __builtin_fmaf(p, u, -9.51952359e-04f);
+        p = __builtin_fmaf(p, u, 9.39021632e-03f);
+        p = __builtin_fmaf(p, u, -6.58312142e-02f);
+        p = __builtin_fmaf(p, u, 3.98723632e-01f);
+        const float Phi = __builtin_fmaf(c, p, 0.5f);
+        const float e = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);   // exp(-x^2 / 2)
         y = x * Phi;
         dy = __builtin_fmaf(x * e, 0.3989422804014327f, Phi);
     } else {
@@ -969,10 +984,11 @@ template <int ACT> __device__ __forceinline__ void act_pair(float x, float &y, f
     }
 }
 
-// One item: the 128 units [u0, u0 + 128) of group h, target (TGT) or score.
-// Wave w owns units u0 + 32 w .. + 31; lane (n, half) = (lane % 32, lane / 32)
-// holds unit n's weights as the B operand of the 32x32x16 MFMA and, per stage
-// of 32 rows, computes
+// One item: the 128 units [u0, u0 + 128) of group h, target (TGT) or score,
+// over all the group's rows.  Wave w owns units u0 + 32 (w % 4) + 0..31 and the
+// row half w / 4 of every 64-row stage (two waves per SIMD, one per half).
+// Lane (n, half) = (lane % 32, lane / 32) holds unit n's first-layer weights as
+// the B operand of the 32x32x16 MFMA and, per stage, computes on its 32 rows
 //   Z (32 rows x 32 units) = Q . W^T + b               (A: query rows from LDS)
 //   target: dH = gA . W2t^T, dZ = dH act'(Z), H = act(Z),
 //           dW2t^T (128 x 32) += gA^T . H,  dW1^T += Q^T . dZ,  db1 += sum dZ
@@ -982,25 +998,18 @@ template <int ACT> __device__ __forceinline__ void act_pair(float x, float &y, f
 // + i % 4 in register i, so registers 8 t .. 8 t + 7 of H or dZ are the B
 // operand of row step t as they stand, provided the transposed A operands
 // (gA^T, Q^T: dims x rows) take their rows in that order: transposing LDS
-// reads (ds_read_b64_tr_b16) of the row-major stage give it.
+// reads (ds_read_b64_tr_b16) of the row-major stage give it.  At the end the
+// second half's sums are added to the first's through LDS (fixed order).
 template <int ACT, bool TGT>
-__device__ __forceinline__ void train_bwd_item(const TrainBwdParams &a, int h, int u0, BwdStage &st_a,
-                                               BwdStage &st_b, BwdStage &st_c) {
-    const int t = threadIdx.x, w = t >> 6, lane = t & 63, hf = lane >> 5, r = lane & 31;
+__device__ __forceinline__ void train_bwd_item(const TrainBwdParams &a, int h, int u0, BwdLds &L) {
+    // the wave index as a scalar: the copies' LDS destinations stay in scalar registers
+    const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, hf = lane >> 5, r = lane & 31;
+    const int ug = w & 3, rh = w >> 2;
     const int H = TGT ? a.Ht : a.Hs;
-    const bool live = u0 + 32 * w < H;        // H is a multiple of 32: whole waves
-    const int n = min(u0 + 32 * w + r, H - 1);
+    const bool live = u0 + 32 * ug < H;       // H is a multiple of 32: whole waves
+    const int n = min(u0 + 32 * ug + r, H - 1);
     const size_t un = (size_t)h * H + n;
 
-    u32x4 wa[8], wb[8];
-    const uint16_t *Wa = (TGT ? a.W1 : a.Ws) + un * 128;
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) wa[kt] = *(const u32x4 *)(Wa + 16 * kt + 8 * hf);
-    if constexpr (TGT) {
-        const uint16_t *Wb = a.W2t + un * 128;
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt) wb[kt] = *(const u32x4 *)(Wb + 16 * kt + 8 * hf);
-    }
     const float bias = TGT ? a.b1[un] : a.bs[un];
     const float wsc = TGT ? 0.f : bf16_to_f32(a.ws2[un]);
 
@@ -1018,7 +1027,9 @@ __device__ __forceinline__ void train_bwd_item(const TrainBwdParams &a, int h, i
                 woff[hh][mi] = (uint32_t)(u * 256 + ((piece ^ tr_swizzle(u)) * 16) + (aa & 1) * 8);
             }
     }
-    const int trs = tr_swizzle(r);
+    const int rr0 = 32 * rh + r;              // this lane's row (A operands) within a stage
+    const int trs = tr_swizzle(rr0);
+    const int wrow = 32 * ug + r;             // this lane's unit row of the staged weight rows
 
     f32x16 gX[4], gY[4];          // target: dW2t^T, dW1^T; score: dWs^T (gX unused)
 #pragma unroll
@@ -1026,43 +1037,90 @@ __device__ __forceinline__ void train_bwd_item(const TrainBwdParams &a, int h, i
         gX[mi] = f32x16{};
         gY[mi] = f32x16{};
     }
-    float db = 0.f, dw = 0.f;
+    float db = 0.f, dw = 0.f, gs = 0.f;
 
     const uint16_t *Qh = a.Q + (size_t)h * a.Rpad * 128;
     const uint16_t *Gh = a.gA + (size_t)h * a.Rpad * 128;
     const float *gah = a.ga + (size_t)h * a.Rpad;
     const int nst = a.Rpad / kBwdRows;
 
-    // Stage i: rows 32 i .. 32 i + 31; every wave copies 8 rows of each table
-    // (two 1 KB copies per table), score blocks' wave 0 also the 32 gradients.
-    auto issue = [&](int i, BwdStage &dst) {
+    // the item's 128 first-layer rows (and read-out rows) once: four 1 KB
+    // copies per wave and table
+    auto stage_units = [&](const uint16_t *W, u32x4 *dst) {
+        const int umax = H - 1 - u0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int r0 = 16 * w + 4 * c, uu = r0 + (lane >> 4);
+            const size_t off = (size_t)min(uu, umax) * 128 + ((lane & 15) ^ (uu & 15)) * 8;
+            __builtin_amdgcn_global_load_lds((const void *)(W + off), (lds_void *)&dst[r0 * 16], 16, 0, 0);
+        }
+    };
+    stage_units((TGT ? a.W1 : a.Ws) + ((size_t)h * H + u0) * 128, L.w1);
+    if constexpr (TGT) stage_units(a.W2t + ((size_t)h * H + u0) * 128, L.x.w2);
+    // Stage i: rows 64 i .. 64 i + 63 into ring slot b; every wave copies 8 rows
+    // of each table (two 1 KB copies per table), score items' wave 0 also the
+    // 64 gradients.
+    auto issue = [&](int i, int b) {
         const int row0 = kBwdRows * i;
+        BwdStage &dst = L.st[b];
+        int lv = lane;                        // addresses formed here, not held across the loop
+        asm volatile("" : "+v"(lv));
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int r0 = 8 * w + 4 * c, rr = r0 + (lane >> 4);
-            const size_t off = (size_t)(row0 + rr) * 128 + ((lane & 15) ^ tr_swizzle(rr)) * 8;
+            const int r0 = 8 * w + 4 * c, rr = r0 + (lv >> 4);
+            const size_t off = (size_t)(row0 + rr) * 128 + ((lv & 15) ^ tr_swizzle(rr)) * 8;
             __builtin_amdgcn_global_load_lds((const void *)(Qh + off), (lds_void *)&dst.q[r0 * 16], 16, 0, 0);
             if constexpr (TGT)
                 __builtin_amdgcn_global_load_lds((const void *)(Gh + off), (lds_void *)&dst.g[r0 * 16], 16, 0, 0);
         }
         if constexpr (!TGT) {
-            if (w == 0 && lane < 8)
-                __builtin_amdgcn_global_load_lds((const void *)(gah + row0 + 4 * lane), (lds_void *)dst.ga, 16, 0, 0);
+            if (w == 0 && lv < 16)
+                __builtin_amdgcn_global_load_lds((const void *)(gah + row0 + 4 * lv), (lds_void *)L.x.ga[b], 16, 0, 0);
         }
     };
 
-    auto compute = [&](const BwdStage &cur) {
+    auto compute = [&](int b) {
+        const BwdStage &cur = L.st[b];
+        // the operand offsets pass through an empty asm each stage, so the
+        // compiler forms the per-read addresses at their use instead of
+        // holding every (ring slot, step) combination in registers across
+        // the loop
+        int sq = trs, sw = wrow & 15;
+        uint32_t wo[2][4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) wo[hh][mi] = woff[hh][mi];
+        asm volatile("" : "+v"(sq), "+v"(sw), "+v"(wo[0][0]), "+v"(wo[0][1]), "+v"(wo[0][2]), "+v"(wo[0][3]),
+                     "+v"(wo[1][0]), "+v"(wo[1][1]), "+v"(wo[1][2]), "+v"(wo[1][3]));
         f32x16 Z, dH;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             Z[i] = bias;
             dH[i] = 0.f;
         }
+        // operands one contraction step ahead of their products; the scheduling
+        // barriers keep the compiler from hoisting every operand read of the
+        // stage (two waves per SIMD leave 256 registers a wave)
+        auto ops = [&](int kt, u32x4 (&o)[4]) {
+            const int pos = rr0 * 16 + ((2 * kt + hf) ^ sq);
+            const int wpos = wrow * 16 + ((2 * kt + hf) ^ sw);
+            o[0] = cur.q[pos];
+            o[1] = L.w1[wpos];
+            if constexpr (TGT) {
+                o[2] = cur.g[pos];
+                o[3] = L.x.w2[wpos];
+            }
+        };
+        u32x4 op[3][4];
+        ops(0, op[0]);
+        ops(1, op[1]);
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
-            const int pos = r * 16 + ((2 * kt + hf) ^ trs);
-            Z = mfma32(cur.q[pos], wa[kt], Z);
-            if constexpr (TGT) dH = mfma32(cur.g[pos], wb[kt], dH);
+            if (kt + 2 < 8) ops(kt + 2, op[(kt + 2) % 3]);
+            Z = mfma32(op[kt % 3][0], op[kt % 3][1], Z);
+            if constexpr (TGT) dH = mfma32(op[kt % 3][2], op[kt % 3][3], dH);
+            __builtin_amdgcn_sched_barrier(0);
         }
         float hv[16], dz[16];
         if constexpr (TGT) {
@@ -1078,7 +1136,7 @@ __device__ __forceinline__ void train_bwd_item(const TrainBwdParams &a, int h, i
             float gr[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const f32x4 g4 = *(const f32x4 *)&cur.ga[8 * q + 4 * hf];
+                const f32x4 g4 = *(const f32x4 *)&L.x.ga[b][32 * rh + 8 * q + 4 * hf];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) gr[4 * q + j] = g4[j];
             }
@@ -1090,32 +1148,38 @@ __device__ __forceinline__ void train_bwd_item(const TrainBwdParams &a, int h, i
                 dz[i] = gr[i] * wsc * dy;
                 db += dz[i];
             }
+            if (u0 == 0 && ug == 0) {
+                // the group's sum of ga (the score output-bias gradient), fixed order
+#pragma unroll
+                for (int i = 0; i < 16; ++i) gs += gr[i];
+            }
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const u32x4 Db = {pack_bf16(dz[8 * tt + 0], dz[8 * tt + 1]), pack_bf16(dz[8 * tt + 2], dz[8 * tt + 3]),
                               pack_bf16(dz[8 * tt + 4], dz[8 * tt + 5]), pack_bf16(dz[8 * tt + 6], dz[8 * tt + 7])};
-            const char *qb = (const char *)cur.q + tt * 16 * 256;
+            const char *qb = (const char *)cur.q + (32 * rh + 16 * tt) * 256;
             if constexpr (TGT) {
                 const u32x4 Hb = {pack_bf16(hv[8 * tt + 0], hv[8 * tt + 1]), pack_bf16(hv[8 * tt + 2], hv[8 * tt + 3]),
                                   pack_bf16(hv[8 * tt + 4], hv[8 * tt + 5]), pack_bf16(hv[8 * tt + 6], hv[8 * tt + 7])};
-                const char *gb = (const char *)cur.g + tt * 16 * 256;
+                const char *gb = (const char *)cur.g + (32 * rh + 16 * tt) * 256;
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) {
-                    const u32x2 g0 = lds_read_tr16(gb, woff[0][mi]), g1 = lds_read_tr16(gb, woff[1][mi]);
+                    const u32x2 g0 = lds_read_tr16(gb, wo[0][mi]), g1 = lds_read_tr16(gb, wo[1][mi]);
                     gX[mi] = mfma32(u32x4{g0.x, g0.y, g1.x, g1.y}, Hb, gX[mi]);
                 }
             }
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
-                const u32x2 q0 = lds_read_tr16(qb, woff[0][mi]), q1 = lds_read_tr16(qb, woff[1][mi]);
+                const u32x2 q0 = lds_read_tr16(qb, wo[0][mi]), q1 = lds_read_tr16(qb, wo[1][mi]);
                 gY[mi] = mfma32(u32x4{q0.x, q0.y, q1.x, q1.y}, Db, gY[mi]);
             }
         }
     };
 
-    // stage i has landed once at most the next stage's copies are pending
-    auto step = [&](int i, const BwdStage &cur, BwdStage &ahead) {
+    // stage i has landed once at most the next stage's copies are pending (the
+    // weight rows, issued first, have landed with stage 0)
+    auto step = [&](int i, int b) {
         if (i + 1 < nst) {
             if constexpr (TGT) wait_vmcnt<4>();
             else {
@@ -1126,24 +1190,66 @@ __device__ __forceinline__ void train_bwd_item(const TrainBwdParams &a, int h, i
             wait_vmcnt<0>();
         }
         stage_barrier();
-        if (i + 2 < nst) issue(i + 2, ahead);
-        if (live) compute(cur);
+        if (i + 2 < nst) issue(i + 2, (b + 2) % 3);
+        if (live) compute(b);
     };
-    if (nst > 0) issue(0, st_a);
-    if (nst > 1) issue(1, st_b);
+    if (nst > 0) issue(0, 0);
+    if (nst > 1) issue(1, 1);
     for (int i = 0; i < nst; i += 3) {
-        step(i, st_a, st_c);
+        step(i, 0);
         if (i + 1 >= nst) break;
-        step(i + 1, st_b, st_a);
+        step(i + 1, 1);
         if (i + 2 >= nst) break;
-        step(i + 2, st_c, st_b);
+        step(i + 2, 2);
     }
 
-    // unit n's sums over both row halves; register i of block mi is dim
-    // 32 mi + 8 (i / 4) + 4 hf + i % 4
+    // unit n's sums: both lane halves, then the second row half's waves hand
+    // theirs to the first's through LDS (every stage read is done after the
+    // barrier), one accumulator array at a time
     db += __shfl_xor(db, 32, 64);
     dw += __shfl_xor(dw, 32, 64);
-    if (!live) return;
+    f32x4 *fold = (f32x4 *)&L;                // [unit group][16 x f32x4][64 lanes]
+    float *fs = (float *)&L + 4 * 64 * 64;    // [unit group][2][32]
+    auto hand_over = [&](f32x16 (&acc)[4]) {
+        __syncthreads();
+        if (rh == 1) {
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    fold[(ug * 16 + 4 * mi + q) * 64 + lane] =
+                        f32x4{acc[mi][4 * q], acc[mi][4 * q + 1], acc[mi][4 * q + 2], acc[mi][4 * q + 3]};
+        }
+        __syncthreads();
+        if (rh == 0) {
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 o = fold[(ug * 16 + 4 * mi + q) * 64 + lane];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[mi][4 * q + j] += o[j];
+                }
+        }
+    };
+    hand_over(gY);
+    if constexpr (TGT) hand_over(gX);
+    // ga sums: the lanes of one half hold the same 16 rows of each stage
+    gs += __shfl_xor(gs, 32, 64);
+    if (rh == 1 && hf == 0) {
+        fs[(ug * 2 + 0) * 32 + r] = db;
+        fs[(ug * 2 + 1) * 32 + r] = dw;
+        if (ug == 0 && r == 0) fs[8 * 32] = gs;
+    }
+    __syncthreads();
+    if (rh == 1 || !live) return;
+    db += fs[(ug * 2 + 0) * 32 + r];
+    dw += fs[(ug * 2 + 1) * 32 + r];
+    if constexpr (!TGT) {
+        if (u0 == 0 && ug == 0 && lane == 0) a.gbs2[h] = gs + fs[8 * 32];
+    }
+
+    // register i of block mi is dim 32 mi + 8 (i / 4) + 4 hf + i % 4
     float *gy = (TGT ? a.gW1 : a.gWs) + un * 128;
     float *gx = a.gW2t + un * 128;
 #pragma unroll
@@ -1170,14 +1276,14 @@ __device__ __forceinline__ void train_bwd_item(const TrainBwdParams &a, int h, i
 // groups' staged rows.
 template <int ACT>
 __global__ __launch_bounds__(64 * kBwdWaves, 1) void train_bwd_lds32(TrainBwdParams a) {
-    __shared__ BwdStage st_a, st_b, st_c;
+    __shared__ BwdLds L;
     const int per = (a.items + 7) / 8;
     const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
     if (item >= a.items) return;
     const int ipg = a.nut + a.nus;
     const int h = item / ipg, ri = item - h * ipg;
-    if (ri < a.nut) train_bwd_item<ACT, true>(a, h, 128 * ri, st_a, st_b, st_c);
-    else train_bwd_item<ACT, false>(a, h, 128 * (ri - a.nut), st_a, st_b, st_c);
+    if (ri < a.nut) train_bwd_item<ACT, true>(a, h, kBwdUnits * ri, L);
+    else train_bwd_item<ACT, false>(a, h, kBwdUnits * (ri - a.nut), L);
 }
 
 hipError_t launch_loss_rows(const LossRowParams &a, hipStream_t st) {

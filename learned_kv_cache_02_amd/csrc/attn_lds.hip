@@ -43,8 +43,10 @@ constexpr int kStreamPolicy = 2;
 
 }  // namespace
 
+// The kernel body for block `bid` of problem set `a` (shared by the launch of one
+// set and the launch of two sets side by side).
 template <int NW, int RT, int kStageKeys>
-__global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
+__device__ __forceinline__ void attn_rows_lds_body(const AttnParams &a, unsigned bid) {
     constexpr int kKeysPerWave = kStageKeys / NW;       // keys of a stage one wave copies
     constexpr int kCopies = kKeysPerWave / 4;           // copy instructions per wave, K and V each
     static_assert(kCopies >= 1 && kCopies * 4 * NW == kStageKeys, "stage split");
@@ -61,12 +63,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
     // 8 XCDs), so the second read of each stage hits that XCD's L2.
     int u, rb;
     if (a.xcd_group) {
-        const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+        const int x = bid & 7, y = bid >> 3;
         rb = y % a.RB;
         u = (y / a.RB) * 8 + x;
     } else {
-        u = blockIdx.x / a.RB;
-        rb = blockIdx.x - u * a.RB;
+        u = bid / a.RB;
+        rb = bid - u * a.RB;
     }
     const int p = u / a.SB, sb = u - p * a.SB;
     const int b = p / a.Hkv, h = p - b * a.Hkv;
@@ -259,6 +261,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
                 }
         }
     }
+}
+
+template <int NW, int RT, int kStageKeys>
+__global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
+    attn_rows_lds_body<NW, RT, kStageKeys>(a, blockIdx.x);
+}
+
+// Two problem sets in one grid, the first set's blocks first (the Quadrature
+// pairs beside the decode local part: the local blocks run beside the pairs'
+// instead of in a launch of their own).  Neither set may use xcd_group.
+template <int NW, int RT, int kStageKeys>
+__global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds_pair(AttnGroup gr) {
+    const unsigned b = blockIdx.x;
+    const bool second = b >= (unsigned)gr.nb0;
+    const AttnParams &a = second ? gr.p[1] : gr.p[0];
+    attn_rows_lds_body<NW, RT, kStageKeys>(a, second ? b - (unsigned)gr.nb0 : b);
 }
 
 // ---------------------------------------------------------------------------
@@ -493,6 +511,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
 // (eight waves, two per SIMD, 64-key stages).
 // RT == 2 selects the 32-row kernel (eight waves, 256 rows per block).
 LdsShape lds_shape_for(int Rp) { return Rp <= 64 ? LdsShape{4, 1, 96} : LdsShape{8, 2, 64}; }
+
+hipError_t launch_attn_rows_lds_pair(const AttnParams &p0, const AttnParams &p1, LdsShape sh, hipStream_t st) {
+    if (p0.xcd_group || p1.xcd_group) return hipErrorInvalidValue;
+    AttnGroup gr;
+    gr.p[0] = p0;
+    gr.p[1] = p1;
+    gr.nb0 = (int)((long)p0.P * p0.RB * p0.SB);
+    dim3 grid((unsigned)(gr.nb0 + (long)p1.P * p1.RB * p1.SB)), block(sh.NW * 64);
+    if (sh.NW == 4 && sh.RT == 1 && sh.SK == 96) hipLaunchKernelGGL((attn_rows_lds_pair<4, 1, 96>), grid, block, 0, st, gr);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st) {
     dim3 grid((unsigned)((long)p.P * p.RB * p.SB)), block(sh.NW * 64);

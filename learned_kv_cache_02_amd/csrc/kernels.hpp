@@ -346,6 +346,8 @@ struct LdsShape {
 };
 LdsShape lds_shape_for(int Rp);
 hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st);
+// Two problem sets of the same shape in one launch (shape {4, 1, 96} only).
+hipError_t launch_attn_rows_lds_pair(const AttnParams &p0, const AttnParams &p1, LdsShape sh, hipStream_t st);
 // One launch for two bf16 problem sets of the register-direct kernel with the same
 // head dimension and row tiling (independent blocks side by side).
 hipError_t launch_attn_partial_pair(const AttnParams &p0, const AttnParams &p1, int d, int rt, hipStream_t st);

@@ -113,14 +113,16 @@ void block_shape(int RG, int &WR, int &WS, int &RB) {
 // batches each (every CU gets the same share: the 4B document's 960 batches in
 // 256 splits = 512 blocks, two per CU, instead of 240 splits of 4 = 480 blocks);
 // otherwise every split but the last covers the same whole number of batches.
+// lds_blocks > 0: the LDS-staged kernel whatever the row count, its split count
+// aiming for that many blocks (a problem set sharing one launch with another).
 AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv, bool balanced = true,
-                   long target_waves = kTargetWaves) {
+                   long target_waves = kTargetWaves, long lds_blocks = 0) {
     AttnPlan pl;
     pl.P = P;
     pl.Rp = Rp;
     if (P == 0 || Rp == 0 || T_kv <= 0) return pl;    // nothing to attend: combine with S = 0
     const bool mfma = d->dtype == NECTAR_BF16;
-    if (mfma && d->d == 128 && Rp >= kLdsRows) {
+    if (mfma && d->d == 128 && (Rp >= kLdsRows || lds_blocks > 0)) {
         // LDS-staged kernel: blocks of 16 * NW * RT rows x key splits of whole
         // SK-key stages; a block finishes its rows in place when S == 1
         pl.lds = true;
@@ -130,7 +132,8 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv, bool bal
         pl.RB = (int)cdiv(Rp, 16L * pl.sh.NW * pl.sh.RT);
         pl.RG = (int)cdiv(Rp, 16L * pl.RT);
         const long stages = cdiv(T_kv, pl.sh.SK);
-        long S = d->splits > 0 ? d->splits : cdiv(kTargetBlocksLds, (long)P * pl.RB);
+        const long target = lds_blocks > 0 ? lds_blocks : kTargetBlocksLds;
+        long S = d->splits > 0 ? d->splits : cdiv(target, (long)P * pl.RB);
         S = S < 1 ? 1 : (S > stages ? stages : S);
         const long per = cdiv(stages, S);
         pl.chunk = (int)(per * pl.sh.SK);
@@ -1090,6 +1093,9 @@ struct StepPlan {
     bool fused = false;
     AttnPlan loc, doc, kvpl;
     MlpPlan mlpl;
+    // Quadrature pairs (LDS-staged) and a decode local part in one launch: the
+    // local part as LDS-staged blocks of the same shape beside the pairs'
+    bool kvp_pair = false;
     size_t off_doc = 0, off_mod = 0;               // fused: partial regions
     size_t off_px = 0, off_pm = 0, off_pl = 0;     // composed: scratch pairs
     size_t off_po = 0;                             // composed: scratch merged output
@@ -1146,6 +1152,27 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
         else if (exact && d->dtype == NECTAR_BF16 && sp.loc.S > 0 && !sp.loc.lds && sp.loc.RT == 1) {
             const long loc_waves = 4L * sp.loc.P * sp.loc.RB * sp.loc.SB;
             if (loc_waves < kTargetWaves / 4) sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n, true, kTargetWaves - loc_waves);
+        }
+        // Quadrature path at decode: the pairs' LDS-staged blocks and the local
+        // part's, as LDS-staged blocks of the same shape, in one launch of at
+        // most one block per CU: the local part takes its key stages as splits
+        // (at most four), the pairs the remaining block slots
+        if (sp.kvp && !exact && sp.kvpl.lds && sp.kvpl.S > 0 && !sp.kvpl.xcd && d->splits <= 0 &&
+            sp.loc.S > 0 && !sp.loc.lds && d->dtype == NECTAR_BF16 && d->d == 128 &&
+            lds_shape_for(sp.loc.Rp).NW == sp.kvpl.sh.NW && lds_shape_for(sp.loc.Rp).SK == sp.kvpl.sh.SK &&
+            lds_shape_for(sp.loc.Rp).RT == sp.kvpl.sh.RT && sp.kvpl.sh.NW == 4 && sp.kvpl.sh.SK == 96) {
+            const long lstages = cdiv(loc->T_loc, sp.kvpl.sh.SK);
+            const long lblocks = (long)sp.loc.P * std::min(lstages, 4L);
+            if (lblocks <= kTargetBlocksLds / 2) {
+                const AttnPlan l2 = plan_attn(d, sp.loc.P, sp.loc.Rp, loc->T_loc, true, kTargetWaves, lblocks);
+                const AttnPlan k2 = plan_attn(d, sp.kvpl.P, sp.kvpl.Rp, (long)m->p, true, kTargetWaves,
+                                              kTargetBlocksLds - (long)l2.P * l2.RB * l2.SB);
+                if (l2.lds && k2.lds && !l2.xcd && !k2.xcd) {
+                    sp.loc = l2;
+                    sp.kvpl = k2;
+                    sp.kvp_pair = true;
+                }
+            }
         }
         size_t off = align256(attn_partial_bytes(d, sp.loc));
         if (exact) {
@@ -1439,9 +1466,15 @@ static hipError_t run_layer_step(const nectar_attn_desc *desc, const StepPlan &s
             x.s = (const float *)(w + sp.off_mod + (size_t)desc->Hkv * sp.mlpl.SB * sp.mlpl.Rp * desc->d * 4);
             x.b2 = module->b2; x.bs2 = module->bs2;
         } else {
-            e = launch_plan(desc, sp.kvpl, attn_partial_params(desc, sp.kvpl, q, module->W, module->Z, 0,
-                                                               module->p * desc->d, 1, desc->R, (long)module->p,
-                                                               0, 0, w + sp.off_mod), st);
+            const AttnParams ap_kvp = attn_partial_params(desc, sp.kvpl, q, module->W, module->Z, 0,
+                                                          module->p * desc->d, 1, desc->R, (long)module->p, 0, 0,
+                                                          w + sp.off_mod);
+            if (sp.kvp_pair) {
+                e = launch_attn_rows_lds_pair(ap_kvp, ap_loc, sp.kvpl.sh, st);
+                loc_done = true;
+            } else {
+                e = launch_plan(desc, sp.kvpl, ap_kvp, st);
+            }
             x.S = sp.kvpl.S > 0 ? sp.kvpl.SB : 0;
             x.ml = (const float2 *)(w + sp.off_mod + (size_t)sp.kvpl.P * sp.kvpl.SB * sp.kvpl.Rp * desc->d * 4);
         }

@@ -67,6 +67,26 @@ def test_mlp_loss_grad(nx, act, R, Hq, Hkv, d, Ht, Hs):
         assert r < 3e-2, k
 
 
+def test_mlp_loss_grad_timed_shape(nx):
+    """The benchmark's training shape per KV head: 1,024 tokens x 4 query heads
+    (4,096 rows, whole 64-row stages), the 4608/2944 module (36 target and 23
+    score unit blocks of the fused backward)."""
+    R, Hq, Hkv, d, Ht, Hs = 1024, 4, 1, 128, 4608, 2944
+    print("case loss_grad timed shape R=%d Hq=%d Hkv=%d Ht=%d Hs=%d" % (R, Hq, Hkv, Ht, Hs), flush=True)
+    P, q, alpha, At = _case(7, R, Hq, Hkv, d, Ht, Hs)
+    mod = _module(nx, P, "gelu")
+    grad, loss = nx.mlp_loss_grad(dev(q), mod, dev(alpha), dev(At), Hkv, lambda_alpha=0.1, lambda_A=1.0)
+    eloss, eg = oracle.mlp_loss_grad(q, P, alpha, At, dt="bf16", Hq=Hq, Hkv=Hkv, act="gelu", lam_alpha=0.1, lam_A=1.0)
+    gl = host(loss)
+    print("  loss %s vs %s" % (gl, eloss), flush=True)
+    assert np.all(np.abs(gl - eloss) <= 2e-3 * np.abs(eloss))
+    parts = nx.mlp_grad_split(grad, mod)
+    for k in nx.MLP_PARAMS:
+        r = _rel(host(parts[k]), eg[k])
+        print("  grad %-4s rel-L2 %.3e" % (k, r), flush=True)
+        assert r < 3e-2, k
+
+
 def test_adamw_step(nx):
     import torch
     g = np.random.default_rng(5)

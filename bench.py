@@ -86,8 +86,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="CPU oracle budget of the headline sample (0: skip every CPU leg)")
     ap.add_argument("--only", default=None,
-                    choices=["stack", "c5_doc_partial", "c4_doc_partial", "c3_mlp10", "c2_doc_partial"],
-                    help="time one leg only (profiling runs): the stack, or one kernel's launches")
+                    choices=["stack", "c5_doc_partial", "c4_doc_partial", "c3_mlp10", "c2_doc_partial", "train_step"],
+                    help="time one leg only (profiling runs): the stack, one kernel's launches, or the "
+                         "module's training step")
     ap.add_argument("--no-extras", action="store_true", help="skip the extra workloads and kernels")
     return ap.parse_args()
 
@@ -126,6 +127,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.only in ("c4_doc_partial", "c3_mlp10", "c2_doc_partial"):
         print(json.dumps(profile_leg(torch, np, nectar, configs, synth, dev, args)), flush=True)
+        return
+    if args.only == "train_step":
+        print(json.dumps(train_step_bench(torch, nectar, configs, dev)), flush=True)
         return
 
     res = {
@@ -892,9 +896,10 @@ def deep_modules(torch, nectar, configs, dev):
 def train_step_bench(torch, nectar, configs, dev, tokens=1024):
     """One regression training step (loss, backward, clipping, AdamW) of the
     Qwen3-4B-shaped layer's 4608/2944 module on a batch of 1,024 query tokens x
-    32 heads with fp32 targets; roofline = the MFMA flops of its seven products
-    (two first layers, the read-out, its back-propagation, three weight
-    gradients).  Inputs N(0, 1) from a seeded device generator."""
+    32 heads with fp32 targets; roofline = the algorithmic MFMA flops of its
+    seven products (two first layers, the read-out, its back-propagation, three
+    weight gradients; the backward's recomputed pre-activations are not
+    counted).  Inputs N(0, 1) from a seeded device generator."""
     cfg = configs.C2
     m = cfg.mlps[0]
     d, Hkv, Hq = cfg.d, cfg.Hkv, cfg.Hq

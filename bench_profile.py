@@ -10,7 +10,8 @@ whose earlier launches are its warm-up).
 With ``--counters`` the file is a counter_collection.csv (``rocprofv3 --pmc``):
 per dispatch of kernel K (its most frequent launch shape) every counter is
 summed over its instances, and the table gives the average per dispatch; MFMA
-utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1,024 SIMDs).
+busy per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1,024 SIMDs), the
+GRBM counter being summed over the 8 XCDs.
 
     python3 bench_profile.py <counter_collection.csv> --counters --kernel attn_rows_lds32
 """
@@ -78,7 +79,12 @@ def counters(args):
     for c in names:
         print("| %s | %.6g |" % (c, avg[c]))
     if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
-        print("\nMFMA utilisation: %.3f" % (avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] * 1024)))
+        # GRBM_GUI_ACTIVE comes summed over the 8 XCDs' instances: / 8 = the kernel's cycles
+        cyc = avg["GRBM_GUI_ACTIVE"] / 8
+        print("\nkernel cycles %.4g; MFMA busy per SIMD: %.3f" % (cyc, avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024)))
+        if "SQ_INSTS_VALU" in avg:
+            print("VALU issue per SIMD (4 cycles a wave64 instruction): %.3f; VALU instructions per MFMA: %.1f"
+                  % (4 * avg["SQ_INSTS_VALU"] / (cyc * 1024), avg["SQ_INSTS_VALU"] / max(avg.get("SQ_INSTS_MFMA", 0), 1)))
 
 
 if __name__ == "__main__":

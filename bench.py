@@ -86,9 +86,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="CPU oracle budget of the headline sample (0: skip every CPU leg)")
     ap.add_argument("--only", default=None,
-                    choices=["stack", "c5_doc_partial", "c4_doc_partial", "c3_mlp10", "c2_doc_partial", "train_step"],
-                    help="time one leg only (profiling runs): the stack, one kernel's launches, or the "
-                         "module's training step")
+                    choices=["stack", "c5_doc_partial", "c4_doc_partial", "c3_mlp10", "c2_doc_partial", "train_step",
+                             "deep_modules"],
+                    help="time one leg only (profiling runs): the stack, one kernel's launches, the "
+                         "module's training step, or the deep modules")
     ap.add_argument("--no-extras", action="store_true", help="skip the extra workloads and kernels")
     return ap.parse_args()
 
@@ -130,6 +131,9 @@ def main():
         return
     if args.only == "train_step":
         print(json.dumps(train_step_bench(torch, nectar, configs, dev)), flush=True)
+        return
+    if args.only == "deep_modules":
+        print(json.dumps(deep_modules(torch, nectar, configs, dev)), flush=True)
         return
 
     res = {

@@ -201,8 +201,11 @@ def stack_c5(torch, nectar, configs, dev, args):
         return out
 
     t0 = time.time()
-    K = [rn(Hkv, n, d) for _ in range(L)]
-    V = [rn(Hkv, n, d) for _ in range(L)]
+    # each layer's document cache: one [Hkv][n][2][d] array, K and V interleaved by
+    # key (a KV head's key range streams as one contiguous range)
+    KV = [rn(Hkv, n, 2, d) for _ in range(L)]
+    K = [x[:, :, 0] for x in KV]
+    V = [x[:, :, 1] for x in KV]
     steps_total = args.warmup + args.steps
     z = lambda *s: torch.zeros(*s, device=dev)
     layers = []
@@ -345,6 +348,7 @@ def stack_c5(torch, nectar, configs, dev, args):
                                   "257..384 local keys; one step = one decode step of all 28 layers through the "
                                   "Nectar (MLP 5120/3072), Quadrature (p=10,486) and exact paths; value = Nectar path",
                       "global_batch": B, "seq_len": n + cfg.T_cap, "layers": L, "parallelism": "single-gpu",
+                      "document_cache": "per layer one bf16 [Hkv][n][2][d] array, K and V interleaved by key",
                       "graph": "one HIP graph per path and decode step"}
     extra["paths"] = paths
     extra["timing"] = {"ms_per_step": "all three paths (Nectar, Quadrature, exact) of one decode step of the stack",
@@ -379,7 +383,13 @@ def c2_layer(torch, np, nectar, configs, synth, dev, nrep=24, passes=10):
     Kl0, Vl0 = (up(x) for x in synth.local_kv(cfg))
     P = synth.mlp_params(cfg)
     mod0 = [up(P[k]) for k in ("W1", "b1", "W2t", "b2", "Ws", "bs", "ws2", "bs2")]
-    reps = [dict(q=q0.clone(), K=K0.clone(), V=V0.clone(), Kl=Kl0.clone(), Vl=Vl0.clone(),
+
+    def interleaved(K_, V_):
+        # one [Hkv][n][2][d] array, K and V interleaved by key, as the stack stores its caches
+        kv = torch.stack((K_, V_), dim=2)
+        return kv[:, :, 0], kv[:, :, 1]
+
+    reps = [dict(q=q0.clone(), **dict(zip(("K", "V"), interleaved(K0, V0))), Kl=Kl0.clone(), Vl=Vl0.clone(),
                  mod=nectar.MLPModule(*(t.clone() for t in mod0))) for _ in range(nrep)]
     del K0, V0
     f32 = dict(dtype=torch.float32, device=dev)
@@ -501,7 +511,7 @@ def profile_leg(torch, np, nectar, configs, synth, dev, args):
     if args.only == "c4_doc_partial":
         cfg = configs.C4
         q = rn(cfg.R, cfg.Hq, cfg.d)
-        KV = [(rn(cfg.Hkv, cfg.n, cfg.d), rn(cfg.Hkv, cfg.n, cfg.d)) for _ in range(2)]
+        KV = [(x[:, :, 0], x[:, :, 1]) for x in (rn(cfg.Hkv, cfg.n, 2, cfg.d) for _ in range(2))]   # interleaved by key
         part = torch.empty(max(16, nectar.doc_attn_partials_size(nectar.desc(cfg.R, cfg.Hq, cfg.Hkv, cfg.d, nectar.BF16),
                                                                   cfg.n)), dtype=torch.uint8, device=dev)
         call = lambda i: nectar.doc_attn_partials(q, KV[i % 2][0], KV[i % 2][1], cfg.Hkv, partials=part)
@@ -509,7 +519,7 @@ def profile_leg(torch, np, nectar, configs, synth, dev, args):
     elif args.only == "c2_doc_partial":
         cfg = configs.C2
         q = rn(cfg.R, cfg.Hq, cfg.d)
-        KV = [(rn(cfg.Hkv, cfg.n, cfg.d), rn(cfg.Hkv, cfg.n, cfg.d)) for _ in range(16)]
+        KV = [(x[:, :, 0], x[:, :, 1]) for x in (rn(cfg.Hkv, cfg.n, 2, cfg.d) for _ in range(16))]  # interleaved by key
         part = torch.empty(max(16, nectar.doc_attn_partials_size(nectar.desc(cfg.R, cfg.Hq, cfg.Hkv, cfg.d, nectar.BF16),
                                                                   cfg.n)), dtype=torch.uint8, device=dev)
         call = lambda i: nectar.doc_attn_partials(q, KV[i % 16][0], KV[i % 16][1], cfg.Hkv, partials=part)
@@ -659,7 +669,8 @@ def workload_layer(torch, nectar, cfg, dev):
     doc_bytes = Hkv * n * 2 * d * 2
     nrep = 1 if cfg.prefill or doc_bytes >= (2 << 30) else 2
     q = rn(R, Hq, d)
-    KV = [(rn(Hkv, n, d), rn(Hkv, n, d)) for _ in range(nrep)]
+    # document caches interleaved by key ([Hkv][n][2][d]), as the stack stores them
+    KV = [(x[:, :, 0], x[:, :, 1]) for x in (rn(Hkv, n, 2, d) for _ in range(nrep))]
     Kl, Vl = rn(cfg.B, Hkv, cfg.T_cap, d), rn(cfg.B, Hkv, cfg.T_cap, d)
     m = cfg.mlps[-1]
     z = lambda *s: torch.zeros(*s, device=dev)

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define NECTAR_ABI_VERSION 2
+#define NECTAR_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define NECTAR_API __attribute__((visibility("default")))
@@ -96,6 +96,15 @@ typedef struct {
                         splits per head, clamped to [1, number of key tiles]
                         (64 keys per tile for bf16, 32 for fp32; 32 hidden units).
                         Results agree across split counts up to rounding. */
+    int32_t kv_stride; /* document cache rows (the k, v arguments of the exact
+                        document attention and of the layer step; not the local
+                        cache, not module tensors): elements from one key's row
+                        to the next's, the KV head's rows starting n of these
+                        apart.  0 (or d): dense [Hkv][n][d] arrays.  2d with
+                        v = k + d: K and V interleaved by key in one
+                        [Hkv][n][2][d] array, which streams as one contiguous
+                        range per key range.  Otherwise a multiple of 8, d or
+                        more, at most 2^20; anything else is NECTAR_EINVAL. */
 } nectar_attn_desc;
 
 /* The local (question + generated tokens) cache of nectar_local_attn_lse. */

@@ -69,14 +69,14 @@ __global__ __launch_bounds__(256) void attn_partial_valu(AttnParams a) {
     for (int j = k_lo; j < k_hi; ++j) {
         float part = 0.f;
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) part += qf[i] * Elem<T>::ld(kb, (size_t)j * D + lane + 64 * i);
+        for (int i = 0; i < NPL; ++i) part += qf[i] * Elem<T>::ld(kb, (size_t)j * a.kv_row + lane + 64 * i);
         const float s2 = wave_sum(part) * a.sl2;
         const float mnew = fmaxf(m, s2);
         const float alpha = exp2f(m - mnew);
         const float pj = exp2f(s2 - mnew);
         l = l * alpha + pj;
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) acc[i] = acc[i] * alpha + pj * Elem<T>::ld(vb, (size_t)j * D + lane + 64 * i);
+        for (int i = 0; i < NPL; ++i) acc[i] = acc[i] * alpha + pj * Elem<T>::ld(vb, (size_t)j * a.kv_row + lane + 64 * i);
         m = mnew;
     }
     const size_t row = (size_t)(p * a.S + s) * a.Rp + rho;

@@ -18,19 +18,19 @@ template <int D> struct KVTile {
 
 template <int D>
 __device__ __forceinline__ void load_kv_tile(KVTile<D> &T, const uint16_t *kb, const uint16_t *vb,
-                                             int k0, int kmax, int g, int c) {
+                                             int64_t row, int k0, int kmax, int g, int c) {
     constexpr int KS = D / 32, DV = D / 16;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int key = min(k0 + 16 * hh + c, kmax);
-        const uint16_t *kp = kb + (size_t)key * D;
+        const uint16_t *kp = kb + (size_t)key * row;
 #pragma unroll
         for (int kt = 0; kt < KS; ++kt) T.k[hh][kt] = stream_load((const u32x4 *)(kp + (4 * kt + g) * 8));
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int key = min(k0 + slot_key(g, j), kmax);
-        T.v[j] = stream_load((const typename VRow<D>::T *)(vb + (size_t)key * D + c * DV));
+        T.v[j] = stream_load((const typename VRow<D>::T *)(vb + (size_t)key * row + c * DV));
     }
 }
 
@@ -177,7 +177,7 @@ __device__ __forceinline__ void attn_partial_body(const AttnParams &a, int blk_i
         for (int k0 = k_lo; k0 < k_hi; k0 += 32 * SUB) {
             KVTile<D> tl[SUB];
 #pragma unroll
-            for (int u = 0; u < SUB; ++u) load_kv_tile<D>(tl[u], kb, vb, min(k0 + 32 * u, kmax), kmax, g, c);
+            for (int u = 0; u < SUB; ++u) load_kv_tile<D>(tl[u], kb, vb, a.kv_row, min(k0 + 32 * u, kmax), kmax, g, c);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < SUB; ++u) attend_tile<D, RT>(tl[u], k0 + 32 * u, qv, limw, a.sl2, g, O, m, l);

@@ -130,7 +130,7 @@ __device__ __forceinline__ void attn_rows_lds_body(const AttnParams &a, unsigned
             const int r0 = kKeysPerWave * w + 4 * u, r = r0 + (lane >> 4);
             const int key = min(key0 + r, kmax);
             const int piece = (lane & 15) ^ (r & 15);
-            const size_t off = (size_t)key * kD + piece * 8;
+            const size_t off = (size_t)key * a.kv_row + piece * 8;
             __builtin_amdgcn_global_load_lds((const void *)(kb + off), (lds_void *)&dst[0][r0 * kPieces],
                                              16, 0, kStreamPolicy);
             __builtin_amdgcn_global_load_lds((const void *)(vb + off), (lds_void *)&dst[1][r0 * kPieces],
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
             const int key = min(key0 + rr, kmax);
             // K rows swizzled by the key (conflict-free 16-byte reads), V rows by
             // tr_swizzle (conflict-free transposing reads)
-            const size_t row = (size_t)key * kD;
+            const size_t row = (size_t)key * a.kv_row;
             const int kpiece = (lane & 15) ^ (rr & 15), vpiece = (lane & 15) ^ tr_swizzle(rr);
             __builtin_amdgcn_global_load_lds((const void *)(kb + row + kpiece * 8), (lds_void *)&dst[0][r0 * kPieces], 16, 0, kStreamPolicy);
             __builtin_amdgcn_global_load_lds((const void *)(vb + row + vpiece * 8), (lds_void *)&dst[1][r0 * kPieces], 16, 0, kStreamPolicy);

@@ -13,6 +13,7 @@ namespace nectar {
 struct AttnParams {
     const void *q, *k, *v;
     int64_t kv_bstride, kv_hstride;
+    int64_t kv_row;      // elements from one key's K (or V) row to the next's (d: dense rows)
     int Hq, G, Hkv, Tq, B, Rp, T_kv, causal, q_offset;
     float sl2;           // score scale * log2(e)
     // split plan: S key splits of `chunk` keys; RG row groups of 16*RT rows.

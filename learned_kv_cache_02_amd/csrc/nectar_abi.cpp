@@ -76,6 +76,9 @@ nectar_status check_desc(const nectar_attn_desc *d) {
     if (d->d <= 0) return NECTAR_EINVAL;
     if (d->d != 64 && d->d != 128) return NECTAR_EUNSUPPORTED;
     if (!std::isfinite(d->scale) || d->splits < 0) return NECTAR_EINVAL;
+    // document K/V row stride: 0 (dense rows) or at least d, whole 16-byte pieces
+    if (d->kv_stride != 0 && (d->kv_stride < d->d || d->kv_stride % 8 != 0 || d->kv_stride > (1 << 20)))
+        return NECTAR_EINVAL;
     if ((long)d->R * d->Hq > 0x7fffffffL / 2) return NECTAR_EUNSUPPORTED;
     return NECTAR_OK;
 }
@@ -83,6 +86,10 @@ nectar_status check_desc(const nectar_attn_desc *d) {
 inline float score_scale(const nectar_attn_desc *d) {
     return d->scale != 0.f ? d->scale : 1.0f / std::sqrt((float)d->d);
 }
+
+// Elements from one document key's K (or V) row to the next's; a KV head's
+// rows start n of these apart.
+inline int64_t doc_row(const nectar_attn_desc *d) { return d->kv_stride > 0 ? d->kv_stride : d->d; }
 
 // Tensors read with 16-byte vector loads must be 16-byte aligned; fp32 scalars
 // and outputs written element-wise need their natural alignment.
@@ -317,7 +324,7 @@ nectar_status finish(hipError_t e, hipStream_t st) {
 // Attention over a batched cache, then (unless one block per row group covered
 // every key) the combine pass.
 hipError_t run_attention(const nectar_attn_desc *d, const AttnPlan &pl, const void *q, const void *k,
-                         const void *v, int64_t bstride, int64_t hstride, int B, int Tq, long T_kv,
+                         const void *v, int64_t bstride, int64_t hstride, int64_t row, int B, int Tq, long T_kv,
                          int causal, int q_offset, CombineParams cp, void *ws, hipStream_t st) {
     const bool mfma = d->dtype == NECTAR_BF16;
     float *part_O = (float *)ws;
@@ -325,7 +332,7 @@ hipError_t run_attention(const nectar_attn_desc *d, const AttnPlan &pl, const vo
     if (pl.S > 0) {
         AttnParams a{};
         a.q = q; a.k = k; a.v = v;
-        a.kv_bstride = bstride; a.kv_hstride = hstride;
+        a.kv_bstride = bstride; a.kv_hstride = hstride; a.kv_row = row;
         a.Hq = d->Hq; a.G = d->Hq / d->Hkv; a.Hkv = d->Hkv; a.Tq = Tq; a.B = B; a.Rp = pl.Rp;
         a.T_kv = (int)T_kv; a.causal = causal; a.q_offset = q_offset;
         a.sl2 = score_scale(d) * 1.4426950408889634f;
@@ -391,7 +398,7 @@ nectar_status nectar_doc_attn_exact(const nectar_attn_desc *desc, int64_t n, con
     cp.lse_out = alpha_out;
     cp.A_out = A_out;
     hipStream_t st = (hipStream_t)stream;
-    return finish(run_attention(desc, pl, q, k, v, 0, (int64_t)n * desc->d, 1, desc->R, (long)n, 0, 0,
+    return finish(run_attention(desc, pl, q, k, v, 0, (int64_t)n * doc_row(desc), doc_row(desc), 1, desc->R, (long)n, 0, 0,
                                 cp, ws, st), st);
 }
 
@@ -597,7 +604,7 @@ nectar_status nectar_module_forward(const nectar_attn_desc *desc, const nectar_m
         CombineParams cp{};
         cp.lse_out = a_out;
         cp.A_out = A_out;
-        return finish(run_attention(desc, pl, q, m->W, m->Z, 0, m->p * desc->d, 1, desc->R, (long)m->p,
+        return finish(run_attention(desc, pl, q, m->W, m->Z, 0, m->p * desc->d, desc->d, 1, desc->R, (long)m->p,
                                     0, 0, cp, ws, st), st);
     }
     if (m->kind == NECTAR_MODULE_DEEP_MLP) {
@@ -651,7 +658,7 @@ nectar_status nectar_local_attn_lse(const nectar_attn_desc *desc, const nectar_l
     cp.out_lse = out_lse;
     hipStream_t st = (hipStream_t)stream;
     const int64_t hstride = (int64_t)loc->T_cap * desc->d;
-    return finish(run_attention(desc, pl, q, k_loc, v_loc, hstride * desc->Hkv, hstride, loc->B, loc->Tq,
+    return finish(run_attention(desc, pl, q, k_loc, v_loc, hstride * desc->Hkv, hstride, desc->d, loc->B, loc->Tq,
                                 loc->T_loc, 1, loc->q_offset, cp, ws, st), st);
 }
 
@@ -1207,11 +1214,11 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
 // Deferred-finish parameters of one attention plan writing into part
 // (read-outs, then statistics).
 static AttnParams attn_partial_params(const nectar_attn_desc *d, const AttnPlan &pl, const void *q, const void *k,
-                                      const void *v, int64_t bstride, int64_t hstride, int B, int Tq, long T_kv,
-                                      int causal, int q_offset, void *part) {
+                                      const void *v, int64_t bstride, int64_t hstride, int64_t row, int B, int Tq,
+                                      long T_kv, int causal, int q_offset, void *part) {
     AttnParams a{};
     a.q = q; a.k = k; a.v = v;
-    a.kv_bstride = bstride; a.kv_hstride = hstride;
+    a.kv_bstride = bstride; a.kv_hstride = hstride; a.kv_row = row;
     a.Hq = d->Hq; a.G = d->Hq / d->Hkv; a.Hkv = d->Hkv; a.Tq = Tq; a.B = B; a.Rp = pl.Rp;
     a.T_kv = (int)T_kv; a.causal = causal; a.q_offset = q_offset;
     a.sl2 = score_scale(d) * 1.4426950408889634f;
@@ -1275,7 +1282,8 @@ static hipError_t run_step_composed(const nectar_attn_desc *desc, const StepPlan
         pair(sp.off_px, outs->alpha_out, outs->A_out, &al, &Ax);
         CombineParams cp{};
         cp.lse_out = al; cp.A_out = Ax;
-        e = run_attention(desc, sp.doc, q, k, v, 0, n * desc->d, 1, desc->R, (long)n, 0, 0, cp, w, st);
+        e = run_attention(desc, sp.doc, q, k, v, 0, n * doc_row(desc), doc_row(desc), 1, desc->R, (long)n, 0, 0, cp,
+                          w, st);
         if (outs->out_exact || outs->lse_exact) mg[nm++] = Merge{al, Ax, outs->out_exact, outs->lse_exact};
     }
     if (e == hipSuccess && module) {
@@ -1288,7 +1296,7 @@ static hipError_t run_step_composed(const nectar_attn_desc *desc, const StepPlan
         } else {
             CombineParams cp{};
             cp.lse_out = am; cp.A_out = Am;
-            e = run_attention(desc, sp.kvpl, q, module->W, module->Z, 0, module->p * desc->d, 1, desc->R,
+            e = run_attention(desc, sp.kvpl, q, module->W, module->Z, 0, module->p * desc->d, desc->d, 1, desc->R,
                               (long)module->p, 0, 0, cp, w, st);
         }
         if (outs->out_nectar || outs->lse_nectar) mg[nm++] = Merge{am, Am, outs->out_nectar, outs->lse_nectar};
@@ -1304,7 +1312,7 @@ static hipError_t run_step_composed(const nectar_attn_desc *desc, const StepPlan
         cp.x_lse = mg[0].lse; cp.x_A = mg[0].A; cp.out = mg[0].out; cp.out_lse = mg[0].out_lse;
     }
     const int64_t hstride = (int64_t)loc->T_cap * desc->d;
-    e = run_attention(desc, sp.loc, q, k_loc, v_loc, hstride * desc->Hkv, hstride, loc->B, loc->Tq, loc->T_loc, 1,
+    e = run_attention(desc, sp.loc, q, k_loc, v_loc, hstride * desc->Hkv, hstride, desc->d, loc->B, loc->Tq, loc->T_loc, 1,
                       loc->q_offset, cp, w, st);
     for (int i = 1; i < nm && e == hipSuccess; ++i) {
         // out may be NULL (only the merged log-normaliser requested): write the output to scratch
@@ -1338,7 +1346,8 @@ nectar_status nectar_doc_attn_partials(const nectar_attn_desc *desc, int64_t n, 
     const AttnPlan pl = plan_attn(desc, desc->Hkv, desc->R * (desc->Hq / desc->Hkv), (long)n);
     if ((s = check_ws(attn_partial_bytes(desc, pl), partials, bytes)) != NECTAR_OK) return s;
     hipStream_t st = (hipStream_t)stream;
-    const AttnParams a = attn_partial_params(desc, pl, q, k, v, 0, n * desc->d, 1, desc->R, (long)n, 0, 0, partials);
+    const AttnParams a = attn_partial_params(desc, pl, q, k, v, 0, n * doc_row(desc), doc_row(desc), 1, desc->R,
+                                             (long)n, 0, 0, partials);
     return finish(launch_plan(desc, pl, a, st), st);
 }
 
@@ -1420,11 +1429,11 @@ static hipError_t run_layer_step(const nectar_attn_desc *desc, const StepPlan &s
     f.lam_out = outs->lam_out; f.Aloc_out = outs->Aloc_out;
     hipError_t e = hipSuccess;
     const int64_t hstride = (int64_t)loc->T_cap * desc->d;
-    const AttnParams ap_loc = attn_partial_params(desc, sp.loc, q, k_loc, v_loc, hstride * desc->Hkv, hstride,
+    const AttnParams ap_loc = attn_partial_params(desc, sp.loc, q, k_loc, v_loc, hstride * desc->Hkv, hstride, desc->d,
                                                   loc->B, loc->Tq, loc->T_loc, 1, loc->q_offset, w);
     bool loc_done = false, mod_done = false;
-    const AttnParams ap_doc = attn_partial_params(desc, sp.doc, q, k, v, 0, n * desc->d, 1, desc->R, (long)n,
-                                                  0, 0, w + sp.off_doc);
+    const AttnParams ap_doc = attn_partial_params(desc, sp.doc, q, k, v, 0, n * doc_row(desc), doc_row(desc), 1,
+                                                  desc->R, (long)n, 0, 0, w + sp.off_doc);
     MlpParams mp{};
     if (sp.mlp) mp = mlp_partial_params(desc, sp.mlpl, module, q, w + sp.off_mod);
     // decode shapes: the attention blocks and the module's blocks in one launch
@@ -1467,8 +1476,8 @@ static hipError_t run_layer_step(const nectar_attn_desc *desc, const StepPlan &s
             x.b2 = module->b2; x.bs2 = module->bs2;
         } else {
             const AttnParams ap_kvp = attn_partial_params(desc, sp.kvpl, q, module->W, module->Z, 0,
-                                                          module->p * desc->d, 1, desc->R, (long)module->p, 0, 0,
-                                                          w + sp.off_mod);
+                                                          module->p * desc->d, desc->d, 1, desc->R, (long)module->p,
+                                                          0, 0, w + sp.off_mod);
             if (sp.kvp_pair) {
                 e = launch_attn_rows_lds_pair(ap_kvp, ap_loc, sp.kvpl.sh, st);
                 loc_done = true;

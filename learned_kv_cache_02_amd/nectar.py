@@ -37,7 +37,7 @@ STATUS = {0: "NECTAR_OK", 1: "NECTAR_EINVAL", 2: "NECTAR_EUNSUPPORTED", 3: "NECT
 class AttnDesc(ctypes.Structure):
     _fields_ = [("R", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("splits", ctypes.c_int32)]
+                ("splits", ctypes.c_int32), ("kv_stride", ctypes.c_int32)]
 
 
 class LocalDesc(ctypes.Structure):
@@ -144,6 +144,12 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _kv_ptr(t: Optional[torch.Tensor]):
+    """Address of a document K or V argument whose layout _doc_kv has checked
+    (possibly a strided view)."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -178,9 +184,10 @@ def _arg(x, name, shape, dtype):
     return x
 
 
-def _on_gpu(ref, *named):
-    """Every given tensor on the GPU device of `ref` and contiguous (after the shape
-    and type checks, so those are reported first)."""
+def _on_gpu(ref, *named, strided=()):
+    """Every given tensor on the GPU device of `ref` and contiguous, except the
+    names in `strided` (whose layout the caller has checked) -- after the shape and
+    type checks, so those are reported first."""
     dev = ref.device
     for name, t in named:
         if t is None:
@@ -189,8 +196,29 @@ def _on_gpu(ref, *named):
             raise ValueError("%s must be in GPU device memory, got a tensor on %s" % (name, t.device))
         if t.device != dev:
             raise ValueError("%s is on %s, the call's tensors are on %s" % (name, t.device, dev))
-        if not t.is_contiguous():
+        if name not in strided and not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
+
+
+def _doc_kv(k, v, Hkv, d, code, ref):
+    """The document cache k, v [Hkv][n][d]: two contiguous arrays, or two views with
+    one row stride s (a multiple of 8, at least d) and head stride n * s -- e.g.
+    k = kv[:, :, 0] and v = kv[:, :, 1] of one contiguous [Hkv][n][2][d] array (K
+    and V interleaved by key).  Shapes, types and strides checked on the host (the
+    device by _on_gpu, which lets these two be strided); returns (n, kv_stride for
+    the descriptor, 0 when dense)."""
+    _arg(k, "k", (Hkv, None, d), code)
+    n = k.shape[1]
+    _arg(v, "v", (Hkv, n, d), code)
+    if k.is_contiguous() and v.is_contiguous():
+        return n, 0
+    s_ = k.stride(1)
+    if (k.stride(2) != 1 or v.stride(2) != 1 or v.stride(1) != s_ or s_ < d or s_ % 8 or s_ > (1 << 20)
+            or (Hkv > 1 and (k.stride(0) != n * s_ or v.stride(0) != n * s_))):
+        raise ValueError("k and v must be contiguous [Hkv][n][d] arrays or views with one row stride (a multiple "
+                         "of 8, at least d) and head stride n * row stride; got strides %s and %s"
+                         % (tuple(k.stride()), tuple(v.stride())))
+    return n, s_
 
 
 def _q(q, name="q"):
@@ -200,8 +228,8 @@ def _q(q, name="q"):
     return q.shape[0], q.shape[1], q.shape[2], dtype_code(q)
 
 
-def desc(R, Hq, Hkv, d, dtype, scale=0.0, splits=0) -> AttnDesc:
-    return AttnDesc(int(R), int(Hq), int(Hkv), int(d), int(dtype), float(scale), int(splits))
+def desc(R, Hq, Hkv, d, dtype, scale=0.0, splits=0, kv_stride=0) -> AttnDesc:
+    return AttnDesc(int(R), int(Hq), int(Hkv), int(d), int(dtype), float(scale), int(splits), int(kv_stride))
 
 
 _ws_cache = {}
@@ -243,21 +271,19 @@ def doc_attn_workspace_size(dsc: AttnDesc, n: int) -> int:
 def doc_attn_exact(q, k, v, Hkv, *, scale=0.0, splits=0, alpha_out=None, A_out=None):
     """Exact document attention (alpha [R][Hq], A [R][Hq][d] fp32); q [R][Hq][d], k/v [Hkv][n][d]."""
     R, Hq, d, code = _q(q)
-    _arg(k, "k", (Hkv, None, d), code)
-    n = k.shape[1]
-    _arg(v, "v", (Hkv, n, d), code)
+    n, kvs = _doc_kv(k, v, Hkv, d, code, q)
     if alpha_out is not None:
         _arg(alpha_out, "alpha_out", (R, Hq), F32T)
     if A_out is not None:
         _arg(A_out, "A_out", (R, Hq, d), F32T)
-    _on_gpu(q, ("q", q), ("k", k), ("v", v), ("alpha_out", alpha_out), ("A_out", A_out))
-    dsc = desc(R, Hq, Hkv, d, code, scale, splits)
+    _on_gpu(q, ("q", q), ("k", k), ("v", v), ("alpha_out", alpha_out), ("A_out", A_out), strided=("k", "v"))
+    dsc = desc(R, Hq, Hkv, d, code, scale, splits, kvs)
     if alpha_out is None:
         alpha_out = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
     if A_out is None:
         A_out = torch.empty((R, Hq, d), dtype=torch.float32, device=q.device)
     wp, wn = _ws_args(doc_attn_workspace_size(dsc, n), q.device)
-    _check(_lib.nectar_doc_attn_exact(ctypes.byref(dsc), n, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha_out),
+    _check(_lib.nectar_doc_attn_exact(ctypes.byref(dsc), n, _ptr(q), _kv_ptr(k), _kv_ptr(v), _ptr(alpha_out),
                                       _ptr(A_out), wp, wn, _stream()))
     return alpha_out, A_out
 
@@ -270,17 +296,15 @@ def doc_attn_partials(q, k, v, Hkv, *, scale=0.0, splits=0, partials=None):
     """First pass of the exact document attention: the split-K partials, into a
     uint8 device tensor (allocated when not given).  Returns the tensor."""
     R, Hq, d, code = _q(q)
-    _arg(k, "k", (Hkv, None, d), code)
-    n = k.shape[1]
-    _arg(v, "v", (Hkv, n, d), code)
+    n, kvs = _doc_kv(k, v, Hkv, d, code, q)
     if partials is not None:
         _arg(partials, "partials", (None,), torch.uint8)
-    _on_gpu(q, ("q", q), ("k", k), ("v", v), ("partials", partials))
-    dsc = desc(R, Hq, Hkv, d, code, scale, splits)
+    _on_gpu(q, ("q", q), ("k", k), ("v", v), ("partials", partials), strided=("k", "v"))
+    dsc = desc(R, Hq, Hkv, d, code, scale, splits, kvs)
     nbytes = int(_lib.nectar_doc_attn_partials_size(ctypes.byref(dsc), n))
     if partials is None:
         partials = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    _check(_lib.nectar_doc_attn_partials(ctypes.byref(dsc), n, _ptr(q), _ptr(k), _ptr(v), _ptr(partials),
+    _check(_lib.nectar_doc_attn_partials(ctypes.byref(dsc), n, _ptr(q), _kv_ptr(k), _kv_ptr(v), _ptr(partials),
                                          partials.numel(), _stream()))
     return partials
 
@@ -680,11 +704,9 @@ def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, 
     _arg(k_loc, "k_loc", (B, Hkv, None, d), code)
     T_cap = k_loc.shape[2]
     _arg(v_loc, "v_loc", (B, Hkv, T_cap, d), code)
-    n = 0
+    n, kvs = 0, 0
     if exact and k is not None:
-        _arg(k, "k", (Hkv, None, d), code)
-        n = k.shape[1]
-        _arg(v, "v", (Hkv, n, d), code)
+        n, kvs = _doc_kv(k, v, Hkv, d, code, q)
     named = module.check(Hkv, d, code) if module is not None else []
     shapes = {"out_exact": ((R, Hq, d), code), "lse_exact": ((R, Hq), F32T), "alpha": ((R, Hq), F32T),
               "A": ((R, Hq, d), F32T), "out_nectar": ((R, Hq, d), code), "lse_nectar": ((R, Hq), F32T),
@@ -694,8 +716,8 @@ def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, 
             raise ValueError("layer_step: unknown output %r" % key)
         _arg(t, "out[%r]" % key, *shapes[key])
     _on_gpu(q, ("q", q), ("k_loc", k_loc), ("v_loc", v_loc), ("k", k if exact else None), ("v", v if exact else None),
-            *named, *[("out[%r]" % key, t) for key, t in (out or {}).items()])
-    dsc = desc(R, Hq, Hkv, d, code, scale, splits)
+            *named, *[("out[%r]" % key, t) for key, t in (out or {}).items()], strided=("k", "v"))
+    dsc = desc(R, Hq, Hkv, d, code, scale, splits, kvs)
     loc = LocalDesc(int(B), int(Tq), int(T_loc), int(T_cap), int(q_offset))
     o = dict(out or {})
     f32 = dict(dtype=torch.float32, device=q.device)
@@ -722,13 +744,13 @@ def layer_step(q, k_loc, v_loc, Hkv, *, B, Tq, T_loc, q_offset, k=None, v=None, 
     mp = ctypes.byref(m) if m is not None else None
     if no_alloc:
         _check(_lib.nectar_layer_step_static(ctypes.byref(dsc), n, ctypes.byref(loc), _ptr(q),
-                                             _ptr(k) if exact else None, _ptr(v) if exact else None, _ptr(k_loc),
+                                             _kv_ptr(k) if exact else None, _kv_ptr(v) if exact else None, _ptr(k_loc),
                                              _ptr(v_loc), mp, ctypes.byref(so), _stream()))
         return o
     nbytes = int(_lib.nectar_layer_step_workspace_size(ctypes.byref(dsc), n, ctypes.byref(loc), mp, int(exact)))
     wp, wn = _ws_args(nbytes, q.device)
-    _check(_lib.nectar_layer_step(ctypes.byref(dsc), n, ctypes.byref(loc), _ptr(q), _ptr(k) if exact else None,
-                                  _ptr(v) if exact else None, _ptr(k_loc), _ptr(v_loc), mp, ctypes.byref(so),
+    _check(_lib.nectar_layer_step(ctypes.byref(dsc), n, ctypes.byref(loc), _ptr(q), _kv_ptr(k) if exact else None,
+                                  _kv_ptr(v) if exact else None, _ptr(k_loc), _ptr(v_loc), mp, ctypes.byref(so),
                                   wp, wn, _stream()))
     return o
 

@@ -20,7 +20,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 class Desc(ctypes.Structure):
     _fields_ = [("R", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("splits", ctypes.c_int32)]
+                ("splits", ctypes.c_int32), ("kv_stride", ctypes.c_int32)]
 
 
 class Local(ctypes.Structure):
@@ -110,7 +110,7 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.nectar_abi_version() == 2
+    assert lib.nectar_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -134,6 +134,11 @@ def test_doc_attn_validation(lib):
     assert _doc(lib, Desc(-1, 8, 4, 128, 1, 0.0, 0)) == EINVAL
     assert _doc(lib, Desc(2, 8, 4, 128, 1, float("nan"), 0)) == EINVAL
     assert _doc(lib, Desc(2, 8, 4, 128, 1, 0.0, -3)) == EINVAL
+    # document K/V row stride: 0, or whole 16-byte pieces of at least d elements
+    assert _doc(lib, Desc(2, 8, 4, 128, 1, 0.0, 0, 64)) == EINVAL       # shorter than a row
+    assert _doc(lib, Desc(2, 8, 4, 128, 1, 0.0, 0, 132)) == EINVAL      # not a multiple of 8
+    assert _doc(lib, Desc(2, 8, 4, 128, 1, 0.0, 0, -256)) == EINVAL
+    assert _doc(lib, Desc(2, 8, 4, 128, 1, 0.0, 0, 1 << 21)) == EINVAL
     ok = Desc(2, 8, 4, 128, 1, 0.0, 0)
     assert _doc(lib, ok, n=-1) == EINVAL
     assert _doc(lib, ok, q=None) == EINVAL

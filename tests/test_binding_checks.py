@@ -44,6 +44,20 @@ def test_doc_attn_checks():
            partials=t(64, dtype=torch.float32))
 
 
+def test_doc_kv_layout_checks():
+    """The document cache may be two views with one row stride (K and V
+    interleaved by key); other layouts are refused on the host."""
+    kv = t(Hkv, n, 2, d)
+    # interleaved views pass the layout check (then the device check: CPU tensors here)
+    raises("GPU device memory", nx.doc_attn_exact, t(R, Hq, d), kv[:, :, 0], kv[:, :, 1], Hkv)
+    raises("GPU device memory", nx.doc_attn_partials, t(R, Hq, d), kv[:, :, 0], kv[:, :, 1], Hkv)
+    raises("one row stride", nx.doc_attn_exact, t(R, Hq, d), kv[:, :, 0], t(Hkv, n, d), Hkv)   # strides differ
+    kt = t(Hkv, d, n).transpose(1, 2)                                                          # dims strided
+    raises("one row stride", nx.doc_attn_exact, t(R, Hq, d), kt, kt, Hkv)
+    odd = t(Hkv, n, d + 4)[:, :, :d]                                                           # stride d + 4
+    raises("one row stride", nx.doc_attn_exact, t(R, Hq, d), odd, odd, Hkv)
+
+
 def test_module_checks():
     q = t(R, Hq, d)
     raises("b1 has element type", nx.module_forward, q, mlp(b1=t(Hkv, 64)), Hkv)                  # bf16 bias

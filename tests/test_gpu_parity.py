@@ -84,6 +84,72 @@ def test_doc_attn_balanced_splits(nx, n):
     assert np.array_equal(host(a2), host(a)) and np.array_equal(host(A2), host(A))
 
 
+def _kv_views(K, V, gap=0):
+    """Device views k = kv[:, :, 0], v = kv[:, :, 1 + gap] of one contiguous
+    [Hkv][n][2 + gap][d] array holding K and V interleaved by key."""
+    Hkv, n, d = K.shape
+    kv = np.zeros((Hkv, n, 2 + gap, d), K.dtype)
+    kv[:, :, 0], kv[:, :, 1 + gap] = K, V
+    t = dev(kv)
+    return t[:, :, 0], t[:, :, 1 + gap]
+
+
+@pytest.mark.parametrize("dt,d,R,Hq,Hkv,n,gap", [("bf16", 128, 1, 32, 8, 3000, 0),      # register-direct
+                                                 ("bf16", 128, 8, 28, 4, 5000, 0),      # LDS-staged, 56 rows
+                                                 ("bf16", 128, 64, 32, 8, 2000, 0),     # 32-row waves, 256 rows
+                                                 ("bf16", 128, 8, 28, 4, 1001, 2),      # row stride 4d
+                                                 ("bf16", 64, 3, 8, 2, 777, 0),
+                                                 ("f32", 128, 5, 6, 2, 300, 0), ("f32", 64, 5, 6, 2, 300, 1)])
+def test_doc_attn_interleaved_kv(nx, dt, d, R, Hq, Hkv, n, gap):
+    """The document cache as one array with K and V interleaved by key (row
+    stride (2 + gap) d): the same kernels over strided rows give the dense
+    layout's results bit for bit, for the one-call and two-pass forms."""
+    print("case doc_attn interleaved %s d=%d R=%d Hq=%d Hkv=%d n=%d gap=%d" % (dt, d, R, Hq, Hkv, n, gap), flush=True)
+    g = _rng(41, d, R, n, gap)
+    if dt == "bf16":
+        q, K, V = (_bf(g.standard_normal(s)) for s in ((R, Hq, d), (Hkv, n, d), (Hkv, n, d)))
+    else:
+        q, K, V = (g.standard_normal(s).astype(np.float32) for s in ((R, Hq, d), (Hkv, n, d), (Hkv, n, d)))
+    k, v = _kv_views(K, V, gap)
+    assert not k.is_contiguous() and k.stride(1) == (2 + gap) * d
+    a, A = nx.doc_attn_exact(dev(q), k, v, Hkv)
+    a0, A0 = nx.doc_attn_exact(dev(q), dev(K), dev(V), Hkv)
+    assert np.array_equal(host(a), host(a0)) and np.array_equal(host(A), host(A0))
+    ea, eA = oracle.doc_attn(q, K, V, dt=dt, Hq=Hq, Hkv=Hkv)
+    if dt == "bf16":
+        check("alpha", host(a), ea, 1e-3)
+        check("A", host(A), eA, ATOL_OUT_BF16, REL_L2_BF16)
+    else:
+        check("alpha", host(a), ea, ATOL_F32)
+        check("A", host(A), eA, ATOL_F32)
+    part = nx.doc_attn_partials(dev(q), k, v, Hkv)
+    a2, A2 = nx.doc_attn_combine(part, R, Hq, Hkv, d, n, nx.BF16 if dt == "bf16" else nx.F32)
+    assert np.array_equal(host(a2), host(a)) and np.array_equal(host(A2), host(A))
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "both_rows56", "exact_only", "batch64_bf16"])
+def test_layer_step_interleaved_kv(nx, name):
+    """nectar_layer_step with the document cache interleaved by key: every output
+    equal bit for bit to the dense layout's."""
+    dt, d, B, Tq, T, T_cap, qoff, Hq, Hkv, n, mod = STEP_CASES[name]
+    print("case layer_step interleaved %s" % name, flush=True)
+    g = _rng(42, len(name), B, Tq, T)
+    R = B * Tq
+    q = _store(g.standard_normal((R, Hq, d)), dt)
+    Kl, Vl = (_store(g.standard_normal((B, Hkv, T_cap, d)), dt) for _ in range(2))
+    K, V = (_store(g.standard_normal((Hkv, n, d)), dt) for _ in range(2))
+    module = None
+    if mod is not None:
+        module = _mlp_dev(nx, _mlp_np(g, Hkv, d, mod[1], mod[2], dt), nx.GELU)
+    kw = dict(B=B, Tq=Tq, T_loc=T, q_offset=qoff, module=module, exact=True, pairs=True)
+    k, v = _kv_views(K, V)
+    o1 = {key: host(t) for key, t in nx.layer_step(dev(q), dev(Kl), dev(Vl), Hkv, k=k, v=v, **kw).items()}
+    o0 = {key: host(t) for key, t in nx.layer_step(dev(q), dev(Kl), dev(Vl), Hkv, k=dev(K), v=dev(V), **kw).items()}
+    assert sorted(o1) == sorted(o0)
+    for key in o0:
+        assert np.array_equal(o1[key], o0[key], equal_nan=True), key
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_doc_attn_f32(nx, d):
     R, Hq, Hkv, n = 5, 6, 2, 300
@@ -559,7 +625,8 @@ def test_c2_layer_step_as_timed(nx):
     MLP 4608/2944) through nectar_layer_step exactly as the benchmark calls it:
     both paths in one call with every pair requested (the document's balanced
     splits share the launch with the module's blocks, then one finishing pass),
-    then each path alone.  Every pair and both merged outputs against the oracle."""
+    then each path alone, the document cache interleaved by key.  Every pair and
+    both merged outputs against the oracle."""
     cfg = configs.C2
     print("case c2 layer step as timed", flush=True)
     q = synth.queries(cfg)
@@ -567,7 +634,8 @@ def test_c2_layer_step_as_timed(nx):
     Kl, Vl = synth.local_kv(cfg)
     P = synth.mlp_params(cfg)
     T, qoff = cfg.local_len(0), cfg.q_offset(0)
-    qd, Kd, Vd, Kld, Vld = dev(q), dev(K), dev(V), dev(Kl), dev(Vl)
+    qd, Kld, Vld = dev(q), dev(Kl), dev(Vl)
+    Kd, Vd = _kv_views(K, V)          # the document cache interleaved by key, as the benchmark stores it
     mod = _mlp_dev(nx, P, nx.GELU)
     kw = dict(dt="bf16", Hq=cfg.Hq, Hkv=cfg.Hkv)
     Klv, Vlv = (np.ascontiguousarray(x[:, :, :T]) for x in (Kl, Vl))

@@ -18,6 +18,7 @@ and last questions, and first/last decode steps or layers:
 import functools
 
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -80,14 +81,18 @@ def _layer(nx, cfg, layer, step, toks, modules=(), kv_pairs=False):
     _check_pair("local", lam, Al, el, eAl)
     _check_merged("exact", out_x, lse_x, eo, e_lse)
 
-    # the exact path as the benchmark times it: merged output and lse only
-    st = nx.layer_step(qd, Kld, Vld, cfg.Hkv, k=Kd, v=Vd, module=None, exact=True, **skw)
+    # the exact path as the benchmark times it: the document cache as one array with
+    # K and V interleaved by key; merged output and lse only
+    kv = torch.stack((Kd, Vd), dim=2)
+    del Kd, Vd
+    Ki, Vi = kv[:, :, 0], kv[:, :, 1]
+    st = nx.layer_step(qd, Kld, Vld, cfg.Hkv, k=Ki, v=Vi, module=None, exact=True, **skw)
     _check_merged("layer step exact path", *pick(st["out_exact"], st["lse_exact"]), eo, e_lse)
     # ... and with every pair requested
-    st = nx.layer_step(qd, Kld, Vld, cfg.Hkv, k=Kd, v=Vd, module=None, exact=True, pairs=True, **skw)
+    st = nx.layer_step(qd, Kld, Vld, cfg.Hkv, k=Ki, v=Vi, module=None, exact=True, pairs=True, **skw)
     _check_pair("layer step alpha/A", *pick(st["alpha"], st["A"]), ea, eA)
     _check_pair("layer step local", *pick(st["lam"], st["Aloc"]), el, eAl)
-    del Kd, Vd, st
+    del kv, Ki, Vi, st
 
     for which in modules:
         P = synth.mlp_params(cfg, layer, which)

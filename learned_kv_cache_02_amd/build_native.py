@@ -49,16 +49,22 @@ def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
     # the sources compile independently: one hipcc per source, in parallel
     jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     tag = "b%d" % os.getpid()
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda src: _compile(src, extra_flags, verbose, tag), SOURCES))
+    objs = [os.path.join(CSRC, "%s.%s.o" % (src.rsplit(".", 1)[0], tag)) for src in SOURCES]
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, out)
-    for o in objs:
-        os.remove(o)
+    try:
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            list(ex.map(lambda src: _compile(src, extra_flags, verbose, tag), SOURCES))
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout)
+        os.replace(tmp, out)
+    finally:
+        # objects of this build (also those of sources that compiled before a
+        # failure) and a partial link never stay in the tree
+        for o in objs + [tmp]:
+            if os.path.exists(o):
+                os.remove(o)
     return out
 
 

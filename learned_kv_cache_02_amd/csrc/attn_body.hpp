@@ -99,16 +99,21 @@ __device__ __forceinline__ void attend_tile(const KVTile<D> &T, int k0, const u3
 #ifndef NECTAR_RT1_SUB
 #define NECTAR_RT1_SUB 2
 #endif
+// Fold buffers of a block (used when WS > 1, hence WR <= 2): per row group
+// one f32x4 per (register, lane), lane-major so each wave access is
+// conflict-free.
+template <int D, int RT> struct AttnFoldLds {
+    f32x4 O[2][RT * (D / 16)][64];
+    float l[2][RT][64];
+    float m[4][RT][16];
+};
+
 // RT == 1: two waves per SIMD (8 per CU), each with a 32 KB batch in flight.
-// Block blk_id of one problem set's grid (P x RB x SB blocks of 4 waves).
+// Block blk_id of one problem set's grid (P x RB x SB blocks of 4 waves); fl
+// is the block's fold buffer (a kernel that also runs other bodies shares it).
 template <int D, int RT, int SUB, typename OutT>
-__device__ __forceinline__ void attn_partial_body(const AttnParams &a, int blk_id) {
+__device__ __forceinline__ void attn_partial_body_lds(const AttnParams &a, int blk_id, AttnFoldLds<D, RT> &fl) {
     constexpr int KS = D / 32, DV = D / 16;
-    // Fold buffers (used when WS > 1, hence WR <= 2): per row group one f32x4
-    // per (register, lane), lane-major so each wave access is conflict-free.
-    __shared__ f32x4 fold_O[2][RT * DV][64];
-    __shared__ float fold_l[2][RT][64];
-    __shared__ float fold_m[4][RT][16];
 
     const int w = threadIdx.x >> 6;
     const int wr = w % a.WR, ws = w / a.WR;
@@ -190,12 +195,12 @@ __device__ __forceinline__ void attn_partial_body(const AttnParams &a, int blk_i
         // Fold the WS splits of this row group: common max, rescale, sum.
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-            if (g == 0) fold_m[w][rt][c] = m[rt];
+            if (g == 0) fl.m[w][rt][c] = m[rt];
         __syncthreads();
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             float M = -INFINITY;
-            for (int k = 0; k < a.WS; ++k) M = fmaxf(M, fold_m[k * a.WR + wr][rt][c]);
+            for (int k = 0; k < a.WS; ++k) M = fmaxf(M, fl.m[k * a.WR + wr][rt][c]);
             const float sc = (m[rt] == -INFINITY) ? 0.f : exp2f(m[rt] - M);
             l[rt] *= sc;
 #pragma unroll
@@ -206,11 +211,11 @@ __device__ __forceinline__ void attn_partial_body(const AttnParams &a, int blk_i
             if (ws == k) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    fold_l[wr][rt][lane] = (k == a.WS - 1) ? l[rt] : fold_l[wr][rt][lane] + l[rt];
+                    fl.l[wr][rt][lane] = (k == a.WS - 1) ? l[rt] : fl.l[wr][rt][lane] + l[rt];
 #pragma unroll
                     for (int mm = 0; mm < DV; ++mm)
-                        fold_O[wr][rt * DV + mm][lane] =
-                            (k == a.WS - 1) ? O[rt][mm] : fold_O[wr][rt * DV + mm][lane] + O[rt][mm];
+                        fl.O[wr][rt * DV + mm][lane] =
+                            (k == a.WS - 1) ? O[rt][mm] : fl.O[wr][rt * DV + mm][lane] + O[rt][mm];
                 }
             }
             __syncthreads();
@@ -218,9 +223,9 @@ __device__ __forceinline__ void attn_partial_body(const AttnParams &a, int blk_i
         if (ws == 0) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                l[rt] += fold_l[wr][rt][lane];
+                l[rt] += fl.l[wr][rt][lane];
 #pragma unroll
-                for (int mm = 0; mm < DV; ++mm) O[rt][mm] += fold_O[wr][rt * DV + mm][lane];
+                for (int mm = 0; mm < DV; ++mm) O[rt][mm] += fl.O[wr][rt * DV + mm][lane];
             }
         }
     }
@@ -246,6 +251,12 @@ __device__ __forceinline__ void attn_partial_body(const AttnParams &a, int blk_i
         }
     }
 
+}
+
+template <int D, int RT, int SUB, typename OutT>
+__device__ __forceinline__ void attn_partial_body(const AttnParams &a, int blk_id) {
+    __shared__ AttnFoldLds<D, RT> fl;
+    attn_partial_body_lds<D, RT, SUB, OutT>(a, blk_id, fl);
 }
 
 // Problem set of block b of a two-set grid and the block's index within it.

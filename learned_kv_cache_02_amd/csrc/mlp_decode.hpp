@@ -109,7 +109,13 @@ template <int D, int RT, int SL> struct DecFold {
 // operand reads of sixteen rows fall in distinct banks.  The fold reuses the
 // same LDS after a barrier.
 template <int D, int RT, int NT, int SL> union DecLds {
-    u32x4 tiles[SL][NT * 2 * 32 * (D / 8)];
+    // the block's query rows (16 RT rows, same swizzle) where two waves share a
+    // slot: staged once instead of loaded by every slot's waves
+    static constexpr int QROWS = (D == 128 && dec_wps(D, RT) > 1) ? 16 * RT : 1;
+    struct {
+        u32x4 tiles[SL][NT * 2 * 32 * (D / 8)];
+        u32x4 q[QROWS * (D / 8)];
+    } st;
     DecFold<D, RT, SL> fold;
 };
 
@@ -122,6 +128,24 @@ __device__ __forceinline__ void stage_rows128(u32x4 *dst, const uint16_t *W, int
         const int rr = 4 * i + (lane >> 4);
         const int piece = (lane & 15) ^ (rr & 15);
         const uint16_t *src = W + (size_t)min(u0 + rr, umax) * 128 + piece * 8;
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + 64 * i), 16, 0, 0);
+    }
+}
+
+// Copy the query rows rg * 16 RT + 0 .. 16 RT - 1 of KV head h (clamped to the
+// last row: rows past it feed only results that are never written) into LDS
+// rows at dst, pieces swizzled as in stage_rows128; the wave takes copies
+// i0 .. i0 + n - 1 of four rows each.
+template <int RT>
+__device__ __forceinline__ void stage_q128(u32x4 *dst, const uint16_t *q, int Rp, int G, int Hq, int h, int rg,
+                                           int lane, int i0, int n) {
+#pragma unroll
+    for (int i = i0; i < i0 + n; ++i) {
+        const int rr = 4 * i + (lane >> 4);
+        const int piece = (lane & 15) ^ (rr & 15);
+        const int rho = min(rg * 16 * RT + rr, Rp - 1);
+        const int t = rho / G, gg = rho - t * G;
+        const uint16_t *src = q + ((size_t)t * Hq + h * G + gg) * 128 + piece * 8;
         __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + 64 * i), 16, 0, 0);
     }
 }
@@ -154,12 +178,13 @@ template <int D> __device__ __forceinline__ void lds_w2_128(MTile<D> &T, const u
 // tiles (v / SL) * RT / WPS ...).  Slot w of block sb of (KV head h, row group
 // rg) is slot i = SL sb + w of that group: target slot i < nwt, score slot
 // i - nwt < nws, idle otherwise.
+// lds is the block's LDS (a kernel that also runs other bodies shares it).
 template <int D, int RT, int ACT, int NT>
-__device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) {
+__device__ __forceinline__ void mlp_decode_body_lds(const MlpParams &a, int blk_id,
+                                                    DecLds<D, RT, NT, dec_slots(D, RT)> &lds) {
     constexpr int KS = D / 32, DV = D / 16;
     constexpr int WPS = dec_wps(D, RT), SL = dec_slots(D, RT), RTW = RT / WPS;   // waves per slot, slots, row tiles per wave
     constexpr int NS = dec_score_tiles(RT);                 // score tiles per score slot
-    __shared__ DecLds<D, RT, NT, SL> lds;
     DecFold<D, RT, SL> &fold = lds.fold;
 
     const int v = threadIdx.x >> 6;
@@ -182,20 +207,35 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
         for (int mm = 0; mm < DV; ++mm) O[rt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const bool tgt = wi < a.nwt, scw = !tgt && wi < a.nwt + a.nws;
+    constexpr bool QLDS = D == 128 && WPS > 1;   // query rows staged in LDS (lds.st.q)
     u32x4 qv[RTW][KS];
+    if constexpr (!QLDS) {
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-        const int rho = (rg * RT + rt0 + rt) * 16 + c;
-        if ((tgt || scw) && rho < a.Rp) {
-            const int t = rho / a.G, gg = rho - t * a.G;
-            const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.Hq + h * a.G + gg) * D;
+        for (int rt = 0; rt < RTW; ++rt) {
+            const int rho = (rg * RT + rt0 + rt) * 16 + c;
+            if ((tgt || scw) && rho < a.Rp) {
+                const int t = rho / a.G, gg = rho - t * a.G;
+                const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.Hq + h * a.G + gg) * D;
 #pragma unroll
-            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
-        } else {
+                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
+            } else {
 #pragma unroll
-            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
+                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
+            }
         }
     }
+    // the query operands from the staged rows (after the barrier that follows
+    // every wave's wait for its own copies)
+    auto q_from_lds = [&]() {
+        if constexpr (QLDS) {
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) {
+                const int r = (rt0 + rt) * 16 + c;
+#pragma unroll
+                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = lds.st.q[r * 16 + ((4 * kt + g) ^ (r & 15))];
+            }
+        }
+    };
     // this slot's tile range
     const int Tt = (a.Ht + 31) / 32, Ts = (a.Hs + 31) / 32;
     const int si = wi - a.nwt;
@@ -210,14 +250,17 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
 
     // d = 128: the slot's weight rows are staged in LDS (lds.tiles[w]), every
     // copy and bias load first, then one wait before the first product.
-    u32x4 *buf = lds.tiles[w];
+    u32x4 *buf = lds.st.tiles[w];
+    // Biases (and score read-out weights): one load per lane and pair of
+    // tiles -- lane l holds unit l % 32 of tile 2 i + l / 32 -- handed to the
+    // lanes that use them (hidden slots hslot(g, j)) when the tile's products
+    // start, instead of eight loads per lane and tile.
+    auto tile_unit = [&](int k) { return 32 * (t0 + max(min(k, n - 1), 0)); };
+    auto bias_lane = [&](int i) { return tile_unit(2 * i + (lane >> 5)) + (lane & 31); };
+    auto from_lane = [&](float v, int k, int j) { return __shfl(v, 32 * (k & 1) + hslot(g, j), 64); };
     auto tgt_bias = [&](auto &bias) {
 #pragma unroll
-        for (int k = 0; k < NT; ++k) {
-            const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bias[k][j] = b1[min(u0 + hslot(g, j), a.Ht - 1)];
-        }
+        for (int i = 0; i < (NT + 1) / 2; ++i) bias[i] = b1[min(bias_lane(i), a.Ht - 1)];
     };
     auto tgt_copies = [&](int i0, int ni) {
 #pragma unroll
@@ -232,19 +275,15 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
         lds_rows128(T, buf + k * 1024, g, c);
         lds_w2_128(T, buf + k * 1024 + 512, g, c);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) T.bias[j] = bias[k][j];
+        for (int j = 0; j < 8; ++j) T.bias[j] = from_lane(bias[k >> 1], k, j);
         dec_tgt_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Ht, qv, g, O);
     };
     auto sc_bias = [&](auto &bias, auto &wsv) {
 #pragma unroll
-        for (int k = 0; k < NS; ++k) {
-            const int u0 = 32 * (t0 + max(min(k, n - 1), 0));
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int u = min(u0 + hslot(g, j), a.Hs - 1);
-                bias[k][j] = bs[u];
-                wsv[k][j] = ws2[u];            // bf16 bits, widened at use (no wait here)
-            }
+        for (int i = 0; i < (NS + 1) / 2; ++i) {
+            const int u = min(bias_lane(i), a.Hs - 1);
+            bias[i] = bs[u];
+            wsv[i] = ws2[u];                   // bf16 bits, widened at use
         }
     };
     auto sc_copies = [&](int i0, int ni) {
@@ -257,10 +296,11 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
     auto sc_tile = [&](const auto &bias, const auto &wsv, int k) {
         MTile<D> T;
         lds_rows128(T, buf + k * 512, g, c);
+        const float wsk = __uint_as_float((uint32_t)wsv[k >> 1] << 16);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            T.bias[j] = bias[k][j];
-            T.ws[j] = __uint_as_float(wsv[k][j] << 16);
+            T.bias[j] = from_lane(bias[k >> 1], k, j);
+            T.ws[j] = from_lane(wsk, k, j);
         }
         dec_score_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Hs, qv, g, sc);
     };
@@ -277,43 +317,52 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
         // makes the other wave's half of the copies visible.
         static_assert(NT == 2 && NS == 2, "two tiles per slot, one barrier each");
         constexpr int CI = 8 / WPS;
+        constexpr int QC = 16 * RT / 4 / (SL * WPS);   // query-row copies per wave
+        static_assert(QC * 4 * SL * WPS == 16 * RT, "query rows split evenly over the waves");
+        // every wave first copies its share of the block's query rows
+        stage_q128<RT>(lds.st.q, (const uint16_t *)a.q, a.Rp, a.G, a.Hq, h, rg, lane, v * QC, QC);
+        asm volatile("" ::: "memory");       // ... ahead of every other load
         // each role runs its whole sequence in its own branch, so the
         // compiler's wait analysis sees straight-line code (a join before the
-        // products would make it wait for every load)
+        // products would make it wait for every load).  Loads complete in
+        // issue order: query rows, biases, tile 0's copies, tile 1's copies.
         if (tgt) {
-            float tb[NT][8];
+            float tb[(NT + 1) / 2];
             tgt_bias(tb);
             asm volatile("" ::: "memory");   // the bias loads stay ahead of the copies
             tgt_copies(part * CI, CI);
             wait_vmcnt<2 * CI>();            // tile 1's copies of both tables may be pending
             stage_barrier();
-            asm volatile("" ::: "memory");   // tile 0's LDS reads stay below
+            asm volatile("" ::: "memory");   // the LDS reads stay below
+            q_from_lds();
             if (n > 0) tgt_tile(tb, 0);
             wait_vmcnt<0>();
             stage_barrier();
             asm volatile("" ::: "memory");
             if (n > 1) tgt_tile(tb, 1);
         } else if (scw) {
-            float sbias[NS][8];
-            uint32_t swsv[NS][8];
-            sc_copies(part * CI, CI);
-            asm volatile("" ::: "memory");
+            float sbias[(NS + 1) / 2];
+            uint16_t swsv[(NS + 1) / 2];
             sc_bias(sbias, swsv);
-            wait_vmcnt<CI>();
+            asm volatile("" ::: "memory");
+            sc_copies(part * CI, CI);
+            wait_vmcnt<CI>();                // tile 1's copies may be pending
             stage_barrier();
             asm volatile("" ::: "memory");
+            q_from_lds();
             if (n > 0) sc_tile(sbias, swsv, 0);
             wait_vmcnt<0>();
             stage_barrier();
             asm volatile("" ::: "memory");
             if (n > 1) sc_tile(sbias, swsv, 1);
         } else {
+            wait_vmcnt<0>();
             stage_barrier();
             stage_barrier();
         }
     } else if constexpr (D == 128) {
         if (tgt) {
-            float tb[NT][8];
+            float tb[(NT + 1) / 2];
             tgt_bias(tb);
             tgt_copies(0, 8);
             wait_vmcnt<0>();
@@ -322,8 +371,8 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
             for (int k = 0; k < NT; ++k)
                 if (k < n) tgt_tile(tb, k);
         } else if (scw) {
-            float sbias[NS][8];
-            uint32_t swsv[NS][8];
+            float sbias[(NS + 1) / 2];
+            uint16_t swsv[(NS + 1) / 2];
             sc_bias(sbias, swsv);
             sc_copies(0, 8);
             wait_vmcnt<0>();
@@ -405,6 +454,12 @@ __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) 
             if (lead) a.part_s[row] = s;
         }
     }
+}
+
+template <int D, int RT, int ACT, int NT>
+__device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) {
+    __shared__ DecLds<D, RT, NT, dec_slots(D, RT)> lds;
+    mlp_decode_body_lds<D, RT, ACT, NT>(a, blk_id, lds);
 }
 
 }  // namespace nectar

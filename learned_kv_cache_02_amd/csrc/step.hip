@@ -33,13 +33,18 @@ __global__ __launch_bounds__(256, NECTAR_RT1_WAVES_PER_SIMD) void step_partials(
 // once: the attention body is written for four).
 template <int D, int ACT, int RTM>
 __global__ __launch_bounds__((dec_threads(D, RTM)), 1) void step_partials_dec(AttnGroup gr, int nb_attn, MlpParams m) {
+    // one LDS allocation for whichever body the block runs
+    __shared__ union {
+        DecLds<D, RTM, kDecTiles, dec_slots(D, RTM)> mlp;
+        AttnFoldLds<D, 1> attn;
+    } lds;
     const int b = (int)blockIdx.x;
     if (b < nb_attn) {
         if (threadIdx.x >= 256) return;
         const int set = group_set(gr, b);
-        attn_partial_body<D, 1, NECTAR_RT1_SUB, uint16_t>(gr.p[set], b - (set ? gr.nb0 : 0));
+        attn_partial_body_lds<D, 1, NECTAR_RT1_SUB, uint16_t>(gr.p[set], b - (set ? gr.nb0 : 0), lds.attn);
     } else {
-        mlp_decode_body<D, RTM, ACT, kDecTiles>(m, b - nb_attn);
+        mlp_decode_body_lds<D, RTM, ACT, kDecTiles>(m, b - nb_attn, lds.mlp);
     }
 }
 

@@ -42,4 +42,8 @@ __device__ __forceinline__ int tr_swizzle(int r) { return ((r & 1) * 10) ^ ((r &
 // no waits of its own: the LDS copies are waited for explicitly above it.
 __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Workgroup barrier after this wave's LDS accesses have completed (its
+// vector-memory loads may still be in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace nectar

@@ -109,24 +109,40 @@ template <int D, int RT, int SL> struct DecFold {
 // operand reads of sixteen rows fall in distinct banks.  The fold reuses the
 // same LDS after a barrier.
 template <int D, int RT, int NT, int SL> union DecLds {
-    // the block's query rows (16 RT rows, same swizzle) where two waves share a
-    // slot: staged once instead of loaded by every slot's waves
-    static constexpr int QROWS = (D == 128 && dec_wps(D, RT) > 1) ? 16 * RT : 1;
-    struct {
-        u32x4 tiles[SL][NT * 2 * 32 * (D / 8)];
-        u32x4 q[QROWS * (D / 8)];
-    } st;
+    u32x4 tiles[SL][NT * 2 * 32 * (D / 8)];
     DecFold<D, RT, SL> fold;
+};
+
+// Swizzle of the W2t stages of the paired kernel, read by transposing operand
+// reads: piece j of unit row r sits at j ^ pair_swizzle(r).  One 16-lane
+// group's read touches rows 8G + 4h + 0..3 and two adjacent pieces (an even
+// one and the next); bits 1-2 of the swizzle separate the four rows and bit 3
+// the two groups that share a half-wave, so the sixteen 16-byte slots a
+// half-wave reads fall on distinct banks (and any 16 lanes' eight slots on
+// distinct banks of a 32-bank model).
+__device__ __forceinline__ int pair_swizzle(int r) { return ((r & 3) << 1) | (((r >> 3) & 1) << 3); }
+
+// LDS of the paired kernel (d = 128, 33..64 rows per KV head, 160 KB): per
+// slot two tiles of [32 W1 rows | 32 W2t rows] (score slots: two tiles of 32
+// Ws rows), the block's query rows (their region later holds the score sums),
+// and the hidden values of one tile round of every slot, [slot][group of 8
+// units][row][8 units] in bf16.
+struct DecPairLds {
+    u32x4 tiles[4][2 * 2 * 32 * 16];
+    u32x4 q[64 * 16];
+    u32x4 H[4 * 4 * 64];
 };
 
 // Copy rows u0 .. u0 + 31 (clamped to umax) of W into LDS rows 0..31 at dst:
 // eight copies of four rows; the wave takes copies i0, i0 + 1, ..., i0 + n - 1.
+// PSW: pieces at pair_swizzle positions instead of piece ^ (r % 16).
+template <bool PSW = false>
 __device__ __forceinline__ void stage_rows128(u32x4 *dst, const uint16_t *W, int u0, int umax, int lane, int i0 = 0,
                                               int n = 8) {
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i) {
         const int rr = 4 * i + (lane >> 4);
-        const int piece = (lane & 15) ^ (rr & 15);
+        const int piece = (lane & 15) ^ (PSW ? pair_swizzle(rr) : (rr & 15));
         const uint16_t *src = W + (size_t)min(u0 + rr, umax) * 128 + piece * 8;
         __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + 64 * i), 16, 0, 0);
     }
@@ -180,8 +196,9 @@ template <int D> __device__ __forceinline__ void lds_w2_128(MTile<D> &T, const u
 // i - nwt < nws, idle otherwise.
 // lds is the block's LDS (a kernel that also runs other bodies shares it).
 template <int D, int RT, int ACT, int NT>
-__device__ __forceinline__ void mlp_decode_body_lds(const MlpParams &a, int blk_id,
-                                                    DecLds<D, RT, NT, dec_slots(D, RT)> &lds) {
+__device__ __forceinline__ void mlp_decode_slots(const MlpParams &a, int blk_id,
+                                                 DecLds<D, RT, NT, dec_slots(D, RT)> &lds) {
+    static_assert(dec_wps(D, RT) == 1, "one wave per slot");
     constexpr int KS = D / 32, DV = D / 16;
     constexpr int WPS = dec_wps(D, RT), SL = dec_slots(D, RT), RTW = RT / WPS;   // waves per slot, slots, row tiles per wave
     constexpr int NS = dec_score_tiles(RT);                 // score tiles per score slot
@@ -207,35 +224,20 @@ __device__ __forceinline__ void mlp_decode_body_lds(const MlpParams &a, int blk_
         for (int mm = 0; mm < DV; ++mm) O[rt][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const bool tgt = wi < a.nwt, scw = !tgt && wi < a.nwt + a.nws;
-    constexpr bool QLDS = D == 128 && WPS > 1;   // query rows staged in LDS (lds.st.q)
     u32x4 qv[RTW][KS];
-    if constexpr (!QLDS) {
 #pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) {
-            const int rho = (rg * RT + rt0 + rt) * 16 + c;
-            if ((tgt || scw) && rho < a.Rp) {
-                const int t = rho / a.G, gg = rho - t * a.G;
-                const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.Hq + h * a.G + gg) * D;
+    for (int rt = 0; rt < RTW; ++rt) {
+        const int rho = (rg * RT + rt0 + rt) * 16 + c;
+        if ((tgt || scw) && rho < a.Rp) {
+            const int t = rho / a.G, gg = rho - t * a.G;
+            const uint16_t *qp = (const uint16_t *)a.q + ((size_t)t * a.Hq + h * a.G + gg) * D;
 #pragma unroll
-                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
-            } else {
+            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = *(const u32x4 *)(qp + (4 * kt + g) * 8);
+        } else {
 #pragma unroll
-                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = u32x4{0u, 0u, 0u, 0u};
         }
     }
-    // the query operands from the staged rows (after the barrier that follows
-    // every wave's wait for its own copies)
-    auto q_from_lds = [&]() {
-        if constexpr (QLDS) {
-#pragma unroll
-            for (int rt = 0; rt < RTW; ++rt) {
-                const int r = (rt0 + rt) * 16 + c;
-#pragma unroll
-                for (int kt = 0; kt < KS; ++kt) qv[rt][kt] = lds.st.q[r * 16 + ((4 * kt + g) ^ (r & 15))];
-            }
-        }
-    };
     // this slot's tile range
     const int Tt = (a.Ht + 31) / 32, Ts = (a.Hs + 31) / 32;
     const int si = wi - a.nwt;
@@ -250,7 +252,7 @@ __device__ __forceinline__ void mlp_decode_body_lds(const MlpParams &a, int blk_
 
     // d = 128: the slot's weight rows are staged in LDS (lds.tiles[w]), every
     // copy and bias load first, then one wait before the first product.
-    u32x4 *buf = lds.st.tiles[w];
+    u32x4 *buf = lds.tiles[w];
     // Biases (and score read-out weights): one load per lane and pair of
     // tiles -- lane l holds unit l % 32 of tile 2 i + l / 32 -- handed to the
     // lanes that use them (hidden slots hslot(g, j)) when the tile's products
@@ -304,63 +306,7 @@ __device__ __forceinline__ void mlp_decode_body_lds(const MlpParams &a, int blk_
         }
         dec_score_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Hs, qv, g, sc);
     };
-    if constexpr (D == 128 && WPS > 1) {
-        // Two waves per slot share the copies (four of the eight per 32-row
-        // table each).  Loads complete in the order issued.  Target slots load
-        // their biases, then tile 0's copies, then tile 1's: once at most tile
-        // 1's copies are pending, tile 0 has landed, and its products run while
-        // tile 1 is still in flight.  Score slots issue their copies first and
-        // their biases and read-out weights after (those are widened from bf16
-        // as they arrive, which waits for everything issued before): at most CI
-        // pending operations are then bias loads, every copy has landed.  A
-        // block barrier per tile (every wave takes the same two, idle ones too)
-        // makes the other wave's half of the copies visible.
-        static_assert(NT == 2 && NS == 2, "two tiles per slot, one barrier each");
-        constexpr int CI = 8 / WPS;
-        constexpr int QC = 16 * RT / 4 / (SL * WPS);   // query-row copies per wave
-        static_assert(QC * 4 * SL * WPS == 16 * RT, "query rows split evenly over the waves");
-        // every wave first copies its share of the block's query rows
-        stage_q128<RT>(lds.st.q, (const uint16_t *)a.q, a.Rp, a.G, a.Hq, h, rg, lane, v * QC, QC);
-        asm volatile("" ::: "memory");       // ... ahead of every other load
-        // each role runs its whole sequence in its own branch, so the
-        // compiler's wait analysis sees straight-line code (a join before the
-        // products would make it wait for every load).  Loads complete in
-        // issue order: query rows, biases, tile 0's copies, tile 1's copies.
-        if (tgt) {
-            float tb[(NT + 1) / 2];
-            tgt_bias(tb);
-            asm volatile("" ::: "memory");   // the bias loads stay ahead of the copies
-            tgt_copies(part * CI, CI);
-            wait_vmcnt<2 * CI>();            // tile 1's copies of both tables may be pending
-            stage_barrier();
-            asm volatile("" ::: "memory");   // the LDS reads stay below
-            q_from_lds();
-            if (n > 0) tgt_tile(tb, 0);
-            wait_vmcnt<0>();
-            stage_barrier();
-            asm volatile("" ::: "memory");
-            if (n > 1) tgt_tile(tb, 1);
-        } else if (scw) {
-            float sbias[(NS + 1) / 2];
-            uint16_t swsv[(NS + 1) / 2];
-            sc_bias(sbias, swsv);
-            asm volatile("" ::: "memory");
-            sc_copies(part * CI, CI);
-            wait_vmcnt<CI>();                // tile 1's copies may be pending
-            stage_barrier();
-            asm volatile("" ::: "memory");
-            q_from_lds();
-            if (n > 0) sc_tile(sbias, swsv, 0);
-            wait_vmcnt<0>();
-            stage_barrier();
-            asm volatile("" ::: "memory");
-            if (n > 1) sc_tile(sbias, swsv, 1);
-        } else {
-            wait_vmcnt<0>();
-            stage_barrier();
-            stage_barrier();
-        }
-    } else if constexpr (D == 128) {
+    if constexpr (D == 128) {
         if (tgt) {
             float tb[(NT + 1) / 2];
             tgt_bias(tb);
@@ -456,9 +402,286 @@ __device__ __forceinline__ void mlp_decode_body_lds(const MlpParams &a, int blk_
     }
 }
 
+// d = 128 with 33..64 rows per KV head: a block of four slots of two waves.
+// Wave v = 4 part + w stages slot w's weights (with the other wave of the
+// slot: four of the eight copies per 32-row table each) and computes, for the
+// rows 32 part .. 32 part + 31 of the block's 64,
+//   phase 1 (its slot's tile k): Z^T = W1 . Q^T + b1 on the 16x16x32 MFMA,
+//     H = act(Z) rounded to bf16 into LDS -- or, in a score slot, the score
+//     terms ws2 . act(Ws . q + bs) summed in fp32;
+//   phase 2 (every target slot's tile k): O^T += W2t^T . H^T for the output
+//     dims 32 w .. 32 w + 31, the W2t operands from the unit-major stage by
+//     transposing reads, the hidden values from LDS,
+// so each wave ends with its own 32 dims x 32 rows of the block's read-out
+// sum, written straight from its accumulators: no fold of slot partials.
+// Two tile rounds, four block barriers: tile 0 landed; round 0's hidden
+// values written; tile 1 landed (round 0's reads done); round 1's hidden
+// values and the score sums written.  Loads complete in issue order: query
+// rows, biases, tile 0's copies, tile 1's copies, so round 0 runs while tile
+// 1 is in flight.  A target slot with one tile writes zero hidden values in
+// round 1 (its second stage holds the first tile's rows again: finite).
+template <int ACT>
+__device__ __forceinline__ void mlp_decode_pair128(const MlpParams &a, int blk_id, DecPairLds &lds) {
+    constexpr int D = 128, SL = 4, NT = 2, CI = 4;
+    const int v = threadIdx.x >> 6;
+    const int w = v & 3, part = v >> 2;
+    int blk = blk_id;
+    const int sb = blk % a.SB;
+    blk /= a.SB;
+    const int rg = blk % a.RG;
+    const int h = blk / a.RG;
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    const int wi = SL * sb + w;
+    const bool tgt = wi < a.nwt, scw = !tgt && wi < a.nwt + a.nws;
+    const int nto = min(max(a.nwt - SL * sb, 0), SL);   // target slots of the block: the first nto
+    const int Tt = (a.Ht + 31) / 32, Ts = (a.Hs + 31) / 32;
+    const int si = wi - a.nwt;
+    const int t0 = tgt ? (int)((long)wi * Tt / a.nwt) : (scw ? (int)((long)si * Ts / a.nws) : 0);
+    const int n = tgt ? (int)((long)(wi + 1) * Tt / a.nwt) - t0 : (scw ? (int)((long)(si + 1) * Ts / a.nws) - t0 : 0);
+    const uint16_t *W1 = (const uint16_t *)a.W1 + (size_t)h * a.Ht * D;
+    const uint16_t *W2t = (const uint16_t *)a.W2t + (size_t)h * a.Ht * D;
+    const float *b1 = a.b1 + (size_t)h * a.Ht;
+    const uint16_t *Ws = (const uint16_t *)a.Ws + (size_t)h * a.Hs * D;
+    const uint16_t *ws2 = (const uint16_t *)a.ws2 + (size_t)h * a.Hs;
+    const float *bs = a.bs + (size_t)h * a.Hs;
+    u32x4 *buf = lds.tiles[w];
+    float *fs = (float *)lds.q;   // score sums [slot][64 rows], once the query rows are in registers
+
+    auto tile_unit = [&](int k) { return 32 * (t0 + max(min(k, n - 1), 0)); };
+    // biases: lane l loads unit l % 32 of tile l / 32; the lanes that use a
+    // unit (hidden slots hslot(g, j)) take it by a wave shuffle
+    const int ulane = tile_unit(lane >> 5) + (lane & 31);
+    auto from_lane = [&](float x, int k, int j) { return __shfl(x, 32 * (k & 1) + hslot(g, j), 64); };
+
+    u32x4 qv[2][4];
+    auto q_from_lds = [&]() {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int r = 32 * part + 16 * rt + c;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) qv[rt][kt] = lds.q[r * 16 + ((4 * kt + g) ^ (r & 15))];
+        }
+    };
+    // Z^T of this wave's rows for tile k of the slot (rows of W1 or Ws at rows)
+    auto zt = [&](const u32x4 *rows, const float (&bias)[8], int rt, f32x4 &z0, f32x4 &z1) {
+        z0 = f32x4{bias[0], bias[1], bias[2], bias[3]};
+        z1 = f32x4{bias[4], bias[5], bias[6], bias[7]};
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int r0 = c, r1 = 16 + c;
+            z0 = mfma16(rows[r0 * 16 + ((4 * kt + g) ^ (r0 & 15))], qv[rt][kt], z0);
+            z1 = mfma16(rows[r1 * 16 + ((4 * kt + g) ^ (r1 & 15))], qv[rt][kt], z1);
+        }
+    };
+    // phase 1 of a target slot: H of tile k (zero past the slot's tiles)
+    auto tgt_phase1 = [&](float bv, int k) {
+        uint32_t hw[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hw[rt][i] = 0u;
+        if (k < n) {
+            float bias[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bias[j] = from_lane(bv, k, j);
+            const int j0 = 32 * (t0 + k);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4 z0, z1;
+                zt(buf + k * 1024, bias, rt, z0, z1);
+                float hv[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    hv[r] = act_dec<ACT>(z0[r]);
+                    hv[4 + r] = act_dec<ACT>(z1[r]);
+                }
+                if (j0 + 32 > a.Ht) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (j0 + hslot(g, j) >= a.Ht) hv[j] = 0.f;
+                }
+                hw[rt][0] = pack_bf16(hv[0], hv[1]);
+                hw[rt][1] = pack_bf16(hv[2], hv[3]);
+                hw[rt][2] = pack_bf16(hv[4], hv[5]);
+                hw[rt][3] = pack_bf16(hv[6], hv[7]);
+            }
+        }
+        // lane (g, c) holds units 16 hh + 4 g .. + 3 of row 32 part + 16 rt + c:
+        // half (g & 1) of the 8-unit group 2 hh + g / 2
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                u32x4 *e = lds.H + (w * 4 + 2 * hh + (g >> 1)) * 64 + 32 * part + 16 * rt + c;
+                *(u32x2 *)((char *)e + 8 * (g & 1)) = u32x2{hw[rt][2 * hh], hw[rt][2 * hh + 1]};
+            }
+    };
+    // phase 1 of a score slot: the score terms of tile k
+    float sc[2] = {0.f, 0.f};
+    auto sc_phase1 = [&](float bv, float wsv, int k) {
+        if (k >= n) return;                  // uniform
+        float bias[8], wsj[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bias[j] = from_lane(bv, k, j);
+            wsj[j] = from_lane(wsv, k, j);
+        }
+        const int j0 = 32 * (t0 + k);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4 z0, z1;
+            zt(buf + k * 512, bias, rt, z0, z1);
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float y = act_dec<ACT>(j < 4 ? z0[j] : z1[j - 4]) * wsj[j];
+                if (j0 + hslot(g, j) >= a.Hs) y = 0.f;
+                acc += y;
+            }
+            sc[rt] += acc;
+        }
+    };
+    // phase 2: O^T (dims 32 w + 16 mb + ., rows 32 part + 16 nt + .) over the
+    // target slots' tile k.  A operand of lane (G, x): dim 32 w + 16 mb + x and
+    // units 8 G .. 8 G + 7, by two transposing reads of four units each (lane
+    // x = a + 4 j names the 8 bytes of unit row 8 G + 4 i + j at dims
+    // 32 w + 16 mb + 4 a .. + 3); B operand: units 8 G .. 8 G + 7 of row x.
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto phase2 = [&](int k) {
+#pragma unroll
+        for (int s2 = 0; s2 < SL; ++s2) {
+            if (s2 >= nto) break;             // uniform
+            const u32x4 *wt = lds.tiles[s2] + k * 1024 + 512;
+            u32x4 A[2], B[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                u32x2 half[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int row = 8 * g + 4 * i + (c >> 2);
+                    const int p = 4 * w + 2 * mb + ((c & 3) >> 1);
+                    half[i] = lds_read_tr16(wt, (uint32_t)(row * 256 + ((p ^ pair_swizzle(row)) * 16) + (c & 1) * 8));
+                }
+                A[mb] = u32x4{half[0][0], half[0][1], half[1][0], half[1][1]};
+            }
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) B[nt] = lds.H[(s2 * 4 + g) * 64 + 32 * part + 16 * nt + c];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) acc[mb][nt] = mfma16(A[mb], B[nt], acc[mb][nt]);
+        }
+    };
+    auto store_sc = [&]() {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const float t = scw ? group4_sum(sc[rt]) : 0.f;
+            if (g == 0) fs[w * 64 + 32 * part + 16 * rt + c] = t;
+        }
+    };
+
+    // every wave first copies its share of the block's query rows
+    stage_q128<4>(lds.q, (const uint16_t *)a.q, a.Rp, a.G, a.Hq, h, rg, lane, 2 * v, 2);
+    asm volatile("" ::: "memory");   // ... ahead of every other load
+    // each role runs its whole sequence in its own branch, so the compiler's
+    // wait analysis sees straight-line code (a join before the products
+    // would make it wait for every load)
+    if (tgt) {
+        const float bv = b1[min(ulane, a.Ht - 1)];
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            stage_rows128(buf + k * 1024, W1, tile_unit(k), a.Ht - 1, lane, part * CI, CI);
+            stage_rows128<true>(buf + k * 1024 + 512, W2t, tile_unit(k), a.Ht - 1, lane, part * CI, CI);
+        }
+        wait_vmcnt<2 * CI>();            // tile 1's copies may be pending
+        stage_barrier();
+        asm volatile("" ::: "memory");
+        q_from_lds();
+        tgt_phase1(bv, 0);
+        lds_barrier();
+        phase2(0);
+        wait_vmcnt<0>();
+        stage_barrier();
+        asm volatile("" ::: "memory");
+        tgt_phase1(bv, 1);
+        store_sc();
+        lds_barrier();
+        phase2(1);
+    } else if (scw) {
+        const float bv = bs[min(ulane, a.Hs - 1)];
+        const uint16_t wv = ws2[min(ulane, a.Hs - 1)];
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < NT; ++k) stage_rows128(buf + k * 512, Ws, tile_unit(k), a.Hs - 1, lane, part * CI, CI);
+        wait_vmcnt<CI>();                // tile 1's copies may be pending
+        stage_barrier();
+        asm volatile("" ::: "memory");
+        q_from_lds();
+        const float wsv = __uint_as_float((uint32_t)wv << 16);
+        sc_phase1(bv, wsv, 0);
+        lds_barrier();
+        phase2(0);
+        wait_vmcnt<0>();
+        stage_barrier();
+        asm volatile("" ::: "memory");
+        sc_phase1(bv, wsv, 1);
+        store_sc();
+        lds_barrier();
+        phase2(1);
+    } else {
+        wait_vmcnt<0>();
+        stage_barrier();
+        lds_barrier();
+        phase2(0);
+        stage_barrier();
+        store_sc();
+        lds_barrier();
+        phase2(1);
+    }
+
+    // the block's read-out sums (each wave its dims and rows) and score sums
+    const bool direct = a.SB == 1 && !a.defer;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int r = 32 * part + 16 * nt + c;
+        const int rho = rg * 64 + r;
+        if (rho >= a.Rp) continue;
+        const int t = rho / a.G, gg = rho - t * a.G;
+        const size_t o = (size_t)t * a.Hq + h * a.G + gg;
+        const size_t row = (size_t)(h * a.SB + sb) * a.Rp + rho;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int dc = 32 * w + 16 * mb + 4 * g;
+            if (direct) *(f32x4 *)(a.A_out + o * D + dc) = acc[mb][nt] + *(const f32x4 *)(a.b2 + (size_t)h * D + dc);
+            else *(f32x4 *)(a.part_O + row * D + dc) = acc[mb][nt];
+        }
+        if (w == 0 && g == 0) {
+            const float ssum = (fs[r] + fs[64 + r]) + (fs[128 + r] + fs[192 + r]);
+            if (direct) a.a_out[o] = a.bs2[h] + ssum;
+            else a.part_s[row] = ssum;
+        }
+    }
+}
+
+// The LDS a decode block of (D, RT) uses.
+template <int D, int RT, int NT>
+using DecLdsOf = typename std::conditional<(D == 128 && dec_wps(D, RT) > 1), DecPairLds,
+                                           DecLds<D, RT, NT, dec_slots(D, RT)>>::type;
+
+template <int D, int RT, int ACT, int NT>
+__device__ __forceinline__ void mlp_decode_body_lds(const MlpParams &a, int blk_id, DecLdsOf<D, RT, NT> &lds) {
+    if constexpr (D == 128 && dec_wps(D, RT) > 1) mlp_decode_pair128<ACT>(a, blk_id, lds);
+    else mlp_decode_slots<D, RT, ACT, NT>(a, blk_id, lds);
+}
+
 template <int D, int RT, int ACT, int NT>
 __device__ __forceinline__ void mlp_decode_body(const MlpParams &a, int blk_id) {
-    __shared__ DecLds<D, RT, NT, dec_slots(D, RT)> lds;
+    __shared__ DecLdsOf<D, RT, NT> lds;
     mlp_decode_body_lds<D, RT, ACT, NT>(a, blk_id, lds);
 }
 

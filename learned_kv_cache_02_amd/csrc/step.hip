@@ -35,7 +35,7 @@ template <int D, int ACT, int RTM>
 __global__ __launch_bounds__((dec_threads(D, RTM)), 1) void step_partials_dec(AttnGroup gr, int nb_attn, MlpParams m) {
     // one LDS allocation for whichever body the block runs
     __shared__ union {
-        DecLds<D, RTM, kDecTiles, dec_slots(D, RTM)> mlp;
+        DecLdsOf<D, RTM, kDecTiles> mlp;
         AttnFoldLds<D, 1> attn;
     } lds;
     const int b = (int)blockIdx.x;

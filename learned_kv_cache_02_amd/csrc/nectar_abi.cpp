@@ -1181,6 +1181,17 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
                 }
             }
         }
+        // Nectar path at decode (the decode module beside the local part only):
+        // the local part in blocks of two split waves (the block's other two
+        // waves, a second row group that does not exist, end at once), so its
+        // caches spread over more CUs beside the module's blocks
+        if (sp.mlp && !exact && sp.mlpl.dec && d->dtype == NECTAR_BF16 && !sp.loc.lds && sp.loc.S > 0 &&
+            sp.loc.RT == 1 && sp.loc.RG == 1 && sp.loc.WS == 4 && d->splits <= 0) {
+            sp.loc.WR = 2;
+            sp.loc.WS = 2;
+            sp.loc.RB = 1;
+            sp.loc.SB = (int)cdiv(sp.loc.S, 2);
+        }
         size_t off = align256(attn_partial_bytes(d, sp.loc));
         if (exact) {
             sp.off_doc = off;

@@ -278,7 +278,11 @@ def test_mlp_many_rows(nx, d, R, Ht, Hs, splits):
 @pytest.mark.parametrize("R,Hq,Hkv,Ht,Hs", [(5, 14, 2, 100, 70), (1, 32, 8, 256, 96), (20, 8, 2, 64, 33),
                                              (3, 4, 1, 0, 40), (3, 4, 1, 50, 0), (10, 16, 4, 300, 200),
                                              (64, 32, 8, 600, 300), (10, 16, 4, 256, 128), (64, 32, 8, 640, 320),
-                                             (20, 8, 2, 0, 64), (16, 16, 4, 1000, 500), (11, 12, 4, 96, 40)])
+                                             (20, 8, 2, 0, 64), (16, 16, 4, 1000, 500), (11, 12, 4, 96, 40),
+                                             # 33-64 rows per KV head (the paired decode kernel): no target
+                                             # net, no score net, one-tile slots and odd widths
+                                             (10, 16, 4, 0, 200), (10, 16, 4, 300, 0), (14, 16, 4, 33, 7),
+                                             (12, 20, 4, 1000, 90)])
 @pytest.mark.parametrize("act", ["gelu", "silu", "gelu_tanh"])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_mlp_bf16(nx, R, Hq, Hkv, Ht, Hs, act, splits):

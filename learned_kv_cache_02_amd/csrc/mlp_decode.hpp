@@ -307,25 +307,46 @@ __device__ __forceinline__ void mlp_decode_slots(const MlpParams &a, int blk_id,
         dec_score_tile<D, RTW, ACT>(T, 32 * (t0 + k), a.Hs, qv, g, sc);
     };
     if constexpr (D == 128) {
+        // Loads complete in issue order (biases, then the tiles' copies tile by
+        // tile): each tile's products start once its own copies have landed,
+        // while the later tiles' are still in flight.  The wave reads only the
+        // stage it copied itself, so no barrier is needed.
+        static_assert(NT == 2 && (NS == 2 || NS == 4), "tile counts of the staged waits");
         if (tgt) {
             float tb[(NT + 1) / 2];
             tgt_bias(tb);
+            asm volatile("" ::: "memory");   // the bias loads stay ahead of the copies
             tgt_copies(0, 8);
+            wait_vmcnt<16>();                // tile 1's 16 copies may be pending
+            asm volatile("" ::: "memory");   // LDS reads stay below
+            if (n > 0) tgt_tile(tb, 0);
             wait_vmcnt<0>();
-            asm volatile("" ::: "memory");   // the copies landed: LDS reads stay below
-#pragma unroll
-            for (int k = 0; k < NT; ++k)
-                if (k < n) tgt_tile(tb, k);
+            asm volatile("" ::: "memory");
+            if (n > 1) tgt_tile(tb, 1);
         } else if (scw) {
             float sbias[(NS + 1) / 2];
             uint16_t swsv[(NS + 1) / 2];
             sc_bias(sbias, swsv);
-            sc_copies(0, 8);
-            wait_vmcnt<0>();
             asm volatile("" ::: "memory");
-#pragma unroll
-            for (int k = 0; k < NS; ++k)
-                if (k < n) sc_tile(sbias, swsv, k);
+            sc_copies(0, 8);
+            wait_vmcnt<8 * (NS - 1)>();      // tiles 1.. may be pending
+            asm volatile("" ::: "memory");
+            if (n > 0) sc_tile(sbias, swsv, 0);
+            if constexpr (NS == 4) {
+                wait_vmcnt<16>();
+                asm volatile("" ::: "memory");
+                if (n > 1) sc_tile(sbias, swsv, 1);
+                wait_vmcnt<8>();
+                asm volatile("" ::: "memory");
+                if (n > 2) sc_tile(sbias, swsv, 2);
+                wait_vmcnt<0>();
+                asm volatile("" ::: "memory");
+                if (n > 3) sc_tile(sbias, swsv, 3);
+            } else {
+                wait_vmcnt<0>();
+                asm volatile("" ::: "memory");
+                if (n > 1) sc_tile(sbias, swsv, 1);
+            }
         }
     } else {
         if (tgt) {

@@ -1163,13 +1163,16 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
         // Quadrature path at decode: the pairs' LDS-staged blocks and the local
         // part's, as LDS-staged blocks of the same shape, in one launch of at
         // most one block per CU: the local part takes its key stages as splits
-        // (at most four), the pairs the remaining block slots
+        // (at most two: a 384-key local part in 64 blocks of two stages leaves
+        // the pairs 148 blocks of three stages instead of 112 of four beside 128
+        // local blocks of one; 1M-token Quadrature path 19.73 -> 19.12 us, and
+        // 19.73 -> 21.5 us with one split), the pairs the remaining block slots
         if (sp.kvp && !exact && sp.kvpl.lds && sp.kvpl.S > 0 && !sp.kvpl.xcd && d->splits <= 0 &&
             sp.loc.S > 0 && !sp.loc.lds && d->dtype == NECTAR_BF16 && d->d == 128 &&
             lds_shape_for(sp.loc.Rp).NW == sp.kvpl.sh.NW && lds_shape_for(sp.loc.Rp).SK == sp.kvpl.sh.SK &&
             lds_shape_for(sp.loc.Rp).RT == sp.kvpl.sh.RT && sp.kvpl.sh.NW == 4 && sp.kvpl.sh.SK == 96) {
             const long lstages = cdiv(loc->T_loc, sp.kvpl.sh.SK);
-            const long lblocks = (long)sp.loc.P * std::min(lstages, 4L);
+            const long lblocks = (long)sp.loc.P * std::min(lstages, 2L);
             if (lblocks <= kTargetBlocksLds / 2) {
                 const AttnPlan l2 = plan_attn(d, sp.loc.P, sp.loc.Rp, loc->T_loc, true, kTargetWaves, lblocks);
                 const AttnPlan k2 = plan_attn(d, sp.kvpl.P, sp.kvpl.Rp, (long)m->p, true, kTargetWaves,

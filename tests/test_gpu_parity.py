@@ -454,9 +454,11 @@ STEP_CASES = {
     # the pairs' and the local part's LDS-staged blocks in one launch: one partial local
     # stage (40 keys) beside pairs of a ragged last stage (301 = 3 x 96 + 13)
     "kvpair_short_local": ("bf16", 128, 8, 1, 40, 48, 39, 28, 4, None, ("kvpair", 301)),
-    # ... and local stages beyond the paired plan's four (more than 128 local blocks:
-    # the pairs and the local pass launch apart)
-    "kvpair_many_local": ("bf16", 128, 12, 1, 500, 512, 499, 28, 4, None, ("kvpair", 1000)),
+    # ... a local part of several stages per split (12 x 4 problems, 500 keys: two splits
+    # of three stages), and one beyond the paired plan (20 x 4 problems in two splits:
+    # more than 128 local blocks, so the pairs and the local pass launch apart)
+    "kvpair_local_stages": ("bf16", 128, 12, 1, 500, 512, 499, 28, 4, None, ("kvpair", 1000)),
+    "kvpair_many_local": ("bf16", 128, 20, 1, 500, 512, 499, 28, 4, None, ("kvpair", 1000)),
     "tiny_f32_d64": ("f32", 64, 1, 16, 16, 16, 0, 2, 1, 512, ("mlp", 256, 256)),
     "decode_bf16_d64": ("bf16", 64, 3, 1, 40, 48, 39, 8, 2, 777, ("mlp", 100, 70)),
     "empty_doc_and_local": ("bf16", 128, 2, 1, 0, 8, 0, 8, 2, 0, ("mlp", 0, 40)),

@@ -264,7 +264,7 @@ __device__ __forceinline__ void attn_rows_lds_body(const AttnParams &a, unsigned
 }
 
 template <int NW, int RT, int kStageKeys>
-__global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
+__global__ __launch_bounds__(NW * 64, (lds_blocks_per_cu(kStageKeys))) void attn_rows_lds(AttnParams a) {
     attn_rows_lds_body<NW, RT, kStageKeys>(a, blockIdx.x);
 }
 
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds(AttnParams a) {
 // pairs beside the decode local part: the local blocks run beside the pairs'
 // instead of in a launch of their own).  Neither set may use xcd_group.
 template <int NW, int RT, int kStageKeys>
-__global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds_pair(AttnGroup gr) {
+__global__ __launch_bounds__(NW * 64, (lds_blocks_per_cu(kStageKeys))) void attn_rows_lds_pair(AttnGroup gr) {
     const unsigned b = blockIdx.x;
     const bool second = b >= (unsigned)gr.nb0;
     const AttnParams &a = second ? gr.p[1] : gr.p[0];
@@ -510,7 +510,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
 // when a block's four row tiles cover the problem; otherwise the 32-row kernel
 // (eight waves, two per SIMD, 64-key stages).
 // RT == 2 selects the 32-row kernel (eight waves, 256 rows per block).
-LdsShape lds_shape_for(int Rp) { return Rp <= 64 ? LdsShape{4, 1, 96} : LdsShape{8, 2, 64}; }
+// Up to 64 rows per problem: four 16-row waves and 32-key stages, two blocks
+// per CU (1M-token decode layer's document pass, 56 rows per KV head: 0.726 ->
+// 0.80 of HBM against 96-key stages at one block per CU); more rows: the
+// 32-row kernel with 64-key stages.
+LdsShape lds_shape_for(int Rp) {
+    return Rp <= 64 ? LdsShape{4, 1, 32, lds_blocks_per_cu(32)} : LdsShape{8, 2, 64, lds_blocks_per_cu(64)};
+}
 
 hipError_t launch_attn_rows_lds_pair(const AttnParams &p0, const AttnParams &p1, LdsShape sh, hipStream_t st) {
     if (p0.xcd_group || p1.xcd_group) return hipErrorInvalidValue;
@@ -526,8 +532,8 @@ hipError_t launch_attn_rows_lds_pair(const AttnParams &p0, const AttnParams &p1,
 
 hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st) {
     dim3 grid((unsigned)((long)p.P * p.RB * p.SB)), block(sh.NW * 64);
-    if (sh.NW == 4 && sh.RT == 1 && sh.SK == 96) hipLaunchKernelGGL((attn_rows_lds<4, 1, 96>), grid, block, 0, st, p);
-    else if (sh.NW == 8 && sh.RT == 1 && sh.SK == 64) hipLaunchKernelGGL((attn_rows_lds<8, 1, 64>), grid, block, 0, st, p);
+    if (sh.NW == 4 && sh.RT == 1 && sh.SK == 32) hipLaunchKernelGGL((attn_rows_lds<4, 1, 32>), grid, block, 0, st, p);
+    else if (sh.NW == 4 && sh.RT == 1 && sh.SK == 96) hipLaunchKernelGGL((attn_rows_lds<4, 1, 96>), grid, block, 0, st, p);
     else if (sh.NW == 8 && sh.RT == 2 && sh.SK == 64) hipLaunchKernelGGL((attn_rows_lds32<8, 64>), grid, block, 0, st, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();

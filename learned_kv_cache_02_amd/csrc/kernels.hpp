@@ -344,7 +344,11 @@ hipError_t launch_attn_partial(const AttnParams &p, int dtype, int d, int rt, hi
 // RT row tiles per block, 16 * NW * RT rows, keys staged SK at a time.
 struct LdsShape {
     int NW, RT, SK;
+    int BPC;   // blocks per compute unit the kernel of this shape is built for
 };
+// Blocks per compute unit of the LDS-staged kernel with kStageKeys-key stages:
+// two with 32-key stages (48 KB of LDS each), else one.
+constexpr int lds_blocks_per_cu(int stage_keys) { return stage_keys == 32 ? 2 : 1; }
 LdsShape lds_shape_for(int Rp);
 hipError_t launch_attn_rows_lds(const AttnParams &p, LdsShape sh, hipStream_t st);
 // Two problem sets of the same shape in one launch (shape {4, 1, 96} only).

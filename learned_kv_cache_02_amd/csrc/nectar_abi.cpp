@@ -50,8 +50,8 @@ constexpr long kTargetWavesMlp = NECTAR_TARGET_WAVES_MLP;
 #define NECTAR_TARGET_WAVES_MLP_SHARED 2048
 #endif
 constexpr long kTargetWavesMlpShared = NECTAR_TARGET_WAVES_MLP_SHARED;
-// Blocks a split plan of the LDS-staged kernel aims for: one per CU (a block
-// holds 96 KB of LDS, so one is resident per CU).
+// Compute units a split plan of the LDS-staged kernel aims to fill: this many
+// times the shape's blocks per CU (LdsShape::BPC, set by its LDS use).
 #ifndef NECTAR_LDS_TARGET_BLOCKS
 #define NECTAR_LDS_TARGET_BLOCKS 256
 #endif
@@ -123,7 +123,7 @@ void block_shape(int RG, int &WR, int &WS, int &RB) {
 // lds_blocks > 0: the LDS-staged kernel whatever the row count, its split count
 // aiming for that many blocks (a problem set sharing one launch with another).
 AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv, bool balanced = true,
-                   long target_waves = kTargetWaves, long lds_blocks = 0) {
+                   long target_waves = kTargetWaves, long lds_blocks = 0, const LdsShape *lds_shape = nullptr) {
     AttnPlan pl;
     pl.P = P;
     pl.Rp = Rp;
@@ -133,13 +133,13 @@ AttnPlan plan_attn(const nectar_attn_desc *d, int P, int Rp, long T_kv, bool bal
         // LDS-staged kernel: blocks of 16 * NW * RT rows x key splits of whole
         // SK-key stages; a block finishes its rows in place when S == 1
         pl.lds = true;
-        pl.sh = lds_shape_for(Rp);
+        pl.sh = lds_shape ? *lds_shape : lds_shape_for(Rp);
         pl.RT = pl.sh.RT;
         pl.WR = pl.sh.NW;
         pl.RB = (int)cdiv(Rp, 16L * pl.sh.NW * pl.sh.RT);
         pl.RG = (int)cdiv(Rp, 16L * pl.RT);
         const long stages = cdiv(T_kv, pl.sh.SK);
-        const long target = lds_blocks > 0 ? lds_blocks : kTargetBlocksLds;
+        const long target = lds_blocks > 0 ? lds_blocks : kTargetBlocksLds * pl.sh.BPC;
         long S = d->splits > 0 ? d->splits : cdiv(target, (long)P * pl.RB);
         S = S < 1 ? 1 : (S > stages ? stages : S);
         const long per = cdiv(stages, S);
@@ -1161,22 +1161,26 @@ static StepPlan plan_step(const nectar_attn_desc *d, int64_t n, const nectar_loc
             if (loc_waves < kTargetWaves / 4) sp.doc = plan_attn(d, d->Hkv, Rp_doc, (long)n, true, kTargetWaves - loc_waves);
         }
         // Quadrature path at decode: the pairs' LDS-staged blocks and the local
-        // part's, as LDS-staged blocks of the same shape, in one launch of at
-        // most one block per CU: the local part takes its key stages as splits
-        // (at most two: a 384-key local part in 64 blocks of two stages leaves
-        // the pairs 148 blocks of three stages instead of 112 of four beside 128
-        // local blocks of one; 1M-token Quadrature path 19.73 -> 19.12 us, and
-        // 19.73 -> 21.5 us with one split), the pairs the remaining block slots
+        // part's, as LDS-staged blocks of one shape, in one launch of at most
+        // one block per CU.  That launch is short (a few stages per block), and
+        // 96-key stages at one block per CU serve it better than the 32-key
+        // stages at two that stream the long document passes (1M-token
+        // Quadrature path 19.2 us against 20.7-24.3 us).  The local part takes
+        // its key stages as splits (at most two: a 384-key local part in 64
+        // blocks of two stages leaves the pairs 148 blocks of three stages
+        // instead of 112 of four beside 128 local blocks of one; 19.73 -> 19.12
+        // us, and 21.5 us with one split), the pairs the remaining block slots.
         if (sp.kvp && !exact && sp.kvpl.lds && sp.kvpl.S > 0 && !sp.kvpl.xcd && d->splits <= 0 &&
-            sp.loc.S > 0 && !sp.loc.lds && d->dtype == NECTAR_BF16 && d->d == 128 &&
-            lds_shape_for(sp.loc.Rp).NW == sp.kvpl.sh.NW && lds_shape_for(sp.loc.Rp).SK == sp.kvpl.sh.SK &&
-            lds_shape_for(sp.loc.Rp).RT == sp.kvpl.sh.RT && sp.kvpl.sh.NW == 4 && sp.kvpl.sh.SK == 96) {
-            const long lstages = cdiv(loc->T_loc, sp.kvpl.sh.SK);
+            sp.loc.S > 0 && !sp.loc.lds && d->dtype == NECTAR_BF16 && d->d == 128 && sp.loc.Rp <= 64 &&
+            sp.kvpl.Rp <= 64) {
+            const LdsShape psh{4, 1, 96, lds_blocks_per_cu(96)};
+            const long slots = kTargetBlocksLds * psh.BPC;
+            const long lstages = cdiv(loc->T_loc, psh.SK);
             const long lblocks = (long)sp.loc.P * std::min(lstages, 2L);
-            if (lblocks <= kTargetBlocksLds / 2) {
-                const AttnPlan l2 = plan_attn(d, sp.loc.P, sp.loc.Rp, loc->T_loc, true, kTargetWaves, lblocks);
+            if (lblocks <= slots / 2) {
+                const AttnPlan l2 = plan_attn(d, sp.loc.P, sp.loc.Rp, loc->T_loc, true, kTargetWaves, lblocks, &psh);
                 const AttnPlan k2 = plan_attn(d, sp.kvpl.P, sp.kvpl.Rp, (long)m->p, true, kTargetWaves,
-                                              kTargetBlocksLds - (long)l2.P * l2.RB * l2.SB);
+                                              slots - (long)l2.P * l2.RB * l2.SB, &psh);
                 if (l2.lds && k2.lds && !l2.xcd && !k2.xcd) {
                     sp.loc = l2;
                     sp.kvpl = k2;

@@ -99,6 +99,8 @@ constexpr int dec_score_tiles(int rt) { return kDecTiles * (rt > 1 ? 1 : 2); }
 // (Two paired slots per block -- 256 blocks at the 1M-token layer -- measured
 // slower: twice the partials, and beside the local blocks a second round of
 // blocks; 1M-token Nectar path 17.55 -> 23.4 us.)
+// The paired kernel splits the output dims over the eight waves of four slots,
+// so four is the only value it compiles with.
 #ifndef NECTAR_DEC_SLOTS_PAIRED
 #define NECTAR_DEC_SLOTS_PAIRED 4
 #endif

@@ -444,6 +444,9 @@ __device__ __forceinline__ void mlp_decode_slots(const MlpParams &a, int blk_id,
 template <int ACT>
 __device__ __forceinline__ void mlp_decode_pair128(const MlpParams &a, int blk_id, DecPairLds &lds) {
     constexpr int D = 128, SL = 4, NT = 2, CI = 4;
+    // the planner's slots per block (dec_slots) must be the four this kernel's
+    // dim split over its eight waves assumes
+    static_assert(dec_slots(D, 4) == SL && dec_wps(D, 4) == 2, "four paired slots per block");
     const int v = threadIdx.x >> 6;
     const int w = v & 3, part = v >> 2;
     int blk = blk_id;

@@ -26,6 +26,10 @@
 // kSlack (log2 units): until then the old reference stays, so the O rescale is
 // skipped; P <= 2^kSlack keeps every sum finite and the result is unchanged
 // (the same reference max is used for the numerator and the denominator).
+// The 32-row kernel tests the weights instead of the scores: it exponentiates a
+// tile against the current reference and looks for the tile's maximum only
+// when the tile's weights in a lane sum past 2^kSlack (any weight above 2^kSlack
+// does), so the common tile skips the max reduction.
 #include "attn_common.hpp"
 #include "lds_common.hpp"
 
@@ -37,11 +41,22 @@ constexpr int kD = 128, kKS = 4, kDV = 8;
 constexpr int kStages = 3;
 constexpr int kPieces = kD * 2 / 16;            // 16-byte pieces per key row
 constexpr float kSlack = 8.0f;
+constexpr float kSlackSum = 256.0f;                // 2^kSlack
 // Cache policy of the K/V copies: non-temporal (the cache is streamed once per
 // call; measured 6 % faster on a 2 GB cache than the default policy).
 constexpr int kStreamPolicy = 2;
 
 }  // namespace
+
+// Sum of a lane's 16 tile weights as a balanced tree (four dependent adds).
+__device__ __forceinline__ float tile_sum16(const float (&p)[16]) {
+    float s8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s8[j] = p[2 * j] + p[2 * j + 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s8[j] += s8[j + 4];
+    return (s8[0] + s8[2]) + (s8[1] + s8[3]);
+}
 
 // The kernel body for block `bid` of problem set `a` (shared by the launch of one
 // set and the launch of two sets side by side).
@@ -418,25 +433,31 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
                 for (int j = 0; j < 16; ++j)
                     if (kbase + 8 * (j >> 2) + 4 * hf + (j & 3) >= lim) sv[j] = -INFINITY;
             }
-            float mt = sv[0];
+            // weights against the current reference first; the tile's maximum is
+            // looked for only when they sum past 2^kSlack (some weight above
+            // 2^(kSlack - 4)) or the row has no reference yet
+            float nm = (m == -INFINITY) ? 0.f : -m;
+            float pv[16];
 #pragma unroll
-            for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sv[j]);
-            mt *= sl2;
-            if (__ballot(mt > m + kSlack) != 0) {
+            for (int j = 0; j < 16; ++j) pv[j] = fast_exp2(__builtin_fmaf(sv[j], sl2, nm));
+            float lt = tile_sum16(pv);
+            if (__ballot(m == -INFINITY || !(lt <= kSlackSum)) != 0) {
+                float mt = sv[0];
+#pragma unroll
+                for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sv[j]);
+                mt *= sl2;
                 const float mnew = fmaxf(m, fmaxf(mt, __shfl_xor(mt, 32, 64)));
                 const float sc = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
                 l *= sc;
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi) O[mi] *= sc;
                 m = mnew;
-            }
-            const float nm = (m == -INFINITY) ? 0.f : -m;
-            float pv[16];
+                nm = (m == -INFINITY) ? 0.f : -m;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                pv[j] = fast_exp2(__builtin_fmaf(sv[j], sl2, nm));
-                l += pv[j];
+                for (int j = 0; j < 16; ++j) pv[j] = fast_exp2(__builtin_fmaf(sv[j], sl2, nm));
+                lt = tile_sum16(pv);
             }
+            l += lt;
 #pragma unroll
             for (int tg = 0; tg < 2; ++tg) {
                 const u32x4 P = {pack_bf16(pv[8 * tg + 0], pv[8 * tg + 1]), pack_bf16(pv[8 * tg + 2], pv[8 * tg + 3]),

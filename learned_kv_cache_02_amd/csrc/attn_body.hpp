@@ -65,31 +65,45 @@ __device__ __forceinline__ void attend_tile(const KVTile<D> &T, int k0, const u3
         }
         float sv[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) { sv[r] = s0[r] * sl2; sv[4 + r] = s1[r] * sl2; }
+        for (int r = 0; r < 4; ++r) { sv[r] = s0[r]; sv[4 + r] = s1[r]; }
         if (k0 + 32 > lim[rt]) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 if (k0 + slot_key(g, j) >= lim[rt]) sv[j] = -INFINITY;
         }
-        float mt = sv[0];
+        // Lazy reference: the tile's weights against the row's current
+        // reference m first; the reference moves to the running maximum (and
+        // O and l are rescaled) only when a lane's weights sum past 2^8 -- which
+        // every weight above 2^8 makes them do -- or the row has none yet and
+        // sees a key of the tile (rows masked to nothing keep none).  The
+        // same reference enters numerator and denominator, so the function is
+        // unchanged, and the common tile skips the max reduction and the
+        // rescale of O.
+        float nm = (m[rt] == -INFINITY) ? 0.f : -m[rt];
+        float pv[8];
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
-        mt = group4_max(mt);
-        const float mnew = fmaxf(m[rt], mt);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = fast_exp2(m[rt] - muse);
-        float pv[8], ps = 0.f;
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(__builtin_fmaf(sv[j], sl2, nm));
+        float ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        if (__ballot((m[rt] == -INFINITY && k0 < lim[rt]) || !(ps <= 256.f)) != 0) {
+            float mt = sv[0];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { pv[j] = fast_exp2(sv[j] - muse); ps += pv[j]; }
-        l[rt] = l[rt] * alpha + ps;
-        m[rt] = mnew;
+            for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
+            const float mnew = fmaxf(m[rt], group4_max(mt * sl2));
+            const float sc = (m[rt] == -INFINITY) ? 0.f : fast_exp2(m[rt] - mnew);
+            l[rt] *= sc;
+#pragma unroll
+            for (int mm = 0; mm < DV; ++mm) O[rt][mm] *= sc;
+            m[rt] = mnew;
+            nm = (mnew == -INFINITY) ? 0.f : -mnew;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(__builtin_fmaf(sv[j], sl2, nm));
+            ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        }
+        l[rt] += ps;
         const u32x4 P = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
                          pack_bf16(pv[6], pv[7])};
 #pragma unroll
-        for (int mm = 0; mm < DV; ++mm) {
-            O[rt][mm] *= alpha;
-            O[rt][mm] = mfma16(vt[mm], P, O[rt][mm]);
-        }
+        for (int mm = 0; mm < DV; ++mm) O[rt][mm] = mfma16(vt[mm], P, O[rt][mm]);
     }
 }
 
@@ -152,6 +166,16 @@ __device__ __forceinline__ void attn_partial_body_lds(const AttnParams &a, int b
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) wlim = max(wlim, __shfl_xor(wlim, o, 64));
+    // a negative scale is carried by the query's sign (exact for bf16), so the
+    // tile code works with sl2 > 0 (masked scores stay -inf)
+    float sl2 = a.sl2;
+    if (sl2 < 0.f) {
+        sl2 = -sl2;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kt = 0; kt < KS; ++kt) qv[rt][kt] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
 
     f32x4 O[RT][DV];
     float m[RT], l[RT];
@@ -185,7 +209,7 @@ __device__ __forceinline__ void attn_partial_body_lds(const AttnParams &a, int b
             for (int u = 0; u < SUB; ++u) load_kv_tile<D>(tl[u], kb, vb, a.kv_row, min(k0 + 32 * u, kmax), kmax, g, c);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < SUB; ++u) attend_tile<D, RT>(tl[u], k0 + 32 * u, qv, limw, a.sl2, g, O, m, l);
+            for (int u = 0; u < SUB; ++u) attend_tile<D, RT>(tl[u], k0 + 32 * u, qv, limw, sl2, g, O, m, l);
         }
     }
 #pragma unroll

@@ -435,13 +435,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_rows_lds32(AttnParams a) {
             }
             // weights against the current reference first; the tile's maximum is
             // looked for only when they sum past 2^kSlack (some weight above
-            // 2^(kSlack - 4)) or the row has no reference yet
+            // 2^(kSlack - 4)) or the row has no reference yet and a key of the
+            // tile is visible to it (a row masked to nothing keeps none)
             float nm = (m == -INFINITY) ? 0.f : -m;
             float pv[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) pv[j] = fast_exp2(__builtin_fmaf(sv[j], sl2, nm));
             float lt = tile_sum16(pv);
-            if (__ballot(m == -INFINITY || !(lt <= kSlackSum)) != 0) {
+            if (__ballot((m == -INFINITY && kbase < lim) || !(lt <= kSlackSum)) != 0) {
                 float mt = sv[0];
 #pragma unroll
                 for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sv[j]);

@@ -209,6 +209,22 @@ def test_scaled_query_stress(nx):
     check("A (8x query)", host(A), eA, ATOL_OUT_BF16)
 
 
+@pytest.mark.parametrize("R", [1, 12, 40])          # register-direct, 16-row and 32-row LDS-staged kernels
+@pytest.mark.parametrize("scale", [0.2, -0.0884, -0.35])
+def test_doc_attn_explicit_and_negative_scale(nx, R, scale):
+    # An explicit score scale of either sign (Eq. (3.1) with s_j = scale q.k_j):
+    # the kernels carry a negative scale by the query's sign.
+    Hq, Hkv, n, d = 8, 2, 2500, 128
+    g = _rng(40 + R)
+    q = _bf(g.standard_normal((R, Hq, d)))
+    K, V = (_bf(g.standard_normal((Hkv, n, d))) for _ in range(2))
+    print("case doc attn scale %g R %d" % (scale, R), flush=True)
+    a, A = nx.doc_attn_exact(dev(q), dev(K), dev(V), Hkv, scale=scale)
+    ea, eA = oracle.doc_attn(q, K, V, dt="bf16", Hq=Hq, Hkv=Hkv, scale=scale)
+    check("alpha (scale %g)" % scale, host(a), ea, ATOL_LSE_BF16)
+    check("A (scale %g)" % scale, host(A), eA, ATOL_OUT_BF16)
+
+
 def test_doc_attn_empty_document(nx):
     import torch
     R, Hq, Hkv, d = 2, 4, 2, 128

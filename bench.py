@@ -488,7 +488,7 @@ def c2_layer(torch, np, nectar, configs, synth, dev, nrep=24, passes=10):
     ach = doc_bytes / (u * 1e-6) / 1e9
     res["doc_partial_roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic("doc_attn_c2"),
-                                   "kernel": "nectar_doc_attn_partials (attn_partial_mfma), %.2f us per launch, "
+                                   "kernel": "nectar_doc_attn_partials (attn_rows_lds, 32-key stages), %.2f us per launch, "
                                              "%d algorithmic bytes per launch" % (u, doc_bytes)}
     ue = us["doc"]["us"]
     res["exact_doc_entry_point"] = {"us": ue, "gbs": doc_bytes / (ue * 1e-6) / 1e9,

@@ -33,8 +33,8 @@ TARGETS = {
     "doc_attn_c5": dict(kernel="attn_rows_lds", leg="c5_doc_partial", steps=8, algo=4 * 1048576 * 2 * 128 * 2,
                         what="split-K partial pass of the exact document attention (attn_rows_lds) over one "
                              "layer of the 1M-token stack (4 KV heads x 1,048,576 keys)"),
-    "doc_attn_c2": dict(kernel="attn_partial_mfma", leg="c2_doc_partial", steps=48, algo=8 * 61440 * 2 * 128 * 2,
-                        what="split-K partial pass of the exact document attention (attn_partial_mfma) on the "
+    "doc_attn_c2": dict(kernel="attn_rows_lds", leg="c2_doc_partial", steps=48, algo=8 * 61440 * 2 * 128 * 2,
+                        what="split-K partial pass of the exact document attention (attn_rows_lds) on the "
                              "Qwen3-4B-shaped decode layer (8 KV heads x 61,440 keys)"),
 }
 COPY = "copyBuffer"

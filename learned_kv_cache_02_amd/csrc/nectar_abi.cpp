@@ -197,7 +197,11 @@ struct MlpPlan {
 constexpr int kPrefillRows = 65;
 constexpr int kPrefillBlockRows = 256;
 // Blocks a split plan of the batched kernel aims for (one 512-thread block per CU).
-constexpr long kTargetBlocksPrefill = 256;
+// Blocks a batched module plan aims for (256-row blocks x hidden-unit splits).
+#ifndef NECTAR_PREFILL_TARGET_BLOCKS
+#define NECTAR_PREFILL_TARGET_BLOCKS 256
+#endif
+constexpr long kTargetBlocksPrefill = NECTAR_PREFILL_TARGET_BLOCKS;
 
 // The document pass of the exact-attention entry points (no other part shares
 // its launch).  Up to 16 rows per KV head over a long document, the LDS-staged

@@ -157,9 +157,9 @@ def test_doc_attn_validation(lib):
 
 def test_workspace_sizes(lib):
     # n = 61,440 document keys, 8 KV heads, 4 query heads per group, one token:
-    # 960 batches of 64 keys in 256 balanced splits (3 or 4 batches each)
-    # folded four per block -> 64 partials per row, 4 rows per head,
-    # (128 + 2) floats per row.
+    # the entry point's LDS-staged plan, 512 blocks of 32-key stages (two per
+    # CU) -> 64 key splits of 30 stages per head, 4 rows per head, (128 + 2)
+    # floats per row.  (Forced split counts keep the register-direct plan.)
     d = Desc(1, 32, 8, 128, 1, 0.0, 0)
     assert lib.nectar_doc_attn_workspace_size(ctypes.byref(d), 61440) == 8 * 64 * 4 * 520
     assert lib.nectar_doc_attn_workspace_size(ctypes.byref(d), 0) == 0

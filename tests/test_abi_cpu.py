@@ -433,6 +433,41 @@ def test_layer_step_validation(lib):
     assert call(exact_only, desc=d0, lc=Local(0, 1, 513, 513, 512), q=None) == OK
 
 
+def test_layer_step_static_validation(lib):
+    """The allocation-free layer step validates on the host before any HIP call:
+    argument errors, and plans larger than its static device scratch
+    (NECTAR_STATIC_SCRATCH_BYTES = 64 MiB), are rejected without a GPU."""
+    P, D = ctypes.c_void_p, ctypes.POINTER(Desc)
+    f = lib.nectar_layer_step_static
+    f.argtypes = [D, ctypes.c_int64, ctypes.POINTER(Local), P, P, P, P, P, ctypes.POINTER(Module),
+                  ctypes.POINTER(StepOuts), P]
+    static_bytes = 64 << 20
+    hdr = open(HDR).read()
+    assert "#define NECTAR_STATIC_SCRATCH_BYTES (64u << 20)" in hdr
+
+    def call(desc, n, lc, module, outs, q=A16):
+        return f(ctypes.byref(desc), n, ctypes.byref(lc), q, A16, A16, A16, A16,
+                 ctypes.byref(module) if module else None, ctypes.byref(outs), None)
+
+    both = StepOuts(out_exact=A16, lse_exact=A16, out_nectar=A16, lse_nectar=A16)
+    # the 16 x 1,024-token prefill layer with the rho = 10 % module: far beyond the scratch
+    dp = Desc(16 * 1024, 28, 4, 128, 1, 0.0, 0)
+    lp = Local(16, 1024, 1024, 1024, 0)
+    mp = _mlp_module(7680, 5120)
+    need = lib.nectar_layer_step_workspace_size(ctypes.byref(dp), 131072, ctypes.byref(lp), ctypes.byref(mp), 1)
+    assert need > static_bytes
+    assert call(dp, 131072, lp, mp, both) == EWORKSPACE
+    # argument errors come first, as in nectar_layer_step
+    assert call(dp, 131072, lp, mp, both, q=MIS) == EINVAL
+    assert call(dp, -1, lp, mp, both) == EINVAL
+    # the decode shapes fit: the 4B layer with both paths needs a few MiB
+    d = Desc(1, 32, 8, 128, 1, 0.0, 0)
+    loc = Local(1, 1, 513, 513, 512)
+    m = _mlp_module(4608, 2944)
+    assert 0 < lib.nectar_layer_step_workspace_size(ctypes.byref(d), 61440, ctypes.byref(loc), ctypes.byref(m),
+                                                    1) <= static_bytes
+
+
 def test_doc_attn_two_pass_validation(lib):
     P = ctypes.c_void_p
     D = ctypes.POINTER(Desc)
